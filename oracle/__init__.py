@@ -1,0 +1,24 @@
+"""Float64 CPU oracle for paged KV-cache attention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import anything from this package.  The
+product path (``paged_kv_cache_24_amd``) never imports it and shares no code,
+header, table or helper with it.
+
+Every function follows a passage of the source pages; each docstring cites the
+page title and section it restates.
+"""
+
+from .paged_attention import (  # noqa: F401
+    bits_to_float64,
+    kv_bytes_per_token,
+    ref_reshape_and_cache,
+    gather_tokens,
+    ref_contiguous_attention,
+    ref_decode,
+    ref_decode_one,
+    ref_prefill_paged,
+    ref_prefill_rows,
+    ref_partition_state,
+    ref_merge_partitions,
+)
