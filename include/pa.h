@@ -1,0 +1,216 @@
+/*
+ * pa.h -- C ABI of the paged KV-cache attention library (libpa.so, gfx950).
+ *
+ * The KV cache is cut into fixed 16-token blocks that live in one global
+ * pool; every sequence owns a block table mapping its logical blocks to
+ * physical blocks ("vLLM-Ascend 原理", §2.1 "PagedAttention 分页 KV 缓存").
+ * The attention calls read K/V through that table, block by block, with no
+ * gather into contiguous memory ("vLLM 在 CANN 上的推理优化", section
+ * "CANN 上的 PagedAttention 算子" and the note after it on passing block ids
+ * and the table straight to attention).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers.  Every tensor pointer is a DEVICE pointer to contiguous row-major
+ * memory in the layout stated on the call; 16-bit tensors and the workspace
+ * must be 16-byte aligned (the kernels move 16-byte vectors).  The caller allocates and owns
+ * every buffer, including the decode workspace; the library allocates
+ * nothing, keeps no pointer after a call returns, and holds no state, so
+ * every call is re-entrant and may be issued from any host thread.
+ *
+ * Element types.  q, out, key, value and both caches share one 16-bit type,
+ * pa_dtype.  Accumulation is float32; outputs are rounded to nearest even.
+ *
+ * KV cache layout.  k_cache and v_cache are two separate tensors, each
+ * [num_blocks][block_size][num_kv_heads][head_dim].  Token slot
+ * s = physical_block * block_size + offset addresses row s of the
+ * [num_blocks * block_size][num_kv_heads][head_dim] view.  block_size must be
+ * 16, head_dim 64 or 128.
+ *
+ * Streams.  Work is enqueued on `stream` (0 = the null stream).  No call
+ * synchronises, reads device memory from the host or allocates, so every call
+ * may be captured in a HIP graph.  A return of PA_OK means "enqueued";
+ * faults inside kernels surface at the caller's next synchronisation.
+ *
+ * Errors.  Arguments are validated on the host before anything is enqueued;
+ * on a negative status nothing was launched.  No C++ exception crosses this
+ * interface.  Device-resident indices are not validated on the host (that
+ * would need a read-back): a block-table entry outside [0, num_blocks) or a
+ * slot outside [0, num_blocks * block_size) is never dereferenced -- the
+ * kernels skip it -- but results involving it are unspecified.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The HIP runtime's opaque stream handle (the same typedef as hip_runtime_api.h). */
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_NULL_PTR = -1,    /* a required pointer is NULL */
+    PA_ERR_UNSUPPORTED = -2, /* head_dim, block_size or dtype outside what is built */
+    PA_ERR_SHAPE = -3,       /* inconsistent or out-of-range sizes */
+    PA_ERR_WORKSPACE = -4,   /* decode workspace missing or too small */
+    PA_ERR_HIP = -5,         /* the HIP runtime refused a launch */
+    PA_ERR_ALIGNMENT = -6    /* a tensor or the workspace is not 16-byte aligned */
+} pa_status;
+
+typedef enum pa_dtype {
+    PA_F16 = 0,  /* IEEE binary16 */
+    PA_BF16 = 1  /* bfloat16 */
+} pa_dtype;
+
+#define PA_BLOCK_SIZE 16
+
+/*
+ * pa_kv_bytes_per_token -- K+V bytes one token occupies over all layers:
+ * 2 * layers * kv_heads * head_dim * dtype_bytes ("vLLM-Ascend 原理", §2.1,
+ * the KV size formula).  Pure host arithmetic; returns 0 if any argument is
+ * not positive.
+ */
+uint64_t pa_kv_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_dim,
+                               int32_t dtype_bytes);
+
+/* pa_status_string -- static, never-NULL description of a status code. */
+const char* pa_status_string(int32_t status);
+
+/*
+ * pa_reshape_and_cache -- the cache write: store each new token's k and v in
+ * its slot ("vLLM-Ascend 原理", §2.3 step 3 and §2.4 step 3: new k, v go into
+ * the physical blocks named by the block table, 16 tokens per block).
+ *
+ *   key, value    [num_tokens][num_kv_heads][head_dim]            (read)
+ *   k_cache,
+ *   v_cache       [num_blocks][block_size][num_kv_heads][head_dim] (written)
+ *   slot_mapping  int64 [num_tokens]; slot s -> block s / block_size,
+ *                 offset s % block_size.  s < 0 marks a padding row and is
+ *                 skipped; s >= num_blocks * block_size is skipped too.
+ *
+ * A bit copy: no conversion.  Slots must be distinct (two tokens writing one
+ * slot leave either value).  num_tokens == 0 is a no-op returning PA_OK.
+ */
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache,
+                               void* v_cache, const int64_t* slot_mapping,
+                               int64_t num_tokens, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                               pa_dtype dtype, hipStream_t stream);
+
+/*
+ * pa_decode_default_partition -- the split-KV partition length, in tokens, that
+ * pa_decode uses when given partition_tokens == 0 (a multiple of 16).  A
+ * partition covering max_blocks_per_seq * 16 tokens or more means a single
+ * pass with no merge.  The online-softmax merge of partitions is exact
+ * ("vLLM-Ascend 原理", §四 "ATB 算子": softmax statistics kept online), so the
+ * choice changes only float32 rounding.
+ */
+int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads,
+                                    int32_t max_blocks_per_seq);
+
+/*
+ * pa_decode_workspace_size -- bytes of float32 partial results pa_decode needs
+ * for this shape and partition length (0 = default).  0 when every sequence
+ * fits one partition.  Layout (internal to the library): per (sequence,
+ * q head, partition) a running max, a running sum and head_dim accumulators.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_blocks_per_seq,
+                                int32_t partition_tokens);
+
+/*
+ * pa_decode -- paged decode attention ("vLLM-Ascend 原理", §2.4 step 3: the
+ * new position's q attends to the whole prefix, whose K/V are read block by
+ * block through the block table; under GQA only the kv heads are read).
+ *
+ *   out           [num_seqs][num_q_heads][head_dim]                (written)
+ *   q             [num_seqs][num_q_heads][head_dim]
+ *   k_cache,
+ *   v_cache       [num_blocks][block_size][num_kv_heads][head_dim]
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                 ceil(seq_lens[b] / block_size) are never read.
+ *   seq_lens      int32 [num_seqs]: cached tokens INCLUDING the current one
+ *                 (its k/v already written by pa_reshape_and_cache).  0 gives
+ *                 an all-zero output row; values above
+ *                 max_blocks_per_seq * block_size are clamped to it.
+ *   scale         softmax scale applied to q.k (natural-base softmax).
+ *   partition_tokens  split-KV partition length (multiple of 16), or 0 for
+ *                 pa_decode_default_partition().
+ *   workspace     device buffer of at least pa_decode_workspace_size() bytes
+ *                 (may be NULL when that size is 0), 16-byte aligned.
+ *
+ * q head h reads kv head h / (num_q_heads / num_kv_heads); num_q_heads must be
+ * a multiple of num_kv_heads, with at most 16 q heads per kv head.  Slots past
+ * seq_lens[b] inside the last block may hold any bits, NaN included; they
+ * never reach the output.
+ */
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                    float scale, pa_dtype dtype, int32_t partition_tokens, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pa_decode_partitions / pa_decode_merge -- the two phases of pa_decode, for
+ * callers that schedule or time them separately.  Same arguments and
+ * contract as pa_decode; the two calls must get identical arguments.
+ * pa_decode_partitions writes the final output of every sequence that fits
+ * one partition and the partial state of the others; pa_decode_merge
+ * combines the partial states (a no-op when nothing was split).
+ */
+pa_status pa_decode_partitions(void* out, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               const int32_t* seq_lens, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t max_blocks_per_seq,
+                               int64_t num_blocks, float scale, pa_dtype dtype,
+                               int32_t partition_tokens, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+pa_status pa_decode_merge(void* out, const int32_t* seq_lens, int32_t num_seqs,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t max_blocks_per_seq, pa_dtype dtype,
+                          int32_t partition_tokens, const void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pa_prefill_paged -- causal chunked prefill over the paged cache
+ * ("vLLM-Ascend 原理", §2.3 step 3: position i's q dots keys 0..i under a
+ * triangular mask, GQA heads sharing k/v; §2.4 on chunked prefill: a later
+ * chunk reads the KV earlier chunks wrote).
+ *
+ *   out              [num_tokens][num_q_heads][head_dim]           (written)
+ *   q                [num_tokens][num_q_heads][head_dim]; rows of sequence
+ *                    b are query_start_loc[b] .. query_start_loc[b+1]-1.
+ *   k_cache, v_cache as for pa_decode; the new tokens' k/v must already be
+ *                    in the cache (pa_reshape_and_cache first).
+ *   block_tables     int32 [num_seqs][max_blocks_per_seq]
+ *   ctx_lens         int32 [num_seqs]: tokens cached BEFORE this chunk.  Row i
+ *                    of sequence b sits at position ctx_lens[b] + i and sees
+ *                    keys 0 .. ctx_lens[b] + i.
+ *   query_start_loc  int32 [num_seqs + 1], non-decreasing, first entry 0,
+ *                    last entry <= num_tokens.
+ *   max_q_len        host-known upper bound of any sequence's row count
+ *                    (sizes the grid; rows past it are not computed).
+ *
+ * Rows owned by no sequence are left untouched.  head_dim must be 128; the
+ * q-head group (num_q_heads / num_kv_heads) must be 1, 2, 4 or 8.
+ */
+pa_status pa_prefill_paged(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* ctx_lens,
+                           const int32_t* query_start_loc, int32_t num_seqs,
+                           int64_t num_tokens, int32_t max_q_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                           pa_dtype dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,99 @@
+// Device helpers shared by the gfx950 kernels of libpa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace pa {
+
+constexpr int kBlockSize = 16;   // tokens per KV block
+constexpr int kWave = 64;        // CDNA wavefront width
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- conversion
+
+// low / high 16-bit element of a packed dword, widened to float32
+template <int DT>
+__device__ __forceinline__ float lo_to_f32(uint32_t w) {
+    if constexpr (DT == kF16) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+    } else {
+        return __uint_as_float(w << 16);
+    }
+}
+template <int DT>
+__device__ __forceinline__ float hi_to_f32(uint32_t w) {
+    if constexpr (DT == kF16) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    } else {
+        return __uint_as_float(w & 0xffff0000u);
+    }
+}
+
+// float32 -> 16-bit storage, round to nearest even
+template <int DT>
+__device__ __forceinline__ uint16_t f32_to_bits(float x) {
+    if constexpr (DT == kF16) {
+        return __builtin_bit_cast(uint16_t, (_Float16)x);
+    } else {
+        return __builtin_bit_cast(uint16_t, (__bf16)x);
+    }
+}
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return (uint32_t)f32_to_bits<DT>(a) | ((uint32_t)f32_to_bits<DT>(b) << 16);
+}
+
+// dot product of two packed pairs, accumulated in float32
+template <int DT>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    if constexpr (DT == kF16) {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b),
+                                      c, false);
+    } else {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                               __builtin_bit_cast(bf16x2_t, b), c, false);
+    }
+}
+
+// 8-element dot product of two 16-byte vectors
+template <int DT>
+__device__ __forceinline__ float dot8(const uint4& a, const uint4& b) {
+    float s = dot2<DT>(a.x, b.x, 0.f);
+    s = dot2<DT>(a.y, b.y, s);
+    s = dot2<DT>(a.z, b.z, s);
+    return dot2<DT>(a.w, b.w, s);
+}
+
+// ------------------------------------------------------------ DPP reductions
+// DPP control codes (GFX9 encoding)
+constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // reverse within each 8 lanes
+constexpr int kDppMirror = 0x140;     // reverse within each 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of N lanes (N = 8 or 16); every lane gets its group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+    x += dpp<kDppQuadXor1>(x);
+    x += dpp<kDppQuadXor2>(x);
+    x += dpp<kDppHalfMirror>(x);
+    if constexpr (N == 16) x += dpp<kDppMirror>(x);
+    return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+}  // namespace pa

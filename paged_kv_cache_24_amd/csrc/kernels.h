@@ -1,0 +1,70 @@
+// Launch interface between the C ABI layer (pa_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum : int { kF16 = 0, kBF16 = 1 };   // 16-bit element types
+
+struct ReshapeArgs {
+    const void* key;
+    const void* value;
+    void* k_cache;
+    void* v_cache;
+    const int64_t* slot_mapping;
+    int64_t num_tokens;
+    int64_t num_slots;       // num_blocks * block_size
+    int32_t row_vecs;        // 16-byte vectors per token row (kv_heads * head_dim / 8)
+};
+hipError_t launch_reshape_and_cache(const ReshapeArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+    void* out;
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* seq_lens;
+    float* ws_acc;           // [B][Hq][num_parts][D]
+    float2* ws_ml;           // [B][Hq][num_parts] = (max, sum), log2 domain
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t group;           // q heads per kv head
+    int32_t heads_per_wave;  // q heads one wave carries (1, 2, 4 or 8)
+    int32_t head_chunks;     // ceil(group / heads_per_wave)
+    int32_t head_dim;
+    int32_t max_blocks_per_seq;
+    int64_t num_blocks;
+    int32_t part_blocks;     // partition length in blocks
+    int32_t num_parts;       // partitions per sequence the grid covers
+    float scale_log2;        // softmax scale times log2(e)
+    int32_t dtype;
+};
+hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+    void* out;
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* ctx_lens;
+    const int32_t* query_start_loc;
+    int32_t num_seqs;
+    int64_t num_tokens;
+    int32_t max_q_len;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t group;
+    int32_t max_blocks_per_seq;
+    int64_t num_blocks;
+    float scale_log2;
+    int32_t dtype;
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace pa

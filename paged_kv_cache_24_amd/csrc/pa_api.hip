@@ -1,0 +1,291 @@
+// C ABI of libpa: host-side validation, kernel selection and launch.
+//
+// Every check runs before anything is enqueued ("fail early": unsupported
+// configurations are refused at the boundary, not deep inside a kernel --
+// "Hardware abstraction and portability", §九 on early capability checks).
+// No call reads device memory, synchronises or allocates, so each call is
+// capturable in a HIP graph; the decode workspace is owned by the caller.
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "pa.h"
+
+namespace {
+
+constexpr int32_t kNumCUs = 256;          // MI355X compute units
+constexpr int32_t kWavesPerCU = 16;       // resident decode waves per CU we plan for
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool supported_dtype(pa_dtype d) { return d == PA_F16 || d == PA_BF16; }
+
+int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+
+// heads one decode wave carries: the smallest of 1, 2, 4, 8 covering the group
+int32_t heads_per_wave(int32_t group) {
+    if (group <= 1) return 1;
+    if (group <= 2) return 2;
+    if (group <= 4) return 4;
+    return 8;
+}
+
+int32_t default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks_per_seq) {
+    // Aim for about four rounds of resident waves over the whole upper bound of
+    // work, so short and long sequences even out; partitions of 256..2048 tokens.
+    const int64_t tokens = (int64_t)num_seqs * num_kv_heads * max_blocks_per_seq * 16;
+    const int64_t target_items = (int64_t)kNumCUs * kWavesPerCU * 4;
+    int64_t p = 256;
+    while (p < 2048 && p * target_items < tokens) p <<= 1;
+    return (int32_t)p;
+}
+
+struct DecodeShape {
+    int32_t part_tokens;
+    int32_t num_parts;
+    size_t ws_bytes;
+};
+
+DecodeShape decode_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t max_blocks_per_seq, int32_t partition_tokens) {
+    DecodeShape s;
+    s.part_tokens = partition_tokens > 0
+                        ? partition_tokens
+                        : default_partition(num_seqs, num_kv_heads, max_blocks_per_seq);
+    const int32_t part_blocks = s.part_tokens / 16;
+    s.num_parts = max_blocks_per_seq <= part_blocks ? 1 : ceil_div(max_blocks_per_seq, part_blocks);
+    if (s.num_parts <= 1) {
+        s.ws_bytes = 0;
+    } else {
+        const size_t states = (size_t)num_seqs * num_q_heads * s.num_parts;
+        s.ws_bytes = states * ((size_t)head_dim * sizeof(float) + 2 * sizeof(float));
+    }
+    return s;
+}
+
+pa_status check_decode(const void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                       float scale, pa_dtype dtype, int32_t partition_tokens) {
+    if (!supported_dtype(dtype) || block_size != PA_BLOCK_SIZE || (head_dim != 64 && head_dim != 128))
+        return PA_ERR_UNSUPPORTED;
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+        num_blocks <= 0 || num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 16 ||
+        partition_tokens < 0 || partition_tokens % PA_BLOCK_SIZE != 0 || !isfinite(scale) ||
+        (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE > INT32_MAX)
+        return PA_ERR_SHAPE;
+    if (num_seqs == 0) return PA_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_NULL_PTR;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PA_ERR_ALIGNMENT;
+    return PA_OK;
+}
+
+pa::DecodeArgs decode_args(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                           pa_dtype dtype, const DecodeShape& shape, void* workspace) {
+    pa::DecodeArgs a;
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = num_q_heads / num_kv_heads;
+    a.heads_per_wave = heads_per_wave(a.group);
+    a.head_chunks = ceil_div(a.group, a.heads_per_wave);
+    a.head_dim = head_dim;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_blocks = num_blocks;
+    a.part_blocks = shape.part_tokens / PA_BLOCK_SIZE;
+    a.num_parts = shape.num_parts;
+    a.scale_log2 = scale * kLog2e;
+    a.dtype = dtype == PA_F16 ? pa::kF16 : pa::kBF16;
+    float* ws = static_cast<float*>(workspace);
+    const size_t states = (size_t)num_seqs * num_q_heads * shape.num_parts;
+    a.ws_acc = shape.ws_bytes ? ws : nullptr;
+    a.ws_ml = shape.ws_bytes ? reinterpret_cast<float2*>(ws + states * head_dim) : nullptr;
+    return a;
+}
+
+pa_status check_workspace(const DecodeShape& shape, const void* workspace, size_t workspace_bytes) {
+    if (shape.ws_bytes == 0) return PA_OK;
+    if (!workspace || workspace_bytes < shape.ws_bytes) return PA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return PA_ERR_ALIGNMENT;
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint64_t pa_kv_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_dim,
+                               int32_t dtype_bytes) {
+    if (layers <= 0 || kv_heads <= 0 || head_dim <= 0 || dtype_bytes <= 0) return 0;
+    return 2ull * (uint64_t)layers * (uint64_t)kv_heads * (uint64_t)head_dim * (uint64_t)dtype_bytes;
+}
+
+const char* pa_status_string(int32_t status) {
+    switch (status) {
+        case PA_OK: return "ok";
+        case PA_ERR_NULL_PTR: return "a required pointer is NULL";
+        case PA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size or dtype";
+        case PA_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+        case PA_ERR_WORKSPACE: return "decode workspace missing or too small";
+        case PA_ERR_HIP: return "the HIP runtime refused a kernel launch";
+        case PA_ERR_ALIGNMENT: return "a tensor or the workspace is not 16-byte aligned";
+        default: return "unknown status";
+    }
+}
+
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                               const int64_t* slot_mapping, int64_t num_tokens,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, pa_dtype dtype, hipStream_t stream) {
+    if (!supported_dtype(dtype) || block_size != PA_BLOCK_SIZE || (head_dim != 64 && head_dim != 128))
+        return PA_ERR_UNSUPPORTED;
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+    if (num_tokens == 0) return PA_OK;
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL_PTR;
+    if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PA_ERR_ALIGNMENT;
+    pa::ReshapeArgs a;
+    a.key = key;
+    a.value = value;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.slot_mapping = slot_mapping;
+    a.num_tokens = num_tokens;
+    a.num_slots = num_blocks * PA_BLOCK_SIZE;
+    a.row_vecs = num_kv_heads * head_dim / 8;
+    return pa::launch_reshape_and_cache(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads,
+                                    int32_t max_blocks_per_seq) {
+    if (num_seqs <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0) return 256;
+    return default_partition(num_seqs, num_kv_heads, max_blocks_per_seq);
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_blocks_per_seq,
+                                int32_t partition_tokens) {
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        max_blocks_per_seq <= 0 || partition_tokens < 0 || partition_tokens % PA_BLOCK_SIZE)
+        return 0;
+    return decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                        partition_tokens).ws_bytes;
+}
+
+pa_status pa_decode_partitions(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                               int64_t num_blocks, float scale, pa_dtype dtype,
+                               int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    pa_status st = check_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+                                num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_blocks_per_seq, num_blocks, scale, dtype, partition_tokens);
+    if (st != PA_OK || num_seqs == 0) return st;
+    const DecodeShape shape = decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                           max_blocks_per_seq, partition_tokens);
+    st = check_workspace(shape, workspace, workspace_bytes);
+    if (st != PA_OK) return st;
+    const pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, seq_lens,
+                                         num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                         max_blocks_per_seq, num_blocks, scale, dtype, shape,
+                                         workspace);
+    return pa::launch_decode_partitions(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_decode_merge(void* out, const int32_t* seq_lens, int32_t num_seqs,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t max_blocks_per_seq, pa_dtype dtype,
+                          int32_t partition_tokens, const void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    if (!supported_dtype(dtype) || block_size != PA_BLOCK_SIZE || (head_dim != 64 && head_dim != 128))
+        return PA_ERR_UNSUPPORTED;
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
+        num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 16 ||
+        partition_tokens < 0 || partition_tokens % PA_BLOCK_SIZE != 0)
+        return PA_ERR_SHAPE;
+    if (num_seqs == 0) return PA_OK;
+    if (!out || !seq_lens) return PA_ERR_NULL_PTR;
+    if (!aligned16(out)) return PA_ERR_ALIGNMENT;
+    const DecodeShape shape = decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                           max_blocks_per_seq, partition_tokens);
+    const pa_status st = check_workspace(shape, workspace, workspace_bytes);
+    if (st != PA_OK) return st;
+    if (shape.num_parts <= 1) return PA_OK;
+    const pa::DecodeArgs a = decode_args(out, nullptr, nullptr, nullptr, nullptr, seq_lens,
+                                         num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                         max_blocks_per_seq, 1, 1.f, dtype, shape,
+                                         const_cast<void*>(workspace));
+    return pa::launch_decode_merge(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                    float scale, pa_dtype dtype, int32_t partition_tokens, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+    pa_status st = pa_decode_partitions(out, q, k_cache, v_cache, block_tables, seq_lens,
+                                        num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                        block_size, max_blocks_per_seq, num_blocks, scale, dtype,
+                                        partition_tokens, workspace, workspace_bytes, stream);
+    if (st != PA_OK || num_seqs == 0) return st;
+    return pa_decode_merge(out, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                           block_size, max_blocks_per_seq, dtype, partition_tokens, workspace,
+                           workspace_bytes, stream);
+}
+
+pa_status pa_prefill_paged(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* ctx_lens,
+                           const int32_t* query_start_loc, int32_t num_seqs, int64_t num_tokens,
+                           int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                           int64_t num_blocks, float scale, pa_dtype dtype, hipStream_t stream) {
+    if (!supported_dtype(dtype) || block_size != PA_BLOCK_SIZE || head_dim != 128)
+        return PA_ERR_UNSUPPORTED;
+    if (num_seqs < 0 || num_tokens < 0 || max_q_len < 0 || num_q_heads <= 0 ||
+        num_kv_heads <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
+        num_q_heads % num_kv_heads != 0 || !isfinite(scale) ||
+        (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE > INT32_MAX)
+        return PA_ERR_SHAPE;
+    const int32_t group = num_q_heads / num_kv_heads;
+    if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || num_tokens == 0 || max_q_len == 0) return PA_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !ctx_lens || !query_start_loc)
+        return PA_ERR_NULL_PTR;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PA_ERR_ALIGNMENT;
+    pa::PrefillArgs a;
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.ctx_lens = ctx_lens;
+    a.query_start_loc = query_start_loc;
+    a.num_seqs = num_seqs;
+    a.num_tokens = num_tokens;
+    a.max_q_len = max_q_len;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = group;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_blocks = num_blocks;
+    a.scale_log2 = scale * kLog2e;
+    a.dtype = dtype == PA_F16 ? pa::kF16 : pa::kBF16;
+    return pa::launch_prefill(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // extern "C"

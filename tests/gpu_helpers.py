@@ -1,0 +1,100 @@
+"""Shared helpers of the GPU tests: move workloads to the device and back,
+compare with the oracle.  Tolerances: max-abs error 2e-3 for fp16 outputs and
+1e-2 for bf16 outputs against the float64 oracle."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+TOL = {"f16": 2e-3, "bf16": 1e-2}
+TORCH_DTYPE = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def require_gpu():
+    import pytest
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def dev_bits(arr: np.ndarray, dtype: str) -> torch.Tensor:
+    """uint16 bit patterns -> device tensor of the 16-bit float type."""
+    t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16))
+    return t.to("cuda").view(TORCH_DTYPE[dtype])
+
+
+def dev_int(arr: np.ndarray, dtype=torch.int32) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(dtype).to("cuda")
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().double().numpy()
+
+
+class DecodeOnGPU:
+    """A decode workload resident on the GPU."""
+
+    def __init__(self, case):
+        self.case = case
+        dt = case.dtype
+        self.q = dev_bits(case.q, dt)
+        self.k_cache = dev_bits(case.k_cache, dt)
+        self.v_cache = dev_bits(case.v_cache, dt)
+        self.key = dev_bits(case.key, dt)
+        self.value = dev_bits(case.value, dt)
+        self.slots = dev_int(case.slot_mapping, torch.int64)
+        self.tables = dev_int(case.block_tables)
+        self.lens = dev_int(case.seq_lens)
+        self.out = torch.empty_like(self.q)
+
+    def write(self):
+        import paged_kv_cache_24_amd as pa
+        pa.pa_reshape_and_cache(self.key, self.value, self.k_cache, self.v_cache, self.slots)
+
+    def decode(self, partition_tokens=0, out=None):
+        import paged_kv_cache_24_amd as pa
+        out = self.out if out is None else out
+        pa.pa_decode(out, self.q, self.k_cache, self.v_cache, self.tables, self.lens,
+                     self.case.scale, partition_tokens)
+        return out
+
+
+class PrefillOnGPU:
+    def __init__(self, case):
+        self.case = case
+        dt = case.dtype
+        self.q = dev_bits(case.q, dt)
+        self.k_cache = dev_bits(case.k_cache, dt)
+        self.v_cache = dev_bits(case.v_cache, dt)
+        self.key = dev_bits(case.key, dt)
+        self.value = dev_bits(case.value, dt)
+        self.slots = dev_int(case.slot_mapping, torch.int64)
+        self.tables = dev_int(case.block_tables)
+        self.ctx = dev_int(case.ctx_lens)
+        self.qsl = dev_int(case.query_start_loc)
+        self.out = torch.zeros_like(self.q)
+
+    def write(self):
+        import paged_kv_cache_24_amd as pa
+        pa.pa_reshape_and_cache(self.key, self.value, self.k_cache, self.v_cache, self.slots)
+
+    def prefill(self, out=None):
+        import paged_kv_cache_24_amd as pa
+        out = self.out if out is None else out
+        pa.pa_prefill_paged(out, self.q, self.k_cache, self.v_cache, self.tables, self.ctx,
+                            self.qsl, self.case.scale, max(self.case.max_q_len, 1))
+        return out
+
+
+def assert_close(got64: np.ndarray, ref64: np.ndarray, dtype: str, what: str = ""):
+    assert got64.shape == ref64.shape, (got64.shape, ref64.shape)
+    assert np.isfinite(got64).all(), f"{what}: non-finite output"
+    err = np.abs(got64 - ref64)
+    worst = float(err.max()) if err.size else 0.0
+    assert worst <= TOL[dtype], (
+        f"{what}: max-abs error {worst:.3e} > {TOL[dtype]} (max |ref| {np.abs(ref64).max():.3f})")
+    return worst

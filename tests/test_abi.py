@@ -1,0 +1,151 @@
+"""The C ABI library: it loads, exports every symbol pa.h declares, and
+refuses bad arguments on the host before touching the GPU (CPU only)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+LIB = os.path.join(ROOT, "paged_kv_cache_24_amd", "libpa.so")
+
+PA_OK, NULL, UNSUP, SHAPE, WS, HIP, ALIGN = 0, -1, -2, -3, -4, -5, -6
+F16, BF16 = 0, 1
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(pa_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libpa.so is not built (python -m paged_kv_cache_24_amd.build)")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_calls():
+    names = _declared()
+    for n in ["pa_reshape_and_cache", "pa_decode", "pa_prefill_paged", "pa_decode_workspace_size",
+              "pa_kv_bytes_per_token", "pa_status_string", "pa_decode_partitions",
+              "pa_decode_merge", "pa_decode_default_partition"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_kv_bytes_per_token(lib):
+    f = lib.pa_kv_bytes_per_token
+    f.restype = ctypes.c_uint64
+    assert f(32, 32, 128, 2) == 524288          # LLaMA-2-7B fp16, 512 KiB per token
+    assert f(32, 32, 128, 2) * 4096 == 2 ** 31  # 2 GiB per 4096-token sequence
+    assert f(0, 32, 128, 2) == 0
+
+
+def test_status_strings(lib):
+    f = lib.pa_status_string
+    f.restype = ctypes.c_char_p
+    for s in (PA_OK, NULL, UNSUP, SHAPE, WS, HIP, ALIGN, 7):
+        assert f(s)
+    assert f(PA_OK) == b"ok"
+
+
+P = ctypes.c_void_p
+FAKE = 0x10000   # 16-byte aligned, never dereferenced: validation fails first
+
+
+def _reshape(lib, key=FAKE, value=FAKE, kc=FAKE, vc=FAKE, slots=FAKE, n=4, hkv=2, d=128, bs=16,
+             nb=8, dt=F16):
+    f = lib.pa_reshape_and_cache
+    f.restype = ctypes.c_int32
+    f.argtypes = [P, P, P, P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int64, ctypes.c_int32, P]
+    return f(key, value, kc, vc, slots, n, hkv, d, bs, nb, dt, None)
+
+
+def test_reshape_rejects(lib):
+    assert _reshape(lib, key=None) == NULL
+    assert _reshape(lib, slots=None) == NULL
+    assert _reshape(lib, d=96) == UNSUP
+    assert _reshape(lib, bs=32) == UNSUP
+    assert _reshape(lib, dt=5) == UNSUP
+    assert _reshape(lib, n=-1) == SHAPE
+    assert _reshape(lib, hkv=0) == SHAPE
+    assert _reshape(lib, nb=0) == SHAPE
+    assert _reshape(lib, key=FAKE + 2) == ALIGN
+    assert _reshape(lib, n=0, key=None) == PA_OK    # nothing to do, nothing launched
+
+
+def _decode(lib, fn="pa_decode", out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, b=2, hq=8,
+            hkv=2, d=128, bs=16, mb=64, nb=128, scale=0.1, dt=BF16, part=0, ws=FAKE, wsb=1 << 30):
+    f = getattr(lib, fn)
+    f.restype = ctypes.c_int32
+    f.argtypes = [P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_int32,
+                  ctypes.c_int32, P, ctypes.c_size_t, P]
+    return f(out, q, kc, vc, bt, sl, b, hq, hkv, d, bs, mb, nb, scale, dt, part, ws, wsb, None)
+
+
+@pytest.mark.parametrize("fn", ["pa_decode", "pa_decode_partitions"])
+def test_decode_rejects(lib, fn):
+    assert _decode(lib, fn, q=None) == NULL
+    assert _decode(lib, fn, bt=None) == NULL
+    assert _decode(lib, fn, d=80) == UNSUP
+    assert _decode(lib, fn, bs=8) == UNSUP
+    assert _decode(lib, fn, dt=9) == UNSUP
+    assert _decode(lib, fn, hq=6, hkv=4) == SHAPE        # not a multiple
+    assert _decode(lib, fn, hq=34, hkv=2) == SHAPE       # 17 q heads per kv head
+    assert _decode(lib, fn, part=24) == SHAPE            # not a multiple of 16
+    assert _decode(lib, fn, part=-16) == SHAPE
+    assert _decode(lib, fn, scale=float("nan")) == SHAPE
+    assert _decode(lib, fn, mb=0) == SHAPE
+    assert _decode(lib, fn, out=FAKE + 8) == ALIGN
+    assert _decode(lib, fn, b=0, q=None) == PA_OK
+    # a split that needs a workspace
+    assert _decode(lib, fn, part=256, ws=None) == WS
+    assert _decode(lib, fn, part=256, wsb=16) == WS
+    assert _decode(lib, fn, part=256, ws=FAKE + 4) == ALIGN
+
+
+def test_workspace_size(lib):
+    f = lib.pa_decode_workspace_size
+    f.restype = ctypes.c_size_t
+    f.argtypes = [ctypes.c_int32] * 6
+    # single pass: no workspace
+    assert f(4, 8, 2, 128, 16, 256) == 0
+    # 64 blocks in partitions of 16 blocks: 4 partitions per (seq, q head)
+    assert f(2, 8, 2, 128, 64, 256) == 2 * 8 * 4 * (128 * 4 + 8)
+    assert f(2, 8, 2, 128, 64, 24) == 0                  # invalid partition length
+    g = lib.pa_decode_default_partition
+    g.restype = ctypes.c_int32
+    for args in [(64, 32, 256), (256, 8, 512), (8, 8, 4096), (4, 4, 7)]:
+        p = g(*args)
+        assert p % 16 == 0 and 256 <= p <= 2048
+
+
+def _prefill(lib, out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, qsl=FAKE, b=2, t=64, mq=40,
+             hq=32, hkv=8, d=128, bs=16, mb=16, nb=64, scale=0.1, dt=BF16):
+    f = lib.pa_prefill_paged
+    f.restype = ctypes.c_int32
+    f.argtypes = [P, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int64, ctypes.c_float, ctypes.c_int32, P]
+    return f(out, q, kc, vc, bt, cl, qsl, b, t, mq, hq, hkv, d, bs, mb, nb, scale, dt, None)
+
+
+def test_prefill_rejects(lib):
+    assert _prefill(lib, qsl=None) == NULL
+    assert _prefill(lib, cl=None) == NULL
+    assert _prefill(lib, d=64) == UNSUP
+    assert _prefill(lib, hq=24, hkv=8) == UNSUP          # 3 q heads per kv head
+    assert _prefill(lib, hq=30, hkv=8) == SHAPE
+    assert _prefill(lib, t=-1) == SHAPE
+    assert _prefill(lib, mq=-1) == SHAPE
+    assert _prefill(lib, q=FAKE + 2) == ALIGN
+    assert _prefill(lib, t=0, q=None) == PA_OK

@@ -1,0 +1,230 @@
+"""GPU parity of the cache write and paged decode against the float64 oracle,
+plus GPU-vs-GPU invariances.  Everything goes through the C ABI."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (DecodeOnGPU, TOL, assert_close, dev_bits, dev_int, host_bits, host_f64,
+                         require_gpu)
+from workloads import (decode_gqa_shared_prefix, decode_llama2_7b_layer, decode_long_context,
+                       decode_tiny, make_decode_case, normal_bits)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    import paged_kv_cache_24_amd  # noqa: F401  (fails loudly without libpa.so)
+
+
+def _oracle_after_write(c):
+    kc, vc = oracle.ref_reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache, c.slot_mapping)
+    return kc, vc, oracle.ref_decode(c.q, kc, vc, c.block_tables, c.seq_lens, c.scale, c.dtype)
+
+
+def _check_case(c, partitions=(0,)):
+    g = DecodeOnGPU(c)
+    g.write()
+    kc, vc, ref = _oracle_after_write(c)
+    np.testing.assert_array_equal(host_bits(g.k_cache), kc)   # the cache write is a bit copy
+    np.testing.assert_array_equal(host_bits(g.v_cache), vc)
+    errs = {}
+    for p in partitions:
+        out = g.decode(partition_tokens=p)
+        torch.cuda.synchronize()
+        errs[p] = assert_close(host_f64(out), ref, c.dtype, f"{c.name} partition={p}")
+    return errs
+
+
+def test_decode_tiny():
+    """Batch 4, lengths 1/17/33/100, fp16, D=64, last token through the cache write."""
+    c = decode_tiny()
+    _check_case(c, partitions=(0, 16, 32, 112))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (6, 2), (8, 2), (16, 2), (16, 1)])
+def test_decode_shapes(dtype, d, hq, hkv):
+    lens = [0, 1, 2, 15, 16, 17, 31, 33, 64, 100, 257, 300]
+    c = make_decode_case(name=f"shape-{dtype}-{d}-{hq}-{hkv}", seed=100 + hq + d, dtype=dtype,
+                         num_q_heads=hq, num_kv_heads=hkv, head_dim=d, seq_lens=lens,
+                         num_blocks=64, max_blocks_per_seq=20, scale=1 / math.sqrt(d),
+                         write_last=True)
+    _check_case(c, partitions=(0, 16, 48, 256, 320))
+
+
+def test_decode_llama_reduced():
+    c = decode_llama2_7b_layer(batch=6, max_len=1024, num_heads=32)
+    _check_case(c, partitions=(0, 256, 1024))
+
+
+def test_decode_gqa_shared_prefix_reduced():
+    c = decode_gqa_shared_prefix(batch=32, max_len=2048, min_len=128, group=16, prefix=1024)
+    _check_case(c, partitions=(0, 512, 2048))
+
+
+def test_decode_long_reduced():
+    c = decode_long_context(batch=2, seq_len=8192, num_blocks=1100)
+    _check_case(c, partitions=(0, 256, 2048))
+
+
+def test_one_token_context_returns_v():
+    """seq_len 1: the only weight is exp(0) = 1, so the output is v itself."""
+    for dtype in ("f16", "bf16"):
+        c = make_decode_case(name="one", seed=7, dtype=dtype, num_q_heads=8, num_kv_heads=2,
+                             head_dim=128, seq_lens=[1] * 5, num_blocks=8, max_blocks_per_seq=1,
+                             scale=0.1, write_last=True)
+        g = DecodeOnGPU(c)
+        g.write()
+        out = host_bits(g.decode())
+        for i in range(5):
+            for h in range(8):
+                np.testing.assert_array_equal(out[i, h], c.value[i, h // 4])
+
+
+def _needle_case(dtype, lens, part_tokens, seed=3):
+    """Every key is zero except one needle per sequence whose score is 128;
+    every other weight underflows to zero in float32, so the output must be
+    exactly the needle's value row (small integers)."""
+    b = len(lens)
+    hkv, hq, d = 2, 8, 128
+    mb = max((n + 15) // 16 for n in lens)
+    c = make_decode_case(name="needle", seed=seed, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv,
+                         head_dim=d, seq_lens=lens, num_blocks=b * mb + 3, max_blocks_per_seq=mb,
+                         scale=1.0, write_last=False)
+    one = {"f16": 0x3C00, "bf16": 0x3F80}[dtype]
+    c.q[:] = one                                   # q = all ones
+    rng = np.random.default_rng(seed)
+    needles = []
+    for s in range(b):
+        n = int(c.seq_lens[s])
+        pos = int(rng.integers(0, n))
+        needles.append(pos)
+        for p in range(n):
+            blk, off = int(c.block_tables[s, p // 16]), p % 16
+            c.k_cache[blk, off] = one if p == pos else 0
+            vals = rng.integers(-64, 64, (hkv, d)).astype(np.float32)
+            c.v_cache[blk, off] = (vals.astype(np.float16).view(np.uint16) if dtype == "f16"
+                                   else (vals.view(np.uint32) >> 16).astype(np.uint16))
+    return c, needles
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("part", [0, 16, 64])
+def test_needle_indexing_bit_exact(dtype, part):
+    lens = [1, 16, 17, 40, 77, 130, 257, 300]
+    c, needles = _needle_case(dtype, lens, part)
+    g = DecodeOnGPU(c)
+    out = host_bits(g.decode(partition_tokens=part))
+    for s, pos in enumerate(needles):
+        blk, off = int(c.block_tables[s, pos // 16]), pos % 16
+        for h in range(8):
+            np.testing.assert_array_equal(out[s, h], c.v_cache[blk, off, h // 4],
+                                          err_msg=f"seq {s} needle {pos} head {h}")
+
+
+def test_block_permutation_invariance_bit_exact():
+    c = decode_gqa_shared_prefix(batch=16, max_len=1024, min_len=16, group=4, prefix=256)
+    g = DecodeOnGPU(c)
+    base = host_bits(g.decode(partition_tokens=256)).copy()
+    perm = np.random.default_rng(8).permutation(c.num_blocks)
+    kc = np.empty_like(c.k_cache)
+    vc = np.empty_like(c.v_cache)
+    kc[perm] = c.k_cache
+    vc[perm] = c.v_cache
+    tables = np.where(c.block_tables >= 0, perm[np.maximum(c.block_tables, 0)], -1).astype(np.int32)
+    g.k_cache = dev_bits(kc, c.dtype)
+    g.v_cache = dev_bits(vc, c.dtype)
+    g.tables = dev_int(tables)
+    moved = host_bits(g.decode(partition_tokens=256))
+    np.testing.assert_array_equal(base, moved)
+
+
+def test_shared_prefix_equals_private_copies_bit_exact():
+    c = decode_gqa_shared_prefix(batch=16, max_len=1024, min_len=16, group=8, prefix=512)
+    g = DecodeOnGPU(c)
+    shared = host_bits(g.decode()).copy()
+    nb = int((c.block_tables >= 0).sum())
+    kc = np.empty((nb,) + c.k_cache.shape[1:], np.uint16)
+    vc = np.empty_like(kc)
+    tables = np.full_like(c.block_tables, -1)
+    cur = 0
+    for b in range(c.num_seqs):
+        for j, blk in enumerate(c.block_tables[b]):
+            if blk < 0:
+                break
+            kc[cur], vc[cur] = c.k_cache[blk], c.v_cache[blk]
+            tables[b, j] = cur
+            cur += 1
+    g.k_cache, g.v_cache, g.tables = dev_bits(kc, c.dtype), dev_bits(vc, c.dtype), dev_int(tables)
+    private = host_bits(g.decode())
+    np.testing.assert_array_equal(shared, private)
+
+
+def test_deterministic_repeat():
+    c = decode_llama2_7b_layer(batch=4, max_len=2048, num_heads=8)
+    g = DecodeOnGPU(c)
+    g.write()
+    a = host_bits(g.decode(partition_tokens=256)).copy()
+    for _ in range(3):
+        np.testing.assert_array_equal(a, host_bits(g.decode(partition_tokens=256)))
+
+
+def test_split_matches_unsplit():
+    c = decode_long_context(batch=2, seq_len=4096, num_blocks=600)
+    g = DecodeOnGPU(c)
+    single = host_f64(g.decode(partition_tokens=4096)).copy()
+    for p in (256, 512, 1024, 2048):
+        split = host_f64(g.decode(partition_tokens=p))
+        assert np.abs(split - single).max() <= TOL[c.dtype]
+
+
+def test_gqa_equals_duplicated_kv_heads():
+    """G q heads sharing one kv head == the same kv head duplicated G times."""
+    c = make_decode_case(name="gqa", seed=12, dtype="bf16", num_q_heads=8, num_kv_heads=2,
+                         head_dim=128, seq_lens=[5, 70, 200], num_blocks=24,
+                         max_blocks_per_seq=13, scale=0.09, write_last=False)
+    g = DecodeOnGPU(c)
+    grouped = host_f64(g.decode())
+    dup_k = np.repeat(c.k_cache, 4, axis=2)
+    dup_v = np.repeat(c.v_cache, 4, axis=2)
+    g.k_cache, g.v_cache = dev_bits(dup_k, c.dtype), dev_bits(dup_v, c.dtype)
+    mha = host_f64(g.decode())
+    assert np.abs(grouped - mha).max() <= TOL["bf16"]
+
+
+def test_empty_batch_and_zero_lengths():
+    import paged_kv_cache_24_amd as pa
+    c = make_decode_case(name="zeros", seed=13, dtype="f16", num_q_heads=4, num_kv_heads=4,
+                         head_dim=64, seq_lens=[0, 0, 3], num_blocks=4, max_blocks_per_seq=2,
+                         scale=0.125, write_last=False)
+    g = DecodeOnGPU(c)
+    g.out.fill_(1.0)
+    out = host_f64(g.decode())
+    assert (out[:2] == 0).all() and np.isfinite(out).all()
+    # batch of zero sequences: a no-op
+    empty_q = torch.empty((0, 4, 64), dtype=torch.float16, device="cuda")
+    pa.pa_decode(empty_q.clone(), empty_q, g.k_cache, g.v_cache, g.tables[:0], g.lens[:0], 0.125)
+
+
+def test_reshape_skips_padding_slots():
+    rng = np.random.default_rng(14)
+    nb, hkv, d = 6, 4, 128
+    kc = normal_bits(rng, (nb, 16, hkv, d), "bf16")
+    vc = normal_bits(rng, (nb, 16, hkv, d), "bf16")
+    key = normal_bits(rng, (7, hkv, d), "bf16")
+    val = normal_bits(rng, (7, hkv, d), "bf16")
+    slots = np.array([3, -1, 95, 17, -5, 40, 0], np.int64)
+    import paged_kv_cache_24_amd as pa
+    gk, gv = dev_bits(kc, "bf16"), dev_bits(vc, "bf16")
+    pa.pa_reshape_and_cache(dev_bits(key, "bf16"), dev_bits(val, "bf16"), gk, gv,
+                            dev_int(slots, torch.int64))
+    rk, rv = oracle.ref_reshape_and_cache(key, val, kc, vc, slots)
+    np.testing.assert_array_equal(host_bits(gk), rk)
+    np.testing.assert_array_equal(host_bits(gv), rv)

@@ -1,0 +1,98 @@
+"""GPU parity of chunked prefill (MFMA) against the float64 oracle, and
+GPU-side consistency with decode and with chunk splitting."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (DecodeOnGPU, PrefillOnGPU, TOL, assert_close, dev_int, host_bits,
+                         host_f64, require_gpu)
+from workloads import make_decode_case, make_prefill_case, prefill_chunked
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    import paged_kv_cache_24_amd  # noqa: F401
+
+
+def _run(c):
+    g = PrefillOnGPU(c)
+    g.write()
+    kc, vc = oracle.ref_reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache, c.slot_mapping)
+    np.testing.assert_array_equal(host_bits(g.k_cache), kc)
+    np.testing.assert_array_equal(host_bits(g.v_cache), vc)
+    out = host_f64(g.prefill())
+    ref = oracle.ref_prefill_paged(c.q, kc, vc, c.block_tables, c.ctx_lens, c.query_start_loc,
+                                   c.scale, c.dtype)
+    return g, out, ref
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (8, 2), (16, 2)])
+def test_prefill_shapes(dtype, hq, hkv):
+    q_lens = [0, 1, 17, 64, 130, 5, 33]
+    ctx = [3, 0, 40, 0, 100, 16, 250]
+    c = make_prefill_case(name=f"prefill-{dtype}-{hq}-{hkv}", seed=200 + hq, dtype=dtype,
+                          num_q_heads=hq, num_kv_heads=hkv, head_dim=128, q_lens=q_lens,
+                          ctx_lens=ctx, scale=1 / math.sqrt(128), extra_blocks=5)
+    _, out, ref = _run(c)
+    assert_close(out, ref, dtype, c.name)
+
+
+def test_prefill_chunked_reduced():
+    c = prefill_chunked(batch=4, new_tokens=600, max_ctx=700)
+    _, out, ref = _run(c)
+    assert_close(out, ref, "bf16", c.name)
+
+
+def test_prefill_rows_outside_sequences_untouched():
+    c = make_prefill_case(name="gap", seed=31, dtype="bf16", num_q_heads=8, num_kv_heads=2,
+                          head_dim=128, q_lens=[20, 9], ctx_lens=[5, 0], scale=0.1)
+    g = PrefillOnGPU(c)
+    g.write()
+    # the second sequence's rows are dropped from query_start_loc: they must stay untouched
+    g.qsl = dev_int(np.array([0, 20, 20], np.int32))
+    g.out.fill_(3.0)
+    out = host_f64(g.prefill())
+    assert (out[20:] == 3.0).all()
+
+
+def test_prefill_row_matches_decode():
+    """A prefill row at position p equals decode with seq_len p + 1."""
+    c = make_prefill_case(name="rowdec", seed=32, dtype="bf16", num_q_heads=16, num_kv_heads=4,
+                          head_dim=128, q_lens=[50, 7], ctx_lens=[90, 300], scale=0.08)
+    g, out, ref = _run(c)
+    assert_close(out, ref, "bf16", c.name)
+    for b, row in [(0, 0), (0, 49), (1, 6)]:
+        r = int(c.query_start_loc[b]) + row
+        q1 = g.q[r:r + 1].contiguous()
+        out1 = torch.empty_like(q1)
+        import paged_kv_cache_24_amd as pa
+        lens = dev_int(np.array([int(c.ctx_lens[b]) + row + 1], np.int32))
+        pa.pa_decode(out1, q1, g.k_cache, g.v_cache, g.tables[b:b + 1].contiguous(), lens, c.scale)
+        assert np.abs(host_f64(out1)[0] - out[r]).max() <= 2 * TOL["bf16"]
+
+
+def test_prefill_two_chunks_match_one():
+    """Chunk 2 reading chunk 1's KV from the cache gives the one-chunk result."""
+    c = make_prefill_case(name="chunks", seed=33, dtype="bf16", num_q_heads=8, num_kv_heads=2,
+                          head_dim=128, q_lens=[200], ctx_lens=[37], scale=0.1)
+    g, whole, ref = _run(c)
+    import paged_kv_cache_24_amd as pa
+    split = 77
+    out1 = torch.zeros_like(g.q[:split])
+    pa.pa_prefill_paged(out1, g.q[:split].contiguous(), g.k_cache, g.v_cache, g.tables, g.ctx,
+                        dev_int(np.array([0, split], np.int32)), c.scale, split)
+    out2 = torch.zeros_like(g.q[split:])
+    pa.pa_prefill_paged(out2, g.q[split:].contiguous(), g.k_cache, g.v_cache, g.tables,
+                        g.ctx + split, dev_int(np.array([0, 200 - split], np.int32)), c.scale,
+                        200 - split)
+    both = np.concatenate([host_f64(out1), host_f64(out2)])
+    assert_close(both, ref, "bf16", "two chunks")
+    assert np.abs(both - whole).max() <= TOL["bf16"]
