@@ -1,0 +1,380 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+Headline workload: one LLaMA-2-7B-shaped attention layer at decode -- batch
+64, 32 q = 32 kv heads, head_dim 128, fp16, block size 16, lengths uniform in
+[512, 4096] (seed 2), blocks scattered by a seeded permutation over a pool of
+16384 blocks.  One step = the cache write of the 64 new tokens followed by
+paged decode (partition kernel + merge kernel).  ``value`` is effective KV
+bandwidth: K+V bytes of all live tokens (each kv head's tile counted once)
+divided by the step time, inputs resident in HBM.
+
+Printed: one JSON line with the headline metric, a ``roofline`` object for
+the dominant kernel (the decode partition kernel, timed with HIP events on
+the stream it runs on), a ``cpu_baseline`` object (the float64 oracle on a
+bounded sample of the same workload, on this host's cores) and
+``secondary`` measurements of the other workloads (GQA + shared prefix,
+chunked prefill, long-context split-KV, tiny decode).
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--quick]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, TFLOP/s
+METRIC = "paged-decode effective KV GB/s (% of MI355X HBM peak); decode tokens/s"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_partition_traffic.json")
+DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_24_amd", "csrc", "decode.hip")
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU budget of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for scaling HBM counters)")
+    return ap.parse_args()
+
+
+def _dev(bits, dtype):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda")
+    return t.view(torch.float16 if dtype == "f16" else torch.bfloat16)
+
+
+def _i(a, dt=None):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dt or torch.int32).to("cuda")
+
+
+class _Timer:
+    """Per-kernel HIP events on the current stream, summed over steps."""
+
+    def __init__(self, names):
+        self.names = names
+        self.events = []
+
+    def step(self):
+        import torch
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(self.names) + 1)]
+        self.events.append(ev)
+        return ev
+
+    def mean_ms(self):
+        out = {}
+        for i, n in enumerate(self.names):
+            out[n] = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in self.events]))
+        return out
+
+
+# ------------------------------------------------------------------ decode workloads
+
+class DecodeRun:
+    def __init__(self, case, partition_tokens=0):
+        import torch
+        import paged_kv_cache_24_amd as pa
+        self.pa = pa
+        self.c = case
+        self.q = _dev(case.q, case.dtype)
+        self.kc = _dev(case.k_cache, case.dtype)
+        self.vc = _dev(case.v_cache, case.dtype)
+        self.key = _dev(case.key, case.dtype)
+        self.value = _dev(case.value, case.dtype)
+        self.slots = _i(case.slot_mapping, torch.int64)
+        self.tables = _i(case.block_tables)
+        self.lens = _i(case.seq_lens)
+        self.out = torch.empty_like(self.q)
+        self.part = partition_tokens or pa.pa_decode_default_partition(
+            case.num_seqs, case.num_kv_heads, case.max_blocks_per_seq)
+        need = pa.pa_decode_workspace_size(case.num_seqs, case.num_q_heads, case.num_kv_heads,
+                                           case.head_dim, case.max_blocks_per_seq, self.part)
+        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        self.has_write = len(case.slot_mapping) > 0
+
+    def step(self, ev=None):
+        pa, c = self.pa, self.c
+        if ev is not None:
+            ev[0].record()
+        if self.has_write:
+            pa.pa_reshape_and_cache(self.key, self.value, self.kc, self.vc, self.slots)
+        if ev is not None:
+            ev[1].record()
+        pa.pa_decode_partitions(self.out, self.q, self.kc, self.vc, self.tables, self.lens, c.scale,
+                                self.ws, self.part)
+        if ev is not None:
+            ev[2].record()
+        pa.pa_decode_merge(self.out, self.lens, c.num_kv_heads, c.max_blocks_per_seq, self.ws,
+                           self.part)
+        if ev is not None:
+            ev[3].record()
+
+    def timed(self, steps, warmup):
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        timer = _Timer(["write", "partitions", "merge"])
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step(timer.step())
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+        return wall_ms, timer.mean_ms()
+
+    def algorithmic_bytes(self):
+        """Bytes any implementation of the decode partition kernel must move:
+        K+V of the live tokens, q, the block-table entries read, the output."""
+        c = self.c
+        lens = c.seq_lens.astype(np.int64)
+        elt = 2
+        kv = int(lens.sum()) * 2 * c.num_kv_heads * c.head_dim * elt
+        q = c.num_seqs * c.num_q_heads * c.head_dim * elt
+        table = int(((lens + 15) // 16).sum()) * 4
+        out = c.num_seqs * c.num_q_heads * c.head_dim * elt
+        return kv, kv + q + table + out
+
+    def free(self):
+        for k in ("q", "kc", "vc", "key", "value", "out", "ws"):
+            setattr(self, k, None)
+
+
+def _traffic_if_current():
+    """HBM bytes per launch of the partition kernel from committed rocprofv3
+    counter runs, valid only if decode.hip is unchanged since they were taken."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            prof = json.load(f)
+        src = hashlib.sha256(open(DECODE_SOURCE, "rb").read()).hexdigest()
+        if prof.get("decode_hip_sha256") != src:
+            return None
+        return prof.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def _cpu_baseline(case, budget_s):
+    """The float64 oracle on a bounded sample: sequences in order until the
+    time budget is spent, after the same cache write."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    kc, vc = oracle.ref_reshape_and_cache(case.key, case.value, case.k_cache, case.v_cache,
+                                          case.slot_mapping)
+    done, kv_bytes = 0, 0
+    t0 = time.perf_counter()
+    for b in range(case.num_seqs):
+        n = int(case.seq_lens[b])
+        oracle.ref_decode_one(case.q[b], kc, vc, case.block_tables[b], n, case.scale, case.dtype)
+        done += 1
+        kv_bytes += n * 2 * case.num_kv_heads * case.head_dim * 2
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 oracle decode of the first {done} of {case.num_seqs} sequences "
+                      f"({kv_bytes / 1e9:.3f} GB of K+V) in {dt:.1f} s; "
+                      f"{done / dt:.2f} sequences/s"}
+
+
+def _secondary_decode(builder, name, steps, warmup, note=None):
+    import torch
+    case = builder()
+    run = DecodeRun(case)
+    wall, per = run.timed(steps, warmup)
+    kv, algo = run.algorithmic_bytes()
+    dec_ms = per["partitions"] + per["merge"]
+    res = {"workload": name, "ms_per_step": round(wall, 4), "decode_ms": round(dec_ms, 4),
+           "partition_kernel_ms": round(per["partitions"], 4), "merge_ms": round(per["merge"], 4),
+           "partition_tokens": run.part, "kv_bytes": kv,
+           "kv_GBs": round(kv / (dec_ms * 1e-3) / 1e9, 1),
+           "pct_hbm_peak": round(100 * kv / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+           "tokens_per_s": round(case.num_seqs / (dec_ms * 1e-3), 1)}
+    if run.has_write:
+        res["write_ms"] = round(per["write"], 4)
+    if note:
+        res.update(note(case))
+    run.free()
+    del run, case
+    torch.cuda.empty_cache()
+    return res
+
+
+def _shared_prefix_note(case):
+    used = np.unique(case.block_tables[case.block_tables >= 0])
+    unique_tokens = 0
+    lens = case.seq_lens.astype(np.int64)
+    # unique bytes: each physical block read by any sequence, counting its live rows once
+    rows = {}
+    for b in range(case.num_seqs):
+        n = int(lens[b])
+        for j in range((n + 15) // 16):
+            blk = int(case.block_tables[b, j])
+            rows[blk] = max(rows.get(blk, 0), min(16, n - 16 * j))
+    unique_tokens = sum(rows.values())
+    unique = unique_tokens * 2 * case.num_kv_heads * case.head_dim * 2
+    return {"unique_kv_bytes": unique, "blocks_used": int(len(used)),
+            "note": "kv_GBs counts logical bytes (shared blocks once per sequence); "
+                    "the shared prefixes may be served from the 256 MB Infinity Cache"}
+
+
+def _secondary_prefill(steps, warmup):
+    import torch
+    import paged_kv_cache_24_amd as pa
+    from workloads import prefill_chunked
+    c = prefill_chunked()
+    q = _dev(c.q, c.dtype)
+    kc, vc = _dev(c.k_cache, c.dtype), _dev(c.v_cache, c.dtype)
+    key, value = _dev(c.key, c.dtype), _dev(c.value, c.dtype)
+    slots = _i(c.slot_mapping, torch.int64)
+    tables, ctx, qsl = _i(c.block_tables), _i(c.ctx_lens), _i(c.query_start_loc)
+    out = torch.empty_like(q)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        pa.pa_reshape_and_cache(key, value, kc, vc, slots)
+        if ev is not None:
+            ev[1].record()
+        pa.pa_prefill_paged(out, q, kc, vc, tables, ctx, qsl, c.scale, c.max_q_len)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    timer = _Timer(["write", "prefill"])
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(timer.step())
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per = timer.mean_ms()
+    L = c.q_lens.astype(np.int64)
+    ctxl = c.ctx_lens.astype(np.int64)
+    pairs = int((L * ctxl + L * (L + 1) // 2).sum())
+    flops = 4 * c.num_q_heads * c.head_dim * pairs
+    write_bytes = 2 * 2 * c.num_tokens * c.num_kv_heads * c.head_dim * 2   # read + write, K and V
+    res = {"workload": "prefill_chunked", "ms_per_step": round(wall, 4),
+           "write_ms": round(per["write"], 4),
+           "write_GBs": round(write_bytes / (per["write"] * 1e-3) / 1e9, 1),
+           "write_pct_hbm_peak": round(100 * write_bytes / (per["write"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+           "prefill_ms": round(per["prefill"], 4), "prefill_flops": flops,
+           "prefill_TFLOPs": round(flops / (per["prefill"] * 1e-3) / 1e12, 1),
+           "prefill_pct_mfma_peak": round(100 * flops / (per["prefill"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 1),
+           "new_tokens": c.num_tokens, "unmasked_pairs_per_head": pairs}
+    del q, kc, vc, key, value, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def _copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n}))
+
+
+def main():
+    args = _args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence or kv head with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        _copy_calibration()
+        return
+    import paged_kv_cache_24_amd  # noqa: F401  (raises if libpa.so is missing)
+    from workloads import (decode_gqa_shared_prefix, decode_llama2_7b_layer,
+                           decode_long_context, decode_tiny)
+
+    t_gen = time.perf_counter()
+    case = decode_llama2_7b_layer()
+    gen_s = time.perf_counter() - t_gen
+    run = DecodeRun(case)
+    wall_ms, per = run.timed(args.steps, args.warmup)
+    kv, algo = run.algorithmic_bytes()
+    part_ms = per["partitions"]
+    achieved = algo / (part_ms * 1e-3) / 1e9
+    traffic = _traffic_if_current()
+    value = kv / (wall_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded N(0,1) q/k/v, random block placement)",
+        "config": {"workload": "decode_llama2_7b_layer", "batch": case.num_seqs,
+                   "q_heads": case.num_q_heads, "kv_heads": case.num_kv_heads,
+                   "head_dim": case.head_dim, "block_size": 16,
+                   "seq_lens": "uniform int [512, 4096], seed 2",
+                   "num_blocks": case.num_blocks, "kv_bytes": kv,
+                   "partition_tokens": run.part,
+                   "step": "cache write of 64 tokens + paged decode (partitions + merge)"},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+        "tokens_per_s": round(case.num_seqs / (wall_ms * 1e-3), 1),
+        "kernel_ms": {k: round(v, 4) for k, v in per.items()},
+        "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel<f16,128,1>",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_launch": algo,
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = _cpu_baseline(case, args.cpu_seconds)
+    run.free()
+    del run, case
+    torch.cuda.empty_cache()
+
+    if not args.quick:
+        sec = []
+        s2, w2 = max(5, args.steps // 5), max(2, args.warmup // 2)
+        sec.append(_secondary_decode(decode_gqa_shared_prefix, "decode_gqa_shared_prefix", s2, w2,
+                                     _shared_prefix_note))
+        sec.append(_secondary_prefill(s2, w2))
+        sec.append(_secondary_decode(decode_long_context, "decode_long_context", s2, w2))
+        sec.append(_secondary_decode(decode_tiny, "decode_tiny", s2, w2))
+        result["secondary"] = sec
+    result["input_generation_s"] = round(gen_s, 1)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
