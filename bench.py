@@ -103,7 +103,7 @@ class DecodeRun:
         self.lens = _i(case.seq_lens)
         self.out = torch.empty_like(self.q)
         self.part = partition_tokens or pa.pa_decode_default_partition(
-            case.num_seqs, case.num_kv_heads, case.max_blocks_per_seq)
+            case.num_q_heads, case.num_kv_heads, case.head_dim, case.max_blocks_per_seq)
         need = pa.pa_decode_workspace_size(case.num_seqs, case.num_q_heads, case.num_kv_heads,
                                            case.head_dim, case.max_blocks_per_seq, self.part)
         self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")

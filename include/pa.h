@@ -104,13 +104,15 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
 
 /*
  * pa_decode_default_partition -- the split-KV partition length, in tokens, that
- * pa_decode uses when given partition_tokens == 0 (a multiple of 16).  A
- * partition covering max_blocks_per_seq * 16 tokens or more means a single
+ * pa_decode uses when given partition_tokens == 0 (a power of two >= 256).  It
+ * depends only on host-known sizes: about max_blocks_per_seq * 16 / 8, capped
+ * at 512 tokens when at most 2 q heads share a kv head and at 2048 otherwise.
+ * A partition covering max_blocks_per_seq * 16 tokens or more means a single
  * pass with no merge.  The online-softmax merge of partitions is exact
  * ("vLLM-Ascend 原理", §四 "ATB 算子": softmax statistics kept online), so the
  * choice changes only float32 rounding.
  */
-int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads,
+int32_t pa_decode_default_partition(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                     int32_t max_blocks_per_seq);
 
 /*

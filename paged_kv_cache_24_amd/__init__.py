@@ -41,7 +41,7 @@ _SIGS = {
     "pa_kv_bytes_per_token": (ctypes.c_uint64, [_i32, _i32, _i32, _i32]),
     "pa_status_string": (ctypes.c_char_p, [_i32]),
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i32, _vp]),
-    "pa_decode_default_partition": (_i32, [_i32, _i32, _i32]),
+    "pa_decode_default_partition": (_i32, [_i32, _i32, _i32, _i32]),
     "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
                          _f32, _i32, _i32, _vp, _sz, _vp]),
@@ -128,8 +128,10 @@ def pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None
         hkv, d, bs, nb, _kv_dtype(k_cache), _stream(stream)))
 
 
-def pa_decode_default_partition(num_seqs: int, num_kv_heads: int, max_blocks_per_seq: int) -> int:
-    return int(lib.pa_decode_default_partition(num_seqs, num_kv_heads, max_blocks_per_seq))
+def pa_decode_default_partition(num_q_heads: int, num_kv_heads: int, head_dim: int,
+                                max_blocks_per_seq: int) -> int:
+    return int(lib.pa_decode_default_partition(num_q_heads, num_kv_heads, head_dim,
+                                               max_blocks_per_seq))
 
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,

@@ -94,8 +94,8 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
         const int64_t off = (int64_t)(ok ? pb : 0) * kBlockSize * row_stride;
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
-            kr[i] = *reinterpret_cast<const uint4*>(kbase + off + (int64_t)i * RPW * row_stride);
-            vr[i] = *reinterpret_cast<const uint4*>(vbase + off + (int64_t)i * RPW * row_stride);
+            kr[i] = load_stream(kbase + off + (int64_t)i * RPW * row_stride);
+            vr[i] = load_stream(vbase + off + (int64_t)i * RPW * row_stride);
         }
         return ok;
     };
@@ -156,16 +156,21 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
         }
     };
 
+    // three register buffers: while one block is computed, the next two are in flight
     if (j0 < j1) {
-        uint4 ka[TPL], va[TPL], kb[TPL], vb[TPL];
+        uint4 ka[TPL], va[TPL], kb[TPL], vb[TPL], kc[TPL], vc[TPL];
         bool oka = load(j0, ka, va);
-        bool okb = false;
-        for (int j = j0; j < j1; j += 2) {
-            if (j + 1 < j1) okb = load(j + 1, kb, vb);
+        bool okb = false, okc = false;
+        if (j0 + 1 < j1) okb = load(j0 + 1, kb, vb);
+        for (int j = j0; j < j1; j += 3) {
+            if (j + 2 < j1) okc = load(j + 2, kc, vc);
             process(ka, va, oka, j);
             if (j + 1 >= j1) break;
-            if (j + 2 < j1) oka = load(j + 2, ka, va);
+            if (j + 3 < j1) oka = load(j + 3, ka, va);
             process(kb, vb, okb, j + 1);
+            if (j + 2 >= j1) break;
+            if (j + 4 < j1) okb = load(j + 4, kb, vb);
+            process(kc, vc, okc, j + 2);
         }
     }
 
@@ -216,13 +221,224 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// GQA decode (head_dim 128, 3..16 q heads per kv head): both products on
+// matrix cores.
+//
+// With G q heads sharing a kv head, one block's S = K Q^T ([16 tokens x 128] .
+// [128 x G]) and O += P V ([G x 16] . [16 x 128]) are real small contractions
+// shared by G heads; on the vector ALUs their cost grows with G until it, not
+// HBM, bounds the kernel (measured: the vector version reached 68% of HBM
+// peak on 8 heads per kv head and did not move with faster loads).  Here:
+//   S^T tile  = MFMA 16x16x32 x 4:  A = K rows (lane l: token pi(l%16),
+//               elements 32*kk + 8*(l/16) .. +8), B = Q^T (lane l: head l%16);
+//               pi(m) = 4*(m%4) + m/4, so lane l receives the scores of
+//               tokens 4*i + l/16 (i = 0..3) for head l%16;
+//   O^T      += MFMA 16x16x16 x 8:  A = V^T (16 elements of head_dim x the 16
+//               tokens), B = P^T -- exactly the probabilities lane l already
+//               holds, in the same token order, so they never move.
+// V^T comes from a per-wave LDS copy of the V tile: each lane writes its
+// row-coalesced 16-byte chunks, and ds_read_b64_tr_b16 returns the transposed
+// 4 x 16-bit fragments in one instruction per 16 columns.  Softmax state is
+// per head (lanes l, l^16, l^32, l^48 share it), so the rescale of O^T, whose
+// column is also the head, stays in-lane.
+// ---------------------------------------------------------------------------
+typedef __bf16 dbf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 dbf16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 df16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 df16x4_t __attribute__((ext_vector_type(4)));
+typedef float df32x4_t __attribute__((ext_vector_type(4)));
+typedef short ds16x4_t __attribute__((ext_vector_type(4)));
+
+template <int DT>
+__device__ __forceinline__ df32x4_t mfma_16x16x32(const uint4& a, const uint4& b, df32x4_t c) {
+    if constexpr (DT == kF16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(df16x8_t, a),
+                                                      __builtin_bit_cast(df16x8_t, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(dbf16x8_t, a),
+                                                       __builtin_bit_cast(dbf16x8_t, b), c, 0, 0, 0);
+    }
+}
+template <int DT>
+__device__ __forceinline__ df32x4_t mfma_16x16x16(const uint2& a, const uint2& b, df32x4_t c) {
+    if constexpr (DT == kF16) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(df16x4_t, a),
+                                                     __builtin_bit_cast(df16x4_t, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(dbf16x4_t, a),
+                                                         __builtin_bit_cast(dbf16x4_t, b), c, 0, 0, 0);
+    }
+}
+
+constexpr int kVRow = 144;   // LDS row stride of the V tile (elements): 288 B staggers banks
+
+template <int DT>
+__global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
+    constexpr int D = 128;
+    __shared__ __attribute__((aligned(16))) uint16_t vlds[4][kBlockSize * kVRow];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uniform(threadIdx.x >> 6);
+    const int lr = lane & 15;    // MFMA column = q head; V column chunk; V^T row
+    const int lg = lane >> 4;    // token group: tokens 4*i + lg of each block
+    uint16_t* vt = vlds[wave];
+
+    const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.head_chunks;
+    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+    if (item >= units * a.num_parts) return;
+    const int part = (int)(item / units);
+    int64_t u = item - (int64_t)part * units;
+    const int hc = (int)(u % a.head_chunks);
+    u /= a.head_chunks;
+    const int g = (int)(u % a.num_kv_heads);
+    const int b = (int)(u / a.num_kv_heads);
+
+    const int max_tokens = a.max_blocks_per_seq * kBlockSize;
+    int n = a.seq_lens[b];
+    n = n < 0 ? 0 : (n > max_tokens ? max_tokens : n);
+    const int nblk = (n + kBlockSize - 1) / kBlockSize;
+    const int nparts = nblk <= a.part_blocks ? 1 : (nblk + a.part_blocks - 1) / a.part_blocks;
+    if (part >= nparts) return;
+    const int j0 = part * a.part_blocks;
+    const int j1 = min(nblk, j0 + a.part_blocks);
+    const int hcount = min(16, a.group - hc * 16);
+    const int64_t q_row0 = (int64_t)b * a.num_q_heads + (int64_t)g * a.group + hc * 16;
+    const bool head_live = lr < hcount;
+
+    uint4 qf[4];
+    {
+        const uint16_t* q = static_cast<const uint16_t*>(a.q) + (q_row0 + (head_live ? lr : 0)) * D + 8 * lg;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            qf[kk] = head_live ? *reinterpret_cast<const uint4*>(q + 32 * kk) : make_uint4(0, 0, 0, 0);
+    }
+
+    float m = -INFINITY;   // running max of head lr (same in lanes l, l^16, l^32, l^48)
+    float l = 0.f;         // this lane's share of the running sum
+    df32x4_t o[8];         // O^T: lane holds elements 16*mt + 4*lg + i of head lr
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) o[mt] = df32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t row_stride = (int64_t)a.num_kv_heads * D;
+    const int tk = (lr & 3) * 4 + (lr >> 2);
+    const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache) + (int64_t)g * D + 8 * lg +
+                            (int64_t)tk * row_stride;
+    const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + (int64_t)g * D + 8 * lr +
+                            (int64_t)lg * row_stride;
+    const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
+    const float cs = a.scale_log2;
+    // transposed-read address of this lane: row 4*(lr/4) + lg, column 4*(lr%4) (+16 per tile)
+    const uint16_t* vtr = vt + (4 * (lr >> 2) + lg) * kVRow + 4 * (lr & 3);
+
+    auto load = [&](int j, uint4 (&kr)[4], uint4 (&vr)[4]) -> bool {
+        const int pb = table[j];
+        const bool ok = pb >= 0 && (int64_t)pb < a.num_blocks;
+        const int64_t off = (int64_t)(ok ? pb : 0) * kBlockSize * row_stride;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            kr[i] = *reinterpret_cast<const uint4*>(kbase + off + 32 * i);
+            vr[i] = *reinterpret_cast<const uint4*>(vbase + off + (int64_t)4 * i * row_stride);
+        }
+        return ok;
+    };
+
+    auto process = [&](const uint4 (&kr)[4], const uint4 (&vr)[4], bool ok, int j) {
+        df32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) sacc = mfma_16x16x32<DT>(kr[kk], qf[kk], sacc);
+        const bool full = ok && (j + 1) * kBlockSize <= n;
+        bool valid[4];
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            valid[i] = full || (ok && (j * kBlockSize + 4 * i + lg < n));
+            x[i] = valid[i] ? sacc[i] * cs : -INFINITY;
+        }
+        float mb = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        mb = fmaxf(mb, __shfl_xor(mb, 16));
+        mb = fmaxf(mb, __shfl_xor(mb, 32));
+        const float mn = fmaxf(m, mb);
+        const float mu = mn == -INFINITY ? 0.f : mn;
+        const float alpha = fast_exp2(m - mu);
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - mu);
+        l = fmaf(l, alpha, (p[0] + p[1]) + (p[2] + p[3]));
+        m = mn;
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) o[mt] *= alpha;
+        }
+        // V tile to LDS, rows past the sequence end as zeros (MFMA would turn 0 x NaN into NaN)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint4*>(vt + (4 * i + lg) * kVRow + 8 * lr) =
+                valid[i] ? vr[i] : make_uint4(0, 0, 0, 0);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        uint2 pb;
+        pb.x = pack2<DT>(p[0], p[1]);
+        pb.y = pack2<DT>(p[2], p[3]);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            const ds16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (ds16x4_t __attribute__((address_space(3)))*)(vtr + 16 * mt));
+            o[mt] = mfma_16x16x16<DT>(__builtin_bit_cast(uint2, va), pb, o[mt]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    if (j0 < j1) {
+        uint4 ka[4], va[4], kb[4], vb[4];
+        bool oka = load(j0, ka, va);
+        bool okb = false;
+        for (int j = j0; j < j1; j += 2) {
+            if (j + 1 < j1) okb = load(j + 1, kb, vb);
+            process(ka, va, oka, j);
+            if (j + 1 >= j1) break;
+            if (j + 2 < j1) oka = load(j + 2, ka, va);
+            process(kb, vb, okb, j + 1);
+        }
+    }
+
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+    if (!head_live) return;
+    if (nparts == 1) {
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        uint16_t* dst = static_cast<uint16_t*>(a.out) + (q_row0 + lr) * D + 4 * lg;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            uint2 w;
+            w.x = pack2<DT>(o[mt][0] * inv, o[mt][1] * inv);
+            w.y = pack2<DT>(o[mt][2] * inv, o[mt][3] * inv);
+            *reinterpret_cast<uint2*>(dst + 16 * mt) = w;
+        }
+    } else {
+        const int64_t idx = (q_row0 + lr) * a.num_parts + part;
+        float* dst = a.ws_acc + idx * D + 4 * lg;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+            *reinterpret_cast<float4*>(dst + 16 * mt) = make_float4(o[mt][0], o[mt][1], o[mt][2], o[mt][3]);
+        if (lg == 0) a.ws_ml[idx] = make_float2(m, lt);
+    }
+}
+
 // Combine the partition states of one (sequence, q head):
 // out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p with M = max_p m_p.
+// One workgroup per (sequence, q head); its 256 threads split the partitions
+// (max pass) and then the (partition, element) pairs (sum pass).
 template <int DT, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-    constexpr int EPL = D / kWave;   // output elements per lane
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t item = (int64_t)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
+    constexpr int GROUPS = 256 / D;   // partition groups in the sum pass
+    __shared__ float red[4];
+    __shared__ float part_num[GROUPS][D];
+    __shared__ float part_den[GROUPS];
+    const int tid = threadIdx.x;
+    const int64_t item = blockIdx.x;
     if (item >= (int64_t)a.num_seqs * a.num_q_heads) return;
     const int b = (int)(item / a.num_q_heads);
 
@@ -235,26 +451,36 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 
     const int64_t base = item * a.num_parts;
     float big = -INFINITY;
-    for (int i = 0; i < nparts; ++i) big = fmaxf(big, a.ws_ml[base + i].x);
-    float den = 0.f;
-    float num[EPL];
+    for (int i = tid; i < nparts; i += 256) big = fmaxf(big, a.ws_ml[base + i].x);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) num[e] = 0.f;
-    for (int i = 0; i < nparts; ++i) {
+    for (int off = 32; off > 0; off >>= 1) big = fmaxf(big, __shfl_xor(big, off));
+    if ((tid & 63) == 0) red[tid >> 6] = big;
+    __syncthreads();
+    big = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+    const int d = tid % D;
+    const int grp = tid / D;
+    float num = 0.f, den = 0.f;
+#pragma unroll 4
+    for (int i = grp; i < nparts; i += GROUPS) {
         const float2 ml = a.ws_ml[base + i];
         const float w = ml.x == -INFINITY ? 0.f : fast_exp2(ml.x - big);
         den = fmaf(w, ml.y, den);
-        const float* src = a.ws_acc + (base + i) * D + lane * EPL;
+        num = fmaf(w, a.ws_acc[(base + i) * D + d], num);
+    }
+    part_num[grp][d] = num;
+    if (d == 0) part_den[grp] = den;
+    __syncthreads();
+    if (tid >= D) return;
+    num = 0.f;
+    den = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, src[e], num[e]);
+    for (int g2 = 0; g2 < GROUPS; ++g2) {
+        num += part_num[g2][tid];
+        den += part_den[g2];
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
-    uint16_t* dst = static_cast<uint16_t*>(a.out) + item * D + lane * EPL;
-    if constexpr (EPL == 2) {
-        *reinterpret_cast<uint32_t*>(dst) = pack2<DT>(num[0] * inv, num[1] * inv);
-    } else {
-        *dst = f32_to_bits<DT>(num[0] * inv);
-    }
+    static_cast<uint16_t*>(a.out)[item * D + tid] = f32_to_bits<DT>(num * inv);
 }
 
 template <int DT, int D>
@@ -275,6 +501,11 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t s) {
     const int64_t wgs = (items + 3) / 4;
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs);
+    if (a.gqa_mfma) {
+        if (a.dtype == kF16) hipLaunchKernelGGL((decode_gqa_kernel<kF16>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((decode_gqa_kernel<kBF16>), grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     if (a.dtype == kF16) {
         return a.head_dim == 128 ? launch_partitions_d<kF16, 128>(a, s, grid)
                                  : launch_partitions_d<kF16, 64>(a, s, grid);
@@ -286,9 +517,8 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {
     const int64_t items = (int64_t)a.num_seqs * a.num_q_heads;
     if (items == 0 || a.num_parts <= 1) return hipSuccess;
-    const int64_t wgs = (items + 3) / 4;
-    if (wgs > 0x7fffffff) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)wgs);
+    if (items > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)items);
     if (a.dtype == kF16) {
         if (a.head_dim == 128) hipLaunchKernelGGL((decode_merge_kernel<kF16, 128>), grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL((decode_merge_kernel<kF16, 64>), grid, dim3(256), 0, s, a);

@@ -33,7 +33,8 @@ struct DecodeArgs {
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t group;           // q heads per kv head
-    int32_t heads_per_wave;  // q heads one wave carries (1, 2, 4 or 8)
+    int32_t gqa_mfma;        // 1: QK^T on matrix cores (head_dim 128, group 3..16)
+    int32_t heads_per_wave;  // q heads one wave carries (1, 2, 4, 8; 16 with gqa_mfma)
     int32_t head_chunks;     // ceil(group / heads_per_wave)
     int32_t head_dim;
     int32_t max_blocks_per_seq;

@@ -13,8 +13,6 @@
 
 namespace {
 
-constexpr int32_t kNumCUs = 256;          // MI355X compute units
-constexpr int32_t kWavesPerCU = 16;       // resident decode waves per CU we plan for
 constexpr float kLog2e = 1.4426950408889634f;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -30,14 +28,23 @@ int32_t heads_per_wave(int32_t group) {
     return 8;
 }
 
-int32_t default_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks_per_seq) {
-    // Aim for about four rounds of resident waves over the whole upper bound of
-    // work, so short and long sequences even out; partitions of 256..2048 tokens.
-    const int64_t tokens = (int64_t)num_seqs * num_kv_heads * max_blocks_per_seq * 16;
-    const int64_t target_items = (int64_t)kNumCUs * kWavesPerCU * 4;
-    int64_t p = 256;
-    while (p < 2048 && p * target_items < tokens) p <<= 1;
-    return (int32_t)p;
+// decode runs on matrix cores when 3+ q heads share a kv head at head_dim 128
+bool uses_gqa_kernel(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
+    return head_dim == 128 && num_kv_heads > 0 && num_q_heads / num_kv_heads >= 3;
+}
+
+int32_t default_partition(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t max_blocks_per_seq) {
+    // About eight partitions for the longest sequence the tables allow, within
+    // [256, cap] tokens.  Measured on MI355X: the vector-ALU kernel (group <= 2)
+    // is fastest at 512-token partitions (more items even out the length mix),
+    // the matrix-core kernel at 1024-2048 (it keeps fewer waves resident, so
+    // longer items hide its start-up latency better).
+    const int32_t cap = uses_gqa_kernel(num_q_heads, num_kv_heads, head_dim) ? 2048 : 512;
+    const int64_t want = (int64_t)max_blocks_per_seq * 16 / 8;
+    int32_t p = 256;
+    while (p < cap && p < want) p <<= 1;
+    return p;
 }
 
 struct DecodeShape {
@@ -51,7 +58,7 @@ DecodeShape decode_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_h
     DecodeShape s;
     s.part_tokens = partition_tokens > 0
                         ? partition_tokens
-                        : default_partition(num_seqs, num_kv_heads, max_blocks_per_seq);
+                        : default_partition(num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq);
     const int32_t part_blocks = s.part_tokens / 16;
     s.num_parts = max_blocks_per_seq <= part_blocks ? 1 : ceil_div(max_blocks_per_seq, part_blocks);
     if (s.num_parts <= 1) {
@@ -98,7 +105,9 @@ pa::DecodeArgs decode_args(void* out, const void* q, const void* k_cache, const 
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = num_kv_heads;
     a.group = num_q_heads / num_kv_heads;
-    a.heads_per_wave = heads_per_wave(a.group);
+    // 3 or more q heads per kv head make QK^T and PV real contractions: matrix cores
+    a.gqa_mfma = uses_gqa_kernel(num_q_heads, num_kv_heads, head_dim);
+    a.heads_per_wave = a.gqa_mfma ? 16 : heads_per_wave(a.group);
     a.head_chunks = ceil_div(a.group, a.heads_per_wave);
     a.head_dim = head_dim;
     a.max_blocks_per_seq = max_blocks_per_seq;
@@ -167,10 +176,10 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
     return pa::launch_reshape_and_cache(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_kv_heads,
+int32_t pa_decode_default_partition(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                     int32_t max_blocks_per_seq) {
-    if (num_seqs <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0) return 256;
-    return default_partition(num_seqs, num_kv_heads, max_blocks_per_seq);
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0) return 256;
+    return default_partition(num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq);
 }
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

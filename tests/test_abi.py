@@ -124,7 +124,12 @@ def test_workspace_size(lib):
     assert f(2, 8, 2, 128, 64, 24) == 0                  # invalid partition length
     g = lib.pa_decode_default_partition
     g.restype = ctypes.c_int32
-    for args in [(64, 32, 256), (256, 8, 512), (8, 8, 4096), (4, 4, 7)]:
+    g.argtypes = [ctypes.c_int32] * 4
+    assert g(32, 32, 128, 256) == 512       # vector-ALU path, 4096-token tables
+    assert g(32, 8, 128, 512) == 1024       # matrix-core path, 8192-token tables
+    assert g(64, 8, 128, 4096) == 2048      # matrix-core path, capped
+    assert g(4, 4, 64, 7) == 256            # short tables: the floor
+    for args in [(32, 32, 128, 256), (32, 8, 128, 512), (64, 8, 128, 4096), (4, 4, 64, 7)]:
         p = g(*args)
         assert p % 16 == 0 and 256 <= p <= 2048
 
