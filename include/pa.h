@@ -140,7 +140,8 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  *                 (its k/v already written by pa_reshape_and_cache).  0 gives
  *                 an all-zero output row; values above
  *                 max_blocks_per_seq * block_size are clamped to it.
- *   scale         softmax scale applied to q.k (natural-base softmax).
+ *   scale         softmax scale applied to q.k (natural-base softmax); must be
+ *                 positive and finite.
  *   partition_tokens  split-KV partition length (multiple of 16), or 0 for
  *                 pa_decode_default_partition().
  *   workspace     device buffer of at least pa_decode_workspace_size() bytes
@@ -199,6 +200,7 @@ pa_status pa_decode_merge(void* out, const int32_t* seq_lens, int32_t num_seqs,
  *                    last entry <= num_tokens.
  *   max_q_len        host-known upper bound of any sequence's row count
  *                    (sizes the grid; rows past it are not computed).
+ *   scale            softmax scale, positive and finite.
  *
  * Rows owned by no sequence are left untouched.  head_dim must be 128; the
  * q-head group (num_q_heads / num_kv_heads) must be 1, 2, 4 or 8.

@@ -43,9 +43,19 @@ __device__ __forceinline__ uint16_t f32_to_bits(float x) {
         return __builtin_bit_cast(uint16_t, (__bf16)x);
     }
 }
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// two float32 -> one packed dword of 16-bit values (a in the low half), RNE;
+// a single v_cvt_pk_{bf16,f16}_f32
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-    return (uint32_t)f32_to_bits<DT>(a) | ((uint32_t)f32_to_bits<DT>(b) << 16);
+    const f32x2_t v = {a, b};
+    if constexpr (DT == kF16) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+    } else {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    }
 }
 
 // dot product of two packed pairs, accumulated in float32

@@ -79,7 +79,7 @@ pa_status check_decode(const void* out, const void* q, const void* k_cache, cons
         return PA_ERR_UNSUPPORTED;
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
         num_blocks <= 0 || num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 16 ||
-        partition_tokens < 0 || partition_tokens % PA_BLOCK_SIZE != 0 || !isfinite(scale) ||
+        partition_tokens < 0 || partition_tokens % PA_BLOCK_SIZE != 0 || !(scale > 0.f) || !isfinite(scale) ||
         (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE > INT32_MAX)
         return PA_ERR_SHAPE;
     if (num_seqs == 0) return PA_OK;
@@ -266,7 +266,7 @@ pa_status pa_prefill_paged(void* out, const void* q, const void* k_cache, const 
         return PA_ERR_UNSUPPORTED;
     if (num_seqs < 0 || num_tokens < 0 || max_q_len < 0 || num_q_heads <= 0 ||
         num_kv_heads <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
-        num_q_heads % num_kv_heads != 0 || !isfinite(scale) ||
+        num_q_heads % num_kv_heads != 0 || !(scale > 0.f) || !isfinite(scale) ||
         (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE > INT32_MAX)
         return PA_ERR_SHAPE;
     const int32_t group = num_q_heads / num_kv_heads;

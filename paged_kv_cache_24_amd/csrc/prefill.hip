@@ -8,9 +8,11 @@
 // merged with an online softmax, as fused attention kernels do
 // ("vLLM-Ascend 原理", §2.3 step 3 and §四 "ATB 算子").
 //
-// Mapping.  One workgroup (4 waves) owns 128 query rows of one (sequence, kv
+// Mapping.  One workgroup (8 waves) owns 128 query rows of one (sequence, kv
 // head): 128/G positions times the G q heads that share the kv head, so every
-// K/V tile is staged in LDS once for all of them.  Each wave owns 32 rows.
+// K/V tile is staged in LDS once for all of them.  Each wave owns 16 rows, which
+// keeps it at ~128 VGPRs so four waves share each SIMD (two workgroups per CU):
+// the softmax of one wave overlaps the matrix work of the others.
 // For each 64-key tile:
 //   S^T[key][row] = K[key][:] . Q[row][:]     (MFMA 16x16x32: A = K from LDS,
 //                                              B = Q kept in registers)
@@ -18,10 +20,15 @@
 //   l, l^16, l^32, l^48, so the row max/sum is an in-lane reduction plus two
 //   cross-lane steps;
 //   O^T[d][row] += V^T[d][key] . P^T[key][row] (MFMA 16x16x32: B = P^T straight
-//   from the softmax registers, A = V^T read from a transposed LDS copy).
+//   from the softmax registers, A = V^T fragments produced by ds_read_b64_tr_b16
+//   from the row-major V tile in LDS).
 // Working on the transposed products keeps each row's statistics in the lanes
 // that own the row in both products, so no shuffle of the probabilities or
-// of the rescale factors is needed.
+// of the rescale factors is needed.  The next tile's K/V rows are loaded into
+// registers while the current tile is computed and stored to the other LDS
+// buffer afterwards (one barrier per tile).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -44,19 +51,23 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, 
 
 constexpr int kPD = 128;            // head_dim
 constexpr int kKT = 64;             // keys per tile
-constexpr int kRows = 128;          // query rows per workgroup
-constexpr int kKRow = kPD + 8;      // LDS K row stride (elements): 272 bytes, staggers banks
-constexpr int kVRow = kKT + 4;      // LDS V^T row stride (elements): 136 bytes
+constexpr int kRows = 128;          // query rows per workgroup (8 waves x 16)
+constexpr int kVRow = kPD + 16;     // LDS V row stride (elements): 288 bytes, conflict-free transposed reads
+
+typedef short ps16x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kKRow = kPD + 8;      // LDS K row stride (elements): 272 bytes, so the 16 rows of
+                                    // an MFMA A fragment start 4 banks apart (conflict-free)
 
 template <int DT, int G>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     constexpr int P = kRows / G;    // positions per workgroup
     __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kKT * kKRow];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kPD * kVRow];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kKT * kVRow];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = uniform(tid >> 6);
+    const int wave = uniform(tid >> 6);   // 0..7: rows 16*wave .. 16*wave+15
     const int lr = lane & 15;       // row (or column) within a 16-wide MFMA tile
     const int lg = lane >> 4;       // lane group 0..3
 
@@ -85,189 +96,185 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
     const int64_t row_stride = (int64_t)a.num_kv_heads * kPD;
 
-    // ---- this lane's two query rows (one per 16-row tile) and their Q^T fragments
-    uint4 qf[2][4];
-    int qpos[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const int rho = wave * 32 + nt * 16 + lr;
+    // ---- this lane's query row and its Q^T fragments
+    uint4 qf[4];
+    const int rho = wave * 16 + lr;
+    const int qpos = ctx + pos0 + rho / G;
+    {
         const int pos = pos0 + rho / G;
-        qpos[nt] = ctx + pos;
         const bool ok = pos < L;
         const uint16_t* src = static_cast<const uint16_t*>(a.q) +
-                              ((int64_t)(row0 + (ok ? pos : 0)) * a.num_q_heads + g * G + rho % G) * kPD +
-                              8 * lg;
+                              ((row0 + (ok ? pos : 0)) * a.num_q_heads + g * G + rho % G) * kPD + 8 * lg;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-            qf[nt][kk] = ok ? *reinterpret_cast<const uint4*>(src + 32 * kk) : make_uint4(0, 0, 0, 0);
+            qf[kk] = ok ? *reinterpret_cast<const uint4*>(src + 32 * kk) : make_uint4(0, 0, 0, 0);
     }
-    const int wave_pos_lo = pos0 + (wave * 32) / G;
-    const int wave_pos_hi = min(pos_end - 1, pos0 + (wave * 32 + 31) / G);
+    const int wave_pos_lo = pos0 + (wave * 16) / G;
+    const int wave_pos_hi = min(pos_end - 1, pos0 + (wave * 16 + 15) / G);
     const bool wave_live = wave_pos_lo < pos_end;
     const int wave_q_lo = ctx + wave_pos_lo;
     const int wave_q_hi = ctx + wave_pos_hi;
 
-    f32x4_t o[8][2];
+    f32x4_t o[8];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) o[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m[2] = {-INFINITY, -INFINITY};
-    float lsum[2] = {0.f, 0.f};   // this lane's share of the row sums
+    for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY;
+    float lsum = 0.f;   // this lane's share of the row sum
     const float cs = a.scale_log2;
 
-    // ---- K/V tile staging: thread t moves 16-byte chunk (t % 16) of key rows t/16 + 16 i
+    // ---- K/V tile staging: thread t moves 16-byte chunk (t % 16) of key rows t/16 and
+    // t/16 + 32.  Rows 32 i .. 32 i + 31 of tile tt are blocks 4 tt + 2 i and 4 tt + 2 i + 1.
     const int ck = tid & 15;
-    auto load_tile = [&](int t, uint4 (&gk)[4], uint4 (&gv)[4]) {
+    const int krow = tid >> 4;      // 0..31
+    auto load_tile = [&](int tt, uint4 (&gk)[2], uint4 (&gv)[2]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = t * kKT + (tid >> 4) + 16 * i;
-            int pb = -1;
-            if (key < n_keys && key < max_keys) pb = table[key / kBlockSize];
-            if (pb >= 0 && (int64_t)pb < a.num_blocks) {
-                const int64_t off = ((int64_t)pb * kBlockSize + key % kBlockSize) * row_stride +
-                                    (int64_t)g * kPD + 8 * ck;
-                gk[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_cache) + off);
-                gv[i] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_cache) + off);
-            } else {
-                gk[i] = make_uint4(0, 0, 0, 0);   // past the sequence: zeros, never NaN
-                gv[i] = make_uint4(0, 0, 0, 0);
-            }
+        for (int i = 0; i < 2; ++i) {
+            const int blk_a = tt * 4 + 2 * i;   // uniform
+            const int pba = blk_a * kBlockSize < n_keys ? table[blk_a] : -1;
+            const int pbb = (blk_a + 1) * kBlockSize < n_keys ? table[blk_a + 1] : -1;
+            const int pb = krow < 16 ? pba : pbb;
+            const int key = tt * kKT + 32 * i + krow;
+            const bool ok = pb >= 0 && (int64_t)pb < a.num_blocks;
+            const bool valid = ok && key < n_keys;
+            // an invalid row still reads (in bounds) block 0, then is replaced by zeros:
+            // keys past the sequence end must be zeros in LDS, never NaN
+            const int64_t off = ((int64_t)(ok ? pb : 0) * kBlockSize + (krow & 15)) * row_stride +
+                                (int64_t)g * kPD + 8 * ck;
+            const uint4 k4 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_cache) + off);
+            const uint4 v4 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_cache) + off);
+            gk[i] = valid ? k4 : make_uint4(0, 0, 0, 0);
+            gv[i] = valid ? v4 : make_uint4(0, 0, 0, 0);
         }
     };
-    auto store_tile = [&](int buf, const uint4 (&gk)[4], const uint4 (&gv)[4]) {
+    auto store_tile = [&](int buf, const uint4 (&gk)[2], const uint4 (&gv)[2]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int kr = (tid >> 4) + 16 * i;
+        for (int i = 0; i < 2; ++i) {
+            const int kr = krow + 32 * i;
             *reinterpret_cast<uint4*>(&lds_k[buf][kr * kKRow + 8 * ck]) = gk[i];
-            const uint32_t w[4] = {gv[i].x, gv[i].y, gv[i].z, gv[i].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                lds_v[buf][(8 * ck + 2 * e) * kVRow + kr] = (uint16_t)(w[e] & 0xffffu);
-                lds_v[buf][(8 * ck + 2 * e + 1) * kVRow + kr] = (uint16_t)(w[e] >> 16);
-            }
+            *reinterpret_cast<uint4*>(&lds_v[buf][kr * kVRow + 8 * ck]) = gv[i];
         }
     };
+    // transposed V^T fragment address of this lane: row 4*lg + lr/4 (+16), column 4*(lr%4) (+16 mt)
+    const int v_tr_off = (4 * lg + (lr >> 2)) * kVRow + 4 * (lr & 3);
 
-    uint4 gk[4], gv[4];
+    uint4 gk[2], gv[2];
     load_tile(0, gk, gv);
+    store_tile(0, gk, gv);
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
-        store_tile(buf, gk, gv);
-        __syncthreads();
-        if (t + 1 < ntiles) load_tile(t + 1, gk, gv);
+        __syncthreads();   // tile t is in LDS; everybody is done with tile t-1's buffer
+        const bool more = t + 1 < ntiles;
+        if (more) load_tile(t + 1, gk, gv);   // in flight while this tile is computed
         const int k0 = t * kKT;
-        if (!wave_live || k0 > wave_q_hi) continue;   // every key of the tile is in this wave's future
-
-        // ---- S^T = K Q^T for 64 keys x 32 rows
-        f32x4_t s[4][2];
+        if (wave_live && k0 <= wave_q_hi) {
+            // ---- S^T = K Q^T for 64 keys x 16 rows
+            f32x4_t s[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < 4; ++mt) s[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) s[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const uint4 ka = *reinterpret_cast<const uint4*>(
-                    &lds_k[buf][(16 * mt + lr) * kKRow + 32 * kk + 8 * lg]);
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) s[mt][nt] = mfma16x16x32<DT>(ka, qf[nt][kk], s[mt][nt]);
-            }
-        }
-
-        // ---- causal mask (select) and online softmax, per row
-        const bool diag = k0 + kKT - 1 > wave_q_lo;
-        uint4 pb[2][2];   // P^T fragments [key chunk][row tile]
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            float x[4][4];
-            float mb = -INFINITY;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float v = s[mt][nt][i] * cs;
-                    if (diag) {
-                        const int key = k0 + 16 * mt + 4 * lg + i;
-                        v = key > qpos[nt] ? -INFINITY : v;
-                    }
-                    x[mt][i] = v;
-                    mb = fmaxf(mb, v);
+                for (int mt = 0; mt < 4; ++mt) {
+                    const uint4 ka = *reinterpret_cast<const uint4*>(
+                        &lds_k[buf][(16 * mt + lr) * kKRow + 32 * kk + 8 * lg]);
+                    s[mt] = mfma16x16x32<DT>(ka, qf[kk], s[mt]);
                 }
+            }
+
+            // ---- online softmax of this lane's row (P overwrites S).  The scale is folded
+            // into the exponent (scale > 0, so the max commutes with it).  The running max
+            // is raised only when a tile beats it by more than 2^8: otherwise the old max
+            // is kept, p <= 256 (exact algebra, no overflow in the 16-bit P), and the
+            // rescale of O^T is skipped for the whole wave.
+            if (k0 + kKT - 1 > wave_q_lo) {   // diagonal tile: causal mask by select
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (k0 + 16 * mt + 4 * lg + i > qpos) s[mt][i] = -INFINITY;
+            }
+            float mb = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+#pragma unroll
+            for (int mt = 1; mt < 4; ++mt)
+                mb = fmaxf(mb, fmaxf(fmaxf(s[mt][0], s[mt][1]), fmaxf(s[mt][2], s[mt][3])));
             mb = fmaxf(mb, __shfl_xor(mb, 16));
             mb = fmaxf(mb, __shfl_xor(mb, 32));
-            const float mn = fmaxf(m[nt], mb);
-            const float mu = mn == -INFINITY ? 0.f : mn;
-            const float alpha = fast_exp2(m[nt] - mu);
-            m[nt] = mn;
+            const float mbs = mb * cs;
+            const bool raise = mbs > m + 8.f;   // also true on the first live tile
+            const float mn = raise ? mbs : m;
+            if (__any(raise)) {
+                const float alpha = raise ? fast_exp2(m - mn) : 1.f;   // exp2(-inf) = 0
+                lsum *= alpha;
+#pragma unroll
+                for (int mt = 0; mt < 8; ++mt) o[mt] *= alpha;
+            }
+            m = mn;
+            const float nmu = mn == -INFINITY ? 0.f : -mn;
             float ps = 0.f;
-            float p[4][4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    p[mt][i] = fast_exp2(x[mt][i] - mu);
-                    ps += p[mt][i];
+                    const float pv = fast_exp2(fmaf(s[mt][i], cs, nmu));
+                    s[mt][i] = pv;
+                    ps += pv;
                 }
-            lsum[nt] = fmaf(lsum[nt], alpha, ps);
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt) o[mt][nt] *= alpha;
+            lsum += ps;
             // key slot 8*lg + i <-> key 32*kc + 4*lg + i; slot 8*lg + 4 + i <-> key 32*kc + 16 + 4*lg + i
+            uint4 pb[2];
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
-                pb[kc][nt].x = pack2<DT>(p[2 * kc][0], p[2 * kc][1]);
-                pb[kc][nt].y = pack2<DT>(p[2 * kc][2], p[2 * kc][3]);
-                pb[kc][nt].z = pack2<DT>(p[2 * kc + 1][0], p[2 * kc + 1][1]);
-                pb[kc][nt].w = pack2<DT>(p[2 * kc + 1][2], p[2 * kc + 1][3]);
+                pb[kc].x = pack2<DT>(s[2 * kc][0], s[2 * kc][1]);
+                pb[kc].y = pack2<DT>(s[2 * kc][2], s[2 * kc][3]);
+                pb[kc].z = pack2<DT>(s[2 * kc + 1][0], s[2 * kc + 1][1]);
+                pb[kc].w = pack2<DT>(s[2 * kc + 1][2], s[2 * kc + 1][3]);
             }
-        }
 
-        // ---- O^T += V^T P^T
+            // ---- O^T += V^T P^T; V^T fragments by transposed LDS reads of the row-major V tile
+            const uint16_t* vbuf = lds_v[buf] + v_tr_off;
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
+            for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                const uint16_t* vrow = &lds_v[buf][(16 * mt + lr) * kVRow + 32 * kc + 4 * lg];
-                const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-                const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-                const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) o[mt][nt] = mfma16x16x32<DT>(va, pb[kc][nt], o[mt][nt]);
+                for (int mt = 0; mt < 8; ++mt) {
+                    const ps16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (ps16x4_t __attribute__((address_space(3)))*)(vbuf + 32 * kc * kVRow + 16 * mt));
+                    const ps16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (ps16x4_t __attribute__((address_space(3)))*)(vbuf + (32 * kc + 16) * kVRow + 16 * mt));
+                    const uint2 l2 = __builtin_bit_cast(uint2, lo);
+                    const uint2 h2 = __builtin_bit_cast(uint2, hi);
+                    o[mt] = mfma16x16x32<DT>(make_uint4(l2.x, l2.y, h2.x, h2.y), pb[kc], o[mt]);
+                }
             }
         }
+        if (more) store_tile(buf ^ 1, gk, gv);
     }
 
     if (!wave_live) return;
-    // ---- epilogue: full row sums, normalise, store rows that exist
+    // ---- epilogue: full row sum, normalise, store the row if it exists
+    float l = lsum;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int pos = pos0 + rho / G;
+    if (pos >= L) return;
+    uint16_t* dst = static_cast<uint16_t*>(a.out) +
+                    ((row0 + pos) * a.num_q_heads + g * G + rho % G) * kPD + 4 * lg;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        float l = lsum[nt];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        const int rho = wave * 32 + nt * 16 + lr;
-        const int pos = pos0 + rho / G;
-        if (pos >= L) continue;
-        uint16_t* dst = static_cast<uint16_t*>(a.out) +
-                        ((int64_t)(row0 + pos) * a.num_q_heads + g * G + rho % G) * kPD + 4 * lg;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            uint2 w;
-            w.x = pack2<DT>(o[mt][nt][0] * inv, o[mt][nt][1] * inv);
-            w.y = pack2<DT>(o[mt][nt][2] * inv, o[mt][nt][3] * inv);
-            *reinterpret_cast<uint2*>(dst + 16 * mt) = w;
-        }
+    for (int mt = 0; mt < 8; ++mt) {
+        uint2 w;
+        w.x = pack2<DT>(o[mt][0] * inv, o[mt][1] * inv);
+        w.y = pack2<DT>(o[mt][2] * inv, o[mt][3] * inv);
+        *reinterpret_cast<uint2*>(dst + 16 * mt) = w;
     }
 }
 
 template <int DT>
 static void launch_prefill_g(const PrefillArgs& a, hipStream_t s, dim3 grid) {
     switch (a.group) {
-        case 1: hipLaunchKernelGGL((prefill_kernel<DT, 1>), grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<DT, 2>), grid, dim3(256), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((prefill_kernel<DT, 4>), grid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((prefill_kernel<DT, 8>), grid, dim3(256), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((prefill_kernel<DT, 1>), grid, dim3(512), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<DT, 2>), grid, dim3(512), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((prefill_kernel<DT, 4>), grid, dim3(512), 0, s, a); break;
+        default: hipLaunchKernelGGL((prefill_kernel<DT, 8>), grid, dim3(512), 0, s, a); break;
     }
 }
 

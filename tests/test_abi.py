@@ -104,6 +104,8 @@ def test_decode_rejects(lib, fn):
     assert _decode(lib, fn, part=24) == SHAPE            # not a multiple of 16
     assert _decode(lib, fn, part=-16) == SHAPE
     assert _decode(lib, fn, scale=float("nan")) == SHAPE
+    assert _decode(lib, fn, scale=0.0) == SHAPE
+    assert _decode(lib, fn, scale=-0.1) == SHAPE
     assert _decode(lib, fn, mb=0) == SHAPE
     assert _decode(lib, fn, out=FAKE + 8) == ALIGN
     assert _decode(lib, fn, b=0, q=None) == PA_OK
@@ -152,5 +154,7 @@ def test_prefill_rejects(lib):
     assert _prefill(lib, hq=30, hkv=8) == SHAPE
     assert _prefill(lib, t=-1) == SHAPE
     assert _prefill(lib, mq=-1) == SHAPE
+    assert _prefill(lib, scale=0.0) == SHAPE
+    assert _prefill(lib, scale=float("inf")) == SHAPE
     assert _prefill(lib, q=FAKE + 2) == ALIGN
     assert _prefill(lib, t=0, q=None) == PA_OK
