@@ -108,6 +108,11 @@ class DecodeRun:
                                            case.head_dim, case.max_blocks_per_seq, self.part)
         self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
         self.has_write = len(case.slot_mapping) > 0
+        # the streaming hint is a promise that no physical block is read twice in the
+        # call; a block manager knows it from its reference counts, here from the tables
+        used = case.block_tables[case.block_tables >= 0]
+        self.shared_blocks = len(np.unique(used)) < len(used)
+        self.flags = 0 if self.shared_blocks else pa.PA_DECODE_STREAM_KV
 
     def step(self, ev=None):
         pa, c = self.pa, self.c
@@ -118,7 +123,7 @@ class DecodeRun:
         if ev is not None:
             ev[1].record()
         pa.pa_decode_partitions(self.out, self.q, self.kc, self.vc, self.tables, self.lens, c.scale,
-                                self.ws, self.part)
+                                self.ws, self.part, flags=self.flags)
         if ev is not None:
             ev[2].record()
         pa.pa_decode_merge(self.out, self.lens, c.num_kv_heads, c.max_blocks_per_seq, self.ws,
@@ -206,7 +211,7 @@ def _secondary_decode(builder, name, steps, warmup, note=None):
     dec_ms = per["partitions"] + per["merge"]
     res = {"workload": name, "ms_per_step": round(wall, 4), "decode_ms": round(dec_ms, 4),
            "partition_kernel_ms": round(per["partitions"], 4), "merge_ms": round(per["merge"], 4),
-           "partition_tokens": run.part, "kv_bytes": kv,
+           "partition_tokens": run.part, "stream_kv": bool(run.flags), "kv_bytes": kv,
            "kv_GBs": round(kv / (dec_ms * 1e-3) / 1e9, 1),
            "pct_hbm_peak": round(100 * kv / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
            "tokens_per_s": round(case.num_seqs / (dec_ms * 1e-3), 1)}
@@ -346,7 +351,7 @@ def main():
                    "head_dim": case.head_dim, "block_size": 16,
                    "seq_lens": "uniform int [512, 4096], seed 2",
                    "num_blocks": case.num_blocks, "kv_bytes": kv,
-                   "partition_tokens": run.part,
+                   "partition_tokens": run.part, "stream_kv": bool(run.flags),
                    "step": "cache write of 64 tokens + paged decode (partitions + merge)"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
         "tokens_per_s": round(case.num_seqs / (wall_ms * 1e-3), 1),

@@ -70,6 +70,18 @@ typedef enum pa_dtype {
 #define PA_BLOCK_SIZE 16
 
 /*
+ * Decode flags.
+ * PA_DECODE_STREAM_KV -- the caller guarantees that no physical block is read
+ * twice within the call (no block shared by two sequences of the batch, as a
+ * block manager knows from its reference counts -- "vLLM学习整理", §三 on
+ * prefix caching).  K/V are then loaded with a non-temporal hint, which streams
+ * them faster from HBM on gfx950.  Without the flag the loads stay cacheable,
+ * which lets shared-prefix blocks be served from cache.  Results are
+ * bit-identical either way; a wrong promise costs speed, not correctness.
+ */
+#define PA_DECODE_STREAM_KV 1u
+
+/*
  * pa_kv_bytes_per_token -- K+V bytes one token occupies over all layers:
  * 2 * layers * kv_heads * head_dim * dtype_bytes ("vLLM-Ascend 原理", §2.1,
  * the KV size formula).  Pure host arithmetic; returns 0 if any argument is
@@ -144,6 +156,7 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  *                 positive and finite.
  *   partition_tokens  split-KV partition length (multiple of 16), or 0 for
  *                 pa_decode_default_partition().
+ *   flags         0 or PA_DECODE_STREAM_KV; other bits give PA_ERR_UNSUPPORTED.
  *   workspace     device buffer of at least pa_decode_workspace_size() bytes
  *                 (may be NULL when that size is 0), 16-byte aligned.
  *
@@ -156,13 +169,13 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                     int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
-                    float scale, pa_dtype dtype, int32_t partition_tokens, void* workspace,
-                    size_t workspace_bytes, hipStream_t stream);
+                    float scale, pa_dtype dtype, int32_t partition_tokens, uint32_t flags,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * pa_decode_partitions / pa_decode_merge -- the two phases of pa_decode, for
  * callers that schedule or time them separately.  Same arguments and
- * contract as pa_decode; the two calls must get identical arguments.
+ * contract as pa_decode; the arguments the two calls share must be identical.
  * pa_decode_partitions writes the final output of every sequence that fits
  * one partition and the partial state of the others; pa_decode_merge
  * combines the partial states (a no-op when nothing was split).
@@ -173,7 +186,7 @@ pa_status pa_decode_partitions(void* out, const void* q, const void* k_cache,
                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                int32_t block_size, int32_t max_blocks_per_seq,
                                int64_t num_blocks, float scale, pa_dtype dtype,
-                               int32_t partition_tokens, void* workspace,
+                               int32_t partition_tokens, uint32_t flags, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 pa_status pa_decode_merge(void* out, const int32_t* seq_lens, int32_t num_seqs,
                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,

@@ -19,7 +19,7 @@ import os
 import torch
 
 __all__ = [
-    "PagedKVError", "LIB_PATH", "BLOCK_SIZE", "lib",
+    "PagedKVError", "LIB_PATH", "BLOCK_SIZE", "PA_DECODE_STREAM_KV", "lib",
     "pa_kv_bytes_per_token", "pa_status_string", "pa_reshape_and_cache",
     "pa_decode_default_partition", "pa_decode_workspace_size", "pa_decode",
     "pa_decode_partitions", "pa_decode_merge", "pa_prefill_paged",
@@ -27,6 +27,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 BLOCK_SIZE = 16
+PA_DECODE_STREAM_KV = 1   # no physical block is read twice in the call: stream K/V
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -36,6 +37,7 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_u32 = ctypes.c_uint32
 
 _SIGS = {
     "pa_kv_bytes_per_token": (ctypes.c_uint64, [_i32, _i32, _i32, _i32]),
@@ -44,9 +46,9 @@ _SIGS = {
     "pa_decode_default_partition": (_i32, [_i32, _i32, _i32, _i32]),
     "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
-                         _f32, _i32, _i32, _vp, _sz, _vp]),
+                         _f32, _i32, _i32, _u32, _vp, _sz, _vp]),
     "pa_decode_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
-                                    _i32, _i64, _f32, _i32, _i32, _vp, _sz, _vp]),
+                                    _i32, _i64, _f32, _i32, _i32, _u32, _vp, _sz, _vp]),
     "pa_decode_merge": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz,
                                _vp]),
     "pa_prefill_paged": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
@@ -167,27 +169,28 @@ def _workspace(workspace, need, device):
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, partition_tokens=0,
-              workspace=None, stream=None):
+              workspace=None, stream=None, flags=0):
     """Paged decode attention into ``out`` (``[B, Hq, D]``).  ``workspace`` (bytes,
-    see ``pa_decode_workspace_size``) is allocated with torch when not given."""
+    see ``pa_decode_workspace_size``) is allocated with torch when not given.
+    ``flags``: 0 or ``PA_DECODE_STREAM_KV`` (no block shared within the batch)."""
     nb, bs, hkv, d, b, hq, mb = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens)
     need = pa_decode_workspace_size(b, hq, hkv, d, mb, partition_tokens)
     ws, ws_bytes = _workspace(workspace, need, q.device)
     _check("pa_decode", lib.pa_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), b, hq,
-        hkv, d, bs, mb, nb, float(scale), _kv_dtype(k_cache), partition_tokens, _ptr(ws), ws_bytes,
+        hkv, d, bs, mb, nb, float(scale), _kv_dtype(k_cache), partition_tokens, flags, _ptr(ws), ws_bytes,
         _stream(stream)))
     return out
 
 
 def pa_decode_partitions(out, q, k_cache, v_cache, block_tables, seq_lens, scale, workspace,
-                         partition_tokens=0, stream=None):
+                         partition_tokens=0, stream=None, flags=0):
     nb, bs, hkv, d, b, hq, mb = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens)
     need = pa_decode_workspace_size(b, hq, hkv, d, mb, partition_tokens)
     ws, ws_bytes = _workspace(workspace, need, q.device)
     _check("pa_decode_partitions", lib.pa_decode_partitions(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), b, hq,
-        hkv, d, bs, mb, nb, float(scale), _kv_dtype(k_cache), partition_tokens, _ptr(ws), ws_bytes,
+        hkv, d, bs, mb, nb, float(scale), _kv_dtype(k_cache), partition_tokens, flags, _ptr(ws), ws_bytes,
         _stream(stream)))
 
 

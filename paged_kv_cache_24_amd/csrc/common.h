@@ -106,11 +106,17 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// 16-byte load marked non-temporal: K/V tiles are streamed once per step, and
-// the streaming hint lets HBM reads run measurably faster on gfx950
-__device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
+// 16-byte K/V load.  NT: marked non-temporal, for calls in which no block is
+// read twice -- the streaming hint lets HBM reads run measurably faster on
+// gfx950, but it also keeps shared (prefix) blocks from being served from cache.
+template <bool NT>
+__device__ __forceinline__ uint4 load_kv(const uint16_t* p) {
+    if constexpr (NT) {
+        const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+        return *reinterpret_cast<const uint4*>(p);
+    }
 }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }

@@ -30,7 +30,7 @@
 
 namespace pa {
 
-template <int DT, int D, int HPW>
+template <int DT, int D, int HPW, bool NT>
 __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
     constexpr int LPR = D / 8;              // lanes per token row
     constexpr int RPW = kWave / LPR;        // token rows per load instruction
@@ -94,8 +94,8 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
         const int64_t off = (int64_t)(ok ? pb : 0) * kBlockSize * row_stride;
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
-            kr[i] = load_stream(kbase + off + (int64_t)i * RPW * row_stride);
-            vr[i] = load_stream(vbase + off + (int64_t)i * RPW * row_stride);
+            kr[i] = load_kv<NT>(kbase + off + (int64_t)i * RPW * row_stride);
+            vr[i] = load_kv<NT>(vbase + off + (int64_t)i * RPW * row_stride);
         }
         return ok;
     };
@@ -273,8 +273,8 @@ __device__ __forceinline__ df32x4_t mfma_16x16x16(const uint2& a, const uint2& b
 
 constexpr int kVRow = 144;   // LDS row stride of the V tile (elements): 288 B staggers banks
 
-template <int DT>
-__global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
+template <int DT, bool NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void decode_gqa_kernel(DecodeArgs a) {
     constexpr int D = 128;
     __shared__ __attribute__((aligned(16))) uint16_t vlds[4][kBlockSize * kVRow];
     const int lane = threadIdx.x & (kWave - 1);
@@ -336,8 +336,8 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
         const int64_t off = (int64_t)(ok ? pb : 0) * kBlockSize * row_stride;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            kr[i] = *reinterpret_cast<const uint4*>(kbase + off + 32 * i);
-            vr[i] = *reinterpret_cast<const uint4*>(vbase + off + (int64_t)4 * i * row_stride);
+            kr[i] = load_kv<NT>(kbase + off + 32 * i);
+            vr[i] = load_kv<NT>(vbase + off + (int64_t)4 * i * row_stride);
         }
         return ok;
     };
@@ -357,18 +357,22 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
         float mb = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
         mb = fmaxf(mb, __shfl_xor(mb, 16));
         mb = fmaxf(mb, __shfl_xor(mb, 32));
-        const float mn = fmaxf(m, mb);
-        const float mu = mn == -INFINITY ? 0.f : mn;
-        const float alpha = fast_exp2(m - mu);
-        float p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - mu);
-        l = fmaf(l, alpha, (p[0] + p[1]) + (p[2] + p[3]));
-        m = mn;
-        if (__any(alpha != 1.f)) {
+        // raise the running max only when this block beats it by more than 2^8:
+        // otherwise keep it (p <= 256, exact algebra) and skip the rescale of O^T
+        const bool raise = mb > m + 8.f;   // also true on the first live block
+        const float mn = raise ? mb : m;
+        if (__any(raise)) {
+            const float alpha = raise ? fast_exp2(m - mn) : 1.f;   // exp2(-inf) = 0
+            l *= alpha;
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt) o[mt] *= alpha;
         }
+        m = mn;
+        const float mu = mn == -INFINITY ? 0.f : mn;
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - mu);
+        l += (p[0] + p[1]) + (p[2] + p[3]);
         // V tile to LDS, rows past the sequence end as zeros (MFMA would turn 0 x NaN into NaN)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -392,15 +396,19 @@ __global__ __launch_bounds__(256) void decode_gqa_kernel(DecodeArgs a) {
     };
 
     if (j0 < j1) {
-        uint4 ka[4], va[4], kb[4], vb[4];
-        bool oka = load(j0, ka, va);
-        bool okb = false;
-        for (int j = j0; j < j1; j += 2) {
-            if (j + 1 < j1) okb = load(j + 1, kb, vb);
-            process(ka, va, oka, j);
-            if (j + 1 >= j1) break;
-            if (j + 2 < j1) oka = load(j + 2, ka, va);
-            process(kb, vb, okb, j + 1);
+        uint4 kc[4], vc[4];
+        bool okc = load(j0, kc, vc);
+        for (int j = j0; j < j1; ++j) {
+            uint4 kn[4], vn[4];
+            bool okn = false;
+            if (j + 1 < j1) okn = load(j + 1, kn, vn);   // next block in flight
+            process(kc, vc, okc, j);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                kc[i] = kn[i];
+                vc[i] = vn[i];
+            }
+            okc = okn;
         }
     }
 
@@ -483,16 +491,26 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     static_cast<uint16_t*>(a.out)[item * D + tid] = f32_to_bits<DT>(num * inv);
 }
 
-template <int DT, int D>
+template <int DT, int D, bool NT>
 static hipError_t launch_partitions_d(const DecodeArgs& a, hipStream_t s, dim3 grid) {
     switch (a.heads_per_wave) {
-        case 1: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 1>), grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 2>), grid, dim3(256), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 4>), grid, dim3(256), 0, s, a); break;
-        case 8: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 8>), grid, dim3(256), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 1, NT>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 2, NT>), grid, dim3(256), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 4, NT>), grid, dim3(256), 0, s, a); break;
+        case 8: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 8, NT>), grid, dim3(256), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <int DT, bool NT>
+static hipError_t launch_partitions_t(const DecodeArgs& a, hipStream_t s, dim3 grid) {
+    if (a.gqa_mfma) {
+        hipLaunchKernelGGL((decode_gqa_kernel<DT, NT>), grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
+    return a.head_dim == 128 ? launch_partitions_d<DT, 128, NT>(a, s, grid)
+                             : launch_partitions_d<DT, 64, NT>(a, s, grid);
 }
 
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t s) {
@@ -501,17 +519,12 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t s) {
     const int64_t wgs = (items + 3) / 4;
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs);
-    if (a.gqa_mfma) {
-        if (a.dtype == kF16) hipLaunchKernelGGL((decode_gqa_kernel<kF16>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((decode_gqa_kernel<kBF16>), grid, dim3(256), 0, s, a);
-        return hipGetLastError();
-    }
     if (a.dtype == kF16) {
-        return a.head_dim == 128 ? launch_partitions_d<kF16, 128>(a, s, grid)
-                                 : launch_partitions_d<kF16, 64>(a, s, grid);
+        return a.stream_kv ? launch_partitions_t<kF16, true>(a, s, grid)
+                           : launch_partitions_t<kF16, false>(a, s, grid);
     }
-    return a.head_dim == 128 ? launch_partitions_d<kBF16, 128>(a, s, grid)
-                             : launch_partitions_d<kBF16, 64>(a, s, grid);
+    return a.stream_kv ? launch_partitions_t<kBF16, true>(a, s, grid)
+                       : launch_partitions_t<kBF16, false>(a, s, grid);
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {

@@ -43,6 +43,7 @@ struct DecodeArgs {
     int32_t num_parts;       // partitions per sequence the grid covers
     float scale_log2;        // softmax scale times log2(e)
     int32_t dtype;
+    int32_t stream_kv;       // 1: no block is read twice in this call; stream K/V
 };
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);

@@ -93,7 +93,8 @@ pa::DecodeArgs decode_args(void* out, const void* q, const void* k_cache, const 
                            const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                            int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
-                           pa_dtype dtype, const DecodeShape& shape, void* workspace) {
+                           pa_dtype dtype, const DecodeShape& shape, void* workspace,
+                           uint32_t flags) {
     pa::DecodeArgs a;
     a.out = out;
     a.q = q;
@@ -116,6 +117,7 @@ pa::DecodeArgs decode_args(void* out, const void* q, const void* k_cache, const 
     a.num_parts = shape.num_parts;
     a.scale_log2 = scale * kLog2e;
     a.dtype = dtype == PA_F16 ? pa::kF16 : pa::kBF16;
+    a.stream_kv = (flags & PA_DECODE_STREAM_KV) != 0;
     float* ws = static_cast<float*>(workspace);
     const size_t states = (size_t)num_seqs * num_q_heads * shape.num_parts;
     a.ws_acc = shape.ws_bytes ? ws : nullptr;
@@ -197,8 +199,9 @@ pa_status pa_decode_partitions(void* out, const void* q, const void* k_cache, co
                                int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                int64_t num_blocks, float scale, pa_dtype dtype,
-                               int32_t partition_tokens, void* workspace, size_t workspace_bytes,
-                               hipStream_t stream) {
+                               int32_t partition_tokens, uint32_t flags, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    if (flags & ~PA_DECODE_STREAM_KV) return PA_ERR_UNSUPPORTED;
     pa_status st = check_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
                                 num_q_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, num_blocks, scale, dtype, partition_tokens);
@@ -210,7 +213,7 @@ pa_status pa_decode_partitions(void* out, const void* q, const void* k_cache, co
     const pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, seq_lens,
                                          num_seqs, num_q_heads, num_kv_heads, head_dim,
                                          max_blocks_per_seq, num_blocks, scale, dtype, shape,
-                                         workspace);
+                                         workspace, flags);
     return pa::launch_decode_partitions(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -236,7 +239,7 @@ pa_status pa_decode_merge(void* out, const int32_t* seq_lens, int32_t num_seqs,
     const pa::DecodeArgs a = decode_args(out, nullptr, nullptr, nullptr, nullptr, seq_lens,
                                          num_seqs, num_q_heads, num_kv_heads, head_dim,
                                          max_blocks_per_seq, 1, 1.f, dtype, shape,
-                                         const_cast<void*>(workspace));
+                                         const_cast<void*>(workspace), 0u);
     return pa::launch_decode_merge(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -244,12 +247,13 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                     int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
-                    float scale, pa_dtype dtype, int32_t partition_tokens, void* workspace,
-                    size_t workspace_bytes, hipStream_t stream) {
+                    float scale, pa_dtype dtype, int32_t partition_tokens, uint32_t flags,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
     pa_status st = pa_decode_partitions(out, q, k_cache, v_cache, block_tables, seq_lens,
                                         num_seqs, num_q_heads, num_kv_heads, head_dim,
                                         block_size, max_blocks_per_seq, num_blocks, scale, dtype,
-                                        partition_tokens, workspace, workspace_bytes, stream);
+                                        partition_tokens, flags, workspace, workspace_bytes,
+                                        stream);
     if (st != PA_OK || num_seqs == 0) return st;
     return pa_decode_merge(out, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                            block_size, max_blocks_per_seq, dtype, partition_tokens, workspace,

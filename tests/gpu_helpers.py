@@ -55,11 +55,11 @@ class DecodeOnGPU:
         import paged_kv_cache_24_amd as pa
         pa.pa_reshape_and_cache(self.key, self.value, self.k_cache, self.v_cache, self.slots)
 
-    def decode(self, partition_tokens=0, out=None):
+    def decode(self, partition_tokens=0, out=None, flags=0):
         import paged_kv_cache_24_amd as pa
         out = self.out if out is None else out
         pa.pa_decode(out, self.q, self.k_cache, self.v_cache, self.tables, self.lens,
-                     self.case.scale, partition_tokens)
+                     self.case.scale, partition_tokens, flags=flags)
         return out
 
 

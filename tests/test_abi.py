@@ -83,13 +83,14 @@ def test_reshape_rejects(lib):
 
 
 def _decode(lib, fn="pa_decode", out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, b=2, hq=8,
-            hkv=2, d=128, bs=16, mb=64, nb=128, scale=0.1, dt=BF16, part=0, ws=FAKE, wsb=1 << 30):
+            hkv=2, d=128, bs=16, mb=64, nb=128, scale=0.1, dt=BF16, part=0, flags=0, ws=FAKE,
+            wsb=1 << 30):
     f = getattr(lib, fn)
     f.restype = ctypes.c_int32
     f.argtypes = [P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_int32,
-                  ctypes.c_int32, P, ctypes.c_size_t, P]
-    return f(out, q, kc, vc, bt, sl, b, hq, hkv, d, bs, mb, nb, scale, dt, part, ws, wsb, None)
+                  ctypes.c_int32, ctypes.c_uint32, P, ctypes.c_size_t, P]
+    return f(out, q, kc, vc, bt, sl, b, hq, hkv, d, bs, mb, nb, scale, dt, part, flags, ws, wsb, None)
 
 
 @pytest.mark.parametrize("fn", ["pa_decode", "pa_decode_partitions"])
@@ -99,6 +100,7 @@ def test_decode_rejects(lib, fn):
     assert _decode(lib, fn, d=80) == UNSUP
     assert _decode(lib, fn, bs=8) == UNSUP
     assert _decode(lib, fn, dt=9) == UNSUP
+    assert _decode(lib, fn, flags=2) == UNSUP             # unknown flag bit
     assert _decode(lib, fn, hq=6, hkv=4) == SHAPE        # not a multiple
     assert _decode(lib, fn, hq=34, hkv=2) == SHAPE       # 17 q heads per kv head
     assert _decode(lib, fn, part=24) == SHAPE            # not a multiple of 16

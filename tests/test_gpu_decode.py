@@ -28,6 +28,9 @@ def _oracle_after_write(c):
 
 
 def _check_case(c, partitions=(0,)):
+    """Cache write bit-exact; decode within tolerance for every partition length,
+    with and without the streaming hint, which must not change a single bit."""
+    import paged_kv_cache_24_amd as pa
     g = DecodeOnGPU(c)
     g.write()
     kc, vc, ref = _oracle_after_write(c)
@@ -38,6 +41,9 @@ def _check_case(c, partitions=(0,)):
         out = g.decode(partition_tokens=p)
         torch.cuda.synchronize()
         errs[p] = assert_close(host_f64(out), ref, c.dtype, f"{c.name} partition={p}")
+        plain = host_bits(out).copy()
+        streamed = host_bits(g.decode(partition_tokens=p, flags=pa.PA_DECODE_STREAM_KV))
+        np.testing.assert_array_equal(plain, streamed)
     return errs
 
 
