@@ -202,7 +202,27 @@ def _cpu_baseline(case, budget_s):
                       f"{done / dt:.2f} sequences/s"}
 
 
-def _secondary_decode(builder, name, steps, warmup, note=None):
+def _oracle_decode_rate(case, budget_s=3.0):
+    """The float64 oracle on a bounded sample of a decode workload (whole
+    sequences in order until the budget is spent): K+V GB/s."""
+    import oracle
+    kc, vc = oracle.ref_reshape_and_cache(case.key, case.value, case.k_cache, case.v_cache,
+                                          case.slot_mapping)
+    done, kv_bytes = 0, 0
+    t0 = time.perf_counter()
+    for b in range(case.num_seqs):
+        n = int(case.seq_lens[b])
+        oracle.ref_decode_one(case.q[b], kc, vc, case.block_tables[b], n, case.scale, case.dtype)
+        done += 1
+        kv_bytes += n * 2 * case.num_kv_heads * case.head_dim * 2
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(kv_bytes / dt / 1e9, 3), "unit": "GB/s", "kind": "oracle",
+            "sample": f"{done} of {case.num_seqs} sequences in {dt:.1f} s"}
+
+
+def _secondary_decode(builder, name, steps, warmup, note=None, cpu=True):
     import torch
     case = builder()
     run = DecodeRun(case)
@@ -219,6 +239,8 @@ def _secondary_decode(builder, name, steps, warmup, note=None):
         res["write_ms"] = round(per["write"], 4)
     if note:
         res.update(note(case))
+    if cpu:
+        res["cpu_oracle"] = _oracle_decode_rate(case)
     run.free()
     del run, case
     torch.cuda.empty_cache()
@@ -243,7 +265,7 @@ def _shared_prefix_note(case):
                     "the shared prefixes may be served from the 256 MB Infinity Cache"}
 
 
-def _secondary_prefill(steps, warmup):
+def _secondary_prefill(steps, warmup, oracle_budget_s=3.0):
     import torch
     import paged_kv_cache_24_amd as pa
     from workloads import prefill_chunked
@@ -280,6 +302,24 @@ def _secondary_prefill(steps, warmup):
     pairs = int((L * ctxl + L * (L + 1) // 2).sum())
     flops = 4 * c.num_q_heads * c.head_dim * pairs
     write_bytes = 2 * 2 * c.num_tokens * c.num_kv_heads * c.head_dim * 2   # read + write, K and V
+    cpu = None
+    if oracle_budget_s > 0:
+        import oracle
+        rk, rv = oracle.ref_reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache, c.slot_mapping)
+        done_pairs, t0 = 0, time.perf_counter()
+        for b in range(c.num_seqs):
+            lo, n_rows = int(c.query_start_loc[b]), int(L[b])
+            rows = np.arange(min(n_rows, 64))
+            if len(rows):
+                oracle.ref_prefill_rows(c.q, rk, rv, c.block_tables[b], int(ctxl[b]), lo, rows,
+                                        c.scale, c.dtype)
+                done_pairs += int((ctxl[b] + rows + 1).sum())
+            if time.perf_counter() - t0 > oracle_budget_s:
+                break
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(4 * c.num_q_heads * c.head_dim * done_pairs / dt / 1e12, 5),
+               "unit": "TFLOP/s", "kind": "oracle",
+               "sample": f"first <=64 rows of {b + 1} sequences ({done_pairs} (row, key) pairs per head) in {dt:.1f} s"}
     res = {"workload": "prefill_chunked", "ms_per_step": round(wall, 4),
            "write_ms": round(per["write"], 4),
            "write_GBs": round(write_bytes / (per["write"] * 1e-3) / 1e9, 1),
@@ -288,9 +328,40 @@ def _secondary_prefill(steps, warmup):
            "prefill_TFLOPs": round(flops / (per["prefill"] * 1e-3) / 1e12, 1),
            "prefill_pct_mfma_peak": round(100 * flops / (per["prefill"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 1),
            "new_tokens": c.num_tokens, "unmasked_pairs_per_head": pairs}
+    if cpu:
+        res["cpu_oracle"] = cpu
     del q, kc, vc, key, value, out
     torch.cuda.empty_cache()
     return res
+
+
+def _secondary_copy_blocks(steps, warmup, pairs_n=2048):
+    """Copy-on-write / swap block copy: 2048 random (src, dst) pairs in a
+    32768-block bf16 pool with 8 kv heads of 128 (64 KiB of K+V per pair)."""
+    import torch
+    import paged_kv_cache_24_amd as pa
+    nb, hkv, d = 32768, 8, 128
+    kc = torch.empty((nb, 16, hkv, d), dtype=torch.bfloat16, device="cuda").normal_()
+    vc = torch.empty_like(kc).normal_()
+    perm = np.random.default_rng(6).permutation(nb)
+    pairs = torch.from_numpy(np.stack([perm[:pairs_n], perm[pairs_n:2 * pairs_n]], 1).astype(np.int64)).cuda()
+    for _ in range(warmup):
+        pa.pa_copy_blocks(kc, vc, pairs)
+    torch.cuda.synchronize()
+    timer = _Timer(["copy"])
+    for _ in range(steps):
+        ev = timer.step()
+        ev[0].record()
+        pa.pa_copy_blocks(kc, vc, pairs)
+        ev[1].record()
+    torch.cuda.synchronize()
+    ms = timer.mean_ms()["copy"]
+    moved = 2 * pairs_n * 2 * 16 * hkv * d * 2   # read + write, K and V
+    del kc, vc
+    torch.cuda.empty_cache()
+    return {"workload": "copy_blocks", "pairs": pairs_n, "ms": round(ms, 4),
+            "GBs_read_plus_write": round(moved / (ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)}
 
 
 def _copy_calibration():
@@ -376,6 +447,7 @@ def main():
         sec.append(_secondary_prefill(s2, w2))
         sec.append(_secondary_decode(decode_long_context, "decode_long_context", s2, w2))
         sec.append(_secondary_decode(decode_tiny, "decode_tiny", s2, w2))
+        sec.append(_secondary_copy_blocks(s2, w2))
         result["secondary"] = sec
     result["input_generation_s"] = round(gen_s, 1)
     print(json.dumps(result), flush=True)

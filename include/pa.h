@@ -115,6 +115,27 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
                                pa_dtype dtype, hipStream_t stream);
 
 /*
+ * pa_copy_blocks -- copy whole physical blocks: block dst becomes a copy of
+ * block src, K and V, every kv head.  This is the block copy behind a
+ * copy-on-write fork of a shared prefix ("vLLM-Ascend 原理", §2.1: sequences
+ * with the same prefix point at the same physical blocks and fork by
+ * copy-on-write) and behind swapping ("vLLM学习整理", §三 "Preemption").
+ *
+ *   k_cache, v_cache  [num_blocks][block_size][num_kv_heads][head_dim] (read/written)
+ *   block_pairs       int64 [num_pairs][2] = (src, dst), device memory.  A pair
+ *                     with a negative or out-of-range entry, or src == dst, is
+ *                     skipped.
+ *
+ * Destinations must be distinct and no destination may be the source of
+ * another pair; otherwise the result depends on scheduling.  num_pairs == 0
+ * is a no-op returning PA_OK.
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs,
+                         int64_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int64_t num_blocks, pa_dtype dtype,
+                         hipStream_t stream);
+
+/*
  * pa_decode_default_partition -- the split-KV partition length, in tokens, that
  * pa_decode uses when given partition_tokens == 0 (a power of two >= 256).  It
  * depends only on host-known sizes: about max_blocks_per_seq * 16 / 8, capped

@@ -13,6 +13,7 @@ from .paged_attention import (  # noqa: F401
     bits_to_float64,
     kv_bytes_per_token,
     ref_reshape_and_cache,
+    ref_copy_blocks,
     gather_tokens,
     ref_contiguous_attention,
     ref_decode,

@@ -111,6 +111,37 @@ def ref_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping):
     return kc, vc
 
 
+def ref_copy_blocks(k_cache, v_cache, block_pairs):
+    """Copy whole physical blocks, K and V: block ``dst`` becomes a copy of block
+    ``src`` for every ``(src, dst)`` pair.
+
+    This is the block copy behind copy-on-write: sequences that share a prefix
+    point at the same physical blocks until one of them writes, and then forks
+    onto a copy ["vLLM-Ascend 原理", §2.1, prefix sharing with copy-on-write];
+    the same copy moves blocks for swapping ["vLLM学习整理", §三 "Preemption"].
+    Pairs with a negative entry are skipped.  Destinations must be distinct and
+    no destination may also be a source, so the order of the pairs does not
+    matter.  Returns new ``(k_cache, v_cache)``.
+    """
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    num_blocks = kc.shape[0]
+    pairs = [(int(a), int(b)) for a, b in np.asarray(block_pairs).reshape(-1, 2)]
+    live = [(a, b) for a, b in pairs if a >= 0 and b >= 0]
+    dsts = [b for _, b in live]
+    if len(set(dsts)) != len(dsts):
+        raise ValueError("a destination block appears twice")
+    for a, b in live:
+        if a >= num_blocks or b >= num_blocks:
+            raise IndexError(f"block pair ({a}, {b}) outside a pool of {num_blocks}")
+    if any(b in {a for a, _ in live} and (b, b) not in live for b in dsts):
+        raise ValueError("a destination block is also a source")
+    for a, b in live:
+        kc[b] = k_cache[a]
+        vc[b] = v_cache[a]
+    return kc, vc
+
+
 def gather_tokens(cache: np.ndarray, table_row: np.ndarray, n: int) -> np.ndarray:
     """The first ``n`` tokens of one sequence, in logical order.
 

@@ -5,7 +5,7 @@ Each function here marshals torch tensors into the C ABI of ``libpa.so``
 runs in the library's HIP kernels, on torch's current stream.  There is no
 fallback: if ``libpa.so`` is missing, importing this package raises.
 
-Names follow the C ABI: ``pa_reshape_and_cache``, ``pa_decode``,
+Names follow the C ABI: ``pa_reshape_and_cache``, ``pa_copy_blocks``, ``pa_decode``,
 ``pa_decode_partitions``, ``pa_decode_merge``, ``pa_prefill_paged``,
 ``pa_decode_workspace_size``, ``pa_decode_default_partition``,
 ``pa_kv_bytes_per_token``, ``pa_status_string``.
@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "PagedKVError", "LIB_PATH", "BLOCK_SIZE", "PA_DECODE_STREAM_KV", "lib",
-    "pa_kv_bytes_per_token", "pa_status_string", "pa_reshape_and_cache",
+    "pa_kv_bytes_per_token", "pa_status_string", "pa_reshape_and_cache", "pa_copy_blocks",
     "pa_decode_default_partition", "pa_decode_workspace_size", "pa_decode",
     "pa_decode_partitions", "pa_decode_merge", "pa_prefill_paged",
 ]
@@ -31,7 +31,7 @@ PA_DECODE_STREAM_KV = 1   # no physical block is read twice in the call: stream 
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m paged_kv_cache_24_amd.build` "
+        f"{LIB_PATH} is not built; run `python paged_kv_cache_24_amd/build.py` "
         "(hipcc for gfx950). There is no non-HIP fallback.")
 
 lib = ctypes.CDLL(LIB_PATH)
@@ -43,6 +43,7 @@ _SIGS = {
     "pa_kv_bytes_per_token": (ctypes.c_uint64, [_i32, _i32, _i32, _i32]),
     "pa_status_string": (ctypes.c_char_p, [_i32]),
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i32, _vp]),
+    "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i32, _vp]),
     "pa_decode_default_partition": (_i32, [_i32, _i32, _i32, _i32]),
     "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
@@ -128,6 +129,19 @@ def pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None
     _check("pa_reshape_and_cache", lib.pa_reshape_and_cache(
         _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), key.shape[0],
         hkv, d, bs, nb, _kv_dtype(k_cache), _stream(stream)))
+
+
+def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None):
+    """Copy whole blocks: ``block_pairs`` is int64 ``[N, 2]`` of (src, dst) rows."""
+    _need(k_cache, "k_cache", ndim=4)
+    _need(v_cache, "v_cache", k_cache.dtype, 4)
+    _need(block_pairs, "block_pairs", torch.int64, 2)
+    nb, bs, hkv, d = k_cache.shape
+    if v_cache.shape != k_cache.shape or block_pairs.shape[1] != 2:
+        raise ValueError("cache shapes disagree or block_pairs is not [N, 2]")
+    _check("pa_copy_blocks", lib.pa_copy_blocks(
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_pairs), block_pairs.shape[0], hkv, d, bs, nb,
+        _kv_dtype(k_cache), _stream(stream)))
 
 
 def pa_decode_default_partition(num_q_heads: int, num_kv_heads: int, head_dim: int,

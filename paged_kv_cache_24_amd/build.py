@@ -1,7 +1,8 @@
 """Build libpa.so for gfx950 in-tree with hipcc.
 
-``python -m paged_kv_cache_24_amd.build`` compiles every HIP source under
-``csrc/`` (in parallel) and links ``paged_kv_cache_24_amd/libpa.so``.
+``python paged_kv_cache_24_amd/build.py`` compiles every HIP source under
+``csrc/`` (in parallel) and links ``paged_kv_cache_24_amd/libpa.so``.  Run it as
+a script (or load it by path): importing the package itself needs the library.
 """
 
 from __future__ import annotations
@@ -20,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["pa_api.hip", "reshape_and_cache.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["pa_api.hip", "reshape_and_cache.hip", "copy_blocks.hip", "decode.hip", "prefill.hip"]
 
 COMPILE_FLAGS = [
     f"--offload-arch={ARCH}",

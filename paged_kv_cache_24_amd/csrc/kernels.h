@@ -20,6 +20,17 @@ struct ReshapeArgs {
 };
 hipError_t launch_reshape_and_cache(const ReshapeArgs& a, hipStream_t stream);
 
+struct CopyBlocksArgs {
+    void* k_cache;
+    void* v_cache;
+    const int64_t* block_pairs;   // [num_pairs][2] = (src, dst)
+    int64_t num_pairs;
+    int64_t num_blocks;
+    int64_t block_vecs;           // 16-byte vectors per block (block_size * kv_heads * head_dim / 8)
+    int64_t wgs_per_pair;         // workgroups per pair (1024 vectors each)
+};
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
+
 struct DecodeArgs {
     void* out;
     const void* q;

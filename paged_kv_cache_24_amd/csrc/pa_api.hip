@@ -178,6 +178,26 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
     return pa::launch_reshape_and_cache(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs, int64_t num_pairs,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int64_t num_blocks, pa_dtype dtype, hipStream_t stream) {
+    if (!supported_dtype(dtype) || block_size != PA_BLOCK_SIZE || (head_dim != 64 && head_dim != 128))
+        return PA_ERR_UNSUPPORTED;
+    if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+    if (num_pairs == 0) return PA_OK;
+    if (!k_cache || !v_cache || !block_pairs) return PA_ERR_NULL_PTR;
+    if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGNMENT;
+    pa::CopyBlocksArgs a;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_pairs = block_pairs;
+    a.num_pairs = num_pairs;
+    a.num_blocks = num_blocks;
+    a.block_vecs = (int64_t)PA_BLOCK_SIZE * num_kv_heads * head_dim / 8;
+    a.wgs_per_pair = (a.block_vecs + 1023) / 1024;
+    return pa::launch_copy_blocks(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 int32_t pa_decode_default_partition(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                     int32_t max_blocks_per_seq) {
     if (num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0) return 256;

@@ -278,6 +278,41 @@ def pin_reshape_semantics(o):
             raise AssertionError(f"slots {bad} accepted")
 
 
+def pin_copy_on_write_fork_golden(o):
+    """Fork by copy-on-write, worked by hand: after the block copy and the write,
+    sequence a still reads the old tokens and sequence b reads its new one."""
+    g = _golden("copy_on_write_fork.json")
+    nb, bs = g["num_blocks"], g["block_size"]
+    rng = np.random.default_rng(51)
+    kc = normal_bits(rng, (nb, bs, 1, 8), "f16")
+    vc = normal_bits(rng, (nb, bs, 1, 8), "f16")
+    kc2, vc2 = o.ref_copy_blocks(kc, vc, np.array(g["copy_pairs"], np.int64))
+    src, dst = g["copy_pairs"][0]
+    np.testing.assert_array_equal(kc2[dst], kc[src])
+    np.testing.assert_array_equal(vc2[dst], vc[src])
+    untouched = [b for b in range(nb) if b != dst]
+    np.testing.assert_array_equal(kc2[untouched], kc[untouched])
+    new_k = normal_bits(rng, (1, 1, 8), "f16")
+    kc3, vc3 = o.ref_reshape_and_cache(new_k, new_k, kc2, vc2, np.array([g["fork_slot_b"]], np.int64))
+    ta, tb = np.array(g["table_a"]), np.array(g["table_b_after"])
+    n = g["tokens"]
+    a_k = o.gather_tokens(kc3, ta, n)
+    b_k = o.gather_tokens(kc3, tb, n)
+    np.testing.assert_array_equal(a_k, o.gather_tokens(kc, ta, n))       # a unchanged
+    np.testing.assert_array_equal(b_k[:g["write_token_b"]], a_k[:g["write_token_b"]])
+    np.testing.assert_array_equal(b_k[g["write_token_b"]], new_k[0])
+    assert g["shared_slot_b"] == ta[g["write_token_b"] // bs] * bs + g["write_token_b"] % bs
+    for bad in ([[1, 6], [2, 6]], [[1, 6], [6, 3]], [[1, 9]]):
+        try:
+            o.ref_copy_blocks(kc, vc, np.array(bad, np.int64))
+        except (ValueError, IndexError):
+            pass
+        else:
+            raise AssertionError(f"pairs {bad} accepted")
+    same, _ = o.ref_copy_blocks(kc, vc, np.array([[-1, 3], [2, -1]], np.int64))
+    np.testing.assert_array_equal(same, kc)                                # negative entries skip
+
+
 # ------------------------------------------------------------ chunked prefill
 
 def _small_prefill(seed=31, q_lens=(5, 0, 17, 1, 33), ctx=(0, 9, 20, 15, 40)):

@@ -23,7 +23,7 @@ def _declared():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        pytest.fail("libpa.so is not built (python -m paged_kv_cache_24_amd.build)")
+        pytest.fail("libpa.so is not built (python paged_kv_cache_24_amd/build.py)")
     return ctypes.CDLL(LIB)
 
 
@@ -31,7 +31,7 @@ def test_header_declares_the_calls():
     names = _declared()
     for n in ["pa_reshape_and_cache", "pa_decode", "pa_prefill_paged", "pa_decode_workspace_size",
               "pa_kv_bytes_per_token", "pa_status_string", "pa_decode_partitions",
-              "pa_decode_merge", "pa_decode_default_partition"]:
+              "pa_decode_merge", "pa_decode_default_partition", "pa_copy_blocks"]:
         assert n in names
 
 
@@ -160,3 +160,21 @@ def test_prefill_rejects(lib):
     assert _prefill(lib, scale=float("inf")) == SHAPE
     assert _prefill(lib, q=FAKE + 2) == ALIGN
     assert _prefill(lib, t=0, q=None) == PA_OK
+
+
+def test_copy_blocks_rejects(lib):
+    f = lib.pa_copy_blocks
+    f.restype = ctypes.c_int32
+    f.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int64, ctypes.c_int32, P]
+
+    def call(kc=FAKE, vc=FAKE, pairs=FAKE, n=3, hkv=8, d=128, bs=16, nb=32, dt=BF16):
+        return f(kc, vc, pairs, n, hkv, d, bs, nb, dt, None)
+    assert call(pairs=None) == NULL
+    assert call(vc=None) == NULL
+    assert call(d=32) == UNSUP
+    assert call(bs=8) == UNSUP
+    assert call(n=-1) == SHAPE
+    assert call(nb=0) == SHAPE
+    assert call(kc=FAKE + 4) == ALIGN
+    assert call(n=0, pairs=None) == PA_OK

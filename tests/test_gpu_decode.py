@@ -234,3 +234,54 @@ def test_reshape_skips_padding_slots():
     rk, rv = oracle.ref_reshape_and_cache(key, val, kc, vc, slots)
     np.testing.assert_array_equal(host_bits(gk), rk)
     np.testing.assert_array_equal(host_bits(gv), rv)
+
+
+def test_copy_blocks_bit_exact():
+    """Block copy (copy-on-write fork / swap) against the oracle, whole pools."""
+    import paged_kv_cache_24_amd as pa
+    rng = np.random.default_rng(15)
+    for dtype, hkv, d in (("bf16", 8, 128), ("f16", 4, 64), ("f16", 32, 128)):
+        nb = 40
+        kc = normal_bits(rng, (nb, 16, hkv, d), dtype)
+        vc = normal_bits(rng, (nb, 16, hkv, d), dtype)
+        perm = rng.permutation(nb)
+        pairs = np.stack([perm[:12], perm[12:24]], axis=1).astype(np.int64)
+        spare = int(perm[30])   # in no other pair: its self-copy is a no-op
+        pairs = np.concatenate([pairs, [[-1, 5], [3, -1], [spare, spare], [2, nb + 3]]]).astype(np.int64)
+        gk, gv = dev_bits(kc, dtype), dev_bits(vc, dtype)
+        pa.pa_copy_blocks(gk, gv, dev_int(pairs, torch.int64))
+        ok = pairs[(pairs[:, 0] >= 0) & (pairs[:, 1] >= 0) & (pairs[:, 1] < nb)]
+        rk, rv = oracle.ref_copy_blocks(kc, vc, ok)
+        np.testing.assert_array_equal(host_bits(gk), rk)
+        np.testing.assert_array_equal(host_bits(gv), rv)
+
+
+def test_copy_on_write_fork_then_decode():
+    """Two sequences share every block; one forks its last block (copy, then its
+    new token goes into the copy).  Decode of the untouched sequence is unchanged
+    and the forked one matches the oracle."""
+    import paged_kv_cache_24_amd as pa
+    c = make_decode_case(name="fork", seed=16, dtype="bf16", num_q_heads=8, num_kv_heads=2,
+                         head_dim=128, seq_lens=[37, 37], num_blocks=8, max_blocks_per_seq=3,
+                         scale=0.09, write_last=False, share_group=2, share_tokens=48)
+    assert (c.block_tables[0] == c.block_tables[1]).all()
+    g = DecodeOnGPU(c)
+    before = host_bits(g.decode()).copy()
+    used = set(c.block_tables[c.block_tables >= 0].tolist())
+    free = next(b for b in range(c.num_blocks) if b not in used)
+    last = int(c.block_tables[1, 2])
+    pa.pa_copy_blocks(g.k_cache, g.v_cache, dev_int(np.array([[last, free]], np.int64), torch.int64))
+    tables = c.block_tables.copy()
+    tables[1, 2] = free
+    key = normal_bits(np.random.default_rng(17), (1, 2, 128), "bf16")
+    slot = np.array([free * 16 + 37 % 16], np.int64)
+    pa.pa_reshape_and_cache(dev_bits(key, "bf16"), dev_bits(key, "bf16"), g.k_cache, g.v_cache,
+                            dev_int(slot, torch.int64))
+    g.tables = dev_int(tables)
+    g.lens = dev_int(np.array([37, 38], np.int32))
+    after = host_f64(g.decode())
+    np.testing.assert_array_equal(host_bits(g.out)[0], before[0])
+    rk, rv = oracle.ref_copy_blocks(c.k_cache, c.v_cache, np.array([[last, free]], np.int64))
+    rk, rv = oracle.ref_reshape_and_cache(key, key, rk, rv, slot)
+    ref = oracle.ref_decode(c.q, rk, rv, tables, np.array([37, 38]), c.scale, "bf16")
+    assert_close(after, ref, "bf16", "forked decode")

@@ -39,6 +39,9 @@ MUTANTS = {
                                  "return layers * kv_heads * head_dim * dtype_bytes"),
     "bf16_widened_wrong": ("(bits.astype(np.uint32) << 16)", "(bits.astype(np.uint32) << 15)"),
     "scale_kept_in_float64": ("return float(np.float32(scale))", "return float(scale)"),
+    "copy_blocks_reversed": ("        kc[b] = k_cache[a]\n        vc[b] = v_cache[a]",
+                             "        kc[a] = k_cache[b]\n        vc[a] = v_cache[b]"),
+    "copy_blocks_v_from_k": ("        vc[b] = v_cache[a]", "        vc[b] = k_cache[a]"),
 }
 
 
