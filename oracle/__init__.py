@@ -23,3 +23,15 @@ from .paged_attention import (  # noqa: F401
     ref_partition_state,
     ref_merge_partitions,
 )
+from .kv_fp8 import (  # noqa: F401
+    E4M3_MAX,
+    e4m3_to_float64,
+    float_to_e4m3,
+    quantize_e4m3_rows,
+    dequantize_e4m3_rows,
+    ref_reshape_and_cache_fp8,
+    gather_scales,
+    ref_decode_fp8,
+    ref_prefill_rows_fp8,
+    ref_prefill_paged_fp8,
+)
