@@ -19,7 +19,9 @@
  * every call is re-entrant and may be issued from any host thread.
  *
  * Element types.  q, out, key, value and both caches share one 16-bit type,
- * pa_dtype.  Accumulation is float32; outputs are rounded to nearest even.
+ * pa_dtype (the *_fp8 calls at the end keep the caches as 8-bit codes with
+ * float32 scales instead).  Accumulation is float32; outputs are rounded to
+ * nearest even.
  *
  * KV cache layout.  k_cache and v_cache are two separate tensors, each
  * [num_blocks][block_size][num_kv_heads][head_dim].  Token slot
@@ -246,6 +248,79 @@ pa_status pa_prefill_paged(void* out, const void* q, const void* k_cache, const 
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                            int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
                            pa_dtype dtype, hipStream_t stream);
+
+/*
+ * ------------------------------------------------------------------------
+ * FP8 KV cache.  Each layer's per-head k and v are stored in 8 bits, which
+ * halves the cache; they are quantised when written and dequantised inside
+ * the attention kernels after the block-table lookup ("vLLM-Ascend 原理",
+ * §四, the paragraph on KV-cache quantisation).
+ *
+ * Format: OCP 8-bit floating point E4M3 (bias 7, no infinities, S.1111.111 =
+ * NaN, largest finite magnitude 448).  One float32 scale per (token, kv head)
+ * row of head_dim elements:
+ *     s = amax / 448   (amax = largest |x| of the row; s = 1 if amax == 0)
+ *     code = e4m3(clamp(x / s, -448, 448)),  x / s rounded once in float32,
+ *            the conversion rounding to nearest, ties to even
+ *     value = decode(code) * s
+ * Pools:
+ *     k_cache, v_cache    uint8   [num_blocks][block_size][num_kv_heads][head_dim]
+ *     k_scales, v_scales  float32 [num_blocks][num_kv_heads][block_size]
+ * (the scales of one block and head are 64 contiguous bytes).  q, out, key and
+ * value keep the 16-bit type `dtype`.  Inputs must be finite and, for the
+ * attention calls, every scale of a live token a normal float32 (amax of
+ * each row at least 448 * 2^-126); slots past a sequence's end may hold any
+ * bits.  All pointers 16-byte aligned.
+ * ------------------------------------------------------------------------
+ */
+
+/*
+ * pa_reshape_and_cache_fp8 -- the cache write into an FP8 cache: quantise
+ * each new token's k and v per kv head and store codes and scales in its slot
+ * (codes at row s of the [num_blocks * block_size] view, scales at
+ * [s / block_size][head][s % block_size]).  Slot conventions as for
+ * pa_reshape_and_cache; key and value are [num_tokens][num_kv_heads][head_dim]
+ * of `dtype`.  num_tokens == 0 is a no-op returning PA_OK.
+ */
+pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache,
+                                   void* v_cache, float* k_scales, float* v_scales,
+                                   const int64_t* slot_mapping, int64_t num_tokens,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int64_t num_blocks, pa_dtype dtype, hipStream_t stream);
+
+/*
+ * pa_copy_blocks_fp8 -- pa_copy_blocks for an FP8 cache: block dst of the code
+ * pools and of the scale pools becomes a copy of block src.  Same pair rules.
+ */
+pa_status pa_copy_blocks_fp8(void* k_cache, void* v_cache, float* k_scales, float* v_scales,
+                             const int64_t* block_pairs, int64_t num_pairs, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                             hipStream_t stream);
+
+/*
+ * pa_decode_fp8 / pa_decode_partitions_fp8 -- pa_decode and its first phase
+ * over an FP8 cache: k_cache / v_cache hold codes and k_scales / v_scales
+ * their scales; every other argument, the workspace (pa_decode_workspace_size)
+ * and the default partition are those of pa_decode.  The second phase of
+ * pa_decode_partitions_fp8 is pa_decode_merge, unchanged.  Output: attention
+ * over the dequantised K/V, accumulated in float32, rounded to `dtype`.
+ */
+pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                        const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                        pa_dtype dtype, int32_t partition_tokens, uint32_t flags,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+pa_status pa_decode_partitions_fp8(void* out, const void* q, const void* k_cache,
+                                   const void* v_cache, const float* k_scales,
+                                   const float* v_scales, const int32_t* block_tables,
+                                   const int32_t* seq_lens, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t max_blocks_per_seq,
+                                   int64_t num_blocks, float scale, pa_dtype dtype,
+                                   int32_t partition_tokens, uint32_t flags, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -8,7 +8,9 @@ fallback: if ``libpa.so`` is missing, importing this package raises.
 Names follow the C ABI: ``pa_reshape_and_cache``, ``pa_copy_blocks``, ``pa_decode``,
 ``pa_decode_partitions``, ``pa_decode_merge``, ``pa_prefill_paged``,
 ``pa_decode_workspace_size``, ``pa_decode_default_partition``,
-``pa_kv_bytes_per_token``, ``pa_status_string``.
+``pa_kv_bytes_per_token``, ``pa_status_string``, and for an FP8 (E4M3) cache
+``pa_reshape_and_cache_fp8``, ``pa_copy_blocks_fp8``, ``pa_decode_fp8``,
+``pa_decode_partitions_fp8``.
 """
 
 from __future__ import annotations
@@ -23,6 +25,7 @@ __all__ = [
     "pa_kv_bytes_per_token", "pa_status_string", "pa_reshape_and_cache", "pa_copy_blocks",
     "pa_decode_default_partition", "pa_decode_workspace_size", "pa_decode",
     "pa_decode_partitions", "pa_decode_merge", "pa_prefill_paged",
+    "pa_reshape_and_cache_fp8", "pa_copy_blocks_fp8", "pa_decode_fp8", "pa_decode_partitions_fp8",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
@@ -54,6 +57,14 @@ _SIGS = {
                                _vp]),
     "pa_prefill_paged": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
                                 _i32, _i32, _i32, _i64, _f32, _i32, _vp]),
+    "pa_reshape_and_cache_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+                                        _i64, _i32, _vp]),
+    "pa_copy_blocks_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp]),
+    "pa_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                             _i32, _i64, _f32, _i32, _i32, _u32, _vp, _sz, _vp]),
+    "pa_decode_partitions_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                        _i32, _i32, _i32, _i64, _f32, _i32, _i32, _u32, _vp, _sz,
+                                        _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -243,3 +254,87 @@ def pa_prefill_paged(out, q, k_cache, v_cache, block_tables, ctx_lens, query_sta
         _ptr(query_start_loc), b, t, int(max_q_len), hq, hkv, d, bs, block_tables.shape[1], nb,
         float(scale), _kv_dtype(k_cache), _stream(stream)))
     return out
+
+
+# ------------------------------------------------------------- FP8 KV cache
+
+def _fp8_pools(k_cache, v_cache, k_scales, v_scales):
+    _need(k_cache, "k_cache", torch.uint8, 4)
+    _need(v_cache, "v_cache", torch.uint8, 4)
+    _need(k_scales, "k_scales", torch.float32, 3)
+    _need(v_scales, "v_scales", torch.float32, 3)
+    nb, bs, hkv, d = k_cache.shape
+    if v_cache.shape != k_cache.shape or k_scales.shape != (nb, hkv, bs) or v_scales.shape != (nb, hkv, bs):
+        raise ValueError("FP8 pools need codes [NB, 16, Hkv, D] and scales [NB, Hkv, 16]")
+    return nb, bs, hkv, d
+
+
+def pa_reshape_and_cache_fp8(key, value, k_cache, v_cache, k_scales, v_scales, slot_mapping,
+                             stream=None):
+    """Quantise ``key[t]``/``value[t]`` (``[N, Hkv, D]``, fp16 or bf16) to E4M3 with one
+    float32 scale per (token, kv head) and store codes and scales at slot
+    ``slot_mapping[t]``; negative slots are skipped."""
+    nb, bs, hkv, d = _fp8_pools(k_cache, v_cache, k_scales, v_scales)
+    _need(key, "key", None, 3)
+    _need(value, "value", key.dtype, 3)
+    _need(slot_mapping, "slot_mapping", torch.int64, 1)
+    if key.shape != value.shape or tuple(key.shape[1:]) != (hkv, d):
+        raise ValueError("key/value/cache shapes disagree")
+    if slot_mapping.shape[0] != key.shape[0]:
+        raise ValueError("slot_mapping needs one entry per token")
+    _check("pa_reshape_and_cache_fp8", lib.pa_reshape_and_cache_fp8(
+        _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
+        _ptr(slot_mapping), key.shape[0], hkv, d, bs, nb, _kv_dtype(key), _stream(stream)))
+
+
+def pa_copy_blocks_fp8(k_cache, v_cache, k_scales, v_scales, block_pairs, stream=None):
+    """Copy whole blocks of an FP8 cache (codes and scales): ``block_pairs`` is int64
+    ``[N, 2]`` of (src, dst) rows."""
+    nb, bs, hkv, d = _fp8_pools(k_cache, v_cache, k_scales, v_scales)
+    _need(block_pairs, "block_pairs", torch.int64, 2)
+    if block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs is not [N, 2]")
+    _check("pa_copy_blocks_fp8", lib.pa_copy_blocks_fp8(
+        _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales), _ptr(block_pairs),
+        block_pairs.shape[0], hkv, d, bs, nb, _stream(stream)))
+
+
+def _decode_fp8_args(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens):
+    nb, bs, hkv, d = _fp8_pools(k_cache, v_cache, k_scales, v_scales)
+    _need(q, "q", None, 3)
+    _need(out, "out", q.dtype, 3)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    b, hq, dq = q.shape
+    if out.shape != q.shape or dq != d:
+        raise ValueError("q/out/cache shapes disagree")
+    if block_tables.shape[0] != b or seq_lens.shape[0] != b:
+        raise ValueError("block_tables and seq_lens need one row per sequence")
+    return nb, bs, hkv, d, b, hq, block_tables.shape[1]
+
+
+def pa_decode_fp8(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens, scale,
+                  partition_tokens=0, workspace=None, stream=None, flags=0):
+    """Paged decode over an FP8 cache into ``out`` (``[B, Hq, D]``, the type of ``q``);
+    the other arguments as for ``pa_decode``."""
+    nb, bs, hkv, d, b, hq, mb = _decode_fp8_args(out, q, k_cache, v_cache, k_scales, v_scales,
+                                                 block_tables, seq_lens)
+    need = pa_decode_workspace_size(b, hq, hkv, d, mb, partition_tokens)
+    ws, ws_bytes = _workspace(workspace, need, q.device)
+    _check("pa_decode_fp8", lib.pa_decode_fp8(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
+        _ptr(block_tables), _ptr(seq_lens), b, hq, hkv, d, bs, mb, nb, float(scale), _kv_dtype(q),
+        partition_tokens, flags, _ptr(ws), ws_bytes, _stream(stream)))
+    return out
+
+
+def pa_decode_partitions_fp8(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, seq_lens,
+                             scale, workspace, partition_tokens=0, stream=None, flags=0):
+    nb, bs, hkv, d, b, hq, mb = _decode_fp8_args(out, q, k_cache, v_cache, k_scales, v_scales,
+                                                 block_tables, seq_lens)
+    need = pa_decode_workspace_size(b, hq, hkv, d, mb, partition_tokens)
+    ws, ws_bytes = _workspace(workspace, need, q.device)
+    _check("pa_decode_partitions_fp8", lib.pa_decode_partitions_fp8(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
+        _ptr(block_tables), _ptr(seq_lens), b, hq, hkv, d, bs, mb, nb, float(scale), _kv_dtype(q),
+        partition_tokens, flags, _ptr(ws), ws_bytes, _stream(stream)))

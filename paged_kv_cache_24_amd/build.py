@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["pa_api.hip", "reshape_and_cache.hip", "copy_blocks.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["pa_api.hip", "reshape_and_cache.hip", "copy_blocks.hip", "decode.hip", "decode_fp8.hip", "prefill.hip"]
 
 COMPILE_FLAGS = [
     f"--offload-arch={ARCH}",

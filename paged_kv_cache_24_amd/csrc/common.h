@@ -102,7 +102,61 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Max over aligned groups of N lanes (N = 8 or 16); every lane gets its group's max.
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+    static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+    x = fmaxf(x, dpp<kDppQuadXor1>(x));
+    x = fmaxf(x, dpp<kDppQuadXor2>(x));
+    x = fmaxf(x, dpp<kDppHalfMirror>(x));
+    if constexpr (N == 16) x = fmaxf(x, dpp<kDppMirror>(x));
+    return x;
+}
+
+// Sum over aligned groups of 4 lanes.
+__device__ __forceinline__ float quad_sum(float x) {
+    x += dpp<kDppQuadXor1>(x);
+    return x + dpp<kDppQuadXor2>(x);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// --------------------------------------------------------- FP8 (OCP E4M3)
+// Hardware conversions of gfx950, both exact where used here:
+//  * v_cvt_scalef32_pk_{f16,bf16}_fp8 turns two E4M3 codes into two 16-bit
+//    values times 2^e, e the exponent of the scale operand (its mantissa is
+//    ignored).  Every E4M3 value is exact in fp16 and bf16.
+//  * v_cvt_pk_f32_fp8 turns two codes into two float32.
+//  * v_cvt_pk_fp8_f32 rounds two float32 to E4M3, nearest-even; inputs must
+//    already be clamped to +-448 (it does not saturate).
+
+// codes 2*HI, 2*HI+1 of w -> packed 16-bit pair, times 2^exponent(pow2_scale)
+template <int DT, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_16(uint32_t w, float pow2_scale) {
+    if constexpr (DT == kF16) {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, pow2_scale, HI));
+    } else {
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, pow2_scale, HI));
+    }
+}
+
+// 4 codes of w -> 2 packed 16-bit pairs
+template <int DT>
+__device__ __forceinline__ uint2 fp8x4_to_16(uint32_t w, float pow2_scale) {
+    return make_uint2(fp8x2_to_16<DT, false>(w, pow2_scale), fp8x2_to_16<DT, true>(w, pow2_scale));
+}
+
+// codes 2*HI, 2*HI+1 of w -> two float32 (exact)
+template <bool HI>
+__device__ __forceinline__ f32x2_t fp8x2_to_f32(uint32_t w) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+}
+
+// 1 <= mantissa factor < 2 with s = 2^e * factor (s positive, normal): the part
+// of a scale that the conversions above leave out
+__device__ __forceinline__ float scale_mantissa(float s) {
+    return __uint_as_float((__float_as_uint(s) & 0x007fffffu) | 0x3f800000u);
+}
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 

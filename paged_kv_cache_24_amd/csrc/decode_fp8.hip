@@ -1,0 +1,558 @@
+// Paged decode attention over an FP8 (OCP E4M3) KV cache on gfx950.
+//
+// What is computed ("vLLM-Ascend 原理", §四 on KV-cache quantisation, with
+// §2.4 step 3 for decode): the K/V rows are fetched through the block table as
+// 8-bit codes, dequantised on chip with their per-(token, kv head) float32
+// scale, and attended to exactly as in the 16-bit kernels of decode.hip:
+//     score_t = scale * k_scale_t * (q . code_k_t)
+//     out     = sum_t p_t * v_scale_t * code_v_t / sum_t p_t
+// The partition / merge structure, the softmax state and the workspace format
+// are those of the 16-bit kernels (the merge kernel is shared).  Half the
+// bytes per token leave HBM, so the same bandwidth carries twice the tokens.
+#include "common.h"
+#include "kernels.h"
+
+namespace pa {
+
+typedef uint32_t u32x4_f8 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const uint8_t* p) {
+    if constexpr (NT) {
+        const u32x4_f8 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_f8*>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+        return *reinterpret_cast<const uint4*>(p);
+    }
+}
+
+// 16 codes -> 8 packed 16-bit pairs, exact (scale 1)
+template <int DT>
+__device__ __forceinline__ void codes16_to_16bit(const uint4& c, uint4& lo, uint4& hi) {
+    const uint2 a = fp8x4_to_16<DT>(c.x, 1.f), b = fp8x4_to_16<DT>(c.y, 1.f);
+    const uint2 d = fp8x4_to_16<DT>(c.z, 1.f), e = fp8x4_to_16<DT>(c.w, 1.f);
+    lo = make_uint4(a.x, a.y, b.x, b.y);
+    hi = make_uint4(d.x, d.y, e.x, e.y);
+}
+
+// ---------------------------------------------------------------------------
+// Vector-ALU kernel (group <= 2, or head_dim 64).
+//
+// One wave owns one (sequence, kv head, q-head chunk, partition) item.  A
+// token row of one kv head is D bytes of codes; LPR = D/16 lanes each load
+// 16 of them with one 16-byte load, so a load instruction covers 64/LPR whole
+// rows.  Lane (r, c) owns the TPL consecutive tokens r*TPL .. r*TPL+TPL-1 of
+// every block: their scales are TPL consecutive floats, one small load.
+// QK^T: the codes become 16-bit pairs (exact) for v_dot2 against q, summed
+// over the row's lanes with DPP, then scaled by k_scale.  PV: codes become
+// float32 and meet p * v_scale in float32 FMAs.
+// ---------------------------------------------------------------------------
+template <int DT, int D, int HPW, bool NT>
+__global__ __launch_bounds__(256) void decode_fp8_partition_kernel(DecodeArgs a) {
+    constexpr int LPR = D / 16;             // lanes per token row
+    constexpr int RPW = kWave / LPR;        // token rows per load instruction
+    constexpr int TPL = kBlockSize / RPW;   // tokens per lane per block
+    constexpr int NBUF = 4;                 // blocks in registers: one computed, three in flight
+    static_assert(TPL == 1 || TPL == 2, "head_dim 64 or 128");
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int r = lane / LPR;
+    const int c = lane % LPR;
+
+    const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.head_chunks;
+    const int64_t item = (int64_t)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
+    if (item >= units * a.num_parts) return;
+    const int part = (int)(item / units);
+    int64_t u = item - (int64_t)part * units;
+    const int hc = (int)(u % a.head_chunks);
+    u /= a.head_chunks;
+    const int g = (int)(u % a.num_kv_heads);
+    const int b = (int)(u / a.num_kv_heads);
+
+    const int max_tokens = a.max_blocks_per_seq * kBlockSize;
+    int n = a.seq_lens[b];
+    n = n < 0 ? 0 : (n > max_tokens ? max_tokens : n);
+    const int nblk = (n + kBlockSize - 1) / kBlockSize;
+    const int nparts = nblk <= a.part_blocks ? 1 : (nblk + a.part_blocks - 1) / a.part_blocks;
+    if (part >= nparts) return;
+    const int j0 = part * a.part_blocks;
+    const int j1 = min(nblk, j0 + a.part_blocks);
+
+    const int hbase = hc * HPW;
+    const int hcount = min(HPW, a.group - hbase);
+    const int64_t q_row0 = (int64_t)b * a.num_q_heads + (int64_t)g * a.group + hbase;
+
+    uint4 qv[HPW][2];   // q elements 16c .. 16c+15 of each head
+    {
+        const uint16_t* q = static_cast<const uint16_t*>(a.q) + q_row0 * D + 16 * c;
+#pragma unroll
+        for (int h = 0; h < HPW; ++h) {
+            const bool live = h < hcount;
+            qv[h][0] = live ? *reinterpret_cast<const uint4*>(q + (int64_t)h * D) : make_uint4(0, 0, 0, 0);
+            qv[h][1] = live ? *reinterpret_cast<const uint4*>(q + (int64_t)h * D + 8) : make_uint4(0, 0, 0, 0);
+        }
+    }
+
+    float m[HPW], l[HPW], acc[HPW][16];
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[h][e] = 0.f;
+    }
+
+    const int64_t row_stride = (int64_t)a.num_kv_heads * D;   // bytes between token rows
+    const int64_t lane_off = (int64_t)g * D + 16 * c + (int64_t)(r * TPL) * row_stride;
+    const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache) + lane_off;
+    const uint8_t* vbase = static_cast<const uint8_t*>(a.v_cache) + lane_off;
+    const float* ksb = a.k_scales + (int64_t)g * kBlockSize + r * TPL;
+    const float* vsb = a.v_scales + (int64_t)g * kBlockSize + r * TPL;
+    const int64_t scale_block_stride = (int64_t)a.num_kv_heads * kBlockSize;
+    const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
+    const float cs = a.scale_log2;
+
+    struct Buf {
+        uint4 k[TPL], v[TPL];
+        float ks[TPL], vs[TPL];
+        bool ok;
+    };
+
+    auto load = [&](int j, Buf& buf) {
+        const int pb = table[j];
+        buf.ok = pb >= 0 && (int64_t)pb < a.num_blocks;
+        const int64_t blk = buf.ok ? pb : 0;
+        const int64_t off = blk * kBlockSize * row_stride;
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            buf.k[i] = load16<NT>(kbase + off + (int64_t)i * row_stride);
+            buf.v[i] = load16<NT>(vbase + off + (int64_t)i * row_stride);
+        }
+        if constexpr (TPL == 2) {
+            const float2 ks = *reinterpret_cast<const float2*>(ksb + blk * scale_block_stride);
+            const float2 vs = *reinterpret_cast<const float2*>(vsb + blk * scale_block_stride);
+            buf.ks[0] = ks.x; buf.ks[1] = ks.y;
+            buf.vs[0] = vs.x; buf.vs[1] = vs.y;
+        } else {
+            buf.ks[0] = ksb[blk * scale_block_stride];
+            buf.vs[0] = vsb[blk * scale_block_stride];
+        }
+    };
+
+    auto process = [&](const Buf& buf, int j) {
+        const bool full = buf.ok && (j + 1) * kBlockSize <= n;
+        bool valid[TPL];
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) valid[i] = full || (buf.ok && j * kBlockSize + r * TPL + i < n);
+
+        float s[HPW][TPL];
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            uint4 k0, k1;
+            codes16_to_16bit<DT>(buf.k[i], k0, k1);
+            const float ksc = buf.ks[i] * cs;
+#pragma unroll
+            for (int h = 0; h < HPW; ++h) {
+                const float d = dot8<DT>(qv[h][0], k0) + dot8<DT>(qv[h][1], k1);
+                float t;
+                if constexpr (LPR == 8) t = group_sum<8>(d);
+                else t = quad_sum(d);
+                // rows past the end or in a bad block: -inf (a select, so NaN
+                // codes or scales there cannot leak)
+                s[h][i] = valid[i] ? t * ksc : -INFINITY;
+            }
+        }
+        float vf[TPL][16];
+        float vsc[TPL];
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            const uint32_t w[4] = {buf.v[i].x, buf.v[i].y, buf.v[i].z, buf.v[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const f32x2_t lo = fp8x2_to_f32<false>(w[e]);
+                const f32x2_t hi = fp8x2_to_f32<true>(w[e]);
+                vf[i][4 * e] = valid[i] ? lo.x : 0.f;
+                vf[i][4 * e + 1] = valid[i] ? lo.y : 0.f;
+                vf[i][4 * e + 2] = valid[i] ? hi.x : 0.f;
+                vf[i][4 * e + 3] = valid[i] ? hi.y : 0.f;
+            }
+            vsc[i] = valid[i] ? buf.vs[i] : 0.f;
+        }
+#pragma unroll
+        for (int h = 0; h < HPW; ++h) {
+            float mb = s[h][0];
+#pragma unroll
+            for (int i = 1; i < TPL; ++i) mb = fmaxf(mb, s[h][i]);
+            const float mn = fmaxf(m[h], mb);
+            const float mu = mn == -INFINITY ? 0.f : mn;
+            const float alpha = fast_exp2(m[h] - mu);
+            float pv[TPL];
+            float ps = 0.f;
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                const float p = fast_exp2(s[h][i] - mu);
+                ps += p;
+                pv[i] = p * vsc[i];
+            }
+            l[h] = fmaf(l[h], alpha, ps);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float x = acc[h][e] * alpha;
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) x = fmaf(pv[i], vf[i][e], x);
+                acc[h][e] = x;
+            }
+            m[h] = mn;
+        }
+    };
+
+    // NBUF register buffers: while one block is computed, NBUF-1 are in flight
+    if (j0 < j1) {
+        Buf buf[NBUF];
+#pragma unroll
+        for (int s = 0; s < NBUF - 1; ++s)
+            if (j0 + s < j1) load(j0 + s, buf[s]);
+        for (int j = j0; j < j1; j += NBUF) {
+#pragma unroll
+            for (int s = 0; s < NBUF; ++s) {
+                if (j + s >= j1) break;
+                if (j + s + NBUF - 1 < j1) load(j + s + NBUF - 1, buf[(s + NBUF - 1) % NBUF]);
+                process(buf[s], j + s);
+            }
+        }
+    }
+
+    // merge the row groups' states: rescale to the common max, then sum
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+        float big = m[h];
+#pragma unroll
+        for (int off = LPR; off < kWave; off <<= 1) big = fmaxf(big, __shfl_xor(big, off));
+        const float w = m[h] == -INFINITY ? 0.f : fast_exp2(m[h] - big);
+        float lt = l[h] * w;
+#pragma unroll
+        for (int off = LPR; off < kWave; off <<= 1) lt += __shfl_xor(lt, off);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            float x = acc[h][e] * w;
+#pragma unroll
+            for (int off = LPR; off < kWave; off <<= 1) x += __shfl_xor(x, off);
+            acc[h][e] = x;
+        }
+        m[h] = big;
+        l[h] = lt;
+    }
+
+    if (r != 0) return;
+    if (nparts == 1) {
+#pragma unroll
+        for (int h = 0; h < HPW; ++h) {
+            if (h >= hcount) break;
+            const float inv = l[h] > 0.f ? 1.f / l[h] : 0.f;
+            uint4 o0, o1;
+            o0.x = pack2<DT>(acc[h][0] * inv, acc[h][1] * inv);
+            o0.y = pack2<DT>(acc[h][2] * inv, acc[h][3] * inv);
+            o0.z = pack2<DT>(acc[h][4] * inv, acc[h][5] * inv);
+            o0.w = pack2<DT>(acc[h][6] * inv, acc[h][7] * inv);
+            o1.x = pack2<DT>(acc[h][8] * inv, acc[h][9] * inv);
+            o1.y = pack2<DT>(acc[h][10] * inv, acc[h][11] * inv);
+            o1.z = pack2<DT>(acc[h][12] * inv, acc[h][13] * inv);
+            o1.w = pack2<DT>(acc[h][14] * inv, acc[h][15] * inv);
+            uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + (q_row0 + h) * D + 16 * c);
+            dst[0] = o0;
+            dst[1] = o1;
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < HPW; ++h) {
+            if (h >= hcount) break;
+            const int64_t idx = (q_row0 + h) * a.num_parts + part;
+            float4* dst = reinterpret_cast<float4*>(a.ws_acc + idx * D + 16 * c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dst[e] = make_float4(acc[h][4 * e], acc[h][4 * e + 1], acc[h][4 * e + 2], acc[h][4 * e + 3]);
+            if (c == 0) a.ws_ml[idx] = make_float2(m[h], l[h]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// GQA kernel (head_dim 128, 3..16 q heads per kv head): both products on
+// matrix cores, as in decode.hip, with the codes widened on the way in.
+//   S^T = K Q^T: MFMA 16x16x32 x 4.  Lane (lr, lg) feeds token lr of the block
+//        and head_dim elements 32*lg + 8*kk .. +8 for step kk (the order of the
+//        head_dim sum is free as long as Q uses the same one): two 16-byte
+//        loads of 16 codes, widened exactly to 16-bit.  Lane l then holds the
+//        scores of tokens 4*lg + i (i = 0..3) for head lr, so their k/v scales
+//        are one 16-byte load each.
+//   O^T += V^T P^T: MFMA 16x16x16 x 8 from a per-wave LDS tile of V.  The V
+//        codes are widened times 2^e (e = exponent of the token's v_scale, exact
+//        in 16 bits) and the mantissa factor in [1, 2) of v_scale multiplies the
+//        probabilities, so P never meets a tiny scale in 16-bit precision; P
+//        enters as a 16-bit head and tail, two MFMAs, so the factor adds no
+//        rounding of its own.
+//        Lane (lr, lg) loads tokens 4*lg + (lr/8) and 4*lg + 2 + (lr/8), codes
+//        16*(lr%8) .. +16: tokens among its own four, whose scales it holds.
+//        The transposed LDS read (ds_read_b64_tr_b16) at row 4*lg + lr/4,
+//        column 4*(lr%4) hands lane (lr, lg) the four tokens 4*lg + j of
+//        head_dim element lr: the A operand that matches P^T.
+// ---------------------------------------------------------------------------
+typedef __bf16 f8bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 f8bf16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f8f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f8f16x4_t __attribute__((ext_vector_type(4)));
+typedef float f8f32x4_t __attribute__((ext_vector_type(4)));
+typedef short f8s16x4_t __attribute__((ext_vector_type(4)));
+
+template <int DT>
+__device__ __forceinline__ f8f32x4_t f8_mfma_16x16x32(const uint4& a, const uint4& b, f8f32x4_t c) {
+    if constexpr (DT == kF16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f8f16x8_t, a),
+                                                      __builtin_bit_cast(f8f16x8_t, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(f8bf16x8_t, a),
+                                                       __builtin_bit_cast(f8bf16x8_t, b), c, 0, 0, 0);
+    }
+}
+template <int DT>
+__device__ __forceinline__ f8f32x4_t f8_mfma_16x16x16(const uint2& a, const uint2& b, f8f32x4_t c) {
+    if constexpr (DT == kF16) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f8f16x4_t, a),
+                                                     __builtin_bit_cast(f8f16x4_t, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(f8bf16x4_t, a),
+                                                         __builtin_bit_cast(f8bf16x4_t, b), c, 0, 0, 0);
+    }
+}
+
+constexpr int kVRowF8 = 144;   // LDS row stride of the widened V tile (16-bit elements)
+
+template <int DT, bool NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void decode_fp8_gqa_kernel(DecodeArgs a) {
+    constexpr int D = 128;
+    __shared__ __attribute__((aligned(16))) uint16_t vlds[4][kBlockSize * kVRowF8];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uniform(threadIdx.x >> 6);
+    const int lr = lane & 15;    // MFMA column = q head; token of the K rows; V^T row
+    const int lg = lane >> 4;    // tokens 4*lg .. 4*lg+3 of each block
+    uint16_t* vt = vlds[wave];
+
+    const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.head_chunks;
+    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
+    if (item >= units * a.num_parts) return;
+    const int part = (int)(item / units);
+    int64_t u = item - (int64_t)part * units;
+    const int hc = (int)(u % a.head_chunks);
+    u /= a.head_chunks;
+    const int g = (int)(u % a.num_kv_heads);
+    const int b = (int)(u / a.num_kv_heads);
+
+    const int max_tokens = a.max_blocks_per_seq * kBlockSize;
+    int n = a.seq_lens[b];
+    n = n < 0 ? 0 : (n > max_tokens ? max_tokens : n);
+    const int nblk = (n + kBlockSize - 1) / kBlockSize;
+    const int nparts = nblk <= a.part_blocks ? 1 : (nblk + a.part_blocks - 1) / a.part_blocks;
+    if (part >= nparts) return;
+    const int j0 = part * a.part_blocks;
+    const int j1 = min(nblk, j0 + a.part_blocks);
+    const int hcount = min(16, a.group - hc * 16);
+    const int64_t q_row0 = (int64_t)b * a.num_q_heads + (int64_t)g * a.group + hc * 16;
+    const bool head_live = lr < hcount;
+
+    uint4 qf[4];   // head lr, elements 32*lg + 8*kk .. +8
+    {
+        const uint16_t* q = static_cast<const uint16_t*>(a.q) + (q_row0 + (head_live ? lr : 0)) * D + 32 * lg;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            qf[kk] = head_live ? *reinterpret_cast<const uint4*>(q + 8 * kk) : make_uint4(0, 0, 0, 0);
+    }
+
+    float m = -INFINITY;   // running max of head lr (same in lanes l, l^16, l^32, l^48)
+    float l = 0.f;         // this lane's share of the running sum
+    f8f32x4_t o[8];        // O^T: lane holds elements 16*mt + 4*lg + i of head lr
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) o[mt] = f8f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t row_stride = (int64_t)a.num_kv_heads * D;   // bytes
+    const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache) + (int64_t)g * D + 32 * lg +
+                           (int64_t)lr * row_stride;
+    const int vrow0 = 4 * lg + (lr >> 3);      // V rows of this lane: vrow0 and vrow0 + 2
+    const uint8_t* vbase = static_cast<const uint8_t*>(a.v_cache) + (int64_t)g * D + 16 * (lr & 7) +
+                           (int64_t)vrow0 * row_stride;
+    const float* ksb = a.k_scales + (int64_t)g * kBlockSize + 4 * lg;
+    const float* vsb = a.v_scales + (int64_t)g * kBlockSize + 4 * lg;
+    const int64_t scale_block_stride = (int64_t)a.num_kv_heads * kBlockSize;
+    const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
+    const float cs = a.scale_log2;
+    const uint16_t* vtr = vt + (4 * lg + (lr >> 2)) * kVRowF8 + 4 * (lr & 3);
+
+    struct Buf {
+        uint4 k[2], v[2];
+        float4 ks, vs;
+        bool ok;
+    };
+
+    auto load = [&](int j, Buf& buf) {
+        const int pb = table[j];
+        buf.ok = pb >= 0 && (int64_t)pb < a.num_blocks;
+        const int64_t blk = buf.ok ? pb : 0;
+        const int64_t off = blk * kBlockSize * row_stride;
+        buf.k[0] = load16<NT>(kbase + off);
+        buf.k[1] = load16<NT>(kbase + off + 16);
+        buf.v[0] = load16<NT>(vbase + off);
+        buf.v[1] = load16<NT>(vbase + off + 2 * row_stride);
+        buf.ks = *reinterpret_cast<const float4*>(ksb + blk * scale_block_stride);
+        buf.vs = *reinterpret_cast<const float4*>(vsb + blk * scale_block_stride);
+    };
+
+    auto process = [&](const Buf& buf, int j) {
+        f8f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const uint4& w = buf.k[kk >> 1];
+            const uint32_t w0 = (kk & 1) ? w.z : w.x;
+            const uint32_t w1 = (kk & 1) ? w.w : w.y;
+            const uint2 e0 = fp8x4_to_16<DT>(w0, 1.f), e1 = fp8x4_to_16<DT>(w1, 1.f);
+            sacc = f8_mfma_16x16x32<DT>(make_uint4(e0.x, e0.y, e1.x, e1.y), qf[kk], sacc);
+        }
+        const float ks[4] = {buf.ks.x, buf.ks.y, buf.ks.z, buf.ks.w};
+        const float vs[4] = {buf.vs.x, buf.vs.y, buf.vs.z, buf.vs.w};
+        const bool full = buf.ok && (j + 1) * kBlockSize <= n;
+        bool valid[4];
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            valid[i] = full || (buf.ok && (j * kBlockSize + 4 * lg + i < n));
+            x[i] = valid[i] ? sacc[i] * (ks[i] * cs) : -INFINITY;
+        }
+        float mb = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        mb = fmaxf(mb, __shfl_xor(mb, 16));
+        mb = fmaxf(mb, __shfl_xor(mb, 32));
+        // raise the running max only when this block beats it by more than 2^8:
+        // otherwise keep it (p <= 256, exact algebra) and skip the rescale of O^T
+        const bool raise = mb > m + 8.f;   // also true on the first live block
+        const float mn = raise ? mb : m;
+        if (__any(raise)) {
+            const float alpha = raise ? fast_exp2(m - mn) : 1.f;   // exp2(-inf) = 0
+            l *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) o[mt] *= alpha;
+        }
+        m = mn;
+        const float mu = mn == -INFINITY ? 0.f : mn;
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - mu);
+        l += (p[0] + p[1]) + (p[2] + p[3]);
+        // V tile to LDS, widened times 2^exponent(v_scale); rows past the
+        // sequence end as zeros (MFMA would turn 0 x NaN into NaN)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int row = vrow0 + 2 * k;
+            const int sel = (lr >> 3) + 2 * k;
+            const float vsr = sel == 0 ? vs[0] : sel == 1 ? vs[1] : sel == 2 ? vs[2] : vs[3];
+            const bool ok = full || (buf.ok && (j * kBlockSize + row < n));
+            const uint4& w = buf.v[k];
+            const uint2 e0 = fp8x4_to_16<DT>(w.x, vsr), e1 = fp8x4_to_16<DT>(w.y, vsr);
+            const uint2 e2 = fp8x4_to_16<DT>(w.z, vsr), e3 = fp8x4_to_16<DT>(w.w, vsr);
+            uint4* dst = reinterpret_cast<uint4*>(vt + row * kVRowF8 + 16 * (lr & 7));
+            dst[0] = ok ? make_uint4(e0.x, e0.y, e1.x, e1.y) : make_uint4(0, 0, 0, 0);
+            dst[1] = ok ? make_uint4(e2.x, e2.y, e3.x, e3.y) : make_uint4(0, 0, 0, 0);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // P^T = p * mantissa(v_scale) as a 16-bit head plus a 16-bit tail
+        // (p * mu - head): two MFMAs carry ~16 significant bits of P, so the
+        // widening of the scale costs no precision next to the 16-bit cache
+        float pm[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pm[i] = valid[i] ? p[i] * scale_mantissa(vs[i]) : 0.f;
+        uint2 ph, pt;
+        ph.x = pack2<DT>(pm[0], pm[1]);
+        ph.y = pack2<DT>(pm[2], pm[3]);
+        pt.x = pack2<DT>(pm[0] - lo_to_f32<DT>(ph.x), pm[1] - hi_to_f32<DT>(ph.x));
+        pt.y = pack2<DT>(pm[2] - lo_to_f32<DT>(ph.y), pm[3] - hi_to_f32<DT>(ph.y));
+        uint2 va[8];
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+            va[mt] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (f8s16x4_t __attribute__((address_space(3)))*)(vtr + 16 * mt)));
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) o[mt] = f8_mfma_16x16x16<DT>(va[mt], ph, o[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) o[mt] = f8_mfma_16x16x16<DT>(va[mt], pt, o[mt]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    if (j0 < j1) {
+        Buf cur;
+        load(j0, cur);
+        for (int j = j0; j < j1; ++j) {
+            Buf nxt;
+            nxt.ok = false;
+            if (j + 1 < j1) load(j + 1, nxt);   // next block in flight
+            process(cur, j);
+            cur = nxt;
+        }
+    }
+
+    float lt = l + __shfl_xor(l, 16);
+    lt += __shfl_xor(lt, 32);
+    if (!head_live) return;
+    if (nparts == 1) {
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        uint16_t* dst = static_cast<uint16_t*>(a.out) + (q_row0 + lr) * D + 4 * lg;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            uint2 w;
+            w.x = pack2<DT>(o[mt][0] * inv, o[mt][1] * inv);
+            w.y = pack2<DT>(o[mt][2] * inv, o[mt][3] * inv);
+            *reinterpret_cast<uint2*>(dst + 16 * mt) = w;
+        }
+    } else {
+        const int64_t idx = (q_row0 + lr) * a.num_parts + part;
+        float* dst = a.ws_acc + idx * D + 4 * lg;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+            *reinterpret_cast<float4*>(dst + 16 * mt) = make_float4(o[mt][0], o[mt][1], o[mt][2], o[mt][3]);
+        if (lg == 0) a.ws_ml[idx] = make_float2(m, lt);
+    }
+}
+
+template <int DT, int D, bool NT>
+static hipError_t launch_fp8_vector(const DecodeArgs& a, hipStream_t s, dim3 grid) {
+    switch (a.heads_per_wave) {
+        case 1: hipLaunchKernelGGL((decode_fp8_partition_kernel<DT, D, 1, NT>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_fp8_partition_kernel<DT, D, 2, NT>), grid, dim3(256), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_fp8_partition_kernel<DT, D, 4, NT>), grid, dim3(256), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int DT, bool NT>
+static hipError_t launch_fp8_t(const DecodeArgs& a, hipStream_t s, dim3 grid) {
+    if (a.gqa_mfma) {
+        hipLaunchKernelGGL((decode_fp8_gqa_kernel<DT, NT>), grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
+    return a.head_dim == 128 ? launch_fp8_vector<DT, 128, NT>(a, s, grid)
+                             : launch_fp8_vector<DT, 64, NT>(a, s, grid);
+}
+
+hipError_t launch_decode_partitions_fp8(const DecodeArgs& a, hipStream_t s) {
+    const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * a.head_chunks * a.num_parts;
+    if (items == 0) return hipSuccess;
+    const int64_t wgs = (items + 3) / 4;
+    if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)wgs);
+    if (a.dtype == kF16) {
+        return a.stream_kv ? launch_fp8_t<kF16, true>(a, s, grid) : launch_fp8_t<kF16, false>(a, s, grid);
+    }
+    return a.stream_kv ? launch_fp8_t<kBF16, true>(a, s, grid) : launch_fp8_t<kBF16, false>(a, s, grid);
+}
+
+}  // namespace pa

@@ -20,6 +20,24 @@ struct ReshapeArgs {
 };
 hipError_t launch_reshape_and_cache(const ReshapeArgs& a, hipStream_t stream);
 
+// Cache write into an FP8 (E4M3) cache: per (token, kv head) row, scale =
+// amax / 448 and codes = e4m3(x / scale).
+struct ReshapeFp8Args {
+    const void* key;
+    const void* value;
+    uint8_t* k_cache;        // [NB][16][Hkv][D] codes
+    uint8_t* v_cache;
+    float* k_scales;         // [NB][Hkv][16]
+    float* v_scales;
+    const int64_t* slot_mapping;
+    int64_t num_tokens;
+    int64_t num_slots;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t dtype;           // type of key / value
+};
+hipError_t launch_reshape_and_cache_fp8(const ReshapeFp8Args& a, hipStream_t stream);
+
 struct CopyBlocksArgs {
     void* k_cache;
     void* v_cache;
@@ -55,8 +73,12 @@ struct DecodeArgs {
     float scale_log2;        // softmax scale times log2(e)
     int32_t dtype;
     int32_t stream_kv;       // 1: no block is read twice in this call; stream K/V
+    // FP8 cache only: per (block, kv head, token) float32 scales
+    const float* k_scales;   // [NB][Hkv][16]
+    const float* v_scales;
 };
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_partitions_fp8(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
 
 struct PrefillArgs {

@@ -109,6 +109,8 @@ pa::DecodeArgs decode_args(void* out, const void* q, const void* k_cache, const 
     // 3 or more q heads per kv head make QK^T and PV real contractions: matrix cores
     a.gqa_mfma = uses_gqa_kernel(num_q_heads, num_kv_heads, head_dim);
     a.heads_per_wave = a.gqa_mfma ? 16 : heads_per_wave(a.group);
+    a.k_scales = nullptr;
+    a.v_scales = nullptr;
     a.head_chunks = ceil_div(a.group, a.heads_per_wave);
     a.head_dim = head_dim;
     a.max_blocks_per_seq = max_blocks_per_seq;
@@ -198,6 +200,64 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pair
     return pa::launch_copy_blocks(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
+pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache,
+                                   void* v_cache, float* k_scales, float* v_scales,
+                                   const int64_t* slot_mapping, int64_t num_tokens,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int64_t num_blocks, pa_dtype dtype, hipStream_t stream) {
+    if (!supported_dtype(dtype) || block_size != PA_BLOCK_SIZE || (head_dim != 64 && head_dim != 128))
+        return PA_ERR_UNSUPPORTED;
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+    if (num_tokens == 0) return PA_OK;
+    if (!key || !value || !k_cache || !v_cache || !k_scales || !v_scales || !slot_mapping)
+        return PA_ERR_NULL_PTR;
+    if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        !aligned16(k_scales) || !aligned16(v_scales))
+        return PA_ERR_ALIGNMENT;
+    pa::ReshapeFp8Args a;
+    a.key = key;
+    a.value = value;
+    a.k_cache = static_cast<uint8_t*>(k_cache);
+    a.v_cache = static_cast<uint8_t*>(v_cache);
+    a.k_scales = k_scales;
+    a.v_scales = v_scales;
+    a.slot_mapping = slot_mapping;
+    a.num_tokens = num_tokens;
+    a.num_slots = num_blocks * PA_BLOCK_SIZE;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.dtype = dtype == PA_F16 ? pa::kF16 : pa::kBF16;
+    return pa::launch_reshape_and_cache_fp8(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_copy_blocks_fp8(void* k_cache, void* v_cache, float* k_scales, float* v_scales,
+                             const int64_t* block_pairs, int64_t num_pairs, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                             hipStream_t stream) {
+    if (block_size != PA_BLOCK_SIZE || (head_dim != 64 && head_dim != 128)) return PA_ERR_UNSUPPORTED;
+    if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+    if (num_pairs == 0) return PA_OK;
+    if (!k_cache || !v_cache || !k_scales || !v_scales || !block_pairs) return PA_ERR_NULL_PTR;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_scales) || !aligned16(v_scales))
+        return PA_ERR_ALIGNMENT;
+    // the copy kernel moves 16-byte vectors: a code block is 16 * Hkv * D bytes,
+    // a scale block 16 * Hkv floats
+    pa::CopyBlocksArgs a;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_pairs = block_pairs;
+    a.num_pairs = num_pairs;
+    a.num_blocks = num_blocks;
+    a.block_vecs = (int64_t)num_kv_heads * head_dim;
+    a.wgs_per_pair = (a.block_vecs + 1023) / 1024;
+    if (pa::launch_copy_blocks(a, stream) != hipSuccess) return PA_ERR_HIP;
+    a.k_cache = k_scales;
+    a.v_cache = v_scales;
+    a.block_vecs = (int64_t)num_kv_heads * 4;
+    a.wgs_per_pair = (a.block_vecs + 1023) / 1024;
+    return pa::launch_copy_blocks(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 int32_t pa_decode_default_partition(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                     int32_t max_blocks_per_seq) {
     if (num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0) return 256;
@@ -261,6 +321,57 @@ pa_status pa_decode_merge(void* out, const int32_t* seq_lens, int32_t num_seqs,
                                          max_blocks_per_seq, 1, 1.f, dtype, shape,
                                          const_cast<void*>(workspace), 0u);
     return pa::launch_decode_merge(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_decode_partitions_fp8(void* out, const void* q, const void* k_cache,
+                                   const void* v_cache, const float* k_scales,
+                                   const float* v_scales, const int32_t* block_tables,
+                                   const int32_t* seq_lens, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t max_blocks_per_seq,
+                                   int64_t num_blocks, float scale, pa_dtype dtype,
+                                   int32_t partition_tokens, uint32_t flags, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+    if (flags & ~PA_DECODE_STREAM_KV) return PA_ERR_UNSUPPORTED;
+    pa_status st = check_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+                                num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_blocks_per_seq, num_blocks, scale, dtype, partition_tokens);
+    if (st != PA_OK || num_seqs == 0) return st;
+    if (!k_scales || !v_scales) return PA_ERR_NULL_PTR;
+    if (!aligned16(k_scales) || !aligned16(v_scales)) return PA_ERR_ALIGNMENT;
+    const DecodeShape shape = decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                           max_blocks_per_seq, partition_tokens);
+    st = check_workspace(shape, workspace, workspace_bytes);
+    if (st != PA_OK) return st;
+    pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+                                   num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                                   num_blocks, scale, dtype, shape, workspace, flags);
+    if (!a.gqa_mfma && a.heads_per_wave > 4) {   // the FP8 vector kernel carries up to 4 heads
+        a.heads_per_wave = 4;
+        a.head_chunks = ceil_div(a.group, 4);
+    }
+    a.k_scales = k_scales;
+    a.v_scales = v_scales;
+    return pa::launch_decode_partitions_fp8(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                        const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                        pa_dtype dtype, int32_t partition_tokens, uint32_t flags,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    pa_status st = pa_decode_partitions_fp8(out, q, k_cache, v_cache, k_scales, v_scales,
+                                            block_tables, seq_lens, num_seqs, num_q_heads,
+                                            num_kv_heads, head_dim, block_size,
+                                            max_blocks_per_seq, num_blocks, scale, dtype,
+                                            partition_tokens, flags, workspace, workspace_bytes,
+                                            stream);
+    if (st != PA_OK || num_seqs == 0) return st;
+    return pa_decode_merge(out, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                           block_size, max_blocks_per_seq, dtype, partition_tokens, workspace,
+                           workspace_bytes, stream);
 }
 
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

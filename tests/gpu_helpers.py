@@ -98,3 +98,63 @@ def assert_close(got64: np.ndarray, ref64: np.ndarray, dtype: str, what: str = "
     assert worst <= TOL[dtype], (
         f"{what}: max-abs error {worst:.3e} > {TOL[dtype]} (max |ref| {np.abs(ref64).max():.3f})")
     return worst
+
+
+def live_slots(block_tables: np.ndarray, lens: np.ndarray) -> np.ndarray:
+    """Sorted distinct slots of every token the sequences hold (shared
+    blocks counted once)."""
+    out = []
+    for b in range(block_tables.shape[0]):
+        p = np.arange(int(lens[b]))
+        out.append(block_tables[b, p // 16].astype(np.int64) * 16 + p % 16)
+    return np.unique(np.concatenate(out)) if out else np.zeros(0, np.int64)
+
+
+class Fp8DecodeOnGPU:
+    """A decode workload over an FP8 cache: the 16-bit pools of a DecodeCase
+    (after its cache write) give the k/v of every live token, which the FP8
+    cache write quantises into code pools that start as NaN codes (0x7F) with
+    NaN scales, so nothing unwritten can go unnoticed."""
+
+    def __init__(self, case, slots=None):
+        import oracle
+        self.case = case
+        dt = case.dtype
+        kc16, vc16 = oracle.ref_reshape_and_cache(case.key, case.value, case.k_cache, case.v_cache,
+                                                  case.slot_mapping)
+        self.slots_np = live_slots(case.block_tables, case.seq_lens) if slots is None else slots
+        blk, off = self.slots_np // 16, self.slots_np % 16
+        self.key_np = np.ascontiguousarray(kc16[blk, off])
+        self.value_np = np.ascontiguousarray(vc16[blk, off])
+        nb, hkv, d = case.num_blocks, case.num_kv_heads, case.head_dim
+        self.codes0 = np.full((nb, 16, hkv, d), 0x7F, np.uint8)
+        self.scales0 = np.full((nb, hkv, 16), np.nan, np.float32)
+        self.q = dev_bits(case.q, dt)
+        self.key = dev_bits(self.key_np, dt)
+        self.value = dev_bits(self.value_np, dt)
+        self.slots = dev_int(self.slots_np, torch.int64)
+        self.k_cache = torch.from_numpy(self.codes0).cuda()
+        self.v_cache = torch.from_numpy(self.codes0).cuda()
+        self.k_scales = torch.from_numpy(self.scales0).cuda()
+        self.v_scales = torch.from_numpy(self.scales0).cuda()
+        self.tables = dev_int(case.block_tables)
+        self.lens = dev_int(case.seq_lens)
+        self.out = torch.empty_like(self.q)
+
+    def write(self):
+        import paged_kv_cache_24_amd as pa
+        pa.pa_reshape_and_cache_fp8(self.key, self.value, self.k_cache, self.v_cache, self.k_scales,
+                                    self.v_scales, self.slots)
+
+    def oracle_pools(self):
+        import oracle
+        return oracle.ref_reshape_and_cache_fp8(self.key_np, self.value_np, self.codes0, self.codes0,
+                                                self.scales0, self.scales0, self.slots_np,
+                                                self.case.dtype)
+
+    def decode(self, partition_tokens=0, out=None, flags=0):
+        import paged_kv_cache_24_amd as pa
+        out = self.out if out is None else out
+        pa.pa_decode_fp8(out, self.q, self.k_cache, self.v_cache, self.k_scales, self.v_scales,
+                         self.tables, self.lens, self.case.scale, partition_tokens, flags=flags)
+        return out

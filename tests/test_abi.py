@@ -31,7 +31,9 @@ def test_header_declares_the_calls():
     names = _declared()
     for n in ["pa_reshape_and_cache", "pa_decode", "pa_prefill_paged", "pa_decode_workspace_size",
               "pa_kv_bytes_per_token", "pa_status_string", "pa_decode_partitions",
-              "pa_decode_merge", "pa_decode_default_partition", "pa_copy_blocks"]:
+              "pa_decode_merge", "pa_decode_default_partition", "pa_copy_blocks",
+              "pa_reshape_and_cache_fp8", "pa_copy_blocks_fp8", "pa_decode_fp8",
+              "pa_decode_partitions_fp8"]:
         assert n in names
 
 
@@ -178,3 +180,67 @@ def test_copy_blocks_rejects(lib):
     assert call(nb=0) == SHAPE
     assert call(kc=FAKE + 4) == ALIGN
     assert call(n=0, pairs=None) == PA_OK
+
+
+def test_reshape_fp8_rejects(lib):
+    f = lib.pa_reshape_and_cache_fp8
+    f.restype = ctypes.c_int32
+    f.argtypes = [P, P, P, P, P, P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, P]
+
+    def call(key=FAKE, value=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, slots=FAKE, n=4, hkv=2,
+             d=128, bs=16, nb=8, dt=BF16):
+        return f(key, value, kc, vc, ks, vs, slots, n, hkv, d, bs, nb, dt, None)
+    assert call(ks=None) == NULL
+    assert call(vs=None) == NULL
+    assert call(slots=None) == NULL
+    assert call(d=96) == UNSUP
+    assert call(dt=3) == UNSUP
+    assert call(bs=32) == UNSUP
+    assert call(n=-1) == SHAPE
+    assert call(ks=FAKE + 4) == ALIGN
+    assert call(kc=FAKE + 8) == ALIGN
+    assert call(n=0, key=None) == PA_OK
+
+
+def test_copy_blocks_fp8_rejects(lib):
+    f = lib.pa_copy_blocks_fp8
+    f.restype = ctypes.c_int32
+    f.argtypes = [P, P, P, P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int64, P]
+
+    def call(kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, pairs=FAKE, n=3, hkv=8, d=128, bs=16, nb=32):
+        return f(kc, vc, ks, vs, pairs, n, hkv, d, bs, nb, None)
+    assert call(vs=None) == NULL
+    assert call(pairs=None) == NULL
+    assert call(d=32) == UNSUP
+    assert call(n=-1) == SHAPE
+    assert call(ks=FAKE + 4) == ALIGN
+    assert call(n=0, pairs=None) == PA_OK
+
+
+@pytest.mark.parametrize("fn", ["pa_decode_fp8", "pa_decode_partitions_fp8"])
+def test_decode_fp8_rejects(lib, fn):
+    f = getattr(lib, fn)
+    f.restype = ctypes.c_int32
+    f.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32, P, ctypes.c_size_t, P]
+
+    def call(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, sl=FAKE, b=2, hq=8,
+             hkv=2, d=128, bs=16, mb=64, nb=128, scale=0.1, dt=BF16, part=0, flags=0, ws=FAKE,
+             wsb=1 << 30):
+        return f(out, q, kc, vc, ks, vs, bt, sl, b, hq, hkv, d, bs, mb, nb, scale, dt, part, flags,
+                 ws, wsb, None)
+    assert call(ks=None) == NULL
+    assert call(vs=None) == NULL
+    assert call(q=None) == NULL
+    assert call(d=80) == UNSUP
+    assert call(dt=2) == UNSUP
+    assert call(flags=4) == UNSUP
+    assert call(hq=34, hkv=2) == SHAPE
+    assert call(scale=0.0) == SHAPE
+    assert call(part=24) == SHAPE
+    assert call(vs=FAKE + 4) == ALIGN
+    assert call(b=0, ks=None) == PA_OK
+    assert call(part=256, ws=None) == WS
