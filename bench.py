@@ -13,7 +13,8 @@ the dominant kernel (the decode partition kernel, timed with HIP events on
 the stream it runs on), a ``cpu_baseline`` object (the float64 oracle on a
 bounded sample of the same workload, on this host's cores) and
 ``secondary`` measurements of the other workloads (GQA + shared prefix,
-chunked prefill, long-context split-KV, tiny decode).
+chunked prefill, long-context split-KV, tiny decode, block copy) and of the
+decode workloads over an FP8 (E4M3) cache.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--quick]
 """
@@ -161,6 +162,106 @@ class DecodeRun:
             setattr(self, k, None)
 
 
+class Fp8DecodeRun(DecodeRun):
+    """The same decode workload over an FP8 (E4M3) cache.  Set-up (untimed):
+    the 16-bit pools after the cache write give every live token's k/v, which
+    the library's FP8 cache write quantises into code and scale pools.  The
+    timed step is the FP8 cache write of the new tokens plus FP8 decode."""
+
+    def __init__(self, case, partition_tokens=0):
+        import torch
+        super().__init__(case, partition_tokens)
+        pa, c = self.pa, case
+        if self.has_write:
+            pa.pa_reshape_and_cache(self.key, self.value, self.kc, self.vc, self.slots)
+        lens = c.seq_lens.astype(np.int64)
+        live = np.unique(np.concatenate([
+            c.block_tables[b, np.arange(int(lens[b])) // 16].astype(np.int64) * 16
+            + np.arange(int(lens[b])) % 16 for b in range(c.num_seqs)]))
+        idx = _i(live, torch.int64)
+        nb, hkv, d = c.num_blocks, c.num_kv_heads, c.head_dim
+        self.kc8 = torch.full((nb, 16, hkv, d), 0x7F, dtype=torch.uint8, device="cuda")
+        self.vc8 = torch.full_like(self.kc8, 0x7F)
+        self.ks = torch.full((nb, hkv, 16), float("nan"), dtype=torch.float32, device="cuda")
+        self.vs = torch.full_like(self.ks, float("nan"))
+        for lo in range(0, len(live), 1 << 16):
+            sl = idx[lo:lo + (1 << 16)]
+            pa.pa_reshape_and_cache_fp8(
+                self.kc.view(-1, hkv, d).index_select(0, sl).contiguous(),
+                self.vc.view(-1, hkv, d).index_select(0, sl).contiguous(),
+                self.kc8, self.vc8, self.ks, self.vs, sl.contiguous())
+        torch.cuda.synchronize()
+        self.kc = self.vc = None            # the 16-bit pools are not used by the timed step
+
+    def step(self, ev=None):
+        pa, c = self.pa, self.c
+        if ev is not None:
+            ev[0].record()
+        if self.has_write:
+            pa.pa_reshape_and_cache_fp8(self.key, self.value, self.kc8, self.vc8, self.ks, self.vs,
+                                        self.slots)
+        if ev is not None:
+            ev[1].record()
+        pa.pa_decode_partitions_fp8(self.out, self.q, self.kc8, self.vc8, self.ks, self.vs,
+                                    self.tables, self.lens, c.scale, self.ws, self.part,
+                                    flags=self.flags)
+        if ev is not None:
+            ev[2].record()
+        pa.pa_decode_merge(self.out, self.lens, c.num_kv_heads, c.max_blocks_per_seq, self.ws,
+                           self.part)
+        if ev is not None:
+            ev[3].record()
+
+    def algorithmic_bytes(self):
+        """K+V codes and their float32 scales of the live tokens, q, table, output."""
+        c = self.c
+        lens = c.seq_lens.astype(np.int64)
+        kv = int(lens.sum()) * 2 * c.num_kv_heads * (c.head_dim + 4)
+        q = c.num_seqs * c.num_q_heads * c.head_dim * 2
+        table = int(((lens + 15) // 16).sum()) * 4
+        return kv, kv + q + table + q
+
+    def free(self):
+        super().free()
+        for k in ("kc8", "vc8", "ks", "vs"):
+            setattr(self, k, None)
+
+
+def _oracle_fp8_rate(case, budget_s=3.0):
+    """The float64 oracle's FP8 decode on a bounded sample (whole sequences in
+    order until the budget is spent; each sequence's tokens quantised by the
+    oracle's cache write first, untimed): GB/s of codes + scales."""
+    import oracle
+    kc, vc = oracle.ref_reshape_and_cache(case.key, case.value, case.k_cache, case.v_cache,
+                                          case.slot_mapping)
+    hkv, d = case.num_kv_heads, case.head_dim
+    done, nbytes, spent = 0, 0, 0.0
+    for b in range(case.num_seqs):
+        n = int(case.seq_lens[b])
+        nblk = (n + 15) // 16
+        blocks = case.block_tables[b, :nblk]
+        p = np.arange(n)
+        slots = (p // 16) * 16 + p % 16                     # blocks renumbered 0..nblk-1
+        key = kc[blocks[p // 16], p % 16]
+        val = vc[blocks[p // 16], p % 16]
+        codes0 = np.zeros((max(nblk, 1), 16, hkv, d), np.uint8)
+        sc0 = np.ones((max(nblk, 1), hkv, 16), np.float32)
+        k8, v8, ks, vs = oracle.ref_reshape_and_cache_fp8(key, val, codes0, codes0, sc0, sc0,
+                                                          slots, case.dtype)
+        table = np.arange(max(nblk, 1), dtype=np.int32)[None]
+        t0 = time.perf_counter()
+        oracle.ref_decode_fp8(case.q[b:b + 1], k8, v8, ks, vs, table, np.array([n]), case.scale,
+                              case.dtype)
+        spent += time.perf_counter() - t0
+        done += 1
+        nbytes += n * 2 * hkv * (d + 4)
+        if spent > budget_s:
+            break
+    return {"value": round(nbytes / spent / 1e9, 3), "unit": "GB/s", "kind": "oracle",
+            "sample": f"{done} of {case.num_seqs} sequences in {spent:.1f} s of attention "
+                      "(the oracle's quantisation of their tokens not timed)"}
+
+
 def _traffic_if_current():
     """HBM bytes per launch of the partition kernel from committed rocprofv3
     counter runs, valid only if decode.hip is unchanged since they were taken."""
@@ -222,10 +323,10 @@ def _oracle_decode_rate(case, budget_s=3.0):
             "sample": f"{done} of {case.num_seqs} sequences in {dt:.1f} s"}
 
 
-def _secondary_decode(builder, name, steps, warmup, note=None, cpu=True):
+def _secondary_decode(builder, name, steps, warmup, note=None, cpu=True, fp8=False):
     import torch
     case = builder()
-    run = DecodeRun(case)
+    run = Fp8DecodeRun(case) if fp8 else DecodeRun(case)
     wall, per = run.timed(steps, warmup)
     kv, algo = run.algorithmic_bytes()
     dec_ms = per["partitions"] + per["merge"]
@@ -239,8 +340,12 @@ def _secondary_decode(builder, name, steps, warmup, note=None, cpu=True):
         res["write_ms"] = round(per["write"], 4)
     if note:
         res.update(note(case))
+    if fp8:
+        res["kv_cache"] = "fp8 e4m3 codes + float32 scale per (token, kv head)"
+        res["kv_bytes_16bit_equivalent"] = int(case.seq_lens.astype(np.int64).sum()) * 2 * \
+            case.num_kv_heads * case.head_dim * 2
     if cpu:
-        res["cpu_oracle"] = _oracle_decode_rate(case)
+        res["cpu_oracle"] = _oracle_fp8_rate(case) if fp8 else _oracle_decode_rate(case)
     run.free()
     del run, case
     torch.cuda.empty_cache()
@@ -265,7 +370,7 @@ def _shared_prefix_note(case):
                     "the shared prefixes may be served from the 256 MB Infinity Cache"}
 
 
-def _secondary_prefill(steps, warmup, oracle_budget_s=3.0):
+def _secondary_prefill(steps, warmup, oracle_budget_s=3.0, fp8=False):
     import torch
     import paged_kv_cache_24_amd as pa
     from workloads import prefill_chunked
@@ -276,14 +381,38 @@ def _secondary_prefill(steps, warmup, oracle_budget_s=3.0):
     slots = _i(c.slot_mapping, torch.int64)
     tables, ctx, qsl = _i(c.block_tables), _i(c.ctx_lens), _i(c.query_start_loc)
     out = torch.empty_like(q)
+    if fp8:
+        # set-up (untimed): quantise the cached context into FP8 pools with the
+        # library's FP8 cache write; the timed step writes the new tokens the same way
+        hkv, d = c.num_kv_heads, c.head_dim
+        kc8 = torch.full((c.num_blocks, 16, hkv, d), 0x7F, dtype=torch.uint8, device="cuda")
+        vc8 = torch.full_like(kc8, 0x7F)
+        ks8 = torch.full((c.num_blocks, hkv, 16), float("nan"), dtype=torch.float32, device="cuda")
+        vs8 = torch.full_like(ks8, float("nan"))
+        live = np.unique(np.concatenate([
+            c.block_tables[b, np.arange(int(c.ctx_lens[b])) // 16].astype(np.int64) * 16
+            + np.arange(int(c.ctx_lens[b])) % 16 for b in range(c.num_seqs)] + [np.zeros(0, np.int64)]))
+        if len(live):
+            idx = _i(live, torch.int64)
+            pa.pa_reshape_and_cache_fp8(kc.view(-1, hkv, d).index_select(0, idx).contiguous(),
+                                        vc.view(-1, hkv, d).index_select(0, idx).contiguous(),
+                                        kc8, vc8, ks8, vs8, idx)
+        torch.cuda.synchronize()
+        kc = vc = None
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        pa.pa_reshape_and_cache(key, value, kc, vc, slots)
+        if fp8:
+            pa.pa_reshape_and_cache_fp8(key, value, kc8, vc8, ks8, vs8, slots)
+        else:
+            pa.pa_reshape_and_cache(key, value, kc, vc, slots)
         if ev is not None:
             ev[1].record()
-        pa.pa_prefill_paged(out, q, kc, vc, tables, ctx, qsl, c.scale, c.max_q_len)
+        if fp8:
+            pa.pa_prefill_paged_fp8(out, q, kc8, vc8, ks8, vs8, tables, ctx, qsl, c.scale, c.max_q_len)
+        else:
+            pa.pa_prefill_paged(out, q, kc, vc, tables, ctx, qsl, c.scale, c.max_q_len)
         if ev is not None:
             ev[2].record()
 
@@ -302,8 +431,10 @@ def _secondary_prefill(steps, warmup, oracle_budget_s=3.0):
     pairs = int((L * ctxl + L * (L + 1) // 2).sum())
     flops = 4 * c.num_q_heads * c.head_dim * pairs
     write_bytes = 2 * 2 * c.num_tokens * c.num_kv_heads * c.head_dim * 2   # read + write, K and V
+    if fp8:   # 16-bit rows in, codes and scales out
+        write_bytes = 2 * c.num_tokens * c.num_kv_heads * (c.head_dim * 2 + c.head_dim + 4)
     cpu = None
-    if oracle_budget_s > 0:
+    if oracle_budget_s > 0 and not fp8:
         import oracle
         rk, rv = oracle.ref_reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache, c.slot_mapping)
         done_pairs, t0 = 0, time.perf_counter()
@@ -320,7 +451,7 @@ def _secondary_prefill(steps, warmup, oracle_budget_s=3.0):
         cpu = {"value": round(4 * c.num_q_heads * c.head_dim * done_pairs / dt / 1e12, 5),
                "unit": "TFLOP/s", "kind": "oracle",
                "sample": f"first <=64 rows of {b + 1} sequences ({done_pairs} (row, key) pairs per head) in {dt:.1f} s"}
-    res = {"workload": "prefill_chunked", "ms_per_step": round(wall, 4),
+    res = {"workload": "prefill_chunked_fp8" if fp8 else "prefill_chunked", "ms_per_step": round(wall, 4),
            "write_ms": round(per["write"], 4),
            "write_GBs": round(write_bytes / (per["write"] * 1e-3) / 1e9, 1),
            "write_pct_hbm_peak": round(100 * write_bytes / (per["write"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
@@ -330,6 +461,9 @@ def _secondary_prefill(steps, warmup, oracle_budget_s=3.0):
            "new_tokens": c.num_tokens, "unmasked_pairs_per_head": pairs}
     if cpu:
         res["cpu_oracle"] = cpu
+    if fp8:
+        res["kv_cache"] = "fp8 e4m3 codes + float32 scale per (token, kv head)"
+        del kc8, vc8, ks8, vs8
     del q, kc, vc, key, value, out
     torch.cuda.empty_cache()
     return res
@@ -448,6 +582,13 @@ def main():
         sec.append(_secondary_decode(decode_long_context, "decode_long_context", s2, w2))
         sec.append(_secondary_decode(decode_tiny, "decode_tiny", s2, w2))
         sec.append(_secondary_copy_blocks(s2, w2))
+        sec.append(_secondary_decode(decode_llama2_7b_layer, "decode_llama2_7b_layer_fp8", s2, w2,
+                                     fp8=True))
+        sec.append(_secondary_decode(decode_gqa_shared_prefix, "decode_gqa_shared_prefix_fp8", s2,
+                                     w2, fp8=True))
+        sec.append(_secondary_decode(decode_long_context, "decode_long_context_fp8", s2, w2,
+                                     fp8=True))
+        sec.append(_secondary_prefill(s2, w2, fp8=True))
         result["secondary"] = sec
     result["input_generation_s"] = round(gen_s, 1)
     print(json.dumps(result), flush=True)

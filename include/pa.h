@@ -322,6 +322,21 @@ pa_status pa_decode_partitions_fp8(void* out, const void* q, const void* k_cache
                                    int32_t partition_tokens, uint32_t flags, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * pa_prefill_paged_fp8 -- pa_prefill_paged over an FP8 cache: k_cache /
+ * v_cache hold codes and k_scales / v_scales their scales (the new tokens
+ * written by pa_reshape_and_cache_fp8 first); every other argument and rule
+ * as for pa_prefill_paged.  Output: causal attention over the dequantised K/V,
+ * accumulated in float32, rounded to `dtype`.
+ */
+pa_status pa_prefill_paged_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const float* k_scales, const float* v_scales,
+                               const int32_t* block_tables, const int32_t* ctx_lens,
+                               const int32_t* query_start_loc, int32_t num_seqs, int64_t num_tokens,
+                               int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                               int64_t num_blocks, float scale, pa_dtype dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

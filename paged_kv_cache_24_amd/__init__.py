@@ -10,7 +10,7 @@ Names follow the C ABI: ``pa_reshape_and_cache``, ``pa_copy_blocks``, ``pa_decod
 ``pa_decode_workspace_size``, ``pa_decode_default_partition``,
 ``pa_kv_bytes_per_token``, ``pa_status_string``, and for an FP8 (E4M3) cache
 ``pa_reshape_and_cache_fp8``, ``pa_copy_blocks_fp8``, ``pa_decode_fp8``,
-``pa_decode_partitions_fp8``.
+``pa_decode_partitions_fp8``, ``pa_prefill_paged_fp8``.
 """
 
 from __future__ import annotations
@@ -26,6 +26,7 @@ __all__ = [
     "pa_decode_default_partition", "pa_decode_workspace_size", "pa_decode",
     "pa_decode_partitions", "pa_decode_merge", "pa_prefill_paged",
     "pa_reshape_and_cache_fp8", "pa_copy_blocks_fp8", "pa_decode_fp8", "pa_decode_partitions_fp8",
+    "pa_prefill_paged_fp8",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
@@ -60,6 +61,8 @@ _SIGS = {
     "pa_reshape_and_cache_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
                                         _i64, _i32, _vp]),
     "pa_copy_blocks_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp]),
+    "pa_prefill_paged_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32,
+                                    _i32, _i32, _i32, _i32, _i32, _i64, _f32, _i32, _vp]),
     "pa_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                              _i32, _i64, _f32, _i32, _i32, _u32, _vp, _sz, _vp]),
     "pa_decode_partitions_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
@@ -338,3 +341,26 @@ def pa_decode_partitions_fp8(out, q, k_cache, v_cache, k_scales, v_scales, block
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
         _ptr(block_tables), _ptr(seq_lens), b, hq, hkv, d, bs, mb, nb, float(scale), _kv_dtype(q),
         partition_tokens, flags, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def pa_prefill_paged_fp8(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, ctx_lens,
+                         query_start_loc, scale, max_q_len, stream=None):
+    """Causal chunked prefill of the packed rows ``q`` over an FP8 cache into ``out``;
+    the other arguments as for ``pa_prefill_paged``."""
+    nb, bs, hkv, d = _fp8_pools(k_cache, v_cache, k_scales, v_scales)
+    _need(q, "q", None, 3)
+    _need(out, "out", q.dtype, 3)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(ctx_lens, "ctx_lens", torch.int32, 1)
+    _need(query_start_loc, "query_start_loc", torch.int32, 1)
+    t, hq, dq = q.shape
+    b = ctx_lens.shape[0]
+    if out.shape != q.shape or dq != d:
+        raise ValueError("q/out/cache shapes disagree")
+    if block_tables.shape[0] != b or query_start_loc.shape[0] != b + 1:
+        raise ValueError("block_tables / query_start_loc do not match ctx_lens")
+    _check("pa_prefill_paged_fp8", lib.pa_prefill_paged_fp8(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
+        _ptr(block_tables), _ptr(ctx_lens), _ptr(query_start_loc), b, t, int(max_q_len), hq, hkv, d,
+        bs, block_tables.shape[1], nb, float(scale), _kv_dtype(q), _stream(stream)))
+    return out

@@ -85,6 +85,7 @@ constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // reverse within each 8 lanes
 constexpr int kDppMirror = 0x140;     // reverse within each 16 lanes
+constexpr int kDppRowRor8 = 0x128;    // rotate each 16-lane row by 8 lanes
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -120,6 +121,27 @@ __device__ __forceinline__ float quad_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Reductions over lanes {l, l^16} and {l, l^32} on the VALU (gfx950 lane
+// swaps, no LDS round trip).  permlane16_swap(x, x) returns the even 16-lane
+// rows of each row pair in its first result and the odd rows in its second;
+// permlane32_swap(x, x) the low and high halves of the wave.
+__device__ __forceinline__ float xor16_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // --------------------------------------------------------- FP8 (OCP E4M3)
 // Hardware conversions of gfx950, both exact where used here:

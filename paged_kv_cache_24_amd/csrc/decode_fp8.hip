@@ -205,7 +205,6 @@ __global__ __launch_bounds__(256) void decode_fp8_partition_kernel(DecodeArgs a)
             m[h] = mn;
         }
     };
-
     // NBUF register buffers: while one block is computed, NBUF-1 are in flight
     if (j0 < j1) {
         Buf buf[NBUF];
@@ -278,29 +277,32 @@ __global__ __launch_bounds__(256) void decode_fp8_partition_kernel(DecodeArgs a)
 
 // ---------------------------------------------------------------------------
 // GQA kernel (head_dim 128, 3..16 q heads per kv head): both products on
-// matrix cores, as in decode.hip, with the codes widened on the way in.
-//   S^T = K Q^T: MFMA 16x16x32 x 4.  Lane (lr, lg) feeds token lr of the block
-//        and head_dim elements 32*lg + 8*kk .. +8 for step kk (the order of the
-//        head_dim sum is free as long as Q uses the same one): two 16-byte
-//        loads of 16 codes, widened exactly to 16-bit.  Lane l then holds the
-//        scores of tokens 4*lg + i (i = 0..3) for head lr, so their k/v scales
-//        are one 16-byte load each.
-//   O^T += V^T P^T: MFMA 16x16x16 x 8 from a per-wave LDS tile of V.  The V
-//        codes are widened times 2^e (e = exponent of the token's v_scale, exact
-//        in 16 bits) and the mantissa factor in [1, 2) of v_scale multiplies the
-//        probabilities, so P never meets a tiny scale in 16-bit precision; P
-//        enters as a 16-bit head and tail, two MFMAs, so the factor adds no
-//        rounding of its own.
-//        Lane (lr, lg) loads tokens 4*lg + (lr/8) and 4*lg + 2 + (lr/8), codes
-//        16*(lr%8) .. +16: tokens among its own four, whose scales it holds.
-//        The transposed LDS read (ds_read_b64_tr_b16) at row 4*lg + lr/4,
-//        column 4*(lr%4) hands lane (lr, lg) the four tokens 4*lg + j of
-//        head_dim element lr: the A operand that matches P^T.
+// matrix cores, as in decode.hip, with the codes widened on the way in.  A
+// step takes TWO blocks (32 tokens): one softmax update, one max reduction and
+// one LDS hand-off per 32 tokens, and P V contracts over all 32 at once.
+//   S^T = K Q^T, per block: MFMA 16x16x32 x 4.  Lane (lr, lg) feeds token lr of
+//        the block and head_dim elements 32*lg + 8*kk .. +8 for step kk (the
+//        order of the head_dim sum is free as long as Q uses the same one): two
+//        16-byte loads of 16 codes, widened exactly to 16-bit.  Lane l then
+//        holds the scores of tokens 4*lg + i (i = 0..3) of each block for head
+//        lr, so their k/v scales are one 16-byte load per block.
+//   O^T += V^T P^T: MFMA 16x16x32 x 8 per step.  Contraction index
+//        k = 8*lg + j stands for token 4*lg + j of the first block (j < 4) and
+//        token 4*lg + j - 4 of the second (j >= 4): exactly the probabilities
+//        lane (lr, lg) already holds, so P never moves.  V^T comes from one
+//        per-wave LDS tile per block: the transposed read (ds_read_b64_tr_b16)
+//        at row 4*lg + lr/4, column 4*(lr%4) hands lane (lr, lg) tokens
+//        4*lg .. 4*lg+3 of head_dim element lr; one read per tile fills the
+//        eight A elements.  The V codes are widened times 2^e (e = exponent of
+//        the token's v_scale, exact in 16 bits) and the mantissa factor in
+//        [1, 2) of v_scale multiplies the probabilities, so P never meets a
+//        tiny scale in 16-bit precision; P enters as a 16-bit head and tail,
+//        two MFMAs, so the factor adds no rounding of its own.
+//        Lane (lr, lg) loads tokens 4*lg + (lr/8) and 4*lg + 2 + (lr/8) of a
+//        block, codes 16*(lr%8) .. +16: tokens among its own four.
 // ---------------------------------------------------------------------------
 typedef __bf16 f8bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 f8bf16x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f8f16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f8f16x4_t __attribute__((ext_vector_type(4)));
 typedef float f8f32x4_t __attribute__((ext_vector_type(4)));
 typedef short f8s16x4_t __attribute__((ext_vector_type(4)));
 
@@ -314,23 +316,24 @@ __device__ __forceinline__ f8f32x4_t f8_mfma_16x16x32(const uint4& a, const uint
                                                        __builtin_bit_cast(f8bf16x8_t, b), c, 0, 0, 0);
     }
 }
-template <int DT>
-__device__ __forceinline__ f8f32x4_t f8_mfma_16x16x16(const uint2& a, const uint2& b, f8f32x4_t c) {
-    if constexpr (DT == kF16) {
-        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f8f16x4_t, a),
-                                                     __builtin_bit_cast(f8f16x4_t, b), c, 0, 0, 0);
-    } else {
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(f8bf16x4_t, a),
-                                                         __builtin_bit_cast(f8bf16x4_t, b), c, 0, 0, 0);
-    }
+
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (f8s16x4_t __attribute__((address_space(3)))*)(p)));
 }
 
-constexpr int kVRowF8 = 144;   // LDS row stride of the widened V tile (16-bit elements)
+constexpr int kVRowF8 = 144;   // LDS row stride of a widened V tile (16-bit elements)
+// Register ring depth, in block pairs.  Measured on MI355X: a deeper ring
+// (one or two pairs in flight while a pair is computed) needs more registers
+// than 3 waves per SIMD allow, or drops to 2 waves, and was no faster than one
+// pair at a time with 4 resident waves (122 registers) hiding each other's loads.
+constexpr int kGqaFp8Pairs = 1;
 
-template <int DT, bool NT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void decode_fp8_gqa_kernel(DecodeArgs a) {
+template <int DT, bool NT, int NBUF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_fp8_gqa_kernel(DecodeArgs a) {
     constexpr int D = 128;
-    __shared__ __attribute__((aligned(16))) uint16_t vlds[4][kBlockSize * kVRowF8];
+    constexpr int kTile = kBlockSize * kVRowF8;
+    __shared__ __attribute__((aligned(16))) uint16_t vlds[4][2 * kTile];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x >> 6);
     const int lr = lane & 15;    // MFMA column = q head; token of the K rows; V^T row
@@ -379,58 +382,85 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     const int vrow0 = 4 * lg + (lr >> 3);      // V rows of this lane: vrow0 and vrow0 + 2
     const uint8_t* vbase = static_cast<const uint8_t*>(a.v_cache) + (int64_t)g * D + 16 * (lr & 7) +
                            (int64_t)vrow0 * row_stride;
-    const float* ksb = a.k_scales + (int64_t)g * kBlockSize + 4 * lg;
-    const float* vsb = a.v_scales + (int64_t)g * kBlockSize + 4 * lg;
+    // scales of tokens 4*lg .. 4*lg+3: lanes lr < 8 load the k scales, lanes
+    // lr >= 8 the v scales (half the registers per buffer); a DPP rotation by
+    // 8 lanes hands each lane the other half when the block is computed
+    const bool k_half = lr < 8;
+    const float* scb = (k_half ? a.k_scales : a.v_scales) + (int64_t)g * kBlockSize + 4 * lg;
     const int64_t scale_block_stride = (int64_t)a.num_kv_heads * kBlockSize;
     const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
     const float cs = a.scale_log2;
-    const uint16_t* vtr = vt + (4 * lg + (lr >> 2)) * kVRowF8 + 4 * (lr & 3);
+    const int tr_off = (4 * lg + (lr >> 2)) * kVRowF8 + 4 * (lr & 3);
 
-    struct Buf {
+    struct Blk {
         uint4 k[2], v[2];
-        float4 ks, vs;
+        float4 sc;
         bool ok;
     };
-
-    auto load = [&](int j, Buf& buf) {
-        const int pb = table[j];
-        buf.ok = pb >= 0 && (int64_t)pb < a.num_blocks;
-        const int64_t blk = buf.ok ? pb : 0;
-        const int64_t off = blk * kBlockSize * row_stride;
-        buf.k[0] = load16<NT>(kbase + off);
-        buf.k[1] = load16<NT>(kbase + off + 16);
-        buf.v[0] = load16<NT>(vbase + off);
-        buf.v[1] = load16<NT>(vbase + off + 2 * row_stride);
-        buf.ks = *reinterpret_cast<const float4*>(ksb + blk * scale_block_stride);
-        buf.vs = *reinterpret_cast<const float4*>(vsb + blk * scale_block_stride);
+    struct Pair {
+        Blk x[2];
     };
 
-    auto process = [&](const Buf& buf, int j) {
-        f8f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const uint4& w = buf.k[kk >> 1];
-            const uint32_t w0 = (kk & 1) ? w.z : w.x;
-            const uint32_t w1 = (kk & 1) ? w.w : w.y;
-            const uint2 e0 = fp8x4_to_16<DT>(w0, 1.f), e1 = fp8x4_to_16<DT>(w1, 1.f);
-            sacc = f8_mfma_16x16x32<DT>(make_uint4(e0.x, e0.y, e1.x, e1.y), qf[kk], sacc);
+    auto load_blk = [&](int j, Blk& blk_regs) {
+        if (j >= j1) {   // the odd block after the last one: nothing to read, every row masked
+            blk_regs.ok = false;
+            blk_regs.k[0] = blk_regs.k[1] = blk_regs.v[0] = blk_regs.v[1] = make_uint4(0, 0, 0, 0);
+            blk_regs.sc = make_float4(1.f, 1.f, 1.f, 1.f);
+            return;
         }
-        const float ks[4] = {buf.ks.x, buf.ks.y, buf.ks.z, buf.ks.w};
-        const float vs[4] = {buf.vs.x, buf.vs.y, buf.vs.z, buf.vs.w};
-        const bool full = buf.ok && (j + 1) * kBlockSize <= n;
-        bool valid[4];
-        float x[4];
+        const int pb = table[j];
+        blk_regs.ok = pb >= 0 && (int64_t)pb < a.num_blocks;
+        const int64_t blk = blk_regs.ok ? pb : 0;
+        const int64_t off = blk * kBlockSize * row_stride;
+        blk_regs.k[0] = load16<NT>(kbase + off);
+        blk_regs.k[1] = load16<NT>(kbase + off + 16);
+        blk_regs.v[0] = load16<NT>(vbase + off);
+        blk_regs.v[1] = load16<NT>(vbase + off + 2 * row_stride);
+        blk_regs.sc = *reinterpret_cast<const float4*>(scb + blk * scale_block_stride);
+    };
+    auto load = [&](int j, Pair& pr) {
+        load_blk(j, pr.x[0]);
+        load_blk(j + 1, pr.x[1]);
+    };
+
+    auto process = [&](const Pair& pr, int j) {
+        f8f32x4_t sacc[2];
+        float ks[2][4], vs[2][4];
+        bool valid[2][4];
+        float x[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            valid[i] = full || (buf.ok && (j * kBlockSize + 4 * lg + i < n));
-            x[i] = valid[i] ? sacc[i] * (ks[i] * cs) : -INFINITY;
+        for (int h = 0; h < 2; ++h) {
+            const Blk& bk = pr.x[h];
+            sacc[h] = f8f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const uint4& w = bk.k[kk >> 1];
+                const uint32_t w0 = (kk & 1) ? w.z : w.x;
+                const uint32_t w1 = (kk & 1) ? w.w : w.y;
+                const uint2 e0 = fp8x4_to_16<DT>(w0, 1.f), e1 = fp8x4_to_16<DT>(w1, 1.f);
+                sacc[h] = f8_mfma_16x16x32<DT>(make_uint4(e0.x, e0.y, e1.x, e1.y), qf[kk], sacc[h]);
+            }
+            const float mine[4] = {bk.sc.x, bk.sc.y, bk.sc.z, bk.sc.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float other = dpp<kDppRowRor8>(mine[i]);
+                ks[h][i] = k_half ? mine[i] : other;
+                vs[h][i] = k_half ? other : mine[i];
+            }
+            const int t0 = (j + h) * kBlockSize;
+            const bool full = bk.ok && t0 + kBlockSize <= n;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                valid[h][i] = full || (bk.ok && (t0 + 4 * lg + i < n));
+                x[h][i] = valid[h][i] ? sacc[h][i] * (ks[h][i] * cs) : -INFINITY;
+            }
         }
-        float mb = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        mb = fmaxf(mb, __shfl_xor(mb, 16));
-        mb = fmaxf(mb, __shfl_xor(mb, 32));
-        // raise the running max only when this block beats it by more than 2^8:
+        float mb = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                         fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+        mb = xor32_max(xor16_max(mb));
+        // raise the running max only when this step beats it by more than 2^8:
         // otherwise keep it (p <= 256, exact algebra) and skip the rescale of O^T
-        const bool raise = mb > m + 8.f;   // also true on the first live block
+        const bool raise = mb > m + 8.f;   // also true on the first live step
         const float mn = raise ? mb : m;
         if (__any(raise)) {
             const float alpha = raise ? fast_exp2(m - mn) : 1.f;   // exp2(-inf) = 0
@@ -440,67 +470,82 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         }
         m = mn;
         const float mu = mn == -INFINITY ? 0.f : mn;
-        float p[4];
+        float pm[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - mu);
-        l += (p[0] + p[1]) + (p[2] + p[3]);
-        // V tile to LDS, widened times 2^exponent(v_scale); rows past the
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = fast_exp2(x[h][i] - mu);
+                l += p;
+                pm[h][i] = valid[h][i] ? p * scale_mantissa(vs[h][i]) : 0.f;
+            }
+        // V tiles to LDS, widened times 2^exponent(v_scale); rows past the
         // sequence end as zeros (MFMA would turn 0 x NaN into NaN)
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int row = vrow0 + 2 * k;
-            const int sel = (lr >> 3) + 2 * k;
-            const float vsr = sel == 0 ? vs[0] : sel == 1 ? vs[1] : sel == 2 ? vs[2] : vs[3];
-            const bool ok = full || (buf.ok && (j * kBlockSize + row < n));
-            const uint4& w = buf.v[k];
-            const uint2 e0 = fp8x4_to_16<DT>(w.x, vsr), e1 = fp8x4_to_16<DT>(w.y, vsr);
-            const uint2 e2 = fp8x4_to_16<DT>(w.z, vsr), e3 = fp8x4_to_16<DT>(w.w, vsr);
-            uint4* dst = reinterpret_cast<uint4*>(vt + row * kVRowF8 + 16 * (lr & 7));
-            dst[0] = ok ? make_uint4(e0.x, e0.y, e1.x, e1.y) : make_uint4(0, 0, 0, 0);
-            dst[1] = ok ? make_uint4(e2.x, e2.y, e3.x, e3.y) : make_uint4(0, 0, 0, 0);
+        for (int h = 0; h < 2; ++h) {
+            const Blk& bk = pr.x[h];
+            const int t0 = (j + h) * kBlockSize;
+            const bool full = bk.ok && t0 + kBlockSize <= n;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int row = vrow0 + 2 * k;
+                const int sel = (lr >> 3) + 2 * k;
+                const float vsr = sel == 0 ? vs[h][0] : sel == 1 ? vs[h][1] : sel == 2 ? vs[h][2] : vs[h][3];
+                const bool ok = full || (bk.ok && (t0 + row < n));
+                const uint4& w = bk.v[k];
+                const uint2 e0 = fp8x4_to_16<DT>(w.x, vsr), e1 = fp8x4_to_16<DT>(w.y, vsr);
+                const uint2 e2 = fp8x4_to_16<DT>(w.z, vsr), e3 = fp8x4_to_16<DT>(w.w, vsr);
+                uint4* dst = reinterpret_cast<uint4*>(vt + h * kTile + row * kVRowF8 + 16 * (lr & 7));
+                dst[0] = ok ? make_uint4(e0.x, e0.y, e1.x, e1.y) : make_uint4(0, 0, 0, 0);
+                dst[1] = ok ? make_uint4(e2.x, e2.y, e3.x, e3.y) : make_uint4(0, 0, 0, 0);
+            }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // P^T = p * mantissa(v_scale) as a 16-bit head plus a 16-bit tail
-        // (p * mu - head): two MFMAs carry ~16 significant bits of P, so the
-        // widening of the scale costs no precision next to the 16-bit cache
-        float pm[4];
+        // (p * mu - head): two MFMAs carry ~16 significant bits of P
+        uint4 ph, pt;
+        ph.x = pack2<DT>(pm[0][0], pm[0][1]);
+        ph.y = pack2<DT>(pm[0][2], pm[0][3]);
+        ph.z = pack2<DT>(pm[1][0], pm[1][1]);
+        ph.w = pack2<DT>(pm[1][2], pm[1][3]);
+        pt.x = pack2<DT>(pm[0][0] - lo_to_f32<DT>(ph.x), pm[0][1] - hi_to_f32<DT>(ph.x));
+        pt.y = pack2<DT>(pm[0][2] - lo_to_f32<DT>(ph.y), pm[0][3] - hi_to_f32<DT>(ph.y));
+        pt.z = pack2<DT>(pm[1][0] - lo_to_f32<DT>(ph.z), pm[1][1] - hi_to_f32<DT>(ph.z));
+        pt.w = pack2<DT>(pm[1][2] - lo_to_f32<DT>(ph.w), pm[1][3] - hi_to_f32<DT>(ph.w));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pm[i] = valid[i] ? p[i] * scale_mantissa(vs[i]) : 0.f;
-        uint2 ph, pt;
-        ph.x = pack2<DT>(pm[0], pm[1]);
-        ph.y = pack2<DT>(pm[2], pm[3]);
-        pt.x = pack2<DT>(pm[0] - lo_to_f32<DT>(ph.x), pm[1] - hi_to_f32<DT>(ph.x));
-        pt.y = pack2<DT>(pm[2] - lo_to_f32<DT>(ph.y), pm[3] - hi_to_f32<DT>(ph.y));
-        uint2 va[8];
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-            va[mt] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (f8s16x4_t __attribute__((address_space(3)))*)(vtr + 16 * mt)));
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) o[mt] = f8_mfma_16x16x16<DT>(va[mt], ph, o[mt]);
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) o[mt] = f8_mfma_16x16x16<DT>(va[mt], pt, o[mt]);
+        for (int mt = 0; mt < 8; ++mt) {
+            const uint2 v0 = lds_read_tr16(vt + tr_off + 16 * mt);
+            const uint2 v1 = lds_read_tr16(vt + kTile + tr_off + 16 * mt);
+            const uint4 va = make_uint4(v0.x, v0.y, v1.x, v1.y);
+            o[mt] = f8_mfma_16x16x32<DT>(va, ph, o[mt]);
+            o[mt] = f8_mfma_16x16x32<DT>(va, pt, o[mt]);
+        }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
+    // NBUF register buffers of block pairs: while one pair is computed,
+    // NBUF-1 are in flight
     if (j0 < j1) {
-        Buf cur;
-        load(j0, cur);
-        for (int j = j0; j < j1; ++j) {
-            Buf nxt;
-            nxt.ok = false;
-            if (j + 1 < j1) load(j + 1, nxt);   // next block in flight
-            process(cur, j);
-            cur = nxt;
+        Pair buf[NBUF];
+#pragma unroll
+        for (int s = 0; s < NBUF - 1; ++s)
+            if (j0 + 2 * s < j1) load(j0 + 2 * s, buf[s]);
+        for (int j = j0; j < j1; j += 2 * NBUF) {
+#pragma unroll
+            for (int s = 0; s < NBUF; ++s) {
+                const int jj = j + 2 * s;
+                if (jj >= j1) break;
+                if (jj + 2 * (NBUF - 1) < j1) load(jj + 2 * (NBUF - 1), buf[(s + NBUF - 1) % NBUF]);
+                process(buf[s], jj);
+            }
         }
     }
 
-    float lt = l + __shfl_xor(l, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = xor32_sum(xor16_sum(l));
     if (!head_live) return;
     if (nparts == 1) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
@@ -536,7 +581,7 @@ static hipError_t launch_fp8_vector(const DecodeArgs& a, hipStream_t s, dim3 gri
 template <int DT, bool NT>
 static hipError_t launch_fp8_t(const DecodeArgs& a, hipStream_t s, dim3 grid) {
     if (a.gqa_mfma) {
-        hipLaunchKernelGGL((decode_fp8_gqa_kernel<DT, NT>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((decode_fp8_gqa_kernel<DT, NT, kGqaFp8Pairs>), grid, dim3(256), 0, s, a);
         return hipGetLastError();
     }
     return a.head_dim == 128 ? launch_fp8_vector<DT, 128, NT>(a, s, grid)

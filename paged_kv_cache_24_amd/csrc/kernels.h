@@ -99,7 +99,11 @@ struct PrefillArgs {
     int64_t num_blocks;
     float scale_log2;
     int32_t dtype;
+    // FP8 cache only: per (block, kv head, token) float32 scales
+    const float* k_scales;   // [NB][Hkv][16]
+    const float* v_scales;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_fp8(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace pa

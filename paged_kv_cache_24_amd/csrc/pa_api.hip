@@ -391,12 +391,13 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                            workspace_bytes, stream);
 }
 
-pa_status pa_prefill_paged(void* out, const void* q, const void* k_cache, const void* v_cache,
-                           const int32_t* block_tables, const int32_t* ctx_lens,
-                           const int32_t* query_start_loc, int32_t num_seqs, int64_t num_tokens,
-                           int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
-                           int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
-                           int64_t num_blocks, float scale, pa_dtype dtype, hipStream_t stream) {
+static pa_status prefill_common(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                const float* k_scales, const float* v_scales, bool fp8,
+                                const int32_t* block_tables, const int32_t* ctx_lens,
+                                const int32_t* query_start_loc, int32_t num_seqs, int64_t num_tokens,
+                                int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                int64_t num_blocks, float scale, pa_dtype dtype, hipStream_t stream) {
     if (!supported_dtype(dtype) || block_size != PA_BLOCK_SIZE || head_dim != 128)
         return PA_ERR_UNSUPPORTED;
     if (num_seqs < 0 || num_tokens < 0 || max_q_len < 0 || num_q_heads <= 0 ||
@@ -409,8 +410,10 @@ pa_status pa_prefill_paged(void* out, const void* q, const void* k_cache, const 
     if (num_seqs == 0 || num_tokens == 0 || max_q_len == 0) return PA_OK;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !ctx_lens || !query_start_loc)
         return PA_ERR_NULL_PTR;
+    if (fp8 && (!k_scales || !v_scales)) return PA_ERR_NULL_PTR;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return PA_ERR_ALIGNMENT;
+    if (fp8 && (!aligned16(k_scales) || !aligned16(v_scales))) return PA_ERR_ALIGNMENT;
     pa::PrefillArgs a;
     a.out = out;
     a.q = q;
@@ -429,7 +432,35 @@ pa_status pa_prefill_paged(void* out, const void* q, const void* k_cache, const 
     a.num_blocks = num_blocks;
     a.scale_log2 = scale * kLog2e;
     a.dtype = dtype == PA_F16 ? pa::kF16 : pa::kBF16;
-    return pa::launch_prefill(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+    a.k_scales = k_scales;
+    a.v_scales = v_scales;
+    const hipError_t e = fp8 ? pa::launch_prefill_fp8(a, stream) : pa::launch_prefill(a, stream);
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_prefill_paged_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const float* k_scales, const float* v_scales,
+                               const int32_t* block_tables, const int32_t* ctx_lens,
+                               const int32_t* query_start_loc, int32_t num_seqs, int64_t num_tokens,
+                               int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                               int64_t num_blocks, float scale, pa_dtype dtype, hipStream_t stream) {
+    return prefill_common(out, q, k_cache, v_cache, k_scales, v_scales, true, block_tables, ctx_lens,
+                          query_start_loc, num_seqs, num_tokens, max_q_len, num_q_heads,
+                          num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                          dtype, stream);
+}
+
+pa_status pa_prefill_paged(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* ctx_lens,
+                           const int32_t* query_start_loc, int32_t num_seqs, int64_t num_tokens,
+                           int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                           int64_t num_blocks, float scale, pa_dtype dtype, hipStream_t stream) {
+    return prefill_common(out, q, k_cache, v_cache, nullptr, nullptr, false, block_tables, ctx_lens,
+                          query_start_loc, num_seqs, num_tokens, max_q_len, num_q_heads,
+                          num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                          dtype, stream);
 }
 
 }  // extern "C"

@@ -27,6 +27,15 @@
 // of the rescale factors is needed.  The next tile's K/V rows are loaded into
 // registers while the current tile is computed and stored to the other LDS
 // buffer afterwards (one barrier per tile).
+//
+// FP8 cache (F8): the same kernel over E4M3 codes with per-(token, kv head)
+// float32 scales ("vLLM-Ascend 原理", §四 on KV-cache quantisation: dequantised
+// after the block-table lookup, inside the operator).  Each thread stages 16
+// codes of one key row; K enters LDS as exact 16-bit codes and its scale
+// multiplies the scores, V enters as codes times 2^e (e = exponent of its
+// scale, exact) and the scale's mantissa factor in [1, 2) multiplies P, which
+// goes to the matrix cores as a 16-bit head and tail so the factor adds no
+// rounding.  The per-key factors sit in two small LDS arrays beside the tiles.
 #include <type_traits>
 
 #include "common.h"
@@ -59,11 +68,14 @@ typedef short ps16x4_t __attribute__((ext_vector_type(4)));
 constexpr int kKRow = kPD + 8;      // LDS K row stride (elements): 272 bytes, so the 16 rows of
                                     // an MFMA A fragment start 4 banks apart (conflict-free)
 
-template <int DT, int G>
+template <int DT, int G, bool F8>
 __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     constexpr int P = kRows / G;    // positions per workgroup
     __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kKT * kKRow];
     __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kKT * kVRow];
+    // FP8 only: per-key k scale and v-scale mantissa factor of each staged tile
+    __shared__ __attribute__((aligned(16))) float lds_ks[F8 ? 2 : 1][F8 ? kKT : 4];
+    __shared__ __attribute__((aligned(16))) float lds_mu[F8 ? 2 : 1][F8 ? kKT : 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -154,17 +166,73 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
             *reinterpret_cast<uint4*>(&lds_v[buf][kr * kVRow + 8 * ck]) = gv[i];
         }
     };
+    // ---- FP8 staging: thread t moves the 16 codes 16*(t % 8) .. +16 of key row t / 8
+    // (K and V) and that row's two scales.  Invalid rows stage zeros with k scale 0
+    // and v scale 1, so NaN bits in unused slots never reach the products.
+    const int c8 = tid & 7;
+    const int kr8 = tid >> 3;       // 0..63
+    auto load_tile8 = [&](int tt, uint4& ck8, uint4& cv8, float& ksc, float& vsc) {
+        int pbs[4];   // the tile's four blocks (uniform table reads), then this row's
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pbs[q] = (tt * 4 + q) * kBlockSize < n_keys ? table[tt * 4 + q] : -1;
+        const int sub = kr8 >> 4;
+        const int pb = sub == 0 ? pbs[0] : sub == 1 ? pbs[1] : sub == 2 ? pbs[2] : pbs[3];
+        const int key = tt * kKT + kr8;
+        const bool ok = pb >= 0 && (int64_t)pb < a.num_blocks;
+        const bool valid = ok && key < n_keys;
+        const int64_t pblk = ok ? pb : 0;
+        const int64_t off = (pblk * kBlockSize + (kr8 & 15)) * row_stride + (int64_t)g * kPD + 16 * c8;
+        const uint4 k4 = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.k_cache) + off);
+        const uint4 v4 = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.v_cache) + off);
+        const int64_t soff = (pblk * a.num_kv_heads + g) * kBlockSize + (kr8 & 15);
+        const float ks = a.k_scales[soff];
+        const float vs = a.v_scales[soff];
+        ck8 = valid ? k4 : make_uint4(0, 0, 0, 0);
+        cv8 = valid ? v4 : make_uint4(0, 0, 0, 0);
+        ksc = valid ? ks : 0.f;
+        vsc = valid ? vs : 1.f;
+    };
+    auto store_tile8 = [&](int buf, const uint4& ck8, const uint4& cv8, float ksc, float vsc) {
+        const uint32_t kw[4] = {ck8.x, ck8.y, ck8.z, ck8.w};
+        const uint32_t vw[4] = {cv8.x, cv8.y, cv8.z, cv8.w};
+        uint2 ke[4], ve[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ke[e] = fp8x4_to_16<DT>(kw[e], 1.f);
+            ve[e] = fp8x4_to_16<DT>(vw[e], vsc);
+        }
+        uint4* kd = reinterpret_cast<uint4*>(&lds_k[buf][kr8 * kKRow + 16 * c8]);
+        uint4* vd = reinterpret_cast<uint4*>(&lds_v[buf][kr8 * kVRow + 16 * c8]);
+        kd[0] = make_uint4(ke[0].x, ke[0].y, ke[1].x, ke[1].y);
+        kd[1] = make_uint4(ke[2].x, ke[2].y, ke[3].x, ke[3].y);
+        vd[0] = make_uint4(ve[0].x, ve[0].y, ve[1].x, ve[1].y);
+        vd[1] = make_uint4(ve[2].x, ve[2].y, ve[3].x, ve[3].y);
+        if (c8 == 0) {
+            lds_ks[buf][kr8] = ksc;
+            lds_mu[buf][kr8] = scale_mantissa(vsc);
+        }
+    };
     // transposed V^T fragment address of this lane: row 4*lg + lr/4 (+16), column 4*(lr%4) (+16 mt)
     const int v_tr_off = (4 * lg + (lr >> 2)) * kVRow + 4 * (lr & 3);
 
     uint4 gk[2], gv[2];
-    load_tile(0, gk, gv);
-    store_tile(0, gk, gv);
+    uint4 ck8, cv8;
+    float ksc = 0.f, vsc = 1.f;
+    if constexpr (F8) {
+        load_tile8(0, ck8, cv8, ksc, vsc);
+        store_tile8(0, ck8, cv8, ksc, vsc);
+    } else {
+        load_tile(0, gk, gv);
+        store_tile(0, gk, gv);
+    }
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
         __syncthreads();   // tile t is in LDS; everybody is done with tile t-1's buffer
         const bool more = t + 1 < ntiles;
-        if (more) load_tile(t + 1, gk, gv);   // in flight while this tile is computed
+        if (more) {   // in flight while this tile is computed
+            if constexpr (F8) load_tile8(t + 1, ck8, cv8, ksc, vsc);
+            else load_tile(t + 1, gk, gv);
+        }
         const int k0 = t * kKT;
         if (wave_live && k0 <= wave_q_hi) {
             // ---- S^T = K Q^T for 64 keys x 16 rows
@@ -178,6 +246,16 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
                     const uint4 ka = *reinterpret_cast<const uint4*>(
                         &lds_k[buf][(16 * mt + lr) * kKRow + 32 * kk + 8 * lg]);
                     s[mt] = mfma16x16x32<DT>(ka, qf[kk], s[mt]);
+                }
+            }
+            if constexpr (F8) {   // k scale of each key (keys 16*mt + 4*lg + i)
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const float4 ks4 = *reinterpret_cast<const float4*>(&lds_ks[buf][16 * mt + 4 * lg]);
+                    s[mt][0] *= ks4.x;
+                    s[mt][1] *= ks4.y;
+                    s[mt][2] *= ks4.z;
+                    s[mt][3] *= ks4.w;
                 }
             }
 
@@ -220,14 +298,30 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
                     ps += pv;
                 }
             lsum += ps;
+            if constexpr (F8) {   // times the v-scale mantissa factor of each key
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    const float4 mu4 = *reinterpret_cast<const float4*>(&lds_mu[buf][16 * mt + 4 * lg]);
+                    s[mt][0] *= mu4.x;
+                    s[mt][1] *= mu4.y;
+                    s[mt][2] *= mu4.z;
+                    s[mt][3] *= mu4.w;
+                }
+            }
             // key slot 8*lg + i <-> key 32*kc + 4*lg + i; slot 8*lg + 4 + i <-> key 32*kc + 16 + 4*lg + i
-            uint4 pb[2];
+            uint4 pb[2], pt[2];
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
                 pb[kc].x = pack2<DT>(s[2 * kc][0], s[2 * kc][1]);
                 pb[kc].y = pack2<DT>(s[2 * kc][2], s[2 * kc][3]);
                 pb[kc].z = pack2<DT>(s[2 * kc + 1][0], s[2 * kc + 1][1]);
                 pb[kc].w = pack2<DT>(s[2 * kc + 1][2], s[2 * kc + 1][3]);
+                if constexpr (F8) {   // the 16-bit tail of P: what the head's rounding lost
+                    pt[kc].x = pack2<DT>(s[2 * kc][0] - lo_to_f32<DT>(pb[kc].x), s[2 * kc][1] - hi_to_f32<DT>(pb[kc].x));
+                    pt[kc].y = pack2<DT>(s[2 * kc][2] - lo_to_f32<DT>(pb[kc].y), s[2 * kc][3] - hi_to_f32<DT>(pb[kc].y));
+                    pt[kc].z = pack2<DT>(s[2 * kc + 1][0] - lo_to_f32<DT>(pb[kc].z), s[2 * kc + 1][1] - hi_to_f32<DT>(pb[kc].z));
+                    pt[kc].w = pack2<DT>(s[2 * kc + 1][2] - lo_to_f32<DT>(pb[kc].w), s[2 * kc + 1][3] - hi_to_f32<DT>(pb[kc].w));
+                }
             }
 
             // ---- O^T += V^T P^T; V^T fragments by transposed LDS reads of the row-major V tile
@@ -242,11 +336,16 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
                         (ps16x4_t __attribute__((address_space(3)))*)(vbuf + (32 * kc + 16) * kVRow + 16 * mt));
                     const uint2 l2 = __builtin_bit_cast(uint2, lo);
                     const uint2 h2 = __builtin_bit_cast(uint2, hi);
-                    o[mt] = mfma16x16x32<DT>(make_uint4(l2.x, l2.y, h2.x, h2.y), pb[kc], o[mt]);
+                    const uint4 va = make_uint4(l2.x, l2.y, h2.x, h2.y);
+                    o[mt] = mfma16x16x32<DT>(va, pb[kc], o[mt]);
+                    if constexpr (F8) o[mt] = mfma16x16x32<DT>(va, pt[kc], o[mt]);
                 }
             }
         }
-        if (more) store_tile(buf ^ 1, gk, gv);
+        if (more) {
+            if constexpr (F8) store_tile8(buf ^ 1, ck8, cv8, ksc, vsc);
+            else store_tile(buf ^ 1, gk, gv);
+        }
     }
 
     if (!wave_live) return;
@@ -268,26 +367,30 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     }
 }
 
-template <int DT>
+template <int DT, bool F8>
 static void launch_prefill_g(const PrefillArgs& a, hipStream_t s, dim3 grid) {
     switch (a.group) {
-        case 1: hipLaunchKernelGGL((prefill_kernel<DT, 1>), grid, dim3(512), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<DT, 2>), grid, dim3(512), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((prefill_kernel<DT, 4>), grid, dim3(512), 0, s, a); break;
-        default: hipLaunchKernelGGL((prefill_kernel<DT, 8>), grid, dim3(512), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((prefill_kernel<DT, 1, F8>), grid, dim3(512), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<DT, 2, F8>), grid, dim3(512), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((prefill_kernel<DT, 4, F8>), grid, dim3(512), 0, s, a); break;
+        default: hipLaunchKernelGGL((prefill_kernel<DT, 8, F8>), grid, dim3(512), 0, s, a); break;
     }
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
+template <bool F8>
+static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
     const int positions = kRows / a.group;
     const int64_t qtiles = (a.max_q_len + positions - 1) / positions;
     const int64_t wgs = qtiles * a.num_seqs * a.num_kv_heads;
     if (wgs == 0) return hipSuccess;
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs);
-    if (a.dtype == kF16) launch_prefill_g<kF16>(a, s, grid);
-    else launch_prefill_g<kBF16>(a, s, grid);
+    if (a.dtype == kF16) launch_prefill_g<kF16, F8>(a, s, grid);
+    else launch_prefill_g<kBF16, F8>(a, s, grid);
     return hipGetLastError();
 }
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) { return launch_prefill_t<false>(a, s); }
+hipError_t launch_prefill_fp8(const PrefillArgs& a, hipStream_t s) { return launch_prefill_t<true>(a, s); }
 
 }  // namespace pa

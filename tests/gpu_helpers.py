@@ -158,3 +158,55 @@ class Fp8DecodeOnGPU:
         pa.pa_decode_fp8(out, self.q, self.k_cache, self.v_cache, self.k_scales, self.v_scales,
                          self.tables, self.lens, self.case.scale, partition_tokens, flags=flags)
         return out
+
+
+class Fp8PrefillOnGPU:
+    """A chunked-prefill workload over an FP8 cache: every token the chunk
+    reads (cached context and the chunk's own) is quantised by the FP8 cache
+    write from the case's 16-bit k/v, into NaN-poisoned code and scale pools."""
+
+    def __init__(self, case):
+        import oracle
+        self.case = case
+        dt = case.dtype
+        kc16, vc16 = oracle.ref_reshape_and_cache(case.key, case.value, case.k_cache, case.v_cache,
+                                                  case.slot_mapping)
+        lens = case.ctx_lens.astype(np.int64) + case.q_lens.astype(np.int64)
+        self.slots_np = live_slots(case.block_tables, lens)
+        blk, off = self.slots_np // 16, self.slots_np % 16
+        self.key_np = np.ascontiguousarray(kc16[blk, off])
+        self.value_np = np.ascontiguousarray(vc16[blk, off])
+        nb, hkv, d = case.num_blocks, case.num_kv_heads, case.head_dim
+        self.codes0 = np.full((nb, 16, hkv, d), 0x7F, np.uint8)
+        self.scales0 = np.full((nb, hkv, 16), np.nan, np.float32)
+        self.q = dev_bits(case.q, dt)
+        self.key = dev_bits(self.key_np, dt)
+        self.value = dev_bits(self.value_np, dt)
+        self.slots = dev_int(self.slots_np, torch.int64)
+        self.k_cache = torch.from_numpy(self.codes0).cuda()
+        self.v_cache = torch.from_numpy(self.codes0).cuda()
+        self.k_scales = torch.from_numpy(self.scales0).cuda()
+        self.v_scales = torch.from_numpy(self.scales0).cuda()
+        self.tables = dev_int(case.block_tables)
+        self.ctx = dev_int(case.ctx_lens)
+        self.qsl = dev_int(case.query_start_loc)
+        self.out = torch.zeros_like(self.q)
+
+    def write(self):
+        import paged_kv_cache_24_amd as pa
+        pa.pa_reshape_and_cache_fp8(self.key, self.value, self.k_cache, self.v_cache, self.k_scales,
+                                    self.v_scales, self.slots)
+
+    def oracle_pools(self):
+        import oracle
+        return oracle.ref_reshape_and_cache_fp8(self.key_np, self.value_np, self.codes0, self.codes0,
+                                                self.scales0, self.scales0, self.slots_np,
+                                                self.case.dtype)
+
+    def prefill(self, out=None):
+        import paged_kv_cache_24_amd as pa
+        out = self.out if out is None else out
+        pa.pa_prefill_paged_fp8(out, self.q, self.k_cache, self.v_cache, self.k_scales, self.v_scales,
+                                self.tables, self.ctx, self.qsl, self.case.scale,
+                                max(self.case.max_q_len, 1))
+        return out

@@ -33,7 +33,7 @@ def test_header_declares_the_calls():
               "pa_kv_bytes_per_token", "pa_status_string", "pa_decode_partitions",
               "pa_decode_merge", "pa_decode_default_partition", "pa_copy_blocks",
               "pa_reshape_and_cache_fp8", "pa_copy_blocks_fp8", "pa_decode_fp8",
-              "pa_decode_partitions_fp8"]:
+              "pa_decode_partitions_fp8", "pa_prefill_paged_fp8"]:
         assert n in names
 
 
@@ -244,3 +244,23 @@ def test_decode_fp8_rejects(lib, fn):
     assert call(vs=FAKE + 4) == ALIGN
     assert call(b=0, ks=None) == PA_OK
     assert call(part=256, ws=None) == WS
+
+
+def test_prefill_fp8_rejects(lib):
+    f = lib.pa_prefill_paged_fp8
+    f.restype = ctypes.c_int32
+    f.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int64, ctypes.c_float, ctypes.c_int32, P]
+
+    def call(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, cl=FAKE, qsl=FAKE, b=2,
+             t=64, mq=40, hq=32, hkv=8, d=128, bs=16, mb=16, nb=64, scale=0.1, dt=BF16):
+        return f(out, q, kc, vc, ks, vs, bt, cl, qsl, b, t, mq, hq, hkv, d, bs, mb, nb, scale, dt, None)
+    assert call(ks=None) == NULL
+    assert call(vs=None) == NULL
+    assert call(qsl=None) == NULL
+    assert call(d=64) == UNSUP
+    assert call(hq=24, hkv=8) == UNSUP
+    assert call(scale=0.0) == SHAPE
+    assert call(vs=FAKE + 4) == ALIGN
+    assert call(t=0, ks=None) == PA_OK

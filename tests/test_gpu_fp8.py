@@ -9,11 +9,12 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import (TOL, Fp8DecodeOnGPU, assert_close, dev_bits, dev_int, host_bits, host_f64,
+from gpu_helpers import (TOL, Fp8DecodeOnGPU, Fp8PrefillOnGPU, assert_close, dev_bits, dev_int, host_bits, host_f64,
                          require_gpu)
 from oracle_pins_fp8 import tie_rows_f16
 from workloads import (decode_gqa_shared_prefix, decode_llama2_7b_layer, decode_long_context,
-                       decode_tiny, make_decode_case, normal_bits)
+                       decode_tiny, make_decode_case, make_prefill_case, normal_bits,
+                       prefill_chunked)
 
 pytestmark = pytest.mark.gpu
 
@@ -223,3 +224,49 @@ def test_fp8_empty_and_zero_lengths():
     g.write()
     out = host_f64(g.decode())
     assert (out[0] == 0).all() and (out[2] == 0).all() and np.isfinite(out).all()
+
+
+def _check_fp8_prefill(c):
+    g = Fp8PrefillOnGPU(c)
+    g.write()
+    torch.cuda.synchronize()
+    kc, vc, ks, vs = g.oracle_pools()
+    np.testing.assert_array_equal(g.k_cache.cpu().numpy(), kc)
+    np.testing.assert_array_equal(g.v_scales.cpu().numpy(), vs)
+    out = host_f64(g.prefill())
+    ref = oracle.ref_prefill_paged_fp8(c.q, kc, vc, ks, vs, c.block_tables, c.ctx_lens,
+                                       c.query_start_loc, c.scale, c.dtype)
+    return assert_close(out, ref, c.dtype, c.name + " fp8")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (8, 2), (16, 2)])
+def test_fp8_prefill_shapes(dtype, hq, hkv):
+    q_lens = [0, 1, 17, 64, 130, 5, 33]
+    ctx = [3, 0, 40, 0, 100, 16, 250]
+    c = make_prefill_case(name=f"prefill-{dtype}-{hq}-{hkv}", seed=400 + hq, dtype=dtype,
+                          num_q_heads=hq, num_kv_heads=hkv, head_dim=128, q_lens=q_lens,
+                          ctx_lens=ctx, scale=1 / math.sqrt(128), extra_blocks=5)
+    _check_fp8_prefill(c)
+
+
+def test_fp8_prefill_chunked_reduced():
+    _check_fp8_prefill(prefill_chunked(batch=4, new_tokens=600, max_ctx=700))
+
+
+def test_fp8_prefill_row_matches_fp8_decode():
+    """The last row of a chunk and a decode of the same position over the same
+    FP8 cache attend to the same keys: they must agree to the tolerance."""
+    import paged_kv_cache_24_amd as pa
+    c = make_prefill_case(name="fp8-row", seed=47, dtype="bf16", num_q_heads=8, num_kv_heads=2,
+                          head_dim=128, q_lens=[37, 70], ctx_lens=[200, 3], scale=0.09)
+    g = Fp8PrefillOnGPU(c)
+    g.write()
+    out = host_f64(g.prefill())
+    for b in range(2):
+        r = int(c.query_start_loc[b + 1]) - 1
+        n = int(c.ctx_lens[b] + c.q_lens[b])
+        dec = torch.empty((1, 8, 128), dtype=torch.bfloat16, device="cuda")
+        pa.pa_decode_fp8(dec, g.q[r:r + 1].contiguous(), g.k_cache, g.v_cache, g.k_scales, g.v_scales,
+                         g.tables[b:b + 1].contiguous(), dev_int(np.array([n], np.int32)), c.scale)
+        assert float(np.abs(host_f64(dec)[0] - out[r]).max()) <= 1e-2
