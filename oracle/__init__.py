@@ -18,6 +18,7 @@ from .paged_attention import (  # noqa: F401
     ref_contiguous_attention,
     ref_decode,
     ref_decode_one,
+    ref_decode_multi,
     ref_prefill_paged,
     ref_prefill_rows,
     ref_partition_state,

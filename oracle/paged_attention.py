@@ -211,6 +211,34 @@ def ref_decode(q, k_cache, v_cache, block_tables, seq_lens, scale, dtype):
     return out
 
 
+def ref_decode_multi(q, k_cache, v_cache, block_tables, seq_lens, scale, dtype):
+    """Decode with several new queries per sequence, as speculative decoding
+    verifies its draft tokens: the k proposed tokens plus the last accepted one
+    are scored in one pass over the cache ["vLLM-Ascend 原理", §四, the
+    speculative-decoding paragraphs: the target model checks all k draft
+    tokens at once, like a small prefill].
+
+    ``q``: ``[B, Q, Hq, D]`` bits.  ``seq_lens[b] = n`` counts every cached token
+    including the Q new ones (already written); query ``j`` sits at position
+    ``n - Q + j`` and sees keys ``0 .. n - Q + j`` (causal among the new
+    tokens).  A query whose position is negative (``n < Q - j``) gives zeros.
+    Returns float64 ``[B, Q, Hq, D]``.
+    """
+    bsz, nq, hq, d = q.shape
+    out = np.zeros(q.shape, np.float64)
+    for b in range(bsz):
+        n = int(seq_lens[b])
+        pos = n - nq + np.arange(nq)
+        live = np.flatnonzero(pos >= 0)
+        if live.size == 0:
+            continue
+        k = bits_to_float64(gather_tokens(k_cache, block_tables[b], n), dtype)
+        v = bits_to_float64(gather_tokens(v_cache, block_tables[b], n), dtype)
+        qb = bits_to_float64(q[b, live], dtype)
+        out[b, live] = ref_contiguous_attention(qb, k, v, scale, pos[live])
+    return out
+
+
 def ref_prefill_rows(q, k_cache, v_cache, table_row, ctx_len, row_start, rows,
                      scale, dtype):
     """Chunked-prefill attention for some rows of one sequence.

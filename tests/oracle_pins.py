@@ -313,6 +313,53 @@ def pin_copy_on_write_fork_golden(o):
     np.testing.assert_array_equal(same, kc)                                # negative entries skip
 
 
+# ------------------------------------------- multi-query (verification) decode
+
+def _multi_case(seed=25, dtype="bf16", nq=4, lens=(1, 3, 4, 5, 16, 17, 40, 33, 0), hq=8, hkv=2, d=16):
+    """A decode case whose sequences carry ``nq`` new queries each."""
+    c = make_decode_case(name="pin-multi", seed=seed, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv,
+                         head_dim=d, seq_lens=list(lens), num_blocks=30, max_blocks_per_seq=4,
+                         scale=0.3, write_last=False)
+    q = normal_bits(np.random.default_rng(seed + 1), (len(lens), nq, hq, d), dtype)
+    return c, q
+
+
+def pin_multi_query_equals_chunked_prefill(o):
+    """Q queries at positions n-Q .. n-1 are a prefill chunk of Q rows over a
+    context of n-Q cached tokens (sequences with n >= Q)."""
+    c, q = _multi_case()
+    nq = q.shape[1]
+    got = o.ref_decode_multi(q, c.k_cache, c.v_cache, c.block_tables, c.seq_lens, c.scale, "bf16")
+    keep = [b for b in range(c.num_seqs) if int(c.seq_lens[b]) >= nq]
+    ctx = np.array([int(c.seq_lens[b]) - nq for b in keep], np.int32)
+    qsl = np.arange(len(keep) + 1, dtype=np.int32) * nq
+    pre = o.ref_prefill_paged(q[keep].reshape(-1, *q.shape[2:]), c.k_cache, c.v_cache,
+                              c.block_tables[keep], ctx, qsl, c.scale, "bf16")
+    np.testing.assert_allclose(got[keep].reshape(pre.shape), pre, rtol=0, atol=1e-13)
+
+
+def pin_multi_query_rows_are_rolled_back_decodes(o):
+    """Row j equals a plain decode of the same query with seq_len n - Q + j + 1:
+    rejecting drafts is just a shorter sequence; rows before the first token
+    are zero; one query per sequence is plain decode."""
+    c, q = _multi_case(seed=26, dtype="f16")
+    nq = q.shape[1]
+    got = o.ref_decode_multi(q, c.k_cache, c.v_cache, c.block_tables, c.seq_lens, c.scale, "f16")
+    for b in range(c.num_seqs):
+        n = int(c.seq_lens[b])
+        for j in range(nq):
+            lim = n - nq + j + 1
+            if lim <= 0:
+                np.testing.assert_array_equal(got[b, j], 0.0)
+                continue
+            dec = o.ref_decode(q[b:b + 1, j], c.k_cache, c.v_cache, c.block_tables[b:b + 1],
+                               np.array([lim]), c.scale, "f16")
+            np.testing.assert_allclose(got[b, j], dec[0], rtol=0, atol=1e-13)
+    one = o.ref_decode_multi(q[:, :1], c.k_cache, c.v_cache, c.block_tables, c.seq_lens, c.scale, "f16")
+    np.testing.assert_array_equal(one[:, 0], o.ref_decode(q[:, 0], c.k_cache, c.v_cache, c.block_tables,
+                                                          c.seq_lens, c.scale, "f16"))
+
+
 # ------------------------------------------------------------ chunked prefill
 
 def _small_prefill(seed=31, q_lens=(5, 0, 17, 1, 33), ctx=(0, 9, 20, 15, 40)):

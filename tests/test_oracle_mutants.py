@@ -42,6 +42,9 @@ MUTANTS = {
     "copy_blocks_reversed": ("        kc[b] = k_cache[a]\n        vc[b] = v_cache[a]",
                              "        kc[a] = k_cache[b]\n        vc[a] = v_cache[b]"),
     "copy_blocks_v_from_k": ("        vc[b] = v_cache[a]", "        vc[b] = k_cache[a]"),
+    "multi_query_positions_from_start": ("        pos = n - nq + np.arange(nq)\n", "        pos = np.arange(nq) + n - nq - 1\n"),
+    "multi_query_no_causal_among_new": ("out[b, live] = ref_contiguous_attention(qb, k, v, scale, pos[live])",
+                                        "out[b, live] = ref_contiguous_attention(qb, k, v, scale, np.full(len(live), n - 1))"),
 }
 
 
