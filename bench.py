@@ -498,6 +498,52 @@ def _secondary_copy_blocks(steps, warmup, pairs_n=2048):
             "pct_hbm_peak": round(100 * moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)}
 
 
+def _secondary_multi(steps, warmup, nq=4):
+    """Draft-token verification: the LLaMA-2-7B-shaped decode layer with nq
+    queries per sequence (nq - 1 drafts plus the last accepted token), one
+    pass over each sequence's cache."""
+    import torch
+    import paged_kv_cache_24_amd as pa
+    from workloads import decode_llama2_7b_layer
+    c = decode_llama2_7b_layer()
+    run = DecodeRun(c)
+    rng = np.random.default_rng(11)
+    q = torch.from_numpy(rng.standard_normal((c.num_seqs, nq, c.num_q_heads, c.head_dim),
+                                             dtype=np.float32)).to(torch.float16).cuda()
+    out = torch.empty_like(q)
+    need = pa.pa_decode_workspace_size(c.num_seqs * nq, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                                       c.max_blocks_per_seq, run.part)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    if run.has_write:
+        pa.pa_reshape_and_cache(run.key, run.value, run.kc, run.vc, run.slots)
+
+    def step():
+        pa.pa_decode_multi(out, q, run.kc, run.vc, run.tables, run.lens, c.scale, run.part, ws,
+                           flags=run.flags)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    timer = _Timer(["multi"])
+    for _ in range(steps):
+        ev = timer.step()
+        ev[0].record()
+        step()
+        ev[1].record()
+    torch.cuda.synchronize()
+    ms = timer.mean_ms()["multi"]
+    kv, _ = run.algorithmic_bytes()
+    run.free()
+    del run, q, out, ws
+    torch.cuda.empty_cache()
+    return {"workload": "decode_llama2_7b_layer_verify", "queries_per_seq": nq, "ms": round(ms, 4),
+            "kv_bytes": kv, "kv_GBs": round(kv / (ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * kv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
+            "query_tokens_per_s": round(c.num_seqs * nq / (ms * 1e-3), 1),
+            "note": "all queries of a sequence share one read of its K/V (matrix-core kernel: "
+                    "4 (query, head) columns per kv head)"}
+
+
 def _copy_calibration():
     import torch
     n = 1 << 30
@@ -589,6 +635,7 @@ def main():
         sec.append(_secondary_decode(decode_long_context, "decode_long_context_fp8", s2, w2,
                                      fp8=True))
         sec.append(_secondary_prefill(s2, w2, fp8=True))
+        sec.append(_secondary_multi(s2, w2))
         result["secondary"] = sec
     result["input_generation_s"] = round(gen_s, 1)
     print(json.dumps(result), flush=True)

@@ -196,6 +196,33 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pa_decode_multi -- paged decode with several new queries per sequence, as
+ * speculative decoding verifies its draft tokens: the target model scores the
+ * k proposed tokens (and the last accepted one) in one pass, like a small
+ * prefill ("vLLM-Ascend 原理", §四, the speculative-decoding paragraphs).  Each
+ * K/V tile is read once for all q_per_seq queries of its sequence.
+ *
+ *   out, q        [num_seqs][q_per_seq][num_q_heads][head_dim]; query j of
+ *                 sequence b sits at position seq_lens[b] - q_per_seq + j and
+ *                 sees keys 0 .. seq_lens[b] - q_per_seq + j (causal among the
+ *                 new tokens, whose k/v are already in the cache).  A query
+ *                 whose position is negative gives an all-zero row.
+ *   q_per_seq     1 .. PA_MAX_QUERIES_PER_SEQ (1 is exactly pa_decode).
+ *   workspace     pa_decode_workspace_size(num_seqs * q_per_seq, ...) bytes.
+ *
+ * Rejecting drafts needs no work here: the next step simply passes the
+ * shorter seq_lens.  Every other argument and rule as for pa_decode.
+ */
+#define PA_MAX_QUERIES_PER_SEQ 16
+pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                          int32_t q_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                          int64_t num_blocks, float scale, pa_dtype dtype, int32_t partition_tokens,
+                          uint32_t flags, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
  * pa_decode_partitions / pa_decode_merge -- the two phases of pa_decode, for
  * callers that schedule or time them separately.  Same arguments and
  * contract as pa_decode; the arguments the two calls share must be identical.

@@ -6,7 +6,7 @@ runs in the library's HIP kernels, on torch's current stream.  There is no
 fallback: if ``libpa.so`` is missing, importing this package raises.
 
 Names follow the C ABI: ``pa_reshape_and_cache``, ``pa_copy_blocks``, ``pa_decode``,
-``pa_decode_partitions``, ``pa_decode_merge``, ``pa_prefill_paged``,
+``pa_decode_partitions``, ``pa_decode_merge``, ``pa_decode_multi``, ``pa_prefill_paged``,
 ``pa_decode_workspace_size``, ``pa_decode_default_partition``,
 ``pa_kv_bytes_per_token``, ``pa_status_string``, and for an FP8 (E4M3) cache
 ``pa_reshape_and_cache_fp8``, ``pa_copy_blocks_fp8``, ``pa_decode_fp8``,
@@ -26,7 +26,7 @@ __all__ = [
     "pa_decode_default_partition", "pa_decode_workspace_size", "pa_decode",
     "pa_decode_partitions", "pa_decode_merge", "pa_prefill_paged",
     "pa_reshape_and_cache_fp8", "pa_copy_blocks_fp8", "pa_decode_fp8", "pa_decode_partitions_fp8",
-    "pa_prefill_paged_fp8",
+    "pa_prefill_paged_fp8", "pa_decode_multi",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
@@ -54,6 +54,8 @@ _SIGS = {
                          _f32, _i32, _i32, _u32, _vp, _sz, _vp]),
     "pa_decode_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _i64, _f32, _i32, _i32, _u32, _vp, _sz, _vp]),
+    "pa_decode_multi": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _i64, _f32, _i32, _i32, _u32, _vp, _sz, _vp]),
     "pa_decode_merge": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz,
                                _vp]),
     "pa_prefill_paged": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
@@ -208,6 +210,33 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, partition
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), b, hq,
         hkv, d, bs, mb, nb, float(scale), _kv_dtype(k_cache), partition_tokens, flags, _ptr(ws), ws_bytes,
         _stream(stream)))
+    return out
+
+
+def pa_decode_multi(out, q, k_cache, v_cache, block_tables, seq_lens, scale, partition_tokens=0,
+                    workspace=None, stream=None, flags=0):
+    """Decode with several new queries per sequence (draft-token verification):
+    ``q``/``out`` are ``[B, Q, Hq, D]``; query ``j`` of sequence ``b`` sits at position
+    ``seq_lens[b] - Q + j`` and sees the keys up to it."""
+    _need(k_cache, "k_cache", ndim=4)
+    _need(v_cache, "v_cache", k_cache.dtype, 4)
+    _need(q, "q", k_cache.dtype, 4)
+    _need(out, "out", k_cache.dtype, 4)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(seq_lens, "seq_lens", torch.int32, 1)
+    nb, bs, hkv, d = k_cache.shape
+    b, nq, hq, dq = q.shape
+    if v_cache.shape != k_cache.shape or out.shape != q.shape or dq != d:
+        raise ValueError("q/out/cache shapes disagree")
+    if block_tables.shape[0] != b or seq_lens.shape[0] != b:
+        raise ValueError("block_tables and seq_lens need one row per sequence")
+    mb = block_tables.shape[1]
+    need = pa_decode_workspace_size(b * nq, hq, hkv, d, mb, partition_tokens)
+    ws, ws_bytes = _workspace(workspace, need, q.device)
+    _check("pa_decode_multi", lib.pa_decode_multi(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), b, nq,
+        hq, hkv, d, bs, mb, nb, float(scale), _kv_dtype(k_cache), partition_tokens, flags, _ptr(ws),
+        ws_bytes, _stream(stream)))
     return out
 
 

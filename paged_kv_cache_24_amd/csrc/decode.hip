@@ -30,7 +30,9 @@
 
 namespace pa {
 
-template <int DT, int D, int HPW, bool NT>
+// MQ: several queries per sequence (see decode_gqa_kernel); the columns of a
+// kv head are (query, q head) pairs and each sees keys up to its own position.
+template <int DT, int D, int HPW, bool NT, bool MQ>
 __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
     constexpr int LPR = D / 8;              // lanes per token row
     constexpr int RPW = kWave / LPR;        // token rows per load instruction
@@ -60,15 +62,31 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
     const int j1 = min(nblk, j0 + a.part_blocks);
 
     const int hbase = hc * HPW;
-    const int hcount = min(HPW, a.group - hbase);
+    const int hcount = min(HPW, (MQ ? a.cols : a.group) - hbase);
     const int64_t q_row0 = (int64_t)b * a.num_q_heads + (int64_t)g * a.group + hbase;
+    // q / out row of column h; with MQ also the keys it may see
+    int64_t qrow[HPW];
+    int lim[HPW];
+#pragma unroll
+    for (int h = 0; h < HPW; ++h) {
+        if constexpr (MQ) {
+            const int col = hbase + h;
+            const int jq = col / a.group;
+            qrow[h] = ((int64_t)b * a.q_per_seq + jq) * a.num_q_heads + (int64_t)g * a.group + col % a.group;
+            lim[h] = n - a.q_per_seq + 1 + jq;
+        } else {
+            qrow[h] = q_row0 + h;
+            lim[h] = n;
+        }
+    }
+    const int lim_min = MQ ? n - a.q_per_seq + 1 : n;   // keys every column sees
 
     uint4 qv[HPW];
     {
-        const uint16_t* q = static_cast<const uint16_t*>(a.q) + q_row0 * D + 8 * c;
+        const uint16_t* q = static_cast<const uint16_t*>(a.q) + 8 * c;
 #pragma unroll
         for (int h = 0; h < HPW; ++h)
-            qv[h] = h < hcount ? *reinterpret_cast<const uint4*>(q + (int64_t)h * D)
+            qv[h] = h < hcount ? *reinterpret_cast<const uint4*>(q + qrow[h] * D)
                                : make_uint4(0, 0, 0, 0);
     }
 
@@ -118,13 +136,15 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
             }
         }
         // rows past the sequence end (tail block) or in a bad block: score -inf,
-        // value 0 (a select, so NaN bits there cannot leak into the sums)
-        if (!(ok && (j + 1) * kBlockSize <= n)) {
+        // value 0 (a select, so NaN bits there cannot leak into the sums); with
+        // MQ a column also masks the keys past its own position
+        if (!(ok && (j + 1) * kBlockSize <= lim_min)) {
 #pragma unroll
             for (int i = 0; i < TPL; ++i) {
-                const bool valid = ok && (j * kBlockSize + i * RPW + r < n);
+                const int tok = j * kBlockSize + i * RPW + r;
+                const bool valid = ok && (tok < n);
 #pragma unroll
-                for (int h = 0; h < HPW; ++h) s[h][i] = valid ? s[h][i] : -INFINITY;
+                for (int h = 0; h < HPW; ++h) s[h][i] = (ok && tok < lim[h]) ? s[h][i] : -INFINITY;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) vf[i][e] = valid ? vf[i][e] : 0.f;
             }
@@ -206,13 +226,13 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
             o.y = pack2<DT>(acc[h][2] * inv, acc[h][3] * inv);
             o.z = pack2<DT>(acc[h][4] * inv, acc[h][5] * inv);
             o.w = pack2<DT>(acc[h][6] * inv, acc[h][7] * inv);
-            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + (q_row0 + h) * D + 8 * c) = o;
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + qrow[h] * D + 8 * c) = o;
         }
     } else {
 #pragma unroll
         for (int h = 0; h < HPW; ++h) {
             if (h >= hcount) break;
-            const int64_t idx = (q_row0 + h) * a.num_parts + part;
+            const int64_t idx = qrow[h] * a.num_parts + part;
             float4* dst = reinterpret_cast<float4*>(a.ws_acc + idx * D + 8 * c);
             dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
             dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
@@ -273,7 +293,12 @@ __device__ __forceinline__ df32x4_t mfma_16x16x16(const uint2& a, const uint2& b
 
 constexpr int kVRow = 144;   // LDS row stride of the V tile (elements): 288 B staggers banks
 
-template <int DT, bool NT>
+// MQ: several queries per sequence, as speculative decoding verifies its draft
+// tokens ("vLLM-Ascend 原理", §四 on speculative decoding: all draft tokens are
+// checked in one pass).  Column c of the kv head is query c / group and q head
+// c % group; query jq sits at position n - Q + jq and sees keys up to it, so
+// each K/V tile is read once for every query of the sequence.
+template <int DT, bool NT, bool MQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void decode_gqa_kernel(DecodeArgs a) {
     constexpr int D = 128;
     __shared__ __attribute__((aligned(16))) uint16_t vlds[4][kBlockSize * kVRow];
@@ -301,13 +326,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     if (part >= nparts) return;
     const int j0 = part * a.part_blocks;
     const int j1 = min(nblk, j0 + a.part_blocks);
-    const int hcount = min(16, a.group - hc * 16);
-    const int64_t q_row0 = (int64_t)b * a.num_q_heads + (int64_t)g * a.group + hc * 16;
+    const int hcount = min(16, (MQ ? a.cols : a.group) - hc * 16);
     const bool head_live = lr < hcount;
+    // q / out row of this lane's column, and (MQ) the keys the column may see
+    int64_t my_row;
+    int lim;
+    if constexpr (MQ) {
+        const int col = hc * 16 + (head_live ? lr : 0);
+        const int jq = col / a.group;
+        my_row = ((int64_t)b * a.q_per_seq + jq) * a.num_q_heads + (int64_t)g * a.group + col % a.group;
+        lim = n - a.q_per_seq + 1 + jq;
+    } else {
+        my_row = (int64_t)b * a.num_q_heads + (int64_t)g * a.group + hc * 16 + (head_live ? lr : 0);
+        lim = n;
+    }
 
     uint4 qf[4];
     {
-        const uint16_t* q = static_cast<const uint16_t*>(a.q) + (q_row0 + (head_live ? lr : 0)) * D + 8 * lg;
+        const uint16_t* q = static_cast<const uint16_t*>(a.q) + my_row * D + 8 * lg;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
             qf[kk] = head_live ? *reinterpret_cast<const uint4*>(q + 32 * kk) : make_uint4(0, 0, 0, 0);
@@ -352,7 +388,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             valid[i] = full || (ok && (j * kBlockSize + 4 * i + lg < n));
-            x[i] = valid[i] ? sacc[i] * cs : -INFINITY;
+            // MQ: the score of column lr also ends at the column's own position
+            const bool seen = MQ ? (ok && j * kBlockSize + 4 * i + lg < lim) : valid[i];
+            x[i] = seen ? sacc[i] * cs : -INFINITY;
         }
         float mb = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
         mb = fmaxf(mb, __shfl_xor(mb, 16));
@@ -417,7 +455,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     if (!head_live) return;
     if (nparts == 1) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        uint16_t* dst = static_cast<uint16_t*>(a.out) + (q_row0 + lr) * D + 4 * lg;
+        uint16_t* dst = static_cast<uint16_t*>(a.out) + my_row * D + 4 * lg;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             uint2 w;
@@ -426,7 +464,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
             *reinterpret_cast<uint2*>(dst + 16 * mt) = w;
         }
     } else {
-        const int64_t idx = (q_row0 + lr) * a.num_parts + part;
+        const int64_t idx = my_row * a.num_parts + part;
         float* dst = a.ws_acc + idx * D + 4 * lg;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
@@ -446,9 +484,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     __shared__ float part_num[GROUPS][D];
     __shared__ float part_den[GROUPS];
     const int tid = threadIdx.x;
-    const int64_t item = blockIdx.x;
-    if (item >= (int64_t)a.num_seqs * a.num_q_heads) return;
-    const int b = (int)(item / a.num_q_heads);
+    const int64_t item = blockIdx.x;   // q / out row: (sequence, query, q head)
+    if (item >= (int64_t)a.num_seqs * a.q_per_seq * a.num_q_heads) return;
+    const int b = (int)(item / ((int64_t)a.q_per_seq * a.num_q_heads));
 
     const int max_tokens = a.max_blocks_per_seq * kBlockSize;
     int n = a.seq_lens[b];
@@ -491,26 +529,36 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     static_cast<uint16_t*>(a.out)[item * D + tid] = f32_to_bits<DT>(num * inv);
 }
 
-template <int DT, int D, bool NT>
+template <int DT, int D, bool NT, bool MQ>
 static hipError_t launch_partitions_d(const DecodeArgs& a, hipStream_t s, dim3 grid) {
     switch (a.heads_per_wave) {
-        case 1: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 1, NT>), grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 2, NT>), grid, dim3(256), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 4, NT>), grid, dim3(256), 0, s, a); break;
-        case 8: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 8, NT>), grid, dim3(256), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 1, NT, MQ>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 2, NT, MQ>), grid, dim3(256), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 4, NT, MQ>), grid, dim3(256), 0, s, a); break;
+        case 8: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 8, NT, MQ>), grid, dim3(256), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <int DT, bool NT>
+template <int DT, bool NT, bool MQ>
 static hipError_t launch_partitions_t(const DecodeArgs& a, hipStream_t s, dim3 grid) {
     if (a.gqa_mfma) {
-        hipLaunchKernelGGL((decode_gqa_kernel<DT, NT>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((decode_gqa_kernel<DT, NT, MQ>), grid, dim3(256), 0, s, a);
         return hipGetLastError();
     }
-    return a.head_dim == 128 ? launch_partitions_d<DT, 128, NT>(a, s, grid)
-                             : launch_partitions_d<DT, 64, NT>(a, s, grid);
+    return a.head_dim == 128 ? launch_partitions_d<DT, 128, NT, MQ>(a, s, grid)
+                             : launch_partitions_d<DT, 64, NT, MQ>(a, s, grid);
+}
+
+template <bool MQ>
+static hipError_t launch_partitions_mq(const DecodeArgs& a, hipStream_t s, dim3 grid) {
+    if (a.dtype == kF16) {
+        return a.stream_kv ? launch_partitions_t<kF16, true, MQ>(a, s, grid)
+                           : launch_partitions_t<kF16, false, MQ>(a, s, grid);
+    }
+    return a.stream_kv ? launch_partitions_t<kBF16, true, MQ>(a, s, grid)
+                       : launch_partitions_t<kBF16, false, MQ>(a, s, grid);
 }
 
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t s) {
@@ -519,16 +567,11 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t s) {
     const int64_t wgs = (items + 3) / 4;
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs);
-    if (a.dtype == kF16) {
-        return a.stream_kv ? launch_partitions_t<kF16, true>(a, s, grid)
-                           : launch_partitions_t<kF16, false>(a, s, grid);
-    }
-    return a.stream_kv ? launch_partitions_t<kBF16, true>(a, s, grid)
-                       : launch_partitions_t<kBF16, false>(a, s, grid);
+    return a.q_per_seq > 1 ? launch_partitions_mq<true>(a, s, grid) : launch_partitions_mq<false>(a, s, grid);
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {
-    const int64_t items = (int64_t)a.num_seqs * a.num_q_heads;
+    const int64_t items = (int64_t)a.num_seqs * a.q_per_seq * a.num_q_heads;
     if (items == 0 || a.num_parts <= 1) return hipSuccess;
     if (items > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)items);

@@ -76,6 +76,10 @@ struct DecodeArgs {
     // FP8 cache only: per (block, kv head, token) float32 scales
     const float* k_scales;   // [NB][Hkv][16]
     const float* v_scales;
+    // several queries per sequence (draft verification): column c of a kv head
+    // is query c / group, q head c % group; 1 and group for plain decode
+    int32_t q_per_seq;
+    int32_t cols;
 };
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_partitions_fp8(const DecodeArgs& a, hipStream_t stream);

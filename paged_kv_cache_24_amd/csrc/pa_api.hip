@@ -94,7 +94,7 @@ pa::DecodeArgs decode_args(void* out, const void* q, const void* k_cache, const 
                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                            int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
                            pa_dtype dtype, const DecodeShape& shape, void* workspace,
-                           uint32_t flags) {
+                           uint32_t flags, int32_t q_per_seq = 1) {
     pa::DecodeArgs a;
     a.out = out;
     a.q = q;
@@ -106,12 +106,14 @@ pa::DecodeArgs decode_args(void* out, const void* q, const void* k_cache, const 
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = num_kv_heads;
     a.group = num_q_heads / num_kv_heads;
-    // 3 or more q heads per kv head make QK^T and PV real contractions: matrix cores
-    a.gqa_mfma = uses_gqa_kernel(num_q_heads, num_kv_heads, head_dim);
-    a.heads_per_wave = a.gqa_mfma ? 16 : heads_per_wave(a.group);
+    a.q_per_seq = q_per_seq;
+    a.cols = q_per_seq * a.group;   // (query, q head) columns per kv head
+    // 3 or more columns per kv head make QK^T and PV real contractions: matrix cores
+    a.gqa_mfma = head_dim == 128 && a.cols >= 3;
+    a.heads_per_wave = a.gqa_mfma ? 16 : heads_per_wave(a.cols);
     a.k_scales = nullptr;
     a.v_scales = nullptr;
-    a.head_chunks = ceil_div(a.group, a.heads_per_wave);
+    a.head_chunks = ceil_div(a.cols, a.heads_per_wave);
     a.head_dim = head_dim;
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.num_blocks = num_blocks;
@@ -121,7 +123,7 @@ pa::DecodeArgs decode_args(void* out, const void* q, const void* k_cache, const 
     a.dtype = dtype == PA_F16 ? pa::kF16 : pa::kBF16;
     a.stream_kv = (flags & PA_DECODE_STREAM_KV) != 0;
     float* ws = static_cast<float*>(workspace);
-    const size_t states = (size_t)num_seqs * num_q_heads * shape.num_parts;
+    const size_t states = (size_t)num_seqs * q_per_seq * num_q_heads * shape.num_parts;
     a.ws_acc = shape.ws_bytes ? ws : nullptr;
     a.ws_ml = shape.ws_bytes ? reinterpret_cast<float2*>(ws + states * head_dim) : nullptr;
     return a;
@@ -372,6 +374,35 @@ pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache, const voi
     return pa_decode_merge(out, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                            block_size, max_blocks_per_seq, dtype, partition_tokens, workspace,
                            workspace_bytes, stream);
+}
+
+pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                          int32_t q_per_seq, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                          int64_t num_blocks, float scale, pa_dtype dtype, int32_t partition_tokens,
+                          uint32_t flags, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+    if (flags & ~PA_DECODE_STREAM_KV) return PA_ERR_UNSUPPORTED;
+    if (q_per_seq < 1 || q_per_seq > PA_MAX_QUERIES_PER_SEQ) return PA_ERR_SHAPE;
+    pa_status st = check_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+                                num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_blocks_per_seq, num_blocks, scale, dtype, partition_tokens);
+    if (st != PA_OK || num_seqs == 0) return st;
+    if ((int64_t)num_seqs * q_per_seq > INT32_MAX) return PA_ERR_SHAPE;
+    // the partial states are per (sequence, query, q head): the workspace of
+    // num_seqs * q_per_seq single-query sequences
+    const DecodeShape shape = decode_shape(num_seqs * q_per_seq, num_q_heads, num_kv_heads,
+                                           head_dim, max_blocks_per_seq, partition_tokens);
+    st = check_workspace(shape, workspace, workspace_bytes);
+    if (st != PA_OK) return st;
+    const pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, seq_lens,
+                                         num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                         max_blocks_per_seq, num_blocks, scale, dtype, shape,
+                                         workspace, flags, q_per_seq);
+    if (pa::launch_decode_partitions(a, stream) != hipSuccess) return PA_ERR_HIP;
+    if (shape.num_parts <= 1) return PA_OK;
+    return pa::launch_decode_merge(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

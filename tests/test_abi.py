@@ -33,7 +33,7 @@ def test_header_declares_the_calls():
               "pa_kv_bytes_per_token", "pa_status_string", "pa_decode_partitions",
               "pa_decode_merge", "pa_decode_default_partition", "pa_copy_blocks",
               "pa_reshape_and_cache_fp8", "pa_copy_blocks_fp8", "pa_decode_fp8",
-              "pa_decode_partitions_fp8", "pa_prefill_paged_fp8"]:
+              "pa_decode_partitions_fp8", "pa_prefill_paged_fp8", "pa_decode_multi"]:
         assert n in names
 
 
@@ -264,3 +264,25 @@ def test_prefill_fp8_rejects(lib):
     assert call(scale=0.0) == SHAPE
     assert call(vs=FAKE + 4) == ALIGN
     assert call(t=0, ks=None) == PA_OK
+
+
+def test_decode_multi_rejects(lib):
+    f = lib.pa_decode_multi
+    f.restype = ctypes.c_int32
+    f.argtypes = [P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_uint32, P, ctypes.c_size_t, P]
+
+    def call(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, b=2, nq=4, hq=8, hkv=2, d=128,
+             bs=16, mb=64, nb=128, scale=0.1, dt=BF16, part=0, flags=0, ws=FAKE, wsb=1 << 30):
+        return f(out, q, kc, vc, bt, sl, b, nq, hq, hkv, d, bs, mb, nb, scale, dt, part, flags, ws, wsb,
+                 None)
+    assert call(nq=0) == SHAPE
+    assert call(nq=17) == SHAPE
+    assert call(q=None) == NULL
+    assert call(d=96) == UNSUP
+    assert call(flags=8) == UNSUP
+    assert call(scale=-1.0) == SHAPE
+    assert call(b=0, q=None) == PA_OK
+    assert call(part=256, ws=None) == WS
+    assert call(part=256, wsb=16) == WS
