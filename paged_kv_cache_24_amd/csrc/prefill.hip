@@ -134,59 +134,71 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     float lsum = 0.f;   // this lane's share of the row sum
     const float cs = a.scale_log2;
 
-    // ---- K/V tile staging: thread t moves 16-byte chunk (t % 16) of key rows t/16 and
-    // t/16 + 32.  Rows 32 i .. 32 i + 31 of tile tt are blocks 4 tt + 2 i and 4 tt + 2 i + 1.
+    // ---- K/V tile staging.  The block ids of a tile are read through the
+    // constant address space (the kernel never writes the table), so they are
+    // scalar loads, fetched one tile ahead.  Each thread's rows are arranged so
+    // that its block is the same for the whole wave: the block's base address
+    // is scalar and every load is base + a loop-invariant 32-bit lane offset.
+    typedef const __attribute__((address_space(4))) int32_t ctab_t;
+    const ctab_t* ctab = (const ctab_t*)table;
+    auto tile_blocks = [&](int tt, int (&pb)[4]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int blk = tt * 4 + q;
+            pb[q] = blk * kBlockSize < n_keys ? ctab[blk] : -1;
+        }
+    };
+    // 16-bit: thread t moves 16-byte chunk t % 16 of row (t / 16) % 16 of blocks
+    // 2 i + t / 256 (i = 0, 1) of the tile: a wave's two blocks are uniform.
     const int ck = tid & 15;
-    const int krow = tid >> 4;      // 0..31
-    auto load_tile = [&](int tt, uint4 (&gk)[2], uint4 (&gv)[2]) {
+    const int rr = (tid >> 4) & 15;
+    const int half = uniform(tid >> 8);
+    const uint32_t lane_off = (uint32_t)(rr * row_stride + g * kPD + 8 * ck) * 2u;   // bytes
+    auto load_tile = [&](int tt, const int (&pb)[4], uint4 (&gk)[2], uint4 (&gv)[2]) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int blk_a = tt * 4 + 2 * i;   // uniform
-            const int pba = blk_a * kBlockSize < n_keys ? table[blk_a] : -1;
-            const int pbb = (blk_a + 1) * kBlockSize < n_keys ? table[blk_a + 1] : -1;
-            const int pb = krow < 16 ? pba : pbb;
-            const int key = tt * kKT + 32 * i + krow;
-            const bool ok = pb >= 0 && (int64_t)pb < a.num_blocks;
-            const bool valid = ok && key < n_keys;
-            // an invalid row still reads (in bounds) block 0, then is replaced by zeros:
-            // keys past the sequence end must be zeros in LDS, never NaN
-            const int64_t off = ((int64_t)(ok ? pb : 0) * kBlockSize + (krow & 15)) * row_stride +
-                                (int64_t)g * kPD + 8 * ck;
-            const uint4 k4 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_cache) + off);
-            const uint4 v4 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_cache) + off);
-            gk[i] = valid ? k4 : make_uint4(0, 0, 0, 0);
+            const int q = 2 * i + half;
+            const int pbq = half ? pb[2 * i + 1] : pb[2 * i];
+            const bool ok = pbq >= 0 && (int64_t)pbq < a.num_blocks;
+            const int64_t base = (int64_t)(ok ? pbq : 0) * (kBlockSize * row_stride * 2);
+            const uint4 k4 = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_cache) + base + lane_off);
+            const uint4 v4 = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v_cache) + base + lane_off);
+            // rows past the keys or in a bad block: V must be zeros (MFMA would turn
+            // 0 x NaN into NaN); K there only meets masked scores
+            const bool full = ok && tt * kKT + 16 * (q + 1) <= n_keys;   // uniform
+            const bool valid = full || (ok && tt * kKT + 16 * q + rr < n_keys);
+            gk[i] = k4;
             gv[i] = valid ? v4 : make_uint4(0, 0, 0, 0);
         }
     };
     auto store_tile = [&](int buf, const uint4 (&gk)[2], const uint4 (&gv)[2]) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int kr = krow + 32 * i;
+            const int kr = 16 * (2 * i + half) + rr;
             *reinterpret_cast<uint4*>(&lds_k[buf][kr * kKRow + 8 * ck]) = gk[i];
             *reinterpret_cast<uint4*>(&lds_v[buf][kr * kVRow + 8 * ck]) = gv[i];
         }
     };
-    // ---- FP8 staging: thread t moves the 16 codes 16*(t % 8) .. +16 of key row t / 8
-    // (K and V) and that row's two scales.  Invalid rows stage zeros with k scale 0
-    // and v scale 1, so NaN bits in unused slots never reach the products.
+    // ---- FP8 staging: thread t moves the 16 codes 16*(t % 8) .. +16 of key row
+    // t / 8 (block t / 128: uniform per wave) and that row's two scales.  Invalid
+    // rows stage zeros with k scale 0 and v scale 1, so NaN bits in unused slots
+    // never reach the products.
     const int c8 = tid & 7;
     const int kr8 = tid >> 3;       // 0..63
-    auto load_tile8 = [&](int tt, uint4& ck8, uint4& cv8, float& ksc, float& vsc) {
-        int pbs[4];   // the tile's four blocks (uniform table reads), then this row's
-#pragma unroll
-        for (int q = 0; q < 4; ++q) pbs[q] = (tt * 4 + q) * kBlockSize < n_keys ? table[tt * 4 + q] : -1;
-        const int sub = kr8 >> 4;
-        const int pb = sub == 0 ? pbs[0] : sub == 1 ? pbs[1] : sub == 2 ? pbs[2] : pbs[3];
-        const int key = tt * kKT + kr8;
-        const bool ok = pb >= 0 && (int64_t)pb < a.num_blocks;
-        const bool valid = ok && key < n_keys;
-        const int64_t pblk = ok ? pb : 0;
-        const int64_t off = (pblk * kBlockSize + (kr8 & 15)) * row_stride + (int64_t)g * kPD + 16 * c8;
-        const uint4 k4 = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.k_cache) + off);
-        const uint4 v4 = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.v_cache) + off);
-        const int64_t soff = (pblk * a.num_kv_heads + g) * kBlockSize + (kr8 & 15);
-        const float ks = a.k_scales[soff];
-        const float vs = a.v_scales[soff];
+    const int q8 = uniform(tid >> 7);
+    const uint32_t lane_off8 = (uint32_t)((kr8 & 15) * row_stride + g * kPD + 16 * c8);   // bytes
+    const uint32_t lane_soff = (uint32_t)(g * kBlockSize + (kr8 & 15));                  // floats
+    auto load_tile8 = [&](int tt, const int (&pb)[4], uint4& ck8, uint4& cv8, float& ksc, float& vsc) {
+        const int pbq = q8 == 0 ? pb[0] : q8 == 1 ? pb[1] : q8 == 2 ? pb[2] : pb[3];
+        const bool ok = pbq >= 0 && (int64_t)pbq < a.num_blocks;
+        const int64_t pblk = ok ? pbq : 0;
+        const int64_t base = pblk * (kBlockSize * row_stride);
+        const int64_t sbase = pblk * a.num_kv_heads * kBlockSize;
+        const uint4 k4 = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.k_cache) + base + lane_off8);
+        const uint4 v4 = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.v_cache) + base + lane_off8);
+        const float ks = a.k_scales[sbase + lane_soff];
+        const float vs = a.v_scales[sbase + lane_soff];
+        const bool valid = ok && tt * kKT + kr8 < n_keys;
         ck8 = valid ? k4 : make_uint4(0, 0, 0, 0);
         cv8 = valid ? v4 : make_uint4(0, 0, 0, 0);
         ksc = valid ? ks : 0.f;
@@ -218,20 +230,24 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     uint4 gk[2], gv[2];
     uint4 ck8, cv8;
     float ksc = 0.f, vsc = 1.f;
+    int pbn[4];                     // block ids of the next tile to stage
+    tile_blocks(0, pbn);
     if constexpr (F8) {
-        load_tile8(0, ck8, cv8, ksc, vsc);
+        load_tile8(0, pbn, ck8, cv8, ksc, vsc);
         store_tile8(0, ck8, cv8, ksc, vsc);
     } else {
-        load_tile(0, gk, gv);
+        load_tile(0, pbn, gk, gv);
         store_tile(0, gk, gv);
     }
+    if (ntiles > 1) tile_blocks(1, pbn);
     for (int t = 0; t < ntiles; ++t) {
         const int buf = t & 1;
         __syncthreads();   // tile t is in LDS; everybody is done with tile t-1's buffer
         const bool more = t + 1 < ntiles;
         if (more) {   // in flight while this tile is computed
-            if constexpr (F8) load_tile8(t + 1, ck8, cv8, ksc, vsc);
-            else load_tile(t + 1, gk, gv);
+            if constexpr (F8) load_tile8(t + 1, pbn, ck8, cv8, ksc, vsc);
+            else load_tile(t + 1, pbn, gk, gv);
+            if (t + 2 < ntiles) tile_blocks(t + 2, pbn);
         }
         const int k0 = t * kKT;
         if (wave_live && k0 <= wave_q_hi) {
@@ -275,8 +291,7 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int mt = 1; mt < 4; ++mt)
                 mb = fmaxf(mb, fmaxf(fmaxf(s[mt][0], s[mt][1]), fmaxf(s[mt][2], s[mt][3])));
-            mb = fmaxf(mb, __shfl_xor(mb, 16));
-            mb = fmaxf(mb, __shfl_xor(mb, 32));
+            mb = xor32_max(xor16_max(mb));
             const float mbs = mb * cs;
             const bool raise = mbs > m + 8.f;   // also true on the first live tile
             const float mn = raise ? mbs : m;
@@ -350,9 +365,7 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
 
     if (!wave_live) return;
     // ---- epilogue: full row sum, normalise, store the row if it exists
-    float l = lsum;
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = xor32_sum(xor16_sum(lsum));
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int pos = pos0 + rho / G;
     if (pos >= L) return;
