@@ -79,11 +79,17 @@ class _Timer:
         self.events.append(ev)
         return ev
 
+    def samples(self, name):
+        i = self.names.index(name)
+        return np.array([ev[i].elapsed_time(ev[i + 1]) for ev in self.events])
+
     def mean_ms(self):
-        out = {}
-        for i, n in enumerate(self.names):
-            out[n] = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in self.events]))
-        return out
+        return {n: float(np.mean(self.samples(n))) for n in self.names}
+
+    def spread_ms(self, name):
+        x = self.samples(name)
+        return {"p10": round(float(np.percentile(x, 10)), 4), "p50": round(float(np.median(x)), 4),
+                "p90": round(float(np.percentile(x, 90)), 4)}
 
 
 # ------------------------------------------------------------------ decode workloads
@@ -143,7 +149,21 @@ class DecodeRun:
             self.step(timer.step())
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+        self.last_timer = timer
         return wall_ms, timer.mean_ms()
+
+    def timed_cold(self, steps, evict_bytes=512 << 20):
+        """Per-step kernel times with a write of ``evict_bytes`` between steps
+        (outside the events) so no K/V is left in the 256 MB Infinity Cache."""
+        import torch
+        scratch = torch.empty(evict_bytes, dtype=torch.uint8, device="cuda")
+        timer = _Timer(["write", "partitions", "merge"])
+        for _ in range(steps):
+            scratch.fill_(1)
+            self.step(timer.step())
+        torch.cuda.synchronize()
+        del scratch
+        return timer
 
     def algorithmic_bytes(self):
         """Bytes any implementation of the decode partition kernel must move:
@@ -300,7 +320,8 @@ def _cpu_baseline(case, budget_s):
     return {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"float64 oracle decode of the first {done} of {case.num_seqs} sequences "
                       f"({kv_bytes / 1e9:.3f} GB of K+V) in {dt:.1f} s; "
-                      f"{done / dt:.2f} sequences/s"}
+                      f"{done / dt:.2f} sequences/s",
+            "host": {"cpu_model": _cpu_model(), "affinity_cores": len(os.sched_getaffinity(0))}}
 
 
 def _oracle_decode_rate(case, budget_s=3.0):
@@ -544,6 +565,38 @@ def _secondary_multi(steps, warmup, nq=4):
                     "4 (query, head) columns per kv head)"}
 
 
+def _copy_probe(nbytes=4 << 30):
+    """Achievable-bandwidth reference: a device-to-device copy of ``nbytes``
+    (read + write counted), median of 5."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del a, b
+    torch.cuda.empty_cache()
+    ms = float(np.median(ts))
+    return {"bytes": 2 * nbytes, "ms": round(ms, 3), "GBs_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def _copy_calibration():
     import torch
     n = 1 << 30
@@ -613,6 +666,15 @@ def main():
                      "algorithmic_bytes_per_launch": algo,
                      "traffic": traffic},
     }
+    result["partition_kernel_ms_spread"] = run.last_timer.spread_ms("partitions")
+    cold = run.timed_cold(max(5, args.steps // 2))
+    cold_part = cold.spread_ms("partitions")
+    result["cold_cache"] = {
+        "note": "512 MiB written between steps (outside the events) to evict the Infinity Cache",
+        "partition_kernel_ms": cold_part,
+        "partition_kernel_GBs_p50": round(algo / (cold_part["p50"] * 1e-3) / 1e9, 1),
+        "step_kernels_ms_p50": round(sum(cold.spread_ms(n)["p50"] for n in ("write", "partitions", "merge")), 4)}
+    result["llama2_7b_attention_step_ms"] = round(32 * wall_ms, 3)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = _cpu_baseline(case, args.cpu_seconds)
     run.free()
@@ -637,6 +699,8 @@ def main():
         sec.append(_secondary_prefill(s2, w2, fp8=True))
         sec.append(_secondary_multi(s2, w2))
         result["secondary"] = sec
+    if not args.quick:
+        result["achievable_copy_probe"] = _copy_probe()
     result["input_generation_s"] = round(gen_s, 1)
     print(json.dumps(result), flush=True)
 
