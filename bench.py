@@ -373,6 +373,42 @@ def _secondary_decode(builder, name, steps, warmup, note=None, cpu=True, fp8=Fal
     return res
 
 
+def _secondary_tiny_latency(steps=200, warmup=20):
+    """decode_tiny as a latency figure: one step (cache write of 4 tokens +
+    decode) launched eagerly, and the same step captured once in a HIP graph
+    and replayed; wall time per step with no events in between."""
+    import torch
+    from workloads import decode_tiny
+    case = decode_tiny()
+    run = DecodeRun(case)
+    for _ in range(warmup):
+        run.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run.step()
+    torch.cuda.synchronize()
+    eager_us = (time.perf_counter() - t0) * 1e6 / steps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run.step()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_us = (time.perf_counter() - t0) * 1e6 / steps
+    run.free()
+    del graph, run
+    torch.cuda.empty_cache()
+    return {"workload": "decode_tiny_latency", "eager_us_per_step": round(eager_us, 2),
+            "graph_replay_us_per_step": round(graph_us, 2),
+            "note": "write + decode of batch 4; wall clock over back-to-back steps, no events; "
+                    "the graph holds the same kernel launches (one decode partition, no merge)"}
+
+
 def _shared_prefix_note(case):
     used = np.unique(case.block_tables[case.block_tables >= 0])
     unique_tokens = 0
@@ -689,6 +725,7 @@ def main():
         sec.append(_secondary_prefill(s2, w2))
         sec.append(_secondary_decode(decode_long_context, "decode_long_context", s2, w2))
         sec.append(_secondary_decode(decode_tiny, "decode_tiny", s2, w2))
+        sec.append(_secondary_tiny_latency())
         sec.append(_secondary_copy_blocks(s2, w2))
         sec.append(_secondary_decode(decode_llama2_7b_layer, "decode_llama2_7b_layer_fp8", s2, w2,
                                      fp8=True))

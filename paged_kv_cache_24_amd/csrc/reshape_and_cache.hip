@@ -3,7 +3,7 @@
 // With the [num_blocks][16][kv_heads][head_dim] layout a token slot is one
 // contiguous row of kv_heads * head_dim elements, so the write is a row copy
 // from key[t] / value[t] to row slot_mapping[t] ("vLLM-Ascend 原理", §2.3 step
-// 3 and §2.4 step 3).  Each lane moves one 16-byte vector; consecutive lanes
+// 3 and §2.4 step 3).  Each lane moves 16-byte vectors; consecutive lanes
 // cover consecutive bytes of a row, so loads and stores are fully coalesced.
 #include "common.h"
 #include "kernels.h"
@@ -12,28 +12,44 @@ namespace pa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// One workgroup per TPW tokens: the slot of each token is one scalar load, and
+// the workgroup's threads stream the token's K and V rows (row_vecs 16-byte
+// vectors each), so no thread divides a flat index.  Small writes (a decode
+// step) take one token per workgroup for parallelism; large ones four.
+template <int TPW>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(ReshapeArgs a) {
-    const int64_t vecs_per_token = 2 * (int64_t)a.row_vecs;   // K row then V row
-    const int64_t total = a.num_tokens * vecs_per_token;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-        const int64_t t = i / vecs_per_token;
-        int64_t v = i - t * vecs_per_token;
-        const int64_t slot = a.slot_mapping[t];
+    typedef const __attribute__((address_space(4))) int64_t cslot_t;
+    const cslot_t* slots = (const cslot_t*)a.slot_mapping;   // read-only in this kernel: scalar loads
+    const int64_t t0 = (int64_t)blockIdx.x * TPW;
+    const int row_vecs = a.row_vecs;
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+        const int64_t t = t0 + k;
+        if (t >= a.num_tokens) return;
+        const int64_t slot = slots[t];
         if (slot < 0 || slot >= a.num_slots) continue;   // padding row or outside the pool
-        const bool is_v = v >= a.row_vecs;
-        v -= is_v ? a.row_vecs : 0;
-        const u32x4* src = static_cast<const u32x4*>(is_v ? a.value : a.key) + t * a.row_vecs + v;
-        u32x4* dst = static_cast<u32x4*>(is_v ? a.v_cache : a.k_cache) + slot * a.row_vecs + v;
-        *dst = __builtin_nontemporal_load(src);   // the new rows are read exactly once
+        const u32x4* ks = static_cast<const u32x4*>(a.key) + t * row_vecs;
+        const u32x4* vs = static_cast<const u32x4*>(a.value) + t * row_vecs;
+        u32x4* kd = static_cast<u32x4*>(a.k_cache) + slot * row_vecs;
+        u32x4* vd = static_cast<u32x4*>(a.v_cache) + slot * row_vecs;
+        for (int v = threadIdx.x; v < row_vecs; v += blockDim.x) {
+            const u32x4 kx = __builtin_nontemporal_load(ks + v);   // the new rows are read exactly once
+            const u32x4 vx = __builtin_nontemporal_load(vs + v);
+            kd[v] = kx;
+            vd[v] = vx;
+        }
     }
 }
 
 hipError_t launch_reshape_and_cache(const ReshapeArgs& a, hipStream_t stream) {
-    const int64_t total = a.num_tokens * 2 * (int64_t)a.row_vecs;
-    const int64_t want = (total + 255) / 256;
-    const int grid = (int)(want < 65536 ? want : 65536);
-    hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(grid), dim3(256), 0, stream, a);
+    const bool big = a.num_tokens >= 2048;
+    const int tpw = big ? 4 : 1;
+    const int64_t wgs = (a.num_tokens + tpw - 1) / tpw;
+    if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+    // a token row is kv_heads * head_dim / 8 vectors: 128 threads cover Hkv = 8 at D = 128
+    const int threads = a.row_vecs >= 256 ? 256 : (a.row_vecs >= 128 ? 128 : 64);
+    if (big) hipLaunchKernelGGL(reshape_and_cache_kernel<4>, dim3((unsigned)wgs), dim3(threads), 0, stream, a);
+    else hipLaunchKernelGGL(reshape_and_cache_kernel<1>, dim3((unsigned)wgs), dim3(threads), 0, stream, a);
     return hipGetLastError();
 }
 
