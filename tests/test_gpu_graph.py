@@ -1,4 +1,5 @@
-"""HIP-graph capture and replay of a decode step (cache write + paged decode).
+"""HIP-graph capture and replay of decode steps: cache write + paged decode in
+16-bit and FP8 caches, and multi-query (verification) decode.
 
 Graph mode keeps every tensor at a fixed address and changes only contents
 between replays, the block table included ("vLLM-Ascend 原理", §四, graph mode).
@@ -25,6 +26,19 @@ def _gpu():
     import paged_kv_cache_24_amd  # noqa: F401
 
 
+def _capture(step):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    return graph
+
+
 @pytest.mark.parametrize("hq,hkv,dtype", [(8, 8, "f16"), (16, 2, "bf16")])
 def test_captured_decode_step_matches_eager(hq, hkv, dtype):
     import paged_kv_cache_24_amd as pa
@@ -39,19 +53,11 @@ def test_captured_decode_step_matches_eager(hq, hkv, dtype):
     out_graph = torch.empty_like(g.q)
     torch.cuda.synchronize()
 
-    def step(out):
+    def step(out=out_graph):
         pa.pa_reshape_and_cache(g.key, g.value, g.k_cache, g.v_cache, g.slots)
         pa.pa_decode(out, g.q, g.k_cache, g.v_cache, g.tables, g.lens, c.scale, part, workspace=ws)
 
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step(out_graph)                         # warm-up outside the capture
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step(out_graph)
+    graph = _capture(step)
 
     rng = np.random.default_rng(22)
     for replay in range(4):
@@ -75,3 +81,69 @@ def test_captured_decode_step_matches_eager(hq, hkv, dtype):
         torch.cuda.synchronize()
         np.testing.assert_array_equal(host_bits(out_graph), host_bits(eager),
                                       err_msg=f"replay {replay}")
+
+
+def test_captured_fp8_step_matches_eager():
+    """FP8 cache write + FP8 decode (GQA, split) captured once, replayed with new
+    q and new k/v contents; every replay equals the eager step bit for bit."""
+    import paged_kv_cache_24_amd as pa
+    from gpu_helpers import Fp8DecodeOnGPU
+    c = make_decode_case(name="graph-fp8", seed=23, dtype="bf16", num_q_heads=16, num_kv_heads=2,
+                         head_dim=128, seq_lens=[300, 17, 1, 129, 64], num_blocks=64,
+                         max_blocks_per_seq=20, scale=0.088, write_last=False)
+    g = Fp8DecodeOnGPU(c)
+    part = 64
+    need = pa.pa_decode_workspace_size(c.num_seqs, 16, 2, 128, c.max_blocks_per_seq, part)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out_graph = torch.empty_like(g.q)
+
+    def step(out=out_graph):
+        pa.pa_reshape_and_cache_fp8(g.key, g.value, g.k_cache, g.v_cache, g.k_scales, g.v_scales, g.slots)
+        pa.pa_decode_fp8(out, g.q, g.k_cache, g.v_cache, g.k_scales, g.v_scales, g.tables, g.lens,
+                         c.scale, part, workspace=ws)
+
+    graph = _capture(step)
+    rng = np.random.default_rng(24)
+    for replay in range(3):
+        g.q.copy_(dev_bits(normal_bits(rng, tuple(g.q.shape), "bf16"), "bf16"))
+        g.key.copy_(dev_bits(normal_bits(rng, tuple(g.key.shape), "bf16"), "bf16"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        eager = torch.empty_like(g.q)
+        step(eager)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_bits(out_graph), host_bits(eager), err_msg=f"replay {replay}")
+
+
+def test_captured_verification_step_matches_eager():
+    """Multi-query decode (4 draft queries per sequence) captured once and replayed
+    with the sequence lengths shortened in place, as after rejected drafts."""
+    import paged_kv_cache_24_amd as pa
+    nq = 4
+    lens = [300, 17, 2, 129]
+    c = make_decode_case(name="graph-multi", seed=25, dtype="f16", num_q_heads=32, num_kv_heads=32,
+                         head_dim=128, seq_lens=lens, num_blocks=64, max_blocks_per_seq=20,
+                         scale=0.088, write_last=False)
+    g = DecodeOnGPU(c)
+    rng = np.random.default_rng(26)
+    qm = dev_bits(normal_bits(rng, (c.num_seqs, nq, 32, 128), "f16"), "f16")
+    part = 64
+    need = pa.pa_decode_workspace_size(c.num_seqs * nq, 32, 32, 128, c.max_blocks_per_seq, part)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out_graph = torch.empty_like(qm)
+
+    def step(out=out_graph):
+        pa.pa_decode_multi(out, qm, g.k_cache, g.v_cache, g.tables, g.lens, c.scale, part, workspace=ws)
+
+    graph = _capture(step)
+    for replay in range(3):
+        g.lens.copy_(dev_int(np.maximum(np.array(lens) - 3 * replay, 0).astype(np.int32)))
+        qm.copy_(dev_bits(normal_bits(rng, tuple(qm.shape), "f16"), "f16"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        eager = torch.empty_like(qm)
+        step(eager)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_bits(out_graph), host_bits(eager), err_msg=f"replay {replay}")
