@@ -8,12 +8,17 @@
 // merged with an online softmax, as fused attention kernels do
 // ("vLLM-Ascend 原理", §2.3 step 3 and §四 "ATB 算子").
 //
-// Mapping.  One workgroup (8 waves) owns 128 query rows of one (sequence, kv
-// head): 128/G positions times the G q heads that share the kv head, so every
-// K/V tile is staged in LDS once for all of them.  Each wave owns 16 rows, which
-// keeps it at ~128 VGPRs so four waves share each SIMD (two workgroups per CU):
-// the softmax of one wave overlaps the matrix work of the others.
-// For each 64-key tile:
+// Two kernels:
+//  * prefill16_kernel (fp16 / bf16 cache): 32x32x16 matrix-core products,
+//    K/V tiles copied from HBM straight into LDS, S(t+1) = K Q^T overlapped
+//    with the softmax of tile t; described at the kernel.
+//  * prefill_kernel<.., F8 = true> (FP8 cache): 16x16x32 products over tiles
+//    that are widened to 16 bits while they are staged, as follows.
+//
+// prefill_kernel.  One workgroup (8 waves) owns 128 query rows of one
+// (sequence, kv head): 128/G positions times the G q heads that share the kv
+// head, so every K/V tile is staged in LDS once for all of them.  Each wave
+// owns 16 rows (~128 VGPRs, four waves per SIMD).  For each 64-key tile:
 //   S^T[key][row] = K[key][:] . Q[row][:]     (MFMA 16x16x32: A = K from LDS,
 //                                              B = Q kept in registers)
 //   online softmax per row: the C layout puts one row's keys in the four lanes
@@ -27,15 +32,13 @@
 // of the rescale factors is needed.  The next tile's K/V rows are loaded into
 // registers while the current tile is computed and stored to the other LDS
 // buffer afterwards (one barrier per tile).
-//
-// FP8 cache (F8): the same kernel over E4M3 codes with per-(token, kv head)
-// float32 scales ("vLLM-Ascend 原理", §四 on KV-cache quantisation: dequantised
-// after the block-table lookup, inside the operator).  Each thread stages 16
-// codes of one key row; K enters LDS as exact 16-bit codes and its scale
-// multiplies the scores, V enters as codes times 2^e (e = exponent of its
-// scale, exact) and the scale's mantissa factor in [1, 2) multiplies P, which
-// goes to the matrix cores as a 16-bit head and tail so the factor adds no
-// rounding.  The per-key factors sit in two small LDS arrays beside the tiles.
+// Over the FP8 cache, each thread stages 16 codes of one key row
+// ("vLLM-Ascend 原理", §四 on KV-cache quantisation: dequantised after the
+// block-table lookup, inside the operator); K enters LDS as exact 16-bit codes
+// and its scale multiplies the scores, V enters as codes times 2^e (e = exponent
+// of its scale, exact) and the scale's mantissa factor in [1, 2) multiplies P,
+// which goes to the matrix cores as a 16-bit head and tail so the factor adds
+// no rounding.  The per-key factors sit in two small LDS arrays beside the tiles.
 #include <type_traits>
 
 #include "common.h"
@@ -380,6 +383,447 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit cache: prefill on 32x32x16 matrix-core products, software-pipelined.
+//
+// One workgroup (4 waves) owns 128 query rows of one (sequence, kv head); each
+// wave owns 32 rows, so every K/V fragment read from LDS feeds a 32-row product
+// (half the LDS bytes per flop of 16-row waves).  Per 64-key tile and wave:
+//   S^T[key][row] = K Q^T : 2 key blocks x 8 steps of v_mfma_f32_32x32x16
+//     (A = K rows from LDS, B = Q^T kept in registers); lane l holds 16 keys
+//     8*(r/4) + 4*(l/32) + r%4 of row l%32 per key block, so a row lives in
+//     lanes l and l^32 only;
+//   O^T[d][row] += V^T P^T : 4 d blocks x 4 steps of 16 keys (A = V^T
+//     fragments by ds_read_b64_tr_b16, B = P^T straight from the lane's own
+//     probabilities: step ks uses accumulator values 8*(ks%2) .. +7 of key
+//     block ks/2, which are keys 16 ks + 4 (l/32) + {0..3, 8..11}).
+// K/V tiles go from HBM straight into LDS (global_load_lds_dwordx4: a wave's
+// 64 lanes fill 1 KiB = 4 token rows), with the 16-byte chunks of each row
+// permuted by an XOR of the row index so that neither the K fragment reads nor
+// the transposed V reads meet bank conflicts.  Pipeline per tile t: the loads
+// of V(t+1) and K(t+2) are issued first, then S(t+1) is computed on the matrix
+// cores while the vector ALUs turn S(t) into probabilities, then O += V(t) P(t).
+// The softmax is optimistic: probabilities are taken against the running max m
+// and only if some score exceeds m by more than 2^8 (log2 domain) is the row max
+// raised, O and the sum rescaled and the tile redone -- an exact rewrite of the
+// softmax ("vLLM-Ascend 原理", §四 ATB fused attention), with p <= 256.
+// Row sums add the same 16-bit probabilities that enter the PV product.
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int DT>
+__device__ __forceinline__ f32x16_t mfma32x32x16(const uint4& a, const uint4& b, f32x16_t c) {
+    if constexpr (DT == kF16) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+}
+
+// 16-byte global -> LDS copy; the wave's LDS destination is lds_row0 + 16 * lane
+__device__ __forceinline__ void load_lds16(const void* src, uint16_t* lds_row0) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)lds_row0, 16, 0, 0);
+}
+
+constexpr int kTileElems = kKT * kPD;   // one K or V tile in LDS, 16 KiB
+
+// Work order.  A workgroup's cost is its number of key tiles, which grows with
+// the sequence's cached context and with the q tile's position, so neither the
+// q-tile index nor the sequence index orders the work.  Workgroup x takes kv
+// head x % Hkv and the (x / Hkv)-th costliest (sequence, q tile) item -- ties
+// broken by sequence, then by later q tile first -- so the grid runs
+// longest-first and the last wave of workgroups is short.  Each wave finds its
+// item on its own from the lengths in device memory: a binary search over the
+// tile count, with a closed-form count per sequence, then a prefix count over
+// the sequences whose items tie.
+struct SeqLens {
+    int ctx, len, nq;
+};
+
+__device__ __forceinline__ SeqLens prefill_seq(const PrefillArgs& a, int b, int P, int max_keys) {
+    const int64_t r0 = a.query_start_loc[b];
+    const int64_t r1 = min((int64_t)a.query_start_loc[b + 1], a.num_tokens);
+    SeqLens s;
+    s.len = (r0 < 0 || r1 <= r0) ? 0 : (int)min(r1 - r0, (int64_t)a.max_q_len);
+    s.ctx = min(max(a.ctx_lens[b], 0), max_keys);
+    s.nq = (s.len + P - 1) / P;
+    return s;
+}
+
+// items of one sequence with at least t key tiles: q tile q has
+// min(ctx + min((q + 1) P, len), max_keys) keys
+__device__ __forceinline__ int items_with_tiles(const SeqLens& s, int t, int P, int max_keys) {
+    if (s.nq == 0) return 0;
+    const int w = kKT * (t - 1) + 1;          // tiles >= t  <=>  keys >= w
+    if (w > max_keys) return 0;
+    const int d = w - s.ctx;
+    if (d <= 0) return s.nq;
+    if (d > s.len) return 0;
+    return s.nq - (d + P - 1) / P + 1;
+}
+
+__device__ __forceinline__ int wave_sum_i32(int x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+// (sequence, q tile) of rank j in the cost order; false if there are fewer items
+__device__ bool prefill_item(const PrefillArgs& a, int P, int64_t j, int& b_out, int& qt_out) {
+    const int lane = threadIdx.x & 63;
+    const int max_keys = a.max_blocks_per_seq * kBlockSize;
+    auto count = [&](int t) -> int {
+        int c = 0;
+        for (int b = lane; b < a.num_seqs; b += 64) c += items_with_tiles(prefill_seq(a, b, P, max_keys), t, P, max_keys);
+        return wave_sum_i32(c);
+    };
+    if (j >= count(1)) return false;
+    // largest t with count(t) > j
+    int lo = 1, hi = (max_keys + kKT - 1) / kKT + 1;   // count(lo) > j >= count(hi)
+    while (hi - lo > 1) {
+        const int mid = lo + (hi - lo) / 2;
+        if (count(mid) > (int)j) lo = mid;
+        else hi = mid;
+    }
+    int rank = (int)j - count(lo + 1);                  // among the items with exactly lo tiles
+    for (int b0 = 0; b0 < a.num_seqs; b0 += 64) {
+        const int b = b0 + lane;
+        int eq = 0, above = 0, nq = 0;
+        if (b < a.num_seqs) {
+            const SeqLens sl = prefill_seq(a, b, P, max_keys);
+            above = items_with_tiles(sl, lo + 1, P, max_keys);
+            eq = items_with_tiles(sl, lo, P, max_keys) - above;
+            nq = sl.nq;
+        }
+        // inclusive prefix sum of eq over the lanes
+        int incl = eq;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(incl, off);
+            if (lane >= off) incl += v;
+        }
+        const int total = __shfl(incl, 63);
+        if (rank < total) {
+            const uint64_t hit = __ballot(incl > rank && incl - eq <= rank);
+            const int src = __builtin_ctzll(hit);
+            b_out = b0 + src;
+            const int excl = __shfl(incl - eq, src);
+            qt_out = __shfl(nq - 1 - above, src) - (rank - excl);
+            return true;
+        }
+        rank -= total;
+    }
+    return false;
+}
+
+template <int DT, int G>
+__global__ __launch_bounds__(256, 2) void prefill16_kernel(PrefillArgs a) {
+    constexpr int P = kRows / G;    // positions per workgroup
+    // separate arrays so that the compiler can tell the in-flight copies from
+    // the buffers being read
+    __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds_k1[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds_v0[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds_v1[kTileElems];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uniform(tid >> 6);   // 0..3: rows 32*wave .. 32*wave+31
+    const int lr = lane & 31;
+    const int h = lane >> 5;
+
+    const int g = blockIdx.x % a.num_kv_heads;
+    int b, qtile;
+    if (!prefill_item(a, P, blockIdx.x / a.num_kv_heads, b, qtile)) return;   // uniform
+
+    // clamp what comes from device memory so no access can leave its buffer
+    const int64_t row0 = a.query_start_loc[b];
+    const int64_t row1 = min((int64_t)a.query_start_loc[b + 1], a.num_tokens);
+    if (row0 < 0 || row1 <= row0) return;
+    const int L = (int)min(row1 - row0, (int64_t)a.max_q_len);
+    const int max_keys = a.max_blocks_per_seq * kBlockSize;
+    const int ctx = min(max(a.ctx_lens[b], 0), max_keys);
+    const int pos0 = qtile * P;
+    if (qtile < 0 || pos0 >= L) return;
+    const int pos_end = min(L, pos0 + P);
+    const int n_keys = min(ctx + pos_end, max_keys);
+    const int ntiles = (n_keys + kKT - 1) / kKT;
+    const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
+    const int64_t row_stride = (int64_t)a.num_kv_heads * kPD;
+
+    // ---- Q^T fragments: row rho, elements 16 kk + 8 h .. +7
+    uint4 qf[8];
+    const int rho = wave * 32 + lr;
+    const int qpos = ctx + pos0 + rho / G;
+    {
+        const int pos = pos0 + rho / G;
+        const bool ok = pos < L;
+        const uint16_t* src = static_cast<const uint16_t*>(a.q) +
+                              ((row0 + (ok ? pos : 0)) * a.num_q_heads + g * G + rho % G) * kPD + 8 * h;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+            qf[kk] = ok ? *reinterpret_cast<const uint4*>(src + 16 * kk) : make_uint4(0, 0, 0, 0);
+    }
+    const int wave_pos_lo = pos0 + (wave * 32) / G;
+    const int wave_pos_hi = min(pos_end - 1, pos0 + (wave * 32 + 31) / G);
+    const int wave_q_lo = ctx + wave_pos_lo;
+    // tiles this wave computes (its last row's keys), at most the workgroup's
+    const int wave_tiles = wave_pos_lo < pos_end ? min(ntiles, (ctx + wave_pos_hi) / kKT + 1) : 0;
+
+    // ---- staging.  Wave w copies block w of each tile (tile rows 16 w .. 16 w + 15):
+    // 4 copies of 4 token rows for K and 4 for V.  Lane i writes LDS slot i % 16 of
+    // row 4 j + i / 16 and so reads chunk (i % 16) ^ f(row) of that token row:
+    // f = row & 15 for K, (row & 3) << 2 for V.  Rows past the last key read the
+    // block's first row (blocks past it the sequence's first block): any finite
+    // data will do, since their probabilities are exactly 0.
+    typedef const __attribute__((address_space(4))) int32_t ctab_t;
+    const ctab_t* ctab = (const ctab_t*)table;
+    const uint32_t rs2 = (uint32_t)(row_stride * 2);          // bytes between token rows
+    const int64_t block_bytes = (int64_t)kBlockSize * rs2;
+    const uint32_t goff = (uint32_t)(g * kPD * 2);
+    const int l15 = lane & 15;
+    const int l4 = lane >> 4;
+    // chunk of copy j: l15 ^ (4 j + l4) = (l15 ^ l4) ^ 4 j
+    const uint32_t koff0 = goff + (uint32_t)((l15 ^ l4) << 4);
+    const uint32_t voff = goff + (uint32_t)((l15 ^ (l4 << 2)) << 4);
+    const int nb32 = (int)min(a.num_blocks, (int64_t)INT32_MAX);
+    int first_blk = ctab[0];
+    first_blk = first_blk >= 0 && first_blk < nb32 ? first_blk : 0;
+
+    // Block ids of this wave's blocks: lane i of tab[c & 1] holds the id for tile
+    // 64 c + i, loaded with a vector load (waited for at the tile barriers, so no
+    // scalar-load round trip sits on the critical path).  Ids of blocks past the
+    // keys, and ids out of range, become the first block and block 0.
+    auto load_tab = [&](int c) -> int {
+        const int blk = 4 * (64 * c + lane) + wave;
+        return blk * kBlockSize < n_keys ? table[blk] : first_blk;
+    };
+    int tab[2];
+    tab[0] = load_tab(0);
+    tab[1] = ntiles > 64 ? load_tab(1) : first_blk;
+    auto block_of = [&](int tt) -> int {   // uniform
+        const int i = tt & 63;
+        const int pb = (tt >> 6) & 1 ? __builtin_amdgcn_readlane(tab[1], i) : __builtin_amdgcn_readlane(tab[0], i);
+        return pb >= 0 && pb < nb32 ? pb : 0;
+    };
+    auto block_of_scalar = [&](int tt) -> int {   // uniform, before the ids have arrived
+        const int blk = tt * 4 + wave;
+        if (blk * kBlockSize >= n_keys) return first_blk;
+        const int pb = ctab[blk];
+        return pb >= 0 && pb < nb32 ? pb : 0;
+    };
+    auto stage = [&](int tt, int pb, uint16_t* kdst, uint16_t* vdst) {
+        const int nval = n_keys - (tt * kKT + 16 * wave);   // valid rows of this block (uniform)
+        const char* kb = static_cast<const char*>(a.k_cache) + pb * block_bytes;
+        const char* vb = static_cast<const char*>(a.v_cache) + pb * block_bytes;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * j + l4;
+            const uint32_t rowoff = r < nval ? (uint32_t)r * rs2 : 0u;
+            if (kdst) load_lds16(kb + (rowoff + (koff0 ^ (uint32_t)(j << 6))), kdst + (16 * wave + 4 * j) * kPD);
+            if (vdst) load_lds16(vb + (rowoff + voff), vdst + (16 * wave + 4 * j) * kPD);
+        }
+    };
+
+    // ---- LDS read addresses (bytes).  K fragment of step kk: row 32 kb + lr,
+    // chunk 2 kk + h, stored at slot (2 kk + h) ^ (lane & 15).
+    uint32_t kaddr[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) kaddr[kk] = (uint32_t)(lr * kPD + (((2 * kk + h) ^ l15) << 3)) * 2u;
+    // V^T fragments: within each 16-lane group (h, dsub) lane j reads 4 elements of
+    // row 4 h + j / 4 (+ 8, + 16 ks), columns 32 db + 16 dsub + 4 (j % 4)
+    const int jq = l15 >> 2;
+    const int dsub = (lane >> 4) & 1;
+    uint32_t vaddr[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const int slot = 4 * (db ^ jq) + 2 * dsub + ((l15 >> 1) & 1);
+        vaddr[db] = (uint32_t)((4 * h + jq) * kPD + slot * 8 + 4 * (l15 & 1)) * 2u;
+    }
+
+    f32x16_t o[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+    f32x16_t sbuf[2][2];            // S^T of tiles t (sbuf[t & 1]) and t + 1
+    float m = -INFINITY;            // running max of the lane's row (log2 domain, scaled)
+    float lsum0 = 0.f, lsum1 = 0.f; // this lane's share of the row sum
+    const float cs = a.scale_log2;
+    constexpr uint32_t kOnes = DT == kF16 ? 0x3C003C00u : 0x3F803F80u;
+
+    auto qk = [&](const uint16_t* kbuf, f32x16_t (&s)[2]) {
+        const char* base = reinterpret_cast<const char*>(kbuf);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const uint4 ka = *reinterpret_cast<const uint4*>(base + kaddr[kk] + kb * 32 * kPD * 2);
+                s[kb] = mfma32x32x16<DT>(ka, qf[kk], s[kb]);
+            }
+    };
+
+    // prologue: K(0), V(0), K(1) in flight, then S(0)
+    stage(0, block_of_scalar(0), lds_k0, lds_v0);
+    if (ntiles > 1) stage(1, block_of_scalar(1), lds_k1, nullptr);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    if (wave_tiles > 0) qk(lds_k0, sbuf[0]);
+
+    auto body = [&](int t, auto par) {
+        constexpr int B = decltype(par)::value;          // t & 1
+        uint16_t* kcur = B ? lds_k1 : lds_k0;            // K(t): free (S(t) done)
+        uint16_t* knext = B ? lds_k0 : lds_k1;           // K(t+1)
+        uint16_t* vcur = B ? lds_v1 : lds_v0;            // V(t)
+        uint16_t* vnext = B ? lds_v0 : lds_v1;           // V(t+1) goes here (V(t-1) done)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        if (t + 1 < ntiles) stage(t + 1, block_of(t + 1), nullptr, vnext);
+        if (t + 2 < ntiles) stage(t + 2, block_of(t + 2), kcur, nullptr);
+        // ids of the chunk after next: its slot held the chunk last used at tile t + 1
+        if (((t + 2) & 63) == 1 && 64 * (((t + 2) >> 6) + 1) < ntiles) {
+            const int c = ((t + 2) >> 6) + 1;
+            if (c & 1) tab[1] = load_tab(c);
+            else tab[0] = load_tab(c);
+        }
+        if (t >= wave_tiles) return;                      // uniform
+
+        f32x16_t (&sc)[2] = sbuf[B];
+        f32x16_t (&sn)[2] = sbuf[B ^ 1];
+        const int k0 = t * kKT;
+        if (k0 + kKT - 1 > wave_q_lo) {   // diagonal tile: causal mask by select
+            const int lim = qpos - k0 - 4 * h;   // key offset 32 kb + 8 (r/4) + r%4 must not exceed it
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sc[kb][r] = -INFINITY;
+        }
+
+        // ---- one scheduling region: S(t+1) on the matrix cores (K(t+1) fragments
+        // read ahead) while the vector ALUs take the max and the probabilities of
+        // tile t.  For the wave's last tile S(t+1) is computed from whatever the
+        // buffer holds and dropped, which keeps this region free of branches.
+        qk(knext, sn);
+        float lmax0 = -INFINITY, lmax1 = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            lmax0 = __builtin_elementwise_maximum(lmax0, sc[0][r]);
+            lmax1 = __builtin_elementwise_maximum(lmax1, sc[1][r]);
+        }
+        const float lmax = __builtin_elementwise_maximum(lmax0, lmax1);
+        uint4 pb[4];
+        auto probs = [&](float nmu) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int kb = ks >> 1, r0 = 8 * (ks & 1);
+                uint32_t w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    w[i] = pack2<DT>(fast_exp2(fmaf(sc[kb][r0 + 2 * i], cs, nmu)),
+                                     fast_exp2(fmaf(sc[kb][r0 + 2 * i + 1], cs, nmu)));
+                pb[ks] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        };
+        probs(m == -INFINITY ? 0.f : -m);
+        // interleave: K reads PF ahead, then MFMA / VALU / read
+        constexpr int PF = 6;
+        __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+        for (int i = 0; i < 16 - PF; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        }
+
+        if (__any(lmax * cs > m + 8.f)) {   // raise the row max (rows of lanes l, l^32 agree)
+            const float mb = xor32_max(lmax) * cs;
+            const bool raise = mb > m + 8.f;
+            const float mn = raise ? mb : m;
+            const float alpha = raise ? fast_exp2(m - mn) : 1.f;   // exp2(-inf) = 0
+            lsum0 *= alpha;
+            lsum1 *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db) o[db] *= alpha;
+            m = mn;
+            const uint4 keep[4] = {pb[0], pb[1], pb[2], pb[3]};
+            probs(m == -INFINITY ? 0.f : -m);
+            if (!raise) {   // rows whose max stays: their probabilities were right
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) pb[ks] = keep[ks];
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ks += 2) {
+            lsum0 = dot2<DT>(pb[ks].x, kOnes, lsum0);
+            lsum1 = dot2<DT>(pb[ks].y, kOnes, lsum1);
+            lsum0 = dot2<DT>(pb[ks].z, kOnes, lsum0);
+            lsum1 = dot2<DT>(pb[ks].w, kOnes, lsum1);
+            lsum0 = dot2<DT>(pb[ks + 1].x, kOnes, lsum0);
+            lsum1 = dot2<DT>(pb[ks + 1].y, kOnes, lsum1);
+            lsum0 = dot2<DT>(pb[ks + 1].z, kOnes, lsum0);
+            lsum1 = dot2<DT>(pb[ks + 1].w, kOnes, lsum1);
+        }
+
+        // ---- O^T += V^T P^T
+        const char* vbase = reinterpret_cast<const char*>(vcur);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const ps16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (ps16x4_t __attribute__((address_space(3)))*)(vbase + vaddr[db] + (16 * ks) * kPD * 2));
+                const ps16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (ps16x4_t __attribute__((address_space(3)))*)(vbase + vaddr[db] + (16 * ks + 8) * kPD * 2));
+                const uint2 l2 = __builtin_bit_cast(uint2, lo);
+                const uint2 h2 = __builtin_bit_cast(uint2, hi);
+                o[db] = mfma32x32x16<DT>(make_uint4(l2.x, l2.y, h2.x, h2.y), pb[ks], o[db]);
+            }
+        // V reads two MFMAs ahead, the row-sum dot products in between
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+        for (int i = 0; i < 14; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x002, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        body(t, std::integral_constant<int, 0>());
+        if (t + 1 < ntiles) body(t + 1, std::integral_constant<int, 1>());
+    }
+
+    if (wave_tiles == 0) return;
+    // ---- epilogue: full row sum, normalise, store the row if it exists
+    const float l = xor32_sum(lsum0 + lsum1);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int pos = pos0 + rho / G;
+    if (pos >= L) return;
+    uint16_t* dst = static_cast<uint16_t*>(a.out) +
+                    ((row0 + pos) * a.num_q_heads + g * G + rho % G) * kPD + 4 * h;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            uint2 w;
+            w.x = pack2<DT>(o[db][4 * r4] * inv, o[db][4 * r4 + 1] * inv);
+            w.y = pack2<DT>(o[db][4 * r4 + 2] * inv, o[db][4 * r4 + 3] * inv);
+            *reinterpret_cast<uint2*>(dst + 32 * db + 8 * r4) = w;
+        }
+}
+
 template <int DT, bool F8>
 static void launch_prefill_g(const PrefillArgs& a, hipStream_t s, dim3 grid) {
     switch (a.group) {
@@ -403,7 +847,27 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) { return launch_prefill_t<false>(a, s); }
+template <int DT>
+static void launch_prefill16_g(const PrefillArgs& a, hipStream_t s, dim3 grid) {
+    switch (a.group) {
+        case 1: hipLaunchKernelGGL((prefill16_kernel<DT, 1>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((prefill16_kernel<DT, 2>), grid, dim3(256), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((prefill16_kernel<DT, 4>), grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((prefill16_kernel<DT, 8>), grid, dim3(256), 0, s, a); break;
+    }
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
+    const int positions = kRows / a.group;
+    const int64_t qtiles = (a.max_q_len + positions - 1) / positions;
+    const int64_t wgs = qtiles * a.num_seqs * a.num_kv_heads;
+    if (wgs == 0) return hipSuccess;
+    if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)wgs);
+    if (a.dtype == kF16) launch_prefill16_g<kF16>(a, s, grid);
+    else launch_prefill16_g<kBF16>(a, s, grid);
+    return hipGetLastError();
+}
 hipError_t launch_prefill_fp8(const PrefillArgs& a, hipStream_t s) { return launch_prefill_t<true>(a, s); }
 
 }  // namespace pa
