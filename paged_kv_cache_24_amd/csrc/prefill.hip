@@ -471,13 +471,35 @@ __device__ __forceinline__ int wave_sum_i32(int x) {
     return x;
 }
 
-// (sequence, q tile) of rank j in the cost order; false if there are fewer items
+// (sequence, q tile) of rank j in the cost order; false if there are fewer items.
+// The lengths of up to 256 sequences stay in registers (4 per lane); the
+// lengths of any further sequences are read again at each step.
 __device__ bool prefill_item(const PrefillArgs& a, int P, int64_t j, int& b_out, int& qt_out) {
     const int lane = threadIdx.x & 63;
     const int max_keys = a.max_blocks_per_seq * kBlockSize;
+    constexpr int kHeld = 4;
+    SeqLens held[kHeld];
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) {
+        const int b = lane + 64 * i;
+        held[i] = b < a.num_seqs ? prefill_seq(a, b, P, max_keys) : SeqLens{0, 0, 0};
+    }
+    auto seq_at = [&](int i) -> SeqLens {   // sequence lane + 64 i
+        if (i < kHeld) {
+            SeqLens s = held[0];
+#pragma unroll
+            for (int k = 1; k < kHeld; ++k) s = i == k ? held[k] : s;
+            return s;
+        }
+        const int b = lane + 64 * i;
+        return b < a.num_seqs ? prefill_seq(a, b, P, max_keys) : SeqLens{0, 0, 0};
+    };
+    const int chunks = (a.num_seqs + 63) / 64;
     auto count = [&](int t) -> int {
         int c = 0;
-        for (int b = lane; b < a.num_seqs; b += 64) c += items_with_tiles(prefill_seq(a, b, P, max_keys), t, P, max_keys);
+#pragma unroll
+        for (int i = 0; i < kHeld; ++i) c += items_with_tiles(held[i], t, P, max_keys);
+        for (int i = kHeld; i < chunks; ++i) c += items_with_tiles(seq_at(i), t, P, max_keys);
         return wave_sum_i32(c);
     };
     if (j >= count(1)) return false;
@@ -489,15 +511,10 @@ __device__ bool prefill_item(const PrefillArgs& a, int P, int64_t j, int& b_out,
         else hi = mid;
     }
     int rank = (int)j - count(lo + 1);                  // among the items with exactly lo tiles
-    for (int b0 = 0; b0 < a.num_seqs; b0 += 64) {
-        const int b = b0 + lane;
-        int eq = 0, above = 0, nq = 0;
-        if (b < a.num_seqs) {
-            const SeqLens sl = prefill_seq(a, b, P, max_keys);
-            above = items_with_tiles(sl, lo + 1, P, max_keys);
-            eq = items_with_tiles(sl, lo, P, max_keys) - above;
-            nq = sl.nq;
-        }
+    for (int i = 0; i < chunks; ++i) {
+        const SeqLens sl = seq_at(i);
+        const int above = items_with_tiles(sl, lo + 1, P, max_keys);
+        const int eq = items_with_tiles(sl, lo, P, max_keys) - above;
         // inclusive prefix sum of eq over the lanes
         int incl = eq;
 #pragma unroll
@@ -509,9 +526,9 @@ __device__ bool prefill_item(const PrefillArgs& a, int P, int64_t j, int& b_out,
         if (rank < total) {
             const uint64_t hit = __ballot(incl > rank && incl - eq <= rank);
             const int src = __builtin_ctzll(hit);
-            b_out = b0 + src;
+            b_out = 64 * i + src;
             const int excl = __shfl(incl - eq, src);
-            qt_out = __shfl(nq - 1 - above, src) - (rank - excl);
+            qt_out = __shfl(sl.nq - 1 - above, src) - (rank - excl);
             return true;
         }
         rank -= total;

@@ -96,3 +96,28 @@ def test_prefill_two_chunks_match_one():
     both = np.concatenate([host_f64(out1), host_f64(out2)])
     assert_close(both, ref, "bf16", "two chunks")
     assert np.abs(both - whole).max() <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_long_context(dtype):
+    """A context of ~9000 keys: more than two 64-tile chunks of block ids, so
+    the kernel refills its cached ids twice while it runs."""
+    c = make_prefill_case(name=f"long-{dtype}", seed=34, dtype=dtype, num_q_heads=8,
+                          num_kv_heads=2, head_dim=128, q_lens=[70, 3], ctx_lens=[9050, 4100],
+                          scale=1 / math.sqrt(128))
+    _, out, ref = _run(c)
+    assert_close(out, ref, dtype, c.name)
+
+
+def test_prefill_many_sequences():
+    """300 short sequences of mixed cost: the longest-first work order reads
+    the lengths of sequences beyond those it keeps in registers."""
+    rng = np.random.default_rng(35)
+    q_lens = rng.integers(0, 6, 300)
+    ctx = rng.integers(0, 200, 300)
+    q_lens[[3, 150, 299]] = [40, 33, 70]
+    ctx[[3, 150, 299]] = [700, 0, 260]
+    c = make_prefill_case(name="many", seed=35, dtype="bf16", num_q_heads=8, num_kv_heads=2,
+                          head_dim=128, q_lens=q_lens, ctx_lens=ctx, scale=0.09)
+    _, out, ref = _run(c)
+    assert_close(out, ref, "bf16", c.name)
