@@ -423,9 +423,16 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(const uint4& a, const uint4& b,
 }
 
 // 16-byte global -> LDS copy; the wave's LDS destination is lds_row0 + 16 * lane
+// (lds_row0 wave-uniform).  Written as an instruction the compiler does not
+// model, so that it adds no waits of its own for these copies: the kernel waits
+// for them explicitly (vmcnt) before the barrier that publishes a buffer, and
+// no buffer is read in the tile in which it is being filled.
 __device__ __forceinline__ void load_lds16(const void* src, uint16_t* lds_row0) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)lds_row0, 16, 0, 0);
+    const uint32_t m0v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)lds_row0;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(m0v)
+                 : "m0");
 }
 
 constexpr int kTileElems = kKT * kPD;   // one K or V tile in LDS, 16 KiB
@@ -536,25 +543,47 @@ __device__ bool prefill_item(const PrefillArgs& a, int P, int64_t j, int& b_out,
     return false;
 }
 
+constexpr int kW16 = 8;                 // waves per workgroup
+constexpr int kRows16 = 32 * kW16;      // query rows per workgroup
+constexpr int kStages = 4;              // LDS buffers of K and of V
+
 template <int DT, int G>
-__global__ __launch_bounds__(256, 2) void prefill16_kernel(PrefillArgs a) {
-    constexpr int P = kRows / G;    // positions per workgroup
+__global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) {
+    constexpr int P = kRows16 / G;  // positions per workgroup
     // separate arrays so that the compiler can tell the in-flight copies from
     // the buffers being read
     __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[kTileElems];
     __shared__ __attribute__((aligned(1024))) uint16_t lds_k1[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds_k2[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds_k3[kTileElems];
     __shared__ __attribute__((aligned(1024))) uint16_t lds_v0[kTileElems];
     __shared__ __attribute__((aligned(1024))) uint16_t lds_v1[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds_v2[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds_v3[kTileElems];
+    auto kbuf = [&](auto i) __attribute__((always_inline)) -> uint16_t* {
+        constexpr int I = decltype(i)::value;
+        return I == 0 ? lds_k0 : I == 1 ? lds_k1 : I == 2 ? lds_k2 : lds_k3;
+    };
+    auto vbuf = [&](auto i) __attribute__((always_inline)) -> uint16_t* {
+        constexpr int I = decltype(i)::value;
+        return I == 0 ? lds_v0 : I == 1 ? lds_v1 : I == 2 ? lds_v2 : lds_v3;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = uniform(tid >> 6);   // 0..3: rows 32*wave .. 32*wave+31
+    const int wave = uniform(tid >> 6);   // 0..7: rows 32*wave .. 32*wave+31
     const int lr = lane & 31;
     const int h = lane >> 5;
 
     const int g = blockIdx.x % a.num_kv_heads;
     int b, qtile;
     if (!prefill_item(a, P, blockIdx.x / a.num_kv_heads, b, qtile)) return;   // uniform
+    b = uniform(b);           // the same in every lane: let the compiler know
+    qtile = uniform(qtile);
 
     // clamp what comes from device memory so no access can leave its buffer
     const int64_t row0 = a.query_start_loc[b];
@@ -590,8 +619,9 @@ __global__ __launch_bounds__(256, 2) void prefill16_kernel(PrefillArgs a) {
     // tiles this wave computes (its last row's keys), at most the workgroup's
     const int wave_tiles = wave_pos_lo < pos_end ? min(ntiles, (ctx + wave_pos_hi) / kKT + 1) : 0;
 
-    // ---- staging.  Wave w copies block w of each tile (tile rows 16 w .. 16 w + 15):
-    // 4 copies of 4 token rows for K and 4 for V.  Lane i writes LDS slot i % 16 of
+    // ---- staging.  Waves 0..3 copy the K blocks and waves 4..7 the V blocks:
+    // wave w copies block q = w % 4 of each tile (tile rows 16 q .. 16 q + 15) as
+    // 4 copies of 4 token rows.  Lane i writes LDS slot i % 16 of
     // row 4 j + i / 16 and so reads chunk (i % 16) ^ f(row) of that token row:
     // f = row & 15 for K, (row & 3) << 2 for V.  Rows past the last key read the
     // block's first row (blocks past it the sequence's first block): any finite
@@ -604,44 +634,34 @@ __global__ __launch_bounds__(256, 2) void prefill16_kernel(PrefillArgs a) {
     const int l15 = lane & 15;
     const int l4 = lane >> 4;
     // chunk of copy j: l15 ^ (4 j + l4) = (l15 ^ l4) ^ 4 j
+    const bool kwave = wave < 4;          // uniform: this wave copies K (else V)
+    const int q = wave & 3;               // block of the tile this wave copies
     const uint32_t koff0 = goff + (uint32_t)((l15 ^ l4) << 4);
     const uint32_t voff = goff + (uint32_t)((l15 ^ (l4 << 2)) << 4);
     const int nb32 = (int)min(a.num_blocks, (int64_t)INT32_MAX);
     int first_blk = ctab[0];
     first_blk = first_blk >= 0 && first_blk < nb32 ? first_blk : 0;
 
-    // Block ids of this wave's blocks: lane i of tab[c & 1] holds the id for tile
-    // 64 c + i, loaded with a vector load (waited for at the tile barriers, so no
-    // scalar-load round trip sits on the critical path).  Ids of blocks past the
-    // keys, and ids out of range, become the first block and block 0.
-    auto load_tab = [&](int c) -> int {
-        const int blk = 4 * (64 * c + lane) + wave;
-        return blk * kBlockSize < n_keys ? table[blk] : first_blk;
+    // Block ids are read through the constant address space (scalar loads): for
+    // the copies of a tile, one tile ahead, so that the load has returned by the
+    // time the next barrier has passed.  Ids of blocks past the keys become the
+    // sequence's first block, ids out of range block 0.
+    auto raw_block = [&](int tt) __attribute__((always_inline)) -> int {   // uniform
+        const int blk = tt * 4 + q;
+        return blk * kBlockSize < n_keys ? ctab[blk] : first_blk;
     };
-    int tab[2];
-    tab[0] = load_tab(0);
-    tab[1] = ntiles > 64 ? load_tab(1) : first_blk;
-    auto block_of = [&](int tt) -> int {   // uniform
-        const int i = tt & 63;
-        const int pb = (tt >> 6) & 1 ? __builtin_amdgcn_readlane(tab[1], i) : __builtin_amdgcn_readlane(tab[0], i);
-        return pb >= 0 && pb < nb32 ? pb : 0;
-    };
-    auto block_of_scalar = [&](int tt) -> int {   // uniform, before the ids have arrived
-        const int blk = tt * 4 + wave;
-        if (blk * kBlockSize >= n_keys) return first_blk;
-        const int pb = ctab[blk];
-        return pb >= 0 && pb < nb32 ? pb : 0;
-    };
-    auto stage = [&](int tt, int pb, uint16_t* kdst, uint16_t* vdst) {
-        const int nval = n_keys - (tt * kKT + 16 * wave);   // valid rows of this block (uniform)
-        const char* kb = static_cast<const char*>(a.k_cache) + pb * block_bytes;
-        const char* vb = static_cast<const char*>(a.v_cache) + pb * block_bytes;
+    auto valid_block = [&](int pb) __attribute__((always_inline)) -> int { return pb >= 0 && pb < nb32 ? pb : 0; };
+    auto block_of_scalar = [&](int tt) __attribute__((always_inline)) -> int { return valid_block(raw_block(tt)); };
+    // copies this wave's block of tile tt into dst (a K buffer for K waves, V for V waves)
+    auto stage = [&](int tt, int pb, uint16_t* dst) __attribute__((always_inline)) {
+        const int nval = n_keys - (tt * kKT + 16 * q);   // valid rows of this block (uniform)
+        const char* src = static_cast<const char*>(kwave ? a.k_cache : a.v_cache) + pb * block_bytes;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 4 * j + l4;
             const uint32_t rowoff = r < nval ? (uint32_t)r * rs2 : 0u;
-            if (kdst) load_lds16(kb + (rowoff + (koff0 ^ (uint32_t)(j << 6))), kdst + (16 * wave + 4 * j) * kPD);
-            if (vdst) load_lds16(vb + (rowoff + voff), vdst + (16 * wave + 4 * j) * kPD);
+            const uint32_t coff = kwave ? (koff0 ^ (uint32_t)(j << 6)) : voff;
+            load_lds16(src + (rowoff + coff), dst + (16 * q + 4 * j) * kPD);
         }
     };
 
@@ -666,13 +686,13 @@ __global__ __launch_bounds__(256, 2) void prefill16_kernel(PrefillArgs a) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-    f32x16_t sbuf[2][2];            // S^T of tiles t (sbuf[t & 1]) and t + 1
+    f32x16_t sc[2];                 // S^T of the current tile
     float m = -INFINITY;            // running max of the lane's row (log2 domain, scaled)
     float lsum0 = 0.f, lsum1 = 0.f; // this lane's share of the row sum
     const float cs = a.scale_log2;
     constexpr uint32_t kOnes = DT == kF16 ? 0x3C003C00u : 0x3F803F80u;
 
-    auto qk = [&](const uint16_t* kbuf, f32x16_t (&s)[2]) {
+    auto qk = [&](const uint16_t* kbuf, f32x16_t (&s)[2]) __attribute__((always_inline)) {
         const char* base = reinterpret_cast<const char*>(kbuf);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -685,35 +705,66 @@ __global__ __launch_bounds__(256, 2) void prefill16_kernel(PrefillArgs a) {
                 const uint4 ka = *reinterpret_cast<const uint4*>(base + kaddr[kk] + kb * 32 * kPD * 2);
                 s[kb] = mfma32x32x16<DT>(ka, qf[kk], s[kb]);
             }
+        // K reads four products ahead
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
+        }
     };
 
-    // prologue: K(0), V(0), K(1) in flight, then S(0)
-    stage(0, block_of_scalar(0), lds_k0, lds_v0);
-    if (ntiles > 1) stage(1, block_of_scalar(1), lds_k1, nullptr);
+    // Pipeline.  At tile t the products read K(t), V(t) and (late waves, see
+    // below) V(t-1).  K waves copy K(t+3) into the buffer of K(t-1), V waves copy
+    // V(t+2) into that of V(t-2): both last read before this tile's barrier.
+    // Every wave issues 4 copies per tile, so a K wave waiting until at most 8
+    // are outstanding has K(t) in LDS, and a V wave waiting until at most 4 has
+    // V(t).  Tiles past the last are clamped to it: those copies refill buffers
+    // nobody reads again.
+    // prologue: K(0..2) or V(0..1)
+    const int clampt = ntiles - 1;
+    if (kwave) {
+        stage(0, block_of_scalar(0), lds_k0);
+        stage(min(1, clampt), block_of_scalar(min(1, clampt)), lds_k1);
+        stage(min(2, clampt), block_of_scalar(min(2, clampt)), lds_k2);
+    } else {
+        stage(0, block_of_scalar(0), lds_v0);
+        stage(min(1, clampt), block_of_scalar(min(1, clampt)), lds_v1);
+    }
+    const int ahead = kwave ? 3 : 2;      // tiles between the products and this wave's copies
+    int pb_next = raw_block(min(ahead, clampt));
+    // everything, Q included: the prologue copies were issued back to back, so
+    // this costs little more than waiting for the first ones, and afterwards no
+    // load the compiler knows of is outstanding inside the loop
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    __syncthreads();
-    if (wave_tiles > 0) qk(lds_k0, sbuf[0]);
 
-    auto body = [&](int t, auto par) {
-        constexpr int B = decltype(par)::value;          // t & 1
-        uint16_t* kcur = B ? lds_k1 : lds_k0;            // K(t): free (S(t) done)
-        uint16_t* knext = B ? lds_k0 : lds_k1;           // K(t+1)
-        uint16_t* vcur = B ? lds_v1 : lds_v0;            // V(t)
-        uint16_t* vnext = B ? lds_v0 : lds_v1;           // V(t+1) goes here (V(t-1) done)
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-        __syncthreads();
-        if (t + 1 < ntiles) stage(t + 1, block_of(t + 1), nullptr, vnext);
-        if (t + 2 < ntiles) stage(t + 2, block_of(t + 2), kcur, nullptr);
-        // ids of the chunk after next: its slot held the chunk last used at tile t + 1
-        if (((t + 2) & 63) == 1 && 64 * (((t + 2) >> 6) + 1) < ntiles) {
-            const int c = ((t + 2) >> 6) + 1;
-            if (c & 1) tab[1] = load_tab(c);
-            else tab[0] = load_tab(c);
+    // ---- O^T += V^T P^T over one tile
+    auto pv = [&](const uint16_t* vb, const uint4 (&pb)[4]) __attribute__((always_inline)) {
+        const char* vbase = reinterpret_cast<const char*>(vb);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const ps16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (ps16x4_t __attribute__((address_space(3)))*)(vbase + vaddr[db] + (16 * ks) * kPD * 2));
+                const ps16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (ps16x4_t __attribute__((address_space(3)))*)(vbase + vaddr[db] + (16 * ks + 8) * kPD * 2));
+                const uint2 l2 = __builtin_bit_cast(uint2, lo);
+                const uint2 h2 = __builtin_bit_cast(uint2, hi);
+                o[db] = mfma32x32x16<DT>(make_uint4(l2.x, l2.y, h2.x, h2.y), pb[ks], o[db]);
+            }
+        // V reads ahead of the products
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+        for (int i = 0; i < 14; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
         }
-        if (t >= wave_tiles) return;                      // uniform
+    };
 
-        f32x16_t (&sc)[2] = sbuf[B];
-        f32x16_t (&sn)[2] = sbuf[B ^ 1];
+    // ---- softmax of tile t: S(t) becomes probabilities pb (16-bit) against the
+    // running max; their sums are added to the row sums
+    auto softmax = [&](int t, uint4 (&pb)[4]) __attribute__((always_inline)) {
         const int k0 = t * kKT;
         if (k0 + kKT - 1 > wave_q_lo) {   // diagonal tile: causal mask by select
             const int lim = qpos - k0 - 4 * h;   // key offset 32 kb + 8 (r/4) + r%4 must not exceed it
@@ -723,12 +774,6 @@ __global__ __launch_bounds__(256, 2) void prefill16_kernel(PrefillArgs a) {
                 for (int r = 0; r < 16; ++r)
                     if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sc[kb][r] = -INFINITY;
         }
-
-        // ---- one scheduling region: S(t+1) on the matrix cores (K(t+1) fragments
-        // read ahead) while the vector ALUs take the max and the probabilities of
-        // tile t.  For the wave's last tile S(t+1) is computed from whatever the
-        // buffer holds and dropped, which keeps this region free of branches.
-        qk(knext, sn);
         float lmax0 = -INFINITY, lmax1 = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -736,8 +781,7 @@ __global__ __launch_bounds__(256, 2) void prefill16_kernel(PrefillArgs a) {
             lmax1 = __builtin_elementwise_maximum(lmax1, sc[1][r]);
         }
         const float lmax = __builtin_elementwise_maximum(lmax0, lmax1);
-        uint4 pb[4];
-        auto probs = [&](float nmu) {
+        auto probs = [&](float nmu) __attribute__((always_inline)) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int kb = ks >> 1, r0 = 8 * (ks & 1);
@@ -750,21 +794,6 @@ __global__ __launch_bounds__(256, 2) void prefill16_kernel(PrefillArgs a) {
             }
         };
         probs(m == -INFINITY ? 0.f : -m);
-        // interleave: K reads PF ahead, then MFMA / VALU / read
-        constexpr int PF = 6;
-        __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
-#pragma unroll
-        for (int i = 0; i < 16 - PF; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < PF; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-        }
-
         if (__any(lmax * cs > m + 8.f)) {   // raise the row max (rows of lanes l, l^32 agree)
             const float mb = xor32_max(lmax) * cs;
             const bool raise = mb > m + 8.f;
@@ -793,33 +822,55 @@ __global__ __launch_bounds__(256, 2) void prefill16_kernel(PrefillArgs a) {
             lsum0 = dot2<DT>(pb[ks + 1].z, kOnes, lsum0);
             lsum1 = dot2<DT>(pb[ks + 1].w, kOnes, lsum1);
         }
+    };
 
-        // ---- O^T += V^T P^T
-        const char* vbase = reinterpret_cast<const char*>(vcur);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                const ps16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (ps16x4_t __attribute__((address_space(3)))*)(vbase + vaddr[db] + (16 * ks) * kPD * 2));
-                const ps16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (ps16x4_t __attribute__((address_space(3)))*)(vbase + vaddr[db] + (16 * ks + 8) * kPD * 2));
-                const uint2 l2 = __builtin_bit_cast(uint2, lo);
-                const uint2 h2 = __builtin_bit_cast(uint2, hi);
-                o[db] = mfma32x32x16<DT>(make_uint4(l2.x, l2.y, h2.x, h2.y), pb[ks], o[db]);
+    // Ping-pong: the two waves on each SIMD (w and w + 4) work half a tile apart.
+    // Waves 0..3 do [S(t), softmax(t)] then [PV(t)]; waves 4..7 do [PV(t-1)]
+    // then [S(t), softmax(t)], keeping P(t-1) in registers across the barrier.
+    // While one wave's softmax keeps the vector ALUs busy, the other wave's
+    // products keep the matrix core busy.
+    const bool late = !kwave;               // waves 4..7
+    uint4 pkeep[4];                         // late waves: P of the previous tile
+    auto body = [&](int t, auto par) __attribute__((always_inline)) {
+        constexpr int B = decltype(par)::value;          // t & 3
+        uint16_t* kcur = kbuf(std::integral_constant<int, B>());   // K(t)
+        // K waves copy K(t+3) into the buffer of K(t-1); V waves copy V(t+2) into
+        // that of V(t-2) (read at tile t-2 and, by the late waves, at tile t-1)
+        uint16_t* dst = kwave ? kbuf(std::integral_constant<int, (B + 3) & 3>())
+                              : vbuf(std::integral_constant<int, (B + 2) & 3>());
+        if (kwave) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8): K(t) is in
+        else __builtin_amdgcn_s_waitcnt(0x0F74);         // vmcnt(4): V(t) is in
+        __syncthreads();
+        stage(min(t + ahead, clampt), valid_block(pb_next), dst);
+        pb_next = raw_block(min(t + 1 + ahead, clampt));
+        if (late) {
+            if (t >= 1 && t - 1 < wave_tiles) pv(vbuf(std::integral_constant<int, (B + 3) & 3>()), pkeep);
+            if (t < wave_tiles) {
+                qk(kcur, sc);
+                softmax(t, pkeep);
             }
-        // V reads two MFMAs ahead, the row-sum dot products in between
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-#pragma unroll
-        for (int i = 0; i < 14; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x002, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        } else if (t < wave_tiles) {
+            uint4 pb[4];
+            qk(kcur, sc);
+            softmax(t, pb);
+            pv(vbuf(std::integral_constant<int, B>()), pb);
         }
     };
-    for (int t = 0; t < ntiles; t += 2) {
-        body(t, std::integral_constant<int, 0>());
-        if (t + 1 < ntiles) body(t + 1, std::integral_constant<int, 1>());
+    for (int t = 0; t < ntiles; t += 4) {
+        body(t, I0());
+        if (t + 1 < ntiles) body(t + 1, I1());
+        if (t + 2 < ntiles) body(t + 2, I2());
+        if (t + 3 < ntiles) body(t + 3, I3());
+    }
+    // late waves: PV of their last tile (its V buffer is not refilled after the loop)
+    if (late && wave_tiles == ntiles && ntiles > 0) {
+        const int tl = ntiles - 1;
+        switch (tl & 3) {
+            case 0: pv(lds_v0, pkeep); break;
+            case 1: pv(lds_v1, pkeep); break;
+            case 2: pv(lds_v2, pkeep); break;
+            default: pv(lds_v3, pkeep); break;
+        }
     }
 
     if (wave_tiles == 0) return;
@@ -867,15 +918,15 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
 template <int DT>
 static void launch_prefill16_g(const PrefillArgs& a, hipStream_t s, dim3 grid) {
     switch (a.group) {
-        case 1: hipLaunchKernelGGL((prefill16_kernel<DT, 1>), grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((prefill16_kernel<DT, 2>), grid, dim3(256), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((prefill16_kernel<DT, 4>), grid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((prefill16_kernel<DT, 8>), grid, dim3(256), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((prefill16_kernel<DT, 1>), grid, dim3(64 * kW16), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((prefill16_kernel<DT, 2>), grid, dim3(64 * kW16), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((prefill16_kernel<DT, 4>), grid, dim3(64 * kW16), 0, s, a); break;
+        default: hipLaunchKernelGGL((prefill16_kernel<DT, 8>), grid, dim3(64 * kW16), 0, s, a); break;
     }
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
-    const int positions = kRows / a.group;
+    const int positions = kRows16 / a.group;
     const int64_t qtiles = (a.max_q_len + positions - 1) / positions;
     const int64_t wgs = qtiles * a.num_seqs * a.num_kv_heads;
     if (wgs == 0) return hipSuccess;
