@@ -71,6 +71,112 @@ typedef short ps16x4_t __attribute__((ext_vector_type(4)));
 constexpr int kKRow = kPD + 8;      // LDS K row stride (elements): 272 bytes, so the 16 rows of
                                     // an MFMA A fragment start 4 banks apart (conflict-free)
 
+// Work order.  A workgroup's cost is its number of key tiles, which grows with
+// the sequence's cached context and with the q tile's position, so neither the
+// q-tile index nor the sequence index orders the work.  Workgroup x takes kv
+// head x % Hkv and the (x / Hkv)-th costliest (sequence, q tile) item -- ties
+// broken by sequence, then by later q tile first -- so the grid runs
+// longest-first and the last wave of workgroups is short.  Each wave finds its
+// item on its own from the lengths in device memory: a binary search over the
+// tile count, with a closed-form count per sequence, then a prefix count over
+// the sequences whose items tie.
+struct SeqLens {
+    int ctx, len, nq;
+};
+
+__device__ __forceinline__ SeqLens prefill_seq(const PrefillArgs& a, int b, int P, int max_keys) {
+    const int64_t r0 = a.query_start_loc[b];
+    const int64_t r1 = min((int64_t)a.query_start_loc[b + 1], a.num_tokens);
+    SeqLens s;
+    s.len = (r0 < 0 || r1 <= r0) ? 0 : (int)min(r1 - r0, (int64_t)a.max_q_len);
+    s.ctx = min(max(a.ctx_lens[b], 0), max_keys);
+    s.nq = (s.len + P - 1) / P;
+    return s;
+}
+
+// items of one sequence with at least t key tiles: q tile q has
+// min(ctx + min((q + 1) P, len), max_keys) keys
+__device__ __forceinline__ int items_with_tiles(const SeqLens& s, int t, int P, int max_keys) {
+    if (s.nq == 0) return 0;
+    const int w = kKT * (t - 1) + 1;          // tiles >= t  <=>  keys >= w
+    if (w > max_keys) return 0;
+    const int d = w - s.ctx;
+    if (d <= 0) return s.nq;
+    if (d > s.len) return 0;
+    return s.nq - (d + P - 1) / P + 1;
+}
+
+__device__ __forceinline__ int wave_sum_i32(int x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+// (sequence, q tile) of rank j in the cost order; false if there are fewer items.
+// The lengths of up to 256 sequences stay in registers (4 per lane); the
+// lengths of any further sequences are read again at each step.
+__device__ bool prefill_item(const PrefillArgs& a, int P, int64_t j, int& b_out, int& qt_out) {
+    const int lane = threadIdx.x & 63;
+    const int max_keys = a.max_blocks_per_seq * kBlockSize;
+    constexpr int kHeld = 4;
+    SeqLens held[kHeld];
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i) {
+        const int b = lane + 64 * i;
+        held[i] = b < a.num_seqs ? prefill_seq(a, b, P, max_keys) : SeqLens{0, 0, 0};
+    }
+    auto seq_at = [&](int i) -> SeqLens {   // sequence lane + 64 i
+        if (i < kHeld) {
+            SeqLens s = held[0];
+#pragma unroll
+            for (int k = 1; k < kHeld; ++k) s = i == k ? held[k] : s;
+            return s;
+        }
+        const int b = lane + 64 * i;
+        return b < a.num_seqs ? prefill_seq(a, b, P, max_keys) : SeqLens{0, 0, 0};
+    };
+    const int chunks = (a.num_seqs + 63) / 64;
+    auto count = [&](int t) -> int {
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < kHeld; ++i) c += items_with_tiles(held[i], t, P, max_keys);
+        for (int i = kHeld; i < chunks; ++i) c += items_with_tiles(seq_at(i), t, P, max_keys);
+        return wave_sum_i32(c);
+    };
+    if (j >= count(1)) return false;
+    // largest t with count(t) > j
+    int lo = 1, hi = (max_keys + kKT - 1) / kKT + 1;   // count(lo) > j >= count(hi)
+    while (hi - lo > 1) {
+        const int mid = lo + (hi - lo) / 2;
+        if (count(mid) > (int)j) lo = mid;
+        else hi = mid;
+    }
+    int rank = (int)j - count(lo + 1);                  // among the items with exactly lo tiles
+    for (int i = 0; i < chunks; ++i) {
+        const SeqLens sl = seq_at(i);
+        const int above = items_with_tiles(sl, lo + 1, P, max_keys);
+        const int eq = items_with_tiles(sl, lo, P, max_keys) - above;
+        // inclusive prefix sum of eq over the lanes
+        int incl = eq;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(incl, off);
+            if (lane >= off) incl += v;
+        }
+        const int total = __shfl(incl, 63);
+        if (rank < total) {
+            const uint64_t hit = __ballot(incl > rank && incl - eq <= rank);
+            const int src = __builtin_ctzll(hit);
+            b_out = 64 * i + src;
+            const int excl = __shfl(incl - eq, src);
+            qt_out = __shfl(sl.nq - 1 - above, src) - (rank - excl);
+            return true;
+        }
+        rank -= total;
+    }
+    return false;
+}
+
 template <int DT, int G, bool F8>
 __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     constexpr int P = kRows / G;    // positions per workgroup
@@ -86,14 +192,12 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     const int lr = lane & 15;       // row (or column) within a 16-wide MFMA tile
     const int lg = lane >> 4;       // lane group 0..3
 
-    // heaviest tiles (last query positions, most keys) are dispatched first
-    const int units = a.num_seqs * a.num_kv_heads;
-    const int qtiles = (a.max_q_len + P - 1) / P;
-    const int id = blockIdx.x;
-    const int qtile = qtiles - 1 - id / units;
-    const int unit = id % units;
-    const int g = unit % a.num_kv_heads;
-    const int b = unit / a.num_kv_heads;
+    // costliest (sequence, q tile) items first
+    const int g = blockIdx.x % a.num_kv_heads;
+    int b, qtile;
+    if (!prefill_item(a, P, blockIdx.x / a.num_kv_heads, b, qtile)) return;   // uniform
+    b = uniform(b);
+    qtile = uniform(qtile);
 
     // the row range and context come from device memory: clamp them so a
     // malformed query_start_loc or ctx_lens can never send an access out of bounds
@@ -436,112 +540,6 @@ __device__ __forceinline__ void load_lds16(const void* src, uint16_t* lds_row0) 
 }
 
 constexpr int kTileElems = kKT * kPD;   // one K or V tile in LDS, 16 KiB
-
-// Work order.  A workgroup's cost is its number of key tiles, which grows with
-// the sequence's cached context and with the q tile's position, so neither the
-// q-tile index nor the sequence index orders the work.  Workgroup x takes kv
-// head x % Hkv and the (x / Hkv)-th costliest (sequence, q tile) item -- ties
-// broken by sequence, then by later q tile first -- so the grid runs
-// longest-first and the last wave of workgroups is short.  Each wave finds its
-// item on its own from the lengths in device memory: a binary search over the
-// tile count, with a closed-form count per sequence, then a prefix count over
-// the sequences whose items tie.
-struct SeqLens {
-    int ctx, len, nq;
-};
-
-__device__ __forceinline__ SeqLens prefill_seq(const PrefillArgs& a, int b, int P, int max_keys) {
-    const int64_t r0 = a.query_start_loc[b];
-    const int64_t r1 = min((int64_t)a.query_start_loc[b + 1], a.num_tokens);
-    SeqLens s;
-    s.len = (r0 < 0 || r1 <= r0) ? 0 : (int)min(r1 - r0, (int64_t)a.max_q_len);
-    s.ctx = min(max(a.ctx_lens[b], 0), max_keys);
-    s.nq = (s.len + P - 1) / P;
-    return s;
-}
-
-// items of one sequence with at least t key tiles: q tile q has
-// min(ctx + min((q + 1) P, len), max_keys) keys
-__device__ __forceinline__ int items_with_tiles(const SeqLens& s, int t, int P, int max_keys) {
-    if (s.nq == 0) return 0;
-    const int w = kKT * (t - 1) + 1;          // tiles >= t  <=>  keys >= w
-    if (w > max_keys) return 0;
-    const int d = w - s.ctx;
-    if (d <= 0) return s.nq;
-    if (d > s.len) return 0;
-    return s.nq - (d + P - 1) / P + 1;
-}
-
-__device__ __forceinline__ int wave_sum_i32(int x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-    return x;
-}
-
-// (sequence, q tile) of rank j in the cost order; false if there are fewer items.
-// The lengths of up to 256 sequences stay in registers (4 per lane); the
-// lengths of any further sequences are read again at each step.
-__device__ bool prefill_item(const PrefillArgs& a, int P, int64_t j, int& b_out, int& qt_out) {
-    const int lane = threadIdx.x & 63;
-    const int max_keys = a.max_blocks_per_seq * kBlockSize;
-    constexpr int kHeld = 4;
-    SeqLens held[kHeld];
-#pragma unroll
-    for (int i = 0; i < kHeld; ++i) {
-        const int b = lane + 64 * i;
-        held[i] = b < a.num_seqs ? prefill_seq(a, b, P, max_keys) : SeqLens{0, 0, 0};
-    }
-    auto seq_at = [&](int i) -> SeqLens {   // sequence lane + 64 i
-        if (i < kHeld) {
-            SeqLens s = held[0];
-#pragma unroll
-            for (int k = 1; k < kHeld; ++k) s = i == k ? held[k] : s;
-            return s;
-        }
-        const int b = lane + 64 * i;
-        return b < a.num_seqs ? prefill_seq(a, b, P, max_keys) : SeqLens{0, 0, 0};
-    };
-    const int chunks = (a.num_seqs + 63) / 64;
-    auto count = [&](int t) -> int {
-        int c = 0;
-#pragma unroll
-        for (int i = 0; i < kHeld; ++i) c += items_with_tiles(held[i], t, P, max_keys);
-        for (int i = kHeld; i < chunks; ++i) c += items_with_tiles(seq_at(i), t, P, max_keys);
-        return wave_sum_i32(c);
-    };
-    if (j >= count(1)) return false;
-    // largest t with count(t) > j
-    int lo = 1, hi = (max_keys + kKT - 1) / kKT + 1;   // count(lo) > j >= count(hi)
-    while (hi - lo > 1) {
-        const int mid = lo + (hi - lo) / 2;
-        if (count(mid) > (int)j) lo = mid;
-        else hi = mid;
-    }
-    int rank = (int)j - count(lo + 1);                  // among the items with exactly lo tiles
-    for (int i = 0; i < chunks; ++i) {
-        const SeqLens sl = seq_at(i);
-        const int above = items_with_tiles(sl, lo + 1, P, max_keys);
-        const int eq = items_with_tiles(sl, lo, P, max_keys) - above;
-        // inclusive prefix sum of eq over the lanes
-        int incl = eq;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int v = __shfl_up(incl, off);
-            if (lane >= off) incl += v;
-        }
-        const int total = __shfl(incl, 63);
-        if (rank < total) {
-            const uint64_t hit = __ballot(incl > rank && incl - eq <= rank);
-            const int src = __builtin_ctzll(hit);
-            b_out = 64 * i + src;
-            const int excl = __shfl(incl - eq, src);
-            qt_out = __shfl(sl.nq - 1 - above, src) - (rank - excl);
-            return true;
-        }
-        rank -= total;
-    }
-    return false;
-}
 
 constexpr int kW16 = 8;                 // waves per workgroup
 constexpr int kRows16 = 32 * kW16;      // query rows per workgroup
