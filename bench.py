@@ -568,14 +568,16 @@ def _secondary_multi(steps, warmup, nq=4):
     q = torch.from_numpy(rng.standard_normal((c.num_seqs, nq, c.num_q_heads, c.head_dim),
                                              dtype=np.float32)).to(torch.float16).cuda()
     out = torch.empty_like(q)
+    # the library's own default partition for several queries (the size for
+    # partition 0 of num_seqs * nq single-query sequences always suffices)
     need = pa.pa_decode_workspace_size(c.num_seqs * nq, c.num_q_heads, c.num_kv_heads, c.head_dim,
-                                       c.max_blocks_per_seq, run.part)
+                                       c.max_blocks_per_seq, 0)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     if run.has_write:
         pa.pa_reshape_and_cache(run.key, run.value, run.kc, run.vc, run.slots)
 
     def step():
-        pa.pa_decode_multi(out, q, run.kc, run.vc, run.tables, run.lens, c.scale, run.part, ws,
+        pa.pa_decode_multi(out, q, run.kc, run.vc, run.tables, run.lens, c.scale, 0, ws,
                            flags=run.flags)
 
     for _ in range(warmup):

@@ -209,6 +209,11 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
  *                 whose position is negative gives an all-zero row.
  *   q_per_seq     1 .. PA_MAX_QUERIES_PER_SEQ (1 is exactly pa_decode).
  *   workspace     pa_decode_workspace_size(num_seqs * q_per_seq, ...) bytes.
+ *   partition_tokens  0 picks a default: the single-query default, doubled
+ *                 (at most 2048 tokens) when q_per_seq > 1 and the call runs
+ *                 on the matrix-core kernel (head_dim 128, q_per_seq x group >= 3).  The
+ *                 workspace size above, taken with partition_tokens 0, always
+ *                 suffices for it.
  *
  * Rejecting drafts needs no work here: the next step simply passes the
  * shorter seq_lens.  Every other argument and rule as for pa_decode.

@@ -392,9 +392,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
             const bool seen = MQ ? (ok && j * kBlockSize + 4 * i + lg < lim) : valid[i];
             x[i] = seen ? sacc[i] * cs : -INFINITY;
         }
-        float mb = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        mb = fmaxf(mb, __shfl_xor(mb, 16));
-        mb = fmaxf(mb, __shfl_xor(mb, 32));
+        float mb = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0], x[1]),
+                                                 __builtin_elementwise_maximum(x[2], x[3]));
+        mb = xor32_max(xor16_max(mb));   // lanes l, l^16, l^32, l^48: VALU lane swaps
         // raise the running max only when this block beats it by more than 2^8:
         // otherwise keep it (p <= 256, exact algebra) and skip the rescale of O^T
         const bool raise = mb > m + 8.f;   // also true on the first live block
@@ -450,8 +450,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         }
     }
 
-    float lt = l + __shfl_xor(l, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = xor32_sum(xor16_sum(l));
     if (!head_live) return;
     if (nparts == 1) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
