@@ -52,6 +52,12 @@ def _args():
                     help="CPU budget of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--workload", choices=sorted(_ONE_WORKLOAD),
+                    help="run only this workload and print its line (for profilers)")
+    ap.add_argument("--traffic-profile", metavar="DIR",
+                    help="no GPU work: read the rocprofv3 FETCH_SIZE / WRITE_SIZE runs under "
+                         "DIR/{dec,copy}_{FETCH_SIZE,WRITE_SIZE} and write the decode "
+                         "partition kernel's HBM traffic JSON to stdout")
     return ap.parse_args()
 
 
@@ -647,8 +653,102 @@ def _copy_calibration():
     print(json.dumps({"copy_bytes_per_launch": n}))
 
 
+def _run_one(name, steps, warmup):
+    from workloads import (decode_gqa_shared_prefix, decode_llama2_7b_layer,
+                           decode_long_context, decode_tiny)
+    table = {
+        "decode_gqa_shared_prefix": lambda: _secondary_decode(
+            decode_gqa_shared_prefix, name, steps, warmup, _shared_prefix_note, cpu=False),
+        "decode_long_context": lambda: _secondary_decode(decode_long_context, name, steps, warmup, cpu=False),
+        "decode_tiny": lambda: _secondary_decode(decode_tiny, name, steps, warmup, cpu=False),
+        "prefill_chunked": lambda: _secondary_prefill(steps, warmup, oracle_budget_s=0),
+        "prefill_chunked_fp8": lambda: _secondary_prefill(steps, warmup, oracle_budget_s=0, fp8=True),
+        "decode_llama2_7b_layer_fp8": lambda: _secondary_decode(
+            decode_llama2_7b_layer, name, steps, warmup, cpu=False, fp8=True),
+        "decode_gqa_shared_prefix_fp8": lambda: _secondary_decode(
+            decode_gqa_shared_prefix, name, steps, warmup, cpu=False, fp8=True),
+        "decode_long_context_fp8": lambda: _secondary_decode(
+            decode_long_context, name, steps, warmup, cpu=False, fp8=True),
+        "decode_llama2_7b_layer_verify": lambda: _secondary_multi(steps, warmup),
+        "copy_blocks": lambda: _secondary_copy_blocks(steps, warmup),
+    }
+    return table[name]()
+
+
+_ONE_WORKLOAD = ("decode_gqa_shared_prefix", "decode_long_context", "decode_tiny", "prefill_chunked",
+                 "prefill_chunked_fp8", "decode_llama2_7b_layer_fp8", "decode_gqa_shared_prefix_fp8",
+                 "decode_long_context_fp8", "decode_llama2_7b_layer_verify", "copy_blocks")
+
+
+def _pmc_kib_per_dispatch(db_path, kernel_prefix, counter):
+    """Mean of one counter (summed over its instances) per dispatch of the
+    kernels whose name starts with kernel_prefix, from a rocprofv3 database."""
+    import sqlite3
+    con = sqlite3.connect(db_path)
+    rows = con.execute("select dispatch_id, name, counter_name, counter_value from pmc_events").fetchall()
+    con.close()
+    per = {}
+    for disp, name, cname, val in rows:
+        if cname == counter and name.startswith(kernel_prefix):
+            per[disp] = per.get(disp, 0.0) + float(val)
+    if not per:
+        raise SystemExit(f"{db_path}: no {counter} samples for {kernel_prefix}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def _traffic_profile(root):
+    """HBM bytes per launch of the decode partition kernel: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) of the kernel, each scaled by what the same
+    counter reads for a 1 GiB device copy (1 GiB read and 1 GiB written)."""
+    import glob
+
+    def db(sub):
+        hits = glob.glob(os.path.join(root, sub, "**", "*_results.db"), recursive=True)
+        if len(hits) != 1:
+            raise SystemExit(f"expected one results database under {os.path.join(root, sub)}, found {hits}")
+        return hits[0]
+
+    kern = "void pa::decode_partition_kernel<0, 128, 1, true, false>"
+    copy = "__amd_rocclr_copyBuffer"
+    f_dec, n_f = _pmc_kib_per_dispatch(db("dec_FETCH_SIZE"), kern, "FETCH_SIZE")
+    w_dec, n_w = _pmc_kib_per_dispatch(db("dec_WRITE_SIZE"), kern, "WRITE_SIZE")
+    f_copy, _ = _pmc_kib_per_dispatch(db("copy_FETCH_SIZE"), copy, "FETCH_SIZE")
+    w_copy, _ = _pmc_kib_per_dispatch(db("copy_WRITE_SIZE"), copy, "WRITE_SIZE")
+    n = 1 << 30
+    fs, ws = n / (f_copy * 1024), n / (w_copy * 1024)
+    from workloads import decode_llama2_7b_layer
+    case = decode_llama2_7b_layer()
+    lens = case.seq_lens.astype(np.int64)
+    kv = int(lens.sum()) * 2 * case.num_kv_heads * case.head_dim * 2
+    qo = 2 * case.num_seqs * case.num_q_heads * case.head_dim * 2
+    algo = kv + qo + int(((lens + 15) // 16).sum()) * 4
+    out = {
+        "kernel": "decode_partition_kernel<f16,128,1,stream> on decode_llama2_7b_layer (partition 512 tokens)",
+        "decode_hip_sha256": hashlib.sha256(open(DECODE_SOURCE, "rb").read()).hexdigest(),
+        "fetch_size_kib_per_launch": round(f_dec, 1), "write_size_kib_per_launch": round(w_dec, 1),
+        "dispatches": [n_f, n_w],
+        "copy_calibration": {"bytes": n, "fetch_size_kib": round(f_copy, 1), "write_size_kib": round(w_copy, 1),
+                             "fetch_scale": fs, "write_scale": ws},
+        "hbm_fetch_bytes_per_launch": int(f_dec * 1024 * fs),
+        "hbm_write_bytes_per_launch": int(w_dec * 1024 * ws),
+        "hbm_bytes_per_launch": int(f_dec * 1024 * fs + w_dec * 1024 * ws),
+        "algorithmic_bytes_per_launch": algo,
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc/dec_FETCH_SIZE -o run -- python3 -u bench.py --quick --no-cpu-baseline --steps 5 --warmup 2",
+            "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc/dec_WRITE_SIZE -o run -- python3 -u bench.py --quick --no-cpu-baseline --steps 5 --warmup 2",
+            "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc/copy_FETCH_SIZE -o run -- python3 -u bench.py --copy-calibration",
+            "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc/copy_WRITE_SIZE -o run -- python3 -u bench.py --copy-calibration",
+            "python3 bench.py --traffic-profile gpurun_out/pmc > profiles/decode_partition_traffic.json",
+        ],
+    }
+    print(json.dumps(out, indent=1))
+
+
 def main():
     args = _args()
+    if args.traffic_profile:
+        _traffic_profile(args.traffic_profile)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path shards by sequence or kv head with no exchange; see the design notes)",
@@ -660,6 +760,10 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         _copy_calibration()
+        return
+    if args.workload:
+        import paged_kv_cache_24_amd  # noqa: F401  (raises if libpa.so is missing)
+        print(json.dumps(_run_one(args.workload, args.steps, args.warmup)), flush=True)
         return
     import paged_kv_cache_24_amd  # noqa: F401  (raises if libpa.so is missing)
     from workloads import (decode_gqa_shared_prefix, decode_llama2_7b_layer,
