@@ -147,3 +147,39 @@ def test_captured_verification_step_matches_eager():
         step(eager)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(host_bits(out_graph), host_bits(eager), err_msg=f"replay {replay}")
+
+
+def test_captured_prefill_step_matches_eager():
+    """Cache write + chunked prefill captured once, replayed with new q and new
+    k/v and with the cached-context lengths shortened in place; every replay
+    equals the eager step bit for bit."""
+    import paged_kv_cache_24_amd as pa
+    from gpu_helpers import PrefillOnGPU
+    from workloads import make_prefill_case
+    ctx = [40, 0, 300]
+    c = make_prefill_case(name="graph-prefill", seed=27, dtype="bf16", num_q_heads=8,
+                          num_kv_heads=2, head_dim=128, q_lens=[70, 1, 33], ctx_lens=ctx,
+                          scale=0.088)
+    g = PrefillOnGPU(c)
+    out_graph = torch.zeros_like(g.q)
+
+    def step(out=out_graph):
+        pa.pa_reshape_and_cache(g.key, g.value, g.k_cache, g.v_cache, g.slots)
+        pa.pa_prefill_paged(out, g.q, g.k_cache, g.v_cache, g.tables, g.ctx, g.qsl, c.scale,
+                            c.max_q_len)
+
+    graph = _capture(step)
+    rng = np.random.default_rng(28)
+    for replay in range(3):
+        g.q.copy_(dev_bits(normal_bits(rng, tuple(g.q.shape), "bf16"), "bf16"))
+        g.key.copy_(dev_bits(normal_bits(rng, tuple(g.key.shape), "bf16"), "bf16"))
+        g.value.copy_(dev_bits(normal_bits(rng, tuple(g.value.shape), "bf16"), "bf16"))
+        # a shorter cached context: the rows see fewer keys (the slots written stay valid)
+        g.ctx.copy_(dev_int(np.maximum(np.array(ctx) - 16 * replay, 0).astype(np.int32)))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        eager = torch.zeros_like(g.q)
+        step(eager)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_bits(out_graph), host_bits(eager), err_msg=f"replay {replay}")

@@ -121,3 +121,35 @@ def test_prefill_many_sequences():
                           head_dim=128, q_lens=q_lens, ctx_lens=ctx, scale=0.09)
     _, out, ref = _run(c)
     assert_close(out, ref, "bf16", c.name)
+
+
+def test_prefill_block_permutation_invariance_bit_exact():
+    """The same data under a new random placement of the physical blocks gives
+    the same bits: the kernel's arithmetic depends on logical positions only."""
+    from gpu_helpers import dev_bits
+    c = make_prefill_case(name="perm", seed=36, dtype="bf16", num_q_heads=16, num_kv_heads=4,
+                          head_dim=128, q_lens=[90, 5, 300], ctx_lens=[200, 0, 1100],
+                          scale=0.088, extra_blocks=7)
+    g = PrefillOnGPU(c)
+    g.write()
+    base = host_bits(g.prefill()).copy()
+    kc, vc = host_bits(g.k_cache), host_bits(g.v_cache)
+    perm = np.random.default_rng(37).permutation(c.num_blocks)
+    kp, vp = np.empty_like(kc), np.empty_like(vc)
+    kp[perm], vp[perm] = kc, vc
+    tables = np.where(c.block_tables >= 0, perm[np.maximum(c.block_tables, 0)], -1).astype(np.int32)
+    g.k_cache, g.v_cache = dev_bits(kp, c.dtype), dev_bits(vp, c.dtype)
+    g.tables = dev_int(tables)
+    g.out = torch.zeros_like(g.q)
+    np.testing.assert_array_equal(base, host_bits(g.prefill()))
+
+
+def test_prefill_deterministic_repeat():
+    c = make_prefill_case(name="repeat", seed=38, dtype="f16", num_q_heads=32, num_kv_heads=8,
+                          head_dim=128, q_lens=[257, 64, 3], ctx_lens=[700, 2000, 0], scale=0.088)
+    g = PrefillOnGPU(c)
+    g.write()
+    first = host_bits(g.prefill()).copy()
+    for _ in range(3):
+        g.out = torch.zeros_like(g.q)
+        np.testing.assert_array_equal(first, host_bits(g.prefill()))
