@@ -530,13 +530,16 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(const uint4& a, const uint4& b,
 // (lds_row0 wave-uniform).  Written as an instruction the compiler does not
 // model, so that it adds no waits of its own for these copies: the kernel waits
 // for them explicitly (vmcnt) before the barrier that publishes a buffer, and
-// no buffer is read in the tile in which it is being filled.
+// no buffer is read in the tile in which it is being filled.  The copy takes its
+// LDS base from m0, which the sequence saves and restores, so whatever the
+// compiler keeps in m0 is left as it was.
 __device__ __forceinline__ void load_lds16(const void* src, uint16_t* lds_row0) {
     const uint32_t m0v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)lds_row0;
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(m0v)
-                 : "m0");
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(src), "s"(m0v));
 }
 
 constexpr int kTileElems = kKT * kPD;   // one K or V tile in LDS, 16 KiB
