@@ -106,10 +106,10 @@ __device__ __forceinline__ int items_with_tiles(const SeqLens& s, int t, int P, 
     return s.nq - (d + P - 1) / P + 1;
 }
 
+// sum over the wave on the vector ALUs (DPP within 16 lanes, then lane swaps);
+// the counts summed here stay far below 2^24, so float adds are exact
 __device__ __forceinline__ int wave_sum_i32(int x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-    return x;
+    return (int)xor32_sum(xor16_sum(group_sum<16>((float)x)));
 }
 
 // (sequence, q tile) of rank j in the cost order; false if there are fewer items.
