@@ -474,16 +474,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
 
 // Combine the partition states of one (sequence, q head):
 // out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p with M = max_p m_p.
-// One workgroup per (sequence, q head); its 256 threads split the partitions
-// (max pass) and then the (partition, element) pairs (sum pass).
+// One wave per output row (sequence, query, q head); lane i owns elements
+// D/64 * i ..: the max and the denominator are wave reductions over the
+// partitions' (m, l), the numerator one pass over the partial rows -- no LDS,
+// no barrier, so the merge costs little more than reading the partials.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-    constexpr int GROUPS = 256 / D;   // partition groups in the sum pass
-    __shared__ float red[4];
-    __shared__ float part_num[GROUPS][D];
-    __shared__ float part_den[GROUPS];
-    const int tid = threadIdx.x;
-    const int64_t item = blockIdx.x;   // q / out row: (sequence, query, q head)
+    constexpr int EPL = D / kWave;   // elements per lane
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t item = (int64_t)blockIdx.x * 4 + uniform(threadIdx.x >> 6);   // q / out row
     if (item >= (int64_t)a.num_seqs * a.q_per_seq * a.num_q_heads) return;
     const int b = (int)(item / ((int64_t)a.q_per_seq * a.num_q_heads));
 
@@ -496,36 +495,30 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 
     const int64_t base = item * a.num_parts;
     float big = -INFINITY;
-    for (int i = tid; i < nparts; i += 256) big = fmaxf(big, a.ws_ml[base + i].x);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) big = fmaxf(big, __shfl_xor(big, off));
-    if ((tid & 63) == 0) red[tid >> 6] = big;
-    __syncthreads();
-    big = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-
-    const int d = tid % D;
-    const int grp = tid / D;
-    float num = 0.f, den = 0.f;
-#pragma unroll 4
-    for (int i = grp; i < nparts; i += GROUPS) {
-        const float2 ml = a.ws_ml[base + i];
-        const float w = ml.x == -INFINITY ? 0.f : fast_exp2(ml.x - big);
-        den = fmaf(w, ml.y, den);
-        num = fmaf(w, a.ws_acc[(base + i) * D + d], num);
+    for (int p = lane; p < nparts; p += kWave) big = fmaxf(big, a.ws_ml[base + p].x);
+    big = xor32_max(xor16_max(group_max<16>(big)));
+    float den = 0.f;
+    for (int p = lane; p < nparts; p += kWave) {
+        const float2 ml = a.ws_ml[base + p];
+        den = fmaf(ml.x == -INFINITY ? 0.f : fast_exp2(ml.x - big), ml.y, den);
     }
-    part_num[grp][d] = num;
-    if (d == 0) part_den[grp] = den;
-    __syncthreads();
-    if (tid >= D) return;
-    num = 0.f;
-    den = 0.f;
+    den = xor32_sum(xor16_sum(group_sum<16>(den)));
+
+    float num[EPL];
 #pragma unroll
-    for (int g2 = 0; g2 < GROUPS; ++g2) {
-        num += part_num[g2][tid];
-        den += part_den[g2];
+    for (int e = 0; e < EPL; ++e) num[e] = 0.f;
+    const float* acc = a.ws_acc + base * D + EPL * lane;
+#pragma unroll 4
+    for (int p = 0; p < nparts; ++p) {
+        const float mp = a.ws_ml[base + p].x;   // the same address in every lane
+        const float w = mp == -INFINITY ? 0.f : fast_exp2(mp - big);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, acc[(int64_t)p * D + e], num[e]);
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
-    static_cast<uint16_t*>(a.out)[item * D + tid] = f32_to_bits<DT>(num * inv);
+    uint16_t* dst = static_cast<uint16_t*>(a.out) + item * D + EPL * lane;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dst[e] = f32_to_bits<DT>(num[e] * inv);
 }
 
 template <int DT, int D, bool NT, bool MQ>
@@ -572,8 +565,9 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {
     const int64_t items = (int64_t)a.num_seqs * a.q_per_seq * a.num_q_heads;
     if (items == 0 || a.num_parts <= 1) return hipSuccess;
-    if (items > 0x7fffffff) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)items);
+    const int64_t wgs = (items + 3) / 4;   // one wave per row
+    if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)wgs);
     if (a.dtype == kF16) {
         if (a.head_dim == 128) hipLaunchKernelGGL((decode_merge_kernel<kF16, 128>), grid, dim3(256), 0, s, a);
         else hipLaunchKernelGGL((decode_merge_kernel<kF16, 64>), grid, dim3(256), 0, s, a);
