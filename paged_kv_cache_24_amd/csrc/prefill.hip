@@ -82,6 +82,7 @@ constexpr int kKRow = kPD + 8;      // LDS K row stride (elements): 272 bytes, s
 // the sequences whose items tie.
 struct SeqLens {
     int ctx, len, nq;
+    int r0;   // first packed row of the sequence
 };
 
 __device__ __forceinline__ SeqLens prefill_seq(const PrefillArgs& a, int b, int P, int max_keys) {
@@ -91,6 +92,7 @@ __device__ __forceinline__ SeqLens prefill_seq(const PrefillArgs& a, int b, int 
     s.len = (r0 < 0 || r1 <= r0) ? 0 : (int)min(r1 - r0, (int64_t)a.max_q_len);
     s.ctx = min(max(a.ctx_lens[b], 0), max_keys);
     s.nq = (s.len + P - 1) / P;
+    s.r0 = (int)r0;
     return s;
 }
 
@@ -115,7 +117,8 @@ __device__ __forceinline__ int wave_sum_i32(int x) {
 // (sequence, q tile) of rank j in the cost order; false if there are fewer items.
 // The lengths of up to 256 sequences stay in registers (4 per lane); the
 // lengths of any further sequences are read again at each step.
-__device__ bool prefill_item(const PrefillArgs& a, int P, int64_t j, int& b_out, int& qt_out) {
+__device__ bool prefill_item(const PrefillArgs& a, int P, int64_t j, int& b_out, int& qt_out,
+                             SeqLens& seq_out) {
     const int lane = threadIdx.x & 63;
     const int max_keys = a.max_blocks_per_seq * kBlockSize;
     constexpr int kHeld = 4;
@@ -123,7 +126,7 @@ __device__ bool prefill_item(const PrefillArgs& a, int P, int64_t j, int& b_out,
 #pragma unroll
     for (int i = 0; i < kHeld; ++i) {
         const int b = lane + 64 * i;
-        held[i] = b < a.num_seqs ? prefill_seq(a, b, P, max_keys) : SeqLens{0, 0, 0};
+        held[i] = b < a.num_seqs ? prefill_seq(a, b, P, max_keys) : SeqLens{0, 0, 0, 0};
     }
     auto seq_at = [&](int i) -> SeqLens {   // sequence lane + 64 i
         if (i < kHeld) {
@@ -133,7 +136,7 @@ __device__ bool prefill_item(const PrefillArgs& a, int P, int64_t j, int& b_out,
             return s;
         }
         const int b = lane + 64 * i;
-        return b < a.num_seqs ? prefill_seq(a, b, P, max_keys) : SeqLens{0, 0, 0};
+        return b < a.num_seqs ? prefill_seq(a, b, P, max_keys) : SeqLens{0, 0, 0, 0};
     };
     const int chunks = (a.num_seqs + 63) / 64;
     auto count = [&](int t) -> int {
@@ -170,6 +173,10 @@ __device__ bool prefill_item(const PrefillArgs& a, int P, int64_t j, int& b_out,
             b_out = 64 * i + src;
             const int excl = __shfl(incl - eq, src);
             qt_out = __shfl(sl.nq - 1 - above, src) - (rank - excl);
+            seq_out.ctx = __shfl(sl.ctx, src);
+            seq_out.len = __shfl(sl.len, src);
+            seq_out.nq = __shfl(sl.nq, src);
+            seq_out.r0 = __shfl(sl.r0, src);
             return true;
         }
         rank -= total;
@@ -195,7 +202,8 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     // costliest (sequence, q tile) items first
     const int g = blockIdx.x % a.num_kv_heads;
     int b, qtile;
-    if (!prefill_item(a, P, blockIdx.x / a.num_kv_heads, b, qtile)) return;   // uniform
+    SeqLens picked;
+    if (!prefill_item(a, P, blockIdx.x / a.num_kv_heads, b, qtile, picked)) return;   // uniform
     b = uniform(b);
     qtile = uniform(qtile);
 
@@ -582,17 +590,14 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
 
     const int g = blockIdx.x % a.num_kv_heads;
     int b, qtile;
-    if (!prefill_item(a, P, blockIdx.x / a.num_kv_heads, b, qtile)) return;   // uniform
+    SeqLens picked;   // the search's own (clamped) lengths of sequence b
+    if (!prefill_item(a, P, blockIdx.x / a.num_kv_heads, b, qtile, picked)) return;   // uniform
     b = uniform(b);           // the same in every lane: let the compiler know
     qtile = uniform(qtile);
-
-    // clamp what comes from device memory so no access can leave its buffer
-    const int64_t row0 = a.query_start_loc[b];
-    const int64_t row1 = min((int64_t)a.query_start_loc[b + 1], a.num_tokens);
-    if (row0 < 0 || row1 <= row0) return;
-    const int L = (int)min(row1 - row0, (int64_t)a.max_q_len);
+    const int64_t row0 = uniform(picked.r0);
+    const int L = uniform(picked.len);   // > 0: the sequence has this item
     const int max_keys = a.max_blocks_per_seq * kBlockSize;
-    const int ctx = min(max(a.ctx_lens[b], 0), max_keys);
+    const int ctx = uniform(picked.ctx);
     const int pos0 = qtile * P;
     if (qtile < 0 || pos0 >= L) return;
     const int pos_end = min(L, pos0 + P);
@@ -647,9 +652,11 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
     // the copies of a tile, one tile ahead, so that the load has returned by the
     // time the next barrier has passed.  Ids of blocks past the keys become the
     // sequence's first block, ids out of range block 0.
-    auto raw_block = [&](int tt) __attribute__((always_inline)) -> int {   // uniform
+    const int key_blocks = (n_keys + kBlockSize - 1) / kBlockSize;   // >= 1, <= max_blocks_per_seq
+    auto raw_block = [&](int tt) __attribute__((always_inline)) -> int {   // uniform, branch-free
         const int blk = tt * 4 + q;
-        return blk * kBlockSize < n_keys ? ctab[blk] : first_blk;
+        const int pb = ctab[min(blk, key_blocks - 1)];
+        return blk < key_blocks ? pb : first_blk;
     };
     auto valid_block = [&](int pb) __attribute__((always_inline)) -> int { return pb >= 0 && pb < nb32 ? pb : 0; };
     auto block_of_scalar = [&](int tt) __attribute__((always_inline)) -> int { return valid_block(raw_block(tt)); };
@@ -724,13 +731,18 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
     // nobody reads again.
     // prologue: K(0..2) or V(0..1)
     const int clampt = ntiles - 1;
-    if (kwave) {
-        stage(0, block_of_scalar(0), lds_k0);
-        stage(min(1, clampt), block_of_scalar(min(1, clampt)), lds_k1);
-        stage(min(2, clampt), block_of_scalar(min(2, clampt)), lds_k2);
-    } else {
-        stage(0, block_of_scalar(0), lds_v0);
-        stage(min(1, clampt), block_of_scalar(min(1, clampt)), lds_v1);
+    {   // all block ids first: their loads are then in flight together
+        const int id0 = block_of_scalar(0);
+        const int id1 = block_of_scalar(min(1, clampt));
+        const int id2 = block_of_scalar(min(2, clampt));
+        if (kwave) {
+            stage(0, id0, lds_k0);
+            stage(min(1, clampt), id1, lds_k1);
+            stage(min(2, clampt), id2, lds_k2);
+        } else {
+            stage(0, id0, lds_v0);
+            stage(min(1, clampt), id1, lds_v1);
+        }
     }
     const int ahead = kwave ? 3 : 2;      // tiles between the products and this wave's copies
     int pb_next = raw_block(min(ahead, clampt));
