@@ -117,7 +117,7 @@ __device__ __forceinline__ int wave_sum_i32(int x) {
 // (sequence, q tile) of rank j in the cost order; false if there are fewer items.
 // The lengths of up to 256 sequences stay in registers (4 per lane); the
 // lengths of any further sequences are read again at each step.
-__device__ bool prefill_item(const PrefillArgs& a, int P, int64_t j, int& b_out, int& qt_out,
+__device__ __forceinline__ bool prefill_item(const PrefillArgs& a, int P, int64_t j, int& b_out, int& qt_out,
                              SeqLens& seq_out) {
     const int lane = threadIdx.x & 63;
     const int max_keys = a.max_blocks_per_seq * kBlockSize;
@@ -620,10 +620,8 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
             qf[kk] = ok ? *reinterpret_cast<const uint4*>(src + 16 * kk) : make_uint4(0, 0, 0, 0);
     }
     const int wave_pos_lo = pos0 + (wave * 32) / G;
-    const int wave_pos_hi = min(pos_end - 1, pos0 + (wave * 32 + 31) / G);
     const int wave_q_lo = ctx + wave_pos_lo;
-    // tiles this wave computes (its last row's keys), at most the workgroup's
-    const int wave_tiles = wave_pos_lo < pos_end ? min(ntiles, (ctx + wave_pos_hi) / kKT + 1) : 0;
+    const bool has_rows = wave_pos_lo < pos_end;   // uniform
 
     // ---- staging.  Waves 0..3 copy the K blocks and waves 4..7 the V blocks:
     // wave w copies block q = w % 4 of each tile (tile rows 16 q .. 16 q + 15) as
@@ -842,10 +840,18 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
     // then [S(t), softmax(t)], keeping P(t-1) in registers across the barrier.
     // While one wave's softmax keeps the vector ALUs busy, the other wave's
     // products keep the matrix core busy.
+    // A wave with rows computes every tile of the workgroup: tiles wholly past its
+    // rows' keys are masked to probabilities of exactly 0 (at most one such tile),
+    // which costs less than the accumulator copies that skipping them per tile
+    // makes the compiler insert.  A wave without rows only copies and syncs.  Each
+    // role runs a loop of its own, so that the register allocation of one does not
+    // constrain the other's.
     const bool late = !kwave;               // waves 4..7
     uint4 pkeep[4];                         // late waves: P of the previous tile
-    auto body = [&](int t, auto par) __attribute__((always_inline)) {
+    constexpr int kIdle = 0, kEarly = 1, kLate = 2;
+    auto body = [&](int t, auto par, auto role) __attribute__((always_inline)) {
         constexpr int B = decltype(par)::value;          // t & 3
+        constexpr int R = decltype(role)::value;
         uint16_t* kcur = kbuf(std::integral_constant<int, B>());   // K(t)
         // K waves copy K(t+3) into the buffer of K(t-1); V waves copy V(t+2) into
         // that of V(t-2) (read at tile t-2 and, by the late waves, at tile t-1)
@@ -856,27 +862,30 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
         __syncthreads();
         stage(min(t + ahead, clampt), valid_block(pb_next), dst);
         pb_next = raw_block(min(t + 1 + ahead, clampt));
-        if (late) {
-            if (t >= 1 && t - 1 < wave_tiles) pv(vbuf(std::integral_constant<int, (B + 3) & 3>()), pkeep);
-            if (t < wave_tiles) {
-                qk(kcur, sc);
-                softmax(t, pkeep);
-            }
-        } else if (t < wave_tiles) {
+        if constexpr (R == kLate) {
+            if (B != 0 || t >= 1) pv(vbuf(std::integral_constant<int, (B + 3) & 3>()), pkeep);
+            qk(kcur, sc);
+            softmax(t, pkeep);
+        } else if constexpr (R == kEarly) {
             uint4 pb[4];
             qk(kcur, sc);
             softmax(t, pb);
             pv(vbuf(std::integral_constant<int, B>()), pb);
         }
     };
-    for (int t = 0; t < ntiles; t += 4) {
-        body(t, I0());
-        if (t + 1 < ntiles) body(t + 1, I1());
-        if (t + 2 < ntiles) body(t + 2, I2());
-        if (t + 3 < ntiles) body(t + 3, I3());
-    }
+    auto tile_loop = [&](auto role) __attribute__((always_inline)) {
+        for (int t = 0; t < ntiles; t += 4) {
+            body(t, I0(), role);
+            if (t + 1 < ntiles) body(t + 1, I1(), role);
+            if (t + 2 < ntiles) body(t + 2, I2(), role);
+            if (t + 3 < ntiles) body(t + 3, I3(), role);
+        }
+    };
+    if (!has_rows) tile_loop(std::integral_constant<int, kIdle>());
+    else if (late) tile_loop(std::integral_constant<int, kLate>());
+    else tile_loop(std::integral_constant<int, kEarly>());
     // late waves: PV of their last tile (its V buffer is not refilled after the loop)
-    if (late && wave_tiles == ntiles && ntiles > 0) {
+    if (late && has_rows) {
         const int tl = ntiles - 1;
         switch (tl & 3) {
             case 0: pv(lds_v0, pkeep); break;
@@ -886,7 +895,7 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
         }
     }
 
-    if (wave_tiles == 0) return;
+    if (!has_rows) return;
     // ---- epilogue: full row sum, normalise, store the row if it exists
     const float l = xor32_sum(lsum0 + lsum1);
     const float inv = l > 0.f ? 1.f / l : 0.f;
