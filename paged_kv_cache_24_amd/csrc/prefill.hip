@@ -498,7 +498,7 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
 // ---------------------------------------------------------------------------
 // 16-bit cache: prefill on 32x32x16 matrix-core products, software-pipelined.
 //
-// One workgroup (4 waves) owns 128 query rows of one (sequence, kv head); each
+// One workgroup (8 waves) owns 256 query rows of one (sequence, kv head); each
 // wave owns 32 rows, so every K/V fragment read from LDS feeds a 32-row product
 // (half the LDS bytes per flop of 16-row waves).  Per 64-key tile and wave:
 //   S^T[key][row] = K Q^T : 2 key blocks x 8 steps of v_mfma_f32_32x32x16
@@ -510,11 +510,15 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
 //     probabilities: step ks uses accumulator values 8*(ks%2) .. +7 of key
 //     block ks/2, which are keys 16 ks + 4 (l/32) + {0..3, 8..11}).
 // K/V tiles go from HBM straight into LDS (global_load_lds_dwordx4: a wave's
-// 64 lanes fill 1 KiB = 4 token rows), with the 16-byte chunks of each row
-// permuted by an XOR of the row index so that neither the K fragment reads nor
-// the transposed V reads meet bank conflicts.  Pipeline per tile t: the loads
-// of V(t+1) and K(t+2) are issued first, then S(t+1) is computed on the matrix
-// cores while the vector ALUs turn S(t) into probabilities, then O += V(t) P(t).
+// 64 lanes fill 1 KiB = 4 token rows; waves 0..3 copy K, waves 4..7 V, four
+// LDS buffers of each), with the 16-byte chunks of each row permuted by an XOR
+// of the row index so that neither the K fragment reads nor the transposed V
+// reads meet bank conflicts.  The two waves on a SIMD work half a tile apart
+// (one does S, softmax, PV of tile t; the other PV of tile t-1, then S and
+// softmax of tile t), so that one wave's softmax runs on the vector ALUs while
+// the other's products keep the matrix core busy; the product phases run at a
+// raised wave priority, so that a ready product is not held back by the other
+// wave's vector instructions.
 // The softmax is optimistic: probabilities are taken against the running max m
 // and only if some score exceeds m by more than 2^8 (log2 domain) is the row max
 // raised, O and the sum rescaled and the tile redone -- an exact rewrite of the
@@ -534,20 +538,24 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(const uint4& a, const uint4& b,
     }
 }
 
-// 16-byte global -> LDS copy; the wave's LDS destination is lds_row0 + 16 * lane
-// (lds_row0 wave-uniform).  Written as an instruction the compiler does not
-// model, so that it adds no waits of its own for these copies: the kernel waits
-// for them explicitly (vmcnt) before the barrier that publishes a buffer, and
-// no buffer is read in the tile in which it is being filled.  The copy takes its
-// LDS base from m0, which the sequence saves and restores, so whatever the
-// compiler keeps in m0 is left as it was.
-__device__ __forceinline__ void load_lds16(const void* src, uint16_t* lds_row0) {
-    const uint32_t m0v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)lds_row0;
+// 16-byte global -> LDS copy of each lane's bytes at sbase + voff (sbase a
+// wave-uniform 64-bit base in scalar registers, voff a 32-bit per-lane offset,
+// so that no address arithmetic runs on the vector ALUs); the wave's LDS
+// destination is lds_base + kLdsOff + 16 * lane.  Written as an instruction the
+// compiler does not model, so that it adds no waits of its own for these
+// copies: the kernel waits for them explicitly (vmcnt) before the barrier that
+// publishes a buffer, and no buffer is read in the tile in which it is being
+// filled.  The copy takes its LDS base from m0, formed in m0 itself so that no
+// per-copy constants occupy scalar registers; the sequence saves and restores
+// m0, so whatever the compiler keeps there is left as it was.
+template <uint32_t kLdsOff>
+__device__ __forceinline__ void load_lds16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
     uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-                 "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+    asm volatile("s_mov_b32 %0, m0\n\ts_add_u32 m0, %3, %4\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
                  : "=&s"(saved)
-                 : "v"(src), "s"(m0v));
+                 : "v"(voff), "s"(sbase), "s"(lds_base), "i"(kLdsOff)
+                 : "scc");
 }
 
 constexpr int kTileElems = kKT * kPD;   // one K or V tile in LDS, 16 KiB
@@ -555,6 +563,8 @@ constexpr int kTileElems = kKT * kPD;   // one K or V tile in LDS, 16 KiB
 constexpr int kW16 = 8;                 // waves per workgroup
 constexpr int kRows16 = 32 * kW16;      // query rows per workgroup
 constexpr int kStages = 4;              // LDS buffers of K and of V
+constexpr int kQkAhead = 6;             // K fragment reads in flight ahead of the products
+constexpr int kPvAhead = 4;             // products whose V fragments are read ahead
 
 template <int DT, int G>
 __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) {
@@ -658,16 +668,31 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
     };
     auto valid_block = [&](int pb) __attribute__((always_inline)) -> int { return pb >= 0 && pb < nb32 ? pb : 0; };
     auto block_of_scalar = [&](int tt) __attribute__((always_inline)) -> int { return valid_block(raw_block(tt)); };
+    // byte offset of this lane's 16 bytes of copy j within a block
+    uint32_t coff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        coff[j] = (uint32_t)(4 * j + l4) * rs2 + (kwave ? (koff0 ^ (uint32_t)(j << 6)) : voff);
     // copies this wave's block of tile tt into dst (a K buffer for K waves, V for V waves)
     auto stage = [&](int tt, int pb, uint16_t* dst) __attribute__((always_inline)) {
         const int nval = n_keys - (tt * kKT + 16 * q);   // valid rows of this block (uniform)
         const char* src = static_cast<const char*>(kwave ? a.k_cache : a.v_cache) + pb * block_bytes;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 4 * j + l4;
-            const uint32_t rowoff = r < nval ? (uint32_t)r * rs2 : 0u;
-            const uint32_t coff = kwave ? (koff0 ^ (uint32_t)(j << 6)) : voff;
-            load_lds16(src + (rowoff + coff), dst + (16 * q + 4 * j) * kPD);
+        const uint32_t lb = uniform((uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)(dst + 16 * q * kPD));
+        constexpr uint32_t kRow4 = 4 * kPD * 2;   // LDS bytes of 4 token rows
+        if (nval >= kBlockSize) {
+            load_lds16_sv<0 * kRow4>(src, coff[0], lb);
+            load_lds16_sv<1 * kRow4>(src, coff[1], lb);
+            load_lds16_sv<2 * kRow4>(src, coff[2], lb);
+            load_lds16_sv<3 * kRow4>(src, coff[3], lb);
+        } else {   // the sequence's last, partial block
+            auto off = [&](int j) __attribute__((always_inline)) -> uint32_t {
+                const int r = 4 * j + l4;
+                return r < nval ? coff[j] : coff[j] - (uint32_t)r * rs2;
+            };
+            load_lds16_sv<0 * kRow4>(src, off(0), lb);
+            load_lds16_sv<1 * kRow4>(src, off(1), lb);
+            load_lds16_sv<2 * kRow4>(src, off(2), lb);
+            load_lds16_sv<3 * kRow4>(src, off(3), lb);
         }
     };
 
@@ -700,6 +725,7 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
 
     auto qk = [&](const uint16_t* kbuf, f32x16_t (&s)[2]) __attribute__((always_inline)) {
         const char* base = reinterpret_cast<const char*>(kbuf);
+        __builtin_amdgcn_s_setprio(2);   // the matrix core is the shared resource
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -711,13 +737,15 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
                 const uint4 ka = *reinterpret_cast<const uint4*>(base + kaddr[kk] + kb * 32 * kPD * 2);
                 s[kb] = mfma32x32x16<DT>(ka, qf[kk], s[kb]);
             }
-        // K reads four products ahead
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
+        // K reads kQkAhead products ahead of their use
+        __builtin_amdgcn_sched_group_barrier(0x100, kQkAhead, 2);
 #pragma unroll
-        for (int i = 0; i < 12; ++i) {
+        for (int i = 0; i < 16 - kQkAhead; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 2);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, kQkAhead, 2);
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // Pipeline.  At tile t the products read K(t), V(t) and (late waves, see
@@ -752,6 +780,7 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
     // ---- O^T += V^T P^T over one tile
     auto pv = [&](const uint16_t* vb, const uint4 (&pb)[4]) __attribute__((always_inline)) {
         const char* vbase = reinterpret_cast<const char*>(vb);
+        __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -764,13 +793,15 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
                 const uint2 h2 = __builtin_bit_cast(uint2, hi);
                 o[db] = mfma32x32x16<DT>(make_uint4(l2.x, l2.y, h2.x, h2.y), pb[ks], o[db]);
             }
-        // V reads ahead of the products
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+        // V reads (two per product) kPvAhead products ahead of their use
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPvAhead, 1);
 #pragma unroll
-        for (int i = 0; i < 14; ++i) {
+        for (int i = 0; i < 16 - kPvAhead; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, kPvAhead, 1);
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // ---- softmax of tile t: S(t) becomes probabilities pb (16-bit) against the
@@ -861,16 +892,23 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
         else __builtin_amdgcn_s_waitcnt(0x0F74);         // vmcnt(4): V(t) is in
         __syncthreads();
         stage(min(t + ahead, clampt), valid_block(pb_next), dst);
-        pb_next = raw_block(min(t + 1 + ahead, clampt));
+        // The next copy's block id is a scalar load, which shares its wait counter
+        // with the LDS reads and may complete out of order: the first LDS wait
+        // after it waits for it too.  It is issued after the K products, so that
+        // the softmax (no LDS waits) covers its latency.
         if constexpr (R == kLate) {
             if (B != 0 || t >= 1) pv(vbuf(std::integral_constant<int, (B + 3) & 3>()), pkeep);
             qk(kcur, sc);
+            pb_next = raw_block(min(t + 1 + ahead, clampt));
             softmax(t, pkeep);
         } else if constexpr (R == kEarly) {
             uint4 pb[4];
             qk(kcur, sc);
+            pb_next = raw_block(min(t + 1 + ahead, clampt));
             softmax(t, pb);
             pv(vbuf(std::integral_constant<int, B>()), pb);
+        } else {
+            pb_next = raw_block(min(t + 1 + ahead, clampt));
         }
     };
     auto tile_loop = [&](auto role) __attribute__((always_inline)) {
