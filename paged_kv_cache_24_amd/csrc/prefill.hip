@@ -76,10 +76,11 @@ constexpr int kKRow = kPD + 8;      // LDS K row stride (elements): 272 bytes, s
 // q-tile index nor the sequence index orders the work.  Workgroup x takes kv
 // head x % Hkv and the (x / Hkv)-th costliest (sequence, q tile) item -- ties
 // broken by sequence, then by later q tile first -- so the grid runs
-// longest-first and the last wave of workgroups is short.  Each wave finds its
-// item on its own from the lengths in device memory: a binary search over the
-// tile count, with a closed-form count per sequence, then a prefix count over
-// the sequences whose items tie.
+// longest-first and the last wave of workgroups is short.  The workgroup finds
+// its item from the lengths in device memory: a search over the tile count t
+// for the largest t with more than x / Hkv items of at least t tiles (a
+// closed-form count per sequence), in which the eight waves test eight
+// candidates per step, then a prefix count over the sequences whose items tie.
 struct SeqLens {
     int ctx, len, nq;
     int r0;   // first packed row of the sequence
@@ -114,12 +115,28 @@ __device__ __forceinline__ int wave_sum_i32(int x) {
     return (int)xor32_sum(xor16_sum(group_sum<16>((float)x)));
 }
 
-// (sequence, q tile) of rank j in the cost order; false if there are fewer items.
+// inclusive prefix sum over the wave's 64 lanes (DPP row shifts, then the
+// row broadcasts of lanes 15 and 31)
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+    return x;
+}
+
+// (sequence, q tile) of rank j in the cost order; false if there are fewer
+// items.  Called by all waves of the workgroup together (it holds barriers);
+// flags is 2 x kSearchWaves ints of LDS that nothing else uses meanwhile.
 // The lengths of up to 256 sequences stay in registers (4 per lane); the
 // lengths of any further sequences are read again at each step.
+constexpr int kSearchWaves = 8;
 __device__ __forceinline__ bool prefill_item(const PrefillArgs& a, int P, int64_t j, int& b_out, int& qt_out,
-                             SeqLens& seq_out) {
+                                             SeqLens& seq_out, int* flags) {
     const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
     const int max_keys = a.max_blocks_per_seq * kBlockSize;
     constexpr int kHeld = 4;
     SeqLens held[kHeld];
@@ -139,50 +156,61 @@ __device__ __forceinline__ bool prefill_item(const PrefillArgs& a, int P, int64_
         return b < a.num_seqs ? prefill_seq(a, b, P, max_keys) : SeqLens{0, 0, 0, 0};
     };
     const int chunks = (a.num_seqs + 63) / 64;
-    auto count = [&](int t) -> int {
+    auto count = [&](int t) -> int {   // items with at least t tiles (the same in every lane)
         int c = 0;
 #pragma unroll
         for (int i = 0; i < kHeld; ++i) c += items_with_tiles(held[i], t, P, max_keys);
         for (int i = kHeld; i < chunks; ++i) c += items_with_tiles(seq_at(i), t, P, max_keys);
         return wave_sum_i32(c);
     };
-    if (j >= count(1)) return false;
-    // largest t with count(t) > j
-    int lo = 1, hi = (max_keys + kKT - 1) / kKT + 1;   // count(lo) > j >= count(hi)
-    while (hi - lo > 1) {
-        const int mid = lo + (hi - lo) / 2;
-        if (count(mid) > (int)j) lo = mid;
-        else hi = mid;
+    // largest t with count(t) > j: invariant count(lo) > j >= count(hi), with
+    // lo = 0 standing for "none yet" (count(0) = all items).  Each step wave w
+    // tests candidate lo + 1 + w (hi - lo - 1) / 8; counts fall as t grows, so
+    // the passing candidates are a prefix.  Flags alternate between two slots,
+    // so one barrier per step suffices.
+    int lo = 0, hi = (max_keys + kKT - 1) / kKT + 1;   // count(hi) = 0
+    for (int step = 0; hi - lo > 1; ++step) {
+        const int c = lo + 1 + (wave * (hi - lo - 1)) / kSearchWaves;   // lo < c < hi
+        const bool pass = count(c) > (int)j;
+        int* slot = flags + (step & 1) * kSearchWaves;
+        if (lane == 0) slot[wave] = pass ? c : -c;
+        __syncthreads();
+        int nlo = lo, nhi = hi;
+#pragma unroll
+        for (int w = 0; w < kSearchWaves; ++w) {
+            const int v = slot[w];
+            nlo = v > 0 ? max(nlo, v) : nlo;
+            nhi = v > 0 ? nhi : min(nhi, -v);
+        }
+        lo = uniform(nlo);
+        hi = uniform(nhi);
     }
+    if (lo == 0) return false;   // j >= number of items
     int rank = (int)j - count(lo + 1);                  // among the items with exactly lo tiles
     for (int i = 0; i < chunks; ++i) {
         const SeqLens sl = seq_at(i);
         const int above = items_with_tiles(sl, lo + 1, P, max_keys);
         const int eq = items_with_tiles(sl, lo, P, max_keys) - above;
-        // inclusive prefix sum of eq over the lanes
-        int incl = eq;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int v = __shfl_up(incl, off);
-            if (lane >= off) incl += v;
-        }
-        const int total = __shfl(incl, 63);
+        const int incl = wave_incl_scan(eq);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
         if (rank < total) {
             const uint64_t hit = __ballot(incl > rank && incl - eq <= rank);
-            const int src = __builtin_ctzll(hit);
+            const int src = uniform(__builtin_ctzll(hit));
             b_out = 64 * i + src;
-            const int excl = __shfl(incl - eq, src);
-            qt_out = __shfl(sl.nq - 1 - above, src) - (rank - excl);
-            seq_out.ctx = __shfl(sl.ctx, src);
-            seq_out.len = __shfl(sl.len, src);
-            seq_out.nq = __shfl(sl.nq, src);
-            seq_out.r0 = __shfl(sl.r0, src);
+            const int excl = __builtin_amdgcn_readlane(incl - eq, src);
+            qt_out = __builtin_amdgcn_readlane(sl.nq - 1 - above, src) - (rank - excl);
+            seq_out.ctx = __builtin_amdgcn_readlane(sl.ctx, src);
+            seq_out.len = __builtin_amdgcn_readlane(sl.len, src);
+            seq_out.nq = __builtin_amdgcn_readlane(sl.nq, src);
+            seq_out.r0 = __builtin_amdgcn_readlane(sl.r0, src);
             return true;
         }
         rank -= total;
     }
     return false;
 }
+
+static_assert(kRows / 16 == kSearchWaves, "the work-order search takes one candidate per wave");
 
 template <int DT, int G, bool F8>
 __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
@@ -203,7 +231,8 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     const int g = blockIdx.x % a.num_kv_heads;
     int b, qtile;
     SeqLens picked;
-    if (!prefill_item(a, P, blockIdx.x / a.num_kv_heads, b, qtile, picked)) return;   // uniform
+    __shared__ int search_flags[2 * kSearchWaves];
+    if (!prefill_item(a, P, blockIdx.x / a.num_kv_heads, b, qtile, picked, search_flags)) return;   // uniform
     b = uniform(b);
     qtile = uniform(qtile);
 
@@ -561,6 +590,7 @@ __device__ __forceinline__ void load_lds16_sv(const void* sbase, uint32_t voff, 
 constexpr int kTileElems = kKT * kPD;   // one K or V tile in LDS, 16 KiB
 
 constexpr int kW16 = 8;                 // waves per workgroup
+static_assert(kW16 == kSearchWaves, "the work-order search takes one candidate per wave");
 constexpr int kRows16 = 32 * kW16;      // query rows per workgroup
 constexpr int kStages = 4;              // LDS buffers of K and of V
 constexpr int kQkAhead = 6;             // K fragment reads in flight ahead of the products
@@ -601,7 +631,10 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
     const int g = blockIdx.x % a.num_kv_heads;
     int b, qtile;
     SeqLens picked;   // the search's own (clamped) lengths of sequence b
-    if (!prefill_item(a, P, blockIdx.x / a.num_kv_heads, b, qtile, picked)) return;   // uniform
+    // the search's flags live in the last K buffer, which no copy fills before
+    // the first barrier of the tile loop
+    if (!prefill_item(a, P, blockIdx.x / a.num_kv_heads, b, qtile, picked, reinterpret_cast<int*>(lds_k3)))
+        return;               // uniform
     b = uniform(b);           // the same in every lane: let the compiler know
     qtile = uniform(qtile);
     const int64_t row0 = uniform(picked.r0);
