@@ -395,7 +395,10 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
         }
         const int k0 = t * kKT;
         if (wave_live && k0 <= wave_q_hi) {
-            // ---- S^T = K Q^T for 64 keys x 16 rows
+            // ---- S^T = K Q^T for 64 keys x 16 rows (the product phases run at a
+            // raised wave priority: a ready product goes ahead of other waves'
+            // vector instructions)
+            __builtin_amdgcn_s_setprio(2);
             f32x4_t s[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) s[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -408,6 +411,7 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
                     s[mt] = mfma16x16x32<DT>(ka, qf[kk], s[mt]);
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
             if constexpr (F8) {   // k scale of each key (keys 16*mt + 4*lg + i)
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
@@ -484,6 +488,7 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
             }
 
             // ---- O^T += V^T P^T; V^T fragments by transposed LDS reads of the row-major V tile
+            __builtin_amdgcn_s_setprio(2);
             const uint16_t* vbuf = lds_v[buf] + v_tr_off;
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
@@ -500,6 +505,7 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
                     if constexpr (F8) o[mt] = mfma16x16x32<DT>(va, pt[kc], o[mt]);
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
         }
         if (more) {
             if constexpr (F8) store_tile8(buf ^ 1, ck8, cv8, ksc, vsc);
