@@ -598,7 +598,6 @@ constexpr int kTileElems = kKT * kPD;   // one K or V tile in LDS, 16 KiB
 constexpr int kW16 = 8;                 // waves per workgroup
 static_assert(kW16 == kSearchWaves, "the work-order search takes one candidate per wave");
 constexpr int kRows16 = 32 * kW16;      // query rows per workgroup
-constexpr int kStages = 4;              // LDS buffers of K and of V
 constexpr int kQkAhead = 6;             // K fragment reads in flight ahead of the products
 constexpr int kPvAhead = 4;             // products whose V fragments are read ahead
 
