@@ -103,6 +103,7 @@ struct PrefillArgs {
     int64_t num_blocks;
     float scale_log2;
     int32_t dtype;
+    int32_t head_dim;        // 64 or 128
     // FP8 cache only: per (block, kv head, token) float32 scales
     const float* k_scales;   // [NB][Hkv][16]
     const float* v_scales;

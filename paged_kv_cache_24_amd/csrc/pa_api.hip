@@ -442,7 +442,7 @@ static pa_status prefill_common(void* out, const void* q, const void* k_cache, c
                                 int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                 int64_t num_blocks, float scale, pa_dtype dtype, hipStream_t stream) {
-    if (!supported_dtype(dtype) || block_size != PA_BLOCK_SIZE || head_dim != 128)
+    if (!supported_dtype(dtype) || block_size != PA_BLOCK_SIZE || (head_dim != 64 && head_dim != 128))
         return PA_ERR_UNSUPPORTED;
     if (num_seqs < 0 || num_tokens < 0 || max_q_len < 0 || num_q_heads <= 0 ||
         num_kv_heads <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
@@ -476,6 +476,7 @@ static pa_status prefill_common(void* out, const void* q, const void* k_cache, c
     a.num_blocks = num_blocks;
     a.scale_log2 = scale * kLog2e;
     a.dtype = dtype == PA_F16 ? pa::kF16 : pa::kBF16;
+    a.head_dim = head_dim;
     a.k_scales = k_scales;
     a.v_scales = v_scales;
     const hipError_t e = fp8 ? pa::launch_prefill_fp8(a, stream) : pa::launch_prefill(a, stream);

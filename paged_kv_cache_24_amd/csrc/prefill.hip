@@ -61,15 +61,11 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, 
     }
 }
 
-constexpr int kPD = 128;            // head_dim
+constexpr int kPD = 128;            // head_dim of the 32x32x16 kernel
 constexpr int kKT = 64;             // keys per tile
 constexpr int kRows = 128;          // query rows per workgroup (8 waves x 16)
-constexpr int kVRow = kPD + 16;     // LDS V row stride (elements): 288 bytes, conflict-free transposed reads
 
 typedef short ps16x4_t __attribute__((ext_vector_type(4)));
-
-constexpr int kKRow = kPD + 8;      // LDS K row stride (elements): 272 bytes, so the 16 rows of
-                                    // an MFMA A fragment start 4 banks apart (conflict-free)
 
 // Work order.  A workgroup's cost is its number of key tiles, which grows with
 // the sequence's cached context and with the q tile's position, so neither the
@@ -212,11 +208,16 @@ __device__ __forceinline__ bool prefill_item(const PrefillArgs& a, int P, int64_
 
 static_assert(kRows / 16 == kSearchWaves, "the work-order search takes one candidate per wave");
 
-template <int DT, int G, bool F8>
+template <int DT, int G, bool F8, int D>
 __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
+    static_assert(D == 64 || D == 128, "head_dim 64 or 128");
     constexpr int P = kRows / G;    // positions per workgroup
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kKT * kKRow];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kKT * kVRow];
+    constexpr int KR = D + 8;       // LDS K row stride (elements): rows 4 banks apart
+    constexpr int VR = D + 16;      // LDS V row stride (elements): rows 8 banks apart
+    constexpr int KK = D / 32;      // 32-element steps of QK^T
+    constexpr int MT = D / 16;      // 16-row blocks of O^T
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kKT * KR];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kKT * VR];
     // FP8 only: per-key k scale and v-scale mantissa factor of each staged tile
     __shared__ __attribute__((aligned(16))) float lds_ks[F8 ? 2 : 1][F8 ? kKT : 4];
     __shared__ __attribute__((aligned(16))) float lds_mu[F8 ? 2 : 1][F8 ? kKT : 4];
@@ -250,19 +251,19 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     const int n_keys = min(ctx + pos_end, max_keys);
     const int ntiles = (n_keys + kKT - 1) / kKT;
     const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
-    const int64_t row_stride = (int64_t)a.num_kv_heads * kPD;
+    const int64_t row_stride = (int64_t)a.num_kv_heads * D;
 
     // ---- this lane's query row and its Q^T fragments
-    uint4 qf[4];
+    uint4 qf[KK];
     const int rho = wave * 16 + lr;
     const int qpos = ctx + pos0 + rho / G;
     {
         const int pos = pos0 + rho / G;
         const bool ok = pos < L;
         const uint16_t* src = static_cast<const uint16_t*>(a.q) +
-                              ((row0 + (ok ? pos : 0)) * a.num_q_heads + g * G + rho % G) * kPD + 8 * lg;
+                              ((row0 + (ok ? pos : 0)) * a.num_q_heads + g * G + rho % G) * D + 8 * lg;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+        for (int kk = 0; kk < KK; ++kk)
             qf[kk] = ok ? *reinterpret_cast<const uint4*>(src + 32 * kk) : make_uint4(0, 0, 0, 0);
     }
     const int wave_pos_lo = pos0 + (wave * 16) / G;
@@ -271,9 +272,9 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     const int wave_q_lo = ctx + wave_pos_lo;
     const int wave_q_hi = ctx + wave_pos_hi;
 
-    f32x4_t o[8];
+    f32x4_t o[MT];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY;
     float lsum = 0.f;   // this lane's share of the row sum
     const float cs = a.scale_log2;
@@ -292,17 +293,21 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
             pb[q] = blk * kBlockSize < n_keys ? ctab[blk] : -1;
         }
     };
-    // 16-bit: thread t moves 16-byte chunk t % 16 of row (t / 16) % 16 of blocks
-    // 2 i + t / 256 (i = 0, 1) of the tile: a wave's two blocks are uniform.
-    const int ck = tid & 15;
-    const int rr = (tid >> 4) & 15;
-    const int half = uniform(tid >> 8);
-    const uint32_t lane_off = (uint32_t)(rr * row_stride + g * kPD + 8 * ck) * 2u;   // bytes
-    auto load_tile = [&](int tt, const int (&pb)[4], uint4 (&gk)[2], uint4 (&gv)[2]) {
+    // 16-bit: a row is CPR 16-byte chunks; thread t moves chunk t % CPR of row
+    // (t / CPR) % 16 of blocks QPP i + t / (16 CPR) (i < NI) of the tile, so a
+    // wave's blocks are uniform.
+    constexpr int CPR = D / 8;
+    constexpr int QPP = 32 / CPR;   // blocks per pass of the 512 threads
+    constexpr int NI = 4 / QPP;     // passes per tile
+    const int ck = tid % CPR;
+    const int rr = (tid / CPR) & 15;
+    const int part = uniform(tid / (16 * CPR));
+    const uint32_t lane_off = (uint32_t)(rr * row_stride + g * D + 8 * ck) * 2u;   // bytes
+    auto load_tile = [&](int tt, const int (&pb)[4], uint4 (&gk)[NI], uint4 (&gv)[NI]) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int q = 2 * i + half;
-            const int pbq = half ? pb[2 * i + 1] : pb[2 * i];
+        for (int i = 0; i < NI; ++i) {
+            const int q = QPP * i + part;   // uniform
+            const int pbq = q == 0 ? pb[0] : q == 1 ? pb[1] : q == 2 ? pb[2] : pb[3];
             const bool ok = pbq >= 0 && (int64_t)pbq < a.num_blocks;
             const int64_t base = (int64_t)(ok ? pbq : 0) * (kBlockSize * row_stride * 2);
             const uint4 k4 = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.k_cache) + base + lane_off);
@@ -315,24 +320,28 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
             gv[i] = valid ? v4 : make_uint4(0, 0, 0, 0);
         }
     };
-    auto store_tile = [&](int buf, const uint4 (&gk)[2], const uint4 (&gv)[2]) {
+    auto store_tile = [&](int buf, const uint4 (&gk)[NI], const uint4 (&gv)[NI]) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int kr = 16 * (2 * i + half) + rr;
-            *reinterpret_cast<uint4*>(&lds_k[buf][kr * kKRow + 8 * ck]) = gk[i];
-            *reinterpret_cast<uint4*>(&lds_v[buf][kr * kVRow + 8 * ck]) = gv[i];
+        for (int i = 0; i < NI; ++i) {
+            const int kr = 16 * (QPP * i + part) + rr;
+            *reinterpret_cast<uint4*>(&lds_k[buf][kr * KR + 8 * ck]) = gk[i];
+            *reinterpret_cast<uint4*>(&lds_v[buf][kr * VR + 8 * ck]) = gv[i];
         }
     };
-    // ---- FP8 staging: thread t moves the 16 codes 16*(t % 8) .. +16 of key row
-    // t / 8 (block t / 128: uniform per wave) and that row's two scales.  Invalid
-    // rows stage zeros with k scale 0 and v scale 1, so NaN bits in unused slots
-    // never reach the products.
-    const int c8 = tid & 7;
-    const int kr8 = tid >> 3;       // 0..63
-    const int q8 = uniform(tid >> 7);
-    const uint32_t lane_off8 = (uint32_t)((kr8 & 15) * row_stride + g * kPD + 16 * c8);   // bytes
+    // ---- FP8 staging: a key row is TPR8 runs of 16 codes; thread t < 64 TPR8
+    // moves the codes 16*(t % TPR8) .. +16 of key row t / TPR8 (block t / (16
+    // TPR8): uniform per wave) and that row's two scales; at D = 64 waves 4..7
+    // stage nothing.  Invalid rows stage zeros with k scale 0 and v scale 1, so
+    // NaN bits in unused slots never reach the products.
+    constexpr int TPR8 = D / 16;
+    const bool stage8 = tid < 64 * TPR8;   // uniform per wave
+    const int c8 = tid % TPR8;
+    const int kr8 = (tid / TPR8) & 63;     // key row 0..63 (a copy for the idle waves)
+    const int q8 = uniform(kr8 >> 4);
+    const uint32_t lane_off8 = (uint32_t)((kr8 & 15) * row_stride + g * D + 16 * c8);   // bytes
     const uint32_t lane_soff = (uint32_t)(g * kBlockSize + (kr8 & 15));                  // floats
     auto load_tile8 = [&](int tt, const int (&pb)[4], uint4& ck8, uint4& cv8, float& ksc, float& vsc) {
+        if (!stage8) return;
         const int pbq = q8 == 0 ? pb[0] : q8 == 1 ? pb[1] : q8 == 2 ? pb[2] : pb[3];
         const bool ok = pbq >= 0 && (int64_t)pbq < a.num_blocks;
         const int64_t pblk = ok ? pbq : 0;
@@ -349,6 +358,7 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
         vsc = valid ? vs : 1.f;
     };
     auto store_tile8 = [&](int buf, const uint4& ck8, const uint4& cv8, float ksc, float vsc) {
+        if (!stage8) return;
         const uint32_t kw[4] = {ck8.x, ck8.y, ck8.z, ck8.w};
         const uint32_t vw[4] = {cv8.x, cv8.y, cv8.z, cv8.w};
         uint2 ke[4], ve[4];
@@ -357,8 +367,8 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
             ke[e] = fp8x4_to_16<DT>(kw[e], 1.f);
             ve[e] = fp8x4_to_16<DT>(vw[e], vsc);
         }
-        uint4* kd = reinterpret_cast<uint4*>(&lds_k[buf][kr8 * kKRow + 16 * c8]);
-        uint4* vd = reinterpret_cast<uint4*>(&lds_v[buf][kr8 * kVRow + 16 * c8]);
+        uint4* kd = reinterpret_cast<uint4*>(&lds_k[buf][kr8 * KR + 16 * c8]);
+        uint4* vd = reinterpret_cast<uint4*>(&lds_v[buf][kr8 * VR + 16 * c8]);
         kd[0] = make_uint4(ke[0].x, ke[0].y, ke[1].x, ke[1].y);
         kd[1] = make_uint4(ke[2].x, ke[2].y, ke[3].x, ke[3].y);
         vd[0] = make_uint4(ve[0].x, ve[0].y, ve[1].x, ve[1].y);
@@ -369,9 +379,9 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
         }
     };
     // transposed V^T fragment address of this lane: row 4*lg + lr/4 (+16), column 4*(lr%4) (+16 mt)
-    const int v_tr_off = (4 * lg + (lr >> 2)) * kVRow + 4 * (lr & 3);
+    const int v_tr_off = (4 * lg + (lr >> 2)) * VR + 4 * (lr & 3);
 
-    uint4 gk[2], gv[2];
+    uint4 gk[NI], gv[NI];
     uint4 ck8, cv8;
     float ksc = 0.f, vsc = 1.f;
     int pbn[4];                     // block ids of the next tile to stage
@@ -403,11 +413,11 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) s[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
+            for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     const uint4 ka = *reinterpret_cast<const uint4*>(
-                        &lds_k[buf][(16 * mt + lr) * kKRow + 32 * kk + 8 * lg]);
+                        &lds_k[buf][(16 * mt + lr) * KR + 32 * kk + 8 * lg]);
                     s[mt] = mfma16x16x32<DT>(ka, qf[kk], s[mt]);
                 }
             }
@@ -447,7 +457,7 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
                 const float alpha = raise ? fast_exp2(m - mn) : 1.f;   // exp2(-inf) = 0
                 lsum *= alpha;
 #pragma unroll
-                for (int mt = 0; mt < 8; ++mt) o[mt] *= alpha;
+                for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
             }
             m = mn;
             const float nmu = mn == -INFINITY ? 0.f : -mn;
@@ -493,11 +503,11 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
 #pragma unroll
-                for (int mt = 0; mt < 8; ++mt) {
+                for (int mt = 0; mt < MT; ++mt) {
                     const ps16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (ps16x4_t __attribute__((address_space(3)))*)(vbuf + 32 * kc * kVRow + 16 * mt));
+                        (ps16x4_t __attribute__((address_space(3)))*)(vbuf + 32 * kc * VR + 16 * mt));
                     const ps16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (ps16x4_t __attribute__((address_space(3)))*)(vbuf + (32 * kc + 16) * kVRow + 16 * mt));
+                        (ps16x4_t __attribute__((address_space(3)))*)(vbuf + (32 * kc + 16) * VR + 16 * mt));
                     const uint2 l2 = __builtin_bit_cast(uint2, lo);
                     const uint2 h2 = __builtin_bit_cast(uint2, hi);
                     const uint4 va = make_uint4(l2.x, l2.y, h2.x, h2.y);
@@ -520,9 +530,9 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     const int pos = pos0 + rho / G;
     if (pos >= L) return;
     uint16_t* dst = static_cast<uint16_t*>(a.out) +
-                    ((row0 + pos) * a.num_q_heads + g * G + rho % G) * kPD + 4 * lg;
+                    ((row0 + pos) * a.num_q_heads + g * G + rho % G) * D + 4 * lg;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
         uint2 w;
         w.x = pack2<DT>(o[mt][0] * inv, o[mt][1] * inv);
         w.y = pack2<DT>(o[mt][2] * inv, o[mt][3] * inv);
@@ -990,16 +1000,17 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
         }
 }
 
-template <int DT, bool F8>
+template <int DT, bool F8, int D>
 static void launch_prefill_g(const PrefillArgs& a, hipStream_t s, dim3 grid) {
     switch (a.group) {
-        case 1: hipLaunchKernelGGL((prefill_kernel<DT, 1, F8>), grid, dim3(512), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<DT, 2, F8>), grid, dim3(512), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((prefill_kernel<DT, 4, F8>), grid, dim3(512), 0, s, a); break;
-        default: hipLaunchKernelGGL((prefill_kernel<DT, 8, F8>), grid, dim3(512), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((prefill_kernel<DT, 1, F8, D>), grid, dim3(512), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((prefill_kernel<DT, 2, F8, D>), grid, dim3(512), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((prefill_kernel<DT, 4, F8, D>), grid, dim3(512), 0, s, a); break;
+        default: hipLaunchKernelGGL((prefill_kernel<DT, 8, F8, D>), grid, dim3(512), 0, s, a); break;
     }
 }
 
+// the 16x16x32 kernel: every FP8 prefill, and 16-bit prefill at head_dim 64
 template <bool F8>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
     const int positions = kRows / a.group;
@@ -1008,8 +1019,17 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
     if (wgs == 0) return hipSuccess;
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs);
-    if (a.dtype == kF16) launch_prefill_g<kF16, F8>(a, s, grid);
-    else launch_prefill_g<kBF16, F8>(a, s, grid);
+    if (a.head_dim == 128) {
+        if constexpr (F8) {
+            if (a.dtype == kF16) launch_prefill_g<kF16, F8, 128>(a, s, grid);
+            else launch_prefill_g<kBF16, F8, 128>(a, s, grid);
+        } else {
+            return hipErrorInvalidValue;   // 16-bit at head_dim 128 runs prefill16_kernel
+        }
+    } else {
+        if (a.dtype == kF16) launch_prefill_g<kF16, F8, 64>(a, s, grid);
+        else launch_prefill_g<kBF16, F8, 64>(a, s, grid);
+    }
     return hipGetLastError();
 }
 
@@ -1024,6 +1044,7 @@ static void launch_prefill16_g(const PrefillArgs& a, hipStream_t s, dim3 grid) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
+    if (a.head_dim != kPD) return launch_prefill_t<false>(a, s);
     const int positions = kRows16 / a.group;
     const int64_t qtiles = (a.max_q_len + positions - 1) / positions;
     const int64_t wgs = qtiles * a.num_seqs * a.num_kv_heads;

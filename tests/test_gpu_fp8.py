@@ -239,14 +239,16 @@ def _check_fp8_prefill(c):
     return assert_close(out, ref, c.dtype, c.name + " fp8")
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (8, 2), (16, 2)])
-def test_fp8_prefill_shapes(dtype, hq, hkv):
+def test_fp8_prefill_shapes(dtype, hq, hkv, d):
     q_lens = [0, 1, 17, 64, 130, 5, 33]
     ctx = [3, 0, 40, 0, 100, 16, 250]
-    c = make_prefill_case(name=f"prefill-{dtype}-{hq}-{hkv}", seed=400 + hq, dtype=dtype,
-                          num_q_heads=hq, num_kv_heads=hkv, head_dim=128, q_lens=q_lens,
-                          ctx_lens=ctx, scale=1 / math.sqrt(128), extra_blocks=5)
+    seed = 400 + hq if d == 128 else 500 + hq
+    c = make_prefill_case(name=f"prefill-{dtype}-{hq}-{hkv}-d{d}", seed=seed, dtype=dtype,
+                          num_q_heads=hq, num_kv_heads=hkv, head_dim=d, q_lens=q_lens,
+                          ctx_lens=ctx, scale=1 / math.sqrt(d), extra_blocks=5)
     _check_fp8_prefill(c)
 
 

@@ -33,14 +33,25 @@ def _run(c):
     return g, out, ref
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (8, 2), (16, 2)])
-def test_prefill_shapes(dtype, hq, hkv):
+def test_prefill_shapes(dtype, hq, hkv, d):
     q_lens = [0, 1, 17, 64, 130, 5, 33]
     ctx = [3, 0, 40, 0, 100, 16, 250]
-    c = make_prefill_case(name=f"prefill-{dtype}-{hq}-{hkv}", seed=200 + hq, dtype=dtype,
-                          num_q_heads=hq, num_kv_heads=hkv, head_dim=128, q_lens=q_lens,
-                          ctx_lens=ctx, scale=1 / math.sqrt(128), extra_blocks=5)
+    c = make_prefill_case(name=f"prefill-{dtype}-{hq}-{hkv}-d{d}", seed=200 + hq + d, dtype=dtype,
+                          num_q_heads=hq, num_kv_heads=hkv, head_dim=d, q_lens=q_lens,
+                          ctx_lens=ctx, scale=1 / math.sqrt(d), extra_blocks=5)
+    _, out, ref = _run(c)
+    assert_close(out, ref, dtype, c.name)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_head_dim_64_long(dtype):
+    """head_dim 64 over many key tiles and every q tile of a long chunk."""
+    c = make_prefill_case(name=f"prefill-d64-long-{dtype}", seed=77, dtype=dtype, num_q_heads=32,
+                          num_kv_heads=4, head_dim=64, q_lens=[300, 1, 129], ctx_lens=[700, 1500, 0],
+                          scale=1 / 8, extra_blocks=3)
     _, out, ref = _run(c)
     assert_close(out, ref, dtype, c.name)
 
@@ -63,10 +74,11 @@ def test_prefill_rows_outside_sequences_untouched():
     assert (out[20:] == 3.0).all()
 
 
-def test_prefill_row_matches_decode():
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_row_matches_decode(d):
     """A prefill row at position p equals decode with seq_len p + 1."""
-    c = make_prefill_case(name="rowdec", seed=32, dtype="bf16", num_q_heads=16, num_kv_heads=4,
-                          head_dim=128, q_lens=[50, 7], ctx_lens=[90, 300], scale=0.08)
+    c = make_prefill_case(name=f"rowdec-d{d}", seed=32, dtype="bf16", num_q_heads=16, num_kv_heads=4,
+                          head_dim=d, q_lens=[50, 7], ctx_lens=[90, 300], scale=0.08)
     g, out, ref = _run(c)
     assert_close(out, ref, "bf16", c.name)
     for b, row in [(0, 0), (0, 49), (1, 6)]:
