@@ -271,7 +271,7 @@ pa_status pa_decode_merge(void* out, const int32_t* seq_lens, int32_t num_seqs,
  *   scale            softmax scale, positive and finite.
  *
  * Rows owned by no sequence are left untouched.  head_dim must be 64 or 128;
- * the q-head group (num_q_heads / num_kv_heads) must be 1, 2, 4 or 8.
+ * the q-head group (num_q_heads / num_kv_heads) at most 128.
  */
 pa_status pa_prefill_paged(void* out, const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_tables, const int32_t* ctx_lens,

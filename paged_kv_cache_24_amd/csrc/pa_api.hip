@@ -450,7 +450,7 @@ static pa_status prefill_common(void* out, const void* q, const void* k_cache, c
         (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE > INT32_MAX)
         return PA_ERR_SHAPE;
     const int32_t group = num_q_heads / num_kv_heads;
-    if (group != 1 && group != 2 && group != 4 && group != 8) return PA_ERR_UNSUPPORTED;
+    if (group > 128) return PA_ERR_UNSUPPORTED;   // more q heads per kv head than a workgroup's rows
     if (num_seqs == 0 || num_tokens == 0 || max_q_len == 0) return PA_OK;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !ctx_lens || !query_start_loc)
         return PA_ERR_NULL_PTR;

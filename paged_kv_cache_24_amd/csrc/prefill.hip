@@ -12,12 +12,17 @@
 //  * prefill16_kernel (fp16 / bf16 cache): 32x32x16 matrix-core products,
 //    K/V tiles copied from HBM straight into LDS, S(t+1) = K Q^T overlapped
 //    with the softmax of tile t; described at the kernel.
-//  * prefill_kernel<.., F8 = true> (FP8 cache): 16x16x32 products over tiles
-//    that are widened to 16 bits while they are staged, as follows.
+//  * prefill_kernel<.., F8, D> (FP8 cache, and the 16-bit cache at head_dim
+//    64): 16x16x32 products over tiles staged through registers (FP8 codes
+//    widened to 16 bits on the way), as follows.
+//
+// Both take the q-head group G at run time: a workgroup's rows are floor(R/G)
+// positions times the G q heads that share the kv head (R = 128 or 256 rows),
+// so every K/V tile is staged in LDS once for all of them; when G does not
+// divide R the last R mod G rows are idle (no q, no store).
 //
 // prefill_kernel.  One workgroup (8 waves) owns 128 query rows of one
-// (sequence, kv head): 128/G positions times the G q heads that share the kv
-// head, so every K/V tile is staged in LDS once for all of them.  Each wave
+// (sequence, kv head).  Each wave
 // owns 16 rows (~128 VGPRs, four waves per SIMD).  For each 64-key tile:
 //   S^T[key][row] = K[key][:] . Q[row][:]     (MFMA 16x16x32: A = K from LDS,
 //                                              B = Q kept in registers)
@@ -208,10 +213,11 @@ __device__ __forceinline__ bool prefill_item(const PrefillArgs& a, int P, int64_
 
 static_assert(kRows / 16 == kSearchWaves, "the work-order search takes one candidate per wave");
 
-template <int DT, int G, bool F8, int D>
+template <int DT, bool F8, int D>
 __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     static_assert(D == 64 || D == 128, "head_dim 64 or 128");
-    constexpr int P = kRows / G;    // positions per workgroup
+    const int G = a.group;          // q heads per kv head, 1 .. kRows
+    const int P = kRows / G;        // positions per workgroup; rows P G .. kRows-1 idle
     constexpr int KR = D + 8;       // LDS K row stride (elements): rows 4 banks apart
     constexpr int VR = D + 16;      // LDS V row stride (elements): rows 8 banks apart
     constexpr int KK = D / 32;      // 32-element steps of QK^T
@@ -256,10 +262,11 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     // ---- this lane's query row and its Q^T fragments
     uint4 qf[KK];
     const int rho = wave * 16 + lr;
+    const bool row_live = rho < P * G;   // a row of this workgroup's positions
     const int qpos = ctx + pos0 + rho / G;
     {
         const int pos = pos0 + rho / G;
-        const bool ok = pos < L;
+        const bool ok = row_live && pos < L;
         const uint16_t* src = static_cast<const uint16_t*>(a.q) +
                               ((row0 + (ok ? pos : 0)) * a.num_q_heads + g * G + rho % G) * D + 8 * lg;
 #pragma unroll
@@ -528,7 +535,7 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     const float l = xor32_sum(xor16_sum(lsum));
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int pos = pos0 + rho / G;
-    if (pos >= L) return;
+    if (!row_live || pos >= L) return;
     uint16_t* dst = static_cast<uint16_t*>(a.out) +
                     ((row0 + pos) * a.num_q_heads + g * G + rho % G) * D + 4 * lg;
 #pragma unroll
@@ -611,9 +618,10 @@ constexpr int kRows16 = 32 * kW16;      // query rows per workgroup
 constexpr int kQkAhead = 6;             // K fragment reads in flight ahead of the products
 constexpr int kPvAhead = 4;             // products whose V fragments are read ahead
 
-template <int DT, int G>
+template <int DT>
 __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) {
-    constexpr int P = kRows16 / G;  // positions per workgroup
+    const int G = a.group;          // q heads per kv head, 1 .. kRows16
+    const int P = kRows16 / G;      // positions per workgroup; rows P G .. kRows16-1 idle
     // separate arrays so that the compiler can tell the in-flight copies from
     // the buffers being read
     __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[kTileElems];
@@ -667,10 +675,11 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
     // ---- Q^T fragments: row rho, elements 16 kk + 8 h .. +7
     uint4 qf[8];
     const int rho = wave * 32 + lr;
+    const bool row_live = rho < P * G;   // a row of this workgroup's positions
     const int qpos = ctx + pos0 + rho / G;
     {
         const int pos = pos0 + rho / G;
-        const bool ok = pos < L;
+        const bool ok = row_live && pos < L;
         const uint16_t* src = static_cast<const uint16_t*>(a.q) +
                               ((row0 + (ok ? pos : 0)) * a.num_q_heads + g * G + rho % G) * kPD + 8 * h;
 #pragma unroll
@@ -986,7 +995,7 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
     const float l = xor32_sum(lsum0 + lsum1);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int pos = pos0 + rho / G;
-    if (pos >= L) return;
+    if (!row_live || pos >= L) return;
     uint16_t* dst = static_cast<uint16_t*>(a.out) +
                     ((row0 + pos) * a.num_q_heads + g * G + rho % G) * kPD + 4 * h;
 #pragma unroll
@@ -1002,12 +1011,7 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
 
 template <int DT, bool F8, int D>
 static void launch_prefill_g(const PrefillArgs& a, hipStream_t s, dim3 grid) {
-    switch (a.group) {
-        case 1: hipLaunchKernelGGL((prefill_kernel<DT, 1, F8, D>), grid, dim3(512), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((prefill_kernel<DT, 2, F8, D>), grid, dim3(512), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((prefill_kernel<DT, 4, F8, D>), grid, dim3(512), 0, s, a); break;
-        default: hipLaunchKernelGGL((prefill_kernel<DT, 8, F8, D>), grid, dim3(512), 0, s, a); break;
-    }
+    hipLaunchKernelGGL((prefill_kernel<DT, F8, D>), grid, dim3(512), 0, s, a);
 }
 
 // the 16x16x32 kernel: every FP8 prefill, and 16-bit prefill at head_dim 64
@@ -1035,12 +1039,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
 
 template <int DT>
 static void launch_prefill16_g(const PrefillArgs& a, hipStream_t s, dim3 grid) {
-    switch (a.group) {
-        case 1: hipLaunchKernelGGL((prefill16_kernel<DT, 1>), grid, dim3(64 * kW16), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((prefill16_kernel<DT, 2>), grid, dim3(64 * kW16), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((prefill16_kernel<DT, 4>), grid, dim3(64 * kW16), 0, s, a); break;
-        default: hipLaunchKernelGGL((prefill16_kernel<DT, 8>), grid, dim3(64 * kW16), 0, s, a); break;
-    }
+    hipLaunchKernelGGL((prefill16_kernel<DT>), grid, dim3(64 * kW16), 0, s, a);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {

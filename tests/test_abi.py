@@ -155,7 +155,7 @@ def test_prefill_rejects(lib):
     assert _prefill(lib, cl=None) == NULL
     assert _prefill(lib, d=96) == UNSUP
     assert _prefill(lib, d=64, bs=8) == UNSUP
-    assert _prefill(lib, hq=24, hkv=8) == UNSUP          # 3 q heads per kv head
+    assert _prefill(lib, hq=258, hkv=2) == UNSUP         # 129 q heads per kv head
     assert _prefill(lib, hq=30, hkv=8) == SHAPE
     assert _prefill(lib, t=-1) == SHAPE
     assert _prefill(lib, mq=-1) == SHAPE
@@ -261,7 +261,7 @@ def test_prefill_fp8_rejects(lib):
     assert call(vs=None) == NULL
     assert call(qsl=None) == NULL
     assert call(d=96) == UNSUP
-    assert call(hq=24, hkv=8) == UNSUP
+    assert call(hq=258, hkv=2) == UNSUP
     assert call(scale=0.0) == SHAPE
     assert call(vs=FAKE + 4) == ALIGN
     assert call(t=0, ks=None) == PA_OK

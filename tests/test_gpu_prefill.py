@@ -35,7 +35,8 @@ def _run(c):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (8, 2), (16, 2)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (8, 2), (16, 2), (12, 4), (10, 2), (12, 2),
+                                    (14, 2), (16, 1)])
 def test_prefill_shapes(dtype, hq, hkv, d):
     q_lens = [0, 1, 17, 64, 130, 5, 33]
     ctx = [3, 0, 40, 0, 100, 16, 250]
