@@ -184,7 +184,9 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  *                 (may be NULL when that size is 0), 16-byte aligned.
  *
  * q head h reads kv head h / (num_q_heads / num_kv_heads); num_q_heads must be
- * a multiple of num_kv_heads, with at most 16 q heads per kv head.  Slots past
+ * a multiple of num_kv_heads, with at most 128 q heads per kv head (a wave
+ * carries up to 16 of them; more run as several chunks, each reading the kv
+ * head's K/V).  Slots past
  * seq_lens[b] inside the last block may hold any bits, NaN included; they
  * never reach the output.
  */

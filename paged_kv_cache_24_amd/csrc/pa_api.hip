@@ -29,6 +29,10 @@ int32_t heads_per_wave(int32_t group) {
     return 8;
 }
 
+// most q heads per kv head: decode splits them into chunks of 8 or 16 heads
+// per wave, prefill's workgroups hold at least one position of all of them
+constexpr int32_t kMaxGroup = 128;
+
 // decode runs on matrix cores when 3+ q heads share a kv head at head_dim 128
 bool uses_gqa_kernel(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
     return head_dim == 128 && num_kv_heads > 0 && num_q_heads / num_kv_heads >= 3;
@@ -79,7 +83,7 @@ pa_status check_decode(const void* out, const void* q, const void* k_cache, cons
     if (!supported_dtype(dtype) || block_size != PA_BLOCK_SIZE || (head_dim != 64 && head_dim != 128))
         return PA_ERR_UNSUPPORTED;
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
-        num_blocks <= 0 || num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 16 ||
+        num_blocks <= 0 || num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > kMaxGroup ||
         partition_tokens < 0 || partition_tokens % PA_BLOCK_SIZE != 0 || !(scale > 0.f) || !isfinite(scale) ||
         (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE > INT32_MAX)
         return PA_ERR_SHAPE;
@@ -308,7 +312,7 @@ pa_status pa_decode_merge(void* out, const int32_t* seq_lens, int32_t num_seqs,
     if (!supported_dtype(dtype) || block_size != PA_BLOCK_SIZE || (head_dim != 64 && head_dim != 128))
         return PA_ERR_UNSUPPORTED;
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
-        num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 16 ||
+        num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > kMaxGroup ||
         partition_tokens < 0 || partition_tokens % PA_BLOCK_SIZE != 0)
         return PA_ERR_SHAPE;
     if (num_seqs == 0) return PA_OK;
@@ -450,7 +454,7 @@ static pa_status prefill_common(void* out, const void* q, const void* k_cache, c
         (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE > INT32_MAX)
         return PA_ERR_SHAPE;
     const int32_t group = num_q_heads / num_kv_heads;
-    if (group > 128) return PA_ERR_UNSUPPORTED;   // more q heads per kv head than a workgroup's rows
+    if (group > kMaxGroup) return PA_ERR_UNSUPPORTED;   // more q heads per kv head than a workgroup's rows
     if (num_seqs == 0 || num_tokens == 0 || max_q_len == 0) return PA_OK;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !ctx_lens || !query_start_loc)
         return PA_ERR_NULL_PTR;

@@ -104,7 +104,7 @@ def test_decode_rejects(lib, fn):
     assert _decode(lib, fn, dt=9) == UNSUP
     assert _decode(lib, fn, flags=2) == UNSUP             # unknown flag bit
     assert _decode(lib, fn, hq=6, hkv=4) == SHAPE        # not a multiple
-    assert _decode(lib, fn, hq=34, hkv=2) == SHAPE       # 17 q heads per kv head
+    assert _decode(lib, fn, hq=258, hkv=2) == SHAPE      # 129 q heads per kv head
     assert _decode(lib, fn, part=24) == SHAPE            # not a multiple of 16
     assert _decode(lib, fn, part=-16) == SHAPE
     assert _decode(lib, fn, scale=float("nan")) == SHAPE
@@ -239,7 +239,7 @@ def test_decode_fp8_rejects(lib, fn):
     assert call(d=80) == UNSUP
     assert call(dt=2) == UNSUP
     assert call(flags=4) == UNSUP
-    assert call(hq=34, hkv=2) == SHAPE
+    assert call(hq=258, hkv=2) == SHAPE
     assert call(scale=0.0) == SHAPE
     assert call(part=24) == SHAPE
     assert call(vs=FAKE + 4) == ALIGN

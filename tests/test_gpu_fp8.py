@@ -112,7 +112,8 @@ def test_fp8_decode_tiny():
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (6, 2), (8, 2), (16, 2), (16, 1)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (6, 2), (8, 2), (16, 2), (16, 1), (48, 2),
+                                    (71, 1)])
 def test_fp8_decode_shapes(dtype, d, hq, hkv):
     lens = [0, 1, 2, 15, 16, 17, 31, 33, 64, 100, 257, 300]
     c = make_decode_case(name=f"fp8-{dtype}-{d}-{hq}-{hkv}", seed=300 + hq + d, dtype=dtype,
