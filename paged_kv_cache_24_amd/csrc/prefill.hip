@@ -341,7 +341,7 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     // stage nothing.  Invalid rows stage zeros with k scale 0 and v scale 1, so
     // NaN bits in unused slots never reach the products.
     constexpr int TPR8 = D / 16;
-    const bool stage8 = tid < 64 * TPR8;   // uniform per wave
+    const bool stage8 = TPR8 == kSearchWaves || wave < TPR8;   // whole waves: 8 at D = 128, 4 at 64
     const int c8 = tid % TPR8;
     const int kr8 = (tid / TPR8) & 63;     // key row 0..63 (a copy for the idle waves)
     const int q8 = uniform(kr8 >> 4);
