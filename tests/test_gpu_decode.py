@@ -66,6 +66,16 @@ def test_decode_shapes(dtype, d, hq, hkv):
     _check_case(c, partitions=(0, 16, 48, 256, 320))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_group_128(d):
+    """One kv head for 128 q heads: 8 (matrix-core path) or 16 (vector path) head chunks."""
+    lens = [1, 16, 17, 90]
+    c = make_decode_case(name=f"group128-{d}", seed=600 + d, dtype="f16", num_q_heads=128,
+                         num_kv_heads=1, head_dim=d, seq_lens=lens, num_blocks=16,
+                         max_blocks_per_seq=8, scale=1 / math.sqrt(d), write_last=True)
+    _check_case(c, partitions=(0, 32))
+
+
 def test_decode_llama_reduced():
     c = decode_llama2_7b_layer(batch=6, max_len=1024, num_heads=32)
     _check_case(c, partitions=(0, 256, 1024))

@@ -57,6 +57,18 @@ def test_prefill_head_dim_64_long(dtype):
     assert_close(out, ref, dtype, c.name)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(64, 2), (128, 1)])
+def test_prefill_large_groups(hq, hkv, d):
+    """32 and 128 q heads per kv head: a workgroup then holds 8 / 4 (or 2 / 1)
+    positions, the work order still covers every row."""
+    c = make_prefill_case(name=f"prefill-group-{hq // hkv}-d{d}", seed=91 + hq + d, dtype="bf16",
+                          num_q_heads=hq, num_kv_heads=hkv, head_dim=d, q_lens=[9, 0, 4, 1],
+                          ctx_lens=[30, 5, 0, 70], scale=1 / math.sqrt(d), extra_blocks=2)
+    _, out, ref = _run(c)
+    assert_close(out, ref, "bf16", c.name)
+
+
 def test_prefill_chunked_reduced():
     c = prefill_chunked(batch=4, new_tokens=600, max_ctx=700)
     _, out, ref = _run(c)
