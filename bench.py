@@ -116,9 +116,9 @@ class DecodeRun:
         self.lens = _i(case.seq_lens)
         self.out = torch.empty_like(self.q)
         self.part = partition_tokens or pa.pa_decode_default_partition(
-            case.num_q_heads, case.num_kv_heads, case.head_dim, case.max_blocks_per_seq)
+            case.num_q_heads, case.num_kv_heads, case.head_dim, 16, case.max_blocks_per_seq)
         need = pa.pa_decode_workspace_size(case.num_seqs, case.num_q_heads, case.num_kv_heads,
-                                           case.head_dim, case.max_blocks_per_seq, self.part)
+                                           case.head_dim, 16, case.max_blocks_per_seq, self.part)
         self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
         self.has_write = len(case.slot_mapping) > 0
         # the streaming hint is a promise that no physical block is read twice in the
@@ -577,7 +577,7 @@ def _secondary_multi(steps, warmup, nq=4):
     # the library's own default partition for several queries (the size for
     # partition 0 of num_seqs * nq single-query sequences always suffices)
     need = pa.pa_decode_workspace_size(c.num_seqs * nq, c.num_q_heads, c.num_kv_heads, c.head_dim,
-                                       c.max_blocks_per_seq, 0)
+                                       16, c.max_blocks_per_seq, 0)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     if run.has_write:
         pa.pa_reshape_and_cache(run.key, run.value, run.kc, run.vc, run.slots)

@@ -26,8 +26,11 @@
  * KV cache layout.  k_cache and v_cache are two separate tensors, each
  * [num_blocks][block_size][num_kv_heads][head_dim].  Token slot
  * s = physical_block * block_size + offset addresses row s of the
- * [num_blocks * block_size][num_kv_heads][head_dim] view.  block_size must be
- * 16, head_dim 64 or 128.
+ * [num_blocks * block_size][num_kv_heads][head_dim] view.  block_size is 16
+ * or 32, the two usual block sizes ("vLLM 在 CANN 上的推理优化", section
+ * "vLLM 的 PagedAttention 数据结构", the PagedKVCache sketch); the FP8 calls
+ * take 16 only.  head_dim is 64 or 128.  With 32-token blocks the pool holds
+ * at most 2^30 blocks.
  *
  * Streams.  Work is enqueued on `stream` (0 = the null stream).  No call
  * synchronises, reads device memory from the host or allocates, so every call
@@ -140,24 +143,25 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pair
 /*
  * pa_decode_default_partition -- the split-KV partition length, in tokens, that
  * pa_decode uses when given partition_tokens == 0 (a power of two >= 256).  It
- * depends only on host-known sizes: about max_blocks_per_seq * 16 / 8, capped
- * at 512 tokens when at most 2 q heads share a kv head and at 2048 otherwise.
- * A partition covering max_blocks_per_seq * 16 tokens or more means a single
- * pass with no merge.  The online-softmax merge of partitions is exact
+ * depends only on host-known sizes: about max_blocks_per_seq * block_size / 8,
+ * capped at 512 tokens when at most 2 q heads share a kv head and at 2048
+ * otherwise.  A partition covering max_blocks_per_seq * block_size tokens or
+ * more means a single pass with no merge.  The online-softmax merge of partitions is exact
  * ("vLLM-Ascend 原理", §四 "ATB 算子": softmax statistics kept online), so the
  * choice changes only float32 rounding.
  */
 int32_t pa_decode_default_partition(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                    int32_t max_blocks_per_seq);
+                                    int32_t block_size, int32_t max_blocks_per_seq);
 
 /*
  * pa_decode_workspace_size -- bytes of float32 partial results pa_decode needs
  * for this shape and partition length (0 = default).  0 when every sequence
  * fits one partition.  Layout (internal to the library): per (sequence,
  * q head, partition) a running max, a running sum and head_dim accumulators.
+ * Also 0 for a block_size other than 16 or 32 or other invalid sizes.
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                int32_t head_dim, int32_t max_blocks_per_seq,
+                                int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                 int32_t partition_tokens);
 
 /*

@@ -48,8 +48,8 @@ _SIGS = {
     "pa_status_string": (ctypes.c_char_p, [_i32]),
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i32, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i32, _vp]),
-    "pa_decode_default_partition": (_i32, [_i32, _i32, _i32, _i32]),
-    "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_default_partition": (_i32, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
                          _f32, _i32, _i32, _u32, _vp, _sz, _vp]),
     "pa_decode_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -161,15 +161,15 @@ def pa_copy_blocks(k_cache, v_cache, block_pairs, stream=None):
 
 
 def pa_decode_default_partition(num_q_heads: int, num_kv_heads: int, head_dim: int,
-                                max_blocks_per_seq: int) -> int:
-    return int(lib.pa_decode_default_partition(num_q_heads, num_kv_heads, head_dim,
+                                block_size: int, max_blocks_per_seq: int) -> int:
+    return int(lib.pa_decode_default_partition(num_q_heads, num_kv_heads, head_dim, block_size,
                                                max_blocks_per_seq))
 
 
-def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
-                             partition_tokens=0) -> int:
+def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                             max_blocks_per_seq, partition_tokens=0) -> int:
     return int(lib.pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                            max_blocks_per_seq, partition_tokens))
+                                            block_size, max_blocks_per_seq, partition_tokens))
 
 
 def _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens):
@@ -204,7 +204,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, partition
     see ``pa_decode_workspace_size``) is allocated with torch when not given.
     ``flags``: 0 or ``PA_DECODE_STREAM_KV`` (no block shared within the batch)."""
     nb, bs, hkv, d, b, hq, mb = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens)
-    need = pa_decode_workspace_size(b, hq, hkv, d, mb, partition_tokens)
+    need = pa_decode_workspace_size(b, hq, hkv, d, bs, mb, partition_tokens)
     ws, ws_bytes = _workspace(workspace, need, q.device)
     _check("pa_decode", lib.pa_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), b, hq,
@@ -231,7 +231,7 @@ def pa_decode_multi(out, q, k_cache, v_cache, block_tables, seq_lens, scale, par
     if block_tables.shape[0] != b or seq_lens.shape[0] != b:
         raise ValueError("block_tables and seq_lens need one row per sequence")
     mb = block_tables.shape[1]
-    need = pa_decode_workspace_size(b * nq, hq, hkv, d, mb, partition_tokens)
+    need = pa_decode_workspace_size(b * nq, hq, hkv, d, bs, mb, partition_tokens)
     ws, ws_bytes = _workspace(workspace, need, q.device)
     _check("pa_decode_multi", lib.pa_decode_multi(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), b, nq,
@@ -243,7 +243,7 @@ def pa_decode_multi(out, q, k_cache, v_cache, block_tables, seq_lens, scale, par
 def pa_decode_partitions(out, q, k_cache, v_cache, block_tables, seq_lens, scale, workspace,
                          partition_tokens=0, stream=None, flags=0):
     nb, bs, hkv, d, b, hq, mb = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens)
-    need = pa_decode_workspace_size(b, hq, hkv, d, mb, partition_tokens)
+    need = pa_decode_workspace_size(b, hq, hkv, d, bs, mb, partition_tokens)
     ws, ws_bytes = _workspace(workspace, need, q.device)
     _check("pa_decode_partitions", lib.pa_decode_partitions(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), b, hq,
@@ -252,14 +252,15 @@ def pa_decode_partitions(out, q, k_cache, v_cache, block_tables, seq_lens, scale
 
 
 def pa_decode_merge(out, seq_lens, num_kv_heads, max_blocks_per_seq, workspace,
-                    partition_tokens=0, stream=None):
+                    partition_tokens=0, stream=None, block_size=BLOCK_SIZE):
     _need(out, "out", ndim=3)
     _need(seq_lens, "seq_lens", torch.int32, 1)
     b, hq, d = out.shape
-    need = pa_decode_workspace_size(b, hq, num_kv_heads, d, max_blocks_per_seq, partition_tokens)
+    need = pa_decode_workspace_size(b, hq, num_kv_heads, d, block_size, max_blocks_per_seq,
+                                    partition_tokens)
     ws, ws_bytes = _workspace(workspace, need, out.device)
     _check("pa_decode_merge", lib.pa_decode_merge(
-        _ptr(out), _ptr(seq_lens), b, hq, num_kv_heads, d, BLOCK_SIZE, max_blocks_per_seq,
+        _ptr(out), _ptr(seq_lens), b, hq, num_kv_heads, d, block_size, max_blocks_per_seq,
         _kv_dtype(out), partition_tokens, _ptr(ws), ws_bytes, _stream(stream)))
 
 
@@ -351,7 +352,7 @@ def pa_decode_fp8(out, q, k_cache, v_cache, k_scales, v_scales, block_tables, se
     the other arguments as for ``pa_decode``."""
     nb, bs, hkv, d, b, hq, mb = _decode_fp8_args(out, q, k_cache, v_cache, k_scales, v_scales,
                                                  block_tables, seq_lens)
-    need = pa_decode_workspace_size(b, hq, hkv, d, mb, partition_tokens)
+    need = pa_decode_workspace_size(b, hq, hkv, d, bs, mb, partition_tokens)
     ws, ws_bytes = _workspace(workspace, need, q.device)
     _check("pa_decode_fp8", lib.pa_decode_fp8(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),
@@ -364,7 +365,7 @@ def pa_decode_partitions_fp8(out, q, k_cache, v_cache, k_scales, v_scales, block
                              scale, workspace, partition_tokens=0, stream=None, flags=0):
     nb, bs, hkv, d, b, hq, mb = _decode_fp8_args(out, q, k_cache, v_cache, k_scales, v_scales,
                                                  block_tables, seq_lens)
-    need = pa_decode_workspace_size(b, hq, hkv, d, mb, partition_tokens)
+    need = pa_decode_workspace_size(b, hq, hkv, d, bs, mb, partition_tokens)
     ws, ws_bytes = _workspace(workspace, need, q.device)
     _check("pa_decode_partitions_fp8", lib.pa_decode_partitions_fp8(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales),

@@ -8,8 +8,18 @@
 
 namespace pa {
 
-constexpr int kBlockSize = 16;   // tokens per KV block
+constexpr int kBlockSize = 16;   // tokens per KV block as the kernels walk the cache
 constexpr int kWave = 64;        // CDNA wavefront width
+
+// The kernels walk the cache in 16-token blocks.  A cache of 32-token blocks
+// ([NB][32][Hkv][D]) is the same memory as [2 NB][16][Hkv][D]: 16-token block
+// j of a sequence is half j % 2 of its table entry j / 2.  `shift` is
+// log2(block_size / 16).  A negative entry stays negative, and an entry at or
+// above 2^(31 - shift) comes out negative, so the callers' range check on the
+// result (against num_blocks << shift) still rejects every bad entry.
+__device__ __forceinline__ int sub_block(int entry, int j, int shift) {
+    return entry < 0 ? -1 : (int)(((uint32_t)entry << shift) | ((uint32_t)j & ((1u << shift) - 1u)));
+}
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

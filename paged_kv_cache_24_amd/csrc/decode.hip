@@ -103,11 +103,11 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
     const int64_t lane_off = (int64_t)g * D + 8 * c + (int64_t)r * row_stride;
     const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache) + lane_off;
     const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + lane_off;
-    const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
+    const int32_t* table = a.block_tables + (int64_t)b * a.table_stride;
     const float cs = a.scale_log2;
 
     auto load = [&](int j, uint4 (&kr)[TPL], uint4 (&vr)[TPL]) -> bool {
-        const int pb = table[j];
+        const int pb = sub_block(table[j >> a.block_shift], j, a.block_shift);
         const bool ok = pb >= 0 && (int64_t)pb < a.num_blocks;
         const int64_t off = (int64_t)(ok ? pb : 0) * kBlockSize * row_stride;
 #pragma unroll
@@ -361,13 +361,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
                             (int64_t)tk * row_stride;
     const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + (int64_t)g * D + 8 * lr +
                             (int64_t)lg * row_stride;
-    const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
+    const int32_t* table = a.block_tables + (int64_t)b * a.table_stride;
     const float cs = a.scale_log2;
     // transposed-read address of this lane: row 4*(lr/4) + lg, column 4*(lr%4) (+16 per tile)
     const uint16_t* vtr = vt + (4 * (lr >> 2) + lg) * kVRow + 4 * (lr & 3);
 
     auto load = [&](int j, uint4 (&kr)[4], uint4 (&vr)[4]) -> bool {
-        const int pb = table[j];
+        const int pb = sub_block(table[j >> a.block_shift], j, a.block_shift);
         const bool ok = pb >= 0 && (int64_t)pb < a.num_blocks;
         const int64_t off = (int64_t)(ok ? pb : 0) * kBlockSize * row_stride;
 #pragma unroll

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void decode_fp8_partition_kernel(DecodeArgs a)
     const float* ksb = a.k_scales + (int64_t)g * kBlockSize + r * TPL;
     const float* vsb = a.v_scales + (int64_t)g * kBlockSize + r * TPL;
     const int64_t scale_block_stride = (int64_t)a.num_kv_heads * kBlockSize;
-    const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
+    const int32_t* table = a.block_tables + (int64_t)b * a.table_stride;   // FP8 caches: 16-token blocks
     const float cs = a.scale_log2;
 
     struct Buf {
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     const bool k_half = lr < 8;
     const float* scb = (k_half ? a.k_scales : a.v_scales) + (int64_t)g * kBlockSize + 4 * lg;
     const int64_t scale_block_stride = (int64_t)a.num_kv_heads * kBlockSize;
-    const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
+    const int32_t* table = a.block_tables + (int64_t)b * a.table_stride;   // FP8 caches: 16-token blocks
     const float cs = a.scale_log2;
     const int tr_off = (4 * lg + (lr >> 2)) * kVRowF8 + 4 * (lr & 3);
 

@@ -54,7 +54,7 @@ struct DecodeArgs {
     const void* q;
     const void* k_cache;
     const void* v_cache;
-    const int32_t* block_tables;
+    const int32_t* block_tables;   // [num_seqs][table_stride]
     const int32_t* seq_lens;
     float* ws_acc;           // [B][Hq][num_parts][D]
     float2* ws_ml;           // [B][Hq][num_parts] = (max, sum), log2 domain
@@ -66,8 +66,10 @@ struct DecodeArgs {
     int32_t heads_per_wave;  // q heads one wave carries (1, 2, 4, 8; 16 with gqa_mfma)
     int32_t head_chunks;     // ceil(group / heads_per_wave)
     int32_t head_dim;
-    int32_t max_blocks_per_seq;
-    int64_t num_blocks;
+    int32_t max_blocks_per_seq;   // 16-token blocks per sequence (table_stride << block_shift)
+    int64_t num_blocks;           // 16-token blocks in the pool
+    int32_t table_stride;         // entries per block-table row
+    int32_t block_shift;          // log2(cache block size / 16): 0 or 1 (sub_block)
     int32_t part_blocks;     // partition length in blocks
     int32_t num_parts;       // partitions per sequence the grid covers
     float scale_log2;        // softmax scale times log2(e)
@@ -99,8 +101,10 @@ struct PrefillArgs {
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t group;
-    int32_t max_blocks_per_seq;
-    int64_t num_blocks;
+    int32_t max_blocks_per_seq;   // 16-token blocks per sequence (table_stride << block_shift)
+    int64_t num_blocks;           // 16-token blocks in the pool
+    int32_t table_stride;         // entries per block-table row
+    int32_t block_shift;          // log2(cache block size / 16): 0 or 1 (sub_block)
     float scale_log2;
     int32_t dtype;
     int32_t head_dim;        // 64 or 128

@@ -19,6 +19,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool supported_dtype(pa_dtype d) { return d == PA_F16 || d == PA_BF16; }
 
+// log2(block_size / 16) for the block sizes the 16-bit calls take (16, 32), or
+// -1.  The kernels walk every cache in 16-token blocks; a 32-token block is two
+// of them (sub_block in common.h).  The FP8 calls take 16 only: their scales
+// are laid out per 16-token block.
+int32_t block_shift(int32_t block_size) {
+    return block_size == 16 ? 0 : block_size == 32 ? 1 : -1;
+}
+
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
 // heads one decode wave carries: the smallest of 1, 2, 4, 8 covering the group
@@ -38,15 +46,16 @@ bool uses_gqa_kernel(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim
     return head_dim == 128 && num_kv_heads > 0 && num_q_heads / num_kv_heads >= 3;
 }
 
+// max_blocks16: 16-token blocks per sequence
 int32_t default_partition(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                          int32_t max_blocks_per_seq) {
+                          int32_t max_blocks16) {
     // About eight partitions for the longest sequence the tables allow, within
     // [256, cap] tokens.  Measured on MI355X: the vector-ALU kernel (group <= 2)
     // is fastest at 512-token partitions (more items even out the length mix),
     // the matrix-core kernel at 1024-2048 (it keeps fewer waves resident, so
     // longer items hide its start-up latency better).
     const int32_t cap = uses_gqa_kernel(num_q_heads, num_kv_heads, head_dim) ? 2048 : 512;
-    const int64_t want = (int64_t)max_blocks_per_seq * 16 / 8;
+    const int64_t want = (int64_t)max_blocks16 * 16 / 8;
     int32_t p = 256;
     while (p < cap && p < want) p <<= 1;
     return p;
@@ -58,14 +67,15 @@ struct DecodeShape {
     size_t ws_bytes;
 };
 
+// max_blocks16: 16-token blocks per sequence
 DecodeShape decode_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                         int32_t head_dim, int32_t max_blocks_per_seq, int32_t partition_tokens) {
+                         int32_t head_dim, int32_t max_blocks16, int32_t partition_tokens) {
     DecodeShape s;
     s.part_tokens = partition_tokens > 0
                         ? partition_tokens
-                        : default_partition(num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq);
+                        : default_partition(num_q_heads, num_kv_heads, head_dim, max_blocks16);
     const int32_t part_blocks = s.part_tokens / 16;
-    s.num_parts = max_blocks_per_seq <= part_blocks ? 1 : ceil_div(max_blocks_per_seq, part_blocks);
+    s.num_parts = max_blocks16 <= part_blocks ? 1 : ceil_div(max_blocks16, part_blocks);
     if (s.num_parts <= 1) {
         s.ws_bytes = 0;
     } else {
@@ -80,12 +90,13 @@ pa_status check_decode(const void* out, const void* q, const void* k_cache, cons
                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
                        float scale, pa_dtype dtype, int32_t partition_tokens) {
-    if (!supported_dtype(dtype) || block_size != PA_BLOCK_SIZE || (head_dim != 64 && head_dim != 128))
+    const int32_t sh = block_shift(block_size);
+    if (!supported_dtype(dtype) || sh < 0 || (head_dim != 64 && head_dim != 128))
         return PA_ERR_UNSUPPORTED;
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
         num_blocks <= 0 || num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > kMaxGroup ||
-        partition_tokens < 0 || partition_tokens % PA_BLOCK_SIZE != 0 || !(scale > 0.f) || !isfinite(scale) ||
-        (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE > INT32_MAX)
+        partition_tokens < 0 || partition_tokens % 16 != 0 || !(scale > 0.f) || !isfinite(scale) ||
+        (int64_t)max_blocks_per_seq * block_size > INT32_MAX || num_blocks > (INT64_C(1) << (31 - sh)))
         return PA_ERR_SHAPE;
     if (num_seqs == 0) return PA_OK;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens) return PA_ERR_NULL_PTR;
@@ -97,9 +108,10 @@ pa_status check_decode(const void* out, const void* q, const void* k_cache, cons
 pa::DecodeArgs decode_args(void* out, const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                           int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
-                           pa_dtype dtype, const DecodeShape& shape, void* workspace,
+                           int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                           float scale, pa_dtype dtype, const DecodeShape& shape, void* workspace,
                            uint32_t flags, int32_t q_per_seq = 1) {
+    const int32_t sh = block_shift(block_size);
     pa::DecodeArgs a;
     a.out = out;
     a.q = q;
@@ -120,9 +132,11 @@ pa::DecodeArgs decode_args(void* out, const void* q, const void* k_cache, const 
     a.v_scales = nullptr;
     a.head_chunks = ceil_div(a.cols, a.heads_per_wave);
     a.head_dim = head_dim;
-    a.max_blocks_per_seq = max_blocks_per_seq;
-    a.num_blocks = num_blocks;
-    a.part_blocks = shape.part_tokens / PA_BLOCK_SIZE;
+    a.max_blocks_per_seq = max_blocks_per_seq << sh;
+    a.num_blocks = num_blocks << sh;
+    a.table_stride = max_blocks_per_seq;
+    a.block_shift = sh;
+    a.part_blocks = shape.part_tokens / 16;
     a.num_parts = shape.num_parts;
     a.scale_log2 = scale * kLog2e;
     a.dtype = dtype == PA_F16 ? pa::kF16 : pa::kBF16;
@@ -168,9 +182,10 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
                                const int64_t* slot_mapping, int64_t num_tokens,
                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                int64_t num_blocks, pa_dtype dtype, hipStream_t stream) {
-    if (!supported_dtype(dtype) || block_size != PA_BLOCK_SIZE || (head_dim != 64 && head_dim != 128))
+    if (!supported_dtype(dtype) || block_shift(block_size) < 0 || (head_dim != 64 && head_dim != 128))
         return PA_ERR_UNSUPPORTED;
-    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0 || num_blocks > INT64_MAX / block_size)
+        return PA_ERR_SHAPE;
     if (num_tokens == 0) return PA_OK;
     if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL_PTR;
     if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -182,7 +197,7 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
     a.v_cache = v_cache;
     a.slot_mapping = slot_mapping;
     a.num_tokens = num_tokens;
-    a.num_slots = num_blocks * PA_BLOCK_SIZE;
+    a.num_slots = num_blocks * block_size;   // a slot's row sits at the same place for any block_size
     a.row_vecs = num_kv_heads * head_dim / 8;
     return pa::launch_reshape_and_cache(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -190,7 +205,7 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs, int64_t num_pairs,
                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                          int64_t num_blocks, pa_dtype dtype, hipStream_t stream) {
-    if (!supported_dtype(dtype) || block_size != PA_BLOCK_SIZE || (head_dim != 64 && head_dim != 128))
+    if (!supported_dtype(dtype) || block_shift(block_size) < 0 || (head_dim != 64 && head_dim != 128))
         return PA_ERR_UNSUPPORTED;
     if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
     if (num_pairs == 0) return PA_OK;
@@ -202,7 +217,7 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pair
     a.block_pairs = block_pairs;
     a.num_pairs = num_pairs;
     a.num_blocks = num_blocks;
-    a.block_vecs = (int64_t)PA_BLOCK_SIZE * num_kv_heads * head_dim / 8;
+    a.block_vecs = (int64_t)block_size * num_kv_heads * head_dim / 8;
     a.wgs_per_pair = (a.block_vecs + 1023) / 1024;
     return pa::launch_copy_blocks(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -266,18 +281,23 @@ pa_status pa_copy_blocks_fp8(void* k_cache, void* v_cache, float* k_scales, floa
 }
 
 int32_t pa_decode_default_partition(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                    int32_t max_blocks_per_seq) {
-    if (num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0) return 256;
-    return default_partition(num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq);
+                                    int32_t block_size, int32_t max_blocks_per_seq) {
+    const int32_t sh = block_shift(block_size);
+    if (num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 || sh < 0 ||
+        max_blocks_per_seq > (INT32_MAX >> sh))
+        return 256;
+    return default_partition(num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq << sh);
 }
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                int32_t head_dim, int32_t max_blocks_per_seq,
+                                int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                 int32_t partition_tokens) {
-    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-        max_blocks_per_seq <= 0 || partition_tokens < 0 || partition_tokens % PA_BLOCK_SIZE)
+    const int32_t sh = block_shift(block_size);
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || sh < 0 ||
+        max_blocks_per_seq <= 0 || max_blocks_per_seq > (INT32_MAX >> sh) || partition_tokens < 0 ||
+        partition_tokens % 16)
         return 0;
-    return decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+    return decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq << sh,
                         partition_tokens).ws_bytes;
 }
 
@@ -294,11 +314,12 @@ pa_status pa_decode_partitions(void* out, const void* q, const void* k_cache, co
                                 max_blocks_per_seq, num_blocks, scale, dtype, partition_tokens);
     if (st != PA_OK || num_seqs == 0) return st;
     const DecodeShape shape = decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                           max_blocks_per_seq, partition_tokens);
+                                           max_blocks_per_seq << block_shift(block_size),
+                                           partition_tokens);
     st = check_workspace(shape, workspace, workspace_bytes);
     if (st != PA_OK) return st;
     const pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, seq_lens,
-                                         num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                         num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                          max_blocks_per_seq, num_blocks, scale, dtype, shape,
                                          workspace, flags);
     return pa::launch_decode_partitions(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -309,22 +330,24 @@ pa_status pa_decode_merge(void* out, const int32_t* seq_lens, int32_t num_seqs,
                           int32_t block_size, int32_t max_blocks_per_seq, pa_dtype dtype,
                           int32_t partition_tokens, const void* workspace, size_t workspace_bytes,
                           hipStream_t stream) {
-    if (!supported_dtype(dtype) || block_size != PA_BLOCK_SIZE || (head_dim != 64 && head_dim != 128))
+    const int32_t sh = block_shift(block_size);
+    if (!supported_dtype(dtype) || sh < 0 || (head_dim != 64 && head_dim != 128))
         return PA_ERR_UNSUPPORTED;
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
         num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > kMaxGroup ||
-        partition_tokens < 0 || partition_tokens % PA_BLOCK_SIZE != 0)
+        partition_tokens < 0 || partition_tokens % 16 != 0 ||
+        (int64_t)max_blocks_per_seq * block_size > INT32_MAX)
         return PA_ERR_SHAPE;
     if (num_seqs == 0) return PA_OK;
     if (!out || !seq_lens) return PA_ERR_NULL_PTR;
     if (!aligned16(out)) return PA_ERR_ALIGNMENT;
     const DecodeShape shape = decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                           max_blocks_per_seq, partition_tokens);
+                                           max_blocks_per_seq << sh, partition_tokens);
     const pa_status st = check_workspace(shape, workspace, workspace_bytes);
     if (st != PA_OK) return st;
     if (shape.num_parts <= 1) return PA_OK;
     const pa::DecodeArgs a = decode_args(out, nullptr, nullptr, nullptr, nullptr, seq_lens,
-                                         num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                         num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                          max_blocks_per_seq, 1, 1.f, dtype, shape,
                                          const_cast<void*>(workspace), 0u);
     return pa::launch_decode_merge(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -340,6 +363,7 @@ pa_status pa_decode_partitions_fp8(void* out, const void* q, const void* k_cache
                                    int32_t partition_tokens, uint32_t flags, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream) {
     if (flags & ~PA_DECODE_STREAM_KV) return PA_ERR_UNSUPPORTED;
+    if (block_size != PA_BLOCK_SIZE) return PA_ERR_UNSUPPORTED;   // scales are per 16-token block
     pa_status st = check_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
                                 num_q_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, num_blocks, scale, dtype, partition_tokens);
@@ -351,8 +375,9 @@ pa_status pa_decode_partitions_fp8(void* out, const void* q, const void* k_cache
     st = check_workspace(shape, workspace, workspace_bytes);
     if (st != PA_OK) return st;
     pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
-                                   num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
-                                   num_blocks, scale, dtype, shape, workspace, flags);
+                                   num_q_heads, num_kv_heads, head_dim, block_size,
+                                   max_blocks_per_seq, num_blocks, scale, dtype, shape, workspace,
+                                   flags);
     if (!a.gqa_mfma && a.heads_per_wave > 4) {   // the FP8 vector kernel carries up to 4 heads
         a.heads_per_wave = 4;
         a.head_chunks = ceil_div(a.group, 4);
@@ -403,18 +428,19 @@ pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const v
     // query keeps the single-query default, so it stays identical to pa_decode); never
     // more partitions than the single-query default, so the workspace size
     // documented for it always suffices.
+    const int32_t mb16 = max_blocks_per_seq << block_shift(block_size);
     if (partition_tokens == 0 && q_per_seq > 1 && head_dim == 128 &&
         q_per_seq * (num_q_heads / num_kv_heads) >= 3)
         partition_tokens = std::min<int32_t>(
-            2 * default_partition(num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq), 2048);
+            2 * default_partition(num_q_heads, num_kv_heads, head_dim, mb16), 2048);
     // the partial states are per (sequence, query, q head): the workspace of
     // num_seqs * q_per_seq single-query sequences
     const DecodeShape shape = decode_shape(num_seqs * q_per_seq, num_q_heads, num_kv_heads,
-                                           head_dim, max_blocks_per_seq, partition_tokens);
+                                           head_dim, mb16, partition_tokens);
     st = check_workspace(shape, workspace, workspace_bytes);
     if (st != PA_OK) return st;
     const pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, seq_lens,
-                                         num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                         num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                          max_blocks_per_seq, num_blocks, scale, dtype, shape,
                                          workspace, flags, q_per_seq);
     if (pa::launch_decode_partitions(a, stream) != hipSuccess) return PA_ERR_HIP;
@@ -446,12 +472,13 @@ static pa_status prefill_common(void* out, const void* q, const void* k_cache, c
                                 int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                 int64_t num_blocks, float scale, pa_dtype dtype, hipStream_t stream) {
-    if (!supported_dtype(dtype) || block_size != PA_BLOCK_SIZE || (head_dim != 64 && head_dim != 128))
+    const int32_t sh = block_shift(block_size);
+    if (!supported_dtype(dtype) || sh < 0 || (fp8 && sh != 0) || (head_dim != 64 && head_dim != 128))
         return PA_ERR_UNSUPPORTED;
     if (num_seqs < 0 || num_tokens < 0 || max_q_len < 0 || num_q_heads <= 0 ||
         num_kv_heads <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
         num_q_heads % num_kv_heads != 0 || !(scale > 0.f) || !isfinite(scale) ||
-        (int64_t)max_blocks_per_seq * PA_BLOCK_SIZE > INT32_MAX)
+        (int64_t)max_blocks_per_seq * block_size > INT32_MAX || num_blocks > (INT64_C(1) << (31 - sh)))
         return PA_ERR_SHAPE;
     const int32_t group = num_q_heads / num_kv_heads;
     if (group > kMaxGroup) return PA_ERR_UNSUPPORTED;   // more q heads per kv head than a workgroup's rows
@@ -476,8 +503,10 @@ static pa_status prefill_common(void* out, const void* q, const void* k_cache, c
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = num_kv_heads;
     a.group = group;
-    a.max_blocks_per_seq = max_blocks_per_seq;
-    a.num_blocks = num_blocks;
+    a.max_blocks_per_seq = max_blocks_per_seq << sh;
+    a.num_blocks = num_blocks << sh;
+    a.table_stride = max_blocks_per_seq;
+    a.block_shift = sh;
     a.scale_log2 = scale * kLog2e;
     a.dtype = dtype == PA_F16 ? pa::kF16 : pa::kBF16;
     a.head_dim = head_dim;

@@ -256,7 +256,7 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     const int pos_end = min(L, pos0 + P);
     const int n_keys = min(ctx + pos_end, max_keys);
     const int ntiles = (n_keys + kKT - 1) / kKT;
-    const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
+    const int32_t* table = a.block_tables + (int64_t)b * a.table_stride;
     const int64_t row_stride = (int64_t)a.num_kv_heads * D;
 
     // ---- this lane's query row and its Q^T fragments
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int blk = tt * 4 + q;
-            pb[q] = blk * kBlockSize < n_keys ? ctab[blk] : -1;
+            pb[q] = blk * kBlockSize < n_keys ? sub_block(ctab[blk >> a.block_shift], blk, a.block_shift) : -1;
         }
     };
     // 16-bit: a row is CPR 16-byte chunks; thread t moves chunk t % CPR of row
@@ -669,7 +669,7 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
     const int pos_end = min(L, pos0 + P);
     const int n_keys = min(ctx + pos_end, max_keys);
     const int ntiles = (n_keys + kKT - 1) / kKT;
-    const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks_per_seq;
+    const int32_t* table = a.block_tables + (int64_t)b * a.table_stride;
     const int64_t row_stride = (int64_t)a.num_kv_heads * kPD;
 
     // ---- Q^T fragments: row rho, elements 16 kk + 8 h .. +7
@@ -710,7 +710,8 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
     const uint32_t koff0 = goff + (uint32_t)((l15 ^ l4) << 4);
     const uint32_t voff = goff + (uint32_t)((l15 ^ (l4 << 2)) << 4);
     const int nb32 = (int)min(a.num_blocks, (int64_t)INT32_MAX);
-    int first_blk = ctab[0];
+    const int sh = a.block_shift;
+    int first_blk = sub_block(ctab[0], 0, sh);
     first_blk = first_blk >= 0 && first_blk < nb32 ? first_blk : 0;
 
     // Block ids are read through the constant address space (scalar loads): for
@@ -720,7 +721,8 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
     const int key_blocks = (n_keys + kBlockSize - 1) / kBlockSize;   // >= 1, <= max_blocks_per_seq
     auto raw_block = [&](int tt) __attribute__((always_inline)) -> int {   // uniform, branch-free
         const int blk = tt * 4 + q;
-        const int pb = ctab[min(blk, key_blocks - 1)];
+        const int bc = min(blk, key_blocks - 1);
+        const int pb = sub_block(ctab[bc >> sh], bc, sh);
         return blk < key_blocks ? pb : first_blk;
     };
     auto valid_block = [&](int pb) __attribute__((always_inline)) -> int { return pb >= 0 && pb < nb32 ? pb : 0; };

@@ -193,11 +193,11 @@ def _concat_blocks(pool, table_row, n):
 
 
 def _small_decode(seed=21, dtype="f16", hq=4, hkv=2, d=32, lens=(1, 15, 16, 17, 40, 0, 33),
-                  write_last=True):
+                  write_last=True, block_size=16):
     return make_decode_case(name="pin", seed=seed, dtype=dtype, num_q_heads=hq,
                             num_kv_heads=hkv, head_dim=d, seq_lens=list(lens),
-                            num_blocks=24, max_blocks_per_seq=4, scale=1 / math.sqrt(d),
-                            write_last=write_last)
+                            num_blocks=384 // block_size, max_blocks_per_seq=64 // block_size,
+                            scale=1 / math.sqrt(d), write_last=write_last, block_size=block_size)
 
 
 def pin_paged_decode_equals_contiguous(o):
@@ -216,6 +216,38 @@ def pin_paged_decode_equals_contiguous(o):
             q = o.bits_to_float64(c.q[b], dtype)[None]
             want = _sdpa64(q, k, v, c.scale, np.array([n - 1]))[0]
             np.testing.assert_allclose(got[b], want, rtol=0, atol=1e-12)
+
+
+def pin_block_size_32(o):
+    """With 32-token blocks (the other usual size) paged decode is still plain
+    attention over the sequence's tokens, and decode and prefill give exactly
+    the results of the 16-token layout of the same tokens."""
+    for dtype in ("f16", "bf16"):
+        c16, c32 = (_small_decode(dtype=dtype, block_size=bs) for bs in (16, 32))
+        assert c32.k_cache.shape[1] == 32
+        outs = []
+        for c in (c16, c32):
+            kc, vc = o.ref_reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache, c.slot_mapping)
+            outs.append(o.ref_decode(c.q, kc, vc, c.block_tables, c.seq_lens, c.scale, dtype))
+        np.testing.assert_array_equal(outs[0], outs[1])
+        for b in range(c32.num_seqs):
+            n = int(c32.seq_lens[b])
+            if n == 0:
+                continue
+            k = o.bits_to_float64(_concat_blocks(kc, c32.block_tables[b], n), dtype)
+            v = o.bits_to_float64(_concat_blocks(vc, c32.block_tables[b], n), dtype)
+            q = o.bits_to_float64(c32.q[b], dtype)[None]
+            want = _sdpa64(q, k, v, c32.scale, np.array([n - 1]))[0]
+            np.testing.assert_allclose(outs[1][b], want, rtol=0, atol=1e-12)
+    pre = []
+    for bs in (16, 32):
+        c = make_prefill_case(name="pin", seed=32, dtype="bf16", num_q_heads=4, num_kv_heads=2,
+                              head_dim=16, q_lens=[5, 0, 40, 1], ctx_lens=[31, 3, 16, 33],
+                              scale=0.25, extra_blocks=1, block_size=bs)
+        kc, vc = o.ref_reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache, c.slot_mapping)
+        pre.append(o.ref_prefill_paged(c.q, kc, vc, c.block_tables, c.ctx_lens,
+                                       c.query_start_loc, c.scale, "bf16"))
+    np.testing.assert_array_equal(pre[0], pre[1])
 
 
 def pin_block_permutation_invariance(o):

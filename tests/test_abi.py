@@ -75,7 +75,9 @@ def test_reshape_rejects(lib):
     assert _reshape(lib, key=None) == NULL
     assert _reshape(lib, slots=None) == NULL
     assert _reshape(lib, d=96) == UNSUP
-    assert _reshape(lib, bs=32) == UNSUP
+    assert _reshape(lib, bs=64) == UNSUP
+    assert _reshape(lib, bs=8) == UNSUP
+    assert _reshape(lib, bs=32, key=None) == NULL     # 32-token blocks pass the block-size check
     assert _reshape(lib, dt=5) == UNSUP
     assert _reshape(lib, n=-1) == SHAPE
     assert _reshape(lib, hkv=0) == SHAPE
@@ -101,6 +103,13 @@ def test_decode_rejects(lib, fn):
     assert _decode(lib, fn, bt=None) == NULL
     assert _decode(lib, fn, d=80) == UNSUP
     assert _decode(lib, fn, bs=8) == UNSUP
+    assert _decode(lib, fn, bs=64) == UNSUP
+    assert _decode(lib, fn, bs=32, q=None) == NULL       # 32-token blocks pass the block-size check
+    assert _decode(lib, fn, bs=32, mb=1 << 26) == SHAPE  # 2^31 tokens per table row
+    assert _decode(lib, fn, bs=32, nb=(1 << 30) + 1) == SHAPE
+    # 64 blocks of 32 tokens in 256-token partitions: 8 partitions, twice the
+    # workspace of the same table in 16-token blocks
+    assert _decode(lib, fn, bs=32, part=256, wsb=2 * 8 * 4 * (128 * 4 + 8)) == WS
     assert _decode(lib, fn, dt=9) == UNSUP
     assert _decode(lib, fn, flags=2) == UNSUP             # unknown flag bit
     assert _decode(lib, fn, hq=6, hkv=4) == SHAPE        # not a multiple
@@ -122,20 +131,27 @@ def test_decode_rejects(lib, fn):
 def test_workspace_size(lib):
     f = lib.pa_decode_workspace_size
     f.restype = ctypes.c_size_t
-    f.argtypes = [ctypes.c_int32] * 6
+    f.argtypes = [ctypes.c_int32] * 7
     # single pass: no workspace
-    assert f(4, 8, 2, 128, 16, 256) == 0
+    assert f(4, 8, 2, 128, 16, 16, 256) == 0
     # 64 blocks in partitions of 16 blocks: 4 partitions per (seq, q head)
-    assert f(2, 8, 2, 128, 64, 256) == 2 * 8 * 4 * (128 * 4 + 8)
-    assert f(2, 8, 2, 128, 64, 24) == 0                  # invalid partition length
+    assert f(2, 8, 2, 128, 16, 64, 256) == 2 * 8 * 4 * (128 * 4 + 8)
+    # 32 blocks of 32 tokens: the same 1024 tokens, the same 4 partitions
+    assert f(2, 8, 2, 128, 32, 32, 256) == 2 * 8 * 4 * (128 * 4 + 8)
+    assert f(2, 8, 2, 128, 32, 8, 256) == 0              # 256 tokens: one partition
+    assert f(2, 8, 2, 128, 16, 64, 24) == 0              # invalid partition length
+    assert f(2, 8, 2, 128, 8, 64, 256) == 0              # invalid block size
+    assert f(2, 8, 2, 128, 64, 64, 256) == 0
     g = lib.pa_decode_default_partition
     g.restype = ctypes.c_int32
-    g.argtypes = [ctypes.c_int32] * 4
-    assert g(32, 32, 128, 256) == 512       # vector-ALU path, 4096-token tables
-    assert g(32, 8, 128, 512) == 1024       # matrix-core path, 8192-token tables
-    assert g(64, 8, 128, 4096) == 2048      # matrix-core path, capped
-    assert g(4, 4, 64, 7) == 256            # short tables: the floor
-    for args in [(32, 32, 128, 256), (32, 8, 128, 512), (64, 8, 128, 4096), (4, 4, 64, 7)]:
+    g.argtypes = [ctypes.c_int32] * 5
+    assert g(32, 32, 128, 16, 256) == 512       # vector-ALU path, 4096-token tables
+    assert g(32, 8, 128, 16, 512) == 1024       # matrix-core path, 8192-token tables
+    assert g(32, 8, 128, 32, 256) == 1024       # the same 8192 tokens in 32-token blocks
+    assert g(64, 8, 128, 16, 4096) == 2048      # matrix-core path, capped
+    assert g(4, 4, 64, 16, 7) == 256            # short tables: the floor
+    for args in [(32, 32, 128, 16, 256), (32, 8, 128, 16, 512), (64, 8, 128, 16, 4096),
+                 (4, 4, 64, 16, 7), (32, 8, 128, 32, 300)]:
         p = g(*args)
         assert p % 16 == 0 and 256 <= p <= 2048
 
@@ -155,6 +171,10 @@ def test_prefill_rejects(lib):
     assert _prefill(lib, cl=None) == NULL
     assert _prefill(lib, d=96) == UNSUP
     assert _prefill(lib, d=64, bs=8) == UNSUP
+    assert _prefill(lib, bs=64) == UNSUP
+    assert _prefill(lib, bs=32, cl=None) == NULL         # 32-token blocks pass the block-size check
+    assert _prefill(lib, bs=32, mb=1 << 26) == SHAPE
+    assert _prefill(lib, bs=32, nb=(1 << 30) + 1) == SHAPE
     assert _prefill(lib, hq=258, hkv=2) == UNSUP         # 129 q heads per kv head
     assert _prefill(lib, hq=30, hkv=8) == SHAPE
     assert _prefill(lib, t=-1) == SHAPE
@@ -177,6 +197,8 @@ def test_copy_blocks_rejects(lib):
     assert call(vc=None) == NULL
     assert call(d=32) == UNSUP
     assert call(bs=8) == UNSUP
+    assert call(bs=64) == UNSUP
+    assert call(bs=32, pairs=None) == NULL
     assert call(n=-1) == SHAPE
     assert call(nb=0) == SHAPE
     assert call(kc=FAKE + 4) == ALIGN
@@ -215,6 +237,7 @@ def test_copy_blocks_fp8_rejects(lib):
     assert call(vs=None) == NULL
     assert call(pairs=None) == NULL
     assert call(d=32) == UNSUP
+    assert call(bs=32) == UNSUP            # FP8 scales are laid out per 16-token block
     assert call(n=-1) == SHAPE
     assert call(ks=FAKE + 4) == ALIGN
     assert call(n=0, pairs=None) == PA_OK
@@ -239,6 +262,7 @@ def test_decode_fp8_rejects(lib, fn):
     assert call(d=80) == UNSUP
     assert call(dt=2) == UNSUP
     assert call(flags=4) == UNSUP
+    assert call(bs=32) == UNSUP
     assert call(hq=258, hkv=2) == SHAPE
     assert call(scale=0.0) == SHAPE
     assert call(part=24) == SHAPE
@@ -261,6 +285,7 @@ def test_prefill_fp8_rejects(lib):
     assert call(vs=None) == NULL
     assert call(qsl=None) == NULL
     assert call(d=96) == UNSUP
+    assert call(bs=32) == UNSUP
     assert call(hq=258, hkv=2) == UNSUP
     assert call(scale=0.0) == SHAPE
     assert call(vs=FAKE + 4) == ALIGN
@@ -287,3 +312,24 @@ def test_decode_multi_rejects(lib):
     assert call(b=0, q=None) == PA_OK
     assert call(part=256, ws=None) == WS
     assert call(part=256, wsb=16) == WS
+
+
+def test_decode_merge_rejects(lib):
+    f = lib.pa_decode_merge
+    f.restype = ctypes.c_int32
+    f.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_size_t, P]
+
+    def call(out=FAKE, sl=FAKE, b=2, hq=8, hkv=2, d=128, bs=16, mb=64, dt=BF16, part=0, ws=None,
+             wsb=0):
+        return f(out, sl, b, hq, hkv, d, bs, mb, dt, part, ws, wsb, None)
+    assert call(bs=64) == UNSUP
+    assert call(d=80) == UNSUP
+    assert call(out=None) == NULL
+    assert call(bs=32, sl=None) == NULL
+    assert call(bs=32, mb=1 << 26) == SHAPE
+    assert call(part=24) == SHAPE
+    assert call(ws=None) == WS                    # 1024 tokens: split, so partials to merge
+    assert call(bs=32, mb=32, ws=None) == WS      # the same 1024 tokens in 32-token blocks
+    assert call(bs=32, mb=4, ws=None) == PA_OK    # 128 tokens: one partition, nothing to merge
+    assert call(b=0, out=None) == PA_OK

@@ -176,7 +176,7 @@ def test_full_llama2_7b_layer_verify():
     q = torch.from_numpy(qbits.view(np.float16)).cuda()
     out = torch.empty_like(q)
     need = pa.pa_decode_workspace_size(c.num_seqs * nq, c.num_q_heads, c.num_kv_heads, c.head_dim,
-                                       c.max_blocks_per_seq, 0)
+                                       16, c.max_blocks_per_seq, 0)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     pa.pa_decode_multi(out, q, g.k_cache, g.v_cache, g.tables, g.lens, c.scale, 0, ws)
     got = host_f64(out)

@@ -48,7 +48,7 @@ def test_captured_decode_step_matches_eager(hq, hkv, dtype):
                          scale=1 / math.sqrt(128), write_last=True)
     g = DecodeOnGPU(c)
     part = 64                                   # several partitions: exercises the merge too
-    need = pa.pa_decode_workspace_size(c.num_seqs, hq, hkv, 128, c.max_blocks_per_seq, part)
+    need = pa.pa_decode_workspace_size(c.num_seqs, hq, hkv, 128, 16, c.max_blocks_per_seq, part)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     out_graph = torch.empty_like(g.q)
     torch.cuda.synchronize()
@@ -93,7 +93,7 @@ def test_captured_fp8_step_matches_eager():
                          max_blocks_per_seq=20, scale=0.088, write_last=False)
     g = Fp8DecodeOnGPU(c)
     part = 64
-    need = pa.pa_decode_workspace_size(c.num_seqs, 16, 2, 128, c.max_blocks_per_seq, part)
+    need = pa.pa_decode_workspace_size(c.num_seqs, 16, 2, 128, 16, c.max_blocks_per_seq, part)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     out_graph = torch.empty_like(g.q)
 
@@ -129,7 +129,7 @@ def test_captured_verification_step_matches_eager():
     rng = np.random.default_rng(26)
     qm = dev_bits(normal_bits(rng, (c.num_seqs, nq, 32, 128), "f16"), "f16")
     part = 64
-    need = pa.pa_decode_workspace_size(c.num_seqs * nq, 32, 32, 128, c.max_blocks_per_seq, part)
+    need = pa.pa_decode_workspace_size(c.num_seqs * nq, 32, 32, 128, 16, c.max_blocks_per_seq, part)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     out_graph = torch.empty_like(qm)
 

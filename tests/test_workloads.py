@@ -6,22 +6,23 @@ from workloads import (NAN_BITS, decode_gqa_shared_prefix, decode_llama2_7b_laye
                        make_decode_case, prefill_chunked)
 
 
-def _read_slots(tables, lens):
+def _read_slots(tables, lens, bs=16):
     """(block, offset) pairs some sequence reads, by walking whole blocks."""
     read = set()
     for row, n in zip(tables, lens):
-        for j in range((int(n) + 15) // 16):
-            for off in range(min(16, int(n) - 16 * j)):
+        for j in range((int(n) + bs - 1) // bs):
+            for off in range(min(bs, int(n) - bs * j)):
                 read.add((int(row[j]), off))
     return read
 
 
 def _check_pool(case, lens, written):
     nan = NAN_BITS[case.dtype]
-    read = _read_slots(case.block_tables, lens)
+    bs = case.k_cache.shape[1]
+    read = _read_slots(case.block_tables, lens, bs)
     nb = case.k_cache.shape[0]
     for blk in range(nb):
-        for off in range(16):
+        for off in range(bs):
             is_nan = (case.k_cache[blk, off] == nan).all() and (case.v_cache[blk, off] == nan).all()
             if (blk, off) in read and (blk, off) not in written:
                 assert not (case.k_cache[blk, off] == nan).any(), (blk, off)
@@ -83,3 +84,28 @@ def test_empty_and_block_multiple_lengths():
     assert (c.block_tables[0] == -1).all()
     assert len(c.slot_mapping) == 3
     _check_pool(c, c.seq_lens, {(int(s) // 16, int(s) % 16) for s in c.slot_mapping})
+
+
+def test_block32_layout():
+    """32-token blocks: the same tokens as the 16-token layout of one seed,
+    read slot for slot through either table."""
+    kw = dict(name="t", seed=6, dtype="f16", num_q_heads=2, num_kv_heads=2, head_dim=64,
+              seq_lens=[0, 31, 32, 33, 70], scale=0.125, write_last=True)
+    a = make_decode_case(num_blocks=12, max_blocks_per_seq=5, **kw)
+    b = make_decode_case(num_blocks=7, max_blocks_per_seq=3, block_size=32, **kw)
+    assert b.k_cache.shape == (7, 32, 2, 64) and b.block_size == 32 and a.block_size == 16
+    np.testing.assert_array_equal(a.q, b.q)
+    np.testing.assert_array_equal(a.key, b.key)
+    used = b.block_tables[b.block_tables >= 0]
+    assert len(used) == 0 + 1 + 1 + 2 + 3 and len(set(used.tolist())) == len(used)
+    for i, s in enumerate(b.slot_mapping):
+        blk, off = int(s) // 32, int(s) % 32
+        seq = [x for x in range(5) if b.seq_lens[x] > 0][i]
+        pos = int(b.seq_lens[seq]) - 1
+        assert (blk, off) == (int(b.block_tables[seq, pos // 32]), pos % 32)
+    _check_pool(b, b.seq_lens, {(int(s) // 32, int(s) % 32) for s in b.slot_mapping})
+    for seq in range(5):
+        for pos in range(int(b.seq_lens[seq]) - 1):   # the cached tokens
+            np.testing.assert_array_equal(
+                a.k_cache[a.block_tables[seq, pos // 16], pos % 16],
+                b.k_cache[b.block_tables[seq, pos // 32], pos % 32])

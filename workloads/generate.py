@@ -13,7 +13,9 @@ Recipe (the same for every workload):
 * Physical blocks are handed out from ``rng.permutation(num_blocks)`` in
   order, ``ceil(tokens / block_size)`` per sequence (the host allocator of
   the ``PagedKVCache`` sketch), and every block-table entry past a sequence's
-  last block is -1.
+  last block is -1.  Blocks hold 16 tokens unless ``block_size`` says
+  otherwise (32 is the other usual size); the values drawn do not depend on
+  it, so one seed gives the same tokens in either layout.
 * Every slot that no sequence reads holds NaN, so a kernel that reads past a
   sequence's end cannot go unnoticed.
 * A token whose k/v the cache-write step stores has NaN in the pool beforehand
@@ -74,15 +76,16 @@ def _place(pool: np.ndarray, blocks: np.ndarray, data: np.ndarray, nan: np.uint1
     the unused tail of the last block gets NaN."""
     n = data.shape[0]
     nb = len(blocks)
+    bs = pool.shape[1]
     if nb == 0:
         return
-    padded = np.full((nb * BLOCK_SIZE,) + data.shape[1:], nan, np.uint16)
+    padded = np.full((nb * bs,) + data.shape[1:], nan, np.uint16)
     padded[:n] = data
-    pool[blocks] = padded.reshape((nb, BLOCK_SIZE) + data.shape[1:])
+    pool[blocks] = padded.reshape((nb, bs) + data.shape[1:])
 
 
-def _ceil_blocks(n: int) -> int:
-    return (n + BLOCK_SIZE - 1) // BLOCK_SIZE
+def _ceil_blocks(n: int, block_size: int = BLOCK_SIZE) -> int:
+    return (n + block_size - 1) // block_size
 
 
 @dataclass
@@ -102,7 +105,7 @@ class DecodeCase:
     max_blocks_per_seq: int
     scale: float
     q: np.ndarray               # uint16 [B, Hq, D]
-    k_cache: np.ndarray         # uint16 [NB, 16, Hkv, D]
+    k_cache: np.ndarray         # uint16 [NB, block_size, Hkv, D]
     v_cache: np.ndarray
     block_tables: np.ndarray    # int32 [B, MB], -1 padded
     seq_lens: np.ndarray        # int32 [B]
@@ -117,7 +120,7 @@ class DecodeCase:
 
     @property
     def block_size(self) -> int:
-        return BLOCK_SIZE
+        return int(self.k_cache.shape[1])
 
     def kv_bytes(self) -> int:
         """K+V bytes of all live tokens (each kv head's tile counted once)."""
@@ -136,7 +139,7 @@ class PrefillCase:
     max_blocks_per_seq: int
     scale: float
     q: np.ndarray               # uint16 [T, Hq, D]
-    k_cache: np.ndarray         # uint16 [NB, 16, Hkv, D], before the cache write
+    k_cache: np.ndarray         # uint16 [NB, block_size, Hkv, D], before the cache write
     v_cache: np.ndarray
     block_tables: np.ndarray    # int32 [B, MB]
     ctx_lens: np.ndarray        # int32 [B]
@@ -162,13 +165,17 @@ class PrefillCase:
     def max_q_len(self) -> int:
         return int(self.q_lens.max()) if self.num_seqs else 0
 
+    @property
+    def block_size(self) -> int:
+        return int(self.k_cache.shape[1])
+
 
 def make_decode_case(*, name: str, seed: int, dtype: str, num_q_heads: int,
                      num_kv_heads: int, head_dim: int, seq_lens, num_blocks: int,
                      max_blocks_per_seq: int, scale: float, write_last: bool,
                      share_group: int = 0, share_tokens: int = 0,
                      rng: np.random.Generator | None = None,
-                     perm: np.ndarray | None = None) -> DecodeCase:
+                     perm: np.ndarray | None = None, block_size: int = BLOCK_SIZE) -> DecodeCase:
     """Build a decode workload.
 
     ``share_group > 0`` makes each run of ``share_group`` consecutive sequences
@@ -184,7 +191,7 @@ def make_decode_case(*, name: str, seed: int, dtype: str, num_q_heads: int,
     nan = NAN_BITS[dtype]
     if share_group and write_last:
         raise ValueError("shared-prefix workloads carry no cache write")
-    if share_group and share_tokens % BLOCK_SIZE:
+    if share_group and share_tokens % block_size:
         raise ValueError("the shared prefix must be whole blocks")
 
     # allocation: hand out physical blocks in permutation order
@@ -194,12 +201,12 @@ def make_decode_case(*, name: str, seed: int, dtype: str, num_q_heads: int,
     cursor = 0
     shared_blocks = {}
     for b in range(b_count):
-        nb = _ceil_blocks(int(seq_lens[b]))
+        nb = _ceil_blocks(int(seq_lens[b]), block_size)
         if nb > max_blocks_per_seq:
             raise ValueError(f"sequence {b} needs {nb} blocks > {max_blocks_per_seq}")
         if share_group:
             grp = b // share_group
-            n_shared = share_tokens // BLOCK_SIZE
+            n_shared = share_tokens // block_size
             if grp not in shared_blocks:
                 shared_blocks[grp] = perm[cursor:cursor + n_shared]
                 cursor += n_shared
@@ -214,7 +221,7 @@ def make_decode_case(*, name: str, seed: int, dtype: str, num_q_heads: int,
             raise ValueError("pool too small for the sequences")
 
     q = normal_bits(np.random.default_rng([seed, _Q]), (b_count, num_q_heads, d), dtype)
-    k_cache = np.full((num_blocks, BLOCK_SIZE, hkv, d), nan, np.uint16)
+    k_cache = np.full((num_blocks, block_size, hkv, d), nan, np.uint16)
     v_cache = np.full_like(k_cache, nan)
 
     n_written = 1 if write_last else 0
@@ -227,8 +234,8 @@ def make_decode_case(*, name: str, seed: int, dtype: str, num_q_heads: int,
             return
         kd = normal_bits(np.random.default_rng([seed, _K, b]), (n_own, hkv, d), dtype)
         vd = normal_bits(np.random.default_rng([seed, _V, b]), (n_own, hkv, d), dtype)
-        nb_total = _ceil_blocks(n)
-        first = start // BLOCK_SIZE
+        nb_total = _ceil_blocks(n, block_size)
+        first = start // block_size
         blocks = tables[b, first:nb_total]
         _place(k_cache, blocks, kd, nan)
         _place(v_cache, blocks, vd, nan)
@@ -239,7 +246,7 @@ def make_decode_case(*, name: str, seed: int, dtype: str, num_q_heads: int,
         n = min(share_tokens, longest)
         kd = normal_bits(np.random.default_rng([seed, _SHK, grp]), (n, hkv, d), dtype)
         vd = normal_bits(np.random.default_rng([seed, _SHV, grp]), (n, hkv, d), dtype)
-        blocks = shared_blocks[grp][:_ceil_blocks(n)]
+        blocks = shared_blocks[grp][:_ceil_blocks(n, block_size)]
         _place(k_cache, blocks, kd, nan)
         _place(v_cache, blocks, vd, nan)
 
@@ -257,7 +264,7 @@ def make_decode_case(*, name: str, seed: int, dtype: str, num_q_heads: int,
         pos = int(seq_lens[b]) - 1
         key[i] = normal_bits(np.random.default_rng([seed, _NEWK, b]), (hkv, d), dtype)
         value[i] = normal_bits(np.random.default_rng([seed, _NEWV, b]), (hkv, d), dtype)
-        slots[i] = int(tables[b, pos // BLOCK_SIZE]) * BLOCK_SIZE + pos % BLOCK_SIZE
+        slots[i] = int(tables[b, pos // block_size]) * block_size + pos % block_size
 
     return DecodeCase(name=name, dtype=dtype, num_q_heads=num_q_heads,
                       num_kv_heads=hkv, head_dim=d, num_blocks=num_blocks,
@@ -273,7 +280,8 @@ def make_decode_case(*, name: str, seed: int, dtype: str, num_q_heads: int,
 def make_prefill_case(*, name: str, seed: int, dtype: str, num_q_heads: int,
                       num_kv_heads: int, head_dim: int, q_lens, ctx_lens, scale: float,
                       extra_blocks: int = 0, max_blocks_per_seq: int | None = None,
-                      rng: np.random.Generator | None = None) -> PrefillCase:
+                      rng: np.random.Generator | None = None,
+                      block_size: int = BLOCK_SIZE) -> PrefillCase:
     """Build a chunked-prefill workload: sequence ``b`` has ``ctx_lens[b]``
     tokens already cached and ``q_lens[b]`` new tokens, packed back to back."""
     rng = rng if rng is not None else np.random.default_rng(seed)
@@ -282,7 +290,7 @@ def make_prefill_case(*, name: str, seed: int, dtype: str, num_q_heads: int,
     b_count = len(q_lens)
     hkv, d = num_kv_heads, head_dim
     nan = NAN_BITS[dtype]
-    nbs = [_ceil_blocks(int(c + l)) for c, l in zip(ctx_lens, q_lens)]
+    nbs = [_ceil_blocks(int(c + l), block_size) for c, l in zip(ctx_lens, q_lens)]
     num_blocks = sum(nbs) + extra_blocks
     mb = max_blocks_per_seq if max_blocks_per_seq is not None else max(max(nbs, default=1), 1)
     perm = rng.permutation(num_blocks)
@@ -296,7 +304,7 @@ def make_prefill_case(*, name: str, seed: int, dtype: str, num_q_heads: int,
     t = int(qsl[-1])
 
     q = normal_bits(np.random.default_rng([seed, _Q]), (t, num_q_heads, d), dtype)
-    k_cache = np.full((num_blocks, BLOCK_SIZE, hkv, d), nan, np.uint16)
+    k_cache = np.full((num_blocks, block_size, hkv, d), nan, np.uint16)
     v_cache = np.full_like(k_cache, nan)
     key = np.empty((t, hkv, d), np.uint16)
     value = np.empty_like(key)
@@ -305,8 +313,8 @@ def make_prefill_case(*, name: str, seed: int, dtype: str, num_q_heads: int,
         c = int(ctx_lens[b])
         kd = normal_bits(np.random.default_rng([seed, _K, b]), (c, hkv, d), dtype)
         vd = normal_bits(np.random.default_rng([seed, _V, b]), (c, hkv, d), dtype)
-        _place(k_cache, tables[b, :_ceil_blocks(c)], kd, nan)
-        _place(v_cache, tables[b, :_ceil_blocks(c)], vd, nan)
+        _place(k_cache, tables[b, :_ceil_blocks(c, block_size)], kd, nan)
+        _place(v_cache, tables[b, :_ceil_blocks(c, block_size)], vd, nan)
         lo, hi = int(qsl[b]), int(qsl[b + 1])
         key[lo:hi] = normal_bits(np.random.default_rng([seed, _NEWK, b]), (hi - lo, hkv, d), dtype)
         value[lo:hi] = normal_bits(np.random.default_rng([seed, _NEWV, b]), (hi - lo, hkv, d), dtype)
@@ -318,7 +326,8 @@ def make_prefill_case(*, name: str, seed: int, dtype: str, num_q_heads: int,
     for b in range(b_count):
         lo = int(qsl[b])
         pos = int(ctx_lens[b]) + np.arange(int(q_lens[b]))
-        slots[lo:lo + len(pos)] = tables[b, pos // BLOCK_SIZE].astype(np.int64) * BLOCK_SIZE + pos % BLOCK_SIZE
+        slots[lo:lo + len(pos)] = (tables[b, pos // block_size].astype(np.int64) * block_size +
+                                   pos % block_size)
 
     return PrefillCase(name=name, dtype=dtype, num_q_heads=num_q_heads,
                        num_kv_heads=hkv, head_dim=d, num_blocks=num_blocks,
@@ -345,23 +354,25 @@ def decode_tiny(seed: int = 1) -> DecodeCase:
 
 
 def decode_llama2_7b_layer(seed: int = 2, batch: int = 64, max_len: int = 4096,
-                           num_heads: int = 32, write_last: bool = True) -> DecodeCase:
+                           num_heads: int = 32, write_last: bool = True,
+                           block_size: int = BLOCK_SIZE) -> DecodeCase:
     """One LLaMA-2-7B-shaped attention layer at decode: 32 q = 32 kv heads,
     head_dim 128, fp16, lengths uniform in [512, max_len], a pool of
-    batch x max_len / 16 blocks (2^31 bytes per K pool at full size)."""
+    batch x max_len / block_size blocks (2^31 bytes per K pool at full size)."""
     rng = np.random.default_rng(seed)
     lo = min(512, max_len)
     lens = rng.integers(lo, max_len + 1, batch)
-    mb = max_len // BLOCK_SIZE
+    mb = max_len // block_size
     return make_decode_case(name="decode_llama2_7b_layer", seed=seed, dtype="f16",
                             num_q_heads=num_heads, num_kv_heads=num_heads, head_dim=128,
                             seq_lens=lens, num_blocks=batch * mb, max_blocks_per_seq=mb,
-                            scale=1 / math.sqrt(128), write_last=write_last, rng=rng)
+                            scale=1 / math.sqrt(128), write_last=write_last, rng=rng,
+                            block_size=block_size)
 
 
 def decode_gqa_shared_prefix(seed: int = 3, batch: int = 256, max_len: int = 8192,
                              min_len: int = 128, group: int = 16,
-                             prefix: int = 1024) -> DecodeCase:
+                             prefix: int = 1024, block_size: int = BLOCK_SIZE) -> DecodeCase:
     """GQA decode, 32 q / 8 kv heads, head_dim 128, bf16, lengths log-uniform
     in [min_len, max_len]; each run of ``group`` sequences shares the physical
     blocks of a ``prefix``-token prefix, then diverges into private blocks."""
@@ -369,17 +380,18 @@ def decode_gqa_shared_prefix(seed: int = 3, batch: int = 256, max_len: int = 819
     lens = np.floor(np.exp(rng.uniform(math.log(min_len), math.log(max_len), batch))).astype(np.int64)
     lens = np.clip(lens, min_len, max_len)
     n_groups = (batch + group - 1) // group
-    private = sum(max(0, _ceil_blocks(int(n)) - prefix // BLOCK_SIZE) for n in lens)
-    nb = n_groups * (prefix // BLOCK_SIZE) + private
+    private = sum(max(0, _ceil_blocks(int(n), block_size) - prefix // block_size) for n in lens)
+    nb = n_groups * (prefix // block_size) + private
     return make_decode_case(name="decode_gqa_shared_prefix", seed=seed, dtype="bf16",
                             num_q_heads=32, num_kv_heads=8, head_dim=128, seq_lens=lens,
-                            num_blocks=nb, max_blocks_per_seq=max_len // BLOCK_SIZE,
+                            num_blocks=nb, max_blocks_per_seq=max_len // block_size,
                             scale=1 / math.sqrt(128), write_last=False,
-                            share_group=group, share_tokens=prefix, rng=rng)
+                            share_group=group, share_tokens=prefix, rng=rng,
+                            block_size=block_size)
 
 
 def prefill_chunked(seed: int = 4, batch: int = 16, new_tokens: int = 8192,
-                    max_ctx: int = 4096) -> PrefillCase:
+                    max_ctx: int = 4096, block_size: int = BLOCK_SIZE) -> PrefillCase:
     """Chunked prefill: ``new_tokens`` new tokens split over ``batch``
     sequences by a multinomial draw, cached context uniform in [0, max_ctx],
     32 q / 8 kv heads, head_dim 128, bf16, causal."""
@@ -388,7 +400,7 @@ def prefill_chunked(seed: int = 4, batch: int = 16, new_tokens: int = 8192,
     ctx = rng.integers(0, max_ctx + 1, batch)
     return make_prefill_case(name="prefill_chunked", seed=seed, dtype="bf16", num_q_heads=32,
                              num_kv_heads=8, head_dim=128, q_lens=q_lens, ctx_lens=ctx,
-                             scale=1 / math.sqrt(128), rng=rng)
+                             scale=1 / math.sqrt(128), rng=rng, block_size=block_size)
 
 
 def decode_long_context(seed: int = 5, batch: int = 8, seq_len: int = 65536,
