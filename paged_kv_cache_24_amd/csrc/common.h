@@ -20,6 +20,13 @@ constexpr int kWave = 64;        // CDNA wavefront width
 __device__ __forceinline__ int sub_block(int entry, int j, int shift) {
     return entry < 0 ? -1 : (int)(((uint32_t)entry << shift) | ((uint32_t)j & ((1u << shift) - 1u)));
 }
+// The same with the shift known at compile time; a 16-token table (SH = 0)
+// already names 16-token blocks, so its entries pass through untouched.
+template <int SH>
+__device__ __forceinline__ int sub_block(int entry, int j) {
+    if constexpr (SH == 0) return entry;
+    else return sub_block(entry, j, SH);
+}
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

@@ -19,7 +19,9 @@
 // Both take the q-head group G at run time: a workgroup's rows are floor(R/G)
 // positions times the G q heads that share the kv head (R = 128 or 256 rows),
 // so every K/V tile is staged in LDS once for all of them; when G does not
-// divide R the last R mod G rows are idle (no q, no store).
+// divide R the last R mod G rows are idle (no q, no store).  Both walk the
+// cache in 16-token blocks; a cache of 32-token blocks (template argument
+// SH = 1) is read as two 16-token halves per table entry (sub_block).
 //
 // prefill_kernel.  One workgroup (8 waves) owns 128 query rows of one
 // (sequence, kv head).  Each wave
@@ -213,7 +215,7 @@ __device__ __forceinline__ bool prefill_item(const PrefillArgs& a, int P, int64_
 
 static_assert(kRows / 16 == kSearchWaves, "the work-order search takes one candidate per wave");
 
-template <int DT, bool F8, int D>
+template <int DT, bool F8, int D, int SH>
 __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     static_assert(D == 64 || D == 128, "head_dim 64 or 128");
     const int G = a.group;          // q heads per kv head, 1 .. kRows
@@ -256,7 +258,8 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     const int pos_end = min(L, pos0 + P);
     const int n_keys = min(ctx + pos_end, max_keys);
     const int ntiles = (n_keys + kKT - 1) / kKT;
-    const int32_t* table = a.block_tables + (int64_t)b * a.table_stride;
+    // (16-token tables: the stride is max_blocks_per_seq, already in a register)
+    const int32_t* table = a.block_tables + (int64_t)b * (SH == 0 ? a.max_blocks_per_seq : a.table_stride);
     const int64_t row_stride = (int64_t)a.num_kv_heads * D;
 
     // ---- this lane's query row and its Q^T fragments
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int blk = tt * 4 + q;
-            pb[q] = blk * kBlockSize < n_keys ? sub_block(ctab[blk >> a.block_shift], blk, a.block_shift) : -1;
+            pb[q] = blk * kBlockSize < n_keys ? sub_block<SH>(ctab[blk >> SH], blk) : -1;
         }
     };
     // 16-bit: a row is CPR 16-byte chunks; thread t moves chunk t % CPR of row
@@ -618,7 +621,7 @@ constexpr int kRows16 = 32 * kW16;      // query rows per workgroup
 constexpr int kQkAhead = 6;             // K fragment reads in flight ahead of the products
 constexpr int kPvAhead = 4;             // products whose V fragments are read ahead
 
-template <int DT>
+template <int DT, int SH>
 __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) {
     const int G = a.group;          // q heads per kv head, 1 .. kRows16
     const int P = kRows16 / G;      // positions per workgroup; rows P G .. kRows16-1 idle
@@ -669,7 +672,8 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
     const int pos_end = min(L, pos0 + P);
     const int n_keys = min(ctx + pos_end, max_keys);
     const int ntiles = (n_keys + kKT - 1) / kKT;
-    const int32_t* table = a.block_tables + (int64_t)b * a.table_stride;
+    // (16-token tables: the stride is max_blocks_per_seq, already in a register)
+    const int32_t* table = a.block_tables + (int64_t)b * (SH == 0 ? a.max_blocks_per_seq : a.table_stride);
     const int64_t row_stride = (int64_t)a.num_kv_heads * kPD;
 
     // ---- Q^T fragments: row rho, elements 16 kk + 8 h .. +7
@@ -710,8 +714,7 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
     const uint32_t koff0 = goff + (uint32_t)((l15 ^ l4) << 4);
     const uint32_t voff = goff + (uint32_t)((l15 ^ (l4 << 2)) << 4);
     const int nb32 = (int)min(a.num_blocks, (int64_t)INT32_MAX);
-    const int sh = a.block_shift;
-    int first_blk = sub_block(ctab[0], 0, sh);
+    int first_blk = sub_block<SH>(ctab[0], 0);
     first_blk = first_blk >= 0 && first_blk < nb32 ? first_blk : 0;
 
     // Block ids are read through the constant address space (scalar loads): for
@@ -721,9 +724,8 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
     const int key_blocks = (n_keys + kBlockSize - 1) / kBlockSize;   // >= 1, <= max_blocks_per_seq
     auto raw_block = [&](int tt) __attribute__((always_inline)) -> int {   // uniform, branch-free
         const int blk = tt * 4 + q;
-        const int bc = min(blk, key_blocks - 1);
-        const int pb = sub_block(ctab[bc >> sh], bc, sh);
-        return blk < key_blocks ? pb : first_blk;
+        const int pb = ctab[min(blk, key_blocks - 1) >> SH];
+        return blk < key_blocks ? sub_block<SH>(pb, blk) : first_blk;
     };
     auto valid_block = [&](int pb) __attribute__((always_inline)) -> int { return pb >= 0 && pb < nb32 ? pb : 0; };
     auto block_of_scalar = [&](int tt) __attribute__((always_inline)) -> int { return valid_block(raw_block(tt)); };
@@ -1013,7 +1015,15 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
 
 template <int DT, bool F8, int D>
 static void launch_prefill_g(const PrefillArgs& a, hipStream_t s, dim3 grid) {
-    hipLaunchKernelGGL((prefill_kernel<DT, F8, D>), grid, dim3(512), 0, s, a);
+    // the block shift is a template argument (a runtime one costs the 16-token
+    // case measurable time); FP8 pools only come in 16-token blocks
+    if constexpr (!F8) {
+        if (a.block_shift == 1) {
+            hipLaunchKernelGGL((prefill_kernel<DT, F8, D, 1>), grid, dim3(512), 0, s, a);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((prefill_kernel<DT, F8, D, 0>), grid, dim3(512), 0, s, a);
 }
 
 // the 16x16x32 kernel: every FP8 prefill, and 16-bit prefill at head_dim 64
@@ -1041,7 +1051,8 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
 
 template <int DT>
 static void launch_prefill16_g(const PrefillArgs& a, hipStream_t s, dim3 grid) {
-    hipLaunchKernelGGL((prefill16_kernel<DT>), grid, dim3(64 * kW16), 0, s, a);
+    if (a.block_shift == 1) hipLaunchKernelGGL((prefill16_kernel<DT, 1>), grid, dim3(64 * kW16), 0, s, a);
+    else hipLaunchKernelGGL((prefill16_kernel<DT, 0>), grid, dim3(64 * kW16), 0, s, a);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
