@@ -90,13 +90,27 @@ class PrefillOnGPU:
         return out
 
 
+def ulps(got64: np.ndarray, ref64: np.ndarray, dtype: str) -> np.ndarray:
+    """|got - ref| in units of the spacing of the output type at |ref| (fp16:
+    10 fraction bits, normals from 2^-14; bf16: 7 fraction bits)."""
+    frac, emin = (10, -14) if dtype == "f16" else (7, -126)
+    mag = np.maximum(np.abs(ref64), 2.0 ** emin)
+    spacing = 2.0 ** (np.floor(np.log2(mag)) - frac)
+    return np.abs(got64 - ref64) / spacing
+
+
 def assert_close(got64: np.ndarray, ref64: np.ndarray, dtype: str, what: str = ""):
     assert got64.shape == ref64.shape, (got64.shape, ref64.shape)
     assert np.isfinite(got64).all(), f"{what}: non-finite output"
     err = np.abs(got64 - ref64)
     worst = float(err.max()) if err.size else 0.0
-    assert worst <= TOL[dtype], (
-        f"{what}: max-abs error {worst:.3e} > {TOL[dtype]} (max |ref| {np.abs(ref64).max():.3f})")
+    if worst > TOL[dtype]:
+        i = np.unravel_index(int(np.argmax(err)), err.shape)
+        u = ulps(got64, ref64, dtype)
+        raise AssertionError(
+            f"{what}: max-abs error {worst:.3e} > {TOL[dtype]} at {tuple(int(x) for x in i)} "
+            f"(ref {ref64[i]:.4f}, {u[i]:.2f} ulps of {dtype} there; max |ref| "
+            f"{np.abs(ref64).max():.3f}, max error {u.max():.2f} ulps)")
     return worst
 
 

@@ -8,8 +8,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import (DecodeOnGPU, TOL, assert_close, dev_bits, dev_int, host_bits, host_f64,
-                         require_gpu)
+from gpu_helpers import (TORCH_DTYPE, DecodeOnGPU, TOL, assert_close, dev_bits, dev_int, host_bits,
+                         host_f64, require_gpu, ulps)
 from workloads import (decode_gqa_shared_prefix, decode_llama2_7b_layer, decode_long_context,
                        decode_tiny, make_decode_case, normal_bits)
 
@@ -103,6 +103,41 @@ def test_one_token_context_returns_v():
         for i in range(5):
             for h in range(8):
                 np.testing.assert_array_equal(out[i, h], c.value[i, h // 4])
+
+
+def _scaled_bits(bits: np.ndarray, dtype: str, factor: float) -> np.ndarray:
+    """16-bit patterns times a power of two (exact; NaN stays NaN)."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(TORCH_DTYPE[dtype])
+    return (t * factor).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(4, 4, 128), (4, 2, 128), (4, 4, 64), (8, 4, 64)])
+def test_large_bf16_outputs_within_half_ulp(hq, hkv, d):
+    """Where |out| >= 4 a bf16 output is spaced 2^-5 apart or more, so even a
+    correctly rounded result can miss the 1e-2 bound by up to 1.56e-2.  Such
+    outputs (short contexts, values scaled by 16) are checked in units of the
+    output's own spacing instead: the vector-ALU decode (fp32 products and sums,
+    one rounding at the end) must land within half a spacing plus float32
+    error.  The ulp errors are printed; elements under 4 keep the 1e-2 bound.
+    (The matrix-core paths round P to 16 bits before PV, an error that grows
+    with |V|, so they are held to the tolerance on the workloads' N(0, 1) data.)"""
+    c = make_decode_case(name=f"large-{hq}-{hkv}-{d}", seed=8 + d, dtype="bf16", num_q_heads=hq,
+                         num_kv_heads=hkv, head_dim=d, seq_lens=[1, 2, 3, 2, 5, 3, 40],
+                         num_blocks=12, max_blocks_per_seq=3, scale=0.05, write_last=True)
+    c.v_cache[:] = _scaled_bits(c.v_cache, "bf16", 16.0)
+    c.value[:] = _scaled_bits(c.value, "bf16", 16.0)
+    g = DecodeOnGPU(c)
+    g.write()
+    kc, vc, ref = _oracle_after_write(c)
+    for part in (0, 16):
+        got = host_f64(g.decode(partition_tokens=part))
+        big = np.abs(ref) >= 4
+        assert big.sum() > 200                  # the case really has such outputs
+        u = ulps(got, ref, "bf16")
+        print(f"partition {part}: |ref| >= 4: {int(big.sum())} elements, max error "
+              f"{u[big].max():.3f} ulps; |ref| < 4: max abs error {np.abs(got - ref)[~big].max():.2e}")
+        assert u[big].max() <= 0.5 + 1e-3
+        assert np.abs(got - ref)[~big].max() <= TOL["bf16"]
 
 
 def _needle_case(dtype, lens, part_tokens, seed=3):

@@ -178,3 +178,4 @@ def test_prefill_deterministic_repeat():
     for _ in range(3):
         g.out = torch.zeros_like(g.q)
         np.testing.assert_array_equal(first, host_bits(g.prefill()))
+
