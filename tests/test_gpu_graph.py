@@ -39,16 +39,17 @@ def _capture(step):
     return graph
 
 
+@pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("hq,hkv,dtype", [(8, 8, "f16"), (16, 2, "bf16")])
-def test_captured_decode_step_matches_eager(hq, hkv, dtype):
+def test_captured_decode_step_matches_eager(hq, hkv, dtype, bs):
     import paged_kv_cache_24_amd as pa
     lens = [300, 17, 1, 129, 64, 0]
     c = make_decode_case(name="graph", seed=21, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv,
-                         head_dim=128, seq_lens=lens, num_blocks=64, max_blocks_per_seq=20,
-                         scale=1 / math.sqrt(128), write_last=True)
+                         head_dim=128, seq_lens=lens, num_blocks=64, max_blocks_per_seq=320 // bs,
+                         scale=1 / math.sqrt(128), write_last=True, block_size=bs)
     g = DecodeOnGPU(c)
     part = 64                                   # several partitions: exercises the merge too
-    need = pa.pa_decode_workspace_size(c.num_seqs, hq, hkv, 128, 16, c.max_blocks_per_seq, part)
+    need = pa.pa_decode_workspace_size(c.num_seqs, hq, hkv, 128, bs, c.max_blocks_per_seq, part)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     out_graph = torch.empty_like(g.q)
     torch.cuda.synchronize()
