@@ -29,8 +29,9 @@
  * [num_blocks * block_size][num_kv_heads][head_dim] view.  block_size is 16
  * or 32, the two usual block sizes ("vLLM 在 CANN 上的推理优化", section
  * "vLLM 的 PagedAttention 数据结构", the PagedKVCache sketch); the FP8 calls
- * take 16 only.  head_dim is 64 or 128.  With 32-token blocks the pool holds
- * at most 2^30 blocks.
+ * take 16 only.  head_dim is 64 or 128.  The attention calls take pools of at
+ * most 2^31 blocks (2^30 with 32-token blocks), the range an int32 table entry
+ * can name in 16-token units; a larger num_blocks gives PA_ERR_SHAPE.
  *
  * Streams.  Work is enqueued on `stream` (0 = the null stream).  No call
  * synchronises, reads device memory from the host or allocates, so every call

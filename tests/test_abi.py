@@ -107,6 +107,7 @@ def test_decode_rejects(lib, fn):
     assert _decode(lib, fn, bs=32, q=None) == NULL       # 32-token blocks pass the block-size check
     assert _decode(lib, fn, bs=32, mb=1 << 26) == SHAPE  # 2^31 tokens per table row
     assert _decode(lib, fn, bs=32, nb=(1 << 30) + 1) == SHAPE
+    assert _decode(lib, fn, nb=(1 << 31) + 1) == SHAPE        # more blocks than an int32 entry names
     # 64 blocks of 32 tokens in 256-token partitions: 8 partitions, twice the
     # workspace of the same table in 16-token blocks
     assert _decode(lib, fn, bs=32, part=256, wsb=2 * 8 * 4 * (128 * 4 + 8)) == WS
@@ -175,6 +176,7 @@ def test_prefill_rejects(lib):
     assert _prefill(lib, bs=32, cl=None) == NULL         # 32-token blocks pass the block-size check
     assert _prefill(lib, bs=32, mb=1 << 26) == SHAPE
     assert _prefill(lib, bs=32, nb=(1 << 30) + 1) == SHAPE
+    assert _prefill(lib, nb=(1 << 31) + 1) == SHAPE
     assert _prefill(lib, hq=258, hkv=2) == UNSUP         # 129 q heads per kv head
     assert _prefill(lib, hq=30, hkv=8) == SHAPE
     assert _prefill(lib, t=-1) == SHAPE
