@@ -319,7 +319,8 @@ pa_status pa_prefill_paged(void* out, const void* q, const void* k_cache, const 
  * (codes at row s of the [num_blocks * block_size] view, scales at
  * [s / block_size][head][s % block_size]).  Slot conventions as for
  * pa_reshape_and_cache; key and value are [num_tokens][num_kv_heads][head_dim]
- * of `dtype`.  num_tokens == 0 is a no-op returning PA_OK.
+ * of `dtype`.  num_tokens == 0 is a no-op returning PA_OK; num_tokens *
+ * num_kv_heads above 2^31 - 1 gives PA_ERR_SHAPE.
  */
 pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* k_cache,
                                    void* v_cache, float* k_scales, float* v_scales,

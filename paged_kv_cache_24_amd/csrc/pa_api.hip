@@ -229,7 +229,9 @@ pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* k_c
                                    int64_t num_blocks, pa_dtype dtype, hipStream_t stream) {
     if (!supported_dtype(dtype) || block_size != PA_BLOCK_SIZE || (head_dim != 64 && head_dim != 128))
         return PA_ERR_UNSUPPORTED;
-    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+    if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+        num_tokens > INT32_MAX / num_kv_heads)   // (token, head) pairs are counted in 32 bits
+        return PA_ERR_SHAPE;
     if (num_tokens == 0) return PA_OK;
     if (!key || !value || !k_cache || !v_cache || !k_scales || !v_scales || !slot_mapping)
         return PA_ERR_NULL_PTR;

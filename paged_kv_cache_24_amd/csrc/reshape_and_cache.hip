@@ -57,64 +57,80 @@ hipError_t launch_reshape_and_cache(const ReshapeArgs& a, hipStream_t stream) {
 // Cache write into an FP8 (OCP E4M3) cache ("vLLM-Ascend 原理", §四 on KV-cache
 // quantisation: k and v are quantised when the step writes them).  One row is
 // one (token, kv head, K or V): head_dim elements sharing one float32 scale.
-// D/8 consecutive lanes own a row, 8 elements each (one 16-byte load): the row
-// maximum is a DPP max over those lanes, then
+// D/8 consecutive lanes own the K row and the V row of one (token, kv head),
+// 8 elements of each (two 16-byte loads in flight): a row maximum is a DPP max
+// over those lanes, then
 //     s = amax / 448 (s = 1 for an all-zero row),  code = e4m3(clamp(x / s))
 // with the quotient rounded once in float32 and the conversion rounding to
-// nearest even.  Codes leave as one 8-byte store per lane; the first lane of
-// the row stores the scale at [block][head][offset].
+// nearest even.  Codes leave as one 8-byte store per lane and row; the first
+// lane of the group stores the two scales at [block][head][offset].
 // ---------------------------------------------------------------------------
 template <int DT, int D>
+__device__ __forceinline__ uint2 quantize8(const u32x4& w, float& s_out) {
+    constexpr int L = D / 8;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[2 * e] = lo_to_f32<DT>(w[e]);
+        x[2 * e + 1] = hi_to_f32<DT>(w[e]);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    amax = group_max<L>(amax);
+    const float s = amax > 0.f ? amax / 448.f : 1.f;
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(x[e] / s, -448.f), 448.f);
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+    s_out = s;
+    return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
+// (token, kv head) pairs number below 2^31 (checked by the caller), so the
+// index arithmetic is 32-bit.
+template <int DT, int D>
 __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(ReshapeFp8Args a) {
-    constexpr int L = D / 8;                       // lanes per row
+    constexpr int L = D / 8;                       // lanes per (token, head)
     const int lane_in_row = threadIdx.x % L;
-    const int64_t rows = a.num_tokens * 2 * a.num_kv_heads;
-    const int64_t rows_per_grid = (int64_t)gridDim.x * (blockDim.x / L);
-    for (int64_t row = (int64_t)blockIdx.x * (blockDim.x / L) + threadIdx.x / L; row < rows;
-         row += rows_per_grid) {
-        // row = (token * 2 + is_v) * kv_heads + head: consecutive rows of a
-        // token are consecutive in memory, so a wave reads whole token rows
-        const int64_t th = row / a.num_kv_heads;
-        const int h = (int)(row - th * a.num_kv_heads);
-        const int64_t t = th >> 1;
-        const bool is_v = th & 1;
+    const uint32_t hkv = (uint32_t)a.num_kv_heads;
+    const uint32_t pairs = (uint32_t)a.num_tokens * hkv;
+    const uint32_t per_grid = gridDim.x * (blockDim.x / L);
+    for (uint32_t p = blockIdx.x * (blockDim.x / L) + threadIdx.x / L; p < pairs; p += per_grid) {
+        // consecutive pairs are consecutive heads of a token: a wave reads whole token rows
+        const uint32_t t = p / hkv;
+        const uint32_t h = p - t * hkv;
         const int64_t slot = a.slot_mapping[t];
-        if (slot < 0 || slot >= a.num_slots) continue;   // padding row or outside the pool (whole row)
-        const uint16_t* src = static_cast<const uint16_t*>(is_v ? a.value : a.key) +
-                              (t * a.num_kv_heads + h) * D + 8 * lane_in_row;
-        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            x[2 * e] = lo_to_f32<DT>(w[e]);
-            x[2 * e + 1] = hi_to_f32<DT>(w[e]);
-        }
-        float amax = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
-        amax = group_max<L>(amax);
-        const float s = amax > 0.f ? amax / 448.f : 1.f;
-        float y[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(x[e] / s, -448.f), 448.f);
-        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-        lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
-        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
-        hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+        if (slot < 0 || slot >= a.num_slots) continue;   // padding row or outside the pool
+        const size_t src = (size_t)p * D + 8 * lane_in_row;
+        const u32x4 wk = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            static_cast<const uint16_t*>(a.key) + src));
+        const u32x4 wv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+            static_cast<const uint16_t*>(a.value) + src));
+        float sk, sv;
+        const uint2 ck = quantize8<DT, D>(wk, sk);
+        const uint2 cv = quantize8<DT, D>(wv, sv);
         const int64_t blk = slot / kBlockSize;
         const int off = (int)(slot - blk * kBlockSize);
-        uint8_t* cache = is_v ? a.v_cache : a.k_cache;
-        *reinterpret_cast<uint2*>(cache + (slot * a.num_kv_heads + h) * D + 8 * lane_in_row) =
-            make_uint2((uint32_t)lo, (uint32_t)hi);
-        if (lane_in_row == 0)
-            (is_v ? a.v_scales : a.k_scales)[(blk * a.num_kv_heads + h) * kBlockSize + off] = s;
+        const int64_t dst = (slot * hkv + h) * D + 8 * lane_in_row;
+        *reinterpret_cast<uint2*>(a.k_cache + dst) = ck;
+        *reinterpret_cast<uint2*>(a.v_cache + dst) = cv;
+        if (lane_in_row == 0) {
+            const int64_t si = (blk * hkv + h) * kBlockSize + off;
+            a.k_scales[si] = sk;
+            a.v_scales[si] = sv;
+        }
     }
 }
 
 hipError_t launch_reshape_and_cache_fp8(const ReshapeFp8Args& a, hipStream_t stream) {
-    const int64_t rows = a.num_tokens * 2 * a.num_kv_heads;
-    const int rows_per_wg = 256 / (a.head_dim / 8);
-    const int64_t want = (rows + rows_per_wg - 1) / rows_per_wg;
+    const int64_t pairs = a.num_tokens * a.num_kv_heads;
+    if (pairs > INT32_MAX) return hipErrorInvalidValue;
+    const int pairs_per_wg = 256 / (a.head_dim / 8);
+    const int64_t want = (pairs + pairs_per_wg - 1) / pairs_per_wg;
     const dim3 grid((unsigned)(want < 65536 ? want : 65536));
     if (a.dtype == kF16) {
         if (a.head_dim == 128) hipLaunchKernelGGL((reshape_and_cache_fp8_kernel<kF16, 128>), grid, dim3(256), 0, stream, a);

@@ -223,6 +223,7 @@ def test_reshape_fp8_rejects(lib):
     assert call(dt=3) == UNSUP
     assert call(bs=32) == UNSUP
     assert call(n=-1) == SHAPE
+    assert call(n=1 << 28, hkv=8) == SHAPE   # 2^31 (token, head) pairs
     assert call(ks=FAKE + 4) == ALIGN
     assert call(kc=FAKE + 8) == ALIGN
     assert call(n=0, key=None) == PA_OK
