@@ -57,13 +57,13 @@ hipError_t launch_reshape_and_cache(const ReshapeArgs& a, hipStream_t stream) {
 // Cache write into an FP8 (OCP E4M3) cache ("vLLM-Ascend 原理", §四 on KV-cache
 // quantisation: k and v are quantised when the step writes them).  One row is
 // one (token, kv head, K or V): head_dim elements sharing one float32 scale.
-// D/8 consecutive lanes own the K row and the V row of one (token, kv head),
-// 8 elements of each (two 16-byte loads in flight): a row maximum is a DPP max
+// D/8 consecutive lanes own the K rows and the V rows of two (token, kv head)
+// pairs, 8 elements of each (four 16-byte loads in flight): a row maximum is a DPP max
 // over those lanes, then
 //     s = amax / 448 (s = 1 for an all-zero row),  code = e4m3(clamp(x / s))
 // with the quotient rounded once in float32 and the conversion rounding to
 // nearest even.  Codes leave as one 8-byte store per lane and row; the first
-// lane of the group stores the two scales at [block][head][offset].
+// lane of the group stores the row scales at [block][head][offset].
 // ---------------------------------------------------------------------------
 template <int DT, int D>
 __device__ __forceinline__ uint2 quantize8(const u32x4& w, float& s_out) {
@@ -91,37 +91,56 @@ __device__ __forceinline__ uint2 quantize8(const u32x4& w, float& s_out) {
 }
 
 // (token, kv head) pairs number below 2^31 (checked by the caller), so the
-// index arithmetic is 32-bit.
+// index arithmetic is 32-bit.  Each lane group takes two consecutive pairs and
+// issues all four row loads before quantising (a group past the end reloads
+// its first pair and stores it once).
 template <int DT, int D>
 __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(ReshapeFp8Args a) {
     constexpr int L = D / 8;                       // lanes per (token, head)
     const int lane_in_row = threadIdx.x % L;
     const uint32_t hkv = (uint32_t)a.num_kv_heads;
     const uint32_t pairs = (uint32_t)a.num_tokens * hkv;
-    const uint32_t per_grid = gridDim.x * (blockDim.x / L);
-    for (uint32_t p = blockIdx.x * (blockDim.x / L) + threadIdx.x / L; p < pairs; p += per_grid) {
-        // consecutive pairs are consecutive heads of a token: a wave reads whole token rows
-        const uint32_t t = p / hkv;
-        const uint32_t h = p - t * hkv;
-        const int64_t slot = a.slot_mapping[t];
-        if (slot < 0 || slot >= a.num_slots) continue;   // padding row or outside the pool
-        const size_t src = (size_t)p * D + 8 * lane_in_row;
-        const u32x4 wk = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-            static_cast<const uint16_t*>(a.key) + src));
-        const u32x4 wv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-            static_cast<const uint16_t*>(a.value) + src));
-        float sk, sv;
-        const uint2 ck = quantize8<DT, D>(wk, sk);
-        const uint2 cv = quantize8<DT, D>(wv, sv);
-        const int64_t blk = slot / kBlockSize;
-        const int off = (int)(slot - blk * kBlockSize);
-        const int64_t dst = (slot * hkv + h) * D + 8 * lane_in_row;
-        *reinterpret_cast<uint2*>(a.k_cache + dst) = ck;
-        *reinterpret_cast<uint2*>(a.v_cache + dst) = cv;
-        if (lane_in_row == 0) {
-            const int64_t si = (blk * hkv + h) * kBlockSize + off;
-            a.k_scales[si] = sk;
-            a.v_scales[si] = sv;
+    const uint32_t per_grid = 2 * gridDim.x * (blockDim.x / L);
+    for (uint32_t p0 = 2 * (blockIdx.x * (blockDim.x / L) + threadIdx.x / L); p0 < pairs; p0 += per_grid) {
+        const bool two = p0 + 1 < pairs;
+        const uint32_t p1 = two ? p0 + 1 : p0;
+        const uint32_t t0 = p0 / hkv, t1 = p1 / hkv;
+        const uint32_t h0 = p0 - t0 * hkv, h1 = p1 - t1 * hkv;
+        const int64_t slot0 = a.slot_mapping[t0];
+        const int64_t slot1 = a.slot_mapping[t1];
+        const size_t s0 = (size_t)p0 * D + 8 * lane_in_row, s1 = (size_t)p1 * D + 8 * lane_in_row;
+        const u32x4 wk0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.key) + s0));
+        const u32x4 wv0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.value) + s0));
+        const u32x4 wk1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.key) + s1));
+        const u32x4 wv1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.value) + s1));
+        float sk0, sv0, sk1, sv1;
+        const uint2 ck0 = quantize8<DT, D>(wk0, sk0);
+        const uint2 cv0 = quantize8<DT, D>(wv0, sv0);
+        const uint2 ck1 = quantize8<DT, D>(wk1, sk1);
+        const uint2 cv1 = quantize8<DT, D>(wv1, sv1);
+        if (slot0 >= 0 && slot0 < a.num_slots) {
+            const int64_t blk = slot0 / kBlockSize;
+            const int off = (int)(slot0 - blk * kBlockSize);
+            const int64_t dst = (slot0 * hkv + h0) * D + 8 * lane_in_row;
+            *reinterpret_cast<uint2*>(a.k_cache + dst) = ck0;
+            *reinterpret_cast<uint2*>(a.v_cache + dst) = cv0;
+            if (lane_in_row == 0) {
+                const int64_t si = (blk * hkv + h0) * kBlockSize + off;
+                a.k_scales[si] = sk0;
+                a.v_scales[si] = sv0;
+            }
+        }
+        if (two && slot1 >= 0 && slot1 < a.num_slots) {
+            const int64_t blk = slot1 / kBlockSize;
+            const int off = (int)(slot1 - blk * kBlockSize);
+            const int64_t dst = (slot1 * hkv + h1) * D + 8 * lane_in_row;
+            *reinterpret_cast<uint2*>(a.k_cache + dst) = ck1;
+            *reinterpret_cast<uint2*>(a.v_cache + dst) = cv1;
+            if (lane_in_row == 0) {
+                const int64_t si = (blk * hkv + h1) * kBlockSize + off;
+                a.k_scales[si] = sk1;
+                a.v_scales[si] = sv1;
+            }
         }
     }
 }
@@ -129,7 +148,7 @@ __global__ __launch_bounds__(256) void reshape_and_cache_fp8_kernel(ReshapeFp8Ar
 hipError_t launch_reshape_and_cache_fp8(const ReshapeFp8Args& a, hipStream_t stream) {
     const int64_t pairs = a.num_tokens * a.num_kv_heads;
     if (pairs > INT32_MAX) return hipErrorInvalidValue;
-    const int pairs_per_wg = 256 / (a.head_dim / 8);
+    const int pairs_per_wg = 2 * 256 / (a.head_dim / 8);
     const int64_t want = (pairs + pairs_per_wg - 1) / pairs_per_wg;
     const dim3 grid((unsigned)(want < 65536 ? want : 65536));
     if (a.dtype == kF16) {
