@@ -733,12 +733,13 @@ def _traffic_profile(root):
         "hbm_write_bytes_per_launch": int(w_dec * 1024 * ws),
         "hbm_bytes_per_launch": int(f_dec * 1024 * fs + w_dec * 1024 * ws),
         "algorithmic_bytes_per_launch": algo,
+        # the runs that made the databases under `root` (the directory this was given)
         "commands": [
-            "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc/dec_FETCH_SIZE -o run -- python3 -u bench.py --quick --no-cpu-baseline --steps 5 --warmup 2",
-            "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc/dec_WRITE_SIZE -o run -- python3 -u bench.py --quick --no-cpu-baseline --steps 5 --warmup 2",
-            "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc/copy_FETCH_SIZE -o run -- python3 -u bench.py --copy-calibration",
-            "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc/copy_WRITE_SIZE -o run -- python3 -u bench.py --copy-calibration",
-            "python3 bench.py --traffic-profile gpurun_out/pmc > profiles/decode_partition_traffic.json",
+            f"rocprofv3 --pmc FETCH_SIZE -d {root}/dec_FETCH_SIZE -o run -- python3 -u bench.py --quick --no-cpu-baseline --steps 5 --warmup 2",
+            f"rocprofv3 --pmc WRITE_SIZE -d {root}/dec_WRITE_SIZE -o run -- python3 -u bench.py --quick --no-cpu-baseline --steps 5 --warmup 2",
+            f"rocprofv3 --pmc FETCH_SIZE -d {root}/copy_FETCH_SIZE -o run -- python3 -u bench.py --copy-calibration",
+            f"rocprofv3 --pmc WRITE_SIZE -d {root}/copy_WRITE_SIZE -o run -- python3 -u bench.py --copy-calibration",
+            f"python3 bench.py --traffic-profile {root} > profiles/decode_partition_traffic.json",
         ],
     }
     print(json.dumps(out, indent=1))
