@@ -145,8 +145,9 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pair
  * pa_decode_default_partition -- the split-KV partition length, in tokens, that
  * pa_decode uses when given partition_tokens == 0 (a power of two >= 256).  It
  * depends only on host-known sizes: about max_blocks_per_seq * block_size / 8,
- * capped at 512 tokens when at most 2 q heads share a kv head and at 2048
- * otherwise.  A partition covering max_blocks_per_seq * block_size tokens or
+ * capped at 2048 tokens where decode runs on matrix cores (head_dim 128 and 3
+ * or more q heads per kv head) and at 512 otherwise; 256 for invalid
+ * arguments.  A partition covering max_blocks_per_seq * block_size tokens or
  * more means a single pass with no merge.  The online-softmax merge of partitions is exact
  * ("vLLM-Ascend 原理", §四 "ATB 算子": softmax statistics kept online), so the
  * choice changes only float32 rounding.
