@@ -181,3 +181,24 @@ def test_block32_copy_blocks():
         rk, rv = oracle.ref_copy_blocks(kc, vc, ok)
         np.testing.assert_array_equal(host_bits(gk), rk)
         np.testing.assert_array_equal(host_bits(gv), rv)
+
+
+def test_block32_two_phase_decode_equals_one_call():
+    """pa_decode_partitions then pa_decode_merge (both told block_size 32) give
+    exactly the output of pa_decode."""
+    import paged_kv_cache_24_amd as pa
+    c = make_decode_case(name="two-phase-bs32", seed=980, dtype="bf16", num_q_heads=16,
+                         num_kv_heads=2, head_dim=128, seq_lens=LENS, num_blocks=70,
+                         max_blocks_per_seq=16, scale=1 / math.sqrt(128), write_last=True,
+                         block_size=32)
+    g = DecodeOnGPU(c)
+    g.write()
+    for p in (0, 64):
+        one = host_bits(g.decode(partition_tokens=p)).copy()
+        need = pa.pa_decode_workspace_size(c.num_seqs, 16, 2, 128, 32, 16, p)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(g.q)
+        pa.pa_decode_partitions(out, g.q, g.k_cache, g.v_cache, g.tables, g.lens, c.scale, ws, p)
+        pa.pa_decode_merge(out, g.lens, 2, 16, ws, p, block_size=32)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_bits(out), one)
