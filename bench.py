@@ -116,9 +116,11 @@ class DecodeRun:
         self.lens = _i(case.seq_lens)
         self.out = torch.empty_like(self.q)
         self.part = partition_tokens or pa.pa_decode_default_partition(
-            case.num_q_heads, case.num_kv_heads, case.head_dim, 16, case.max_blocks_per_seq)
+            case.num_q_heads, case.num_kv_heads, case.head_dim, case.block_size,
+            case.max_blocks_per_seq)
         need = pa.pa_decode_workspace_size(case.num_seqs, case.num_q_heads, case.num_kv_heads,
-                                           case.head_dim, 16, case.max_blocks_per_seq, self.part)
+                                           case.head_dim, case.block_size, case.max_blocks_per_seq,
+                                           self.part)
         self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
         self.has_write = len(case.slot_mapping) > 0
         # the streaming hint is a promise that no physical block is read twice in the
@@ -140,7 +142,7 @@ class DecodeRun:
         if ev is not None:
             ev[2].record()
         pa.pa_decode_merge(self.out, self.lens, c.num_kv_heads, c.max_blocks_per_seq, self.ws,
-                           self.part)
+                           self.part, block_size=c.block_size)
         if ev is not None:
             ev[3].record()
 
@@ -179,7 +181,8 @@ class DecodeRun:
         elt = 2
         kv = int(lens.sum()) * 2 * c.num_kv_heads * c.head_dim * elt
         q = c.num_seqs * c.num_q_heads * c.head_dim * elt
-        table = int(((lens + 15) // 16).sum()) * 4
+        bs = c.block_size
+        table = int(((lens + bs - 1) // bs).sum()) * 4
         out = c.num_seqs * c.num_q_heads * c.head_dim * elt
         return kv, kv + q + table + out
 
@@ -359,7 +362,8 @@ def _secondary_decode(builder, name, steps, warmup, note=None, cpu=True, fp8=Fal
     dec_ms = per["partitions"] + per["merge"]
     res = {"workload": name, "ms_per_step": round(wall, 4), "decode_ms": round(dec_ms, 4),
            "partition_kernel_ms": round(per["partitions"], 4), "merge_ms": round(per["merge"], 4),
-           "partition_tokens": run.part, "stream_kv": bool(run.flags), "kv_bytes": kv,
+           "partition_tokens": run.part, "block_size": case.block_size,
+           "stream_kv": bool(run.flags), "kv_bytes": kv,
            "kv_GBs": round(kv / (dec_ms * 1e-3) / 1e9, 1),
            "pct_hbm_peak": round(100 * kv / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
            "tokens_per_s": round(case.num_seqs / (dec_ms * 1e-3), 1)}
@@ -671,13 +675,16 @@ def _run_one(name, steps, warmup):
             decode_long_context, name, steps, warmup, cpu=False, fp8=True),
         "decode_llama2_7b_layer_verify": lambda: _secondary_multi(steps, warmup),
         "copy_blocks": lambda: _secondary_copy_blocks(steps, warmup),
+        "decode_llama2_7b_layer_bs32": lambda: _secondary_decode(
+            lambda: decode_llama2_7b_layer(block_size=32), name, steps, warmup, cpu=False),
     }
     return table[name]()
 
 
 _ONE_WORKLOAD = ("decode_gqa_shared_prefix", "decode_long_context", "decode_tiny", "prefill_chunked",
                  "prefill_chunked_fp8", "decode_llama2_7b_layer_fp8", "decode_gqa_shared_prefix_fp8",
-                 "decode_long_context_fp8", "decode_llama2_7b_layer_verify", "copy_blocks")
+                 "decode_long_context_fp8", "decode_llama2_7b_layer_verify", "copy_blocks",
+                 "decode_llama2_7b_layer_bs32")
 
 
 def _pmc_kib_per_dispatch(db_path, kernel_prefix, counter):
@@ -842,6 +849,8 @@ def main():
                                      fp8=True))
         sec.append(_secondary_prefill(s2, w2, fp8=True))
         sec.append(_secondary_multi(s2, w2))
+        sec.append(_secondary_decode(lambda: decode_llama2_7b_layer(block_size=32),
+                                     "decode_llama2_7b_layer_bs32", s2, w2, cpu=False))
         result["secondary"] = sec
     if not args.quick:
         result["achievable_copy_probe"] = _copy_probe()
