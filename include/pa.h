@@ -38,8 +38,16 @@
  * may be captured in a HIP graph.  A return of PA_OK means "enqueued";
  * faults inside kernels surface at the caller's next synchronisation.
  *
- * Errors.  Arguments are validated on the host before anything is enqueued;
- * on a negative status nothing was launched.  No C++ exception crosses this
+ * Errors.  Arguments, and the launch grids they imply, are validated on the
+ * host before anything is enqueued ("Hardware abstraction and portability",
+ * §九: unsupported configurations fail early, at the boundary): after
+ * PA_ERR_NULL_PTR, PA_ERR_UNSUPPORTED, PA_ERR_SHAPE, PA_ERR_WORKSPACE or
+ * PA_ERR_ALIGNMENT nothing was launched.  PA_ERR_HIP means the HIP runtime
+ * refused a launch; it is that launch's own status, so an error an earlier,
+ * unrelated HIP call left on the thread is neither reported as PA_ERR_HIP nor
+ * cleared.  The calls that enqueue two kernels (pa_decode, pa_decode_multi
+ * and pa_decode_fp8 when they split, pa_copy_blocks_fp8) may have enqueued the
+ * first before the runtime refused the second.  No C++ exception crosses this
  * interface.  Device-resident indices are not validated on the host (that
  * would need a read-back): a block-table entry outside [0, num_blocks) or a
  * slot outside [0, num_blocks * block_size) is never dereferenced -- the
@@ -96,8 +104,9 @@ typedef enum pa_dtype {
 uint64_t pa_kv_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_dim,
                                int32_t dtype_bytes);
 
-/* pa_status_string -- static, never-NULL description of a status code. */
-const char* pa_status_string(int32_t status);
+/* pa_status_string -- static, never-NULL description of a status code
+ * ("unknown status" for a value outside pa_status). */
+const char* pa_status_string(pa_status status);
 
 /*
  * pa_reshape_and_cache -- the cache write: store each new token's k and v in

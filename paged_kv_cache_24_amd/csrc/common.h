@@ -87,6 +87,10 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     }
 }
 
+// packed pair (1, 1) of the 16-bit type: dot2(p, kOnes2, s) adds both halves of p to s
+template <int DT>
+constexpr uint32_t kOnes2 = DT == kF16 ? 0x3C003C00u : 0x3F803F80u;
+
 // 8-element dot product of two 16-byte vectors
 template <int DT>
 __device__ __forceinline__ float dot8(const uint4& a, const uint4& b) {
@@ -213,5 +217,17 @@ __device__ __forceinline__ uint4 load_kv(const uint16_t* p) {
 }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Enqueue `kernel(a)` and return the status of that launch itself.  Every kernel
+// of the library takes one argument struct by value.  hipLaunchKernel's return
+// value belongs to this launch only: an error left on the thread by an earlier,
+// unrelated call is neither reported here nor cleared (hipGetLastError would do
+// both).
+template <typename Args>
+inline hipError_t launch(void (*kernel)(Args), dim3 grid, dim3 block, hipStream_t stream,
+                         const Args& a) {
+    void* args[] = {const_cast<Args*>(&a)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, stream);
+}
 
 }  // namespace pa

@@ -42,8 +42,7 @@ hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream) {
     const int64_t wgs = a.num_pairs * a.wgs_per_pair;
     if (wgs == 0) return hipSuccess;
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, a);
-    return hipGetLastError();
+    return launch(copy_blocks_kernel, dim3((unsigned)wgs), dim3(256), stream, a);
 }
 
 }  // namespace pa

@@ -410,7 +410,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - mu);
-        l += (p[0] + p[1]) + (p[2] + p[3]);
+        // P^T enters the PV product as 16-bit values; the row sum adds those same
+        // rounded values, so the weights that multiply V sum to exactly l
+        uint2 pb;
+        pb.x = pack2<DT>(p[0], p[1]);
+        pb.y = pack2<DT>(p[2], p[3]);
+        l = dot2<DT>(pb.y, kOnes2<DT>, dot2<DT>(pb.x, kOnes2<DT>, l));
         // V tile to LDS, rows past the sequence end as zeros (MFMA would turn 0 x NaN into NaN)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -419,9 +424,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        uint2 pb;
-        pb.x = pack2<DT>(p[0], p[1]);
-        pb.y = pack2<DT>(p[2], p[3]);
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             const ds16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -524,21 +526,17 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 template <int DT, int D, bool NT, bool MQ>
 static hipError_t launch_partitions_d(const DecodeArgs& a, hipStream_t s, dim3 grid) {
     switch (a.heads_per_wave) {
-        case 1: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 1, NT, MQ>), grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 2, NT, MQ>), grid, dim3(256), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 4, NT, MQ>), grid, dim3(256), 0, s, a); break;
-        case 8: hipLaunchKernelGGL((decode_partition_kernel<DT, D, 8, NT, MQ>), grid, dim3(256), 0, s, a); break;
+        case 1: return launch(decode_partition_kernel<DT, D, 1, NT, MQ>, grid, dim3(256), s, a);
+        case 2: return launch(decode_partition_kernel<DT, D, 2, NT, MQ>, grid, dim3(256), s, a);
+        case 4: return launch(decode_partition_kernel<DT, D, 4, NT, MQ>, grid, dim3(256), s, a);
+        case 8: return launch(decode_partition_kernel<DT, D, 8, NT, MQ>, grid, dim3(256), s, a);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 template <int DT, bool NT, bool MQ>
 static hipError_t launch_partitions_t(const DecodeArgs& a, hipStream_t s, dim3 grid) {
-    if (a.gqa_mfma) {
-        hipLaunchKernelGGL((decode_gqa_kernel<DT, NT, MQ>), grid, dim3(256), 0, s, a);
-        return hipGetLastError();
-    }
+    if (a.gqa_mfma) return launch(decode_gqa_kernel<DT, NT, MQ>, grid, dim3(256), s, a);
     return a.head_dim == 128 ? launch_partitions_d<DT, 128, NT, MQ>(a, s, grid)
                              : launch_partitions_d<DT, 64, NT, MQ>(a, s, grid);
 }
@@ -569,13 +567,11 @@ hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs);
     if (a.dtype == kF16) {
-        if (a.head_dim == 128) hipLaunchKernelGGL((decode_merge_kernel<kF16, 128>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((decode_merge_kernel<kF16, 64>), grid, dim3(256), 0, s, a);
-    } else {
-        if (a.head_dim == 128) hipLaunchKernelGGL((decode_merge_kernel<kBF16, 128>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((decode_merge_kernel<kBF16, 64>), grid, dim3(256), 0, s, a);
+        return a.head_dim == 128 ? launch(decode_merge_kernel<kF16, 128>, grid, dim3(256), s, a)
+                                 : launch(decode_merge_kernel<kF16, 64>, grid, dim3(256), s, a);
     }
-    return hipGetLastError();
+    return a.head_dim == 128 ? launch(decode_merge_kernel<kBF16, 128>, grid, dim3(256), s, a)
+                             : launch(decode_merge_kernel<kBF16, 64>, grid, dim3(256), s, a);
 }
 
 }  // namespace pa

@@ -570,20 +570,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
 template <int DT, int D, bool NT>
 static hipError_t launch_fp8_vector(const DecodeArgs& a, hipStream_t s, dim3 grid) {
     switch (a.heads_per_wave) {
-        case 1: hipLaunchKernelGGL((decode_fp8_partition_kernel<DT, D, 1, NT>), grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((decode_fp8_partition_kernel<DT, D, 2, NT>), grid, dim3(256), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((decode_fp8_partition_kernel<DT, D, 4, NT>), grid, dim3(256), 0, s, a); break;
+        case 1: return launch(decode_fp8_partition_kernel<DT, D, 1, NT>, grid, dim3(256), s, a);
+        case 2: return launch(decode_fp8_partition_kernel<DT, D, 2, NT>, grid, dim3(256), s, a);
+        case 4: return launch(decode_fp8_partition_kernel<DT, D, 4, NT>, grid, dim3(256), s, a);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 template <int DT, bool NT>
 static hipError_t launch_fp8_t(const DecodeArgs& a, hipStream_t s, dim3 grid) {
-    if (a.gqa_mfma) {
-        hipLaunchKernelGGL((decode_fp8_gqa_kernel<DT, NT, kGqaFp8Pairs>), grid, dim3(256), 0, s, a);
-        return hipGetLastError();
-    }
+    if (a.gqa_mfma) return launch(decode_fp8_gqa_kernel<DT, NT, kGqaFp8Pairs>, grid, dim3(256), s, a);
     return a.head_dim == 128 ? launch_fp8_vector<DT, 128, NT>(a, s, grid)
                              : launch_fp8_vector<DT, 64, NT>(a, s, grid);
 }

@@ -148,6 +148,15 @@ pa::DecodeArgs decode_args(void* out, const void* q, const void* k_cache, const 
     return a;
 }
 
+// Both decode phases launch one 4-wave workgroup per 4 items; their grids are
+// checked here, before either is enqueued, so that a call that fails its
+// checks has launched nothing.
+bool decode_grids_fit(const pa::DecodeArgs& a) {
+    const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * a.head_chunks * a.num_parts;
+    const int64_t rows = (int64_t)a.num_seqs * a.q_per_seq * a.num_q_heads;
+    return (items + 3) / 4 <= INT32_MAX && (rows + 3) / 4 <= INT32_MAX;
+}
+
 pa_status check_workspace(const DecodeShape& shape, const void* workspace, size_t workspace_bytes) {
     if (shape.ws_bytes == 0) return PA_OK;
     if (!workspace || workspace_bytes < shape.ws_bytes) return PA_ERR_WORKSPACE;
@@ -165,7 +174,7 @@ uint64_t pa_kv_bytes_per_token(int32_t layers, int32_t kv_heads, int32_t head_di
     return 2ull * (uint64_t)layers * (uint64_t)kv_heads * (uint64_t)head_dim * (uint64_t)dtype_bytes;
 }
 
-const char* pa_status_string(int32_t status) {
+const char* pa_status_string(pa_status status) {
     switch (status) {
         case PA_OK: return "ok";
         case PA_ERR_NULL_PTR: return "a required pointer is NULL";
@@ -274,6 +283,7 @@ pa_status pa_copy_blocks_fp8(void* k_cache, void* v_cache, float* k_scales, floa
     a.num_blocks = num_blocks;
     a.block_vecs = (int64_t)num_kv_heads * head_dim;
     a.wgs_per_pair = (a.block_vecs + 1023) / 1024;
+    if (num_pairs > INT32_MAX / a.wgs_per_pair) return PA_ERR_SHAPE;   // checked before either launch
     if (pa::launch_copy_blocks(a, stream) != hipSuccess) return PA_ERR_HIP;
     a.k_cache = k_scales;
     a.v_cache = v_scales;
@@ -324,6 +334,7 @@ pa_status pa_decode_partitions(void* out, const void* q, const void* k_cache, co
                                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                          max_blocks_per_seq, num_blocks, scale, dtype, shape,
                                          workspace, flags);
+    if (!decode_grids_fit(a)) return PA_ERR_SHAPE;
     return pa::launch_decode_partitions(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -386,6 +397,7 @@ pa_status pa_decode_partitions_fp8(void* out, const void* q, const void* k_cache
     }
     a.k_scales = k_scales;
     a.v_scales = v_scales;
+    if (!decode_grids_fit(a)) return PA_ERR_SHAPE;
     return pa::launch_decode_partitions_fp8(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -445,6 +457,7 @@ pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const v
                                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                          max_blocks_per_seq, num_blocks, scale, dtype, shape,
                                          workspace, flags, q_per_seq);
+    if (!decode_grids_fit(a)) return PA_ERR_SHAPE;
     if (pa::launch_decode_partitions(a, stream) != hipSuccess) return PA_ERR_HIP;
     if (shape.num_parts <= 1) return PA_OK;
     return pa::launch_decode_merge(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;

@@ -478,9 +478,13 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
                 for (int i = 0; i < 4; ++i) {
                     const float pv = fast_exp2(fmaf(s[mt][i], cs, nmu));
                     s[mt][i] = pv;
-                    ps += pv;
+                    if constexpr (F8) ps += pv;
                 }
-            lsum += ps;
+            // FP8: P (times the v-scale mantissa) enters PV as a 16-bit head plus a
+            // 16-bit tail, so the row sum takes the float32 p; 16-bit caches: P
+            // enters as one 16-bit value, and the row sum adds those same rounded
+            // values (below), so the weights that multiply V sum to exactly l
+            if constexpr (F8) lsum += ps;
             if constexpr (F8) {   // times the v-scale mantissa factor of each key
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
@@ -504,6 +508,11 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
                     pt[kc].y = pack2<DT>(s[2 * kc][2] - lo_to_f32<DT>(pb[kc].y), s[2 * kc][3] - hi_to_f32<DT>(pb[kc].y));
                     pt[kc].z = pack2<DT>(s[2 * kc + 1][0] - lo_to_f32<DT>(pb[kc].z), s[2 * kc + 1][1] - hi_to_f32<DT>(pb[kc].z));
                     pt[kc].w = pack2<DT>(s[2 * kc + 1][2] - lo_to_f32<DT>(pb[kc].w), s[2 * kc + 1][3] - hi_to_f32<DT>(pb[kc].w));
+                } else {
+                    lsum = dot2<DT>(pb[kc].x, kOnes2<DT>, lsum);
+                    lsum = dot2<DT>(pb[kc].y, kOnes2<DT>, lsum);
+                    lsum = dot2<DT>(pb[kc].z, kOnes2<DT>, lsum);
+                    lsum = dot2<DT>(pb[kc].w, kOnes2<DT>, lsum);
                 }
             }
 
@@ -782,7 +791,6 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
     float m = -INFINITY;            // running max of the lane's row (log2 domain, scaled)
     float lsum0 = 0.f, lsum1 = 0.f; // this lane's share of the row sum
     const float cs = a.scale_log2;
-    constexpr uint32_t kOnes = DT == kF16 ? 0x3C003C00u : 0x3F803F80u;
 
     auto qk = [&](const uint16_t* kbuf, f32x16_t (&s)[2]) __attribute__((always_inline)) {
         const char* base = reinterpret_cast<const char*>(kbuf);
@@ -916,14 +924,14 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
         }
 #pragma unroll
         for (int ks = 0; ks < 4; ks += 2) {
-            lsum0 = dot2<DT>(pb[ks].x, kOnes, lsum0);
-            lsum1 = dot2<DT>(pb[ks].y, kOnes, lsum1);
-            lsum0 = dot2<DT>(pb[ks].z, kOnes, lsum0);
-            lsum1 = dot2<DT>(pb[ks].w, kOnes, lsum1);
-            lsum0 = dot2<DT>(pb[ks + 1].x, kOnes, lsum0);
-            lsum1 = dot2<DT>(pb[ks + 1].y, kOnes, lsum1);
-            lsum0 = dot2<DT>(pb[ks + 1].z, kOnes, lsum0);
-            lsum1 = dot2<DT>(pb[ks + 1].w, kOnes, lsum1);
+            lsum0 = dot2<DT>(pb[ks].x, kOnes2<DT>, lsum0);
+            lsum1 = dot2<DT>(pb[ks].y, kOnes2<DT>, lsum1);
+            lsum0 = dot2<DT>(pb[ks].z, kOnes2<DT>, lsum0);
+            lsum1 = dot2<DT>(pb[ks].w, kOnes2<DT>, lsum1);
+            lsum0 = dot2<DT>(pb[ks + 1].x, kOnes2<DT>, lsum0);
+            lsum1 = dot2<DT>(pb[ks + 1].y, kOnes2<DT>, lsum1);
+            lsum0 = dot2<DT>(pb[ks + 1].z, kOnes2<DT>, lsum0);
+            lsum1 = dot2<DT>(pb[ks + 1].w, kOnes2<DT>, lsum1);
         }
     };
 
@@ -1014,16 +1022,13 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
 }
 
 template <int DT, bool F8, int D>
-static void launch_prefill_g(const PrefillArgs& a, hipStream_t s, dim3 grid) {
+static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t s, dim3 grid) {
     // the block shift is a template argument (a runtime one costs the 16-token
     // case measurable time); FP8 pools only come in 16-token blocks
     if constexpr (!F8) {
-        if (a.block_shift == 1) {
-            hipLaunchKernelGGL((prefill_kernel<DT, F8, D, 1>), grid, dim3(512), 0, s, a);
-            return;
-        }
+        if (a.block_shift == 1) return launch(prefill_kernel<DT, F8, D, 1>, grid, dim3(512), s, a);
     }
-    hipLaunchKernelGGL((prefill_kernel<DT, F8, D, 0>), grid, dim3(512), 0, s, a);
+    return launch(prefill_kernel<DT, F8, D, 0>, grid, dim3(512), s, a);
 }
 
 // the 16x16x32 kernel: every FP8 prefill, and 16-bit prefill at head_dim 64
@@ -1037,22 +1042,20 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)wgs);
     if (a.head_dim == 128) {
         if constexpr (F8) {
-            if (a.dtype == kF16) launch_prefill_g<kF16, F8, 128>(a, s, grid);
-            else launch_prefill_g<kBF16, F8, 128>(a, s, grid);
+            return a.dtype == kF16 ? launch_prefill_g<kF16, F8, 128>(a, s, grid)
+                                   : launch_prefill_g<kBF16, F8, 128>(a, s, grid);
         } else {
             return hipErrorInvalidValue;   // 16-bit at head_dim 128 runs prefill16_kernel
         }
-    } else {
-        if (a.dtype == kF16) launch_prefill_g<kF16, F8, 64>(a, s, grid);
-        else launch_prefill_g<kBF16, F8, 64>(a, s, grid);
     }
-    return hipGetLastError();
+    return a.dtype == kF16 ? launch_prefill_g<kF16, F8, 64>(a, s, grid)
+                           : launch_prefill_g<kBF16, F8, 64>(a, s, grid);
 }
 
 template <int DT>
-static void launch_prefill16_g(const PrefillArgs& a, hipStream_t s, dim3 grid) {
-    if (a.block_shift == 1) hipLaunchKernelGGL((prefill16_kernel<DT, 1>), grid, dim3(64 * kW16), 0, s, a);
-    else hipLaunchKernelGGL((prefill16_kernel<DT, 0>), grid, dim3(64 * kW16), 0, s, a);
+static hipError_t launch_prefill16_g(const PrefillArgs& a, hipStream_t s, dim3 grid) {
+    return a.block_shift == 1 ? launch(prefill16_kernel<DT, 1>, grid, dim3(64 * kW16), s, a)
+                              : launch(prefill16_kernel<DT, 0>, grid, dim3(64 * kW16), s, a);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
@@ -1063,9 +1066,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
     if (wgs == 0) return hipSuccess;
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs);
-    if (a.dtype == kF16) launch_prefill16_g<kF16>(a, s, grid);
-    else launch_prefill16_g<kBF16>(a, s, grid);
-    return hipGetLastError();
+    return a.dtype == kF16 ? launch_prefill16_g<kF16>(a, s, grid) : launch_prefill16_g<kBF16>(a, s, grid);
 }
 hipError_t launch_prefill_fp8(const PrefillArgs& a, hipStream_t s) { return launch_prefill_t<true>(a, s); }
 

@@ -48,9 +48,8 @@ hipError_t launch_reshape_and_cache(const ReshapeArgs& a, hipStream_t stream) {
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
     // a token row is kv_heads * head_dim / 8 vectors: 128 threads cover Hkv = 8 at D = 128
     const int threads = a.row_vecs >= 256 ? 256 : (a.row_vecs >= 128 ? 128 : 64);
-    if (big) hipLaunchKernelGGL(reshape_and_cache_kernel<4>, dim3((unsigned)wgs), dim3(threads), 0, stream, a);
-    else hipLaunchKernelGGL(reshape_and_cache_kernel<1>, dim3((unsigned)wgs), dim3(threads), 0, stream, a);
-    return hipGetLastError();
+    return big ? launch(reshape_and_cache_kernel<4>, dim3((unsigned)wgs), dim3(threads), stream, a)
+               : launch(reshape_and_cache_kernel<1>, dim3((unsigned)wgs), dim3(threads), stream, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -152,13 +151,11 @@ hipError_t launch_reshape_and_cache_fp8(const ReshapeFp8Args& a, hipStream_t str
     const int64_t want = (pairs + pairs_per_wg - 1) / pairs_per_wg;
     const dim3 grid((unsigned)(want < 65536 ? want : 65536));
     if (a.dtype == kF16) {
-        if (a.head_dim == 128) hipLaunchKernelGGL((reshape_and_cache_fp8_kernel<kF16, 128>), grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((reshape_and_cache_fp8_kernel<kF16, 64>), grid, dim3(256), 0, stream, a);
-    } else {
-        if (a.head_dim == 128) hipLaunchKernelGGL((reshape_and_cache_fp8_kernel<kBF16, 128>), grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((reshape_and_cache_fp8_kernel<kBF16, 64>), grid, dim3(256), 0, stream, a);
+        return a.head_dim == 128 ? launch(reshape_and_cache_fp8_kernel<kF16, 128>, grid, dim3(256), stream, a)
+                                 : launch(reshape_and_cache_fp8_kernel<kF16, 64>, grid, dim3(256), stream, a);
     }
-    return hipGetLastError();
+    return a.head_dim == 128 ? launch(reshape_and_cache_fp8_kernel<kBF16, 128>, grid, dim3(256), stream, a)
+                             : launch(reshape_and_cache_fp8_kernel<kBF16, 64>, grid, dim3(256), stream, a);
 }
 
 }  // namespace pa

@@ -1,11 +1,16 @@
-"""HIP-graph capture and replay of decode steps: cache write + paged decode in
-16-bit and FP8 caches, and multi-query (verification) decode.
+"""HIP-graph capture and replay of decode and prefill steps: cache write +
+paged decode in 16-bit and FP8 caches, multi-query (verification) decode,
+chunked prefill, and a decode step captured at a batch bucket and replayed
+with fewer live sequences.
 
 Graph mode keeps every tensor at a fixed address and changes only contents
-between replays, the block table included ("vLLM-Ascend 原理", §四, graph mode).
-The library never allocates, reads device memory on the host or memsets, so a
-captured step must equal the eager step on every replay, with the contents of
-q, the tables and the lengths rewritten in place between replays.
+between replays, the block table included; batches are padded up to a fixed
+bucket size ("vLLM-Ascend 原理", §四, graph mode).  The library never
+allocates, reads device memory on the host or memsets, so a captured step is
+replayable as is.  Every replay is checked twice: against the float64 oracle
+on host copies of the contents it ran on (q, k/v, tables, lengths, slots),
+at the attention tolerance and bit-exactly for the cache pools; and against
+the same step run eagerly, bit for bit.
 """
 
 import math
@@ -14,7 +19,9 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import DecodeOnGPU, dev_bits, dev_int, host_bits, require_gpu
+import oracle
+from gpu_helpers import (DecodeOnGPU, assert_close, dev_bits, dev_int, host_bits, host_f64,
+                         require_gpu)
 from workloads import make_decode_case, normal_bits
 
 pytestmark = pytest.mark.gpu
@@ -39,15 +46,29 @@ def _capture(step):
     return graph
 
 
+def _replay_then_eager(graph, step, out_graph, fresh):
+    """Replay, then run the step eagerly into a fresh buffer; both host copies."""
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    eager = fresh()
+    step(eager)
+    torch.cuda.synchronize()
+    return host_bits(out_graph).copy(), host_bits(eager)
+
+
 @pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("hq,hkv,dtype", [(8, 8, "f16"), (16, 2, "bf16")])
-def test_captured_decode_step_matches_eager(hq, hkv, dtype, bs):
+def test_captured_decode_step(hq, hkv, dtype, bs):
+    """Cache write + split decode captured once; replayed with new q, shortened
+    lengths (rollback) and two sequences trading table rows."""
     import paged_kv_cache_24_amd as pa
     lens = [300, 17, 1, 129, 64, 0]
     c = make_decode_case(name="graph", seed=21, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv,
                          head_dim=128, seq_lens=lens, num_blocks=64, max_blocks_per_seq=320 // bs,
                          scale=1 / math.sqrt(128), write_last=True, block_size=bs)
     g = DecodeOnGPU(c)
+    kc, vc = oracle.ref_reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache, c.slot_mapping)
     part = 64                                   # several partitions: exercises the merge too
     need = pa.pa_decode_workspace_size(c.num_seqs, hq, hkv, 128, bs, c.max_blocks_per_seq, part)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
@@ -64,29 +85,137 @@ def test_captured_decode_step_matches_eager(hq, hkv, dtype, bs):
     for replay in range(4):
         # new contents at the same addresses: q, lengths (a shorter sequence = rollback),
         # and block tables (two sequences trade rows)
-        g.q.copy_(dev_bits(normal_bits(rng, tuple(g.q.shape), dtype), dtype))
+        q = normal_bits(rng, tuple(g.q.shape), dtype)
+        g.q.copy_(dev_bits(q, dtype))
         new_lens = np.array(lens, np.int32)
         new_lens[0] = 300 - 7 * replay
-        g.lens.copy_(dev_int(new_lens))
         tables = c.block_tables.copy()
         if replay % 2:
             tables[[1, 3]] = tables[[3, 1]]
             new_lens[[1, 3]] = new_lens[[3, 1]]
-            g.lens.copy_(dev_int(new_lens))
+        g.lens.copy_(dev_int(new_lens))
         g.tables.copy_(dev_int(tables))
+        got, eager = _replay_then_eager(graph, step, out_graph, lambda: torch.empty_like(g.q))
+        np.testing.assert_array_equal(got, eager, err_msg=f"replay {replay}")
+        np.testing.assert_array_equal(host_bits(g.k_cache), kc, err_msg=f"replay {replay}: K pool")
+        np.testing.assert_array_equal(host_bits(g.v_cache), vc, err_msg=f"replay {replay}: V pool")
+        ref = oracle.ref_decode(q, kc, vc, tables, new_lens, c.scale, dtype)
+        assert_close(host_f64(out_graph), ref, dtype, f"replay {replay}")
+        assert not (got[new_lens == 0] & 0x7FFF).any(), "an empty sequence must give zeros"
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_bucket_padded_decode_step(fp8):
+    """A decode step captured once at a bucket of 8 sequences, then replayed
+    with 5, 8, 3 and 1 live sequences: the rows past the live ones are padding
+    with seq_len 0, slot -1 and table entries -1 (and NaN k/v, q), as graph mode
+    pads a batch up to its bucket.  Each replay writes the last token of each
+    live sequence; the pools must equal the oracle's cache write bit for bit
+    (padding writes nothing), padded output rows must be exact zeros, and live
+    rows must match the oracle's decode over the pools as they stand."""
+    import paged_kv_cache_24_amd as pa
+    bucket, dtype, hq, hkv, d = 8, "bf16", 16, 2, 128
+    full_lens = np.array([300, 17, 1, 129, 64, 33, 250, 16], np.int32)
+    c = make_decode_case(name="bucket", seed=41, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv,
+                         head_dim=d, seq_lens=full_lens, num_blocks=72, max_blocks_per_seq=20,
+                         scale=1 / math.sqrt(d), write_last=True)
+    assert len(c.slot_mapping) == bucket        # every sequence owns a last-token slot
+    nan = np.uint16(0x7FC0)
+    part = 64
+    need = pa.pa_decode_workspace_size(bucket, hq, hkv, d, 16, c.max_blocks_per_seq, part)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    # fixed-address step inputs, sized for the bucket
+    q_d = dev_bits(c.q, dtype)
+    key_d = dev_bits(c.key, dtype)
+    value_d = dev_bits(c.value, dtype)
+    slots_d = dev_int(c.slot_mapping, torch.int64)
+    tables_d = dev_int(c.block_tables)
+    lens_d = dev_int(full_lens)
+    out_graph = torch.empty_like(q_d)
+
+    if fp8:
+        # FP8 pools of every live token; the last tokens are written by the step
+        kc16, vc16 = oracle.ref_reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache,
+                                                  c.slot_mapping)
+        pre = np.setdiff1d(_live_slots(c.block_tables, full_lens), c.slot_mapping)
+        codes0 = np.full((c.num_blocks, 16, hkv, d), 0x7F, np.uint8)
+        scales0 = np.full((c.num_blocks, hkv, 16), np.nan, np.float32)
+        pools = list(oracle.ref_reshape_and_cache_fp8(
+            kc16[pre // 16, pre % 16], vc16[pre // 16, pre % 16], codes0, codes0, scales0, scales0,
+            pre, dtype))
+        kd, vd, ksd, vsd = (torch.from_numpy(x).cuda() for x in pools)
+    else:
+        pools = [c.k_cache.copy(), c.v_cache.copy()]
+        kd, vd = dev_bits(pools[0], dtype), dev_bits(pools[1], dtype)
+
+    def step(out=out_graph):
+        if fp8:
+            pa.pa_reshape_and_cache_fp8(key_d, value_d, kd, vd, ksd, vsd, slots_d)
+            pa.pa_decode_fp8(out, q_d, kd, vd, ksd, vsd, tables_d, lens_d, c.scale, part,
+                             workspace=ws)
+        else:
+            pa.pa_reshape_and_cache(key_d, value_d, kd, vd, slots_d)
+            pa.pa_decode(out, q_d, kd, vd, tables_d, lens_d, c.scale, part, workspace=ws)
+
+    # capture on an all-padding batch (nothing is written or read while capturing)
+    lens_d.zero_()
+    slots_d.fill_(-1)
+    tables_d.fill_(-1)
+    graph = _capture(step)
+
+    rng = np.random.default_rng(42)
+    for replay, live in enumerate([5, 8, 3, 1]):
+        pad = np.arange(bucket) >= live
+        q = normal_bits(rng, tuple(q_d.shape), dtype)
+        q[pad] = nan
+        key = c.key.copy()
+        value = c.value.copy()
+        key[pad] = nan
+        value[pad] = nan
+        slots = np.where(pad, -1, c.slot_mapping).astype(np.int64)
+        tables = np.where(pad[:, None], -1, c.block_tables).astype(np.int32)
+        lens = np.where(pad, 0, full_lens).astype(np.int32)
+        for dst, src in ((q_d, dev_bits(q, dtype)), (key_d, dev_bits(key, dtype)),
+                         (value_d, dev_bits(value, dtype)), (slots_d, dev_int(slots, torch.int64)),
+                         (tables_d, dev_int(tables)), (lens_d, dev_int(lens))):
+            dst.copy_(src)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        eager = torch.empty_like(g.q)
+        got = host_bits(out_graph).copy()
+        what = f"{'fp8' if fp8 else 'bf16'} replay {replay} ({live} live of {bucket})"
+        if fp8:
+            # the oracle's quantiser refuses NaN rows: hand it the live rows only
+            live_rows = ~pad
+            pools = list(oracle.ref_reshape_and_cache_fp8(key[live_rows], value[live_rows], *pools,
+                                                          slots[live_rows], dtype))
+            for name, dev, want in zip(("K codes", "V codes", "K scales", "V scales"),
+                                       (kd, vd, ksd, vsd), pools):
+                np.testing.assert_array_equal(dev.cpu().numpy(), want, err_msg=f"{what}: {name}")
+            ref = oracle.ref_decode_fp8(q, *pools, tables, lens, c.scale, dtype)
+        else:
+            pools = list(oracle.ref_reshape_and_cache(key, value, *pools, slots))
+            np.testing.assert_array_equal(host_bits(kd), pools[0], err_msg=f"{what}: K pool")
+            np.testing.assert_array_equal(host_bits(vd), pools[1], err_msg=f"{what}: V pool")
+            ref = oracle.ref_decode(q, *pools, tables, lens, c.scale, dtype)
+        assert not (got[pad] & 0x7FFF).any(), f"{what}: padded rows must be zeros"
+        assert_close(host_f64(out_graph)[~pad], ref[~pad], dtype, what)
+        eager = torch.empty_like(q_d)
         step(eager)
         torch.cuda.synchronize()
-        np.testing.assert_array_equal(host_bits(out_graph), host_bits(eager),
-                                      err_msg=f"replay {replay}")
+        np.testing.assert_array_equal(got, host_bits(eager), err_msg=f"{what}: eager")
 
 
-def test_captured_fp8_step_matches_eager():
+def _live_slots(block_tables, lens):
+    out = [block_tables[b, np.arange(int(n)) // 16].astype(np.int64) * 16 + np.arange(int(n)) % 16
+           for b, n in enumerate(lens)]
+    return np.unique(np.concatenate(out))
+
+
+def test_captured_fp8_step():
     """FP8 cache write + FP8 decode (GQA, split) captured once, replayed with new
-    q and new k/v contents; every replay equals the eager step bit for bit."""
+    q and new k contents."""
     import paged_kv_cache_24_amd as pa
     from gpu_helpers import Fp8DecodeOnGPU
     c = make_decode_case(name="graph-fp8", seed=23, dtype="bf16", num_q_heads=16, num_kv_heads=2,
@@ -106,18 +235,22 @@ def test_captured_fp8_step_matches_eager():
     graph = _capture(step)
     rng = np.random.default_rng(24)
     for replay in range(3):
-        g.q.copy_(dev_bits(normal_bits(rng, tuple(g.q.shape), "bf16"), "bf16"))
-        g.key.copy_(dev_bits(normal_bits(rng, tuple(g.key.shape), "bf16"), "bf16"))
-        torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
-        eager = torch.empty_like(g.q)
-        step(eager)
-        torch.cuda.synchronize()
-        np.testing.assert_array_equal(host_bits(out_graph), host_bits(eager), err_msg=f"replay {replay}")
+        q = normal_bits(rng, tuple(g.q.shape), "bf16")
+        key = normal_bits(rng, tuple(g.key.shape), "bf16")
+        g.q.copy_(dev_bits(q, "bf16"))
+        g.key.copy_(dev_bits(key, "bf16"))
+        got, eager = _replay_then_eager(graph, step, out_graph, lambda: torch.empty_like(g.q))
+        np.testing.assert_array_equal(got, eager, err_msg=f"replay {replay}")
+        pools = oracle.ref_reshape_and_cache_fp8(key, g.value_np, g.codes0, g.codes0, g.scales0,
+                                                 g.scales0, g.slots_np, "bf16")
+        for name, dev, want in zip(("K codes", "V codes", "K scales", "V scales"),
+                                   (g.k_cache, g.v_cache, g.k_scales, g.v_scales), pools):
+            np.testing.assert_array_equal(dev.cpu().numpy(), want, err_msg=f"replay {replay}: {name}")
+        ref = oracle.ref_decode_fp8(q, *pools, c.block_tables, c.seq_lens, c.scale, "bf16")
+        assert_close(host_f64(out_graph), ref, "bf16", f"fp8 replay {replay}")
 
 
-def test_captured_verification_step_matches_eager():
+def test_captured_verification_step():
     """Multi-query decode (4 draft queries per sequence) captured once and replayed
     with the sequence lengths shortened in place, as after rejected drafts."""
     import paged_kv_cache_24_amd as pa
@@ -139,21 +272,19 @@ def test_captured_verification_step_matches_eager():
 
     graph = _capture(step)
     for replay in range(3):
-        g.lens.copy_(dev_int(np.maximum(np.array(lens) - 3 * replay, 0).astype(np.int32)))
-        qm.copy_(dev_bits(normal_bits(rng, tuple(qm.shape), "f16"), "f16"))
-        torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
-        eager = torch.empty_like(qm)
-        step(eager)
-        torch.cuda.synchronize()
-        np.testing.assert_array_equal(host_bits(out_graph), host_bits(eager), err_msg=f"replay {replay}")
+        new_lens = np.maximum(np.array(lens) - 3 * replay, 0).astype(np.int32)
+        q = normal_bits(rng, tuple(qm.shape), "f16")
+        g.lens.copy_(dev_int(new_lens))
+        qm.copy_(dev_bits(q, "f16"))
+        got, eager = _replay_then_eager(graph, step, out_graph, lambda: torch.empty_like(qm))
+        np.testing.assert_array_equal(got, eager, err_msg=f"replay {replay}")
+        ref = oracle.ref_decode_multi(q, c.k_cache, c.v_cache, c.block_tables, new_lens, c.scale, "f16")
+        assert_close(host_f64(out_graph), ref, "f16", f"verification replay {replay}")
 
 
-def test_captured_prefill_step_matches_eager():
+def test_captured_prefill_step():
     """Cache write + chunked prefill captured once, replayed with new q and new
-    k/v and with the cached-context lengths shortened in place; every replay
-    equals the eager step bit for bit."""
+    k/v and with the cached-context lengths shortened in place."""
     import paged_kv_cache_24_amd as pa
     from gpu_helpers import PrefillOnGPU
     from workloads import make_prefill_case
@@ -172,15 +303,19 @@ def test_captured_prefill_step_matches_eager():
     graph = _capture(step)
     rng = np.random.default_rng(28)
     for replay in range(3):
-        g.q.copy_(dev_bits(normal_bits(rng, tuple(g.q.shape), "bf16"), "bf16"))
-        g.key.copy_(dev_bits(normal_bits(rng, tuple(g.key.shape), "bf16"), "bf16"))
-        g.value.copy_(dev_bits(normal_bits(rng, tuple(g.value.shape), "bf16"), "bf16"))
+        q = normal_bits(rng, tuple(g.q.shape), "bf16")
+        key = normal_bits(rng, tuple(g.key.shape), "bf16")
+        value = normal_bits(rng, tuple(g.value.shape), "bf16")
         # a shorter cached context: the rows see fewer keys (the slots written stay valid)
-        g.ctx.copy_(dev_int(np.maximum(np.array(ctx) - 16 * replay, 0).astype(np.int32)))
-        torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
-        eager = torch.zeros_like(g.q)
-        step(eager)
-        torch.cuda.synchronize()
-        np.testing.assert_array_equal(host_bits(out_graph), host_bits(eager), err_msg=f"replay {replay}")
+        new_ctx = np.maximum(np.array(ctx) - 16 * replay, 0).astype(np.int32)
+        g.q.copy_(dev_bits(q, "bf16"))
+        g.key.copy_(dev_bits(key, "bf16"))
+        g.value.copy_(dev_bits(value, "bf16"))
+        g.ctx.copy_(dev_int(new_ctx))
+        got, eager = _replay_then_eager(graph, step, out_graph, lambda: torch.zeros_like(g.q))
+        np.testing.assert_array_equal(got, eager, err_msg=f"replay {replay}")
+        kc, vc = oracle.ref_reshape_and_cache(key, value, c.k_cache, c.v_cache, c.slot_mapping)
+        np.testing.assert_array_equal(host_bits(g.k_cache), kc, err_msg=f"replay {replay}: K pool")
+        ref = oracle.ref_prefill_paged(q, kc, vc, c.block_tables, new_ctx, c.query_start_loc,
+                                       c.scale, "bf16")
+        assert_close(host_f64(out_graph), ref, "bf16", f"prefill replay {replay}")
