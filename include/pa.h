@@ -73,7 +73,8 @@ typedef enum pa_status {
     PA_ERR_SHAPE = -3,       /* inconsistent or out-of-range sizes */
     PA_ERR_WORKSPACE = -4,   /* decode workspace missing or too small */
     PA_ERR_HIP = -5,         /* the HIP runtime refused a launch */
-    PA_ERR_ALIGNMENT = -6    /* a tensor or the workspace is not 16-byte aligned */
+    PA_ERR_ALIGNMENT = -6,   /* a tensor or the workspace is not 16-byte aligned */
+    PA_ERR_SCRATCH = -7      /* pa_decode_noalloc: partials exceed PA_NOALLOC_SCRATCH_BYTES */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -211,6 +212,33 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
                     float scale, pa_dtype dtype, int32_t partition_tokens, uint32_t flags,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments minus the workspace, the same kernels
+ * and the same results bit for bit.  The split-KV partial states go to a
+ * static scratch array inside the library, PA_NOALLOC_SCRATCH_BYTES (64 MiB)
+ * per GPU, held by every GPU the library runs on until the process ends.  The
+ * call itself allocates nothing; on its first call on a device it looks up
+ * that device's copy of the array (the device current on the calling
+ * thread, which must be the stream's device).
+ *
+ * A shape whose partials need more than PA_NOALLOC_SCRATCH_BYTES
+ * (pa_decode_workspace_size) gives PA_ERR_SCRATCH before anything is
+ * enqueued; PA_ERR_HIP if the device or the array's address cannot be
+ * queried.  All calls on one GPU share its scratch: calls that overlap in
+ * time on one GPU (different streams, or host threads, without ordering
+ * between them) race and give undefined results.  Calls ordered on a stream
+ * are safe; nothing needs clearing between them.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                            float scale, pa_dtype dtype, int32_t partition_tokens, uint32_t flags,
+                            hipStream_t stream);
 
 /*
  * pa_decode_multi -- paged decode with several new queries per sequence, as

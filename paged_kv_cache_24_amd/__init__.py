@@ -10,7 +10,8 @@ Names follow the C ABI: ``pa_reshape_and_cache``, ``pa_copy_blocks``, ``pa_decod
 ``pa_decode_workspace_size``, ``pa_decode_default_partition``,
 ``pa_kv_bytes_per_token``, ``pa_status_string``, and for an FP8 (E4M3) cache
 ``pa_reshape_and_cache_fp8``, ``pa_copy_blocks_fp8``, ``pa_decode_fp8``,
-``pa_decode_partitions_fp8``, ``pa_prefill_paged_fp8``.
+``pa_decode_partitions_fp8``, ``pa_prefill_paged_fp8``, and ``pa_decode_noalloc`` for
+callers that cannot allocate (its split-KV partials live in a static scratch).
 """
 
 from __future__ import annotations
@@ -26,12 +27,13 @@ __all__ = [
     "pa_decode_default_partition", "pa_decode_workspace_size", "pa_decode",
     "pa_decode_partitions", "pa_decode_merge", "pa_prefill_paged",
     "pa_reshape_and_cache_fp8", "pa_copy_blocks_fp8", "pa_decode_fp8", "pa_decode_partitions_fp8",
-    "pa_prefill_paged_fp8", "pa_decode_multi",
+    "pa_prefill_paged_fp8", "pa_decode_multi", "pa_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 BLOCK_SIZE = 16
 PA_DECODE_STREAM_KV = 1   # no physical block is read twice in the call: stream K/V
+NOALLOC_SCRATCH_BYTES = 64 << 20   # PA_NOALLOC_SCRATCH_BYTES: static scratch of pa_decode_noalloc
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -54,6 +56,8 @@ _SIGS = {
                          _f32, _i32, _i32, _u32, _vp, _sz, _vp]),
     "pa_decode_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _i64, _f32, _i32, _i32, _u32, _vp, _sz, _vp]),
+    "pa_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                 _i64, _f32, _i32, _i32, _u32, _vp]),
     "pa_decode_multi": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                _i64, _f32, _i32, _i32, _u32, _vp, _sz, _vp]),
     "pa_decode_merge": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz,
@@ -209,6 +213,19 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, partition
     _check("pa_decode", lib.pa_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), b, hq,
         hkv, d, bs, mb, nb, float(scale), _kv_dtype(k_cache), partition_tokens, flags, _ptr(ws), ws_bytes,
+        _stream(stream)))
+    return out
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, seq_lens, scale, partition_tokens=0,
+                      stream=None, flags=0):
+    """``pa_decode`` without a workspace: the split-KV partials go to the library's
+    static per-GPU scratch (``NOALLOC_SCRATCH_BYTES``), so nothing is allocated.
+    Calls that overlap in time on one GPU race on that scratch."""
+    nb, bs, hkv, d, b, hq, mb = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens)
+    _check("pa_decode_noalloc", lib.pa_decode_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), b, hq,
+        hkv, d, bs, mb, nb, float(scale), _kv_dtype(k_cache), partition_tokens, flags,
         _stream(stream)))
     return out
 

@@ -6,13 +6,42 @@
 // No call reads device memory, synchronises or allocates, so each call is
 // capturable in a HIP graph; the decode workspace is owned by the caller.
 #include <algorithm>
+#include <atomic>
 #include <math.h>
+#include <mutex>
 #include <stdint.h>
 
 #include "kernels.h"
 #include "pa.h"
 
+// Static scratch of pa_decode_noalloc: the split-KV partial states of callers
+// that cannot allocate.  Every GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: its device address is looked up once per device with
+// hipGetSymbolAddress, and only that address is ever handed to a kernel.
+static __device__ __align__(256) float scratch[PA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of the current device's scratch copy, or nullptr when the
+// device cannot be queried or the symbol cannot be resolved.
+void* scratch_address() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* ptr = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (ptr) return ptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    ptr = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch_addr[dev].store(ptr, std::memory_order_release);
+    }
+    return ptr;
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -183,6 +212,9 @@ const char* pa_status_string(pa_status status) {
         case PA_ERR_WORKSPACE: return "decode workspace missing or too small";
         case PA_ERR_HIP: return "the HIP runtime refused a kernel launch";
         case PA_ERR_ALIGNMENT: return "a tensor or the workspace is not 16-byte aligned";
+        case PA_ERR_SCRATCH:
+            return "split-KV partial results exceed the static scratch of pa_decode_noalloc "
+                   "(PA_NOALLOC_SCRATCH_BYTES); use pa_decode with a caller workspace";
         default: return "unknown status";
     }
 }
@@ -478,6 +510,34 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
     return pa_decode_merge(out, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                            block_size, max_blocks_per_seq, dtype, partition_tokens, workspace,
                            workspace_bytes, stream);
+}
+
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                            float scale, pa_dtype dtype, int32_t partition_tokens, uint32_t flags,
+                            hipStream_t stream) {
+    if (flags & ~PA_DECODE_STREAM_KV) return PA_ERR_UNSUPPORTED;
+    const pa_status st = check_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+                                      num_q_heads, num_kv_heads, head_dim, block_size,
+                                      max_blocks_per_seq, num_blocks, scale, dtype,
+                                      partition_tokens);
+    if (st != PA_OK || num_seqs == 0) return st;
+    const DecodeShape shape = decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                           max_blocks_per_seq << block_shift(block_size),
+                                           partition_tokens);
+    if (shape.ws_bytes > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_SCRATCH;
+    // The partition kernel writes every partial state the merge reads, so the
+    // scratch needs no clearing between calls.
+    void* ws = nullptr;
+    if (shape.ws_bytes) {
+        ws = scratch_address();
+        if (!ws) return PA_ERR_HIP;
+    }
+    return pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale, dtype,
+                     partition_tokens, flags, ws, ws ? PA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 static pa_status prefill_common(void* out, const void* q, const void* k_cache, const void* v_cache,

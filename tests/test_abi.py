@@ -11,7 +11,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pa.h")
 LIB = os.path.join(ROOT, "paged_kv_cache_24_amd", "libpa.so")
 
-PA_OK, NULL, UNSUP, SHAPE, WS, HIP, ALIGN = 0, -1, -2, -3, -4, -5, -6
+PA_OK, NULL, UNSUP, SHAPE, WS, HIP, ALIGN, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
 F16, BF16 = 0, 1
 
 
@@ -33,7 +33,8 @@ def test_header_declares_the_calls():
               "pa_kv_bytes_per_token", "pa_status_string", "pa_decode_partitions",
               "pa_decode_merge", "pa_decode_default_partition", "pa_copy_blocks",
               "pa_reshape_and_cache_fp8", "pa_copy_blocks_fp8", "pa_decode_fp8",
-              "pa_decode_partitions_fp8", "pa_prefill_paged_fp8", "pa_decode_multi"]:
+              "pa_decode_partitions_fp8", "pa_prefill_paged_fp8", "pa_decode_multi",
+              "pa_decode_noalloc"]:
         assert n in names
 
 
@@ -53,9 +54,10 @@ def test_kv_bytes_per_token(lib):
 def test_status_strings(lib):
     f = lib.pa_status_string
     f.restype = ctypes.c_char_p
-    for s in (PA_OK, NULL, UNSUP, SHAPE, WS, HIP, ALIGN, 7):
+    for s in (PA_OK, NULL, UNSUP, SHAPE, WS, HIP, ALIGN, SCRATCH, 7):
         assert f(s)
     assert f(PA_OK) == b"ok"
+    assert b"scratch" in f(SCRATCH) and f(7) == b"unknown status"
 
 
 P = ctypes.c_void_p
@@ -336,3 +338,31 @@ def test_decode_merge_rejects(lib):
     assert call(bs=32, mb=32, ws=None) == WS      # the same 1024 tokens in 32-token blocks
     assert call(bs=32, mb=4, ws=None) == PA_OK    # 128 tokens: one partition, nothing to merge
     assert call(b=0, out=None) == PA_OK
+
+
+def _decode_noalloc(lib, out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, b=4, hq=8, hkv=2,
+                    d=128, bs=16, mb=16, nb=64, scale=0.088, dt=F16, part=0, flags=0):
+    f = lib.pa_decode_noalloc
+    f.restype = ctypes.c_int32
+    f.argtypes = [P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_uint32, P]
+    return f(out, q, kc, vc, bt, sl, b, hq, hkv, d, bs, mb, nb, scale, dt, part, flags, None)
+
+
+def test_decode_noalloc_rejects(lib):
+    """pa_decode's checks, then the static scratch limit, all before any HIP call."""
+    ws = lib.pa_decode_workspace_size
+    ws.restype = ctypes.c_size_t
+    ws.argtypes = [ctypes.c_int32] * 7
+    limit = 64 << 20   # PA_NOALLOC_SCRATCH_BYTES
+    assert _decode_noalloc(lib, q=None) == NULL
+    assert _decode_noalloc(lib, d=80) == UNSUP
+    assert _decode_noalloc(lib, flags=2) == UNSUP
+    assert _decode_noalloc(lib, hq=6, hkv=4) == SHAPE
+    assert _decode_noalloc(lib, out=FAKE + 8) == ALIGN
+    assert _decode_noalloc(lib, b=0, q=None) == PA_OK
+    # 4096 sequences x 64 q heads in 256-token partitions of 4096-block tables:
+    # far more partials than the scratch holds
+    assert ws(4096, 64, 8, 128, 16, 4096, 256) > limit
+    assert _decode_noalloc(lib, b=4096, hq=64, hkv=8, mb=4096, nb=40000, part=256) == SCRATCH
