@@ -115,9 +115,12 @@ class DecodeRun:
         self.tables = _i(case.block_tables)
         self.lens = _i(case.seq_lens)
         self.out = torch.empty_like(self.q)
-        self.part = partition_tokens or pa.pa_decode_default_partition(
-            case.num_q_heads, case.num_kv_heads, case.head_dim, case.block_size,
-            case.max_blocks_per_seq)
+        # 0: the library's default split (the balanced split where fixed partitions
+        # would need several rounds of waves); `split` records which one it makes
+        self.part = partition_tokens
+        split = pa.pa_decode_split(case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim,
+                                   case.block_size, case.max_blocks_per_seq, self.part)
+        self.split = "balanced" if split == pa.PA_PARTITION_BALANCED else f"partitions of {split} tokens"
         need = pa.pa_decode_workspace_size(case.num_seqs, case.num_q_heads, case.num_kv_heads,
                                            case.head_dim, case.block_size, case.max_blocks_per_seq,
                                            self.part)
@@ -362,7 +365,7 @@ def _secondary_decode(builder, name, steps, warmup, note=None, cpu=True, fp8=Fal
     dec_ms = per["partitions"] + per["merge"]
     res = {"workload": name, "ms_per_step": round(wall, 4), "decode_ms": round(dec_ms, 4),
            "partition_kernel_ms": round(per["partitions"], 4), "merge_ms": round(per["merge"], 4),
-           "partition_tokens": run.part, "block_size": case.block_size,
+           "split": run.split, "block_size": case.block_size,
            "stream_kv": bool(run.flags), "kv_bytes": kv,
            "kv_GBs": round(kv / (dec_ms * 1e-3) / 1e9, 1),
            "pct_hbm_peak": round(100 * kv / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
@@ -715,7 +718,7 @@ def _traffic_profile(root):
             raise SystemExit(f"expected one results database under {os.path.join(root, sub)}, found {hits}")
         return hits[0]
 
-    kern = "void pa::decode_partition_kernel<0, 128, 1, true, false>"
+    kern = "void pa::decode_balanced_kernel<0, 128, 1, true>"
     copy = "__amd_rocclr_copyBuffer"
     f_dec, n_f = _pmc_kib_per_dispatch(db("dec_FETCH_SIZE"), kern, "FETCH_SIZE")
     w_dec, n_w = _pmc_kib_per_dispatch(db("dec_WRITE_SIZE"), kern, "WRITE_SIZE")
@@ -730,7 +733,7 @@ def _traffic_profile(root):
     qo = 2 * case.num_seqs * case.num_q_heads * case.head_dim * 2
     algo = kv + qo + int(((lens + 15) // 16).sum()) * 4
     out = {
-        "kernel": "decode_partition_kernel<f16,128,1,stream> on decode_llama2_7b_layer (partition 512 tokens)",
+        "kernel": "decode_balanced_kernel<f16,128,1,stream> on decode_llama2_7b_layer (balanced split)",
         "decode_hip_sha256": hashlib.sha256(open(DECODE_SOURCE, "rb").read()).hexdigest(),
         "fetch_size_kib_per_launch": round(f_dec, 1), "write_size_kib_per_launch": round(w_dec, 1),
         "dispatches": [n_f, n_w],
@@ -805,12 +808,14 @@ def main():
                    "head_dim": case.head_dim, "block_size": 16,
                    "seq_lens": "uniform int [512, 4096], seed 2",
                    "num_blocks": case.num_blocks, "kv_bytes": kv,
-                   "partition_tokens": run.part, "stream_kv": bool(run.flags),
+                   "split": run.split, "stream_kv": bool(run.flags),
                    "step": "cache write of 64 tokens + paged decode (partitions + merge)"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
         "tokens_per_s": round(case.num_seqs / (wall_ms * 1e-3), 1),
         "kernel_ms": {k: round(v, 4) for k, v in per.items()},
-        "roofline": {"bound": "hbm", "kernel": "decode_partition_kernel<f16,128,1>",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("decode_balanced_kernel<f16,128,1>" if run.split == "balanced"
+                                else "decode_partition_kernel<f16,128,1>"),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes_per_launch": algo,

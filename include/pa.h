@@ -97,6 +97,24 @@ typedef enum pa_dtype {
 #define PA_DECODE_STREAM_KV 1u
 
 /*
+ * Split-KV work split of the decode calls (their partition_tokens argument).
+ *   > 0  fixed partitions of that many tokens (a multiple of 16): one wave per
+ *        (sequence, kv head, q-head chunk, partition), states merged by length.
+ *   0    library default: the balanced split when fixed partitions of the
+ *        default length would need more than one round of resident waves (a
+ *        mix of lengths then leaves the last round to a few long sequences),
+ *        else those fixed partitions.
+ *   PA_PARTITION_BALANCED  the balanced split: the blocks of all sequences,
+ *        one after another, are cut into equal stretches, each read by one
+ *        wave per kv head (and q-head chunk), so every wave gets the same
+ *        work whatever the mix of lengths.  Single-query calls with at most
+ *        512 sequences only; otherwise PA_ERR_SHAPE.
+ * The split changes float32 rounding only: the online-softmax merge of
+ * partial states is exact ("vLLM-Ascend 原理", §四 "ATB 算子").
+ */
+#define PA_PARTITION_BALANCED (-1)
+
+/*
  * pa_kv_bytes_per_token -- K+V bytes one token occupies over all layers:
  * 2 * layers * kv_heads * head_dim * dtype_bytes ("vLLM-Ascend 原理", §2.1,
  * the KV size formula).  Pure host arithmetic; returns 0 if any argument is
@@ -153,7 +171,8 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pair
 
 /*
  * pa_decode_default_partition -- the split-KV partition length, in tokens, that
- * pa_decode uses when given partition_tokens == 0 (a power of two >= 256).  It
+ * pa_decode uses when given partition_tokens == 0 and the default is fixed
+ * partitions rather than the balanced split (a power of two >= 256).  It
  * depends only on host-known sizes: about max_blocks_per_seq * block_size / 8,
  * capped at 2048 tokens where decode runs on matrix cores (head_dim 128 and 3
  * or more q heads per kv head) and at 512 otherwise; 256 for invalid
@@ -166,11 +185,21 @@ int32_t pa_decode_default_partition(int32_t num_q_heads, int32_t num_kv_heads, i
                                     int32_t block_size, int32_t max_blocks_per_seq);
 
 /*
- * pa_decode_workspace_size -- bytes of float32 partial results pa_decode needs
- * for this shape and partition length (0 = default).  0 when every sequence
- * fits one partition.  Layout (internal to the library): per (sequence,
- * q head, partition) a running max, a running sum and head_dim accumulators.
- * Also 0 for a block_size other than 16 or 32 or other invalid sizes.
+ * pa_decode_split -- the split a single-query decode call (pa_decode,
+ * pa_decode_fp8, pa_decode_noalloc) of this shape makes for partition_tokens:
+ * its partition length in tokens, or PA_PARTITION_BALANCED for the balanced
+ * split; 0 for invalid arguments.  Host arithmetic only.
+ */
+int32_t pa_decode_split(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int32_t max_blocks_per_seq, int32_t partition_tokens);
+
+/*
+ * pa_decode_workspace_size -- bytes of float32 partial results the decode calls
+ * (16-bit and FP8) need for this shape and split (partition_tokens as for
+ * pa_decode).  0 when every sequence fits one partition.  Layout (internal to
+ * the library): per partial state a running max, a running sum and head_dim
+ * accumulators.  Also 0 for a block_size other than 16 or 32 or other invalid
+ * sizes.
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
@@ -193,8 +222,8 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  *                 max_blocks_per_seq * block_size are clamped to it.
  *   scale         softmax scale applied to q.k (natural-base softmax); must be
  *                 positive and finite.
- *   partition_tokens  split-KV partition length (multiple of 16), or 0 for
- *                 pa_decode_default_partition().
+ *   partition_tokens  split-KV work split: a partition length (multiple of
+ *                 16), 0 for the library default or PA_PARTITION_BALANCED.
  *   flags         0 or PA_DECODE_STREAM_KV; other bits give PA_ERR_UNSUPPORTED.
  *   workspace     device buffer of at least pa_decode_workspace_size() bytes
  *                 (may be NULL when that size is 0), 16-byte aligned.
@@ -276,9 +305,11 @@ pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const v
  * pa_decode_partitions / pa_decode_merge -- the two phases of pa_decode, for
  * callers that schedule or time them separately.  Same arguments and
  * contract as pa_decode; the arguments the two calls share must be identical.
- * pa_decode_partitions writes the final output of every sequence that fits
- * one partition and the partial state of the others; pa_decode_merge
- * combines the partial states (a no-op when nothing was split).
+ * pa_decode_partitions writes the final output of every sequence one
+ * partition (or one stretch of the balanced split) covers whole, and partial
+ * states for the others; pa_decode_merge combines the partial states and, in
+ * the balanced split, writes the zero rows of empty sequences (a no-op when
+ * nothing was split).
  */
 pa_status pa_decode_partitions(void* out, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_tables,

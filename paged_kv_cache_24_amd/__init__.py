@@ -22,9 +22,9 @@ import os
 import torch
 
 __all__ = [
-    "PagedKVError", "LIB_PATH", "BLOCK_SIZE", "PA_DECODE_STREAM_KV", "lib",
+    "PagedKVError", "LIB_PATH", "BLOCK_SIZE", "PA_DECODE_STREAM_KV", "PA_PARTITION_BALANCED", "lib",
     "pa_kv_bytes_per_token", "pa_status_string", "pa_reshape_and_cache", "pa_copy_blocks",
-    "pa_decode_default_partition", "pa_decode_workspace_size", "pa_decode",
+    "pa_decode_default_partition", "pa_decode_split", "pa_decode_workspace_size", "pa_decode",
     "pa_decode_partitions", "pa_decode_merge", "pa_prefill_paged",
     "pa_reshape_and_cache_fp8", "pa_copy_blocks_fp8", "pa_decode_fp8", "pa_decode_partitions_fp8",
     "pa_prefill_paged_fp8", "pa_decode_multi", "pa_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
@@ -33,6 +33,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 BLOCK_SIZE = 16
 PA_DECODE_STREAM_KV = 1   # no physical block is read twice in the call: stream K/V
+PA_PARTITION_BALANCED = -1   # partition_tokens value: the balanced split of decode work
 NOALLOC_SCRATCH_BYTES = 64 << 20   # PA_NOALLOC_SCRATCH_BYTES: static scratch of pa_decode_noalloc
 
 if not os.path.exists(LIB_PATH):
@@ -52,6 +53,7 @@ _SIGS = {
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i32, _vp]),
     "pa_decode_default_partition": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "pa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_split": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i64,
                          _f32, _i32, _i32, _u32, _vp, _sz, _vp]),
     "pa_decode_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -168,6 +170,14 @@ def pa_decode_default_partition(num_q_heads: int, num_kv_heads: int, head_dim: i
                                 block_size: int, max_blocks_per_seq: int) -> int:
     return int(lib.pa_decode_default_partition(num_q_heads, num_kv_heads, head_dim, block_size,
                                                max_blocks_per_seq))
+
+
+def pa_decode_split(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                    partition_tokens=0) -> int:
+    """Partition length (tokens) a single-query decode of this shape uses, or
+    ``PA_PARTITION_BALANCED`` for the balanced split; 0 for invalid arguments."""
+    return int(lib.pa_decode_split(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                   max_blocks_per_seq, partition_tokens))
 
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,

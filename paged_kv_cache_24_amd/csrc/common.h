@@ -218,6 +218,186 @@ __device__ __forceinline__ uint4 load_kv(const uint16_t* p) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// ------------------------------------------------------- decode work order
+// A decode wave's work item: one partition of one (sequence, kv head, q-head
+// chunk) unit.  Items are numbered partition-major, so that every sequence's
+// first partitions run first and the empty items of short sequences (partitions
+// past their end) cluster at the end of the grid; then by sequence, kv head and
+// head chunk, so that adjacent workgroups read all kv heads of a block -- one
+// contiguous stretch of the pool -- at about the same time.
+//
+// When blocks may be shared (no PA_DECODE_STREAM_KV: a prefix held once for a
+// group of consecutive sequences), the workgroup index is also permuted so
+// that runs of kXcdRun consecutive workgroups execute on one XCD: the
+// dispatcher deals workgroup x to XCD x % 8, and each XCD has its own L2, so
+// the sequences of a run read a shared block through one L2 instead of
+// several.  The XCD of a run rotates by one from each round of eight runs to
+// the next, so that no XCD is tied to the same sequences in every partition.
+constexpr int kXcds = 8;
+constexpr int kXcdRun = 32;
+
+// Workgroup index after the XCD-run permutation above (identity when NT).
+template <bool NT>
+__device__ __forceinline__ int64_t decode_workgroup() {
+    int64_t x = blockIdx.x;
+    if constexpr (!NT) {
+        constexpr int64_t R = (int64_t)kXcds * kXcdRun;
+        if (x < (int64_t)(gridDim.x / R) * R) {   // whole rounds of R workgroups; the rest unpermuted
+            const int64_t t = x / kXcds;
+            const int64_t round = t / kXcdRun;
+            // run (round, slot) executes on XCD (slot + round) % 8
+            const int64_t slot = (x % kXcds - round % kXcds + kXcds) % kXcds;
+            x = round * R + slot * kXcdRun + t % kXcdRun;
+        }
+    }
+    return x;
+}
+
+struct DecodeItem {
+    int part, b, g, hc;
+};
+
+template <bool NT>
+__device__ __forceinline__ bool decode_item(const DecodeArgs& a, int wave, DecodeItem& it) {
+    const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.head_chunks;
+    const int64_t item = decode_workgroup<NT>() * 4 + wave;
+    if (item >= units * a.num_parts) return false;
+    it.part = (int)(item / units);
+    int64_t u = item - (int64_t)it.part * units;
+    it.hc = (int)(u % a.head_chunks);
+    u /= a.head_chunks;
+    it.g = (int)(u % a.num_kv_heads);
+    it.b = (int)(u / a.num_kv_heads);
+    return true;
+}
+
+// Tokens of sequence b, clamped to what its table row can name.
+__device__ __forceinline__ int seq_tokens(const DecodeArgs& a, int b) {
+    const int max_tokens = a.max_blocks_per_seq * kBlockSize;
+    const int n = a.seq_lens[b];
+    return n < 0 ? 0 : (n > max_tokens ? max_tokens : n);
+}
+
+__device__ __forceinline__ int ceil_blocks(int n) { return (n + kBlockSize - 1) / kBlockSize; }
+
+// Sum over the 64 lanes; every lane gets it.
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+// Inclusive prefix sum over the lanes in lane order.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        x += lane >= off ? y : 0;
+    }
+    return x;
+}
+
+// ------------------------------------------- balanced split of decode work
+// The blocks of all sequences form one stream, sequence after sequence, T =
+// sum_b ceil(n_b / 16) blocks.  It is cut into S = num_items / upb equal
+// stretches of C = ceil(T / S) blocks (at least kMinStretch), and stretch s is
+// processed by upb = num_kv_heads * head_chunks adjacent waves, one per unit
+// (kv head, q-head chunk): wave w = s * upb + ui.  Every wave gets the same
+// work whatever the mix of lengths, where fixed partitions leave the grid's
+// last round to the longest sequences; and the waves that read one block are
+// neighbours, so all kv heads of a block -- one contiguous stretch of the pool
+// -- leave HBM together.  T and the sequence holding a stretch's first block
+// come from a prefix sum of the lengths, a wave-wide scan of seq_lens in
+// device memory: nothing is read on the host, so the launch is capturable.
+//
+// The part of one sequence that one stretch covers is a segment.  A segment
+// that is the whole sequence is finished in place; every other one leaves the
+// partial state of unit ui in slot (b + s) * upb + ui, which is unique: the
+// segments of one sequence fall in consecutive stretches, and a later sequence
+// starts in the stretch where the previous one ends or after it.  Slots
+// therefore number fewer than (num_seqs + S) * upb.
+constexpr int kMinStretch = 16;
+constexpr int kStretchStride = 1;
+
+__device__ __forceinline__ int balanced_stretch(const DecodeArgs& a, int total) {
+    const int stretches = a.num_items / (a.num_kv_heads * a.head_chunks);
+    const int c = (total + stretches - 1) / stretches;
+    return c > kMinStretch ? c : kMinStretch;
+}
+
+// Blocks of the whole stream (every lane gets the sum); with `prefix`, also
+// the blocks of the sequences before `before`.
+__device__ __forceinline__ int stream_blocks(const DecodeArgs& a, int before, int* prefix) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int total = 0, pre = 0;
+    for (int base = 0; base < a.num_seqs; base += kWave) {
+        const int i = base + lane;
+        const int nb = i < a.num_seqs ? ceil_blocks(seq_tokens(a, i)) : 0;
+        total += wave_sum(nb);
+        if (prefix) pre += wave_sum(i < before ? nb : 0);
+    }
+    if (prefix) *prefix = uniform(pre);
+    return uniform(total);
+}
+
+// Calls segment(b, g, hc, n, j0, j1, whole, slot) for every segment of this
+// wave's stretch, in stream order: blocks j0 .. j1-1 of unit (b, g, hc) of a
+// sequence of n tokens; whole = the segment is the entire sequence.
+template <bool NT, typename Segment>
+__device__ __forceinline__ void balanced_walk(const DecodeArgs& a, int wave, Segment&& segment) {
+    const int upb = a.num_kv_heads * a.head_chunks;
+    const int64_t w = decode_workgroup<NT>() * 4 + wave;
+    const int64_t nst = a.num_items / upb;
+    int64_t st = w / upb;   // stretch, in dispatch order
+    const int ui = (int)(w - st * upb);
+    if (st >= nst) return;
+    if constexpr (kStretchStride > 1) {   // dispatch order i -> stretch (i % Q) * F + i / Q
+        const int64_t f = nst / kStretchStride;
+        if (st < f * kStretchStride) st = (st % kStretchStride) * f + st / kStretchStride;
+    }
+    const int lane = threadIdx.x & (kWave - 1);
+    const int total = stream_blocks(a, 0, nullptr);
+    const int stretch = balanced_stretch(a, total);
+    const int64_t lo = st * stretch;
+    if (lo >= total) return;
+    int s = (int)lo;
+    const int s1 = (int)min((int64_t)total, lo + stretch);
+    // the sequence b holding block s, and the stream position pb of its first block
+    int b = 0, pb = 0, run = 0;
+    for (int base = 0; base < a.num_seqs; base += kWave) {
+        const int i = base + lane;
+        const int nb = i < a.num_seqs ? ceil_blocks(seq_tokens(a, i)) : 0;
+        const int incl = wave_inclusive_scan(nb);
+        const int sum = uniform(__shfl(incl, kWave - 1));
+        if (run + sum > s) {
+            const unsigned long long hit = __ballot(run + incl > s);
+            const int f = __ffsll(hit) - 1;
+            b = base + f;
+            pb = run + __shfl(incl - nb, f);
+            break;
+        }
+        run += sum;
+    }
+    b = uniform(b);
+    pb = uniform(pb);
+    const int g = ui / a.head_chunks;
+    const int hc = ui - g * a.head_chunks;
+    while (s < s1 && b < a.num_seqs) {
+        const int n = seq_tokens(a, b);
+        const int nblk = ceil_blocks(n);
+        if (s >= pb + nblk) {   // past this sequence (also skips empty ones)
+            pb += nblk;
+            ++b;
+            continue;
+        }
+        const int j0 = s - pb;
+        const int j1 = min(nblk, j0 + (s1 - s));
+        segment(b, g, hc, n, j0, j1, j0 == 0 && j1 == nblk, ((int64_t)b + st) * upb + ui);
+        s += j1 - j0;
+    }
+}
+
 // Enqueue `kernel(a)` and return the status of that launch itself.  Every kernel
 // of the library takes one argument struct by value.  hipLaunchKernel's return
 // value belongs to this launch only: an error left on the thread by an earlier,

@@ -30,10 +30,16 @@
 
 namespace pa {
 
+// Blocks j0 .. j1-1 of unit (b, g, hc) -- sequence b, kv head g, q-head chunk
+// hc, n tokens -- for one wave: the online softmax over them, then the final
+// output (final_out) or the partial state, in slot qrow * num_parts + slot
+// (fixed partitions: slot = partition) or slot * state_heads + h (balanced
+// split, slot from balanced_walk).
 // MQ: several queries per sequence (see decode_gqa_kernel); the columns of a
 // kv head are (query, q head) pairs and each sees keys up to its own position.
-template <int DT, int D, int HPW, bool NT, bool MQ>
-__global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
+template <int DT, int D, int HPW, bool NT, bool MQ, bool BAL>
+__device__ __forceinline__ void vector_segment(const DecodeArgs& a, int b, int g, int hc, int n,
+                                               int j0, int j1, bool final_out, int64_t slot) {
     constexpr int LPR = D / 8;              // lanes per token row
     constexpr int RPW = kWave / LPR;        // token rows per load instruction
     constexpr int TPL = kBlockSize / RPW;   // token rows per lane per block
@@ -41,25 +47,6 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     const int r = lane / LPR;
     const int c = lane % LPR;
-
-    const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.head_chunks;
-    const int64_t item = (int64_t)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
-    if (item >= units * a.num_parts) return;
-    const int part = (int)(item / units);
-    int64_t u = item - (int64_t)part * units;
-    const int hc = (int)(u % a.head_chunks);
-    u /= a.head_chunks;
-    const int g = (int)(u % a.num_kv_heads);
-    const int b = (int)(u / a.num_kv_heads);
-
-    const int max_tokens = a.max_blocks_per_seq * kBlockSize;
-    int n = a.seq_lens[b];
-    n = n < 0 ? 0 : (n > max_tokens ? max_tokens : n);
-    const int nblk = (n + kBlockSize - 1) / kBlockSize;
-    const int nparts = nblk <= a.part_blocks ? 1 : (nblk + a.part_blocks - 1) / a.part_blocks;
-    if (part >= nparts) return;
-    const int j0 = part * a.part_blocks;
-    const int j1 = min(nblk, j0 + a.part_blocks);
 
     const int hbase = hc * HPW;
     const int hcount = min(HPW, (MQ ? a.cols : a.group) - hbase);
@@ -216,7 +203,7 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
     }
 
     if (r != 0) return;
-    if (nparts == 1) {
+    if (final_out) {
 #pragma unroll
         for (int h = 0; h < HPW; ++h) {
             if (h >= hcount) break;
@@ -232,13 +219,36 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
         for (int h = 0; h < HPW; ++h) {
             if (h >= hcount) break;
-            const int64_t idx = qrow[h] * a.num_parts + part;
+            const int64_t idx = BAL ? slot * a.state_heads + h : qrow[h] * a.num_parts + slot;
             float4* dst = reinterpret_cast<float4*>(a.ws_acc + idx * D + 8 * c);
             dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
             dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
             if (c == 0) a.ws_ml[idx] = make_float2(m[h], l[h]);
         }
     }
+}
+
+// Fixed partitions: one wave per (partition, unit) item.
+template <int DT, int D, int HPW, bool NT, bool MQ>
+__global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
+    DecodeItem it;
+    if (!decode_item<NT>(a, uniform(threadIdx.x >> 6), it)) return;
+    const int n = seq_tokens(a, it.b);
+    const int nblk = ceil_blocks(n);
+    const int nparts = nblk <= a.part_blocks ? 1 : (nblk + a.part_blocks - 1) / a.part_blocks;
+    if (it.part >= nparts) return;
+    const int j0 = it.part * a.part_blocks;
+    vector_segment<DT, D, HPW, NT, MQ, false>(a, it.b, it.g, it.hc, n, j0, min(nblk, j0 + a.part_blocks),
+                                              nparts == 1, it.part);
+}
+
+// Balanced split: each wave an equal stretch of the stream of all units' blocks.
+template <int DT, int D, int HPW, bool NT>
+__global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeArgs a) {
+    balanced_walk<NT>(a, uniform(threadIdx.x >> 6),
+                      [&](int b, int g, int hc, int n, int j0, int j1, bool whole, int64_t slot) {
+                          vector_segment<DT, D, HPW, NT, false, true>(a, b, g, hc, n, j0, j1, whole, slot);
+                      });
 }
 
 // ---------------------------------------------------------------------------
@@ -298,34 +308,18 @@ constexpr int kVRow = 144;   // LDS row stride of the V tile (elements): 288 B s
 // checked in one pass).  Column c of the kv head is query c / group and q head
 // c % group; query jq sits at position n - Q + jq and sees keys up to it, so
 // each K/V tile is read once for every query of the sequence.
-template <int DT, bool NT, bool MQ>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void decode_gqa_kernel(DecodeArgs a) {
+//
+// gqa_segment: blocks j0 .. j1-1 of unit (b, g, hc) for one wave, `vt` its V
+// tile in LDS; the final output (final_out) or the partial state of column lr
+// in slot my_row * num_parts + slot (fixed partitions) or
+// slot * state_heads + lr (balanced split).
+template <int DT, bool NT, bool MQ, bool BAL>
+__device__ __forceinline__ void gqa_segment(const DecodeArgs& a, uint16_t* vt, int b, int g, int hc, int n,
+                                            int j0, int j1, bool final_out, int64_t slot) {
     constexpr int D = 128;
-    __shared__ __attribute__((aligned(16))) uint16_t vlds[4][kBlockSize * kVRow];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = uniform(threadIdx.x >> 6);
     const int lr = lane & 15;    // MFMA column = q head; V column chunk; V^T row
     const int lg = lane >> 4;    // token group: tokens 4*i + lg of each block
-    uint16_t* vt = vlds[wave];
-
-    const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.head_chunks;
-    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-    if (item >= units * a.num_parts) return;
-    const int part = (int)(item / units);
-    int64_t u = item - (int64_t)part * units;
-    const int hc = (int)(u % a.head_chunks);
-    u /= a.head_chunks;
-    const int g = (int)(u % a.num_kv_heads);
-    const int b = (int)(u / a.num_kv_heads);
-
-    const int max_tokens = a.max_blocks_per_seq * kBlockSize;
-    int n = a.seq_lens[b];
-    n = n < 0 ? 0 : (n > max_tokens ? max_tokens : n);
-    const int nblk = (n + kBlockSize - 1) / kBlockSize;
-    const int nparts = nblk <= a.part_blocks ? 1 : (nblk + a.part_blocks - 1) / a.part_blocks;
-    if (part >= nparts) return;
-    const int j0 = part * a.part_blocks;
-    const int j1 = min(nblk, j0 + a.part_blocks);
     const int hcount = min(16, (MQ ? a.cols : a.group) - hc * 16);
     const bool head_live = lr < hcount;
     // q / out row of this lane's column, and (MQ) the keys the column may see
@@ -454,7 +448,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
 
     const float lt = xor32_sum(xor16_sum(l));
     if (!head_live) return;
-    if (nparts == 1) {
+    if (final_out) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         uint16_t* dst = static_cast<uint16_t*>(a.out) + my_row * D + 4 * lg;
 #pragma unroll
@@ -465,7 +459,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
             *reinterpret_cast<uint2*>(dst + 16 * mt) = w;
         }
     } else {
-        const int64_t idx = my_row * a.num_parts + part;
+        const int64_t idx = BAL ? slot * a.state_heads + lr : my_row * a.num_parts + slot;
         float* dst = a.ws_acc + idx * D + 4 * lg;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
@@ -474,12 +468,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     }
 }
 
-// Combine the partition states of one (sequence, q head):
+template <int DT, bool NT, bool MQ>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void decode_gqa_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t vlds[4][kBlockSize * kVRow];
+    const int wave = uniform(threadIdx.x >> 6);
+    DecodeItem it;
+    if (!decode_item<NT>(a, wave, it)) return;
+    const int n = seq_tokens(a, it.b);
+    const int nblk = ceil_blocks(n);
+    const int nparts = nblk <= a.part_blocks ? 1 : (nblk + a.part_blocks - 1) / a.part_blocks;
+    if (it.part >= nparts) return;
+    const int j0 = it.part * a.part_blocks;
+    gqa_segment<DT, NT, MQ, false>(a, vlds[wave], it.b, it.g, it.hc, n, j0, min(nblk, j0 + a.part_blocks),
+                                   nparts == 1, it.part);
+}
+
+template <int DT, bool NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void decode_gqa_balanced_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t vlds[4][kBlockSize * kVRow];
+    const int wave = uniform(threadIdx.x >> 6);
+    balanced_walk<NT>(a, wave, [&](int b, int g, int hc, int n, int j0, int j1, bool whole, int64_t slot) {
+        gqa_segment<DT, NT, false, true>(a, vlds[wave], b, g, hc, n, j0, j1, whole, slot);
+    });
+}
+
+// Combine the partial states of one (sequence, q head):
 // out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p with M = max_p m_p.
 // One wave per output row (sequence, query, q head); lane i owns elements
 // D/64 * i ..: the max and the denominator are wave reductions over the
-// partitions' (m, l), the numerator one pass over the partial rows -- no LDS,
-// no barrier, so the merge costs little more than reading the partials.
+// partial states' (m, l), the numerator one pass over the partial rows -- no
+// LDS, no barrier, so the merge costs little more than reading the partials.
+// Fixed partitions: the row's states are slots row * num_parts + p.  Balanced
+// split: sequence b covers stream blocks [P, P + nblk), so stretches
+// s0 = P / C .. s1 = (P + nblk - 1) / C left the state of the row's unit ui in
+// slots ((b + s) * upb + ui) * state_heads + h; a row whose sequence one stretch
+// covered whole was finished there, and a row of an empty sequence, which no
+// stretch covers, gets its zeros here.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     constexpr int EPL = D / kWave;   // elements per lane
@@ -487,21 +511,46 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     const int64_t item = (int64_t)blockIdx.x * 4 + uniform(threadIdx.x >> 6);   // q / out row
     if (item >= (int64_t)a.num_seqs * a.q_per_seq * a.num_q_heads) return;
     const int b = (int)(item / ((int64_t)a.q_per_seq * a.num_q_heads));
+    uint16_t* dst = static_cast<uint16_t*>(a.out) + item * D + EPL * lane;
 
-    const int max_tokens = a.max_blocks_per_seq * kBlockSize;
-    int n = a.seq_lens[b];
-    n = n < 0 ? 0 : (n > max_tokens ? max_tokens : n);
-    const int nblk = (n + kBlockSize - 1) / kBlockSize;
-    const int nparts = nblk <= a.part_blocks ? 1 : (nblk + a.part_blocks - 1) / a.part_blocks;
-    if (nparts <= 1) return;   // finished by the partition kernel
+    const int n = seq_tokens(a, b);
+    const int nblk = ceil_blocks(n);
+    int64_t base;
+    int stride, count;
+    if (a.balanced) {
+        if (nblk == 0) {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) dst[e] = 0;
+            return;
+        }
+        const int head = (int)(item % a.num_q_heads);
+        const int g = head / a.group;
+        const int hc = (head - g * a.group) / a.heads_per_wave;
+        const int h = head - g * a.group - hc * a.heads_per_wave;
+        const int upb = a.num_kv_heads * a.head_chunks;
+        int before;
+        const int total = stream_blocks(a, b, &before);
+        const int stretch = balanced_stretch(a, total);
+        const int s0 = before / stretch;
+        const int s1 = (before + nblk - 1) / stretch;
+        if (s0 == s1) return;   // one stretch covered the whole sequence
+        base = (((int64_t)b + s0) * upb + g * a.head_chunks + hc) * a.state_heads + h;
+        stride = upb * a.state_heads;
+        count = s1 - s0 + 1;
+    } else {
+        const int nparts = nblk <= a.part_blocks ? 1 : (nblk + a.part_blocks - 1) / a.part_blocks;
+        if (nparts <= 1) return;   // finished by the partition kernel
+        base = item * a.num_parts;
+        stride = 1;
+        count = nparts;
+    }
 
-    const int64_t base = item * a.num_parts;
     float big = -INFINITY;
-    for (int p = lane; p < nparts; p += kWave) big = fmaxf(big, a.ws_ml[base + p].x);
+    for (int p = lane; p < count; p += kWave) big = fmaxf(big, a.ws_ml[base + (int64_t)p * stride].x);
     big = xor32_max(xor16_max(group_max<16>(big)));
     float den = 0.f;
-    for (int p = lane; p < nparts; p += kWave) {
-        const float2 ml = a.ws_ml[base + p];
+    for (int p = lane; p < count; p += kWave) {
+        const float2 ml = a.ws_ml[base + (int64_t)p * stride];
         den = fmaf(ml.x == -INFINITY ? 0.f : fast_exp2(ml.x - big), ml.y, den);
     }
     den = xor32_sum(xor16_sum(group_sum<16>(den)));
@@ -511,14 +560,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     for (int e = 0; e < EPL; ++e) num[e] = 0.f;
     const float* acc = a.ws_acc + base * D + EPL * lane;
 #pragma unroll 4
-    for (int p = 0; p < nparts; ++p) {
-        const float mp = a.ws_ml[base + p].x;   // the same address in every lane
+    for (int p = 0; p < count; ++p) {
+        const float mp = a.ws_ml[base + (int64_t)p * stride].x;   // the same address in every lane
         const float w = mp == -INFINITY ? 0.f : fast_exp2(mp - big);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, acc[(int64_t)p * D + e], num[e]);
+        for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, acc[(int64_t)p * stride * D + e], num[e]);
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
-    uint16_t* dst = static_cast<uint16_t*>(a.out) + item * D + EPL * lane;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) dst[e] = f32_to_bits<DT>(num[e] * inv);
 }
@@ -551,7 +599,32 @@ static hipError_t launch_partitions_mq(const DecodeArgs& a, hipStream_t s, dim3 
                        : launch_partitions_t<kBF16, false, MQ>(a, s, grid);
 }
 
+template <int DT, int D, bool NT>
+static hipError_t launch_balanced_d(const DecodeArgs& a, hipStream_t s, dim3 grid) {
+    switch (a.heads_per_wave) {
+        case 1: return launch(decode_balanced_kernel<DT, D, 1, NT>, grid, dim3(256), s, a);
+        case 2: return launch(decode_balanced_kernel<DT, D, 2, NT>, grid, dim3(256), s, a);
+        case 4: return launch(decode_balanced_kernel<DT, D, 4, NT>, grid, dim3(256), s, a);
+        case 8: return launch(decode_balanced_kernel<DT, D, 8, NT>, grid, dim3(256), s, a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int DT, bool NT>
+static hipError_t launch_balanced_t(const DecodeArgs& a, hipStream_t s, dim3 grid) {
+    if (a.gqa_mfma) return launch(decode_gqa_balanced_kernel<DT, NT>, grid, dim3(256), s, a);
+    return a.head_dim == 128 ? launch_balanced_d<DT, 128, NT>(a, s, grid)
+                             : launch_balanced_d<DT, 64, NT>(a, s, grid);
+}
+
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t s) {
+    if (a.balanced) {
+        if (a.q_per_seq != 1 || a.num_items <= 0) return hipErrorInvalidValue;
+        const dim3 grid((unsigned)((a.num_items + 3) / 4));
+        if (a.dtype == kF16)
+            return a.stream_kv ? launch_balanced_t<kF16, true>(a, s, grid) : launch_balanced_t<kF16, false>(a, s, grid);
+        return a.stream_kv ? launch_balanced_t<kBF16, true>(a, s, grid) : launch_balanced_t<kBF16, false>(a, s, grid);
+    }
     const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * a.head_chunks * a.num_parts;
     if (items == 0) return hipSuccess;
     const int64_t wgs = (items + 3) / 4;
@@ -562,7 +635,7 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {
     const int64_t items = (int64_t)a.num_seqs * a.q_per_seq * a.num_q_heads;
-    if (items == 0 || a.num_parts <= 1) return hipSuccess;
+    if (items == 0 || (!a.balanced && a.num_parts <= 1)) return hipSuccess;
     const int64_t wgs = (items + 3) / 4;   // one wave per row
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs);

@@ -47,8 +47,13 @@ __device__ __forceinline__ void codes16_to_16bit(const uint4& c, uint4& lo, uint
 // over the row's lanes with DPP, then scaled by k_scale.  PV: codes become
 // float32 and meet p * v_scale in float32 FMAs.
 // ---------------------------------------------------------------------------
-template <int DT, int D, int HPW, bool NT>
-__global__ __launch_bounds__(256) void decode_fp8_partition_kernel(DecodeArgs a) {
+//
+// fp8_vector_segment: blocks j0 .. j1-1 of unit (b, g, hc) for one wave; the
+// final output (final_out) or the partial state in slot row * num_parts + slot
+// (fixed partitions) or slot * state_heads + h (balanced split), as in decode.hip.
+template <int DT, int D, int HPW, bool NT, bool BAL>
+__device__ __forceinline__ void fp8_vector_segment(const DecodeArgs& a, int b, int g, int hc, int n,
+                                                   int j0, int j1, bool final_out, int64_t slot) {
     constexpr int LPR = D / 16;             // lanes per token row
     constexpr int RPW = kWave / LPR;        // token rows per load instruction
     constexpr int TPL = kBlockSize / RPW;   // tokens per lane per block
@@ -58,25 +63,6 @@ __global__ __launch_bounds__(256) void decode_fp8_partition_kernel(DecodeArgs a)
     const int lane = threadIdx.x & (kWave - 1);
     const int r = lane / LPR;
     const int c = lane % LPR;
-
-    const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.head_chunks;
-    const int64_t item = (int64_t)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
-    if (item >= units * a.num_parts) return;
-    const int part = (int)(item / units);
-    int64_t u = item - (int64_t)part * units;
-    const int hc = (int)(u % a.head_chunks);
-    u /= a.head_chunks;
-    const int g = (int)(u % a.num_kv_heads);
-    const int b = (int)(u / a.num_kv_heads);
-
-    const int max_tokens = a.max_blocks_per_seq * kBlockSize;
-    int n = a.seq_lens[b];
-    n = n < 0 ? 0 : (n > max_tokens ? max_tokens : n);
-    const int nblk = (n + kBlockSize - 1) / kBlockSize;
-    const int nparts = nblk <= a.part_blocks ? 1 : (nblk + a.part_blocks - 1) / a.part_blocks;
-    if (part >= nparts) return;
-    const int j0 = part * a.part_blocks;
-    const int j1 = min(nblk, j0 + a.part_blocks);
 
     const int hbase = hc * HPW;
     const int hcount = min(HPW, a.group - hbase);
@@ -243,7 +229,7 @@ __global__ __launch_bounds__(256) void decode_fp8_partition_kernel(DecodeArgs a)
     }
 
     if (r != 0) return;
-    if (nparts == 1) {
+    if (final_out) {
 #pragma unroll
         for (int h = 0; h < HPW; ++h) {
             if (h >= hcount) break;
@@ -265,7 +251,7 @@ __global__ __launch_bounds__(256) void decode_fp8_partition_kernel(DecodeArgs a)
 #pragma unroll
         for (int h = 0; h < HPW; ++h) {
             if (h >= hcount) break;
-            const int64_t idx = (q_row0 + h) * a.num_parts + part;
+            const int64_t idx = BAL ? slot * a.state_heads + h : (q_row0 + h) * a.num_parts + slot;
             float4* dst = reinterpret_cast<float4*>(a.ws_acc + idx * D + 16 * c);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -273,6 +259,27 @@ __global__ __launch_bounds__(256) void decode_fp8_partition_kernel(DecodeArgs a)
             if (c == 0) a.ws_ml[idx] = make_float2(m[h], l[h]);
         }
     }
+}
+
+template <int DT, int D, int HPW, bool NT>
+__global__ __launch_bounds__(256) void decode_fp8_partition_kernel(DecodeArgs a) {
+    DecodeItem it;
+    if (!decode_item<NT>(a, uniform(threadIdx.x >> 6), it)) return;
+    const int n = seq_tokens(a, it.b);
+    const int nblk = ceil_blocks(n);
+    const int nparts = nblk <= a.part_blocks ? 1 : (nblk + a.part_blocks - 1) / a.part_blocks;
+    if (it.part >= nparts) return;
+    const int j0 = it.part * a.part_blocks;
+    fp8_vector_segment<DT, D, HPW, NT, false>(a, it.b, it.g, it.hc, n, j0, min(nblk, j0 + a.part_blocks),
+                                              nparts == 1, it.part);
+}
+
+template <int DT, int D, int HPW, bool NT>
+__global__ __launch_bounds__(256) void decode_fp8_balanced_kernel(DecodeArgs a) {
+    balanced_walk<NT>(a, uniform(threadIdx.x >> 6),
+                      [&](int b, int g, int hc, int n, int j0, int j1, bool whole, int64_t slot) {
+                          fp8_vector_segment<DT, D, HPW, NT, true>(a, b, g, hc, n, j0, j1, whole, slot);
+                      });
 }
 
 // ---------------------------------------------------------------------------
@@ -329,35 +336,21 @@ constexpr int kVRowF8 = 144;   // LDS row stride of a widened V tile (16-bit ele
 // pair at a time with 4 resident waves (122 registers) hiding each other's loads.
 constexpr int kGqaFp8Pairs = 1;
 
-template <int DT, bool NT, int NBUF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_fp8_gqa_kernel(DecodeArgs a) {
+//
+// fp8_gqa_segment: blocks j0 .. j1-1 of unit (b, g, hc) for one wave, `vt` its
+// two V tiles in LDS; the final output (final_out) or the partial state of
+// column lr in slot row * num_parts + slot (fixed partitions) or
+// slot * state_heads + lr (balanced split).
+constexpr int kFp8Tile = kBlockSize * kVRowF8;
+
+template <int DT, bool NT, int NBUF, bool BAL>
+__device__ __forceinline__ void fp8_gqa_segment(const DecodeArgs& a, uint16_t* vt, int b, int g, int hc, int n,
+                                                int j0, int j1, bool final_out, int64_t slot) {
     constexpr int D = 128;
-    constexpr int kTile = kBlockSize * kVRowF8;
-    __shared__ __attribute__((aligned(16))) uint16_t vlds[4][2 * kTile];
+    constexpr int kTile = kFp8Tile;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = uniform(threadIdx.x >> 6);
     const int lr = lane & 15;    // MFMA column = q head; token of the K rows; V^T row
     const int lg = lane >> 4;    // tokens 4*lg .. 4*lg+3 of each block
-    uint16_t* vt = vlds[wave];
-
-    const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * a.head_chunks;
-    const int64_t item = (int64_t)blockIdx.x * 4 + wave;
-    if (item >= units * a.num_parts) return;
-    const int part = (int)(item / units);
-    int64_t u = item - (int64_t)part * units;
-    const int hc = (int)(u % a.head_chunks);
-    u /= a.head_chunks;
-    const int g = (int)(u % a.num_kv_heads);
-    const int b = (int)(u / a.num_kv_heads);
-
-    const int max_tokens = a.max_blocks_per_seq * kBlockSize;
-    int n = a.seq_lens[b];
-    n = n < 0 ? 0 : (n > max_tokens ? max_tokens : n);
-    const int nblk = (n + kBlockSize - 1) / kBlockSize;
-    const int nparts = nblk <= a.part_blocks ? 1 : (nblk + a.part_blocks - 1) / a.part_blocks;
-    if (part >= nparts) return;
-    const int j0 = part * a.part_blocks;
-    const int j1 = min(nblk, j0 + a.part_blocks);
     const int hcount = min(16, a.group - hc * 16);
     const int64_t q_row0 = (int64_t)b * a.num_q_heads + (int64_t)g * a.group + hc * 16;
     const bool head_live = lr < hcount;
@@ -547,7 +540,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
 
     const float lt = xor32_sum(xor16_sum(l));
     if (!head_live) return;
-    if (nparts == 1) {
+    if (final_out) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         uint16_t* dst = static_cast<uint16_t*>(a.out) + (q_row0 + lr) * D + 4 * lg;
 #pragma unroll
@@ -558,13 +551,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
             *reinterpret_cast<uint2*>(dst + 16 * mt) = w;
         }
     } else {
-        const int64_t idx = (q_row0 + lr) * a.num_parts + part;
+        const int64_t idx = BAL ? slot * a.state_heads + lr : (q_row0 + lr) * a.num_parts + slot;
         float* dst = a.ws_acc + idx * D + 4 * lg;
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
             *reinterpret_cast<float4*>(dst + 16 * mt) = make_float4(o[mt][0], o[mt][1], o[mt][2], o[mt][3]);
         if (lg == 0) a.ws_ml[idx] = make_float2(m, lt);
     }
+}
+
+template <int DT, bool NT, int NBUF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_fp8_gqa_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t vlds[4][2 * kFp8Tile];
+    const int wave = uniform(threadIdx.x >> 6);
+    DecodeItem it;
+    if (!decode_item<NT>(a, wave, it)) return;
+    const int n = seq_tokens(a, it.b);
+    const int nblk = ceil_blocks(n);
+    const int nparts = nblk <= a.part_blocks ? 1 : (nblk + a.part_blocks - 1) / a.part_blocks;
+    if (it.part >= nparts) return;
+    const int j0 = it.part * a.part_blocks;
+    fp8_gqa_segment<DT, NT, NBUF, false>(a, vlds[wave], it.b, it.g, it.hc, n, j0,
+                                         min(nblk, j0 + a.part_blocks), nparts == 1, it.part);
+}
+
+template <int DT, bool NT, int NBUF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_fp8_gqa_balanced_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t vlds[4][2 * kFp8Tile];
+    const int wave = uniform(threadIdx.x >> 6);
+    balanced_walk<NT>(a, wave, [&](int b, int g, int hc, int n, int j0, int j1, bool whole, int64_t slot) {
+        fp8_gqa_segment<DT, NT, NBUF, true>(a, vlds[wave], b, g, hc, n, j0, j1, whole, slot);
+    });
+}
+
+template <int DT, int D, bool NT>
+static hipError_t launch_fp8_balanced_vector(const DecodeArgs& a, hipStream_t s, dim3 grid) {
+    switch (a.heads_per_wave) {
+        case 1: return launch(decode_fp8_balanced_kernel<DT, D, 1, NT>, grid, dim3(256), s, a);
+        case 2: return launch(decode_fp8_balanced_kernel<DT, D, 2, NT>, grid, dim3(256), s, a);
+        case 4: return launch(decode_fp8_balanced_kernel<DT, D, 4, NT>, grid, dim3(256), s, a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int DT, bool NT>
+static hipError_t launch_fp8_balanced_t(const DecodeArgs& a, hipStream_t s, dim3 grid) {
+    if (a.gqa_mfma) return launch(decode_fp8_gqa_balanced_kernel<DT, NT, kGqaFp8Pairs>, grid, dim3(256), s, a);
+    return a.head_dim == 128 ? launch_fp8_balanced_vector<DT, 128, NT>(a, s, grid)
+                             : launch_fp8_balanced_vector<DT, 64, NT>(a, s, grid);
 }
 
 template <int DT, int D, bool NT>
@@ -585,6 +619,15 @@ static hipError_t launch_fp8_t(const DecodeArgs& a, hipStream_t s, dim3 grid) {
 }
 
 hipError_t launch_decode_partitions_fp8(const DecodeArgs& a, hipStream_t s) {
+    if (a.balanced) {
+        if (a.q_per_seq != 1 || a.num_items <= 0) return hipErrorInvalidValue;
+        const dim3 grid((unsigned)((a.num_items + 3) / 4));
+        if (a.dtype == kF16)
+            return a.stream_kv ? launch_fp8_balanced_t<kF16, true>(a, s, grid)
+                               : launch_fp8_balanced_t<kF16, false>(a, s, grid);
+        return a.stream_kv ? launch_fp8_balanced_t<kBF16, true>(a, s, grid)
+                           : launch_fp8_balanced_t<kBF16, false>(a, s, grid);
+    }
     const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * a.head_chunks * a.num_parts;
     if (items == 0) return hipSuccess;
     const int64_t wgs = (items + 3) / 4;

@@ -82,6 +82,11 @@ struct DecodeArgs {
     // is query c / group, q head c % group; 1 and group for plain decode
     int32_t q_per_seq;
     int32_t cols;
+    // balanced split (single query): the waves share the blocks of all units
+    // evenly instead of taking fixed partitions; num_items = waves launched
+    int32_t balanced;
+    int32_t num_items;
+    int32_t state_heads;     // balanced: head slots per partial-state slot, min(heads_per_wave, cols)
 };
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_partitions_fp8(const DecodeArgs& a, hipStream_t stream);

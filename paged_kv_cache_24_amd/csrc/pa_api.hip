@@ -90,26 +90,85 @@ int32_t default_partition(int32_t num_q_heads, int32_t num_kv_heads, int32_t hea
     return p;
 }
 
+// Balanced split of single-query decode (see balanced_walk in common.h): the
+// waves launched, one round of the 16-bit decode kernels at 3 resident waves
+// per SIMD (160 and 131 VGPRs) on 256 CUs x 4 SIMDs, so every wave has the same
+// share of the work and no second round runs behind a few long sequences.
+constexpr int32_t kBalancedWaves = 3072;
+constexpr int32_t kBalancedWavesMfma = 3072;
+// each wave scans seq_lens, 64 sequences per pass: at most 8 passes
+constexpr int32_t kBalancedMaxSeqs = 512;
+
 struct DecodeShape {
+    bool valid;          // false: partition_tokens asks for a split this call cannot make
     int32_t part_tokens;
     int32_t num_parts;
+    bool balanced;
+    int32_t num_items;   // balanced: waves launched
     size_t ws_bytes;
 };
 
-// max_blocks16: 16-token blocks per sequence
+// q heads one wave of the decode kernels carries, for `cols` columns
+// (query, q head pairs) per kv head.  The balanced split numbers its units by
+// head chunks, and its merge runs after the 16-bit and the FP8 kernels alike,
+// so it takes chunks both carry: 16 on matrix cores, else at most 4.
+int32_t decode_wave_heads(int32_t cols, int32_t head_dim, bool balanced) {
+    if (head_dim == 128 && cols >= 3) return 16;
+    return balanced ? std::min(heads_per_wave(cols), 4) : heads_per_wave(cols);
+}
+
+// max_blocks16: 16-token blocks per sequence.  may_balance: a single-query
+// call (the balanced split has no multi-query form).
+//   partition_tokens > 0: fixed partitions of that length.
+//   partition_tokens == 0: the balanced split when fixed partitions of the
+//     default length would need more items than one round of resident waves
+//     (kBalancedWaves) -- then a few long sequences would run alone in the last
+//     round -- otherwise the default partitions, already a single round.
+//   PA_PARTITION_BALANCED: the balanced split (not valid for multi-query calls
+//     or more than kBalancedMaxSeqs sequences).
 DecodeShape decode_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                         int32_t head_dim, int32_t max_blocks16, int32_t partition_tokens) {
+                         int32_t head_dim, int32_t max_blocks16, int32_t partition_tokens,
+                         bool may_balance) {
     DecodeShape s;
-    s.part_tokens = partition_tokens > 0
-                        ? partition_tokens
-                        : default_partition(num_q_heads, num_kv_heads, head_dim, max_blocks16);
-    const int32_t part_blocks = s.part_tokens / 16;
-    s.num_parts = max_blocks16 <= part_blocks ? 1 : ceil_div(max_blocks16, part_blocks);
-    if (s.num_parts <= 1) {
-        s.ws_bytes = 0;
-    } else {
-        const size_t states = (size_t)num_seqs * num_q_heads * s.num_parts;
+    s.valid = true;
+    s.part_tokens = 0;
+    s.num_parts = 0;
+    s.balanced = false;
+    s.num_items = 0;
+    s.ws_bytes = 0;
+    const int32_t group = num_q_heads / num_kv_heads;
+    if (partition_tokens >= 0) {
+        s.part_tokens = partition_tokens > 0
+                            ? partition_tokens
+                            : default_partition(num_q_heads, num_kv_heads, head_dim, max_blocks16);
+        const int32_t part_blocks = s.part_tokens / 16;
+        s.num_parts = max_blocks16 <= part_blocks ? 1 : ceil_div(max_blocks16, part_blocks);
+        if (s.num_parts <= 1) {
+            s.ws_bytes = 0;
+        } else {
+            const size_t states = (size_t)num_seqs * num_q_heads * s.num_parts;
+            s.ws_bytes = states * ((size_t)head_dim * sizeof(float) + 2 * sizeof(float));
+        }
+        if (partition_tokens > 0) return s;
+    }
+    const int64_t part_items = partition_tokens == 0
+        ? (int64_t)num_seqs * num_kv_heads * ceil_div(group, decode_wave_heads(group, head_dim, false)) * s.num_parts
+        : 0;
+    const bool want = partition_tokens == PA_PARTITION_BALANCED || part_items > kBalancedWaves;
+    const int32_t hpw = decode_wave_heads(group, head_dim, true);
+    const int64_t upb = (int64_t)num_kv_heads * ceil_div(group, hpw);   // waves per stretch
+    const int64_t stretches = (hpw == 16 ? kBalancedWavesMfma : kBalancedWaves) / upb;
+    const bool can = may_balance && num_seqs <= kBalancedMaxSeqs && stretches >= 1 &&
+                     (int64_t)num_seqs * max_blocks16 <= INT32_MAX;
+    if (want && can) {
+        s.balanced = true;
+        s.num_items = (int32_t)(stretches * upb);
+        s.part_tokens = 0;
+        s.num_parts = 0;
+        const size_t states = (size_t)(num_seqs + stretches) * upb * std::min(hpw, group);
         s.ws_bytes = states * ((size_t)head_dim * sizeof(float) + 2 * sizeof(float));
+    } else if (partition_tokens == PA_PARTITION_BALANCED) {
+        s.valid = false;
     }
     return s;
 }
@@ -124,7 +183,8 @@ pa_status check_decode(const void* out, const void* q, const void* k_cache, cons
         return PA_ERR_UNSUPPORTED;
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
         num_blocks <= 0 || num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > kMaxGroup ||
-        partition_tokens < 0 || partition_tokens % 16 != 0 || !(scale > 0.f) || !isfinite(scale) ||
+        (partition_tokens != PA_PARTITION_BALANCED && (partition_tokens < 0 || partition_tokens % 16 != 0)) ||
+        !(scale > 0.f) || !isfinite(scale) ||
         (int64_t)max_blocks_per_seq * block_size > INT32_MAX || num_blocks > (INT64_C(1) << (31 - sh)))
         return PA_ERR_SHAPE;
     if (num_seqs == 0) return PA_OK;
@@ -156,7 +216,7 @@ pa::DecodeArgs decode_args(void* out, const void* q, const void* k_cache, const 
     a.cols = q_per_seq * a.group;   // (query, q head) columns per kv head
     // 3 or more columns per kv head make QK^T and PV real contractions: matrix cores
     a.gqa_mfma = head_dim == 128 && a.cols >= 3;
-    a.heads_per_wave = a.gqa_mfma ? 16 : heads_per_wave(a.cols);
+    a.heads_per_wave = decode_wave_heads(a.cols, head_dim, shape.balanced);
     a.k_scales = nullptr;
     a.v_scales = nullptr;
     a.head_chunks = ceil_div(a.cols, a.heads_per_wave);
@@ -170,8 +230,14 @@ pa::DecodeArgs decode_args(void* out, const void* q, const void* k_cache, const 
     a.scale_log2 = scale * kLog2e;
     a.dtype = dtype == PA_F16 ? pa::kF16 : pa::kBF16;
     a.stream_kv = (flags & PA_DECODE_STREAM_KV) != 0;
+    a.balanced = shape.balanced;
+    a.num_items = shape.num_items;
+    a.state_heads = std::min(a.heads_per_wave, a.cols);
     float* ws = static_cast<float*>(workspace);
-    const size_t states = (size_t)num_seqs * q_per_seq * num_q_heads * shape.num_parts;
+    const size_t upb = (size_t)num_kv_heads * a.head_chunks;
+    const size_t states =
+        shape.balanced ? ((size_t)num_seqs + shape.num_items / upb) * upb * a.state_heads
+                       : (size_t)num_seqs * q_per_seq * num_q_heads * shape.num_parts;
     a.ws_acc = shape.ws_bytes ? ws : nullptr;
     a.ws_ml = shape.ws_bytes ? reinterpret_cast<float2*>(ws + states * head_dim) : nullptr;
     return a;
@@ -181,7 +247,8 @@ pa::DecodeArgs decode_args(void* out, const void* q, const void* k_cache, const 
 // checked here, before either is enqueued, so that a call that fails its
 // checks has launched nothing.
 bool decode_grids_fit(const pa::DecodeArgs& a) {
-    const int64_t items = (int64_t)a.num_seqs * a.num_kv_heads * a.head_chunks * a.num_parts;
+    const int64_t items = a.balanced ? a.num_items
+                                     : (int64_t)a.num_seqs * a.num_kv_heads * a.head_chunks * a.num_parts;
     const int64_t rows = (int64_t)a.num_seqs * a.q_per_seq * a.num_q_heads;
     return (items + 3) / 4 <= INT32_MAX && (rows + 3) / 4 <= INT32_MAX;
 }
@@ -333,16 +400,34 @@ int32_t pa_decode_default_partition(int32_t num_q_heads, int32_t num_kv_heads, i
     return default_partition(num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq << sh);
 }
 
+int32_t pa_decode_split(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int32_t max_blocks_per_seq, int32_t partition_tokens) {
+    const int32_t sh = block_shift(block_size);
+    if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 ||
+        (head_dim != 64 && head_dim != 128) || sh < 0 || max_blocks_per_seq <= 0 ||
+        max_blocks_per_seq > (INT32_MAX >> sh) ||
+        (partition_tokens != PA_PARTITION_BALANCED && (partition_tokens < 0 || partition_tokens % 16)))
+        return 0;
+    const DecodeShape shape = decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                           max_blocks_per_seq << sh, partition_tokens, true);
+    if (!shape.valid) return 0;
+    return shape.balanced ? PA_PARTITION_BALANCED : shape.part_tokens;
+}
+
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                 int32_t partition_tokens) {
     const int32_t sh = block_shift(block_size);
     if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || sh < 0 ||
-        max_blocks_per_seq <= 0 || max_blocks_per_seq > (INT32_MAX >> sh) || partition_tokens < 0 ||
-        partition_tokens % 16)
+        max_blocks_per_seq <= 0 || max_blocks_per_seq > (INT32_MAX >> sh) ||
+        (partition_tokens != PA_PARTITION_BALANCED && (partition_tokens < 0 || partition_tokens % 16)))
         return 0;
-    return decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq << sh,
-                        partition_tokens).ws_bytes;
+    // enough for either split of this shape
+    const int32_t mb16 = max_blocks_per_seq << sh;
+    return std::max(decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, mb16, partition_tokens,
+                                 true).ws_bytes,
+                    decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, mb16, partition_tokens,
+                                 false).ws_bytes);
 }
 
 pa_status pa_decode_partitions(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -359,7 +444,8 @@ pa_status pa_decode_partitions(void* out, const void* q, const void* k_cache, co
     if (st != PA_OK || num_seqs == 0) return st;
     const DecodeShape shape = decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                            max_blocks_per_seq << block_shift(block_size),
-                                           partition_tokens);
+                                           partition_tokens, true);
+    if (!shape.valid) return PA_ERR_SHAPE;
     st = check_workspace(shape, workspace, workspace_bytes);
     if (st != PA_OK) return st;
     const pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, seq_lens,
@@ -380,17 +466,18 @@ pa_status pa_decode_merge(void* out, const int32_t* seq_lens, int32_t num_seqs,
         return PA_ERR_UNSUPPORTED;
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 ||
         num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > kMaxGroup ||
-        partition_tokens < 0 || partition_tokens % 16 != 0 ||
+        (partition_tokens != PA_PARTITION_BALANCED && (partition_tokens < 0 || partition_tokens % 16 != 0)) ||
         (int64_t)max_blocks_per_seq * block_size > INT32_MAX)
         return PA_ERR_SHAPE;
     if (num_seqs == 0) return PA_OK;
     if (!out || !seq_lens) return PA_ERR_NULL_PTR;
     if (!aligned16(out)) return PA_ERR_ALIGNMENT;
     const DecodeShape shape = decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                           max_blocks_per_seq << sh, partition_tokens);
+                                           max_blocks_per_seq << sh, partition_tokens, true);
+    if (!shape.valid) return PA_ERR_SHAPE;
     const pa_status st = check_workspace(shape, workspace, workspace_bytes);
     if (st != PA_OK) return st;
-    if (shape.num_parts <= 1) return PA_OK;
+    if (!shape.balanced && shape.num_parts <= 1) return PA_OK;
     const pa::DecodeArgs a = decode_args(out, nullptr, nullptr, nullptr, nullptr, seq_lens,
                                          num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
                                          max_blocks_per_seq, 1, 1.f, dtype, shape,
@@ -416,7 +503,8 @@ pa_status pa_decode_partitions_fp8(void* out, const void* q, const void* k_cache
     if (!k_scales || !v_scales) return PA_ERR_NULL_PTR;
     if (!aligned16(k_scales) || !aligned16(v_scales)) return PA_ERR_ALIGNMENT;
     const DecodeShape shape = decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                           max_blocks_per_seq, partition_tokens);
+                                           max_blocks_per_seq, partition_tokens, true);
+    if (!shape.valid) return PA_ERR_SHAPE;
     st = check_workspace(shape, workspace, workspace_bytes);
     if (st != PA_OK) return st;
     pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
@@ -482,7 +570,8 @@ pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const v
     // the partial states are per (sequence, query, q head): the workspace of
     // num_seqs * q_per_seq single-query sequences
     const DecodeShape shape = decode_shape(num_seqs * q_per_seq, num_q_heads, num_kv_heads,
-                                           head_dim, mb16, partition_tokens);
+                                           head_dim, mb16, partition_tokens, q_per_seq == 1);
+    if (!shape.valid) return PA_ERR_SHAPE;
     st = check_workspace(shape, workspace, workspace_bytes);
     if (st != PA_OK) return st;
     const pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, seq_lens,
@@ -491,7 +580,7 @@ pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const v
                                          workspace, flags, q_per_seq);
     if (!decode_grids_fit(a)) return PA_ERR_SHAPE;
     if (pa::launch_decode_partitions(a, stream) != hipSuccess) return PA_ERR_HIP;
-    if (shape.num_parts <= 1) return PA_OK;
+    if (!shape.balanced && shape.num_parts <= 1) return PA_OK;
     return pa::launch_decode_merge(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -526,7 +615,8 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const
     if (st != PA_OK || num_seqs == 0) return st;
     const DecodeShape shape = decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                            max_blocks_per_seq << block_shift(block_size),
-                                           partition_tokens);
+                                           partition_tokens, true);
+    if (!shape.valid) return PA_ERR_SHAPE;
     if (shape.ws_bytes > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_SCRATCH;
     // The partition kernel writes every partial state the merge reads, so the
     // scratch needs no clearing between calls.

@@ -129,6 +129,11 @@ def test_decode_rejects(lib, fn):
     assert _decode(lib, fn, part=256, ws=None) == WS
     assert _decode(lib, fn, part=256, wsb=16) == WS
     assert _decode(lib, fn, part=256, ws=FAKE + 4) == ALIGN
+    # the balanced split (partition_tokens -1): up to 512 sequences
+    assert _decode(lib, fn, part=-1, ws=None) == WS
+    assert _decode(lib, fn, part=-1, b=513, ws=None) == SHAPE
+    assert _decode(lib, fn, part=-2) == SHAPE
+    assert _decode(lib, fn, part=-16) == SHAPE
 
 
 def test_workspace_size(lib):
@@ -145,6 +150,15 @@ def test_workspace_size(lib):
     assert f(2, 8, 2, 128, 16, 64, 24) == 0              # invalid partition length
     assert f(2, 8, 2, 128, 8, 64, 256) == 0              # invalid block size
     assert f(2, 8, 2, 128, 64, 64, 256) == 0
+    # the balanced split of the LLaMA-shaped layer (64 sequences, 32 kv heads, one
+    # q head each): 3072 waves = 96 stretches x 32 kv heads; states (64 + 96) x 32
+    assert f(64, 32, 32, 128, 16, 256, -1) == (64 + 96) * 32 * (128 * 4 + 8)
+    # GQA on matrix cores (4 q heads per kv head): 384 stretches x 8 kv heads,
+    # 4 head slots per state
+    assert f(256, 32, 8, 128, 16, 512, -1) == (256 + 384) * 8 * 4 * (128 * 4 + 8)
+    # the default (0) takes the balanced split there; the size covers either split
+    assert f(64, 32, 32, 128, 16, 256, 0) >= (64 + 96) * 32 * (128 * 4 + 8)
+    assert f(600, 32, 32, 128, 16, 256, -1) == 0           # more than 512 sequences
     g = lib.pa_decode_default_partition
     g.restype = ctypes.c_int32
     g.argtypes = [ctypes.c_int32] * 5

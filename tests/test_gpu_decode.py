@@ -50,7 +50,7 @@ def _check_case(c, partitions=(0,)):
 def test_decode_tiny():
     """Batch 4, lengths 1/17/33/100, fp16, D=64, last token through the cache write."""
     c = decode_tiny()
-    _check_case(c, partitions=(0, 16, 32, 112))
+    _check_case(c, partitions=(0, 16, 32, 112, -1))
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -63,7 +63,7 @@ def test_decode_shapes(dtype, d, hq, hkv):
                          num_q_heads=hq, num_kv_heads=hkv, head_dim=d, seq_lens=lens,
                          num_blocks=64, max_blocks_per_seq=20, scale=1 / math.sqrt(d),
                          write_last=True)
-    _check_case(c, partitions=(0, 16, 48, 256, 320))
+    _check_case(c, partitions=(0, 16, 48, 256, 320, -1))
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -73,22 +73,22 @@ def test_decode_group_128(d):
     c = make_decode_case(name=f"group128-{d}", seed=600 + d, dtype="f16", num_q_heads=128,
                          num_kv_heads=1, head_dim=d, seq_lens=lens, num_blocks=16,
                          max_blocks_per_seq=8, scale=1 / math.sqrt(d), write_last=True)
-    _check_case(c, partitions=(0, 32))
+    _check_case(c, partitions=(0, 32, -1))
 
 
 def test_decode_llama_reduced():
     c = decode_llama2_7b_layer(batch=6, max_len=1024, num_heads=32)
-    _check_case(c, partitions=(0, 256, 1024))
+    _check_case(c, partitions=(0, 256, 1024, -1))
 
 
 def test_decode_gqa_shared_prefix_reduced():
     c = decode_gqa_shared_prefix(batch=32, max_len=2048, min_len=128, group=16, prefix=1024)
-    _check_case(c, partitions=(0, 512, 2048))
+    _check_case(c, partitions=(0, 512, 2048, -1))
 
 
 def test_decode_long_reduced():
     c = decode_long_context(batch=2, seq_len=8192, num_blocks=1100)
-    _check_case(c, partitions=(0, 256, 2048))
+    _check_case(c, partitions=(0, 256, 2048, -1))
 
 
 def test_one_token_context_returns_v():
@@ -168,7 +168,7 @@ def _needle_case(dtype, lens, part_tokens, seed=3):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("part", [0, 16, 64])
+@pytest.mark.parametrize("part", [0, 16, 64, -1])
 def test_needle_indexing_bit_exact(dtype, part):
     lens = [1, 16, 17, 40, 77, 130, 257, 300]
     c, needles = _needle_case(dtype, lens, part)
@@ -181,10 +181,11 @@ def test_needle_indexing_bit_exact(dtype, part):
                                           err_msg=f"seq {s} needle {pos} head {h}")
 
 
-def test_block_permutation_invariance_bit_exact():
+@pytest.mark.parametrize("part", [256, -1])
+def test_block_permutation_invariance_bit_exact(part):
     c = decode_gqa_shared_prefix(batch=16, max_len=1024, min_len=16, group=4, prefix=256)
     g = DecodeOnGPU(c)
-    base = host_bits(g.decode(partition_tokens=256)).copy()
+    base = host_bits(g.decode(partition_tokens=part)).copy()
     perm = np.random.default_rng(8).permutation(c.num_blocks)
     kc = np.empty_like(c.k_cache)
     vc = np.empty_like(c.v_cache)
@@ -194,7 +195,7 @@ def test_block_permutation_invariance_bit_exact():
     g.k_cache = dev_bits(kc, c.dtype)
     g.v_cache = dev_bits(vc, c.dtype)
     g.tables = dev_int(tables)
-    moved = host_bits(g.decode(partition_tokens=256))
+    moved = host_bits(g.decode(partition_tokens=part))
     np.testing.assert_array_equal(base, moved)
 
 
@@ -232,7 +233,7 @@ def test_split_matches_unsplit():
     c = decode_long_context(batch=2, seq_len=4096, num_blocks=600)
     g = DecodeOnGPU(c)
     single = host_f64(g.decode(partition_tokens=4096)).copy()
-    for p in (256, 512, 1024, 2048):
+    for p in (256, 512, 1024, 2048, -1):   # -1: the balanced split
         split = host_f64(g.decode(partition_tokens=p))
         assert np.abs(split - single).max() <= TOL[c.dtype]
 
@@ -331,3 +332,19 @@ def test_copy_on_write_fork_then_decode():
     rk, rv = oracle.ref_reshape_and_cache(key, key, rk, rv, slot)
     ref = oracle.ref_decode(c.q, rk, rv, tables, np.array([37, 38]), c.scale, "bf16")
     assert_close(after, ref, "bf16", "forked decode")
+
+
+@pytest.mark.parametrize("hq,hkv,d,dtype", [(8, 8, 128, "f16"), (32, 8, 128, "bf16"), (6, 2, 64, "bf16")])
+def test_balanced_split_many_sequences(hq, hkv, d, dtype):
+    """The balanced split over a long batch with a wide mix of lengths (empty
+    sequences, one-token ones, sequences far longer than a stretch): every
+    output against the oracle; the default split of the same call, whatever
+    it picks, too."""
+    rng = np.random.default_rng(90 + hq)
+    lens = rng.integers(0, 1200, 200)
+    lens[::17] = 0
+    lens[5::23] = 1
+    c = make_decode_case(name=f"balanced-{hq}-{hkv}-{d}", seed=91 + d, dtype=dtype, num_q_heads=hq,
+                         num_kv_heads=hkv, head_dim=d, seq_lens=lens, num_blocks=int(((lens + 15) // 16).sum()) + 8,
+                         max_blocks_per_seq=75, scale=1 / math.sqrt(d), write_last=True)
+    _check_case(c, partitions=(-1, 0))

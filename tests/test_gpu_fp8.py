@@ -107,7 +107,7 @@ def test_fp8_cache_write_float32_quotient_ties():
 
 
 def test_fp8_decode_tiny():
-    _check_fp8_case(decode_tiny(), partitions=(0, 16, 32, 112))
+    _check_fp8_case(decode_tiny(), partitions=(0, 16, 32, 112, -1))
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -120,22 +120,22 @@ def test_fp8_decode_shapes(dtype, d, hq, hkv):
                          num_q_heads=hq, num_kv_heads=hkv, head_dim=d, seq_lens=lens,
                          num_blocks=64, max_blocks_per_seq=20, scale=1 / math.sqrt(d),
                          write_last=True)
-    _check_fp8_case(c, partitions=(0, 16, 48, 256, 320))
+    _check_fp8_case(c, partitions=(0, 16, 48, 256, 320, -1))
 
 
 def test_fp8_decode_llama_reduced():
     c = decode_llama2_7b_layer(batch=6, max_len=1024, num_heads=32)
-    _check_fp8_case(c, partitions=(0, 256, 1024))
+    _check_fp8_case(c, partitions=(0, 256, 1024, -1))
 
 
 def test_fp8_decode_gqa_shared_prefix_reduced():
     c = decode_gqa_shared_prefix(batch=32, max_len=2048, min_len=128, group=16, prefix=1024)
-    _check_fp8_case(c, partitions=(0, 512, 2048))
+    _check_fp8_case(c, partitions=(0, 512, 2048, -1))
 
 
 def test_fp8_decode_long_reduced():
     c = decode_long_context(batch=2, seq_len=8192, num_blocks=1100)
-    _check_fp8_case(c, partitions=(0, 256, 2048))
+    _check_fp8_case(c, partitions=(0, 256, 2048, -1))
 
 
 def test_fp8_wide_value_range():
