@@ -37,8 +37,18 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, TFLOP/s
 METRIC = "paged-decode effective KV GB/s (% of MI355X HBM peak); decode tokens/s"
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_partition_traffic.json")
-DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_24_amd", "csrc", "decode.hip")
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_balanced_llama2_7b_layer_traffic.json")
+# the decode kernels' sources: counter runs stay valid while these are unchanged
+DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_24_amd", "csrc", f)
+                  for f in ("decode.hip", "common.h", "kernels.h")]
+
+
+def _decode_sources_sha256():
+    h = hashlib.sha256()
+    for path in DECODE_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def _args():
@@ -98,6 +108,19 @@ class _Timer:
                 "p90": round(float(np.percentile(x, 90)), 4)}
 
 
+def _settle(step, min_s=0.3):
+    """Run `step` untimed until the GPU has been busy for `min_s` seconds.  After
+    the host-side set-up of a workload the GPU clock is still low and a few
+    warm-up steps do not raise it: measured, the first configuration timed after
+    a set-up ran up to 9% slower than the same configuration timed again."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_s:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ decode workloads
 
 class DecodeRun:
@@ -151,6 +174,7 @@ class DecodeRun:
 
     def timed(self, steps, warmup):
         import torch
+        _settle(self.step)
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
@@ -296,12 +320,11 @@ def _oracle_fp8_rate(case, budget_s=3.0):
 
 def _traffic_if_current():
     """HBM bytes per launch of the partition kernel from committed rocprofv3
-    counter runs, valid only if decode.hip is unchanged since they were taken."""
+    counter runs, valid only if the decode sources are unchanged since they were taken."""
     try:
         with open(PROFILE_TRAFFIC) as f:
             prof = json.load(f)
-        src = hashlib.sha256(open(DECODE_SOURCE, "rb").read()).hexdigest()
-        if prof.get("decode_hip_sha256") != src:
+        if prof.get("decode_sources_sha256") != _decode_sources_sha256():
             return None
         return prof.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
@@ -394,6 +417,7 @@ def _secondary_tiny_latency(steps=200, warmup=20):
     from workloads import decode_tiny
     case = decode_tiny()
     run = DecodeRun(case)
+    _settle(run.step)
     for _ in range(warmup):
         run.step()
     torch.cuda.synchronize()
@@ -486,6 +510,7 @@ def _secondary_prefill(steps, warmup, oracle_budget_s=3.0, fp8=False):
         if ev is not None:
             ev[2].record()
 
+    _settle(step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -549,6 +574,7 @@ def _secondary_copy_blocks(steps, warmup, pairs_n=2048):
     vc = torch.empty_like(kc).normal_()
     perm = np.random.default_rng(6).permutation(nb)
     pairs = torch.from_numpy(np.stack([perm[:pairs_n], perm[pairs_n:2 * pairs_n]], 1).astype(np.int64)).cuda()
+    _settle(lambda: pa.pa_copy_blocks(kc, vc, pairs))
     for _ in range(warmup):
         pa.pa_copy_blocks(kc, vc, pairs)
     torch.cuda.synchronize()
@@ -593,6 +619,7 @@ def _secondary_multi(steps, warmup, nq=4):
         pa.pa_decode_multi(out, q, run.kc, run.vc, run.tables, run.lens, c.scale, 0, ws,
                            flags=run.flags)
 
+    _settle(step)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -734,7 +761,8 @@ def _traffic_profile(root):
     algo = kv + qo + int(((lens + 15) // 16).sum()) * 4
     out = {
         "kernel": "decode_balanced_kernel<f16,128,1,stream> on decode_llama2_7b_layer (balanced split)",
-        "decode_hip_sha256": hashlib.sha256(open(DECODE_SOURCE, "rb").read()).hexdigest(),
+        "decode_sources": [os.path.relpath(p, ROOT) for p in DECODE_SOURCES],
+        "decode_sources_sha256": _decode_sources_sha256(),
         "fetch_size_kib_per_launch": round(f_dec, 1), "write_size_kib_per_launch": round(w_dec, 1),
         "dispatches": [n_f, n_w],
         "copy_calibration": {"bytes": n, "fetch_size_kib": round(f_copy, 1), "write_size_kib": round(w_copy, 1),
@@ -749,7 +777,7 @@ def _traffic_profile(root):
             f"rocprofv3 --pmc WRITE_SIZE -d {root}/dec_WRITE_SIZE -o run -- python3 -u bench.py --quick --no-cpu-baseline --steps 5 --warmup 2",
             f"rocprofv3 --pmc FETCH_SIZE -d {root}/copy_FETCH_SIZE -o run -- python3 -u bench.py --copy-calibration",
             f"rocprofv3 --pmc WRITE_SIZE -d {root}/copy_WRITE_SIZE -o run -- python3 -u bench.py --copy-calibration",
-            f"python3 bench.py --traffic-profile {root} > profiles/decode_partition_traffic.json",
+            f"python3 bench.py --traffic-profile {root} > profiles/decode_balanced_llama2_7b_layer_traffic.json",
         ],
     }
     print(json.dumps(out, indent=1))
