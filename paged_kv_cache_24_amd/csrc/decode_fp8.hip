@@ -303,8 +303,9 @@ __global__ __launch_bounds__(256) void decode_fp8_balanced_kernel(DecodeArgs a) 
 //        eight A elements.  The V codes are widened times 2^e (e = exponent of
 //        the token's v_scale, exact in 16 bits) and the mantissa factor in
 //        [1, 2) of v_scale multiplies the probabilities, so P never meets a
-//        tiny scale in 16-bit precision; P enters as a 16-bit head and tail,
-//        two MFMAs, so the factor adds no rounding of its own.
+//        tiny scale in 16-bit precision; P times the factor enters rounded
+//        once to 16 bits, and the row sum adds each rounded weight times
+//        1/factor, so the weights stay consistent with the sum.
 //        Lane (lr, lg) loads tokens 4*lg + (lr/8) and 4*lg + 2 + (lr/8) of a
 //        block, codes 16*(lr%8) .. +16: tokens among its own four.
 // ---------------------------------------------------------------------------
@@ -463,14 +464,19 @@ __device__ __forceinline__ void fp8_gqa_segment(const DecodeArgs& a, uint16_t* v
         }
         m = mn;
         const float mu = mn == -INFINITY ? 0.f : mn;
-        float pm[2][4];
+        // P times the mantissa factor of each key's v scale (V holds code * 2^e)
+        // enters PV rounded once to 16 bits; the row sum adds each rounded weight
+        // times 1/factor, the probability the product used, so the weights that
+        // multiply V stay consistent with the sum
+        float pm[2][4], imu[2][4];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float p = fast_exp2(x[h][i] - mu);
-                l += p;
-                pm[h][i] = valid[h][i] ? p * scale_mantissa(vs[h][i]) : 0.f;
+                const float f = scale_mantissa(vs[h][i]);
+                pm[h][i] = valid[h][i] ? p * f : 0.f;
+                imu[h][i] = __builtin_amdgcn_rcpf(f);
             }
         // V tiles to LDS, widened times 2^exponent(v_scale); rows past the
         // sequence end as zeros (MFMA would turn 0 x NaN into NaN)
@@ -496,24 +502,25 @@ __device__ __forceinline__ void fp8_gqa_segment(const DecodeArgs& a, uint16_t* v
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // P^T = p * mantissa(v_scale) as a 16-bit head plus a 16-bit tail
-        // (p * mu - head): two MFMAs carry ~16 significant bits of P
-        uint4 ph, pt;
+        uint4 ph;
         ph.x = pack2<DT>(pm[0][0], pm[0][1]);
         ph.y = pack2<DT>(pm[0][2], pm[0][3]);
         ph.z = pack2<DT>(pm[1][0], pm[1][1]);
         ph.w = pack2<DT>(pm[1][2], pm[1][3]);
-        pt.x = pack2<DT>(pm[0][0] - lo_to_f32<DT>(ph.x), pm[0][1] - hi_to_f32<DT>(ph.x));
-        pt.y = pack2<DT>(pm[0][2] - lo_to_f32<DT>(ph.y), pm[0][3] - hi_to_f32<DT>(ph.y));
-        pt.z = pack2<DT>(pm[1][0] - lo_to_f32<DT>(ph.z), pm[1][1] - hi_to_f32<DT>(ph.z));
-        pt.w = pack2<DT>(pm[1][2] - lo_to_f32<DT>(ph.w), pm[1][3] - hi_to_f32<DT>(ph.w));
+        l = fmaf(lo_to_f32<DT>(ph.x), imu[0][0], l);
+        l = fmaf(hi_to_f32<DT>(ph.x), imu[0][1], l);
+        l = fmaf(lo_to_f32<DT>(ph.y), imu[0][2], l);
+        l = fmaf(hi_to_f32<DT>(ph.y), imu[0][3], l);
+        l = fmaf(lo_to_f32<DT>(ph.z), imu[1][0], l);
+        l = fmaf(hi_to_f32<DT>(ph.z), imu[1][1], l);
+        l = fmaf(lo_to_f32<DT>(ph.w), imu[1][2], l);
+        l = fmaf(hi_to_f32<DT>(ph.w), imu[1][3], l);
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             const uint2 v0 = lds_read_tr16(vt + tr_off + 16 * mt);
             const uint2 v1 = lds_read_tr16(vt + kTile + tr_off + 16 * mt);
             const uint4 va = make_uint4(v0.x, v0.y, v1.x, v1.y);
             o[mt] = f8_mfma_16x16x32<DT>(va, ph, o[mt]);
-            o[mt] = f8_mfma_16x16x32<DT>(va, pt, o[mt]);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();

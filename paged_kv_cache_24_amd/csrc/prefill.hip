@@ -43,9 +43,11 @@
 // ("vLLM-Ascend 原理", §四 on KV-cache quantisation: dequantised after the
 // block-table lookup, inside the operator); K enters LDS as exact 16-bit codes
 // and its scale multiplies the scores, V enters as codes times 2^e (e = exponent
-// of its scale, exact) and the scale's mantissa factor in [1, 2) multiplies P,
-// which goes to the matrix cores as a 16-bit head and tail so the factor adds
-// no rounding.  The per-key factors sit in two small LDS arrays beside the tiles.
+// of its scale, exact) and the scale's mantissa factor mu in [1, 2) multiplies
+// P, which goes to the matrix cores rounded once to 16 bits; the row sum adds
+// each rounded weight times 1/mu, the probability the product used, so the
+// weights stay consistent with the sum as on the 16-bit cache.  The per-key
+// factors (k scale, mu, 1/mu) sit in small LDS arrays beside the tiles.
 #include <type_traits>
 
 #include "common.h"
@@ -229,6 +231,7 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
     // FP8 only: per-key k scale and v-scale mantissa factor of each staged tile
     __shared__ __attribute__((aligned(16))) float lds_ks[F8 ? 2 : 1][F8 ? kKT : 4];
     __shared__ __attribute__((aligned(16))) float lds_mu[F8 ? 2 : 1][F8 ? kKT : 4];
+    __shared__ __attribute__((aligned(16))) float lds_imu[F8 ? 2 : 1][F8 ? kKT : 4];   // 1 / mu
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -384,8 +387,10 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
         vd[0] = make_uint4(ve[0].x, ve[0].y, ve[1].x, ve[1].y);
         vd[1] = make_uint4(ve[2].x, ve[2].y, ve[3].x, ve[3].y);
         if (c8 == 0) {
+            const float mu = scale_mantissa(vsc);
             lds_ks[buf][kr8] = ksc;
-            lds_mu[buf][kr8] = scale_mantissa(vsc);
+            lds_mu[buf][kr8] = mu;
+            lds_imu[buf][kr8] = 1.f / mu;
         }
     };
     // transposed V^T fragment address of this lane: row 4*lg + lr/4 (+16), column 4*(lr%4) (+16 mt)
@@ -471,43 +476,51 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
             }
             m = mn;
             const float nmu = mn == -INFINITY ? 0.f : -mn;
-            float ps = 0.f;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float pv = fast_exp2(fmaf(s[mt][i], cs, nmu));
                     s[mt][i] = pv;
-                    if constexpr (F8) ps += pv;
                 }
-            // FP8: P (times the v-scale mantissa) enters PV as a 16-bit head plus a
-            // 16-bit tail, so the row sum takes the float32 p; 16-bit caches: P
-            // enters as one 16-bit value, and the row sum adds those same rounded
-            // values (below), so the weights that multiply V sum to exactly l
-            if constexpr (F8) lsum += ps;
+            // P enters PV as one 16-bit value per key, and the row sum adds the
+            // probabilities those values stand for, so the weights that multiply V
+            // sum to exactly l: with a 16-bit cache P itself; over FP8, P times the
+            // mantissa mu of the key's v scale (V holds code * 2^e), whose rounded
+            // value times 1/mu is the probability the product used.
+            float imu[4][4];
             if constexpr (F8) {   // times the v-scale mantissa factor of each key
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) {
                     const float4 mu4 = *reinterpret_cast<const float4*>(&lds_mu[buf][16 * mt + 4 * lg]);
+                    const float4 imu4 = *reinterpret_cast<const float4*>(&lds_imu[buf][16 * mt + 4 * lg]);
                     s[mt][0] *= mu4.x;
                     s[mt][1] *= mu4.y;
                     s[mt][2] *= mu4.z;
                     s[mt][3] *= mu4.w;
+                    imu[mt][0] = imu4.x;
+                    imu[mt][1] = imu4.y;
+                    imu[mt][2] = imu4.z;
+                    imu[mt][3] = imu4.w;
                 }
             }
             // key slot 8*lg + i <-> key 32*kc + 4*lg + i; slot 8*lg + 4 + i <-> key 32*kc + 16 + 4*lg + i
-            uint4 pb[2], pt[2];
+            uint4 pb[2];
 #pragma unroll
             for (int kc = 0; kc < 2; ++kc) {
                 pb[kc].x = pack2<DT>(s[2 * kc][0], s[2 * kc][1]);
                 pb[kc].y = pack2<DT>(s[2 * kc][2], s[2 * kc][3]);
                 pb[kc].z = pack2<DT>(s[2 * kc + 1][0], s[2 * kc + 1][1]);
                 pb[kc].w = pack2<DT>(s[2 * kc + 1][2], s[2 * kc + 1][3]);
-                if constexpr (F8) {   // the 16-bit tail of P: what the head's rounding lost
-                    pt[kc].x = pack2<DT>(s[2 * kc][0] - lo_to_f32<DT>(pb[kc].x), s[2 * kc][1] - hi_to_f32<DT>(pb[kc].x));
-                    pt[kc].y = pack2<DT>(s[2 * kc][2] - lo_to_f32<DT>(pb[kc].y), s[2 * kc][3] - hi_to_f32<DT>(pb[kc].y));
-                    pt[kc].z = pack2<DT>(s[2 * kc + 1][0] - lo_to_f32<DT>(pb[kc].z), s[2 * kc + 1][1] - hi_to_f32<DT>(pb[kc].z));
-                    pt[kc].w = pack2<DT>(s[2 * kc + 1][2] - lo_to_f32<DT>(pb[kc].w), s[2 * kc + 1][3] - hi_to_f32<DT>(pb[kc].w));
+                if constexpr (F8) {
+                    lsum = fmaf(lo_to_f32<DT>(pb[kc].x), imu[2 * kc][0], lsum);
+                    lsum = fmaf(hi_to_f32<DT>(pb[kc].x), imu[2 * kc][1], lsum);
+                    lsum = fmaf(lo_to_f32<DT>(pb[kc].y), imu[2 * kc][2], lsum);
+                    lsum = fmaf(hi_to_f32<DT>(pb[kc].y), imu[2 * kc][3], lsum);
+                    lsum = fmaf(lo_to_f32<DT>(pb[kc].z), imu[2 * kc + 1][0], lsum);
+                    lsum = fmaf(hi_to_f32<DT>(pb[kc].z), imu[2 * kc + 1][1], lsum);
+                    lsum = fmaf(lo_to_f32<DT>(pb[kc].w), imu[2 * kc + 1][2], lsum);
+                    lsum = fmaf(hi_to_f32<DT>(pb[kc].w), imu[2 * kc + 1][3], lsum);
                 } else {
                     lsum = dot2<DT>(pb[kc].x, kOnes2<DT>, lsum);
                     lsum = dot2<DT>(pb[kc].y, kOnes2<DT>, lsum);
@@ -531,7 +544,6 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
                     const uint2 h2 = __builtin_bit_cast(uint2, hi);
                     const uint4 va = make_uint4(l2.x, l2.y, h2.x, h2.y);
                     o[mt] = mfma16x16x32<DT>(va, pb[kc], o[mt]);
-                    if constexpr (F8) o[mt] = mfma16x16x32<DT>(va, pt[kc], o[mt]);
                 }
             }
             __builtin_amdgcn_s_setprio(0);

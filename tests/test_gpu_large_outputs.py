@@ -11,15 +11,15 @@ oracle's value):
                                    +  eps * sum_j w_j |v_j|
 
 * spacing/2: the final round to bf16.
-* 2u term: the 16-bit matrix-core paths (GQA decode, 16-bit prefill) round
-  each probability p_j to bf16 before the PV product (relative error <= u =
-  2^-8) and their row sum adds the same rounded values, so the weights that
-  multiply V still sum to one; a perturbation delta_j of each weight moves
-  the output by sum_j w_j (delta_j - mean delta)(v_j - ref).  With a row sum
-  of unrounded p the error would grow with |v| instead of with the spread
-  of v around the output.  The FP8 paths carry p times the mantissa of v's
-  scale as a bf16 head plus a bf16 tail (relative error ~2^-16, inside the
-  eps term), and the vector-ALU paths keep p in float32: u = 0 for both.
+* 2u term: the matrix-core paths (GQA decode and prefill, 16-bit and FP8)
+  round each weight to bf16 before the PV product (relative error <= u =
+  2^-8) and their row sum adds the probabilities those rounded weights stand
+  for (over FP8 the weight is p times the mantissa factor f of the key's v
+  scale, and the sum adds weight / f), so the weights that multiply V still
+  sum to one; a perturbation delta_j of each weight moves the output by
+  sum_j w_j (delta_j - mean delta)(v_j - ref).  With a row sum of unrounded p
+  the error would grow with |v| instead of with the spread of v around the
+  output.  The vector-ALU paths keep p in float32: u = 0.
 * eps = 2^-13: float32 accumulation in the scores (head_dim 128 products),
   the sums and the division, bounded for these sizes.
 
@@ -146,8 +146,8 @@ def _fp8_tokens(codes, scales, table_row, n):
                                        oracle.gather_scales(scales, table_row, n))
 
 
-@pytest.mark.parametrize("hq,hkv", [(16, 2), (4, 4)])
-def test_fp8_decode_large_outputs(hq, hkv):
+@pytest.mark.parametrize("hq,hkv,u", [(16, 2, U_BF16), (4, 4, 0.0)])
+def test_fp8_decode_large_outputs(hq, hkv, u):
     """FP8 decode: the matrix-core GQA kernel (16/2) and the vector kernel (4/4)."""
     c = _decode_case(hq, hkv, 128, seed=51 + hq)
     g = Fp8DecodeOnGPU(c)
@@ -164,7 +164,7 @@ def test_fp8_decode_large_outputs(hq, hkv):
         dev[b], mag[b] = dv[0], mg[0]
     for part in (0, 16):
         got = host_f64(g.decode(partition_tokens=part))
-        _check(got, ref, dev, mag, 0.0, f"FP8 decode {hq}/{hkv} partition {part}")
+        _check(got, ref, dev, mag, u, f"FP8 decode {hq}/{hkv} partition {part}")
 
 
 def test_fp8_prefill_large_outputs():
@@ -188,4 +188,4 @@ def test_fp8_prefill_large_outputs():
         q64 = oracle.bits_to_float64(c.q[lo:lo + L], "bf16")
         dev[lo:lo + L], mag[lo:lo + L] = _weighted_sums(q64, k64, v64, ctx + np.arange(L), c.scale,
                                                         ref[lo:lo + L])
-    _check(got, ref, dev, mag, 0.0, "FP8 prefill 8/2")
+    _check(got, ref, dev, mag, U_BF16, "FP8 prefill 8/2")
