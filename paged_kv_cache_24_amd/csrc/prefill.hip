@@ -9,12 +9,13 @@
 // ("vLLM-Ascend 原理", §2.3 step 3 and §四 "ATB 算子").
 //
 // Two kernels:
-//  * prefill16_kernel (fp16 / bf16 cache): 32x32x16 matrix-core products,
-//    K/V tiles copied from HBM straight into LDS, S(t+1) = K Q^T overlapped
-//    with the softmax of tile t; described at the kernel.
-//  * prefill_kernel<.., F8, D> (FP8 cache, and the 16-bit cache at head_dim
-//    64): 16x16x32 products over tiles staged through registers (FP8 codes
-//    widened to 16 bits on the way), as follows.
+//  * prefill16_kernel (head_dim 128): 32x32x16 matrix-core products, S(t+1) =
+//    K Q^T overlapped with the softmax of tile t; described at the kernel.  Over
+//    the 16-bit cache K/V tiles go from HBM straight into LDS; over the FP8
+//    cache the codes pass through registers and are widened to 16 bits on the
+//    way into LDS.
+//  * prefill_kernel<.., F8, D> (head_dim 64, either cache): 16x16x32 products
+//    over tiles staged through registers, as follows.
 //
 // Both take the q-head group G at run time: a workgroup's rows are floor(R/G)
 // positions times the G q heads that share the kv head (R = 128 or 256 rows),
@@ -39,9 +40,9 @@
 // of the rescale factors is needed.  The next tile's K/V rows are loaded into
 // registers while the current tile is computed and stored to the other LDS
 // buffer afterwards (one barrier per tile).
-// Over the FP8 cache, each thread stages 16 codes of one key row
-// ("vLLM-Ascend 原理", §四 on KV-cache quantisation: dequantised after the
-// block-table lookup, inside the operator); K enters LDS as exact 16-bit codes
+// Over the FP8 cache (in both kernels), each thread stages 16 or 32 codes of
+// one key row ("vLLM-Ascend 原理", §四 on KV-cache quantisation: dequantised
+// after the block-table lookup, inside the operator); K enters LDS as exact 16-bit codes
 // and its scale multiplies the scores, V enters as codes times 2^e (e = exponent
 // of its scale, exact) and the scale's mantissa factor mu in [1, 2) multiplies
 // P, which goes to the matrix cores rounded once to 16 bits; the row sum adds
@@ -572,7 +573,7 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 16-bit cache: prefill on 32x32x16 matrix-core products, software-pipelined.
+// head_dim 128: prefill on 32x32x16 matrix-core products, software-pipelined.
 //
 // One workgroup (8 waves) owns 256 query rows of one (sequence, kv head); each
 // wave owns 32 rows, so every K/V fragment read from LDS feeds a 32-row product
@@ -600,6 +601,10 @@ __global__ __launch_bounds__(512, 4) void prefill_kernel(PrefillArgs a) {
 // raised, O and the sum rescaled and the tile redone -- an exact rewrite of the
 // softmax ("vLLM-Ascend 原理", §四 ATB fused attention), with p <= 256.
 // Row sums add the same 16-bit probabilities that enter the PV product.
+// Over the FP8 cache (F8) the same waves move the same blocks, but through
+// registers: the codes of tile t+1 are loaded as tile t begins and widened into
+// the 16-bit layout at its end (two LDS buffers would do; the four of the
+// 16-bit ring are kept), and the softmax applies the per-key factors.
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -642,8 +647,9 @@ constexpr int kRows16 = 32 * kW16;      // query rows per workgroup
 constexpr int kQkAhead = 6;             // K fragment reads in flight ahead of the products
 constexpr int kPvAhead = 4;             // products whose V fragments are read ahead
 
-template <int DT, int SH>
+template <int DT, int SH, bool F8>
 __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) {
+    static_assert(!F8 || SH == 0, "FP8 pools come in 16-token blocks");
     const int G = a.group;          // q heads per kv head, 1 .. kRows16
     const int P = kRows16 / G;      // positions per workgroup; rows P G .. kRows16-1 idle
     // separate arrays so that the compiler can tell the in-flight copies from
@@ -656,6 +662,12 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
     __shared__ __attribute__((aligned(1024))) uint16_t lds_v1[kTileElems];
     __shared__ __attribute__((aligned(1024))) uint16_t lds_v2[kTileElems];
     __shared__ __attribute__((aligned(1024))) uint16_t lds_v3[kTileElems];
+    // FP8 only, per key of each buffered tile: k scale times scale_log2; the
+    // mantissa factor mu of the v scale; 1/mu as two 16-bit parts (hi, lo) in
+    // pair order (word 2p: the hi parts of keys 2p, 2p+1; word 2p+1: their lo parts)
+    __shared__ __attribute__((aligned(16))) float lds_c1[F8 ? 4 : 1][F8 ? kKT : 4];
+    __shared__ __attribute__((aligned(16))) float lds_mu[F8 ? 4 : 1][F8 ? kKT : 4];
+    __shared__ __attribute__((aligned(16))) uint32_t lds_imu[F8 ? 4 : 1][F8 ? kKT : 4];
     auto kbuf = [&](auto i) __attribute__((always_inline)) -> uint16_t* {
         constexpr int I = decltype(i)::value;
         return I == 0 ? lds_k0 : I == 1 ? lds_k1 : I == 2 ? lds_k2 : lds_k3;
@@ -778,6 +790,67 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
         }
     };
 
+    // ---- FP8 staging, through registers.  Wave w moves block q of each tile as
+    // above: lane i takes token row r8 = i / 4 of the block, codes 32 (i % 4) ..
+    // +31, and that row's scale.  The codes of tile t+1 are loaded as tile t
+    // begins and at its end widened to 16 bits (K exact, V times 2^e, e the
+    // exponent of the row's v scale) and written to the tile's buffers in the layout above
+    // (chunk c of tile row R at slot c ^ f(R)), with the per-key factors.  Rows
+    // past the keys or in a block outside the pool stage zero codes with k scale
+    // 1 and v scale 1; the choice is applied when the codes are widened, so that
+    // nothing waits for the loads before then.
+    const int r8 = lane >> 2;
+    const int p8 = lane & 3;
+    const uint32_t off8 = (uint32_t)(r8 * row_stride + g * kPD + 32 * p8);   // bytes
+    const uint32_t soff8 = (uint32_t)((g * kBlockSize + r8) * 4);             // bytes
+    struct Staged8 {
+        uint4 c0, c1;
+        float sc;
+        bool ok;
+    };
+    Staged8 st8;
+    auto load8 = [&](int tt, int pb, Staged8& st) __attribute__((always_inline)) {
+        const int nval = n_keys - (tt * kKT + 16 * q);   // valid rows of this block (uniform)
+        const bool blk_ok = pb >= 0 && pb < nb32;        // uniform
+        const int64_t pblk = blk_ok ? pb : 0;
+        const char* src = static_cast<const char*>(kwave ? a.k_cache : a.v_cache) + pblk * (kBlockSize * row_stride);
+        const char* ssrc = reinterpret_cast<const char*>(kwave ? a.k_scales : a.v_scales) +
+                           pblk * ((int64_t)a.num_kv_heads * kBlockSize * 4);
+        st.c0 = *reinterpret_cast<const uint4*>(src + off8);
+        st.c1 = *reinterpret_cast<const uint4*>(src + off8 + 16);
+        st.sc = *reinterpret_cast<const float*>(ssrc + soff8);
+        st.ok = blk_ok && r8 < nval;
+    };
+    auto store8 = [&](const Staged8& st, auto par) __attribute__((always_inline)) {
+        constexpr int B = decltype(par)::value;
+        const uint32_t w[8] = {st.c0.x, st.c0.y, st.c0.z, st.c0.w, st.c1.x, st.c1.y, st.c1.z, st.c1.w};
+        const float sc = st.ok ? st.sc : 1.f;
+        uint2 e[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) e[k] = fp8x4_to_16<DT>(st.ok ? w[k] : 0u, kwave ? 1.f : sc);
+        char* dst = reinterpret_cast<char*>(kwave ? kbuf(par) : vbuf(par));
+        const int R = 16 * q + r8;
+        const int f = kwave ? r8 : (r8 & 3) << 2;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            *reinterpret_cast<uint4*>(dst + R * kPD * 2 + (((4 * p8 + c) ^ f) << 4)) =
+                make_uint4(e[2 * c].x, e[2 * c].y, e[2 * c + 1].x, e[2 * c + 1].y);
+        if (p8 == 0) {
+            if (kwave) {
+                lds_c1[B][R] = sc * a.scale_log2;
+            } else {
+                const float mu = scale_mantissa(sc);
+                const float imu = 1.f / mu;
+                const uint16_t hi = f32_to_bits<DT>(imu);
+                const uint16_t lo = f32_to_bits<DT>(imu - lo_to_f32<DT>(hi));
+                lds_mu[B][R] = mu;
+                uint16_t* iw = reinterpret_cast<uint16_t*>(lds_imu[B]);
+                iw[4 * (R >> 1) + (R & 1)] = hi;
+                iw[4 * (R >> 1) + 2 + (R & 1)] = lo;
+            }
+        }
+    };
+
     // ---- LDS read addresses (bytes).  K fragment of step kk: row 32 kb + lr,
     // chunk 2 kk + h, stored at slot (2 kk + h) ^ (lane & 15).
     uint32_t kaddr[8];
@@ -838,7 +911,10 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
     // nobody reads again.
     // prologue: K(0..2) or V(0..1)
     const int clampt = ntiles - 1;
-    {   // all block ids first: their loads are then in flight together
+    if constexpr (F8) {
+        load8(0, raw_block(0), st8);
+        store8(st8, I0());
+    } else {   // all block ids first: their loads are then in flight together
         const int id0 = block_of_scalar(0);
         const int id1 = block_of_scalar(min(1, clampt));
         const int id2 = block_of_scalar(min(2, clampt));
@@ -851,12 +927,13 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
             stage(min(1, clampt), id1, lds_v1);
         }
     }
-    const int ahead = kwave ? 3 : 2;      // tiles between the products and this wave's copies
+    const int ahead = F8 ? 1 : kwave ? 3 : 2;   // tiles between the products and this wave's copies
     int pb_next = raw_block(min(ahead, clampt));
     // everything, Q included: the prologue copies were issued back to back, so
     // this costs little more than waiting for the first ones, and afterwards no
-    // load the compiler knows of is outstanding inside the loop
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    // load the compiler knows of is outstanding inside the loop (over FP8 the
+    // compiler places the waits for its own loads)
+    if constexpr (!F8) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
     // ---- O^T += V^T P^T over one tile
     auto pv = [&](const uint16_t* vb, const uint4 (&pb)[4]) __attribute__((always_inline)) {
@@ -947,6 +1024,90 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
         }
     };
 
+    // ---- softmax over the FP8 cache.  x = S k_scale scale_log2 - m per key (the
+    // factor from LDS; the mask applies to x, so a zero scale never meets -inf);
+    // P times mu of each key goes to the PV product rounded once, and the row
+    // sums add each rounded weight times 1/mu (two 16-bit parts, so v_dot2 takes
+    // them exactly to float32 accuracy).  m = -inf means reference 0: the first
+    // live tile always raises the max.
+    auto softmax8 = [&](int t, auto par, uint4 (&pb)[4]) __attribute__((always_inline)) {
+        constexpr int B = decltype(par)::value;
+        const float nmu = m == -INFINITY ? 0.f : -m;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {   // keys 32 kb + 8 j + 4 h + i
+                const float4 c = *reinterpret_cast<const float4*>(&lds_c1[B][32 * kb + 8 * j + 4 * h]);
+                sc[kb][4 * j] = fmaf(sc[kb][4 * j], c.x, nmu);
+                sc[kb][4 * j + 1] = fmaf(sc[kb][4 * j + 1], c.y, nmu);
+                sc[kb][4 * j + 2] = fmaf(sc[kb][4 * j + 2], c.z, nmu);
+                sc[kb][4 * j + 3] = fmaf(sc[kb][4 * j + 3], c.w, nmu);
+            }
+        const int k0 = t * kKT;
+        if (k0 + kKT - 1 > wave_q_lo) {   // diagonal tile: causal mask by select
+            const int lim = qpos - k0 - 4 * h;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sc[kb][r] = -INFINITY;
+        }
+        float lmax0 = -INFINITY, lmax1 = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            lmax0 = __builtin_elementwise_maximum(lmax0, sc[0][r]);
+            lmax1 = __builtin_elementwise_maximum(lmax1, sc[1][r]);
+        }
+        const float lmax = __builtin_elementwise_maximum(lmax0, lmax1);
+        // word i of pb[ks] holds keys 16 ks + 8 (i / 2) + 4 h + 2 (i % 2) + {0, 1}
+        auto probs = [&](float sub) __attribute__((always_inline)) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int kb = ks >> 1, r0 = 8 * (ks & 1);
+                const float4 mu0 = *reinterpret_cast<const float4*>(&lds_mu[B][16 * ks + 4 * h]);
+                const float4 mu1 = *reinterpret_cast<const float4*>(&lds_mu[B][16 * ks + 8 + 4 * h]);
+                const float mu[8] = {mu0.x, mu0.y, mu0.z, mu0.w, mu1.x, mu1.y, mu1.z, mu1.w};
+                uint32_t w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    w[i] = pack2<DT>(fast_exp2(sc[kb][r0 + 2 * i] - sub) * mu[2 * i],
+                                     fast_exp2(sc[kb][r0 + 2 * i + 1] - sub) * mu[2 * i + 1]);
+                pb[ks] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        };
+        probs(0.f);
+        const float lim_x = m == -INFINITY ? -INFINITY : 8.f;
+        if (__any(lmax > lim_x)) {   // raise the row max (rows of lanes l, l^32 agree)
+            const float mb = xor32_max(lmax);   // relative to m, or absolute while m = -inf
+            const bool raise = mb > lim_x;
+            const float mn = raise ? (m == -INFINITY ? mb : m + mb) : m;
+            const float alpha = raise ? fast_exp2(m - mn) : 1.f;   // exp2(-inf) = 0
+            lsum0 *= alpha;
+            lsum1 *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db) o[db] *= alpha;
+            m = mn;
+            probs(raise ? mb : 0.f);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {   // (hi, lo) of 1/mu for the pairs of words 0, 1 and 2, 3
+            const uint4 i0 = *reinterpret_cast<const uint4*>(&lds_imu[B][16 * ks + 4 * h]);
+            const uint4 i1 = *reinterpret_cast<const uint4*>(&lds_imu[B][16 * ks + 8 + 4 * h]);
+            lsum0 = dot2<DT>(pb[ks].x, i0.x, lsum0);
+            lsum1 = dot2<DT>(pb[ks].x, i0.y, lsum1);
+            lsum0 = dot2<DT>(pb[ks].y, i0.z, lsum0);
+            lsum1 = dot2<DT>(pb[ks].y, i0.w, lsum1);
+            lsum0 = dot2<DT>(pb[ks].z, i1.x, lsum0);
+            lsum1 = dot2<DT>(pb[ks].z, i1.y, lsum1);
+            lsum0 = dot2<DT>(pb[ks].w, i1.z, lsum0);
+            lsum1 = dot2<DT>(pb[ks].w, i1.w, lsum1);
+        }
+    };
+    auto smax = [&](int t, auto par, uint4 (&pb)[4]) __attribute__((always_inline)) {
+        if constexpr (F8) softmax8(t, par, pb);
+        else softmax(t, pb);
+    };
+
     // Ping-pong: the two waves on each SIMD (w and w + 4) work half a tile apart.
     // Waves 0..3 do [S(t), softmax(t)] then [PV(t)]; waves 4..7 do [PV(t-1)]
     // then [S(t), softmax(t)], keeping P(t-1) in registers across the barrier.
@@ -965,14 +1126,20 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
         constexpr int B = decltype(par)::value;          // t & 3
         constexpr int R = decltype(role)::value;
         uint16_t* kcur = kbuf(std::integral_constant<int, B>());   // K(t)
-        // K waves copy K(t+3) into the buffer of K(t-1); V waves copy V(t+2) into
-        // that of V(t-2) (read at tile t-2 and, by the late waves, at tile t-1)
-        uint16_t* dst = kwave ? kbuf(std::integral_constant<int, (B + 3) & 3>())
-                              : vbuf(std::integral_constant<int, (B + 2) & 3>());
-        if (kwave) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8): K(t) is in
-        else __builtin_amdgcn_s_waitcnt(0x0F74);         // vmcnt(4): V(t) is in
-        __syncthreads();
-        stage(min(t + ahead, clampt), valid_block(pb_next), dst);
+        if constexpr (F8) {
+            // tile t was written during tile t-1; the codes of tile t+1 go out now
+            __syncthreads();
+            load8(min(t + 1, clampt), pb_next, st8);
+        } else {
+            // K waves copy K(t+3) into the buffer of K(t-1); V waves copy V(t+2) into
+            // that of V(t-2) (read at tile t-2 and, by the late waves, at tile t-1)
+            uint16_t* dst = kwave ? kbuf(std::integral_constant<int, (B + 3) & 3>())
+                                  : vbuf(std::integral_constant<int, (B + 2) & 3>());
+            if (kwave) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8): K(t) is in
+            else __builtin_amdgcn_s_waitcnt(0x0F74);         // vmcnt(4): V(t) is in
+            __syncthreads();
+            stage(min(t + ahead, clampt), valid_block(pb_next), dst);
+        }
         // The next copy's block id is a scalar load, which shares its wait counter
         // with the LDS reads and may complete out of order: the first LDS wait
         // after it waits for it too.  It is issued after the K products, so that
@@ -981,16 +1148,20 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
             if (B != 0 || t >= 1) pv(vbuf(std::integral_constant<int, (B + 3) & 3>()), pkeep);
             qk(kcur, sc);
             pb_next = raw_block(min(t + 1 + ahead, clampt));
-            softmax(t, pkeep);
+            smax(t, par, pkeep);
         } else if constexpr (R == kEarly) {
             uint4 pb[4];
             qk(kcur, sc);
             pb_next = raw_block(min(t + 1 + ahead, clampt));
-            softmax(t, pb);
+            smax(t, par, pb);
             pv(vbuf(std::integral_constant<int, B>()), pb);
         } else {
             pb_next = raw_block(min(t + 1 + ahead, clampt));
         }
+        // FP8: widen tile t+1 into its buffers (last read at tile t-3, or t-2 by
+        // the late waves' V products); past the last tile this refills buffers
+        // that nobody reads again
+        if constexpr (F8) store8(st8, std::integral_constant<int, (B + 1) & 3>());
     };
     auto tile_loop = [&](auto role) __attribute__((always_inline)) {
         for (int t = 0; t < ntiles; t += 4) {
@@ -1043,7 +1214,7 @@ static hipError_t launch_prefill_g(const PrefillArgs& a, hipStream_t s, dim3 gri
     return launch(prefill_kernel<DT, F8, D, 0>, grid, dim3(512), s, a);
 }
 
-// the 16x16x32 kernel: every FP8 prefill, and 16-bit prefill at head_dim 64
+// the 16x16x32 kernel: head_dim 64, over either cache
 template <bool F8>
 static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
     const int positions = kRows / a.group;
@@ -1052,34 +1223,35 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t s) {
     if (wgs == 0) return hipSuccess;
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs);
-    if (a.head_dim == 128) {
-        if constexpr (F8) {
-            return a.dtype == kF16 ? launch_prefill_g<kF16, F8, 128>(a, s, grid)
-                                   : launch_prefill_g<kBF16, F8, 128>(a, s, grid);
-        } else {
-            return hipErrorInvalidValue;   // 16-bit at head_dim 128 runs prefill16_kernel
-        }
-    }
+    if (a.head_dim != 64) return hipErrorInvalidValue;   // head_dim 128 runs prefill16_kernel
     return a.dtype == kF16 ? launch_prefill_g<kF16, F8, 64>(a, s, grid)
                            : launch_prefill_g<kBF16, F8, 64>(a, s, grid);
 }
 
-template <int DT>
+template <int DT, bool F8>
 static hipError_t launch_prefill16_g(const PrefillArgs& a, hipStream_t s, dim3 grid) {
-    return a.block_shift == 1 ? launch(prefill16_kernel<DT, 1>, grid, dim3(64 * kW16), s, a)
-                              : launch(prefill16_kernel<DT, 0>, grid, dim3(64 * kW16), s, a);
+    if constexpr (F8) {   // FP8 pools only come in 16-token blocks
+        return launch(prefill16_kernel<DT, 0, true>, grid, dim3(64 * kW16), s, a);
+    } else {
+        return a.block_shift == 1 ? launch(prefill16_kernel<DT, 1, false>, grid, dim3(64 * kW16), s, a)
+                                  : launch(prefill16_kernel<DT, 0, false>, grid, dim3(64 * kW16), s, a);
+    }
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
-    if (a.head_dim != kPD) return launch_prefill_t<false>(a, s);
+// head_dim 128: the 32x32x16 kernel; head_dim 64: the 16x16x32 one
+template <bool F8>
+static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t s) {
+    if (a.head_dim != kPD) return launch_prefill_t<F8>(a, s);
     const int positions = kRows16 / a.group;
     const int64_t qtiles = (a.max_q_len + positions - 1) / positions;
     const int64_t wgs = qtiles * a.num_seqs * a.num_kv_heads;
     if (wgs == 0) return hipSuccess;
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs);
-    return a.dtype == kF16 ? launch_prefill16_g<kF16>(a, s, grid) : launch_prefill16_g<kBF16>(a, s, grid);
+    return a.dtype == kF16 ? launch_prefill16_g<kF16, F8>(a, s, grid) : launch_prefill16_g<kBF16, F8>(a, s, grid);
 }
-hipError_t launch_prefill_fp8(const PrefillArgs& a, hipStream_t s) { return launch_prefill_t<true>(a, s); }
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) { return launch_prefill_d<false>(a, s); }
+hipError_t launch_prefill_fp8(const PrefillArgs& a, hipStream_t s) { return launch_prefill_d<true>(a, s); }
 
 }  // namespace pa

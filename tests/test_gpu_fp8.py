@@ -254,6 +254,65 @@ def test_fp8_prefill_shapes(dtype, hq, hkv, d):
     _check_fp8_prefill(c)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("hq,hkv", [(48, 2), (64, 2), (128, 1)])
+def test_fp8_prefill_large_groups(hq, hkv, d):
+    """24, 32 and 128 q heads per kv head over the FP8 cache: a workgroup holds
+    few positions (idle rows when the group does not divide it)."""
+    c = make_prefill_case(name=f"fp8-prefill-group-{hq // hkv}-d{d}", seed=93 + hq + d,
+                          dtype="bf16", num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                          q_lens=[9, 0, 4, 1, 23], ctx_lens=[30, 5, 0, 70, 2],
+                          scale=1 / math.sqrt(d), extra_blocks=2)
+    _check_fp8_prefill(c)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_fp8_prefill_long_context(dtype):
+    """~9000 cached keys over the FP8 cache: many key tiles per workgroup."""
+    c = make_prefill_case(name=f"fp8-long-{dtype}", seed=36, dtype=dtype, num_q_heads=8,
+                          num_kv_heads=2, head_dim=128, q_lens=[70, 3], ctx_lens=[9050, 4100],
+                          scale=1 / math.sqrt(128))
+    _check_fp8_prefill(c)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_prefill_wide_value_range(d):
+    """The prefill counterpart of the decode range test: k and v rows scaled by
+    powers of two from 2^-12 to 2^8 per token and head, so that the scales'
+    exponents and mantissa factors span a wide range on every key tile."""
+    for dtype, hq in (("f16", 8), ("bf16", 4), ("f16", 2)):
+        c = make_prefill_case(name=f"fp8-prefill-range-{dtype}-{hq}-d{d}", seed=43 + hq + d,
+                              dtype=dtype, num_q_heads=hq, num_kv_heads=2, head_dim=d,
+                              q_lens=[5, 70, 130, 33], ctx_lens=[0, 40, 170, 3], scale=0.08)
+        g = Fp8PrefillOnGPU(c)
+        rng = np.random.default_rng(44)
+        k = rng.integers(-12, 9, size=g.key_np.shape[:2])
+        for arr in (g.key_np, g.value_np):
+            x = oracle.bits_to_float64(arr, dtype) * np.ldexp(1.0, k)[..., None]
+            if dtype == "f16":
+                arr[:] = x.astype(np.float16).view(np.uint16)
+            else:
+                arr[:] = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        g.key = dev_bits(g.key_np, dtype)
+        g.value = dev_bits(g.value_np, dtype)
+        g.write()
+        kc, vc, ks, vs = _check_pools(g)
+        ref = oracle.ref_prefill_paged_fp8(c.q, kc, vc, ks, vs, c.block_tables, c.ctx_lens,
+                                           c.query_start_loc, c.scale, dtype)
+        out = host_f64(g.prefill())
+        # a convex combination of v rows: the error is measured against the
+        # largest |v| of the sequence's kv head, with the usual tolerances
+        vmax = np.ones_like(ref[..., :1])
+        for b in range(c.num_seqs):
+            lo, hi = int(c.query_start_loc[b]), int(c.query_start_loc[b + 1])
+            n = int(c.ctx_lens[b] + c.q_lens[b])
+            v = oracle.dequantize_e4m3_rows(oracle.gather_tokens(vc, c.block_tables[b], n),
+                                            oracle.gather_scales(vs, c.block_tables[b], n))
+            vmax[lo:hi, :, 0] = np.abs(v).max(axis=(0, 2))[np.arange(hq) // (hq // 2)]
+        rel = float((np.abs(out - ref) / vmax).max())
+        assert rel <= TOL[dtype], (dtype, hq, d, rel)
+
+
 def test_fp8_prefill_chunked_reduced():
     _check_fp8_prefill(prefill_chunked(batch=4, new_tokens=600, max_ctx=700))
 
