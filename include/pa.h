@@ -31,7 +31,8 @@
  * "vLLM 的 PagedAttention 数据结构", the PagedKVCache sketch); the FP8 calls
  * take 16 only.  head_dim is 64 or 128.  The attention calls take pools of at
  * most 2^31 blocks (2^30 with 32-token blocks), the range an int32 table entry
- * can name in 16-token units; a larger num_blocks gives PA_ERR_SHAPE.
+ * can name in 16-token units; a larger num_blocks gives PA_ERR_SHAPE, and so
+ * does an empty pool (num_blocks < 1), also in a call with nothing to do.
  *
  * Streams.  Work is enqueued on `stream` (0 = the null stream).  No call
  * synchronises, reads device memory from the host or allocates, so every call

@@ -86,6 +86,7 @@ def test_reshape_rejects(lib):
     assert _reshape(lib, nb=0) == SHAPE
     assert _reshape(lib, key=FAKE + 2) == ALIGN
     assert _reshape(lib, n=0, key=None) == PA_OK    # nothing to do, nothing launched
+    assert _reshape(lib, n=0, nb=0) == SHAPE          # an empty pool, even with nothing to do
 
 
 def _decode(lib, fn="pa_decode", out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, b=2, hq=8,
@@ -201,6 +202,7 @@ def test_prefill_rejects(lib):
     assert _prefill(lib, scale=float("inf")) == SHAPE
     assert _prefill(lib, q=FAKE + 2) == ALIGN
     assert _prefill(lib, t=0, q=None) == PA_OK
+    assert _prefill(lib, t=0, nb=0) == SHAPE           # an empty pool, even with no rows
 
 
 def test_copy_blocks_rejects(lib):

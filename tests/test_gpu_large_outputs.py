@@ -24,7 +24,7 @@ oracle's value):
   the sums and the division, bounded for these sizes.
 
 The two weighted sums are the oracle's own attention applied to |V - ref|
-and |V| (oracle.ref_contiguous_attention over the same keys).
+and |V| (gpu_helpers.weighted_sums).
 """
 
 import numpy as np
@@ -32,14 +32,13 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import (TORCH_DTYPE, DecodeOnGPU, PrefillOnGPU, Fp8DecodeOnGPU, Fp8PrefillOnGPU,
-                         host_f64, require_gpu, ulps)
+from gpu_helpers import (EPS32, TORCH_DTYPE, DecodeOnGPU, PrefillOnGPU, Fp8DecodeOnGPU,
+                         Fp8PrefillOnGPU, host_f64, require_gpu, ulps, weighted_sums)
 from workloads import make_decode_case, make_prefill_case
 
 pytestmark = pytest.mark.gpu
 
 U_BF16 = 2.0 ** -8
-EPS32 = 2.0 ** -13
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -52,22 +51,6 @@ def _scaled_bits(bits: np.ndarray, dtype: str, factor: float) -> np.ndarray:
     """16-bit patterns times a power of two (exact; NaN stays NaN)."""
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(TORCH_DTYPE[dtype])
     return (t * factor).view(torch.int16).numpy().view(np.uint16)
-
-
-def _weighted_sums(q64, k64, v64, pos, scale, ref):
-    """sum_j w_j |v_j - ref| and sum_j w_j |v_j| for every row, head and element,
-    w the softmax weights of the row's visible keys."""
-    lq, hq, _ = q64.shape
-    group = hq // k64.shape[1]
-    mag = oracle.ref_contiguous_attention(q64, k64, np.abs(v64), scale, pos)
-    dev = np.empty_like(ref)
-    for i in range(lq):
-        for h in range(hq):
-            g = h // group
-            dev[i, h] = oracle.ref_contiguous_attention(
-                q64[i:i + 1, h:h + 1], k64[:, g:g + 1], np.abs(v64[:, g:g + 1] - ref[i, h]), scale,
-                pos[i:i + 1])[0, 0]
-    return dev, mag
 
 
 def _check(got, ref, dev, mag, u, what):
@@ -108,7 +91,7 @@ def test_gqa_decode_large_outputs(hq, hkv):
         k64 = oracle.bits_to_float64(oracle.gather_tokens(kc, c.block_tables[b], n), "bf16")
         v64 = oracle.bits_to_float64(oracle.gather_tokens(vc, c.block_tables[b], n), "bf16")
         q64 = oracle.bits_to_float64(c.q[b], "bf16")[None]
-        dv, mg = _weighted_sums(q64, k64, v64, np.array([n - 1]), c.scale, ref[b][None])
+        dv, mg = weighted_sums(q64, k64, v64, np.array([n - 1]), c.scale, ref[b][None])
         dev[b], mag[b] = dv[0], mg[0]
     for part in (0, 16):
         got = host_f64(g.decode(partition_tokens=part))
@@ -136,7 +119,7 @@ def test_prefill_large_outputs(hq, hkv, d):
         k64 = oracle.bits_to_float64(oracle.gather_tokens(kc, c.block_tables[b], n), "bf16")
         v64 = oracle.bits_to_float64(oracle.gather_tokens(vc, c.block_tables[b], n), "bf16")
         q64 = oracle.bits_to_float64(c.q[lo:lo + L], "bf16")
-        dev[lo:lo + L], mag[lo:lo + L] = _weighted_sums(q64, k64, v64, ctx + np.arange(L), c.scale,
+        dev[lo:lo + L], mag[lo:lo + L] = weighted_sums(q64, k64, v64, ctx + np.arange(L), c.scale,
                                                         ref[lo:lo + L])
     _check(got, ref, dev, mag, U_BF16, f"prefill {hq}/{hkv} D={d}")
 
@@ -160,7 +143,7 @@ def test_fp8_decode_large_outputs(hq, hkv, u):
         k64 = _fp8_tokens(kc, ks, c.block_tables[b], n)
         v64 = _fp8_tokens(vc, vs, c.block_tables[b], n)
         q64 = oracle.bits_to_float64(c.q[b], "bf16")[None]
-        dv, mg = _weighted_sums(q64, k64, v64, np.array([n - 1]), c.scale, ref[b][None])
+        dv, mg = weighted_sums(q64, k64, v64, np.array([n - 1]), c.scale, ref[b][None])
         dev[b], mag[b] = dv[0], mg[0]
     for part in (0, 16):
         got = host_f64(g.decode(partition_tokens=part))
@@ -186,6 +169,6 @@ def test_fp8_prefill_large_outputs():
         k64 = _fp8_tokens(kc, ks, c.block_tables[b], n)
         v64 = _fp8_tokens(vc, vs, c.block_tables[b], n)
         q64 = oracle.bits_to_float64(c.q[lo:lo + L], "bf16")
-        dev[lo:lo + L], mag[lo:lo + L] = _weighted_sums(q64, k64, v64, ctx + np.arange(L), c.scale,
+        dev[lo:lo + L], mag[lo:lo + L] = weighted_sums(q64, k64, v64, ctx + np.arange(L), c.scale,
                                                         ref[lo:lo + L])
     _check(got, ref, dev, mag, U_BF16, "FP8 prefill 8/2")

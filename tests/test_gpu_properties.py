@@ -1,0 +1,234 @@
+"""Property tests of the GPU path (Hypothesis): shapes, lengths and block
+placements drawn at random, every output compared with the float64 oracle.
+
+Lengths are drawn from the edges a paged layout has -- 0, 1, one token short
+of a block, a block, one token past it, exact multiples -- and from a uniform
+range; the q-head group, head_dim, dtype, partition length (fixed, or the
+balanced split) and the physical placement of the blocks (a random
+permutation of the pool, with spare blocks) are drawn too.  The draws are
+derandomised, so a run is reproducible and the examples are the same on every
+run; each example prints what it drew before it runs on the GPU.
+
+Each output must meet the stated tolerance (max-abs 2e-3 for fp16, 1e-2 for
+bf16) or, where the rounding of the path's own arithmetic can exceed it, the
+bound that arithmetic guarantees (gpu_helpers.rounding_bound): the
+matrix-core paths round each probability to the 16-bit type before the PV
+product, which on short contexts with outputs of magnitude ~2 and more can
+move a bf16 output past 1e-2 while staying within about one ulp.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+import oracle
+from gpu_helpers import (U_MFMA, DecodeOnGPU, Fp8DecodeOnGPU, Fp8PrefillOnGPU, PrefillOnGPU,
+                         assert_close_or_bound, dev_bits, host_f64, require_gpu, rounding_bound,
+                         weighted_sums)
+from workloads import make_decode_case, make_prefill_case, normal_bits
+
+pytestmark = pytest.mark.gpu
+
+PROPS = settings(max_examples=100, deadline=None, derandomize=True, database=None,
+                 suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
+
+EDGE_LENS = [0, 1, 2, 15, 16, 17, 31, 32, 33, 48, 64, 127, 128, 129, 255, 256, 257]
+LENS = st.one_of(st.sampled_from(EDGE_LENS), st.integers(0, 700))
+CTX = st.one_of(st.sampled_from([0, 1, 15, 16, 17, 32, 63, 64, 65, 200]), st.integers(0, 400))
+QLEN = st.one_of(st.sampled_from([0, 1, 2, 15, 16, 17, 33, 64, 65, 130]), st.integers(0, 150))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    import paged_kv_cache_24_amd  # noqa: F401  (fails loudly without libpa.so)
+
+
+@st.composite
+def decode_cases(draw, fp8=False):
+    dtype = draw(st.sampled_from(["f16", "bf16"]))
+    d = draw(st.sampled_from([64, 128]))
+    hkv = draw(st.sampled_from([1, 2, 4]))
+    group = draw(st.sampled_from([1, 2, 3, 4, 5, 8, 16, 24] if not fp8 else [1, 2, 4, 8, 16]))
+    n = draw(st.integers(1, 6))
+    lens = draw(st.lists(LENS, min_size=n, max_size=n))
+    need = sum((x + 15) // 16 for x in lens)
+    spare = draw(st.integers(0, 8))
+    mb = max(1, max((x + 15) // 16 for x in lens)) + draw(st.integers(0, 3))
+    seed = draw(st.integers(0, 2 ** 31 - 1))
+    part = draw(st.sampled_from([0, 16, 48, 64, 256, -1]))
+    c = make_decode_case(name=f"prop-{dtype}-d{d}-{hkv}x{group}", seed=seed, dtype=dtype,
+                         num_q_heads=hkv * group, num_kv_heads=hkv, head_dim=d, seq_lens=lens,
+                         num_blocks=max(1, need + spare), max_blocks_per_seq=mb,
+                         scale=1 / math.sqrt(d), write_last=True)
+    return c, part
+
+
+def _tokens16(pool, table_row, n, dtype):
+    return oracle.bits_to_float64(oracle.gather_tokens(pool, table_row, n), dtype)
+
+
+def _tokens8(codes, scales, table_row, n):
+    return oracle.dequantize_e4m3_rows(oracle.gather_tokens(codes, table_row, n),
+                                       oracle.gather_scales(scales, table_row, n))
+
+
+def _decode_bound(c, ref, keys, u, nq=1, qm=None):
+    """bound_fn for decode outputs ref [B, Hq, D] (or [B, nq, Hq, D] with the
+    queries qm of multi-query decode); keys(b, n) -> (k64, v64)."""
+    def fn():
+        out = np.zeros_like(ref)
+        for b in range(c.num_seqs):
+            n = int(c.seq_lens[b])
+            if n == 0:
+                continue
+            k64, v64 = keys(b, n)
+            pos = n - nq + np.arange(nq)
+            live = pos >= 0
+            q = (c.q[b][None] if qm is None else qm[b])[live]
+            r = (ref[b][None] if nq == 1 else ref[b])[live]
+            dv, mg = weighted_sums(oracle.bits_to_float64(q, c.dtype), k64, v64, pos[live], c.scale, r)
+            bound = rounding_bound(r, c.dtype, dv, mg, u)
+            if nq == 1:
+                out[b] = bound[0]
+            else:
+                out[b][live] = bound
+        return out
+    return fn
+
+
+def _prefill_bound(c, ref, keys, u):
+    def fn():
+        out = np.zeros_like(ref)
+        for b in range(c.num_seqs):
+            lo, L, ctx = int(c.query_start_loc[b]), int(c.q_lens[b]), int(c.ctx_lens[b])
+            if L == 0:
+                continue
+            k64, v64 = keys(b, ctx + L)
+            dv, mg = weighted_sums(oracle.bits_to_float64(c.q[lo:lo + L], c.dtype), k64, v64,
+                                   ctx + np.arange(L), c.scale, ref[lo:lo + L])
+            out[lo:lo + L] = rounding_bound(ref[lo:lo + L], c.dtype, dv, mg, u)
+        return out
+    return fn
+
+
+def _mfma_decode(c, cols):
+    """The decode paths on matrix cores: head_dim 128 with 3 or more columns per kv head."""
+    return c.head_dim == 128 and cols >= 3
+
+
+def _say(c, **kw):
+    extra = " ".join(f"{k}={v}" for k, v in kw.items())
+    print(f"[property] {c.name} lens={list(map(int, getattr(c, 'seq_lens', getattr(c, 'q_lens', []))))} "
+          f"{extra}", flush=True)
+
+
+@PROPS
+@given(decode_cases())
+def test_decode_matches_oracle(drawn):
+    c, part = drawn
+    _say(c, partition=part)
+    g = DecodeOnGPU(c)
+    g.write()
+    kc, vc = oracle.ref_reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache, c.slot_mapping)
+    ref = oracle.ref_decode(c.q, kc, vc, c.block_tables, c.seq_lens, c.scale, c.dtype)
+    out = host_f64(g.decode(partition_tokens=part))
+    u = U_MFMA[c.dtype] if _mfma_decode(c, c.num_q_heads // c.num_kv_heads) else 0.0
+    keys = lambda b, n: (_tokens16(kc, c.block_tables[b], n, c.dtype),
+                         _tokens16(vc, c.block_tables[b], n, c.dtype))
+    assert_close_or_bound(out, ref, c.dtype, _decode_bound(c, ref, keys, u),
+                          f"{c.name} partition={part}")
+    # the cache write itself: whole pools bit-exact
+    np.testing.assert_array_equal(g.k_cache.view(torch.int16).cpu().numpy().view(np.uint16), kc)
+    np.testing.assert_array_equal(g.v_cache.view(torch.int16).cpu().numpy().view(np.uint16), vc)
+
+
+@PROPS
+@given(decode_cases(fp8=True))
+def test_fp8_decode_matches_oracle(drawn):
+    c, part = drawn
+    _say(c, partition=part, cache="fp8")
+    g = Fp8DecodeOnGPU(c)
+    g.write()
+    kc, vc, ks, vs = g.oracle_pools()
+    np.testing.assert_array_equal(g.k_cache.cpu().numpy(), kc)
+    np.testing.assert_array_equal(g.v_scales.cpu().numpy(), vs)
+    ref = oracle.ref_decode_fp8(c.q, kc, vc, ks, vs, c.block_tables, c.seq_lens, c.scale, c.dtype)
+    out = host_f64(g.decode(partition_tokens=part))
+    u = U_MFMA[c.dtype] if _mfma_decode(c, c.num_q_heads // c.num_kv_heads) else 0.0
+    keys = lambda b, n: (_tokens8(kc, ks, c.block_tables[b], n), _tokens8(vc, vs, c.block_tables[b], n))
+    assert_close_or_bound(out, ref, c.dtype, _decode_bound(c, ref, keys, u),
+                          f"{c.name} fp8 partition={part}")
+
+
+@PROPS
+@given(decode_cases(), st.integers(2, 5))
+def test_multi_query_matches_oracle(drawn, nq):
+    import paged_kv_cache_24_amd as pa
+    c, part = drawn
+    part = max(part, 0)   # the balanced split is a single-query layout
+    _say(c, partition=part, queries=nq)
+    g = DecodeOnGPU(c)
+    g.write()
+    kc, vc = oracle.ref_reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache, c.slot_mapping)
+    q = normal_bits(np.random.default_rng(nq), (c.num_seqs, nq, c.num_q_heads, c.head_dim), c.dtype)
+    qm = dev_bits(q, c.dtype)
+    ref = oracle.ref_decode_multi(q, kc, vc, c.block_tables, c.seq_lens, c.scale, c.dtype)
+    out = torch.empty_like(qm)
+    pa.pa_decode_multi(out, qm, g.k_cache, g.v_cache, g.tables, g.lens, c.scale, part)
+    u = U_MFMA[c.dtype] if _mfma_decode(c, nq * (c.num_q_heads // c.num_kv_heads)) else 0.0
+    keys = lambda b, n: (_tokens16(kc, c.block_tables[b], n, c.dtype),
+                         _tokens16(vc, c.block_tables[b], n, c.dtype))
+    assert_close_or_bound(host_f64(out), ref, c.dtype, _decode_bound(c, ref, keys, u, nq, q),
+                          f"{c.name} Q={nq} partition={part}")
+
+
+@st.composite
+def prefill_cases(draw, fp8=False):
+    dtype = draw(st.sampled_from(["f16", "bf16"]))
+    d = draw(st.sampled_from([64, 128]))
+    hkv = draw(st.sampled_from([1, 2, 4]))
+    group = draw(st.sampled_from([1, 2, 3, 4, 6, 8, 16, 24, 32]))
+    n = draw(st.integers(1, 5))
+    q_lens = draw(st.lists(QLEN, min_size=n, max_size=n))
+    ctx = draw(st.lists(CTX, min_size=n, max_size=n))
+    seed = draw(st.integers(0, 2 ** 31 - 1))
+    spare = draw(st.integers(0, 6))
+    if sum(q_lens) + sum(ctx) == 0:
+        spare = max(spare, 1)   # the calls take pools of at least one block
+    return make_prefill_case(name=f"prop-prefill-{dtype}-d{d}-{hkv}x{group}", seed=seed, dtype=dtype,
+                             num_q_heads=hkv * group, num_kv_heads=hkv, head_dim=d, q_lens=q_lens,
+                             ctx_lens=ctx, scale=1 / math.sqrt(d), extra_blocks=spare)
+
+
+@PROPS
+@given(prefill_cases())
+def test_prefill_matches_oracle(c):
+    _say(c, ctx=list(map(int, c.ctx_lens)))
+    g = PrefillOnGPU(c)
+    g.write()
+    kc, vc = oracle.ref_reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache, c.slot_mapping)
+    ref = oracle.ref_prefill_paged(c.q, kc, vc, c.block_tables, c.ctx_lens, c.query_start_loc,
+                                   c.scale, c.dtype)
+    keys = lambda b, n: (_tokens16(kc, c.block_tables[b], n, c.dtype),
+                         _tokens16(vc, c.block_tables[b], n, c.dtype))
+    assert_close_or_bound(host_f64(g.prefill()), ref, c.dtype,
+                          _prefill_bound(c, ref, keys, U_MFMA[c.dtype]), c.name)
+
+
+@PROPS
+@given(prefill_cases(fp8=True))
+def test_fp8_prefill_matches_oracle(c):
+    _say(c, ctx=list(map(int, c.ctx_lens)), cache="fp8")
+    g = Fp8PrefillOnGPU(c)
+    g.write()
+    kc, vc, ks, vs = g.oracle_pools()
+    ref = oracle.ref_prefill_paged_fp8(c.q, kc, vc, ks, vs, c.block_tables, c.ctx_lens,
+                                       c.query_start_loc, c.scale, c.dtype)
+    keys = lambda b, n: (_tokens8(kc, ks, c.block_tables[b], n), _tokens8(vc, vs, c.block_tables[b], n))
+    assert_close_or_bound(host_f64(g.prefill()), ref, c.dtype,
+                          _prefill_bound(c, ref, keys, U_MFMA[c.dtype]), c.name + " fp8")
