@@ -52,7 +52,8 @@
  * interface.  Device-resident indices are not validated on the host (that
  * would need a read-back): a block-table entry outside [0, num_blocks) or a
  * slot outside [0, num_blocks * block_size) is never dereferenced -- the
- * kernels skip it -- but results involving it are unspecified.
+ * kernels skip it -- but results involving it are unspecified.  A debug build
+ * of the library reports such indices (pa_debug_bounds, at the end).
  */
 #ifndef PA_H
 #define PA_H
@@ -75,13 +76,21 @@ typedef enum pa_status {
     PA_ERR_WORKSPACE = -4,   /* decode workspace missing or too small */
     PA_ERR_HIP = -5,         /* the HIP runtime refused a launch */
     PA_ERR_ALIGNMENT = -6,   /* a tensor or the workspace is not 16-byte aligned */
-    PA_ERR_SCRATCH = -7      /* pa_decode_noalloc: partials exceed PA_NOALLOC_SCRATCH_BYTES */
+    PA_ERR_SCRATCH = -7,     /* pa_decode_noalloc: partials exceed PA_NOALLOC_SCRATCH_BYTES */
+    PA_STATUS_RANGE_MAX_ = 0x7fffffff   /* not a status: see below */
 } pa_status;
 
 typedef enum pa_dtype {
     PA_F16 = 0,  /* IEEE binary16 */
-    PA_BF16 = 1  /* bfloat16 */
+    PA_BF16 = 1, /* bfloat16 */
+    PA_DTYPE_RANGE_MIN_ = -0x7fffffff - 1,   /* not types: see below */
+    PA_DTYPE_RANGE_MAX_ = 0x7fffffff
 } pa_dtype;
+/* The *_RANGE_* enumerators are never returned or accepted as values.  They
+ * make every 32-bit integer a value of the enum type (in C++ an enum holds only
+ * the values of the smallest bit-field that spans its enumerators), so a
+ * caller's unknown dtype or status is refused or named "unknown" instead of
+ * being undefined behaviour inside the library. */
 
 #define PA_BLOCK_SIZE 16
 
@@ -446,6 +455,37 @@ pa_status pa_prefill_paged_fp8(void* out, const void* q, const void* k_cache, co
                                int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
                                int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                int64_t num_blocks, float scale, pa_dtype dtype, hipStream_t stream);
+
+/*
+ * pa_debug_bounds -- the index checks of a debug build.  Device-resident
+ * indices are not validated by the normal library (see "Errors" above).  A
+ * library built with PA_DEBUG_BOUNDS defined (libpa_debug.so) launches, ahead
+ * of each call's own kernels, a check of the indices that call is about to
+ * use, which sets bits of a device word ("Hardware abstraction and
+ * portability", §六: asynchronous errors surface at synchronisation points):
+ *
+ *   PA_DEBUG_BLOCK_ID     a block-table entry of a block some sequence uses
+ *                         (its first ceil(seq_len / 16) blocks, or ctx + chunk
+ *                         in prefill) is outside [0, num_blocks), or a copy
+ *                         pair names a block >= num_blocks;
+ *   PA_DEBUG_SEQ_LEN      a seq_len (or ctx_len + chunk length) is negative or
+ *                         larger than the table row can name;
+ *   PA_DEBUG_SLOT         a cache-write slot is >= num_blocks * block_size;
+ *   PA_DEBUG_QUERY_RANGE  query_start_loc is not non-decreasing within
+ *                         [0, num_tokens], or a chunk is longer than max_q_len.
+ *
+ * Negative slots and copy pairs stay legal padding.  pa_debug_bounds waits for
+ * `stream`, stores the bits set since the last clear in *word and, if `clear`
+ * is non-zero, clears them.  It synchronises, so it is the one call that
+ * cannot be captured in a graph.  In the normal library it returns
+ * PA_ERR_UNSUPPORTED and does nothing.  The word is per device and shared by
+ * every caller of the library on it.
+ */
+#define PA_DEBUG_BLOCK_ID 1u
+#define PA_DEBUG_SEQ_LEN 2u
+#define PA_DEBUG_SLOT 4u
+#define PA_DEBUG_QUERY_RANGE 8u
+pa_status pa_debug_bounds(uint32_t* word, int32_t clear, hipStream_t stream);
 
 #ifdef __cplusplus
 }

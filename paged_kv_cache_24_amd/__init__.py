@@ -12,6 +12,10 @@ Names follow the C ABI: ``pa_reshape_and_cache``, ``pa_copy_blocks``, ``pa_decod
 ``pa_reshape_and_cache_fp8``, ``pa_copy_blocks_fp8``, ``pa_decode_fp8``,
 ``pa_decode_partitions_fp8``, ``pa_prefill_paged_fp8``, and ``pa_decode_noalloc`` for
 callers that cannot allocate (its split-KV partials live in a static scratch).
+
+With the environment variable ``PA_DEBUG_BOUNDS=1`` set at import, the package
+loads ``libpa_debug.so`` instead: the same kernels, with every call's
+device-resident indices checked first; ``pa_debug_bounds`` reads the result.
 """
 
 from __future__ import annotations
@@ -28,13 +32,17 @@ __all__ = [
     "pa_decode_partitions", "pa_decode_merge", "pa_prefill_paged",
     "pa_reshape_and_cache_fp8", "pa_copy_blocks_fp8", "pa_decode_fp8", "pa_decode_partitions_fp8",
     "pa_prefill_paged_fp8", "pa_decode_multi", "pa_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "pa_debug_bounds", "DEBUG_BOUNDS_BITS",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "libpa_debug.so" if os.environ.get("PA_DEBUG_BOUNDS") == "1" else "libpa.so")
 BLOCK_SIZE = 16
 PA_DECODE_STREAM_KV = 1   # no physical block is read twice in the call: stream K/V
 PA_PARTITION_BALANCED = -1   # partition_tokens value: the balanced split of decode work
 NOALLOC_SCRATCH_BYTES = 64 << 20   # PA_NOALLOC_SCRATCH_BYTES: static scratch of pa_decode_noalloc
+# bits of pa_debug_bounds (PA_DEBUG_* in pa.h)
+DEBUG_BOUNDS_BITS = {"block_id": 1, "seq_len": 2, "slot": 4, "query_range": 8}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -76,6 +84,7 @@ _SIGS = {
     "pa_decode_partitions_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                         _i32, _i32, _i32, _i64, _f32, _i32, _i32, _u32, _vp, _sz,
                                         _vp]),
+    "pa_debug_bounds": (_i32, [ctypes.POINTER(_u32), _i32, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -421,3 +430,12 @@ def pa_prefill_paged_fp8(out, q, k_cache, v_cache, k_scales, v_scales, block_tab
         _ptr(block_tables), _ptr(ctx_lens), _ptr(query_start_loc), b, t, int(max_q_len), hq, hkv, d,
         bs, block_tables.shape[1], nb, float(scale), _kv_dtype(q), _stream(stream)))
     return out
+
+
+def pa_debug_bounds(clear: bool = True, stream=None) -> int:
+    """The bits the index checks of a debug build (libpa_debug.so, loaded with
+    PA_DEBUG_BOUNDS=1) set since the last clear; waits for the stream.  Raises
+    PagedKVError (unsupported) with the normal library."""
+    word = _u32(0)
+    _check("pa_debug_bounds", lib.pa_debug_bounds(ctypes.byref(word), 1 if clear else 0, _stream(stream)))
+    return int(word.value)

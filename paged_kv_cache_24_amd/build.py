@@ -1,8 +1,11 @@
 """Build libpa.so for gfx950 in-tree with hipcc.
 
 ``python paged_kv_cache_24_amd/build.py`` compiles every HIP source under
-``csrc/`` (in parallel) and links ``paged_kv_cache_24_amd/libpa.so``.  Run it as
-a script (or load it by path): importing the package itself needs the library.
+``csrc/`` (in parallel) and links ``paged_kv_cache_24_amd/libpa.so``, and beside
+it ``libpa_debug.so``: the same kernels with the C ABI layer compiled with
+PA_DEBUG_BOUNDS, which checks the device-resident indices of every call
+(pa_debug_bounds in include/pa.h).  Run it as a script (or load it by path):
+importing the package itself needs the library.
 """
 
 from __future__ import annotations
@@ -19,9 +22,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libpa.so")
+DEBUG_LIB_PATH = os.path.join(PKG, "libpa_debug.so")
 ARCH = "gfx950"
 
-SOURCES = ["pa_api.hip", "reshape_and_cache.hip", "copy_blocks.hip", "decode.hip", "decode_fp8.hip", "prefill.hip"]
+SOURCES = ["pa_api.hip", "reshape_and_cache.hip", "copy_blocks.hip", "decode.hip", "decode_fp8.hip", "prefill.hip",
+           "debug_bounds.hip"]
 
 COMPILE_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -56,7 +61,8 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile and link libpa.so; returns its path.  Always recompiles."""
+    """Compile and link libpa.so and libpa_debug.so; returns the path of
+    libpa.so.  Always recompiles."""
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     objs = []
@@ -65,11 +71,16 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         jobs.append([hipcc, *COMPILE_FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
+    # the debug library differs in the C ABI layer only
+    api_debug = os.path.join(BUILD_DIR, "pa_api_debug.o")
+    jobs.append([hipcc, *COMPILE_FLAGS, *extra_flags, "-DPA_DEBUG_BOUNDS", "-c",
+                 os.path.join(CSRC, "pa_api.hip"), "-o", api_debug])
     with ThreadPoolExecutor(min(len(jobs), os.cpu_count() or 1)) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
-    tmp = LIB_PATH + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB_PATH)
+    for path, lib_objs in ((LIB_PATH, objs), (DEBUG_LIB_PATH, [api_debug] + objs[1:])):
+        tmp = path + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *lib_objs], verbose)
+        os.replace(tmp, path)
     return LIB_PATH
 
 

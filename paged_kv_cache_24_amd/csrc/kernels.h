@@ -120,4 +120,27 @@ struct PrefillArgs {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_fp8(const PrefillArgs& a, hipStream_t stream);
 
+// Debug builds (PA_DEBUG_BOUNDS): before a call's own kernels, one small kernel
+// checks the device-resident indices the call is about to use and sets bits
+// of a device word for what it finds out of range (the bit values of pa.h).
+enum : uint32_t { kBoundsBlockId = 1u, kBoundsSeqLen = 2u, kBoundsSlot = 4u, kBoundsQueryRange = 8u };
+enum : int32_t { kBoundsDecode = 0, kBoundsPrefill = 1, kBoundsSlots = 2, kBoundsPairs = 3 };
+struct BoundsArgs {
+    uint32_t* word;
+    int32_t kind;
+    const int32_t* block_tables;      // decode, prefill
+    const int32_t* seq_lens;          // decode: tokens of each sequence
+    const int32_t* ctx_lens;          // prefill
+    const int32_t* query_start_loc;   // prefill
+    const int64_t* indices;           // slots (cache write) or (src, dst) pairs (block copy)
+    int64_t count;                    // sequences, tokens or pairs
+    int64_t num_tokens;               // prefill: packed query rows
+    int64_t limit;                    // 16-token blocks in the pool, or slots for a cache write
+    int32_t table_stride;
+    int32_t block_shift;
+    int32_t max_blocks16;             // 16-token blocks a table row can name
+    int32_t max_q_len;
+};
+hipError_t launch_bounds_check(const BoundsArgs& a, hipStream_t stream);
+
 }  // namespace pa

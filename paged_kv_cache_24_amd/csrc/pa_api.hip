@@ -21,26 +21,77 @@
 // hipGetSymbolAddress, and only that address is ever handed to a kernel.
 static __device__ __align__(256) float scratch[PA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
+#ifdef PA_DEBUG_BOUNDS
+// Debug builds: the word the index checks set bits in (one per device, like
+// `scratch`; read and cleared by pa_debug_bounds).
+static __device__ uint32_t debug_word;
+static_assert(pa::kBoundsBlockId == PA_DEBUG_BLOCK_ID && pa::kBoundsSeqLen == PA_DEBUG_SEQ_LEN &&
+                  pa::kBoundsSlot == PA_DEBUG_SLOT && pa::kBoundsQueryRange == PA_DEBUG_QUERY_RANGE,
+              "the kernels' bits are the header's");
+#endif
+
 namespace {
 
 constexpr int kMaxDevices = 64;
 std::atomic<void*> g_scratch_addr[kMaxDevices];
 std::mutex g_scratch_mutex;
 
-// Device address of the current device's scratch copy, or nullptr when the
-// device cannot be queried or the symbol cannot be resolved.
-void* scratch_address() {
+// Device address of the current device's copy of a __device__ variable, looked
+// up once per device and kept in `cache`; nullptr when the device cannot be
+// queried or the symbol cannot be resolved.
+template <class Symbol>
+void* symbol_address(std::atomic<void*> (&cache)[kMaxDevices], const Symbol& symbol) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-    void* ptr = g_scratch_addr[dev].load(std::memory_order_acquire);
+    void* ptr = cache[dev].load(std::memory_order_acquire);
     if (ptr) return ptr;
     std::lock_guard<std::mutex> lock(g_scratch_mutex);
-    ptr = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    ptr = cache[dev].load(std::memory_order_relaxed);
     if (!ptr) {
-        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
-        g_scratch_addr[dev].store(ptr, std::memory_order_release);
+        if (hipGetSymbolAddress(&ptr, symbol) != hipSuccess) return nullptr;
+        cache[dev].store(ptr, std::memory_order_release);
     }
     return ptr;
+}
+
+void* scratch_address() { return symbol_address(g_scratch_addr, HIP_SYMBOL(scratch)); }
+
+#ifdef PA_DEBUG_BOUNDS
+std::atomic<void*> g_debug_addr[kMaxDevices];
+uint32_t* debug_word_address() {
+    return static_cast<uint32_t*>(symbol_address(g_debug_addr, HIP_SYMBOL(debug_word)));
+}
+
+// enqueue the index checks of a call; false if they could not be launched
+bool check_bounds(pa::BoundsArgs a, hipStream_t stream) {
+    a.word = debug_word_address();
+    return a.word && pa::launch_bounds_check(a, stream) == hipSuccess;
+}
+
+pa::BoundsArgs bounds_args(int32_t kind, int64_t count, int64_t limit) {
+    pa::BoundsArgs a{};
+    a.kind = kind;
+    a.count = count;
+    a.limit = limit;
+    return a;
+}
+#endif
+
+// the index checks of a decode call (debug builds; true elsewhere)
+bool check_decode_bounds(const pa::DecodeArgs& d, hipStream_t stream) {
+#ifdef PA_DEBUG_BOUNDS
+    pa::BoundsArgs ba = bounds_args(pa::kBoundsDecode, d.num_seqs, d.num_blocks);
+    ba.block_tables = d.block_tables;
+    ba.seq_lens = d.seq_lens;
+    ba.table_stride = d.table_stride;
+    ba.block_shift = d.block_shift;
+    ba.max_blocks16 = d.max_blocks_per_seq;
+    return check_bounds(ba, stream);
+#else
+    (void)d;
+    (void)stream;
+    return true;
+#endif
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -307,6 +358,11 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
     a.num_tokens = num_tokens;
     a.num_slots = num_blocks * block_size;   // a slot's row sits at the same place for any block_size
     a.row_vecs = num_kv_heads * head_dim / 8;
+#ifdef PA_DEBUG_BOUNDS
+    pa::BoundsArgs ba = bounds_args(pa::kBoundsSlots, num_tokens, a.num_slots);
+    ba.indices = slot_mapping;
+    if (!check_bounds(ba, stream)) return PA_ERR_HIP;
+#endif
     return pa::launch_reshape_and_cache(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -327,6 +383,11 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pair
     a.num_blocks = num_blocks;
     a.block_vecs = (int64_t)block_size * num_kv_heads * head_dim / 8;
     a.wgs_per_pair = (a.block_vecs + 1023) / 1024;
+#ifdef PA_DEBUG_BOUNDS
+    pa::BoundsArgs ba = bounds_args(pa::kBoundsPairs, num_pairs, num_blocks);
+    ba.indices = block_pairs;
+    if (!check_bounds(ba, stream)) return PA_ERR_HIP;
+#endif
     return pa::launch_copy_blocks(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -359,6 +420,11 @@ pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* k_c
     a.num_kv_heads = num_kv_heads;
     a.head_dim = head_dim;
     a.dtype = dtype == PA_F16 ? pa::kF16 : pa::kBF16;
+#ifdef PA_DEBUG_BOUNDS
+    pa::BoundsArgs ba = bounds_args(pa::kBoundsSlots, num_tokens, a.num_slots);
+    ba.indices = slot_mapping;
+    if (!check_bounds(ba, stream)) return PA_ERR_HIP;
+#endif
     return pa::launch_reshape_and_cache_fp8(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -383,6 +449,11 @@ pa_status pa_copy_blocks_fp8(void* k_cache, void* v_cache, float* k_scales, floa
     a.block_vecs = (int64_t)num_kv_heads * head_dim;
     a.wgs_per_pair = (a.block_vecs + 1023) / 1024;
     if (num_pairs > INT32_MAX / a.wgs_per_pair) return PA_ERR_SHAPE;   // checked before either launch
+#ifdef PA_DEBUG_BOUNDS
+    pa::BoundsArgs ba = bounds_args(pa::kBoundsPairs, num_pairs, num_blocks);
+    ba.indices = block_pairs;
+    if (!check_bounds(ba, stream)) return PA_ERR_HIP;
+#endif
     if (pa::launch_copy_blocks(a, stream) != hipSuccess) return PA_ERR_HIP;
     a.k_cache = k_scales;
     a.v_cache = v_scales;
@@ -453,6 +524,7 @@ pa_status pa_decode_partitions(void* out, const void* q, const void* k_cache, co
                                          max_blocks_per_seq, num_blocks, scale, dtype, shape,
                                          workspace, flags);
     if (!decode_grids_fit(a)) return PA_ERR_SHAPE;
+    if (!check_decode_bounds(a, stream)) return PA_ERR_HIP;
     return pa::launch_decode_partitions(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -518,6 +590,7 @@ pa_status pa_decode_partitions_fp8(void* out, const void* q, const void* k_cache
     a.k_scales = k_scales;
     a.v_scales = v_scales;
     if (!decode_grids_fit(a)) return PA_ERR_SHAPE;
+    if (!check_decode_bounds(a, stream)) return PA_ERR_HIP;
     return pa::launch_decode_partitions_fp8(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
@@ -579,6 +652,7 @@ pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const v
                                          max_blocks_per_seq, num_blocks, scale, dtype, shape,
                                          workspace, flags, q_per_seq);
     if (!decode_grids_fit(a)) return PA_ERR_SHAPE;
+    if (!check_decode_bounds(a, stream)) return PA_ERR_HIP;
     if (pa::launch_decode_partitions(a, stream) != hipSuccess) return PA_ERR_HIP;
     if (!shape.balanced && shape.num_parts <= 1) return PA_OK;
     return pa::launch_decode_merge(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -677,6 +751,18 @@ static pa_status prefill_common(void* out, const void* q, const void* k_cache, c
     a.head_dim = head_dim;
     a.k_scales = k_scales;
     a.v_scales = v_scales;
+#ifdef PA_DEBUG_BOUNDS
+    pa::BoundsArgs ba = bounds_args(pa::kBoundsPrefill, num_seqs, a.num_blocks);
+    ba.block_tables = block_tables;
+    ba.ctx_lens = ctx_lens;
+    ba.query_start_loc = query_start_loc;
+    ba.num_tokens = num_tokens;
+    ba.max_q_len = max_q_len;
+    ba.table_stride = a.table_stride;
+    ba.block_shift = sh;
+    ba.max_blocks16 = a.max_blocks_per_seq;
+    if (!check_bounds(ba, stream)) return PA_ERR_HIP;
+#endif
     const hipError_t e = fp8 ? pa::launch_prefill_fp8(a, stream) : pa::launch_prefill(a, stream);
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -704,6 +790,26 @@ pa_status pa_prefill_paged(void* out, const void* q, const void* k_cache, const 
                           query_start_loc, num_seqs, num_tokens, max_q_len, num_q_heads,
                           num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
                           dtype, stream);
+}
+
+pa_status pa_debug_bounds(uint32_t* word, int32_t clear, hipStream_t stream) {
+#ifdef PA_DEBUG_BOUNDS
+    if (!word) return PA_ERR_NULL_PTR;
+    uint32_t* dev = debug_word_address();
+    if (!dev) return PA_ERR_HIP;
+    if (hipMemcpyAsync(word, dev, sizeof(uint32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return PA_ERR_HIP;
+    if (clear && (hipMemsetAsync(dev, 0, sizeof(uint32_t), stream) != hipSuccess ||
+                  hipStreamSynchronize(stream) != hipSuccess))
+        return PA_ERR_HIP;
+    return PA_OK;
+#else
+    (void)word;
+    (void)clear;
+    (void)stream;
+    return PA_ERR_UNSUPPORTED;
+#endif
 }
 
 }  // extern "C"

@@ -10,6 +10,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pa.h")
 LIB = os.path.join(ROOT, "paged_kv_cache_24_amd", "libpa.so")
+DEBUG_LIB = os.path.join(ROOT, "paged_kv_cache_24_amd", "libpa_debug.so")
 
 PA_OK, NULL, UNSUP, SHAPE, WS, HIP, ALIGN, SCRATCH = 0, -1, -2, -3, -4, -5, -6, -7
 F16, BF16 = 0, 1
@@ -41,6 +42,36 @@ def test_header_declares_the_calls():
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared():
         assert hasattr(lib, name), name
+
+
+@pytest.fixture(scope="module")
+def debug_lib():
+    if not os.path.exists(DEBUG_LIB):
+        pytest.fail("libpa_debug.so is not built (python paged_kv_cache_24_amd/build.py)")
+    return ctypes.CDLL(DEBUG_LIB)
+
+
+def test_debug_library_exports_and_refuses_the_same(debug_lib):
+    """libpa_debug.so (PA_DEBUG_BOUNDS) exports every call and validates host
+    arguments exactly as libpa.so does; pa_debug_bounds wants a word."""
+    for name in _declared():
+        assert hasattr(debug_lib, name), name
+    assert _reshape(debug_lib, key=None) == NULL
+    assert _reshape(debug_lib, nb=0) == SHAPE
+    assert _decode(debug_lib, d=96) == UNSUP
+    assert _prefill(debug_lib, t=-1) == SHAPE
+    f = debug_lib.pa_debug_bounds
+    f.restype = ctypes.c_int32
+    f.argtypes = [P, ctypes.c_int32, P]
+    assert f(None, 1, None) == NULL
+
+
+def test_debug_bounds_unsupported_in_the_normal_library(lib):
+    f = lib.pa_debug_bounds
+    f.restype = ctypes.c_int32
+    f.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32, P]
+    word = ctypes.c_uint32(5)
+    assert f(ctypes.byref(word), 1, None) == UNSUP and word.value == 5
 
 
 def test_kv_bytes_per_token(lib):
