@@ -78,9 +78,21 @@ __device__ __forceinline__ uint2 quantize8(const u32x4& w, float& s_out) {
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
     amax = group_max<L>(amax);
     const float s = amax > 0.f ? amax / 448.f : 1.f;
+    // x / s correctly rounded, from the correctly rounded reciprocal r = 1/s (one
+    // IEEE division per row): q = x r is within an ulp of x / s, its residual
+    // x - q s is exact in an FMA, and q + residual * r rounded once is the
+    // correctly rounded quotient (Markstein's correction; no over- or underflow
+    // matters here: |x / s| <= 448, and quotients too small to be normal code
+    // to a signed zero whatever their last bits).  The sign is x's, so that
+    // -0 stays -0.
+    const float r = 1.f / s;
     float y[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf(x[e] / s, -448.f), 448.f);
+    for (int e = 0; e < 8; ++e) {
+        const float q = x[e] * r;
+        const float q1 = __builtin_copysignf(fmaf(fmaf(-q, s, x[e]), r, q), x[e]);
+        y[e] = fminf(fmaxf(q1, -448.f), 448.f);
+    }
     int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
     lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
     int hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
