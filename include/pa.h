@@ -105,6 +105,25 @@ typedef enum pa_dtype {
  * bit-identical either way; a wrong promise costs speed, not correctness.
  */
 #define PA_DECODE_STREAM_KV 1u
+/*
+ * PA_DECODE_SHARED_PREFIX -- the caller (a block manager with prefix caching,
+ * "vLLM学习整理", §三; "vLLM-Ascend 原理", §2.1) says that consecutive sequences
+ * of the batch may point at the same physical blocks, typically their common
+ * prefix.  Honoured by pa_decode and pa_decode_noalloc on the 16-bit matrix-core
+ * decode (head_dim 128, 3 to 8 q heads per kv head) with partition_tokens 0 or
+ * PA_PARTITION_BALANCED, where the balanced split fits (at most 512
+ * sequences): one wave then carries the heads of S = 16 / group consecutive
+ * sequences (S = 5, 4, 3, 2, 2, 2 for groups 3 to 8) through their leading
+ * blocks, as long as two or more of them are still in play and all of those
+ * name the same block, reading each such block once for all of them; the
+ * balanced split takes the rest.  Sharing pays where runs of sequences with a
+ * common prefix are aligned to S.  Everywhere else the flag is accepted and
+ * has no effect.  Results agree with the unflagged call to the decode
+ * tolerance, not bit for bit (the partial sums fall in other places).  Block
+ * rows inside any sequence's context must be finite for the other sequences of
+ * its wave to be exact (a zero weight times an infinite value is NaN).
+ */
+#define PA_DECODE_SHARED_PREFIX 2u
 
 /*
  * Split-KV work split of the decode calls (their partition_tokens argument).
@@ -234,7 +253,8 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  *                 positive and finite.
  *   partition_tokens  split-KV work split: a partition length (multiple of
  *                 16), 0 for the library default or PA_PARTITION_BALANCED.
- *   flags         0 or PA_DECODE_STREAM_KV; other bits give PA_ERR_UNSUPPORTED.
+ *   flags         0, PA_DECODE_STREAM_KV, PA_DECODE_SHARED_PREFIX or both; other
+ *                 bits give PA_ERR_UNSUPPORTED.
  *   workspace     device buffer of at least pa_decode_workspace_size() bytes
  *                 (may be NULL when that size is 0), 16-byte aligned.
  *

@@ -26,7 +26,8 @@ import os
 import torch
 
 __all__ = [
-    "PagedKVError", "LIB_PATH", "BLOCK_SIZE", "PA_DECODE_STREAM_KV", "PA_PARTITION_BALANCED", "lib",
+    "PagedKVError", "LIB_PATH", "BLOCK_SIZE", "PA_DECODE_STREAM_KV", "PA_DECODE_SHARED_PREFIX",
+    "PA_PARTITION_BALANCED", "lib",
     "pa_kv_bytes_per_token", "pa_status_string", "pa_reshape_and_cache", "pa_copy_blocks",
     "pa_decode_default_partition", "pa_decode_split", "pa_decode_workspace_size", "pa_decode",
     "pa_decode_partitions", "pa_decode_merge", "pa_prefill_paged",
@@ -39,6 +40,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "libpa_debug.so" if os.environ.get("PA_DEBUG_BOUNDS") == "1" else "libpa.so")
 BLOCK_SIZE = 16
 PA_DECODE_STREAM_KV = 1   # no physical block is read twice in the call: stream K/V
+PA_DECODE_SHARED_PREFIX = 2   # consecutive sequences may share blocks: read each shared block once per wave
 PA_PARTITION_BALANCED = -1   # partition_tokens value: the balanced split of decode work
 NOALLOC_SCRATCH_BYTES = 64 << 20   # PA_NOALLOC_SCRATCH_BYTES: static scratch of pa_decode_noalloc
 # bits of pa_debug_bounds (PA_DEBUG_* in pa.h)
@@ -225,7 +227,8 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, partition
               workspace=None, stream=None, flags=0):
     """Paged decode attention into ``out`` (``[B, Hq, D]``).  ``workspace`` (bytes,
     see ``pa_decode_workspace_size``) is allocated with torch when not given.
-    ``flags``: 0 or ``PA_DECODE_STREAM_KV`` (no block shared within the batch)."""
+    ``flags``: 0, ``PA_DECODE_STREAM_KV`` (no block shared within the batch) and/or
+    ``PA_DECODE_SHARED_PREFIX`` (consecutive sequences may share blocks)."""
     nb, bs, hkv, d, b, hq, mb = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens)
     need = pa_decode_workspace_size(b, hq, hkv, d, bs, mb, partition_tokens)
     ws, ws_bytes = _workspace(workspace, need, q.device)

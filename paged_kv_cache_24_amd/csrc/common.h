@@ -326,19 +326,60 @@ __device__ __forceinline__ int balanced_stretch(const DecodeArgs& a, int total) 
     return c > kMinStretch ? c : kMinStretch;
 }
 
-// Blocks of the whole stream (every lane gets the sum); with `prefix`, also
-// the blocks of the sequences before `before`.
-__device__ __forceinline__ int stream_blocks(const DecodeArgs& a, int before, int* prefix) {
-    const int lane = threadIdx.x & (kWave - 1);
-    int total = 0, pre = 0;
-    for (int base = 0; base < a.num_seqs; base += kWave) {
-        const int i = base + lane;
-        const int nb = i < a.num_seqs ? ceil_blocks(seq_tokens(a, i)) : 0;
-        total += wave_sum(nb);
-        if (prefix) pre += wave_sum(i < before ? nb : 0);
+// The block counts of a stream's items (sequences, or the owners of the
+// sequence groups) held in registers, lane l holding items l, l + 64, ...: all
+// of them arrive in one round of loads, not one dependent round per 64 items
+// (under a saturated memory system each round costs microseconds).  Holds up
+// to kScanItems items; the launchers check that.
+constexpr int kScanRegs = 12;
+constexpr int kScanItems = kScanRegs * kWave;
+
+struct BlockCounts {
+    int c[kScanRegs];
+
+    template <typename Count>
+    __device__ __forceinline__ BlockCounts(int n, Count count) {
+        const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+        for (int k = 0; k < kScanRegs; ++k) {
+            const int i = k * kWave + lane;
+            c[k] = i < n ? count(i) : 0;
+        }
     }
-    if (prefix) *prefix = uniform(pre);
-    return uniform(total);
+    // blocks of the items before `before` (every lane gets it)
+    __device__ __forceinline__ int prefix(int before) const {
+        const int lane = threadIdx.x & (kWave - 1);
+        int t = 0;
+#pragma unroll
+        for (int k = 0; k < kScanRegs; ++k) t += k * kWave + lane < before ? c[k] : 0;
+        return uniform(wave_sum(t));
+    }
+    __device__ __forceinline__ int total() const { return prefix(kScanItems); }
+    // the item holding stream block s (< total), and the stream position of its first block
+    __device__ __forceinline__ void locate(int s, int& item, int& pos) const {
+        int run = 0;
+        item = 0;
+        pos = 0;
+#pragma unroll
+        for (int k = 0; k < kScanRegs; ++k) {
+            const int incl = wave_inclusive_scan(c[k]);
+            const int sum = uniform(__shfl(incl, kWave - 1));
+            if (run + sum > s) {
+                const unsigned long long hit = __ballot(run + incl > s);
+                const int f = __ffsll(hit) - 1;
+                item = k * kWave + f;
+                pos = run + __shfl(incl - c[k], f);
+                break;
+            }
+            run += sum;
+        }
+        item = uniform(item);
+        pos = uniform(pos);
+    }
+};
+
+__device__ __forceinline__ BlockCounts sequence_blocks(const DecodeArgs& a) {
+    return BlockCounts(a.num_seqs, [&](int i) { return ceil_blocks(seq_tokens(a, i)); });
 }
 
 // Calls segment(b, g, hc, n, j0, j1, whole, slot) for every segment of this
@@ -356,31 +397,16 @@ __device__ __forceinline__ void balanced_walk(const DecodeArgs& a, int wave, Seg
         const int64_t f = nst / kStretchStride;
         if (st < f * kStretchStride) st = (st % kStretchStride) * f + st / kStretchStride;
     }
-    const int lane = threadIdx.x & (kWave - 1);
-    const int total = stream_blocks(a, 0, nullptr);
+    const BlockCounts counts = sequence_blocks(a);
+    const int total = counts.total();
     const int stretch = balanced_stretch(a, total);
     const int64_t lo = st * stretch;
     if (lo >= total) return;
     int s = (int)lo;
     const int s1 = (int)min((int64_t)total, lo + stretch);
     // the sequence b holding block s, and the stream position pb of its first block
-    int b = 0, pb = 0, run = 0;
-    for (int base = 0; base < a.num_seqs; base += kWave) {
-        const int i = base + lane;
-        const int nb = i < a.num_seqs ? ceil_blocks(seq_tokens(a, i)) : 0;
-        const int incl = wave_inclusive_scan(nb);
-        const int sum = uniform(__shfl(incl, kWave - 1));
-        if (run + sum > s) {
-            const unsigned long long hit = __ballot(run + incl > s);
-            const int f = __ffsll(hit) - 1;
-            b = base + f;
-            pb = run + __shfl(incl - nb, f);
-            break;
-        }
-        run += sum;
-    }
-    b = uniform(b);
-    pb = uniform(pb);
+    int b, pb;
+    counts.locate(s, b, pb);
     const int g = ui / a.head_chunks;
     const int hc = ui - g * a.head_chunks;
     while (s < s1 && b < a.num_seqs) {

@@ -493,6 +493,312 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
     });
 }
 
+// ---------------------------------------------------------------------------
+// Sequence groups (PA_DECODE_SHARED_PREFIX).  Sequences that share a prefix
+// point at the same physical blocks ("vLLM-Ascend 原理", §2.1; "vLLM学习整理",
+// §三 on prefix caching).  With G q heads per kv head a matrix-core wave has 16
+// columns but fills G of them; here one wave carries the heads of S = 16 / G
+// consecutive sequences, a group (column c: member c / G, head c % G).  The
+// group's leading blocks, up to the first block at which fewer than two
+// members are still in play or those in play name different blocks, are its
+// shared blocks: each is read once and scored for every member still in play.
+//
+// The balanced split runs over a stream of owners, group after group: the
+// group's cp shared blocks, then each member's blocks past them.  A stretch's
+// segment of a shared run scores all 16 columns; a segment of a member's own
+// blocks scores that member's G columns (the others see -inf).  Slots stay
+// unique as in the one-sequence split (owners appear in stream order): a
+// member's segment writes its G heads' states at ((b + stretch) * Hkv + g) * G
+// + head, a shared segment its 16 columns' at shared_base + ((group + stretch)
+// * Hkv + g) * 16 + column.  A row is finished in place when one segment saw
+// all of its blocks.
+
+constexpr int kMaxGroupSeqs = 5;   // S = 16 / G with G >= 3
+
+__device__ __forceinline__ int group_owners(const DecodeArgs& a) {
+    const int groups = (a.num_seqs + a.seqs_per_wave - 1) / a.seqs_per_wave;
+    return groups * (a.seqs_per_wave + 1);
+}
+
+__device__ __forceinline__ BlockCounts owner_counts(const DecodeArgs& a) {
+    return BlockCounts(group_owners(a), [&](int i) { return a.owner_blocks[i]; });
+}
+
+// The plan: one wave per group finds the shared run cp of its members' tables
+// (lane i tests block base + i; the scan ends by the longest member's last
+// block, where no member is in play) and writes the group's owner counts.
+__global__ __launch_bounds__(256) void decode_group_plan_kernel(DecodeArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int S = a.seqs_per_wave;
+    const int64_t grp = (int64_t)blockIdx.x * 4 + uniform(threadIdx.x >> 6);
+    if (grp * S >= a.num_seqs) return;
+    const int b0 = (int)grp * S;
+    int nb[kMaxGroupSeqs];
+#pragma unroll
+    for (int s = 0; s < kMaxGroupSeqs; ++s) nb[s] = s < S && b0 + s < a.num_seqs ? ceil_blocks(seq_tokens(a, b0 + s)) : 0;
+    int cp = 0;
+    for (int base = 0;; base += kWave) {
+        const int j = base + lane;
+        // every member row's entry j is inside its row (j < max_blocks_per_seq): the
+        // loads need not wait for the lengths
+        int e[kMaxGroupSeqs];
+#pragma unroll
+        for (int s = 0; s < kMaxGroupSeqs; ++s)
+            e[s] = s < S && b0 + s < a.num_seqs && j < a.max_blocks_per_seq
+                       ? a.block_tables[(int64_t)(b0 + s) * a.table_stride + (j >> a.block_shift)]
+                       : -1;
+        int in_play = 0, e0 = 0;
+        bool same = true;
+#pragma unroll
+        for (int s = 0; s < kMaxGroupSeqs; ++s) {
+            if (j < nb[s]) {
+                const int sb = sub_block(e[s], j, a.block_shift);
+                if (in_play == 0) e0 = sb;
+                same = same && sb == e0;
+                ++in_play;
+            }
+        }
+        const unsigned long long stop = __ballot(in_play < 2 || !same);
+        if (stop) {
+            cp = uniform(base + __ffsll(stop) - 1);
+            break;
+        }
+    }
+    // lane 0: the shared run; lane 1 + s: member s's blocks past it
+    int cnt = 0;
+#pragma unroll
+    for (int s = 0; s < kMaxGroupSeqs; ++s)
+        if (lane == 1 + s) cnt = nb[s] - min(cp, nb[s]);
+    if (lane == 0) cnt = cp;
+    if (lane <= S) a.owner_blocks[grp * (S + 1) + lane] = cnt;
+}
+
+// One segment of a stretch: blocks [j0, j1) of owner (group grp, member sel;
+// sel < 0: the group's shared run) among its cnt blocks, for kv head g.
+template <int DT, bool NT>
+__device__ __forceinline__ void grouped_segment(const DecodeArgs& a, uint16_t* vt, int grp, int g, int sel, int j0,
+                                                int j1, int cnt, int64_t st) {
+    constexpr int D = 128;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int lr = lane & 15;                   // MFMA column
+    const int lg = lane >> 4;
+    const int S = a.seqs_per_wave;
+    const int b0 = grp * S;
+    const int s_col = lr / a.group;             // this column's member
+    const int h_col = lr - s_col * a.group;
+    const bool col_live = s_col < S && b0 + s_col < a.num_seqs;
+    const int n_col = col_live ? seq_tokens(a, b0 + s_col) : 0;
+    const int64_t my_row = (int64_t)(col_live ? b0 + s_col : b0) * a.num_q_heads + (int64_t)g * a.group + h_col;
+
+    int nt[kMaxGroupSeqs], nb[kMaxGroupSeqs];   // members' lengths and block counts (uniform)
+    int nmax = 0;
+#pragma unroll
+    for (int s = 0; s < kMaxGroupSeqs; ++s) {
+        nt[s] = s < S && b0 + s < a.num_seqs ? seq_tokens(a, b0 + s) : 0;
+        nb[s] = ceil_blocks(nt[s]);
+        nmax = max(nmax, nt[s]);
+    }
+    // a member's own blocks follow the shared run: offset them by it
+    int off = 0, nsel = 0;
+#pragma unroll
+    for (int s = 0; s < kMaxGroupSeqs; ++s)
+        if (s == sel) {
+            off = nb[s] - cnt;
+            nsel = nt[s];
+        }
+    if (sel >= 0) nmax = nsel;   // V rows past it hold no token of this member
+    const bool on = sel < 0 ? col_live : s_col == sel;
+
+    uint4 qf[4];
+    {
+        const uint16_t* q = static_cast<const uint16_t*>(a.q) + my_row * D + 8 * lg;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            qf[kk] = on ? *reinterpret_cast<const uint4*>(q + 32 * kk) : make_uint4(0, 0, 0, 0);
+    }
+    float m = -INFINITY;
+    float l = 0.f;
+    df32x4_t o[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) o[mt] = df32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t row_stride = (int64_t)a.num_kv_heads * D;
+    const int tk = (lr & 3) * 4 + (lr >> 2);
+    const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache) + (int64_t)g * D + 8 * lg +
+                            (int64_t)tk * row_stride;
+    const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + (int64_t)g * D + 8 * lr +
+                            (int64_t)lg * row_stride;
+    const float cs = a.scale_log2;
+    const uint16_t* vtr = vt + (4 * (lr >> 2) + lg) * kVRow + 4 * (lr & 3);
+    const int32_t* tables = a.block_tables + (int64_t)b0 * a.table_stride;
+
+    // block j of the owner: its own, or the one every member in play names
+    auto load = [&](int j, uint4 (&kr)[4], uint4 (&vr)[4]) __attribute__((always_inline)) -> bool {
+        int who = sel;
+        if (sel < 0) {
+            who = 0;
+#pragma unroll
+            for (int s = kMaxGroupSeqs - 1; s >= 0; --s)
+                if (j < nb[s]) who = s;
+        }
+        const int pb = sub_block(tables[(int64_t)who * a.table_stride + (j >> a.block_shift)], j, a.block_shift);
+        const bool ok = pb >= 0 && (int64_t)pb < a.num_blocks;
+        const int64_t boff = (int64_t)(ok ? pb : 0) * kBlockSize * row_stride;
+        // a member's own blocks are read once in the call: stream them; the
+        // shared run is read by every group of its sharers: keep it cacheable
+        if (sel >= 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                kr[i] = load_kv<true>(kbase + boff + 32 * i);
+                vr[i] = load_kv<true>(vbase + boff + (int64_t)4 * i * row_stride);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                kr[i] = load_kv<NT>(kbase + boff + 32 * i);
+                vr[i] = load_kv<NT>(vbase + boff + (int64_t)4 * i * row_stride);
+            }
+        }
+        return ok;
+    };
+
+    auto process = [&](const uint4 (&kr)[4], const uint4 (&vr)[4], bool ok, int j) __attribute__((always_inline)) {
+        df32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) sacc = mfma_16x16x32<DT>(kr[kk], qf[kk], sacc);
+        bool vrow[4];
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = j * kBlockSize + 4 * i + lg;
+            vrow[i] = ok && key < nmax;
+            x[i] = ok && on && key < n_col ? sacc[i] * cs : -INFINITY;
+        }
+        float mb = __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0], x[1]),
+                                                 __builtin_elementwise_maximum(x[2], x[3]));
+        mb = xor32_max(xor16_max(mb));
+        const bool raise = mb > m + 8.f;
+        const float mn = raise ? mb : m;
+        if (__any(raise)) {
+            const float alpha = raise ? fast_exp2(m - mn) : 1.f;
+            l *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) o[mt] *= alpha;
+        }
+        m = mn;
+        const float mu = mn == -INFINITY ? 0.f : mn;
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - mu);
+        uint2 pb;
+        pb.x = pack2<DT>(p[0], p[1]);
+        pb.y = pack2<DT>(p[2], p[3]);
+        l = dot2<DT>(pb.y, kOnes2<DT>, dot2<DT>(pb.x, kOnes2<DT>, l));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint4*>(vt + (4 * i + lg) * kVRow + 8 * lr) = vrow[i] ? vr[i] : make_uint4(0, 0, 0, 0);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            const ds16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (ds16x4_t __attribute__((address_space(3)))*)(vtr + 16 * mt));
+            o[mt] = mfma_16x16x16<DT>(__builtin_bit_cast(uint2, va), pb, o[mt]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    const int ja = off + j0, jb = off + j1;
+    {
+        uint4 kc[4], vc[4];
+        bool okc = load(ja, kc, vc);
+        for (int j = ja; j < jb; ++j) {
+            uint4 kn[4], vn[4];
+            bool okn = false;
+            if (j + 1 < jb) okn = load(j + 1, kn, vn);   // next block in flight
+            process(kc, vc, okc, j);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                kc[i] = kn[i];
+                vc[i] = vn[i];
+            }
+            okc = okn;
+        }
+    }
+
+    const float lt = xor32_sum(xor16_sum(l));
+    if (!on) return;
+    // the column's row is finished here when this segment saw all of its blocks
+    const bool all = j0 == 0 && j1 == cnt;
+    bool final_out;
+    int64_t idx;
+    if (sel < 0) {
+        if (min(cnt, ceil_blocks(n_col)) == 0) return;   // an empty member: the merge writes its zeros
+        final_out = all && a.owner_blocks[(int64_t)grp * (S + 1) + 1 + s_col] == 0;
+        idx = a.shared_base + (((int64_t)grp + st) * a.num_kv_heads + g) * 16 + lr;
+    } else {
+        final_out = all && off == 0;
+        idx = (((int64_t)b0 + sel + st) * a.num_kv_heads + g) * a.group + h_col;
+    }
+    if (final_out) {
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        uint16_t* dst = static_cast<uint16_t*>(a.out) + my_row * D + 4 * lg;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            uint2 w;
+            w.x = pack2<DT>(o[mt][0] * inv, o[mt][1] * inv);
+            w.y = pack2<DT>(o[mt][2] * inv, o[mt][3] * inv);
+            *reinterpret_cast<uint2*>(dst + 16 * mt) = w;
+        }
+    } else {
+        float* dst = a.ws_acc + idx * D + 4 * lg;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+            *reinterpret_cast<float4*>(dst + 16 * mt) = make_float4(o[mt][0], o[mt][1], o[mt][2], o[mt][3]);
+        if (lg == 0) a.ws_ml[idx] = make_float2(m, lt);
+    }
+}
+
+// The balanced split over the owner stream: stretch st, kv head g per wave.
+template <int DT, bool NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void decode_gqa_grouped_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t vlds[4][kBlockSize * kVRow];
+    const int wave = uniform(threadIdx.x >> 6);
+    const int64_t w = decode_workgroup<NT>() * 4 + wave;
+    const int64_t nst = a.num_items / a.num_kv_heads;
+    const int64_t st = w / a.num_kv_heads;
+    const int g = (int)(w - st * a.num_kv_heads);
+    if (st >= nst) return;
+    const int owners = group_owners(a);
+    const BlockCounts counts = owner_counts(a);
+    const int total = counts.total();
+    const int stretch = balanced_stretch(a, total);
+    const int64_t lo = st * stretch;
+    if (lo >= total) return;
+    int s = (int)lo;
+    const int s1 = (int)min((int64_t)total, lo + stretch);
+    // the owner o holding block s, and the stream position po of its first block
+    int o, po;
+    counts.locate(s, o, po);
+    const int S1 = a.seqs_per_wave + 1;
+    while (s < s1 && o < owners) {
+        const int cnt = a.owner_blocks[o];
+        if (s >= po + cnt) {   // past this owner (also skips empty ones)
+            po += cnt;
+            ++o;
+            continue;
+        }
+        const int grp = o / S1;
+        const int j0 = s - po;
+        const int j1 = min(cnt, j0 + (s1 - s));
+        grouped_segment<DT, NT>(a, vlds[wave], grp, g, o - grp * S1 - 1, j0, j1, cnt, st);
+        s += j1 - j0;
+    }
+}
+
 // Combine the partial states of one (sequence, q head):
 // out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p with M = max_p m_p.
 // One wave per output row (sequence, query, q head); lane i owns elements
@@ -504,7 +810,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
 // s0 = P / C .. s1 = (P + nblk - 1) / C left the state of the row's unit ui in
 // slots ((b + s) * upb + ui) * state_heads + h; a row whose sequence one stretch
 // covered whole was finished there, and a row of an empty sequence, which no
-// stretch covers, gets its zeros here.
+// stretch covers, gets its zeros here.  With sequence groups the stretches of
+// the group's shared run come first, then those of the member's own blocks.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     constexpr int EPL = D / kWave;   // elements per lane
@@ -516,8 +823,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 
     const int n = seq_tokens(a, b);
     const int nblk = ceil_blocks(n);
-    int64_t base;
-    int stride, count;
+    int64_t base = 0, shared = 0;
+    int stride = 0, count = 0, nsh = 0, sh_stride = 0;
     if (a.balanced) {
         if (nblk == 0) {
 #pragma unroll
@@ -526,18 +833,49 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
         }
         const int head = (int)(item % a.num_q_heads);
         const int g = head / a.group;
-        const int hc = (head - g * a.group) / a.heads_per_wave;
-        const int h = head - g * a.group - hc * a.heads_per_wave;
-        const int upb = a.num_kv_heads * a.head_chunks;
-        int before;
-        const int total = stream_blocks(a, b, &before);
-        const int stretch = balanced_stretch(a, total);
-        const int s0 = before / stretch;
-        const int s1 = (before + nblk - 1) / stretch;
-        if (s0 == s1) return;   // one stretch covered the whole sequence
-        base = (((int64_t)b + s0) * upb + g * a.head_chunks + hc) * a.state_heads + h;
-        stride = upb * a.state_heads;
-        count = s1 - s0 + 1;
+        if (a.owner_blocks) {   // sequence groups: the shared run's stretches, then the member's own
+            const int S = a.seqs_per_wave;
+            const int grp = b / S;
+            const int mem = b - grp * S;
+            const int hh = head - g * a.group;
+            const int og = grp * (S + 1);
+            const int cp = a.owner_blocks[og];
+            const int priv = a.owner_blocks[og + 1 + mem];
+            const BlockCounts counts = owner_counts(a);
+            const int pg = counts.prefix(og);
+            const int stretch = balanced_stretch(a, counts.total());
+            if (priv < nblk) {
+                const int t0 = pg / stretch;
+                const int t1 = (pg + cp - 1) / stretch;
+                if (priv == 0 && t0 == t1) return;   // one stretch covered the whole row
+                nsh = t1 - t0 + 1;
+                shared = a.shared_base + (((int64_t)grp + t0) * a.num_kv_heads + g) * 16 + mem * a.group + hh;
+                sh_stride = a.num_kv_heads * 16;
+            }
+            if (priv > 0) {
+                int pb = pg + cp;
+                for (int r = 0; r < mem; ++r) pb += a.owner_blocks[og + 1 + r];
+                const int s0 = pb / stretch;
+                const int s1 = (pb + priv - 1) / stretch;
+                if (nsh == 0 && s0 == s1) return;   // one stretch covered the whole row
+                base = (((int64_t)b + s0) * a.num_kv_heads + g) * a.group + hh;
+                stride = a.num_kv_heads * a.group;
+                count = s1 - s0 + 1;
+            }
+        } else {
+            const int hc = (head - g * a.group) / a.heads_per_wave;
+            const int h = head - g * a.group - hc * a.heads_per_wave;
+            const int upb = a.num_kv_heads * a.head_chunks;
+            const BlockCounts counts = sequence_blocks(a);
+            const int before = counts.prefix(b);
+            const int stretch = balanced_stretch(a, counts.total());
+            const int s0 = before / stretch;
+            const int s1 = (before + nblk - 1) / stretch;
+            if (s0 == s1) return;   // one stretch covered the whole sequence
+            base = (((int64_t)b + s0) * upb + g * a.head_chunks + hc) * a.state_heads + h;
+            stride = upb * a.state_heads;
+            count = s1 - s0 + 1;
+        }
     } else {
         const int nparts = nblk <= a.part_blocks ? 1 : (nblk + a.part_blocks - 1) / a.part_blocks;
         if (nparts <= 1) return;   // finished by the partition kernel
@@ -546,12 +884,17 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
         count = nparts;
     }
 
+    // state p: the shared run's (p < nsh), else the row's own
+    auto slot = [&](int p) -> int64_t {
+        return p < nsh ? shared + (int64_t)p * sh_stride : base + (int64_t)(p - nsh) * stride;
+    };
+    const int states = nsh + count;
     float big = -INFINITY;
-    for (int p = lane; p < count; p += kWave) big = fmaxf(big, a.ws_ml[base + (int64_t)p * stride].x);
+    for (int p = lane; p < states; p += kWave) big = fmaxf(big, a.ws_ml[slot(p)].x);
     big = xor32_max(xor16_max(group_max<16>(big)));
     float den = 0.f;
-    for (int p = lane; p < count; p += kWave) {
-        const float2 ml = a.ws_ml[base + (int64_t)p * stride];
+    for (int p = lane; p < states; p += kWave) {
+        const float2 ml = a.ws_ml[slot(p)];
         den = fmaf(ml.x == -INFINITY ? 0.f : fast_exp2(ml.x - big), ml.y, den);
     }
     den = xor32_sum(xor16_sum(group_sum<16>(den)));
@@ -559,13 +902,14 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     float num[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) num[e] = 0.f;
-    const float* acc = a.ws_acc + base * D + EPL * lane;
+    const float* acc = a.ws_acc + EPL * lane;
 #pragma unroll 4
-    for (int p = 0; p < count; ++p) {
-        const float mp = a.ws_ml[base + (int64_t)p * stride].x;   // the same address in every lane
+    for (int p = 0; p < states; ++p) {
+        const int64_t sl = slot(p);
+        const float mp = a.ws_ml[sl].x;   // the same address in every lane
         const float w = mp == -INFINITY ? 0.f : fast_exp2(mp - big);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, acc[(int64_t)p * stride * D + e], num[e]);
+        for (int e = 0; e < EPL; ++e) num[e] = fmaf(w, acc[sl * D + e], num[e]);
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
 #pragma unroll
@@ -620,7 +964,7 @@ static hipError_t launch_balanced_t(const DecodeArgs& a, hipStream_t s, dim3 gri
 
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t s) {
     if (a.balanced) {
-        if (a.q_per_seq != 1 || a.num_items <= 0) return hipErrorInvalidValue;
+        if (a.q_per_seq != 1 || a.num_items <= 0 || a.num_seqs > kScanItems) return hipErrorInvalidValue;
         const dim3 grid((unsigned)((a.num_items + 3) / 4));
         if (a.dtype == kF16)
             return a.stream_kv ? launch_balanced_t<kF16, true>(a, s, grid) : launch_balanced_t<kF16, false>(a, s, grid);
@@ -634,9 +978,28 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t s) {
     return a.q_per_seq > 1 ? launch_partitions_mq<true>(a, s, grid) : launch_partitions_mq<false>(a, s, grid);
 }
 
+hipError_t launch_decode_grouped(const DecodeArgs& a, hipStream_t s) {
+    if (!a.gqa_mfma || a.head_dim != 128 || a.q_per_seq != 1 || !a.balanced || a.head_chunks != 1 ||
+        a.seqs_per_wave < 2 || a.seqs_per_wave > kMaxGroupSeqs || a.seqs_per_wave * a.group > 16 ||
+        !a.owner_blocks || !a.ws_acc || a.num_items <= 0 || a.num_items % a.num_kv_heads != 0)
+        return hipErrorInvalidValue;
+    const int64_t groups = (a.num_seqs + a.seqs_per_wave - 1) / a.seqs_per_wave;
+    if (groups == 0) return hipSuccess;
+    if (groups * (a.seqs_per_wave + 1) > kScanItems) return hipErrorInvalidValue;
+    hipError_t e = launch(decode_group_plan_kernel, dim3((unsigned)((groups + 3) / 4)), dim3(256), s, a);
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)((a.num_items + 3) / 4));
+    if (a.dtype == kF16)
+        return a.stream_kv ? launch(decode_gqa_grouped_kernel<kF16, true>, grid, dim3(256), s, a)
+                           : launch(decode_gqa_grouped_kernel<kF16, false>, grid, dim3(256), s, a);
+    return a.stream_kv ? launch(decode_gqa_grouped_kernel<kBF16, true>, grid, dim3(256), s, a)
+                       : launch(decode_gqa_grouped_kernel<kBF16, false>, grid, dim3(256), s, a);
+}
+
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t s) {
     const int64_t items = (int64_t)a.num_seqs * a.q_per_seq * a.num_q_heads;
     if (items == 0 || (!a.balanced && a.num_parts <= 1)) return hipSuccess;
+    if (a.balanced && a.num_seqs > kScanItems) return hipErrorInvalidValue;
     const int64_t wgs = (items + 3) / 4;   // one wave per row
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid((unsigned)wgs);

@@ -627,7 +627,7 @@ static hipError_t launch_fp8_t(const DecodeArgs& a, hipStream_t s, dim3 grid) {
 
 hipError_t launch_decode_partitions_fp8(const DecodeArgs& a, hipStream_t s) {
     if (a.balanced) {
-        if (a.q_per_seq != 1 || a.num_items <= 0) return hipErrorInvalidValue;
+        if (a.q_per_seq != 1 || a.num_items <= 0 || a.num_seqs > kScanItems) return hipErrorInvalidValue;
         const dim3 grid((unsigned)((a.num_items + 3) / 4));
         if (a.dtype == kF16)
             return a.stream_kv ? launch_fp8_balanced_t<kF16, true>(a, s, grid)

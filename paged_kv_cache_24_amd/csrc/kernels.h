@@ -87,8 +87,20 @@ struct DecodeArgs {
     int32_t balanced;
     int32_t num_items;
     int32_t state_heads;     // balanced: head slots per partial-state slot, min(heads_per_wave, cols)
+    // sequence groups (shared prefixes; balanced split on matrix cores):
+    // seqs_per_wave > 1 consecutive sequences share one wave, 16 / group
+    // columns' worth (column c: member c / group, head c % group).  The
+    // balanced stream then runs over owners, group after group: the group's
+    // shared blocks, then each member's blocks past them; owner_blocks[o]
+    // holds the counts (the plan kernel writes them).  A shared segment leaves
+    // the states of its 16 columns at slots
+    // shared_base + ((group + stretch) * num_kv_heads + g) * 16 + column.
+    int32_t seqs_per_wave;
+    int64_t shared_base;
+    int32_t* owner_blocks;
 };
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_grouped(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_partitions_fp8(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
 

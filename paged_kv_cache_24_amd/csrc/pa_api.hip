@@ -95,6 +95,7 @@ bool check_decode_bounds(const pa::DecodeArgs& d, hipStream_t stream) {
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr uint32_t kDecodeFlags = PA_DECODE_STREAM_KV | PA_DECODE_SHARED_PREFIX;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool supported_dtype(pa_dtype d) { return d == PA_F16 || d == PA_BF16; }
@@ -250,7 +251,7 @@ pa::DecodeArgs decode_args(void* out, const void* q, const void* k_cache, const 
                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                            int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
                            float scale, pa_dtype dtype, const DecodeShape& shape, void* workspace,
-                           uint32_t flags, int32_t q_per_seq = 1) {
+                           uint32_t flags, int32_t q_per_seq = 1, int32_t seqs_per_wave = 1) {
     const int32_t sh = block_shift(block_size);
     pa::DecodeArgs a;
     a.out = out;
@@ -286,12 +287,52 @@ pa::DecodeArgs decode_args(void* out, const void* q, const void* k_cache, const 
     a.state_heads = std::min(a.heads_per_wave, a.cols);
     float* ws = static_cast<float*>(workspace);
     const size_t upb = (size_t)num_kv_heads * a.head_chunks;
-    const size_t states =
-        shape.balanced ? ((size_t)num_seqs + shape.num_items / upb) * upb * a.state_heads
-                       : (size_t)num_seqs * q_per_seq * num_q_heads * shape.num_parts;
+    size_t states = shape.balanced ? ((size_t)num_seqs + shape.num_items / upb) * upb * a.state_heads
+                                   : (size_t)num_seqs * q_per_seq * num_q_heads * shape.num_parts;
+    a.seqs_per_wave = seqs_per_wave;
+    a.shared_base = (int64_t)states;
+    size_t owners = 0;
+    if (seqs_per_wave > 1) {   // the shared runs' states, 16 columns per (group + stretch, kv head)
+        const size_t groups = ceil_div(num_seqs, seqs_per_wave);
+        states += (groups + shape.num_items / upb) * num_kv_heads * 16;
+        owners = groups * (seqs_per_wave + 1);
+    }
     a.ws_acc = shape.ws_bytes ? ws : nullptr;
     a.ws_ml = shape.ws_bytes ? reinterpret_cast<float2*>(ws + states * head_dim) : nullptr;
+    a.owner_blocks = shape.ws_bytes && owners ? reinterpret_cast<int32_t*>(a.ws_ml + states) : nullptr;
     return a;
+}
+
+// Sequence groups (PA_DECODE_SHARED_PREFIX on pa_decode): where the
+// matrix-core kernel's 16 columns hold two or more sequences' heads (3 to 8 q
+// heads per kv head) and the balanced split fits, one wave carries 16 / group
+// consecutive sequences through the leading blocks they share and the balanced
+// split runs over those shared runs and the members' own blocks.  Returns the
+// sequences per wave, 1 where the groups do not apply.
+int32_t group_seqs(uint32_t flags, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t partition_tokens) {
+    if (!(flags & PA_DECODE_SHARED_PREFIX) || (partition_tokens != 0 && partition_tokens != PA_PARTITION_BALANCED) ||
+        !uses_gqa_kernel(num_q_heads, num_kv_heads, head_dim))
+        return 1;
+    const int32_t group = num_q_heads / num_kv_heads;
+    return group <= 8 ? 16 / group : 1;
+}
+
+// The balanced shape with the groups' workspace: after the one-sequence
+// states, (groups + stretches) * num_kv_heads * 16 states of the shared runs,
+// then groups * (S + 1) int32 owner counts.  valid = false where the balanced
+// split does not fit the call.
+DecodeShape grouped_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t max_blocks16, int32_t seqs_per_wave) {
+    DecodeShape s = decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks16,
+                                 PA_PARTITION_BALANCED, true);
+    if (s.valid) {
+        const size_t groups = ceil_div(num_seqs, seqs_per_wave);
+        const size_t stretches = (size_t)s.num_items / num_kv_heads;
+        s.ws_bytes += (groups + stretches) * num_kv_heads * 16 * ((size_t)head_dim * sizeof(float) + 2 * sizeof(float)) +
+                      groups * (seqs_per_wave + 1) * sizeof(int32_t);
+    }
+    return s;
 }
 
 // Both decode phases launch one 4-wave workgroup per 4 items; their grids are
@@ -493,12 +534,20 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
         max_blocks_per_seq <= 0 || max_blocks_per_seq > (INT32_MAX >> sh) ||
         (partition_tokens != PA_PARTITION_BALANCED && (partition_tokens < 0 || partition_tokens % 16)))
         return 0;
-    // enough for either split of this shape
+    // enough for either split of this shape, and for sequence groups where they apply
     const int32_t mb16 = max_blocks_per_seq << sh;
-    return std::max(decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, mb16, partition_tokens,
-                                 true).ws_bytes,
-                    decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, mb16, partition_tokens,
-                                 false).ws_bytes);
+    size_t need = std::max(decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, mb16, partition_tokens,
+                                        true).ws_bytes,
+                           decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, mb16, partition_tokens,
+                                        false).ws_bytes);
+    if (num_q_heads % num_kv_heads == 0 &&
+        group_seqs(PA_DECODE_SHARED_PREFIX, num_q_heads, num_kv_heads, head_dim, partition_tokens) > 1) {
+        const DecodeShape g = grouped_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, mb16,
+                                            group_seqs(PA_DECODE_SHARED_PREFIX, num_q_heads, num_kv_heads,
+                                                       head_dim, partition_tokens));
+        if (g.valid) need = std::max(need, g.ws_bytes);
+    }
+    return need;
 }
 
 pa_status pa_decode_partitions(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -508,7 +557,7 @@ pa_status pa_decode_partitions(void* out, const void* q, const void* k_cache, co
                                int64_t num_blocks, float scale, pa_dtype dtype,
                                int32_t partition_tokens, uint32_t flags, void* workspace,
                                size_t workspace_bytes, hipStream_t stream) {
-    if (flags & ~PA_DECODE_STREAM_KV) return PA_ERR_UNSUPPORTED;
+    if (flags & ~kDecodeFlags) return PA_ERR_UNSUPPORTED;
     pa_status st = check_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
                                 num_q_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, num_blocks, scale, dtype, partition_tokens);
@@ -566,7 +615,7 @@ pa_status pa_decode_partitions_fp8(void* out, const void* q, const void* k_cache
                                    int64_t num_blocks, float scale, pa_dtype dtype,
                                    int32_t partition_tokens, uint32_t flags, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream) {
-    if (flags & ~PA_DECODE_STREAM_KV) return PA_ERR_UNSUPPORTED;
+    if (flags & ~kDecodeFlags) return PA_ERR_UNSUPPORTED;
     if (block_size != PA_BLOCK_SIZE) return PA_ERR_UNSUPPORTED;   // scales are per 16-token block
     pa_status st = check_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
                                 num_q_heads, num_kv_heads, head_dim, block_size,
@@ -620,7 +669,7 @@ pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const v
                           int64_t num_blocks, float scale, pa_dtype dtype, int32_t partition_tokens,
                           uint32_t flags, void* workspace, size_t workspace_bytes,
                           hipStream_t stream) {
-    if (flags & ~PA_DECODE_STREAM_KV) return PA_ERR_UNSUPPORTED;
+    if (flags & ~kDecodeFlags) return PA_ERR_UNSUPPORTED;
     if (q_per_seq < 1 || q_per_seq > PA_MAX_QUERIES_PER_SEQ) return PA_ERR_SHAPE;
     pa_status st = check_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
                                 num_q_heads, num_kv_heads, head_dim, block_size,
@@ -664,6 +713,29 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
                     float scale, pa_dtype dtype, int32_t partition_tokens, uint32_t flags,
                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (flags & ~kDecodeFlags) return PA_ERR_UNSUPPORTED;
+    if (flags & PA_DECODE_SHARED_PREFIX) {
+        pa_status st = check_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+                                    num_q_heads, num_kv_heads, head_dim, block_size,
+                                    max_blocks_per_seq, num_blocks, scale, dtype, partition_tokens);
+        if (st != PA_OK || num_seqs == 0) return st;
+        const int32_t spw = group_seqs(flags, num_q_heads, num_kv_heads, head_dim, partition_tokens);
+        const DecodeShape shape = spw > 1 ? grouped_shape(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                          max_blocks_per_seq << block_shift(block_size), spw)
+                                          : DecodeShape{};
+        if (spw > 1 && shape.valid) {
+            st = check_workspace(shape, workspace, workspace_bytes);
+            if (st != PA_OK) return st;
+            const pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, seq_lens,
+                                                 num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                                 max_blocks_per_seq, num_blocks, scale, dtype, shape,
+                                                 workspace, flags, 1, spw);
+            if (!decode_grids_fit(a)) return PA_ERR_SHAPE;
+            if (!check_decode_bounds(a, stream)) return PA_ERR_HIP;
+            if (pa::launch_decode_grouped(a, stream) != hipSuccess) return PA_ERR_HIP;
+            return pa::launch_decode_merge(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+        }
+    }
     pa_status st = pa_decode_partitions(out, q, k_cache, v_cache, block_tables, seq_lens,
                                         num_seqs, num_q_heads, num_kv_heads, head_dim,
                                         block_size, max_blocks_per_seq, num_blocks, scale, dtype,
@@ -681,7 +753,7 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const
                             int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
                             float scale, pa_dtype dtype, int32_t partition_tokens, uint32_t flags,
                             hipStream_t stream) {
-    if (flags & ~PA_DECODE_STREAM_KV) return PA_ERR_UNSUPPORTED;
+    if (flags & ~kDecodeFlags) return PA_ERR_UNSUPPORTED;
     const pa_status st = check_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
                                       num_q_heads, num_kv_heads, head_dim, block_size,
                                       max_blocks_per_seq, num_blocks, scale, dtype,
@@ -691,11 +763,23 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const
                                            max_blocks_per_seq << block_shift(block_size),
                                            partition_tokens, true);
     if (!shape.valid) return PA_ERR_SHAPE;
-    if (shape.ws_bytes > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_SCRATCH;
-    // The partition kernel writes every partial state the merge reads, so the
-    // scratch needs no clearing between calls.
+    size_t need = shape.ws_bytes;
+    const int32_t spw = group_seqs(flags, num_q_heads, num_kv_heads, head_dim, partition_tokens);
+    if (spw > 1) {
+        const DecodeShape g = grouped_shape(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                            max_blocks_per_seq << block_shift(block_size), spw);
+        if (g.valid && g.ws_bytes <= PA_NOALLOC_SCRATCH_BYTES) {
+            need = g.ws_bytes;
+        } else {
+            flags &= ~PA_DECODE_SHARED_PREFIX;   // a hint: without room for the groups, decode without them
+        }
+    }
+    if (need > PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_SCRATCH;
+    // The partition kernels write every partial state (and, with sequence
+    // groups, every private block count) that the merge reads, so the scratch
+    // needs no clearing between calls.
     void* ws = nullptr;
-    if (shape.ws_bytes) {
+    if (need) {
         ws = scratch_address();
         if (!ws) return PA_ERR_HIP;
     }

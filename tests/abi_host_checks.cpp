@@ -82,7 +82,7 @@ int main() {
     expect("decode workspace", pa_decode(F, F, F, F, FI, FI, INT32_MAX, 8, 2, 128, 16, 64, 128, 0.1f, PA_BF16, 64,
                                          0, F, 16, nullptr),
            PA_ERR_WORKSPACE);
-    expect("decode flags", pa_decode(F, F, F, F, FI, FI, 2, 8, 2, 128, 16, 64, 128, 0.1f, PA_BF16, 0, 2u, F,
+    expect("decode flags", pa_decode(F, F, F, F, FI, FI, 2, 8, 2, 128, 16, 64, 128, 0.1f, PA_BF16, 0, 4u, F,
                                      1 << 20, nullptr),
            PA_ERR_UNSUPPORTED);
     expect("decode noalloc scratch", pa_decode_noalloc(F, F, F, F, FI, FI, INT32_MAX, 128, 1, 128, 16, 4096, 1 << 20,

@@ -146,7 +146,7 @@ def test_decode_rejects(lib, fn):
     # workspace of the same table in 16-token blocks
     assert _decode(lib, fn, bs=32, part=256, wsb=2 * 8 * 4 * (128 * 4 + 8)) == WS
     assert _decode(lib, fn, dt=9) == UNSUP
-    assert _decode(lib, fn, flags=2) == UNSUP             # unknown flag bit
+    assert _decode(lib, fn, flags=4) == UNSUP             # unknown flag bit
     assert _decode(lib, fn, hq=6, hkv=4) == SHAPE        # not a multiple
     assert _decode(lib, fn, hq=258, hkv=2) == SHAPE      # 129 q heads per kv head
     assert _decode(lib, fn, part=24) == SHAPE            # not a multiple of 16
@@ -168,6 +168,22 @@ def test_decode_rejects(lib, fn):
     assert _decode(lib, fn, part=-16) == SHAPE
 
 
+def test_shared_prefix_flag_needs_the_group_workspace(lib):
+    """PA_DECODE_SHARED_PREFIX on pa_decode with 4 q heads per kv head takes the
+    sequence groups, whose workspace exceeds the plain balanced split's."""
+    f = lib.pa_decode_workspace_size
+    f.restype = ctypes.c_size_t
+    f.argtypes = [ctypes.c_int32] * 7
+    full = f(2, 8, 2, 128, 16, 64, -1)
+    plain = (2 + 3072 // 2) * 2 * 4 * (128 * 4 + 8)      # balanced states alone
+    assert full > plain
+    assert _decode(lib, flags=2, part=-1, ws=None) == WS
+    assert _decode(lib, flags=2, part=-1, wsb=plain) == WS
+    assert _decode(lib, flags=2, part=-1, wsb=full - 1) == WS
+    assert _decode(lib, flags=2, part=-1, ws=FAKE + 8) == ALIGN
+    assert _decode(lib, flags=6, part=-1) == UNSUP         # with an unknown bit
+
+
 def test_workspace_size(lib):
     f = lib.pa_decode_workspace_size
     f.restype = ctypes.c_size_t
@@ -186,8 +202,13 @@ def test_workspace_size(lib):
     # q head each): 3072 waves = 96 stretches x 32 kv heads; states (64 + 96) x 32
     assert f(64, 32, 32, 128, 16, 256, -1) == (64 + 96) * 32 * (128 * 4 + 8)
     # GQA on matrix cores (4 q heads per kv head): 384 stretches x 8 kv heads,
-    # 4 head slots per state
-    assert f(256, 32, 8, 128, 16, 512, -1) == (256 + 384) * 8 * 4 * (128 * 4 + 8)
+    # 4 head slots per state; plus room for sequence groups (PA_DECODE_SHARED_PREFIX:
+    # 64 groups of 4 sequences): 16 column states per (group + stretch, kv head)
+    # and 5 owner counts per group
+    assert f(256, 32, 8, 128, 16, 512, -1) == ((256 + 384) * 8 * 4 + (64 + 384) * 8 * 16) * (128 * 4 + 8) + \
+        64 * 5 * 4
+    # 2 q heads per kv head (vector ALU): no groups
+    assert f(256, 16, 8, 128, 16, 512, -1) < f(256, 32, 8, 128, 16, 512, -1)
     # the default (0) takes the balanced split there; the size covers either split
     assert f(64, 32, 32, 128, 16, 256, 0) >= (64 + 96) * 32 * (128 * 4 + 8)
     assert f(600, 32, 32, 128, 16, 256, -1) == 0           # more than 512 sequences
@@ -405,7 +426,7 @@ def test_decode_noalloc_rejects(lib):
     limit = 64 << 20   # PA_NOALLOC_SCRATCH_BYTES
     assert _decode_noalloc(lib, q=None) == NULL
     assert _decode_noalloc(lib, d=80) == UNSUP
-    assert _decode_noalloc(lib, flags=2) == UNSUP
+    assert _decode_noalloc(lib, flags=4) == UNSUP
     assert _decode_noalloc(lib, hq=6, hkv=4) == SHAPE
     assert _decode_noalloc(lib, out=FAKE + 8) == ALIGN
     assert _decode_noalloc(lib, b=0, q=None) == PA_OK

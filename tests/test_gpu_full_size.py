@@ -43,14 +43,14 @@ def _written_rows_exact(g, c):
     del before_k, before_v
 
 
-def _every_sequence_decode(c):
+def _every_sequence_decode(c, flags=0):
     g = DecodeOnGPU(c)
     if len(c.slot_mapping):
         _written_rows_exact(g, c)
         kc, vc = oracle.ref_reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache, c.slot_mapping)
     else:
         kc, vc = c.k_cache, c.v_cache
-    out = host_f64(g.decode())
+    out = host_f64(g.decode(flags=flags))
     worst = 0.0
     for b in range(c.num_seqs):
         ref = oracle.ref_decode_one(c.q[b], kc, vc, c.block_tables[b], int(c.seq_lens[b]),
@@ -77,6 +77,12 @@ def test_full_llama2_7b_layer_decode():
 
 def test_full_gqa_shared_prefix_decode():
     _every_sequence_decode(decode_gqa_shared_prefix())
+
+
+def test_full_gqa_shared_prefix_decode_sequence_groups():
+    """With PA_DECODE_SHARED_PREFIX: waves of 4 sequences read each shared prefix block once."""
+    import paged_kv_cache_24_amd as pa
+    _every_sequence_decode(decode_gqa_shared_prefix(), flags=pa.PA_DECODE_SHARED_PREFIX)
 
 
 def test_full_long_context_decode():
