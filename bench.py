@@ -239,9 +239,9 @@ class Fp8DecodeRun(DecodeRun):
     the library's FP8 cache write quantises into code and scale pools.  The
     timed step is the FP8 cache write of the new tokens plus FP8 decode."""
 
-    def __init__(self, case, partition_tokens=0):
+    def __init__(self, case, partition_tokens=0, groups=False):
         import torch
-        super().__init__(case, partition_tokens)
+        super().__init__(case, partition_tokens, groups)
         pa, c = self.pa, case
         if self.has_write:
             pa.pa_reshape_and_cache(self.key, self.value, self.kc, self.vc, self.slots)
@@ -273,6 +273,13 @@ class Fp8DecodeRun(DecodeRun):
                                         self.slots)
         if ev is not None:
             ev[1].record()
+        if self.groups:   # the phases run inside one call: all of it counts as "partitions"
+            pa.pa_decode_fp8(self.out, self.q, self.kc8, self.vc8, self.ks, self.vs, self.tables, self.lens,
+                             c.scale, self.part, workspace=self.ws, flags=self.flags)
+            if ev is not None:
+                ev[2].record()
+                ev[3].record()
+            return
         pa.pa_decode_partitions_fp8(self.out, self.q, self.kc8, self.vc8, self.ks, self.vs,
                                     self.tables, self.lens, c.scale, self.ws, self.part,
                                     flags=self.flags)
@@ -397,7 +404,7 @@ def _oracle_decode_rate(case, budget_s=3.0):
 def _secondary_decode(builder, name, steps, warmup, note=None, cpu=True, fp8=False, groups=False):
     import torch
     case = builder()
-    run = Fp8DecodeRun(case) if fp8 else DecodeRun(case, groups=groups)
+    run = Fp8DecodeRun(case, groups=groups) if fp8 else DecodeRun(case, groups=groups)
     wall, per = run.timed(steps, warmup)
     kv, algo = run.algorithmic_bytes()
     dec_ms = per["partitions"] + per["merge"]
@@ -416,7 +423,7 @@ def _secondary_decode(builder, name, steps, warmup, note=None, cpu=True, fp8=Fal
         res["phases"] = ("plan, grouped balanced split and merge in one pa_decode call; "
                          "kernel times in the rocprofv3 summary")
         run.free()
-        plain = DecodeRun(case)   # the same workload without the flag, for comparison
+        plain = Fp8DecodeRun(case) if fp8 else DecodeRun(case)   # without the flag, for comparison
         _, pp = plain.timed(steps, warmup)
         res["decode_ms_without_groups"] = round(pp["partitions"] + pp["merge"], 4)
         plain.free()
@@ -754,7 +761,7 @@ def _run_one(name, steps, warmup):
         "decode_llama2_7b_layer_fp8": lambda: _secondary_decode(
             decode_llama2_7b_layer, name, steps, warmup, cpu=False, fp8=True),
         "decode_gqa_shared_prefix_fp8": lambda: _secondary_decode(
-            decode_gqa_shared_prefix, name, steps, warmup, cpu=False, fp8=True),
+            decode_gqa_shared_prefix, name, steps, warmup, cpu=False, fp8=True, groups=True),
         "decode_long_context_fp8": lambda: _secondary_decode(
             decode_long_context, name, steps, warmup, cpu=False, fp8=True),
         "decode_llama2_7b_layer_verify": lambda: _secondary_multi(steps, warmup),
@@ -931,7 +938,7 @@ def main():
         sec.append(_secondary_decode(decode_llama2_7b_layer, "decode_llama2_7b_layer_fp8", s2, w2,
                                      fp8=True))
         sec.append(_secondary_decode(decode_gqa_shared_prefix, "decode_gqa_shared_prefix_fp8", s2,
-                                     w2, fp8=True))
+                                     w2, fp8=True, groups=True))
         sec.append(_secondary_decode(decode_long_context, "decode_long_context_fp8", s2, w2,
                                      fp8=True))
         sec.append(_secondary_prefill(s2, w2, fp8=True))

@@ -424,6 +424,58 @@ __device__ __forceinline__ void balanced_walk(const DecodeArgs& a, int wave, Seg
     }
 }
 
+// ------------------------------------------------- sequence groups' stream
+// With sequence groups (shared prefixes) the balanced split runs over owners,
+// group after group: the group's shared run, then each member's blocks past
+// it (owner_blocks, written by the plan kernel).
+constexpr int kMaxGroupSeqs = 5;   // S = 16 / G with G >= 3
+
+__device__ __forceinline__ int group_owners(const DecodeArgs& a) {
+    const int groups = (a.num_seqs + a.seqs_per_wave - 1) / a.seqs_per_wave;
+    return groups * (a.seqs_per_wave + 1);
+}
+
+__device__ __forceinline__ BlockCounts owner_counts(const DecodeArgs& a) {
+    return BlockCounts(group_owners(a), [&](int i) { return a.owner_blocks[i]; });
+}
+
+// Calls segment(grp, g, sel, j0, j1, cnt, st) for every segment of this wave's
+// stretch st (kv head g), in stream order: blocks j0 .. j1-1 of owner
+// (group grp, member sel; sel < 0: the group's shared run) of cnt blocks.
+template <bool NT, typename Segment>
+__device__ __forceinline__ void grouped_walk(const DecodeArgs& a, int wave, Segment&& segment) {
+    const int64_t w = decode_workgroup<NT>() * 4 + wave;
+    const int64_t nst = a.num_items / a.num_kv_heads;
+    const int64_t st = w / a.num_kv_heads;
+    const int g = (int)(w - st * a.num_kv_heads);
+    if (st >= nst) return;
+    const int owners = group_owners(a);
+    const BlockCounts counts = owner_counts(a);
+    const int total = counts.total();
+    const int stretch = balanced_stretch(a, total);
+    const int64_t lo = st * stretch;
+    if (lo >= total) return;
+    int s = (int)lo;
+    const int s1 = (int)min((int64_t)total, lo + stretch);
+    // the owner o holding block s, and the stream position po of its first block
+    int o, po;
+    counts.locate(s, o, po);
+    const int S1 = a.seqs_per_wave + 1;
+    while (s < s1 && o < owners) {
+        const int cnt = a.owner_blocks[o];
+        if (s >= po + cnt) {   // past this owner (also skips empty ones)
+            po += cnt;
+            ++o;
+            continue;
+        }
+        const int grp = o / S1;
+        const int j0 = s - po;
+        const int j1 = min(cnt, j0 + (s1 - s));
+        segment(grp, g, o - grp * S1 - 1, j0, j1, cnt, st);
+        s += j1 - j0;
+    }
+}
+
 // Enqueue `kernel(a)` and return the status of that launch itself.  Every kernel
 // of the library takes one argument struct by value.  hipLaunchKernel's return
 // value belongs to this launch only: an error left on the thread by an earlier,

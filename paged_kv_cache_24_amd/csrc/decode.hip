@@ -513,17 +513,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
 // * Hkv + g) * 16 + column.  A row is finished in place when one segment saw
 // all of its blocks.
 
-constexpr int kMaxGroupSeqs = 5;   // S = 16 / G with G >= 3
-
-__device__ __forceinline__ int group_owners(const DecodeArgs& a) {
-    const int groups = (a.num_seqs + a.seqs_per_wave - 1) / a.seqs_per_wave;
-    return groups * (a.seqs_per_wave + 1);
-}
-
-__device__ __forceinline__ BlockCounts owner_counts(const DecodeArgs& a) {
-    return BlockCounts(group_owners(a), [&](int i) { return a.owner_blocks[i]; });
-}
-
 // The plan: one wave per group finds the shared run cp of its members' tables
 // (lane i tests block base + i; the scan ends by the longest member's last
 // block, where no member is in play) and writes the group's owner counts.
@@ -767,36 +756,9 @@ template <int DT, bool NT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void decode_gqa_grouped_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t vlds[4][kBlockSize * kVRow];
     const int wave = uniform(threadIdx.x >> 6);
-    const int64_t w = decode_workgroup<NT>() * 4 + wave;
-    const int64_t nst = a.num_items / a.num_kv_heads;
-    const int64_t st = w / a.num_kv_heads;
-    const int g = (int)(w - st * a.num_kv_heads);
-    if (st >= nst) return;
-    const int owners = group_owners(a);
-    const BlockCounts counts = owner_counts(a);
-    const int total = counts.total();
-    const int stretch = balanced_stretch(a, total);
-    const int64_t lo = st * stretch;
-    if (lo >= total) return;
-    int s = (int)lo;
-    const int s1 = (int)min((int64_t)total, lo + stretch);
-    // the owner o holding block s, and the stream position po of its first block
-    int o, po;
-    counts.locate(s, o, po);
-    const int S1 = a.seqs_per_wave + 1;
-    while (s < s1 && o < owners) {
-        const int cnt = a.owner_blocks[o];
-        if (s >= po + cnt) {   // past this owner (also skips empty ones)
-            po += cnt;
-            ++o;
-            continue;
-        }
-        const int grp = o / S1;
-        const int j0 = s - po;
-        const int j1 = min(cnt, j0 + (s1 - s));
-        grouped_segment<DT, NT>(a, vlds[wave], grp, g, o - grp * S1 - 1, j0, j1, cnt, st);
-        s += j1 - j0;
-    }
+    grouped_walk<NT>(a, wave, [&](int grp, int g, int sel, int j0, int j1, int cnt, int64_t st) {
+        grouped_segment<DT, NT>(a, vlds[wave], grp, g, sel, j0, j1, cnt, st);
+    });
 }
 
 // Combine the partial states of one (sequence, q head):
@@ -978,15 +940,20 @@ hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t s) {
     return a.q_per_seq > 1 ? launch_partitions_mq<true>(a, s, grid) : launch_partitions_mq<false>(a, s, grid);
 }
 
+hipError_t launch_group_plan(const DecodeArgs& a, hipStream_t s) {
+    if (a.seqs_per_wave < 2 || a.seqs_per_wave > kMaxGroupSeqs || !a.owner_blocks || a.num_seqs <= 0)
+        return hipErrorInvalidValue;
+    const int64_t groups = (a.num_seqs + a.seqs_per_wave - 1) / a.seqs_per_wave;
+    if (groups * (a.seqs_per_wave + 1) > kScanItems) return hipErrorInvalidValue;
+    return launch(decode_group_plan_kernel, dim3((unsigned)((groups + 3) / 4)), dim3(256), s, a);
+}
+
 hipError_t launch_decode_grouped(const DecodeArgs& a, hipStream_t s) {
     if (!a.gqa_mfma || a.head_dim != 128 || a.q_per_seq != 1 || !a.balanced || a.head_chunks != 1 ||
         a.seqs_per_wave < 2 || a.seqs_per_wave > kMaxGroupSeqs || a.seqs_per_wave * a.group > 16 ||
         !a.owner_blocks || !a.ws_acc || a.num_items <= 0 || a.num_items % a.num_kv_heads != 0)
         return hipErrorInvalidValue;
-    const int64_t groups = (a.num_seqs + a.seqs_per_wave - 1) / a.seqs_per_wave;
-    if (groups == 0) return hipSuccess;
-    if (groups * (a.seqs_per_wave + 1) > kScanItems) return hipErrorInvalidValue;
-    hipError_t e = launch(decode_group_plan_kernel, dim3((unsigned)((groups + 3) / 4)), dim3(256), s, a);
+    hipError_t e = launch_group_plan(a, s);
     if (e != hipSuccess) return e;
     const dim3 grid((unsigned)((a.num_items + 3) / 4));
     if (a.dtype == kF16)

@@ -591,6 +591,257 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     });
 }
 
+// ---------------------------------------------------------------------------
+// Sequence groups over the FP8 cache (PA_DECODE_SHARED_PREFIX): the owner
+// stream, plan and state slots of the 16-bit grouped decode (decode.hip), with
+// this file's block-pair step.  Column c carries member c / G, head c % G; a
+// shared run's pair scores every member still in play, a member's own pair its
+// G columns.  Own blocks stream (read once in the call), shared runs stay
+// cacheable.
+template <int DT, bool NT>
+__device__ __forceinline__ void fp8_grouped_segment(const DecodeArgs& a, uint16_t* vt, int grp, int g, int sel,
+                                                    int j0, int j1, int cnt, int64_t st) {
+    constexpr int D = 128;
+    constexpr int kTile = kFp8Tile;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int lr = lane & 15;    // MFMA column; token of the K rows; V^T row
+    const int lg = lane >> 4;    // tokens 4*lg .. 4*lg+3 of each block
+    const int S = a.seqs_per_wave;
+    const int b0 = grp * S;
+    const int s_col = lr / a.group;
+    const int h_col = lr - s_col * a.group;
+    const bool col_live = s_col < S && b0 + s_col < a.num_seqs;
+    const int n_col = col_live ? seq_tokens(a, b0 + s_col) : 0;
+    const int64_t my_row = (int64_t)(col_live ? b0 + s_col : b0) * a.num_q_heads + (int64_t)g * a.group + h_col;
+
+    int nt[kMaxGroupSeqs], nb[kMaxGroupSeqs];   // members' lengths and block counts (uniform)
+    int nmax = 0;
+#pragma unroll
+    for (int s = 0; s < kMaxGroupSeqs; ++s) {
+        nt[s] = s < S && b0 + s < a.num_seqs ? seq_tokens(a, b0 + s) : 0;
+        nb[s] = ceil_blocks(nt[s]);
+        nmax = max(nmax, nt[s]);
+    }
+    int off = 0, nsel = 0;
+#pragma unroll
+    for (int s = 0; s < kMaxGroupSeqs; ++s)
+        if (s == sel) {
+            off = nb[s] - cnt;
+            nsel = nt[s];
+        }
+    if (sel >= 0) nmax = nsel;   // V rows past it hold no token of this member
+    const bool on = sel < 0 ? col_live : s_col == sel;
+
+    uint4 qf[4];   // column lr, elements 32*lg + 8*kk .. +8
+    {
+        const uint16_t* q = static_cast<const uint16_t*>(a.q) + my_row * D + 32 * lg;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            qf[kk] = on ? *reinterpret_cast<const uint4*>(q + 8 * kk) : make_uint4(0, 0, 0, 0);
+    }
+    float m = -INFINITY;
+    float l = 0.f;
+    f8f32x4_t o[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) o[mt] = f8f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t row_stride = (int64_t)a.num_kv_heads * D;   // bytes
+    const uint8_t* kbase = static_cast<const uint8_t*>(a.k_cache) + (int64_t)g * D + 32 * lg +
+                           (int64_t)lr * row_stride;
+    const int vrow0 = 4 * lg + (lr >> 3);
+    const uint8_t* vbase = static_cast<const uint8_t*>(a.v_cache) + (int64_t)g * D + 16 * (lr & 7) +
+                           (int64_t)vrow0 * row_stride;
+    const bool k_half = lr < 8;
+    const float* scb = (k_half ? a.k_scales : a.v_scales) + (int64_t)g * kBlockSize + 4 * lg;
+    const int64_t scale_block_stride = (int64_t)a.num_kv_heads * kBlockSize;
+    const int32_t* tables = a.block_tables + (int64_t)b0 * a.table_stride;   // 16-token blocks
+    const float cs = a.scale_log2;
+    const int tr_off = (4 * lg + (lr >> 2)) * kVRowF8 + 4 * (lr & 3);
+    const int ja = off + j0, jb = off + j1;
+
+    struct Blk {
+        uint4 k[2], v[2];
+        float4 sc;
+        bool ok;
+    };
+    auto load_blk = [&](int j, Blk& r) {
+        if (j >= jb) {   // the odd block after the last one: nothing to read, every row masked
+            r.ok = false;
+            r.k[0] = r.k[1] = r.v[0] = r.v[1] = make_uint4(0, 0, 0, 0);
+            r.sc = make_float4(1.f, 1.f, 1.f, 1.f);
+            return;
+        }
+        int who = sel;
+        if (sel < 0) {   // the block every member in play names
+            who = 0;
+#pragma unroll
+            for (int s = kMaxGroupSeqs - 1; s >= 0; --s)
+                if (j < nb[s]) who = s;
+        }
+        const int pb = tables[(int64_t)who * a.table_stride + j];
+        r.ok = pb >= 0 && (int64_t)pb < a.num_blocks;
+        const int64_t blk = r.ok ? pb : 0;
+        const int64_t boff = blk * kBlockSize * row_stride;
+        if (sel >= 0) {
+            r.k[0] = load16<true>(kbase + boff);
+            r.k[1] = load16<true>(kbase + boff + 16);
+            r.v[0] = load16<true>(vbase + boff);
+            r.v[1] = load16<true>(vbase + boff + 2 * row_stride);
+        } else {
+            r.k[0] = load16<NT>(kbase + boff);
+            r.k[1] = load16<NT>(kbase + boff + 16);
+            r.v[0] = load16<NT>(vbase + boff);
+            r.v[1] = load16<NT>(vbase + boff + 2 * row_stride);
+        }
+        r.sc = *reinterpret_cast<const float4*>(scb + blk * scale_block_stride);
+    };
+
+    for (int j = ja; j < jb; j += 2) {
+        Blk pr[2];
+        load_blk(j, pr[0]);
+        load_blk(j + 1, pr[1]);
+        f8f32x4_t sacc[2];
+        float vs[2][4];
+        bool valid[2][4];
+        float x[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const Blk& bk = pr[h];
+            sacc[h] = f8f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const uint4& w = bk.k[kk >> 1];
+                const uint32_t w0 = (kk & 1) ? w.z : w.x;
+                const uint32_t w1 = (kk & 1) ? w.w : w.y;
+                const uint2 e0 = fp8x4_to_16<DT>(w0, 1.f), e1 = fp8x4_to_16<DT>(w1, 1.f);
+                sacc[h] = f8_mfma_16x16x32<DT>(make_uint4(e0.x, e0.y, e1.x, e1.y), qf[kk], sacc[h]);
+            }
+            const float mine[4] = {bk.sc.x, bk.sc.y, bk.sc.z, bk.sc.w};
+            float ks[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float other = dpp<kDppRowRor8>(mine[i]);
+                ks[i] = k_half ? mine[i] : other;
+                vs[h][i] = k_half ? other : mine[i];
+            }
+            const int t0 = (j + h) * kBlockSize;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                valid[h][i] = bk.ok && on && t0 + 4 * lg + i < n_col;
+                x[h][i] = valid[h][i] ? sacc[h][i] * (ks[i] * cs) : -INFINITY;
+            }
+        }
+        float mb = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                         fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+        mb = xor32_max(xor16_max(mb));
+        const bool raise = mb > m + 8.f;
+        const float mn = raise ? mb : m;
+        if (__any(raise)) {
+            const float alpha = raise ? fast_exp2(m - mn) : 1.f;
+            l *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) o[mt] *= alpha;
+        }
+        m = mn;
+        const float mu = mn == -INFINITY ? 0.f : mn;
+        float pm[2][4], imu[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = fast_exp2(x[h][i] - mu);
+                const float f = scale_mantissa(vs[h][i]);
+                pm[h][i] = valid[h][i] ? p * f : 0.f;
+                imu[h][i] = __builtin_amdgcn_rcpf(f);
+            }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const Blk& bk = pr[h];
+            const int t0 = (j + h) * kBlockSize;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int row = vrow0 + 2 * k;
+                const int sv = (lr >> 3) + 2 * k;
+                const float vsr = sv == 0 ? vs[h][0] : sv == 1 ? vs[h][1] : sv == 2 ? vs[h][2] : vs[h][3];
+                const bool ok = bk.ok && t0 + row < nmax;
+                const uint4& w = bk.v[k];
+                const uint2 e0 = fp8x4_to_16<DT>(w.x, vsr), e1 = fp8x4_to_16<DT>(w.y, vsr);
+                const uint2 e2 = fp8x4_to_16<DT>(w.z, vsr), e3 = fp8x4_to_16<DT>(w.w, vsr);
+                uint4* dst = reinterpret_cast<uint4*>(vt + h * kTile + row * kVRowF8 + 16 * (lr & 7));
+                dst[0] = ok ? make_uint4(e0.x, e0.y, e1.x, e1.y) : make_uint4(0, 0, 0, 0);
+                dst[1] = ok ? make_uint4(e2.x, e2.y, e3.x, e3.y) : make_uint4(0, 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        uint4 ph;
+        ph.x = pack2<DT>(pm[0][0], pm[0][1]);
+        ph.y = pack2<DT>(pm[0][2], pm[0][3]);
+        ph.z = pack2<DT>(pm[1][0], pm[1][1]);
+        ph.w = pack2<DT>(pm[1][2], pm[1][3]);
+        l = fmaf(lo_to_f32<DT>(ph.x), imu[0][0], l);
+        l = fmaf(hi_to_f32<DT>(ph.x), imu[0][1], l);
+        l = fmaf(lo_to_f32<DT>(ph.y), imu[0][2], l);
+        l = fmaf(hi_to_f32<DT>(ph.y), imu[0][3], l);
+        l = fmaf(lo_to_f32<DT>(ph.z), imu[1][0], l);
+        l = fmaf(hi_to_f32<DT>(ph.z), imu[1][1], l);
+        l = fmaf(lo_to_f32<DT>(ph.w), imu[1][2], l);
+        l = fmaf(hi_to_f32<DT>(ph.w), imu[1][3], l);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            const uint2 v0 = lds_read_tr16(vt + tr_off + 16 * mt);
+            const uint2 v1 = lds_read_tr16(vt + kTile + tr_off + 16 * mt);
+            o[mt] = f8_mfma_16x16x32<DT>(make_uint4(v0.x, v0.y, v1.x, v1.y), ph, o[mt]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+    const float lt = xor32_sum(xor16_sum(l));
+    if (!on) return;
+    const bool all = j0 == 0 && j1 == cnt;
+    bool final_out;
+    int64_t idx;
+    if (sel < 0) {
+        if (min(cnt, ceil_blocks(n_col)) == 0) return;   // an empty member: the merge writes its zeros
+        final_out = all && a.owner_blocks[(int64_t)grp * (S + 1) + 1 + s_col] == 0;
+        idx = a.shared_base + (((int64_t)grp + st) * a.num_kv_heads + g) * 16 + lr;
+    } else {
+        final_out = all && off == 0;
+        idx = (((int64_t)b0 + sel + st) * a.num_kv_heads + g) * a.group + h_col;
+    }
+    if (final_out) {
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        uint16_t* dst = static_cast<uint16_t*>(a.out) + my_row * D + 4 * lg;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            uint2 w;
+            w.x = pack2<DT>(o[mt][0] * inv, o[mt][1] * inv);
+            w.y = pack2<DT>(o[mt][2] * inv, o[mt][3] * inv);
+            *reinterpret_cast<uint2*>(dst + 16 * mt) = w;
+        }
+    } else {
+        float* dst = a.ws_acc + idx * D + 4 * lg;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+            *reinterpret_cast<float4*>(dst + 16 * mt) = make_float4(o[mt][0], o[mt][1], o[mt][2], o[mt][3]);
+        if (lg == 0) a.ws_ml[idx] = make_float2(m, lt);
+    }
+}
+
+// 3 waves per SIMD hold the balanced split's 3072 waves in one round (at 4 the
+// segment's registers spill)
+template <int DT, bool NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void decode_fp8_gqa_grouped_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t vlds[4][2 * kFp8Tile];
+    const int wave = uniform(threadIdx.x >> 6);
+    grouped_walk<NT>(a, wave, [&](int grp, int g, int sel, int j0, int j1, int cnt, int64_t st) {
+        fp8_grouped_segment<DT, NT>(a, vlds[wave], grp, g, sel, j0, j1, cnt, st);
+    });
+}
+
 template <int DT, int D, bool NT>
 static hipError_t launch_fp8_balanced_vector(const DecodeArgs& a, hipStream_t s, dim3 grid) {
     switch (a.heads_per_wave) {
@@ -623,6 +874,22 @@ static hipError_t launch_fp8_t(const DecodeArgs& a, hipStream_t s, dim3 grid) {
     if (a.gqa_mfma) return launch(decode_fp8_gqa_kernel<DT, NT, kGqaFp8Pairs>, grid, dim3(256), s, a);
     return a.head_dim == 128 ? launch_fp8_vector<DT, 128, NT>(a, s, grid)
                              : launch_fp8_vector<DT, 64, NT>(a, s, grid);
+}
+
+hipError_t launch_decode_grouped_fp8(const DecodeArgs& a, hipStream_t s) {
+    if (!a.gqa_mfma || a.head_dim != 128 || a.q_per_seq != 1 || !a.balanced || a.head_chunks != 1 ||
+        a.block_shift != 0 || a.seqs_per_wave < 2 || a.seqs_per_wave > kMaxGroupSeqs ||
+        a.seqs_per_wave * a.group > 16 || !a.owner_blocks || !a.ws_acc || !a.k_scales || !a.v_scales ||
+        a.num_items <= 0 || a.num_items % a.num_kv_heads != 0)
+        return hipErrorInvalidValue;
+    hipError_t e = launch_group_plan(a, s);
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)((a.num_items + 3) / 4));
+    if (a.dtype == kF16)
+        return a.stream_kv ? launch(decode_fp8_gqa_grouped_kernel<kF16, true>, grid, dim3(256), s, a)
+                           : launch(decode_fp8_gqa_grouped_kernel<kF16, false>, grid, dim3(256), s, a);
+    return a.stream_kv ? launch(decode_fp8_gqa_grouped_kernel<kBF16, true>, grid, dim3(256), s, a)
+                       : launch(decode_fp8_gqa_grouped_kernel<kBF16, false>, grid, dim3(256), s, a);
 }
 
 hipError_t launch_decode_partitions_fp8(const DecodeArgs& a, hipStream_t s) {

@@ -100,7 +100,9 @@ struct DecodeArgs {
     int32_t* owner_blocks;
 };
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_group_plan(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_grouped(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_grouped_fp8(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_partitions_fp8(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
 

@@ -352,6 +352,46 @@ pa_status check_workspace(const DecodeShape& shape, const void* workspace, size_
     return PA_OK;
 }
 
+// pa_decode / pa_decode_fp8 with PA_DECODE_SHARED_PREFIX: the sequence groups'
+// plan, grouped split and merge, or kNotGrouped where the call does not take
+// them (the caller then decodes without them).  fp8: k_scales / v_scales given.
+constexpr pa_status kNotGrouped = static_cast<pa_status>(1);
+
+pa_status decode_grouped(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                         const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                         float scale, pa_dtype dtype, int32_t partition_tokens, uint32_t flags, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+    const bool fp8 = k_scales || v_scales;
+    pa_status st = check_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                                num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale, dtype,
+                                partition_tokens);
+    if (st != PA_OK || num_seqs == 0) return st;
+    if (fp8 && block_size != PA_BLOCK_SIZE) return kNotGrouped;   // the FP8 call refuses it itself
+    const int32_t spw = group_seqs(flags, num_q_heads, num_kv_heads, head_dim, partition_tokens);
+    if (spw <= 1) return kNotGrouped;
+    const DecodeShape shape = grouped_shape(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                            max_blocks_per_seq << block_shift(block_size), spw);
+    if (!shape.valid) return kNotGrouped;
+    if (fp8) {
+        if (!k_scales || !v_scales) return PA_ERR_NULL_PTR;
+        if (!aligned16(k_scales) || !aligned16(v_scales)) return PA_ERR_ALIGNMENT;
+    }
+    st = check_workspace(shape, workspace, workspace_bytes);
+    if (st != PA_OK) return st;
+    pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                                   num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                                   dtype, shape, workspace, flags, 1, spw);
+    a.k_scales = k_scales;
+    a.v_scales = v_scales;
+    if (!decode_grids_fit(a)) return PA_ERR_SHAPE;
+    if (!check_decode_bounds(a, stream)) return PA_ERR_HIP;
+    if ((fp8 ? pa::launch_decode_grouped_fp8(a, stream) : pa::launch_decode_grouped(a, stream)) != hipSuccess)
+        return PA_ERR_HIP;
+    return pa::launch_decode_merge(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -650,6 +690,15 @@ pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache, const voi
                         int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
                         pa_dtype dtype, int32_t partition_tokens, uint32_t flags,
                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (flags & ~kDecodeFlags) return PA_ERR_UNSUPPORTED;
+    if ((flags & PA_DECODE_SHARED_PREFIX) && block_size == PA_BLOCK_SIZE) {
+        if (!k_scales || !v_scales) return PA_ERR_NULL_PTR;
+        const pa_status gst = decode_grouped(out, q, k_cache, v_cache, k_scales, v_scales, block_tables,
+                                             seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                             max_blocks_per_seq, num_blocks, scale, dtype, partition_tokens,
+                                             flags, workspace, workspace_bytes, stream);
+        if (gst != kNotGrouped) return gst;
+    }
     pa_status st = pa_decode_partitions_fp8(out, q, k_cache, v_cache, k_scales, v_scales,
                                             block_tables, seq_lens, num_seqs, num_q_heads,
                                             num_kv_heads, head_dim, block_size,
@@ -715,26 +764,11 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (flags & ~kDecodeFlags) return PA_ERR_UNSUPPORTED;
     if (flags & PA_DECODE_SHARED_PREFIX) {
-        pa_status st = check_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
-                                    num_q_heads, num_kv_heads, head_dim, block_size,
-                                    max_blocks_per_seq, num_blocks, scale, dtype, partition_tokens);
-        if (st != PA_OK || num_seqs == 0) return st;
-        const int32_t spw = group_seqs(flags, num_q_heads, num_kv_heads, head_dim, partition_tokens);
-        const DecodeShape shape = spw > 1 ? grouped_shape(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                                          max_blocks_per_seq << block_shift(block_size), spw)
-                                          : DecodeShape{};
-        if (spw > 1 && shape.valid) {
-            st = check_workspace(shape, workspace, workspace_bytes);
-            if (st != PA_OK) return st;
-            const pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, seq_lens,
-                                                 num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                                                 max_blocks_per_seq, num_blocks, scale, dtype, shape,
-                                                 workspace, flags, 1, spw);
-            if (!decode_grids_fit(a)) return PA_ERR_SHAPE;
-            if (!check_decode_bounds(a, stream)) return PA_ERR_HIP;
-            if (pa::launch_decode_grouped(a, stream) != hipSuccess) return PA_ERR_HIP;
-            return pa::launch_decode_merge(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
-        }
+        const pa_status st = decode_grouped(out, q, k_cache, v_cache, nullptr, nullptr, block_tables, seq_lens,
+                                            num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                            max_blocks_per_seq, num_blocks, scale, dtype, partition_tokens, flags,
+                                            workspace, workspace_bytes, stream);
+        if (st != kNotGrouped) return st;
     }
     pa_status st = pa_decode_partitions(out, q, k_cache, v_cache, block_tables, seq_lens,
                                         num_seqs, num_q_heads, num_kv_heads, head_dim,

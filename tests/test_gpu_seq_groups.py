@@ -2,17 +2,18 @@
 
 With the flag, pa_decode lets one wave carry the q heads of S = 16 / group
 consecutive sequences through the leading blocks they share (read once for
-all of them, cut into four ranges), and the balanced split takes the rest of
-every sequence.  Checked against the float64 oracle: groups of 3 to 8 q heads
+all of them); the balanced split runs over those shared runs and every
+sequence's own blocks.  Checked against the float64 oracle: groups of 3 to 8 q heads
 per kv head (S = 5 to 2), sharing patterns cut across the waves on purpose
 (prefix runs of 3 or 16 sequences against waves of 2 to 5 sequences), a
 ragged last group, empty sequences, sequences shorter than the prefix, and
 hand-built tables for the edges of the shared run: every sequence sharing all
 of its blocks, sharing that ends where fewer than two sequences remain,
-sharing broken and resumed, shared runs of 1 to 3 blocks (empty ranges).
-Where no block is shared the flagged call takes exactly the unflagged
-balanced split's path and must match it bit for bit; everywhere the result
-must not depend on where the pool's blocks sit."""
+sharing broken and resumed, shared runs of 1 to 3 blocks.  The same over the
+FP8 cache (pa_decode_fp8) against the oracle's FP8 decode.  Where no block is
+shared the flagged call takes exactly the unflagged balanced split's path and
+must match it bit for bit; everywhere the result must not depend on where the
+pool's blocks sit."""
 
 import math
 
@@ -21,7 +22,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import DecodeOnGPU, TOL, assert_close, dev_bits, dev_int, host_bits, host_f64, require_gpu
+from gpu_helpers import (DecodeOnGPU, Fp8DecodeOnGPU, TOL, assert_close, dev_bits, dev_int, host_bits, host_f64,
+                         require_gpu)
 from workloads import DecodeCase, decode_gqa_shared_prefix, make_decode_case, normal_bits
 
 pytestmark = pytest.mark.gpu
@@ -234,3 +236,60 @@ def test_noalloc_with_flag_equals_pa_decode():
     pa.pa_decode_noalloc(out, g.q, g.k_cache, g.v_cache, g.tables, g.lens, c.scale,
                          flags=pa.PA_DECODE_SHARED_PREFIX)
     np.testing.assert_array_equal(a, host_bits(out))
+
+
+def _check_fp8(c, parts=(0, -1)):
+    import oracle
+    g = Fp8DecodeOnGPU(c)
+    g.write()
+    kc, vc, ks, vs = g.oracle_pools()
+    ref = oracle.ref_decode_fp8(c.q, kc, vc, ks, vs, c.block_tables, c.seq_lens, c.scale, c.dtype)
+    for part in parts:
+        out = host_f64(g.decode(partition_tokens=part, flags=_flag()))
+        assert_close(out, ref, c.dtype, f"fp8 {c.name} partition={part}")
+    return g
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("group,hkv", [(3, 2), (4, 2), (8, 1)])
+@pytest.mark.parametrize("share_group", [0, 3, 16])
+def test_fp8_groups_match_oracle(dtype, group, hkv, share_group):
+    _check_fp8(_case(dtype, group, hkv, share_group))
+
+
+@pytest.mark.parametrize("name,tables,lens", [
+    ("all-shared", _rows(SHARE, SHARE, SHARE, SHARE), [160, 160, 160, 160]),
+    ("lengths", _rows(SHARE, SHARE, SHARE, SHARE), [5, 40, 100, 160]),
+    ("broken", _rows(SHARE, SHARE[:4] + [20] + SHARE[5:], SHARE, SHARE), [160, 150, 140, 130]),
+    ("run1", _rows([0, 11], [0, 12], [0, 13], [0, 14]), [30, 32, 20, 17]),
+    ("run3", _rows([0, 1, 2, 11], [0, 1, 2, 12], [0, 1, 2, 13], [0, 1, 2, 14]), [60, 64, 49, 50]),
+    ("two-groups", _rows(SHARE, SHARE, [], SHARE, [15, 16, 17], [15, 16, 18], [15], [15, 16, 19]),
+     [150, 160, 0, 1, 40, 48, 3, 37]),
+])
+def test_fp8_shared_run_edges(name, tables, lens):
+    _check_fp8(_explicit_case(f"fp8-edge-{name}", tables, lens, seed=len(name) + 7))
+
+
+def test_fp8_no_shared_block_equals_balanced_bit_exact():
+    c = _case("bf16", 4, 2, 0)
+    g = Fp8DecodeOnGPU(c)
+    g.write()
+    a = host_bits(g.decode(partition_tokens=-1)).copy()
+    np.testing.assert_array_equal(a, host_bits(g.decode(flags=_flag())))
+
+
+def test_fp8_block_permutation_invariance_bit_exact():
+    c = decode_gqa_shared_prefix(batch=19, max_len=1024, min_len=16, group=4, prefix=256)
+    g = Fp8DecodeOnGPU(c)
+    g.write()
+    base = host_bits(g.decode(flags=_flag())).copy()
+    perm = np.random.default_rng(82).permutation(c.num_blocks)
+    inv = torch.from_numpy(np.argsort(perm)).cuda()
+    # move every pool block b to perm[b]
+    for name in ("k_cache", "v_cache", "k_scales", "v_scales"):
+        t = getattr(g, name)
+        setattr(g, name, t[inv].contiguous())
+    tables = np.where(c.block_tables >= 0, perm[np.maximum(c.block_tables, 0)], -1).astype(np.int32)
+    g.tables = dev_int(tables)
+    moved = host_bits(g.decode(flags=_flag()))
+    np.testing.assert_array_equal(base, moved)
