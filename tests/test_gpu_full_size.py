@@ -164,6 +164,12 @@ def test_full_gqa_shared_prefix_decode_fp8():
     _sampled_decode_fp8(c, _pick(c.seq_lens, 16))
 
 
+def test_full_gqa_shared_prefix_decode_fp8_sequence_groups():
+    import paged_kv_cache_24_amd as pa
+    c = decode_gqa_shared_prefix()
+    _sampled_decode_fp8(c, _pick(c.seq_lens, 16), flags=pa.PA_DECODE_SHARED_PREFIX)
+
+
 def test_full_long_context_decode_fp8():
     import paged_kv_cache_24_amd as pa
     _sampled_decode_fp8(decode_long_context(), [0, 2, 5, 7], flags=pa.PA_DECODE_STREAM_KV)

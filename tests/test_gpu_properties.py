@@ -165,6 +165,52 @@ def test_fp8_decode_matches_oracle(drawn):
                           f"{c.name} fp8 partition={part}")
 
 
+@st.composite
+def shared_prefix_cases(draw):
+    """Runs of sequences sharing a prefix, cut across the waves' sequence groups."""
+    dtype = draw(st.sampled_from(["f16", "bf16"]))
+    hkv = draw(st.sampled_from([1, 2]))
+    group = draw(st.sampled_from([3, 4, 5, 6, 8]))
+    n = draw(st.integers(2, 12))
+    share = draw(st.sampled_from([0, 2, 3, 4, 5, 8]))
+    prefix = draw(st.sampled_from([16, 32, 64, 256]))
+    lens = draw(st.lists(LENS, min_size=n, max_size=n))
+    runs = (n + share - 1) // share if share else 0
+    need = sum((x + 15) // 16 for x in lens) + runs * prefix // 16
+    mb = max(1, max((x + 15) // 16 for x in lens)) + draw(st.integers(0, 3))
+    seed = draw(st.integers(0, 2 ** 31 - 1))
+    part = draw(st.sampled_from([0, -1]))
+    c = make_decode_case(name=f"prop-shared-{dtype}-{hkv}x{group}-s{share}-p{prefix}", seed=seed, dtype=dtype,
+                         num_q_heads=hkv * group, num_kv_heads=hkv, head_dim=128, seq_lens=lens,
+                         num_blocks=max(1, need), max_blocks_per_seq=max(mb, prefix // 16),
+                         scale=1 / math.sqrt(128), write_last=False, share_group=share,
+                         share_tokens=prefix if share else 0)
+    return c, part
+
+
+@PROPS
+@given(shared_prefix_cases(), st.booleans())
+def test_sequence_groups_match_oracle(drawn, fp8):
+    """PA_DECODE_SHARED_PREFIX over either cache."""
+    import paged_kv_cache_24_amd as pa
+    c, part = drawn
+    _say(c, partition=part, cache="fp8" if fp8 else "16-bit", flags="shared-prefix")
+    if fp8:
+        g = Fp8DecodeOnGPU(c)
+        g.write()
+        kc, vc, ks, vs = g.oracle_pools()
+        ref = oracle.ref_decode_fp8(c.q, kc, vc, ks, vs, c.block_tables, c.seq_lens, c.scale, c.dtype)
+        keys = lambda b, n: (_tokens8(kc, ks, c.block_tables[b], n), _tokens8(vc, vs, c.block_tables[b], n))
+    else:
+        g = DecodeOnGPU(c)
+        ref = oracle.ref_decode(c.q, c.k_cache, c.v_cache, c.block_tables, c.seq_lens, c.scale, c.dtype)
+        keys = lambda b, n: (_tokens16(c.k_cache, c.block_tables[b], n, c.dtype),
+                             _tokens16(c.v_cache, c.block_tables[b], n, c.dtype))
+    out = host_f64(g.decode(partition_tokens=part, flags=pa.PA_DECODE_SHARED_PREFIX))
+    assert_close_or_bound(out, ref, c.dtype, _decode_bound(c, ref, keys, U_MFMA[c.dtype]),
+                          f"{c.name} partition={part}")
+
+
 @PROPS
 @given(decode_cases(), st.integers(2, 5))
 def test_multi_query_matches_oracle(drawn, nq):
