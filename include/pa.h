@@ -46,9 +46,10 @@
  * PA_ERR_ALIGNMENT nothing was launched.  PA_ERR_HIP means the HIP runtime
  * refused a launch; it is that launch's own status, so an error an earlier,
  * unrelated HIP call left on the thread is neither reported as PA_ERR_HIP nor
- * cleared.  The calls that enqueue two kernels (pa_decode, pa_decode_multi
- * and pa_decode_fp8 when they split, pa_copy_blocks_fp8) may have enqueued the
- * first before the runtime refused the second.  No C++ exception crosses this
+ * cleared.  The calls that enqueue several kernels (pa_decode, pa_decode_multi
+ * and pa_decode_fp8 when they split or take sequence groups,
+ * pa_copy_blocks_fp8) may have enqueued the first before the runtime refused a
+ * later one.  No C++ exception crosses this
  * interface.  Device-resident indices are not validated on the host (that
  * would need a read-back): a block-table entry outside [0, num_blocks) or a
  * slot outside [0, num_blocks * block_size) is never dereferenced -- the

@@ -105,6 +105,71 @@ def test_captured_decode_step(hq, hkv, dtype, bs):
 
 
 @pytest.mark.parametrize("fp8", [False, True])
+def test_captured_shared_prefix_step(fp8):
+    """pa_decode (pa_decode_fp8) with PA_DECODE_SHARED_PREFIX captured once: the
+    sequence groups' shared runs are found on the device at every replay, so
+    replays that change lengths, break a sharing run (one sequence's prefix
+    copied to blocks of its own) and restore it all match the oracle."""
+    # 8 q / 2 kv heads: waves of 4 sequences, aligned with the runs of 4 sharers
+    import paged_kv_cache_24_amd as pa
+    from gpu_helpers import Fp8DecodeOnGPU
+    lens = [300, 17, 1, 129, 64, 0, 250, 200, 96, 33, 5]
+    c = make_decode_case(name="graph-shared", seed=23, dtype="bf16", num_q_heads=8, num_kv_heads=2,
+                         head_dim=128, seq_lens=lens, num_blocks=96, max_blocks_per_seq=20,
+                         scale=1 / math.sqrt(128), write_last=False, share_group=4, share_tokens=64)
+    g = Fp8DecodeOnGPU(c) if fp8 else DecodeOnGPU(c)
+    names = ("k_cache", "v_cache", "k_scales", "v_scales") if fp8 else ("k_cache", "v_cache")
+    if fp8:
+        g.write()
+        host = dict(zip(names, (np.array(x) for x in g.oracle_pools())))   # the oracle's own FP8 write
+        np.testing.assert_array_equal(g.k_cache.cpu().numpy(), host["k_cache"])
+    else:
+        host = {"k_cache": c.k_cache.copy(), "v_cache": c.v_cache.copy()}
+    flags = pa.PA_DECODE_SHARED_PREFIX
+    need = pa.pa_decode_workspace_size(c.num_seqs, 8, 2, 128, 16, c.max_blocks_per_seq, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out_graph = torch.empty_like(g.q)
+    # four free blocks for the prefix copy of sequence 3
+    used = set(c.block_tables[c.block_tables >= 0].tolist())
+    free = [b for b in range(c.num_blocks) if b not in used][:4]
+    assert len(free) == 4
+
+    def step(out=out_graph):
+        if fp8:
+            pa.pa_decode_fp8(out, g.q, g.k_cache, g.v_cache, g.k_scales, g.v_scales, g.tables, g.lens,
+                             c.scale, 0, workspace=ws, flags=flags)
+        else:
+            pa.pa_decode(out, g.q, g.k_cache, g.v_cache, g.tables, g.lens, c.scale, 0, workspace=ws,
+                         flags=flags)
+
+    graph = _capture(step)
+    rng = np.random.default_rng(24)
+    for replay in range(4):
+        q = normal_bits(rng, tuple(g.q.shape), "bf16")
+        g.q.copy_(dev_bits(q, "bf16"))
+        new_lens = np.array(lens, np.int32)
+        new_lens[0] = 300 - 9 * replay
+        tables = c.block_tables.copy()
+        if replay % 2:   # sequence 3 leaves its run: the prefix blocks copied to blocks of its own
+            src = [int(b) for b in c.block_tables[3, :4]]
+            for name in names:
+                t = getattr(g, name)
+                t[free] = t[src]
+                host[name][free] = host[name][src]
+            tables[3, :4] = free
+        g.lens.copy_(dev_int(new_lens))
+        g.tables.copy_(dev_int(tables))
+        got, eager = _replay_then_eager(graph, step, out_graph, lambda: torch.empty_like(g.q))
+        np.testing.assert_array_equal(got, eager, err_msg=f"replay {replay}")
+        if fp8:
+            ref = oracle.ref_decode_fp8(q, host["k_cache"], host["v_cache"], host["k_scales"], host["v_scales"],
+                                        tables, new_lens, c.scale, "bf16")
+        else:
+            ref = oracle.ref_decode(q, host["k_cache"], host["v_cache"], tables, new_lens, c.scale, "bf16")
+        assert_close(host_f64(out_graph), ref, "bf16", f"replay {replay}")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
 def test_bucket_padded_decode_step(fp8):
     """A decode step captured once at a bucket of 8 sequences, then replayed
     with 5, 8, 3 and 1 live sequences: the rows past the live ones are padding
