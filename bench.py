@@ -163,44 +163,66 @@ class DecodeRun:
             self.flags |= pa.PA_DECODE_SHARED_PREFIX
             self.split = "sequence groups + balanced"
 
-    def step(self, ev=None):
+    def _write(self):
+        self.pa.pa_reshape_and_cache(self.key, self.value, self.kc, self.vc, self.slots)
+
+    def _partitions(self):
         pa, c = self.pa, self.c
-        if ev is not None:
-            ev[0].record()
-        if self.has_write:
-            pa.pa_reshape_and_cache(self.key, self.value, self.kc, self.vc, self.slots)
-        if ev is not None:
-            ev[1].record()
         if self.groups:   # the phases run inside one call: all of it counts as "partitions"
             pa.pa_decode(self.out, self.q, self.kc, self.vc, self.tables, self.lens, c.scale, self.part,
                          workspace=self.ws, flags=self.flags)
-            if ev is not None:
-                ev[2].record()
-                ev[3].record()
             return
         pa.pa_decode_partitions(self.out, self.q, self.kc, self.vc, self.tables, self.lens, c.scale,
                                 self.ws, self.part, flags=self.flags)
+
+    def _merge(self):
+        if not self.groups:
+            c = self.c
+            self.pa.pa_decode_merge(self.out, self.lens, c.num_kv_heads, c.max_blocks_per_seq, self.ws,
+                                    self.part, block_size=c.block_size)
+
+    def step(self, ev=None, part_only=False):
+        """One step: cache write, decode partitions, merge.  ev: HIP events on the
+        current stream -- four (before the write, after it, after the partitions,
+        after the merge), or with part_only two, around the partitions alone."""
+        full = ev is not None and not part_only
+        if full:
+            ev[0].record()
+        if self.has_write:
+            self._write()
         if ev is not None:
-            ev[2].record()
-        pa.pa_decode_merge(self.out, self.lens, c.num_kv_heads, c.max_blocks_per_seq, self.ws,
-                           self.part, block_size=c.block_size)
+            ev[0 if part_only else 1].record()
+        self._partitions()
         if ev is not None:
+            ev[1 if part_only else 2].record()
+        self._merge()
+        if full:
             ev[3].record()
 
     def timed(self, steps, warmup):
+        """Wall time per step over `steps` timed steps, with HIP events around the
+        partition kernel only (events between kernels cost time: four per step
+        add 3% here, two 1%); then the same number of untimed steps with events
+        between every kernel for the per-kernel breakdown."""
         import torch
         _settle(self.step)
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        timer = _Timer(["write", "partitions", "merge"])
+        part = _Timer(["partitions"])
         t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step(part.step(), part_only=True)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+        timer = _Timer(["write", "partitions", "merge"])
         for _ in range(steps):
             self.step(timer.step())
         torch.cuda.synchronize()
-        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-        self.last_timer = timer
-        return wall_ms, timer.mean_ms()
+        self.last_timer = part
+        per = timer.mean_ms()
+        per["partitions"] = part.mean_ms()["partitions"]   # the roofline's kernel: from the timed steps
+        return wall_ms, per
 
     def timed_cold(self, steps, evict_bytes=512 << 20):
         """Per-step kernel times with a write of ``evict_bytes`` between steps
@@ -264,31 +286,24 @@ class Fp8DecodeRun(DecodeRun):
         torch.cuda.synchronize()
         self.kc = self.vc = None            # the 16-bit pools are not used by the timed step
 
-    def step(self, ev=None):
+    def _write(self):
+        self.pa.pa_reshape_and_cache_fp8(self.key, self.value, self.kc8, self.vc8, self.ks, self.vs, self.slots)
+
+    def _partitions(self):
         pa, c = self.pa, self.c
-        if ev is not None:
-            ev[0].record()
-        if self.has_write:
-            pa.pa_reshape_and_cache_fp8(self.key, self.value, self.kc8, self.vc8, self.ks, self.vs,
-                                        self.slots)
-        if ev is not None:
-            ev[1].record()
         if self.groups:   # the phases run inside one call: all of it counts as "partitions"
             pa.pa_decode_fp8(self.out, self.q, self.kc8, self.vc8, self.ks, self.vs, self.tables, self.lens,
                              c.scale, self.part, workspace=self.ws, flags=self.flags)
-            if ev is not None:
-                ev[2].record()
-                ev[3].record()
             return
         pa.pa_decode_partitions_fp8(self.out, self.q, self.kc8, self.vc8, self.ks, self.vs,
                                     self.tables, self.lens, c.scale, self.ws, self.part,
                                     flags=self.flags)
-        if ev is not None:
-            ev[2].record()
-        pa.pa_decode_merge(self.out, self.lens, c.num_kv_heads, c.max_blocks_per_seq, self.ws,
-                           self.part)
-        if ev is not None:
-            ev[3].record()
+
+    def _merge(self):
+        if not self.groups:
+            c = self.c
+            self.pa.pa_decode_merge(self.out, self.lens, c.num_kv_heads, c.max_blocks_per_seq, self.ws,
+                                    self.part)
 
     def algorithmic_bytes(self):
         """K+V codes and their float32 scales of the live tokens, q, table, output."""
@@ -446,38 +461,54 @@ def _secondary_decode(builder, name, steps, warmup, note=None, cpu=True, fp8=Fal
 def _secondary_tiny_latency(steps=200, warmup=20):
     """decode_tiny as a latency figure: one step (cache write of 4 tokens +
     decode) launched eagerly, and the same step captured once in a HIP graph
-    and replayed; wall time per step with no events in between."""
+    and replayed; wall time per step with no events in between.  The same for
+    pa_decode_step, whose decode kernels perform the cache write themselves
+    (one kernel per step instead of two)."""
     import torch
     from workloads import decode_tiny
     case = decode_tiny()
     run = DecodeRun(case)
-    _settle(run.step)
-    for _ in range(warmup):
-        run.step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        run.step()
-    torch.cuda.synchronize()
-    eager_us = (time.perf_counter() - t0) * 1e6 / steps
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        run.step()
-    for _ in range(warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    graph_us = (time.perf_counter() - t0) * 1e6 / steps
+    assert len(case.slot_mapping) == case.num_seqs   # every sequence has a newest token
+
+    def fused():
+        run.pa.pa_decode_step(run.out, run.q, run.key, run.value, run.kc, run.vc, run.tables, run.lens,
+                              case.scale, run.part, workspace=run.ws, flags=run.flags)
+
+    def measure(step):
+        _settle(step)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        eager = (time.perf_counter() - t0) * 1e6 / steps
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        replay = (time.perf_counter() - t0) * 1e6 / steps
+        del graph
+        return round(eager, 2), round(replay, 2)
+
+    eager_us, graph_us = measure(run.step)
+    fused_eager_us, fused_graph_us = measure(fused)
     run.free()
-    del graph, run
+    del run
     torch.cuda.empty_cache()
-    return {"workload": "decode_tiny_latency", "eager_us_per_step": round(eager_us, 2),
-            "graph_replay_us_per_step": round(graph_us, 2),
+    return {"workload": "decode_tiny_latency", "eager_us_per_step": eager_us,
+            "graph_replay_us_per_step": graph_us,
+            "decode_step_eager_us_per_step": fused_eager_us, "decode_step_graph_replay_us_per_step": fused_graph_us,
             "note": "write + decode of batch 4; wall clock over back-to-back steps, no events; "
-                    "the graph holds the same kernel launches (one decode partition, no merge)"}
+                    "the graph holds the same kernel launches (one decode partition, no merge); "
+                    "decode_step_*: pa_decode_step, the write inside the decode kernel"}
 
 
 def _shared_prefix_note(case):
@@ -898,7 +929,8 @@ def main():
                    "seq_lens": "uniform int [512, 4096], seed 2",
                    "num_blocks": case.num_blocks, "kv_bytes": kv,
                    "split": run.split, "stream_kv": bool(run.flags),
-                   "step": "cache write of 64 tokens + paged decode (partitions + merge)"},
+                   "step": "cache write of 64 tokens + paged decode (partitions + merge); HIP events "
+                           "around the partition kernel only in the timed steps"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
         "tokens_per_s": round(case.num_seqs / (wall_ms * 1e-3), 1),
         "kernel_ms": {k: round(v, 4) for k, v in per.items()},

@@ -274,6 +274,40 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pa_decode_step -- one decode step: the cache write of each sequence's newest
+ * token and pa_decode over the caches it leaves ("vLLM-Ascend 原理", §2.4 step 3:
+ * the step stores the new k/v, then the new position's q attends to the whole
+ * prefix).  The same as pa_reshape_and_cache with slot_mapping[b] = the slot of
+ * position seq_lens[b] - 1 through block_tables, followed by pa_decode with the
+ * same arguments, except that the decode kernels perform the write themselves:
+ * the wave that reads a sequence's last block takes the newest row from
+ * key / value rather than from the pool, scores it in one more step, and stores
+ * it to its slot -- one kernel fewer per step (16-bit caches).
+ *
+ *   key, value    [num_seqs][num_kv_heads][head_dim], the dtype of q: the k and
+ *                 v of each sequence's newest token (position seq_lens[b] - 1);
+ *                 rows of sequences with seq_lens[b] = 0 are not read.
+ *   the rest      as pa_decode; k_cache / v_cache are written.
+ *
+ * The pools afterwards equal those of the separate write bit for bit; a slot
+ * whose table entry lies outside the pool is not written (as the cache write
+ * skips it).  Outputs agree with the separate calls to the decode tolerance,
+ * not bit for bit (the newest key joins the softmax in its own step).  With
+ * PA_DECODE_SHARED_PREFIX taking effect, the write runs first as its own
+ * kernel and the grouped decode follows (outputs then equal the separate calls
+ * bit for bit).  Two sequences whose newest tokens name the same slot, or a
+ * slot inside another sequence's context, are a caller error, as with the
+ * separate write.  Errors: as pa_decode; PA_ERR_NULL_PTR for a missing
+ * key / value, PA_ERR_ALIGNMENT for one not 16-byte aligned.
+ */
+pa_status pa_decode_step(void* out, const void* q, const void* key, const void* value, void* k_cache,
+                         void* v_cache, const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t max_blocks_per_seq, int64_t num_blocks, float scale, pa_dtype dtype,
+                         int32_t partition_tokens, uint32_t flags, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
  * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): the same arguments minus the workspace, the same kernels
@@ -355,6 +389,19 @@ pa_status pa_decode_merge(void* out, const int32_t* seq_lens, int32_t num_seqs,
                           int32_t block_size, int32_t max_blocks_per_seq, pa_dtype dtype,
                           int32_t partition_tokens, const void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
+/*
+ * pa_decode_partitions_step -- the first phase of pa_decode_step: the decode
+ * partitions with the step's cache write inside them (key / value as for
+ * pa_decode_step), followed by pa_decode_merge.  PA_DECODE_SHARED_PREFIX has
+ * no effect here, as for pa_decode_partitions.
+ */
+pa_status pa_decode_partitions_step(void* out, const void* q, const void* key, const void* value,
+                                    void* k_cache, void* v_cache, const int32_t* block_tables,
+                                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                                    pa_dtype dtype, int32_t partition_tokens, uint32_t flags,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * pa_prefill_paged -- causal chunked prefill over the paged cache

@@ -30,6 +30,7 @@ __all__ = [
     "PA_PARTITION_BALANCED", "lib",
     "pa_kv_bytes_per_token", "pa_status_string", "pa_reshape_and_cache", "pa_copy_blocks",
     "pa_decode_default_partition", "pa_decode_split", "pa_decode_workspace_size", "pa_decode",
+    "pa_decode_step", "pa_decode_partitions_step",
     "pa_decode_partitions", "pa_decode_merge", "pa_prefill_paged",
     "pa_reshape_and_cache_fp8", "pa_copy_blocks_fp8", "pa_decode_fp8", "pa_decode_partitions_fp8",
     "pa_prefill_paged_fp8", "pa_decode_multi", "pa_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
@@ -68,6 +69,10 @@ _SIGS = {
                          _f32, _i32, _i32, _u32, _vp, _sz, _vp]),
     "pa_decode_partitions": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _i64, _f32, _i32, _i32, _u32, _vp, _sz, _vp]),
+    "pa_decode_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                              _i64, _f32, _i32, _i32, _u32, _vp, _sz, _vp]),
+    "pa_decode_partitions_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                         _i32, _i64, _f32, _i32, _i32, _u32, _vp, _sz, _vp]),
     "pa_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                  _i64, _f32, _i32, _i32, _u32, _vp]),
     "pa_decode_multi": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -237,6 +242,43 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, partition
         hkv, d, bs, mb, nb, float(scale), _kv_dtype(k_cache), partition_tokens, flags, _ptr(ws), ws_bytes,
         _stream(stream)))
     return out
+
+
+def _new_rows(key, value, q, hkv, d):
+    _need(key, "key", q.dtype, 3)
+    _need(value, "value", q.dtype, 3)
+    if tuple(key.shape) != (q.shape[0], hkv, d) or tuple(value.shape) != tuple(key.shape):
+        raise ValueError(f"key/value must be [{q.shape[0]}, {hkv}, {d}], got {tuple(key.shape)} / "
+                         f"{tuple(value.shape)}")
+
+
+def pa_decode_step(out, q, key, value, k_cache, v_cache, block_tables, seq_lens, scale, partition_tokens=0,
+                   workspace=None, stream=None, flags=0):
+    """One decode step: the cache write of each sequence's newest token
+    (``key``/``value`` ``[B, Hkv, D]``, position ``seq_lens[b] - 1``) and
+    ``pa_decode``, the write done inside the decode kernels."""
+    nb, bs, hkv, d, b, hq, mb = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens)
+    _new_rows(key, value, q, hkv, d)
+    need = pa_decode_workspace_size(b, hq, hkv, d, bs, mb, partition_tokens)
+    ws, ws_bytes = _workspace(workspace, need, q.device)
+    _check("pa_decode_step", lib.pa_decode_step(
+        _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(seq_lens), b, hq, hkv, d, bs, mb, nb, float(scale), _kv_dtype(k_cache), partition_tokens, flags,
+        _ptr(ws), ws_bytes, _stream(stream)))
+    return out
+
+
+def pa_decode_partitions_step(out, q, key, value, k_cache, v_cache, block_tables, seq_lens, scale, workspace,
+                              partition_tokens=0, stream=None, flags=0):
+    """The first phase of ``pa_decode_step`` (then ``pa_decode_merge``)."""
+    nb, bs, hkv, d, b, hq, mb = _decode_args(out, q, k_cache, v_cache, block_tables, seq_lens)
+    _new_rows(key, value, q, hkv, d)
+    need = pa_decode_workspace_size(b, hq, hkv, d, bs, mb, partition_tokens)
+    ws, ws_bytes = _workspace(workspace, need, q.device)
+    _check("pa_decode_partitions_step", lib.pa_decode_partitions_step(
+        _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(seq_lens), b, hq, hkv, d, bs, mb, nb, float(scale), _kv_dtype(k_cache), partition_tokens, flags,
+        _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, seq_lens, scale, partition_tokens=0,

@@ -51,6 +51,12 @@ __device__ __forceinline__ void vector_segment(const DecodeArgs& a, int b, int g
     const int hbase = hc * HPW;
     const int hcount = min(HPW, (MQ ? a.cols : a.group) - hbase);
     const int64_t q_row0 = (int64_t)b * a.num_q_heads + (int64_t)g * a.group + hbase;
+    // the step's cache write (new_k set, single query): the newest token, at
+    // position n - 1, is not read from the pool (nm = n - 1 keys come from it);
+    // the wave whose segment ends the sequence scores it from new_k / new_v in one
+    // more step and, for the first head chunk, stores it to its slot
+    const bool fused = !MQ && a.new_k != nullptr && n > 0;
+    int nm = fused ? n - 1 : n;
     // q / out row of column h; with MQ also the keys it may see
     int64_t qrow[HPW];
     int lim[HPW];
@@ -63,10 +69,10 @@ __device__ __forceinline__ void vector_segment(const DecodeArgs& a, int b, int g
             lim[h] = n - a.q_per_seq + 1 + jq;
         } else {
             qrow[h] = q_row0 + h;
-            lim[h] = n;
+            lim[h] = nm;
         }
     }
-    const int lim_min = MQ ? n - a.q_per_seq + 1 : n;   // keys every column sees
+    int lim_min = MQ ? n - a.q_per_seq + 1 : nm;   // keys every column sees
 
     uint4 qv[HPW];
     {
@@ -129,7 +135,7 @@ __device__ __forceinline__ void vector_segment(const DecodeArgs& a, int b, int g
 #pragma unroll
             for (int i = 0; i < TPL; ++i) {
                 const int tok = j * kBlockSize + i * RPW + r;
-                const bool valid = ok && (tok < n);
+                const bool valid = ok && (tok < nm);
 #pragma unroll
                 for (int h = 0; h < HPW; ++h) s[h][i] = (ok && tok < lim[h]) ? s[h][i] : -INFINITY;
 #pragma unroll
@@ -178,6 +184,32 @@ __device__ __forceinline__ void vector_segment(const DecodeArgs& a, int b, int g
             if (j + 2 >= j1) break;
             if (j + 4 < j1) okb = load(j + 4, kb, vb);
             process(kc, vc, okc, j + 2);
+        }
+    }
+    if (fused && j1 == ceil_blocks(n)) {   // the newest token: row 0 of one more step
+        const int64_t new_off = ((int64_t)b * a.num_kv_heads + g) * D + 8 * c;
+        uint4 kx[TPL], vx[TPL];
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) kx[i] = vx[i] = make_uint4(0, 0, 0, 0);
+        if (r == 0) {
+            kx[0] = load_kv<true>(static_cast<const uint16_t*>(a.new_k) + new_off);
+            vx[0] = load_kv<true>(static_cast<const uint16_t*>(a.new_v) + new_off);
+        }
+        // a block outside the pool: the token is masked and not written, as the
+        // separate cache write would skip its slot and the decode the block
+        const int jn = (n - 1) / kBlockSize;
+        const int pb = sub_block(table[jn >> a.block_shift], jn, a.block_shift);
+        const bool okn = pb >= 0 && (int64_t)pb < a.num_blocks;
+        nm = 1;
+        lim_min = 1;
+#pragma unroll
+        for (int h = 0; h < HPW; ++h) lim[h] = 1;
+        process(kx, vx, okn, 0);
+        if (hc == 0 && r == 0 && okn) {
+            const int64_t dst = ((int64_t)pb * kBlockSize + (n - 1) % kBlockSize) * row_stride;
+            // the pools are written here only (the step's cache write)
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(const_cast<void*>(a.k_cache)) + lane_off + dst) = kx[0];
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(const_cast<void*>(a.v_cache)) + lane_off + dst) = vx[0];
         }
     }
 
@@ -360,6 +392,11 @@ __device__ __forceinline__ void gqa_segment(const DecodeArgs& a, uint16_t* vt, i
     const float cs = a.scale_log2;
     // transposed-read address of this lane: row 4*(lr/4) + lg, column 4*(lr%4) (+16 per tile)
     const uint16_t* vtr = vt + (4 * (lr >> 2) + lg) * kVRow + 4 * (lr & 3);
+    // the step's cache write (new_k set, single query): as in vector_segment, the
+    // newest token is left out of the pool's keys (nm = n - 1) and scored from
+    // new_k / new_v in one more step by the wave whose segment ends the sequence
+    const bool fused = !MQ && a.new_k != nullptr && n > 0;
+    int nm = fused ? n - 1 : n;
 
     auto load = [&](int j, uint4 (&kr)[4], uint4 (&vr)[4]) -> bool {
         const int pb = sub_block(table[j >> a.block_shift], j, a.block_shift);
@@ -377,12 +414,12 @@ __device__ __forceinline__ void gqa_segment(const DecodeArgs& a, uint16_t* vt, i
         df32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) sacc = mfma_16x16x32<DT>(kr[kk], qf[kk], sacc);
-        const bool full = ok && (j + 1) * kBlockSize <= n;
+        const bool full = ok && (j + 1) * kBlockSize <= nm;
         bool valid[4];
         float x[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            valid[i] = full || (ok && (j * kBlockSize + 4 * i + lg < n));
+            valid[i] = full || (ok && (j * kBlockSize + 4 * i + lg < nm));
             // MQ: the score of column lr also ends at the column's own position
             const bool seen = MQ ? (ok && j * kBlockSize + 4 * i + lg < lim) : valid[i];
             x[i] = seen ? sacc[i] * cs : -INFINITY;
@@ -444,6 +481,35 @@ __device__ __forceinline__ void gqa_segment(const DecodeArgs& a, uint16_t* vt, i
                 vc[i] = vn[i];
             }
             okc = okn;
+        }
+    }
+    if (fused && j1 == ceil_blocks(n)) {   // the newest token: key 0 of one more step
+        const int64_t new_row = ((int64_t)b * a.num_kv_heads + g) * D;
+        uint4 kx[4], vx[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kx[i] = vx[i] = make_uint4(0, 0, 0, 0);
+        if (tk == 0) {   // K row 0: lanes lr = 0, elements 8*lg + 32*i
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                kx[i] = load_kv<true>(static_cast<const uint16_t*>(a.new_k) + new_row + 8 * lg + 32 * i);
+        }
+        if (lg == 0) vx[0] = load_kv<true>(static_cast<const uint16_t*>(a.new_v) + new_row + 8 * lr);   // V row 0
+        // a block outside the pool: the token is masked and not written (as in vector_segment)
+        const int jn = (n - 1) / kBlockSize;
+        const int pb = sub_block(table[jn >> a.block_shift], jn, a.block_shift);
+        const bool okn = pb >= 0 && (int64_t)pb < a.num_blocks;
+        nm = 1;
+        process(kx, vx, okn, 0);
+        if (hc == 0 && okn) {
+            // the pools are written here only (the step's cache write)
+            const int64_t dst = ((int64_t)pb * kBlockSize + (n - 1) % kBlockSize) * row_stride + (int64_t)g * D;
+            uint16_t* kp = static_cast<uint16_t*>(const_cast<void*>(a.k_cache)) + dst;
+            uint16_t* vp = static_cast<uint16_t*>(const_cast<void*>(a.v_cache)) + dst;
+            if (tk == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(kp + 8 * lg + 32 * i) = kx[i];
+            }
+            if (lg == 0) *reinterpret_cast<uint4*>(vp + 8 * lr) = vx[0];
         }
     }
 

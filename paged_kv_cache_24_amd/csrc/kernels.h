@@ -17,6 +17,12 @@ struct ReshapeArgs {
     int64_t num_tokens;
     int64_t num_slots;       // num_blocks * block_size
     int32_t row_vecs;        // 16-byte vectors per token row (kv_heads * head_dim / 8)
+    // slots from the block table instead (slot_mapping nullptr): token t is the
+    // newest of sequence t, at position seq_lens[t] - 1 (clamped to the row)
+    const int32_t* block_tables;
+    const int32_t* seq_lens;
+    int32_t table_stride;
+    int32_t block_size;
 };
 hipError_t launch_reshape_and_cache(const ReshapeArgs& a, hipStream_t stream);
 
@@ -98,6 +104,12 @@ struct DecodeArgs {
     int32_t seqs_per_wave;
     int64_t shared_base;
     int32_t* owner_blocks;
+    // the decode step's cache write, done by the decode itself (pa_decode_step):
+    // new_k / new_v [num_seqs][Hkv][D] hold each sequence's newest token, at
+    // position seq_len - 1; the wave that reads that token's block takes the
+    // row from here and stores it to its slot (nullptr: no write)
+    const void* new_k;
+    const void* new_v;
 };
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_group_plan(const DecodeArgs& a, hipStream_t stream);

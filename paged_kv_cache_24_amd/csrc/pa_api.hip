@@ -289,6 +289,8 @@ pa::DecodeArgs decode_args(void* out, const void* q, const void* k_cache, const 
     const size_t upb = (size_t)num_kv_heads * a.head_chunks;
     size_t states = shape.balanced ? ((size_t)num_seqs + shape.num_items / upb) * upb * a.state_heads
                                    : (size_t)num_seqs * q_per_seq * num_q_heads * shape.num_parts;
+    a.new_k = nullptr;
+    a.new_v = nullptr;
     a.seqs_per_wave = seqs_per_wave;
     a.shared_base = (int64_t)states;
     size_t owners = 0;
@@ -350,6 +352,36 @@ pa_status check_workspace(const DecodeShape& shape, const void* workspace, size_
     if (!workspace || workspace_bytes < shape.ws_bytes) return PA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return PA_ERR_ALIGNMENT;
     return PA_OK;
+}
+
+// The first decode phase; with new_k / new_v also the step's cache write of each
+// sequence's newest token, done by the decode kernels themselves.
+pa_status decode_partitions(void* out, const void* q, const void* new_k, const void* new_v, const void* k_cache,
+                            const void* v_cache, const int32_t* block_tables, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                            pa_dtype dtype, int32_t partition_tokens, uint32_t flags, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    if (flags & ~kDecodeFlags) return PA_ERR_UNSUPPORTED;
+    pa_status st = check_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+                                num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_blocks_per_seq, num_blocks, scale, dtype, partition_tokens);
+    if (st != PA_OK || num_seqs == 0) return st;
+    if (new_k && (!aligned16(new_k) || !aligned16(new_v))) return PA_ERR_ALIGNMENT;
+    const DecodeShape shape = decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                           max_blocks_per_seq << block_shift(block_size),
+                                           partition_tokens, true);
+    if (!shape.valid) return PA_ERR_SHAPE;
+    st = check_workspace(shape, workspace, workspace_bytes);
+    if (st != PA_OK) return st;
+    pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                                   num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                                   dtype, shape, workspace, flags);
+    a.new_k = new_k;
+    a.new_v = new_v;
+    if (!decode_grids_fit(a)) return PA_ERR_SHAPE;
+    if (!check_decode_bounds(a, stream)) return PA_ERR_HIP;
+    return pa::launch_decode_partitions(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 // pa_decode / pa_decode_fp8 with PA_DECODE_SHARED_PREFIX: the sequence groups'
@@ -439,6 +471,10 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
     a.num_tokens = num_tokens;
     a.num_slots = num_blocks * block_size;   // a slot's row sits at the same place for any block_size
     a.row_vecs = num_kv_heads * head_dim / 8;
+    a.block_tables = nullptr;
+    a.seq_lens = nullptr;
+    a.table_stride = 0;
+    a.block_size = block_size;
 #ifdef PA_DEBUG_BOUNDS
     pa::BoundsArgs ba = bounds_args(pa::kBoundsSlots, num_tokens, a.num_slots);
     ba.indices = slot_mapping;
@@ -597,24 +633,22 @@ pa_status pa_decode_partitions(void* out, const void* q, const void* k_cache, co
                                int64_t num_blocks, float scale, pa_dtype dtype,
                                int32_t partition_tokens, uint32_t flags, void* workspace,
                                size_t workspace_bytes, hipStream_t stream) {
-    if (flags & ~kDecodeFlags) return PA_ERR_UNSUPPORTED;
-    pa_status st = check_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs,
-                                num_q_heads, num_kv_heads, head_dim, block_size,
-                                max_blocks_per_seq, num_blocks, scale, dtype, partition_tokens);
-    if (st != PA_OK || num_seqs == 0) return st;
-    const DecodeShape shape = decode_shape(num_seqs, num_q_heads, num_kv_heads, head_dim,
-                                           max_blocks_per_seq << block_shift(block_size),
-                                           partition_tokens, true);
-    if (!shape.valid) return PA_ERR_SHAPE;
-    st = check_workspace(shape, workspace, workspace_bytes);
-    if (st != PA_OK) return st;
-    const pa::DecodeArgs a = decode_args(out, q, k_cache, v_cache, block_tables, seq_lens,
-                                         num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-                                         max_blocks_per_seq, num_blocks, scale, dtype, shape,
-                                         workspace, flags);
-    if (!decode_grids_fit(a)) return PA_ERR_SHAPE;
-    if (!check_decode_bounds(a, stream)) return PA_ERR_HIP;
-    return pa::launch_decode_partitions(a, stream) == hipSuccess ? PA_OK : PA_ERR_HIP;
+    return decode_partitions(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+                             num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                             scale, dtype, partition_tokens, flags, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_partitions_step(void* out, const void* q, const void* key, const void* value,
+                                    void* k_cache, void* v_cache, const int32_t* block_tables,
+                                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                    int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                                    pa_dtype dtype, int32_t partition_tokens, uint32_t flags,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (num_seqs > 0 && (!key || !value)) return PA_ERR_NULL_PTR;
+    return decode_partitions(out, q, key, value, k_cache, v_cache, block_tables, seq_lens, num_seqs,
+                             num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                             scale, dtype, partition_tokens, flags, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_decode_merge(void* out, const int32_t* seq_lens, int32_t num_seqs,
@@ -779,6 +813,53 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
     return pa_decode_merge(out, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                            block_size, max_blocks_per_seq, dtype, partition_tokens, workspace,
                            workspace_bytes, stream);
+}
+
+pa_status pa_decode_step(void* out, const void* q, const void* key, const void* value, void* k_cache,
+                         void* v_cache, const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int32_t max_blocks_per_seq, int64_t num_blocks, float scale, pa_dtype dtype,
+                         int32_t partition_tokens, uint32_t flags, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+    if (flags & ~kDecodeFlags) return PA_ERR_UNSUPPORTED;
+    pa_status st = check_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                                num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale, dtype,
+                                partition_tokens);
+    if (st != PA_OK || num_seqs == 0) return st;
+    if (!key || !value) return PA_ERR_NULL_PTR;
+    if (!aligned16(key) || !aligned16(value)) return PA_ERR_ALIGNMENT;
+    const int32_t spw = group_seqs(flags, num_q_heads, num_kv_heads, head_dim, partition_tokens);
+    if (spw > 1) {
+        const DecodeShape g = grouped_shape(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                            max_blocks_per_seq << block_shift(block_size), spw);
+        if (g.valid) {   // sequence groups read the newest tokens from the pool: the write goes first
+            st = check_workspace(g, workspace, workspace_bytes);
+            if (st != PA_OK) return st;
+            pa::ReshapeArgs w;
+            w.key = key;
+            w.value = value;
+            w.k_cache = k_cache;
+            w.v_cache = v_cache;
+            w.slot_mapping = nullptr;
+            w.num_tokens = num_seqs;
+            w.num_slots = num_blocks * block_size;
+            w.row_vecs = num_kv_heads * head_dim / 8;
+            w.block_tables = block_tables;
+            w.seq_lens = seq_lens;
+            w.table_stride = max_blocks_per_seq;
+            w.block_size = block_size;
+            if (pa::launch_reshape_and_cache(w, stream) != hipSuccess) return PA_ERR_HIP;
+            return decode_grouped(out, q, k_cache, v_cache, nullptr, nullptr, block_tables, seq_lens, num_seqs,
+                                  num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                                  scale, dtype, partition_tokens, flags, workspace, workspace_bytes, stream);
+        }
+    }
+    st = decode_partitions(out, q, key, value, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                           num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale, dtype,
+                           partition_tokens, flags, workspace, workspace_bytes, stream);
+    if (st != PA_OK) return st;
+    return pa_decode_merge(out, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                           max_blocks_per_seq, dtype, partition_tokens, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,

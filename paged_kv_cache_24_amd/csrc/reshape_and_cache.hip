@@ -26,7 +26,16 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(ReshapeArgs a) {
     for (int k = 0; k < TPW; ++k) {
         const int64_t t = t0 + k;
         if (t >= a.num_tokens) return;
-        const int64_t slot = slots[t];
+        int64_t slot;
+        if (a.slot_mapping) {
+            slot = slots[t];
+        } else {   // the newest token of sequence t, through its table row
+            const int max_tokens = a.table_stride * a.block_size;
+            const int n = min(a.seq_lens[t], max_tokens);
+            if (n <= 0) continue;
+            const int e = a.block_tables[t * (int64_t)a.table_stride + (n - 1) / a.block_size];
+            slot = e < 0 ? -1 : (int64_t)e * a.block_size + (n - 1) % a.block_size;
+        }
         if (slot < 0 || slot >= a.num_slots) continue;   // padding row or outside the pool
         const u32x4* ks = static_cast<const u32x4*>(a.key) + t * row_vecs;
         const u32x4* vs = static_cast<const u32x4*>(a.value) + t * row_vecs;

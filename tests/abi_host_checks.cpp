@@ -103,6 +103,14 @@ int main() {
                                                     0, 0, F, 1 << 20, nullptr),
            PA_ERR_SHAPE);
 
+    // the decode step (cache write inside the decode)
+    expect("step key", pa_decode_step(F, F, nullptr, F, F, F, FI, FI, 2, 8, 2, 128, 16, 64, 128, 0.1f, PA_BF16, 0,
+                                      0, F, 1 << 20, nullptr),
+           PA_ERR_NULL_PTR);
+    expect("step table width", pa_decode_partitions_step(F, F, F, F, F, F, FI, FI, 2, 8, 2, 128, 32, INT32_MAX,
+                                                         128, 0.1f, PA_BF16, 0, 0, F, 1 << 20, nullptr),
+           PA_ERR_SHAPE);
+
     // prefill
     expect("prefill null", pa_prefill_paged(F, F, F, F, FI, FI, nullptr, 2, 64, 40, 32, 8, 128, 16, 16, 64, 0.1f,
                                             PA_BF16, nullptr),

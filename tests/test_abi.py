@@ -35,7 +35,7 @@ def test_header_declares_the_calls():
               "pa_decode_merge", "pa_decode_default_partition", "pa_copy_blocks",
               "pa_reshape_and_cache_fp8", "pa_copy_blocks_fp8", "pa_decode_fp8",
               "pa_decode_partitions_fp8", "pa_prefill_paged_fp8", "pa_decode_multi",
-              "pa_decode_noalloc"]:
+              "pa_decode_noalloc", "pa_decode_step", "pa_decode_partitions_step"]:
         assert n in names
 
 
@@ -166,6 +166,34 @@ def test_decode_rejects(lib, fn):
     assert _decode(lib, fn, part=-1, b=513, ws=None) == SHAPE
     assert _decode(lib, fn, part=-2) == SHAPE
     assert _decode(lib, fn, part=-16) == SHAPE
+
+
+def _step(lib, fn="pa_decode_step", key=FAKE, value=FAKE, **kw):
+    f = getattr(lib, fn)
+    f.restype = ctypes.c_int32
+    f.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_uint32, P, ctypes.c_size_t, P]
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, b=2, hq=8, hkv=2, d=128, bs=16, mb=64,
+             nb=128, scale=0.1, dt=BF16, part=0, flags=0, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return f(a["out"], a["q"], key, value, a["kc"], a["vc"], a["bt"], a["sl"], a["b"], a["hq"], a["hkv"], a["d"],
+             a["bs"], a["mb"], a["nb"], a["scale"], a["dt"], a["part"], a["flags"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("fn", ["pa_decode_step", "pa_decode_partitions_step"])
+def test_decode_step_rejects(lib, fn):
+    """The decode step (cache write inside the decode) validates like pa_decode,
+    plus its key / value rows."""
+    assert _step(lib, fn, key=None) == NULL
+    assert _step(lib, fn, value=None) == NULL
+    assert _step(lib, fn, key=FAKE + 2) == ALIGN
+    assert _step(lib, fn, q=None) == NULL
+    assert _step(lib, fn, d=80) == UNSUP
+    assert _step(lib, fn, flags=4) == UNSUP
+    assert _step(lib, fn, part=24) == SHAPE
+    assert _step(lib, fn, part=256, ws=None) == WS
+    assert _step(lib, fn, b=0, q=None, key=None) == PA_OK
 
 
 def test_shared_prefix_flag_needs_the_group_workspace(lib):

@@ -104,6 +104,59 @@ def test_captured_decode_step(hq, hkv, dtype, bs):
         assert not (got[new_lens == 0] & 0x7FFF).any(), "an empty sequence must give zeros"
 
 
+def test_captured_decode_step_fused_write():
+    """pa_decode_step (the cache write inside the decode kernels) captured once and
+    replayed with new key/value/q and lengths that advance by one token per
+    replay, as a serving loop does: pools bit-exact vs the oracle's writes,
+    outputs within tolerance, replay == eager."""
+    import paged_kv_cache_24_amd as pa
+    lens0 = np.array([40, 1, 16, 129, 63], np.int32)
+    c = make_decode_case(name="graph-step", seed=25, dtype="f16", num_q_heads=8, num_kv_heads=8, head_dim=128,
+                         seq_lens=lens0 + 4, num_blocks=48, max_blocks_per_seq=10, scale=1 / math.sqrt(128),
+                         write_last=False)
+    g = DecodeOnGPU(c)
+    kc, vc = c.k_cache.copy(), c.v_cache.copy()
+    key = torch.empty((c.num_seqs, 8, 128), dtype=torch.float16, device="cuda")
+    value = torch.empty_like(key)
+    g.lens.copy_(dev_int(lens0))
+    out_graph = torch.empty_like(g.q)
+
+    def step(out=out_graph):
+        pa.pa_decode_step(out, g.q, key, value, g.k_cache, g.v_cache, g.tables, g.lens, c.scale, 0)
+
+    rng = np.random.default_rng(26)
+    graph = None
+    for replay in range(4):
+        lens = lens0 + replay
+        kn = normal_bits(rng, (c.num_seqs, 8, 128), "f16")
+        vn = normal_bits(rng, (c.num_seqs, 8, 128), "f16")
+        q = normal_bits(rng, tuple(g.q.shape), "f16")
+        key.copy_(dev_bits(kn, "f16"))
+        value.copy_(dev_bits(vn, "f16"))
+        g.q.copy_(dev_bits(q, "f16"))
+        g.lens.copy_(dev_int(lens))
+        # the oracle: each sequence's newest token written at position lens - 1, then the decode
+        slots = np.array([int(c.block_tables[b, (n - 1) // 16]) * 16 + (n - 1) % 16 for b, n in enumerate(lens)],
+                         np.int64)
+        kc, vc = oracle.ref_reshape_and_cache(kn, vn, kc, vc, slots)
+        ref = oracle.ref_decode(q, kc, vc, c.block_tables, lens, c.scale, "f16")
+        if graph is None:
+            pools = (g.k_cache.clone(), g.v_cache.clone())
+            graph = _capture(step)                  # the warm-up and the capture ran the step once
+            g.k_cache.copy_(pools[0])
+            g.v_cache.copy_(pools[1])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_bits(g.k_cache), kc, err_msg=f"replay {replay}: K pool")
+        np.testing.assert_array_equal(host_bits(g.v_cache), vc, err_msg=f"replay {replay}: V pool")
+        assert_close(host_f64(out_graph), ref, "f16", f"replay {replay}")
+        eager = torch.empty_like(g.q)
+        step(eager)                                 # rewrites the same rows with the same values
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host_bits(out_graph), host_bits(eager), err_msg=f"replay {replay}")
+
+
 @pytest.mark.parametrize("fp8", [False, True])
 def test_captured_shared_prefix_step(fp8):
     """pa_decode (pa_decode_fp8) with PA_DECODE_SHARED_PREFIX captured once: the
