@@ -849,9 +849,14 @@ pa_status pa_decode_step(void* out, const void* q, const void* key, const void* 
             w.table_stride = max_blocks_per_seq;
             w.block_size = block_size;
             if (pa::launch_reshape_and_cache(w, stream) != hipSuccess) return PA_ERR_HIP;
-            return decode_grouped(out, q, k_cache, v_cache, nullptr, nullptr, block_tables, seq_lens, num_seqs,
-                                  num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
-                                  scale, dtype, partition_tokens, flags, workspace, workspace_bytes, stream);
+            st = decode_grouped(out, q, k_cache, v_cache, nullptr, nullptr, block_tables, seq_lens, num_seqs,
+                                num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                                scale, dtype, partition_tokens, flags, workspace, workspace_bytes, stream);
+            if (st != kNotGrouped) return st;
+            // (not reached: the checks above are the groups' own) the rows are written: decode them
+            return pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads, num_kv_heads,
+                             head_dim, block_size, max_blocks_per_seq, num_blocks, scale, dtype, partition_tokens,
+                             flags & ~PA_DECODE_SHARED_PREFIX, workspace, workspace_bytes, stream);
         }
     }
     st = decode_partitions(out, q, key, value, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
