@@ -732,7 +732,7 @@ def _secondary_multi(steps, warmup, nq=4):
             "pct_hbm_peak": round(100 * kv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1),
             "query_tokens_per_s": round(c.num_seqs * nq / (ms * 1e-3), 1),
             "note": "all queries of a sequence share one read of its K/V (matrix-core kernel: "
-                    "4 (query, head) columns per kv head)"}
+                    "4 (query, head) columns per kv head; the balanced split at partition 0)"}
 
 
 def _copy_probe(nbytes=4 << 30):

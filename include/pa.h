@@ -137,8 +137,9 @@ typedef enum pa_dtype {
  *   PA_PARTITION_BALANCED  the balanced split: the blocks of all sequences,
  *        one after another, are cut into equal stretches, each read by one
  *        wave per kv head (and q-head chunk), so every wave gets the same
- *        work whatever the mix of lengths.  Single-query calls with at most
- *        512 sequences only; otherwise PA_ERR_SHAPE.
+ *        work whatever the mix of lengths.  At most 512 sequences; several
+ *        queries per sequence (pa_decode_multi) only on the matrix-core path
+ *        (head_dim 128, q_per_seq x group >= 3); otherwise PA_ERR_SHAPE.
  * The split changes float32 rounding only: the online-softmax merge of
  * partial states is exact ("vLLM-Ascend 原理", §四 "ATB 算子").
  */
@@ -348,11 +349,13 @@ pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const
  *                 whose position is negative gives an all-zero row.
  *   q_per_seq     1 .. PA_MAX_QUERIES_PER_SEQ (1 is exactly pa_decode).
  *   workspace     pa_decode_workspace_size(num_seqs * q_per_seq, ...) bytes.
- *   partition_tokens  0 picks a default: the single-query default, doubled
- *                 (at most 2048 tokens) when q_per_seq > 1 and the call runs
- *                 on the matrix-core kernel (head_dim 128, q_per_seq x group >= 3).  The
- *                 workspace size above, taken with partition_tokens 0, always
- *                 suffices for it.
+ *   partition_tokens  0 picks a default: with q_per_seq > 1 on the matrix-core
+ *                 kernel (head_dim 128, q_per_seq x group >= 3) the balanced
+ *                 split, whose units carry the (query, head) columns of a kv
+ *                 head, where its partial states fit the workspace size above;
+ *                 else the single-query default partition, doubled (at most
+ *                 2048 tokens) on the matrix-core kernel.  The workspace size
+ *                 above, taken with partition_tokens 0, always suffices for it.
  *
  * Rejecting drafts needs no work here: the next step simply passes the
  * shorter seq_lens.  Every other argument and rule as for pa_decode.

@@ -550,12 +550,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) voi
                                    nparts == 1, it.part);
 }
 
-template <int DT, bool NT>
+// MQ: several queries per sequence (their (query, head) columns share each block)
+template <int DT, bool NT, bool MQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void decode_gqa_balanced_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t vlds[4][kBlockSize * kVRow];
     const int wave = uniform(threadIdx.x >> 6);
     balanced_walk<NT>(a, wave, [&](int b, int g, int hc, int n, int j0, int j1, bool whole, int64_t slot) {
-        gqa_segment<DT, NT, false, true>(a, vlds[wave], b, g, hc, n, j0, j1, whole, slot);
+        gqa_segment<DT, NT, MQ, true>(a, vlds[wave], b, g, hc, n, j0, j1, whole, slot);
     });
 }
 
@@ -891,8 +892,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
                 count = s1 - s0 + 1;
             }
         } else {
-            const int hc = (head - g * a.group) / a.heads_per_wave;
-            const int h = head - g * a.group - hc * a.heads_per_wave;
+            // the row's column of its kv head: (query, head) = jq * group + head % group
+            const int jq = (int)((item / a.num_q_heads) % a.q_per_seq);
+            const int col = jq * a.group + head - g * a.group;
+            const int hc = col / a.heads_per_wave;
+            const int h = col - hc * a.heads_per_wave;
             const int upb = a.num_kv_heads * a.head_chunks;
             const BlockCounts counts = sequence_blocks(a);
             const int before = counts.prefix(b);
@@ -985,14 +989,18 @@ static hipError_t launch_balanced_d(const DecodeArgs& a, hipStream_t s, dim3 gri
 
 template <int DT, bool NT>
 static hipError_t launch_balanced_t(const DecodeArgs& a, hipStream_t s, dim3 grid) {
-    if (a.gqa_mfma) return launch(decode_gqa_balanced_kernel<DT, NT>, grid, dim3(256), s, a);
+    if (a.gqa_mfma)
+        return a.q_per_seq > 1 ? launch(decode_gqa_balanced_kernel<DT, NT, true>, grid, dim3(256), s, a)
+                               : launch(decode_gqa_balanced_kernel<DT, NT, false>, grid, dim3(256), s, a);
     return a.head_dim == 128 ? launch_balanced_d<DT, 128, NT>(a, s, grid)
                              : launch_balanced_d<DT, 64, NT>(a, s, grid);
 }
 
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t s) {
     if (a.balanced) {
-        if (a.q_per_seq != 1 || a.num_items <= 0 || a.num_seqs > kScanItems) return hipErrorInvalidValue;
+        // several queries per sequence: on matrix cores only
+        if ((a.q_per_seq != 1 && !a.gqa_mfma) || a.num_items <= 0 || a.num_seqs > kScanItems)
+            return hipErrorInvalidValue;
         const dim3 grid((unsigned)((a.num_items + 3) / 4));
         if (a.dtype == kF16)
             return a.stream_kv ? launch_balanced_t<kF16, true>(a, s, grid) : launch_balanced_t<kF16, false>(a, s, grid);

@@ -170,7 +170,7 @@ int32_t decode_wave_heads(int32_t cols, int32_t head_dim, bool balanced) {
 }
 
 // max_blocks16: 16-token blocks per sequence.  may_balance: a single-query
-// call (the balanced split has no multi-query form).
+// call (multi-query calls take multi_balanced_shape instead).
 //   partition_tokens > 0: fixed partitions of that length.
 //   partition_tokens == 0: the balanced split when fixed partitions of the
 //     default length would need more items than one round of resident waves
@@ -222,6 +222,28 @@ DecodeShape decode_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_h
     } else if (partition_tokens == PA_PARTITION_BALANCED) {
         s.valid = false;
     }
+    return s;
+}
+
+// The balanced split of a multi-query decode (q_per_seq > 1): the stream runs
+// over the sequences' blocks and each unit (kv head, chunk of 16 of its
+// q_per_seq * group (query, head) columns) reads a block once for every query
+// of its sequence; matrix-core path only (head_dim 128, 3+ columns per kv head).
+// valid = false where it does not apply.
+DecodeShape multi_balanced_shape(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_blocks16, int32_t q_per_seq) {
+    DecodeShape s{};
+    const int32_t cols = q_per_seq * (num_q_heads / num_kv_heads);
+    if (head_dim != 128 || cols < 3 || num_seqs > kBalancedMaxSeqs || (int64_t)num_seqs * max_blocks16 > INT32_MAX)
+        return s;
+    const int64_t upb = (int64_t)num_kv_heads * ceil_div(cols, 16);
+    const int64_t stretches = kBalancedWavesMfma / upb;
+    if (stretches < 1) return s;
+    s.valid = true;
+    s.balanced = true;
+    s.num_items = (int32_t)(stretches * upb);
+    const size_t states = (size_t)(num_seqs + stretches) * upb * std::min(cols, 16);
+    s.ws_bytes = states * ((size_t)head_dim * sizeof(float) + 2 * sizeof(float));
     return s;
 }
 
@@ -768,14 +790,31 @@ pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const v
     // more partitions than the single-query default, so the workspace size
     // documented for it always suffices.
     const int32_t mb16 = max_blocks_per_seq << block_shift(block_size);
-    if (partition_tokens == 0 && q_per_seq > 1 && head_dim == 128 &&
-        q_per_seq * (num_q_heads / num_kv_heads) >= 3)
-        partition_tokens = std::min<int32_t>(
-            2 * default_partition(num_q_heads, num_kv_heads, head_dim, mb16), 2048);
-    // the partial states are per (sequence, query, q head): the workspace of
-    // num_seqs * q_per_seq single-query sequences
-    const DecodeShape shape = decode_shape(num_seqs * q_per_seq, num_q_heads, num_kv_heads,
-                                           head_dim, mb16, partition_tokens, q_per_seq == 1);
+    // Several queries on matrix cores: the balanced split (partition 0 or
+    // PA_PARTITION_BALANCED) where its partial states fit the workspace that
+    // pa_decode_workspace_size documents for this call (num_seqs * q_per_seq
+    // single-query sequences, the same partition_tokens), so that no caller
+    // needs more; PA_PARTITION_BALANCED is refused otherwise (below).
+    DecodeShape shape{};
+    if (q_per_seq > 1 && (partition_tokens == 0 || partition_tokens == PA_PARTITION_BALANCED)) {
+        const DecodeShape mb = multi_balanced_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, mb16, q_per_seq);
+        const size_t documented =
+            std::max(decode_shape(num_seqs * q_per_seq, num_q_heads, num_kv_heads, head_dim, mb16, partition_tokens,
+                                  true).ws_bytes,
+                     decode_shape(num_seqs * q_per_seq, num_q_heads, num_kv_heads, head_dim, mb16, partition_tokens,
+                                  false).ws_bytes);
+        if (mb.valid && mb.ws_bytes <= documented) shape = mb;
+    }
+    if (!shape.valid) {
+        if (partition_tokens == 0 && q_per_seq > 1 && head_dim == 128 &&
+            q_per_seq * (num_q_heads / num_kv_heads) >= 3)
+            partition_tokens = std::min<int32_t>(
+                2 * default_partition(num_q_heads, num_kv_heads, head_dim, mb16), 2048);
+        // the partial states are per (sequence, query, q head): the workspace of
+        // num_seqs * q_per_seq single-query sequences
+        shape = decode_shape(num_seqs * q_per_seq, num_q_heads, num_kv_heads, head_dim, mb16, partition_tokens,
+                             q_per_seq == 1);
+    }
     if (!shape.valid) return PA_ERR_SHAPE;
     st = check_workspace(shape, workspace, workspace_bytes);
     if (st != PA_OK) return st;

@@ -94,3 +94,17 @@ def test_multi_rows_match_rolled_back_decodes():
         pa.pa_decode(dec, qm[:, j].contiguous(), g.k_cache, g.v_cache, g.tables, dev_int(lens), c.scale)
         torch.cuda.synchronize()
         assert float(np.abs(host_f64(dec) - out[:, j]).max()) <= 2e-3
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_multi_balanced_split(dtype):
+    """Several queries on matrix cores in the balanced split (partition 0 takes it
+    when its partial states, (16 + 96 stretches) x 32 units x 4 columns, fit the
+    documented workspace, 64 x 32 x 8 states of 512-token partitions: 32 heads,
+    4096-token tables): against the oracle, beside fixed 1024-token partitions."""
+    lens = [4096, 1, 2, 3, 4, 5, 17, 1000, 2500, 16, 3333, 64, 0, 4095, 129, 700]
+    c = make_decode_case(name=f"multi-balanced-{dtype}", seed=531, dtype=dtype, num_q_heads=32,
+                         num_kv_heads=32, head_dim=128, seq_lens=lens,
+                         num_blocks=sum((n + 15) // 16 for n in lens) + 4, max_blocks_per_seq=256,
+                         scale=1 / math.sqrt(128), write_last=True)
+    _check(c, 4, partitions=(0, 1024))
