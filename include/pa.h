@@ -227,10 +227,12 @@ int32_t pa_decode_split(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_he
 /*
  * pa_decode_workspace_size -- bytes of float32 partial results the decode calls
  * (16-bit and FP8) need for this shape and split (partition_tokens as for
- * pa_decode).  0 when every sequence fits one partition.  Layout (internal to
- * the library): per partial state a running max, a running sum and head_dim
- * accumulators.  Also 0 for a block_size other than 16 or 32 or other invalid
- * sizes.
+ * pa_decode), enough for either split that partition_tokens 0 may choose and,
+ * where PA_DECODE_SHARED_PREFIX can take effect, for its sequence groups (their
+ * shared runs' states and per-group block counts).  0 when every sequence fits
+ * one partition.  Layout (internal to the library): per partial state a
+ * running max, a running sum and head_dim accumulators.  Also 0 for a
+ * block_size other than 16 or 32 or other invalid sizes.
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
