@@ -165,6 +165,32 @@ def test_fp8_decode_matches_oracle(drawn):
                           f"{c.name} fp8 partition={part}")
 
 
+@PROPS
+@given(decode_cases())
+def test_decode_step_matches_oracle(drawn):
+    """pa_decode_step: the cache write of each sequence's newest token inside the decode."""
+    import paged_kv_cache_24_amd as pa
+    c, part = drawn
+    _say(c, partition=part, call="pa_decode_step")
+    g = DecodeOnGPU(c)
+    shape = (c.num_seqs, c.num_kv_heads, c.head_dim)
+    kn, vn = np.zeros(shape, np.uint16), np.zeros(shape, np.uint16)
+    live = np.flatnonzero(c.seq_lens > 0)
+    kn[live], vn[live] = c.key, c.value
+    out = torch.empty_like(g.q)
+    pa.pa_decode_step(out, g.q, dev_bits(kn, c.dtype), dev_bits(vn, c.dtype), g.k_cache, g.v_cache, g.tables,
+                      g.lens, c.scale, part)
+    kc, vc = oracle.ref_reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache, c.slot_mapping)
+    np.testing.assert_array_equal(g.k_cache.view(torch.int16).cpu().numpy().view(np.uint16), kc)
+    np.testing.assert_array_equal(g.v_cache.view(torch.int16).cpu().numpy().view(np.uint16), vc)
+    ref = oracle.ref_decode(c.q, kc, vc, c.block_tables, c.seq_lens, c.scale, c.dtype)
+    u = U_MFMA[c.dtype] if _mfma_decode(c, c.num_q_heads // c.num_kv_heads) else 0.0
+    keys = lambda b, n: (_tokens16(kc, c.block_tables[b], n, c.dtype),
+                         _tokens16(vc, c.block_tables[b], n, c.dtype))
+    assert_close_or_bound(host_f64(out), ref, c.dtype, _decode_bound(c, ref, keys, u),
+                          f"{c.name} step partition={part}")
+
+
 @st.composite
 def shared_prefix_cases(draw):
     """Runs of sequences sharing a prefix, cut across the waves' sequence groups."""
