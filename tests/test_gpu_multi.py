@@ -108,3 +108,17 @@ def test_multi_balanced_split(dtype):
                          num_blocks=sum((n + 15) // 16 for n in lens) + 4, max_blocks_per_seq=256,
                          scale=1 / math.sqrt(128), write_last=True)
     _check(c, 4, partitions=(0, 1024))
+
+
+def test_multi_balanced_split_head_chunks():
+    """32 (query, head) columns per kv head (8 q heads x 4 queries): two column
+    chunks per kv head in the balanced split (128 sequences, 2048-token tables,
+    so that its states fit the documented workspace)."""
+    rng = np.random.default_rng(532)
+    lens = rng.integers(0, 2049, 128)
+    lens[:6] = [0, 1, 2, 3, 4, 2048]
+    c = make_decode_case(name="multi-balanced-chunks", seed=533, dtype="bf16", num_q_heads=16,
+                         num_kv_heads=2, head_dim=128, seq_lens=lens,
+                         num_blocks=int(sum((n + 15) // 16 for n in lens)) + 4, max_blocks_per_seq=128,
+                         scale=1 / math.sqrt(128), write_last=True)
+    _check(c, 4, partitions=(0,))
