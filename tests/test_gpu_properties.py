@@ -242,7 +242,10 @@ def test_sequence_groups_match_oracle(drawn, fp8):
 def test_multi_query_matches_oracle(drawn, nq):
     import paged_kv_cache_24_amd as pa
     c, part = drawn
-    part = max(part, 0)   # the balanced split is a single-query layout
+    # 0 stands in for a drawn -1: with several queries it takes the balanced split
+    # wherever that applies (matrix cores, partial states within the documented
+    # workspace), which an explicit -1 would require
+    part = max(part, 0)
     _say(c, partition=part, queries=nq)
     g = DecodeOnGPU(c)
     g.write()
