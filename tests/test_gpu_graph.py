@@ -400,6 +400,43 @@ def test_captured_verification_step():
         assert_close(host_f64(out_graph), ref, "f16", f"verification replay {replay}")
 
 
+def test_captured_verification_step_balanced():
+    """The same capture in the balanced split: the default partition takes it for a
+    multi-query call where its partial states fit the workspace documented for the
+    call, as here (128 sequences with 2048-token tables, 8 q heads per kv head, so
+    32 (query, head) columns per kv head in two chunks; the sizes of the
+    two-chunk case of tests/test_gpu_multi.py)."""
+    import paged_kv_cache_24_amd as pa
+    nq, hq, hkv = 4, 16, 2
+    rng = np.random.default_rng(28)
+    lens = rng.integers(0, 301, 128)
+    lens[:4] = [0, 1, 16, 300]
+    c = make_decode_case(name="graph-multi-balanced", seed=29, dtype="f16", num_q_heads=hq,
+                         num_kv_heads=hkv, head_dim=128, seq_lens=lens,
+                         num_blocks=int(sum((n + 15) // 16 for n in lens)) + 4, max_blocks_per_seq=128,
+                         scale=1 / math.sqrt(128), write_last=False)
+    g = DecodeOnGPU(c)
+    qm = dev_bits(normal_bits(rng, (c.num_seqs, nq, hq, 128), "f16"), "f16")
+    part = 0
+    need = pa.pa_decode_workspace_size(c.num_seqs * nq, hq, hkv, 128, 16, c.max_blocks_per_seq, part)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out_graph = torch.empty_like(qm)
+
+    def step(out=out_graph):
+        pa.pa_decode_multi(out, qm, g.k_cache, g.v_cache, g.tables, g.lens, c.scale, part, workspace=ws)
+
+    graph = _capture(step)
+    for replay in range(3):
+        new_lens = np.maximum(lens - 5 * replay, 0).astype(np.int32)
+        q = normal_bits(rng, tuple(qm.shape), "f16")
+        g.lens.copy_(dev_int(new_lens))
+        qm.copy_(dev_bits(q, "f16"))
+        got, eager = _replay_then_eager(graph, step, out_graph, lambda: torch.empty_like(qm))
+        np.testing.assert_array_equal(got, eager, err_msg=f"replay {replay}")
+        ref = oracle.ref_decode_multi(q, c.k_cache, c.v_cache, c.block_tables, new_lens, c.scale, "f16")
+        assert_close(host_f64(out_graph), ref, "f16", f"balanced verification replay {replay}")
+
+
 def test_captured_prefill_step():
     """Cache write + chunked prefill captured once, replayed with new q and new
     k/v and with the cached-context lengths shortened in place."""
