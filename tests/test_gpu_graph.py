@@ -57,11 +57,15 @@ def _replay_then_eager(graph, step, out_graph, fresh):
     return host_bits(out_graph).copy(), host_bits(eager)
 
 
+@pytest.mark.parametrize("part", [64, -1])
 @pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("hq,hkv,dtype", [(8, 8, "f16"), (16, 2, "bf16")])
-def test_captured_decode_step(hq, hkv, dtype, bs):
+def test_captured_decode_step(hq, hkv, dtype, bs, part):
     """Cache write + split decode captured once; replayed with new q, shortened
-    lengths (rollback) and two sequences trading table rows."""
+    lengths (rollback) and two sequences trading table rows.  Fixed 64-token
+    partitions (several per sequence: the merge runs too) or the balanced split
+    (-1), whose stretch boundaries the kernels find from the lengths on the
+    device at every replay."""
     import paged_kv_cache_24_amd as pa
     lens = [300, 17, 1, 129, 64, 0]
     c = make_decode_case(name="graph", seed=21, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv,
@@ -69,7 +73,6 @@ def test_captured_decode_step(hq, hkv, dtype, bs):
                          scale=1 / math.sqrt(128), write_last=True, block_size=bs)
     g = DecodeOnGPU(c)
     kc, vc = oracle.ref_reshape_and_cache(c.key, c.value, c.k_cache, c.v_cache, c.slot_mapping)
-    part = 64                                   # several partitions: exercises the merge too
     need = pa.pa_decode_workspace_size(c.num_seqs, hq, hkv, 128, bs, c.max_blocks_per_seq, part)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     out_graph = torch.empty_like(g.q)
