@@ -58,6 +58,7 @@ __device__ __forceinline__ void fp8_vector_segment(const DecodeArgs& a, int b, i
     constexpr int RPW = kWave / LPR;        // token rows per load instruction
     constexpr int TPL = kBlockSize / RPW;   // tokens per lane per block
     constexpr int NBUF = 4;                 // blocks in registers: one computed, three in flight
+    constexpr float kLazyMax = 8.f;         // log2 margin before the reference max is raised
     static_assert(TPL == 1 || TPL == 2, "head_dim 64 or 128");
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -126,11 +127,7 @@ __device__ __forceinline__ void fp8_vector_segment(const DecodeArgs& a, int b, i
     };
 
     auto process = [&](const Buf& buf, int j) {
-        const bool full = buf.ok && (j + 1) * kBlockSize <= n;
-        bool valid[TPL];
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) valid[i] = full || (buf.ok && j * kBlockSize + r * TPL + i < n);
-
+        const bool full = buf.ok && (j + 1) * kBlockSize <= n;   // uniform
         float s[HPW][TPL];
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
@@ -143,9 +140,7 @@ __device__ __forceinline__ void fp8_vector_segment(const DecodeArgs& a, int b, i
                 float t;
                 if constexpr (LPR == 8) t = group_sum<8>(d);
                 else t = quad_sum(d);
-                // rows past the end or in a bad block: -inf (a select, so NaN
-                // codes or scales there cannot leak)
-                s[h][i] = valid[i] ? t * ksc : -INFINITY;
+                s[h][i] = t * ksc;
             }
         }
         float vf[TPL][16];
@@ -157,21 +152,44 @@ __device__ __forceinline__ void fp8_vector_segment(const DecodeArgs& a, int b, i
             for (int e = 0; e < 4; ++e) {
                 const f32x2_t lo = fp8x2_to_f32<false>(w[e]);
                 const f32x2_t hi = fp8x2_to_f32<true>(w[e]);
-                vf[i][4 * e] = valid[i] ? lo.x : 0.f;
-                vf[i][4 * e + 1] = valid[i] ? lo.y : 0.f;
-                vf[i][4 * e + 2] = valid[i] ? hi.x : 0.f;
-                vf[i][4 * e + 3] = valid[i] ? hi.y : 0.f;
+                vf[i][4 * e] = lo.x;
+                vf[i][4 * e + 1] = lo.y;
+                vf[i][4 * e + 2] = hi.x;
+                vf[i][4 * e + 3] = hi.y;
             }
-            vsc[i] = valid[i] ? buf.vs[i] : 0.f;
+            vsc[i] = buf.vs[i];
+        }
+        if (!full) {
+            // the sequence's last block, or a block outside the pool: rows past the
+            // end score -inf and weigh 0 (selects, so NaN codes or scales there
+            // cannot leak into the sums)
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                const bool valid = buf.ok && j * kBlockSize + r * TPL + i < n;
+#pragma unroll
+                for (int h = 0; h < HPW; ++h) s[h][i] = valid ? s[h][i] : -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) vf[i][e] = valid ? vf[i][e] : 0.f;
+                vsc[i] = valid ? vsc[i] : 0.f;
+            }
         }
 #pragma unroll
         for (int h = 0; h < HPW; ++h) {
             float mb = s[h][0];
 #pragma unroll
             for (int i = 1; i < TPL; ++i) mb = fmaxf(mb, s[h][i]);
-            const float mn = fmaxf(m[h], mb);
-            const float mu = mn == -INFINITY ? 0.f : mn;
-            const float alpha = fast_exp2(m[h] - mu);
+            // The lane's reference max m is raised only when a score passes it by
+            // more than 2^8 (log2 domain), so probabilities stay below 256 and the
+            // state is rescaled once per raise, not once per block; the result is
+            // the same algebra.  While m = -inf any finite score raises it.
+            if (mb > m[h] + kLazyMax) {
+                const float alpha = fast_exp2(m[h] - mb);   // 0 while m = -inf
+                l[h] *= alpha;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[h][e] *= alpha;
+                m[h] = mb;
+            }
+            const float mu = m[h] == -INFINITY ? 0.f : m[h];
             float pv[TPL];
             float ps = 0.f;
 #pragma unroll
@@ -180,15 +198,14 @@ __device__ __forceinline__ void fp8_vector_segment(const DecodeArgs& a, int b, i
                 ps += p;
                 pv[i] = p * vsc[i];
             }
-            l[h] = fmaf(l[h], alpha, ps);
+            l[h] += ps;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                float x = acc[h][e] * alpha;
+                float x = acc[h][e];
 #pragma unroll
                 for (int i = 0; i < TPL; ++i) x = fmaf(pv[i], vf[i][e], x);
                 acc[h][e] = x;
             }
-            m[h] = mn;
         }
     };
     // NBUF register buffers: while one block is computed, NBUF-1 are in flight
