@@ -903,12 +903,12 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
     };
 
     // Pipeline.  At tile t the products read K(t), V(t) and (late waves, see
-    // below) V(t-1).  K waves copy K(t+3) into the buffer of K(t-1), V waves copy
-    // V(t+2) into that of V(t-2): both last read before this tile's barrier.
-    // Every wave issues 4 copies per tile, so a K wave waiting until at most 8
-    // are outstanding has K(t) in LDS, and a V wave waiting until at most 4 has
-    // V(t).  Tiles past the last are clamped to it: those copies refill buffers
-    // nobody reads again.
+    // below) V(t-1).  K waves copy K(t+3) into the buffer of K(t-1) (at the end
+    // of tile t), V waves copy V(t+2) into that of V(t-2) (after tile t's
+    // barrier): both last read before this tile's barrier.  Every wave issues 4
+    // copies per tile, so a K wave waiting until at most 8 are outstanding has
+    // K(t) in LDS, and a V wave waiting until at most 4 has V(t).  Tiles past
+    // the last are clamped to it: those copies refill buffers nobody reads again.
     // prologue: K(0..2) or V(0..1)
     const int clampt = ntiles - 1;
     if constexpr (F8) {
@@ -1126,19 +1126,19 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
         constexpr int B = decltype(par)::value;          // t & 3
         constexpr int R = decltype(role)::value;
         uint16_t* kcur = kbuf(std::integral_constant<int, B>());   // K(t)
+        const int pb_copy = pb_next;   // block id of this tile's copy
         if constexpr (F8) {
             // tile t was written during tile t-1; the codes of tile t+1 go out now
             __syncthreads();
             load8(min(t + 1, clampt), pb_next, st8);
         } else {
-            // K waves copy K(t+3) into the buffer of K(t-1); V waves copy V(t+2) into
-            // that of V(t-2) (read at tile t-2 and, by the late waves, at tile t-1)
-            uint16_t* dst = kwave ? kbuf(std::integral_constant<int, (B + 3) & 3>())
-                                  : vbuf(std::integral_constant<int, (B + 2) & 3>());
+            // K waves copy K(t+3) into the buffer of K(t-1) at the end of the tile
+            // (below); V waves copy V(t+2) into that of V(t-2) (read at tile t-2
+            // and, by the late waves, at tile t-1) right after the barrier
             if (kwave) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8): K(t) is in
             else __builtin_amdgcn_s_waitcnt(0x0F74);         // vmcnt(4): V(t) is in
             __syncthreads();
-            stage(min(t + ahead, clampt), valid_block(pb_next), dst);
+            if (!kwave) stage(min(t + ahead, clampt), valid_block(pb_next), vbuf(std::integral_constant<int, (B + 2) & 3>()));
         }
         // The next copy's block id is a scalar load, which shares its wait counter
         // with the LDS reads and may complete out of order: the first LDS wait
@@ -1162,6 +1162,12 @@ __global__ __launch_bounds__(64 * kW16, 1) void prefill16_kernel(PrefillArgs a) 
         // the late waves' V products); past the last tile this refills buffers
         // that nobody reads again
         if constexpr (F8) store8(st8, std::integral_constant<int, (B + 1) & 3>());
+        // the K waves' copy goes out after their PV, where they wait for the next
+        // barrier anyway, so that it does not delay this tile's S^T products
+        // (1.5% faster than issuing it after the barrier); K(t-1)'s buffer is
+        // not read during tile t
+        if constexpr (!F8)
+            if (kwave) stage(min(t + ahead, clampt), valid_block(pb_copy), kbuf(std::integral_constant<int, (B + 3) & 3>()));
     };
     auto tile_loop = [&](auto role) __attribute__((always_inline)) {
         for (int t = 0; t < ntiles; t += 4) {
